@@ -1,0 +1,246 @@
+"""fp64 CPU oracle for the 4-bit NF4-style codebook GEMV / small-N GEMM.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg load it; the product path never does.  The arithmetic lives
+in ``oracle.c`` (plain C, fp64); this module compiles it with gcc and wraps
+it with numpy arrays via ctypes.  It imports nothing from the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# A test may point the wrapper at another build of oracle.c (the mutation
+# test builds deliberately broken copies to show the pins catch them).
+_OVERRIDE = os.environ.get("Q4_ORACLE_LIB")
+_lib = None
+_lock = threading.Lock()
+
+PACK_NONFINITE = 1
+PACK_OVERFLOW = 2
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc one oracle source file into a shared library (strict IEEE)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-fno-fast-math", "-ffp-contract=off", "-I", _HERE, src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        compile_source(_SRC, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if _OVERRIDE:
+            lib = ctypes.CDLL(_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB_PATH):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.oracle_codebook_f64.argtypes = [P]
+        lib.oracle_codebook_f32.argtypes = [P]
+        lib.oracle_phi_inv.argtypes = [ctypes.c_double]
+        lib.oracle_phi_inv.restype = ctypes.c_double
+        lib.oracle_f32_to_f16_rne.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_f16_rne.restype = ctypes.c_uint16
+        lib.oracle_f32_to_f16_rne_array.argtypes = [P, I64, P]
+        lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_to_f64.restype = ctypes.c_double
+        lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_f64.restype = ctypes.c_double
+        lib.oracle_pack_rows.argtypes = [P, I64, I64, I64, I64, P, P]
+        lib.oracle_pack_rows.restype = ctypes.c_int
+        lib.oracle_dequant.argtypes = [P, P, I64, I64, P]
+        lib.oracle_gemv_rows.argtypes = [P, P, I64, I64, P, I64, I64, P, P]
+        lib.oracle_gemm.argtypes = [P, P, I64, I64, P, I64, P, P]
+        lib.oracle_argmax_f64.argtypes = [P, I64]
+        lib.oracle_argmax_f64.restype = I64
+        lib.oracle_argmax_f32.argtypes = [P, I64]
+        lib.oracle_argmax_f32.restype = I64
+        _lib = lib
+        return lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _check_shape(M: int, K: int):
+    if M < 0 or K < 0 or K % 64 != 0:
+        raise ValueError(f"oracle: need M >= 0 and K a multiple of 64, got M={M} K={K}")
+
+
+def codebook_f64() -> np.ndarray:
+    out = np.zeros(16, np.float64)
+    _load().oracle_codebook_f64(_ptr(out))
+    return out
+
+
+def codebook_f32() -> np.ndarray:
+    out = np.zeros(16, np.float32)
+    _load().oracle_codebook_f32(_ptr(out))
+    return out
+
+
+def phi_inv(p: float) -> float:
+    return _load().oracle_phi_inv(p)
+
+
+def f32_to_f16_bits(v) -> np.ndarray:
+    v = np.ascontiguousarray(np.asarray(v, np.float32).ravel())
+    out = np.zeros(v.size, np.uint16)
+    _load().oracle_f32_to_f16_rne_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def f16_bits_to_f64(h) -> np.ndarray:
+    lib = _load()
+    h = np.asarray(h, np.uint16).ravel()
+    return np.array([lib.oracle_f16_to_f64(int(t)) for t in h], np.float64)
+
+
+def bf16_bits_to_f64(b) -> np.ndarray:
+    lib = _load()
+    b = np.asarray(b, np.uint16).ravel()
+    return np.array([lib.oracle_bf16_to_f64(int(t)) for t in b], np.float64)
+
+
+def pack(W: np.ndarray, threads: int = 1):
+    """W fp32 [M,K] -> (codes uint8 [M,K/2], scales fp16 bits uint16 [M,K/64], status)."""
+    W = np.ascontiguousarray(W, np.float32)
+    M, K = W.shape
+    _check_shape(M, K)
+    codes = np.zeros((M, K // 2), np.uint8)
+    scales = np.zeros((M, K // 64), np.uint16)
+    lib = _load()
+    status = [0]
+
+    def run(r0, r1, slot):
+        slot.append(lib.oracle_pack_rows(_ptr(W), M, K, r0, r1, _ptr(codes), _ptr(scales)))
+
+    _run_rows(M, threads, run, status)
+    st = 0
+    for s in status[1:]:
+        st |= s
+    return codes, scales, st
+
+
+def dequant(codes: np.ndarray, scales: np.ndarray, M: int, K: int) -> np.ndarray:
+    _check_shape(M, K)
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint16)
+    out = np.zeros((M, K), np.float64)
+    _load().oracle_dequant(_ptr(codes), _ptr(scales), M, K, _ptr(out))
+    return out
+
+
+def gemv(codes, scales, M: int, K: int, x_bits, rows=None, threads: int = 1):
+    """y, S (fp64, length M).  rows=(r0, r1) restricts the work to those rows
+    (other entries stay NaN)."""
+    _check_shape(M, K)
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint16)
+    x_bits = np.ascontiguousarray(x_bits, np.uint16)
+    if x_bits.size != K:
+        raise ValueError("oracle.gemv: x must have K entries")
+    y = np.full(M, np.nan)
+    S = np.full(M, np.nan)
+    lib = _load()
+    r0, r1 = (0, M) if rows is None else rows
+
+    def run(a, b, slot):
+        lib.oracle_gemv_rows(_ptr(codes), _ptr(scales), M, K, _ptr(x_bits), a, b, _ptr(y), _ptr(S))
+
+    _run_rows(r1 - r0, threads, lambda a, b, s: run(r0 + a, r0 + b, s), [0])
+    return y, S
+
+
+def gemv_row_list(codes, scales, M: int, K: int, x_bits, rows):
+    """y, S for an explicit list of rows (returned in that order)."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint16)
+    x_bits = np.ascontiguousarray(x_bits, np.uint16)
+    lib = _load()
+    y = np.full(M, np.nan)
+    S = np.full(M, np.nan)
+    rows = np.asarray(rows, np.int64)
+    for r in rows:
+        lib.oracle_gemv_rows(_ptr(codes), _ptr(scales), M, K, _ptr(x_bits), int(r), int(r) + 1,
+                             _ptr(y), _ptr(S))
+    return y[rows], S[rows]
+
+
+def gemm(codes, scales, M: int, K: int, X_bits):
+    """Y, S fp64 [N, M] for X bf16 bits [N, K]."""
+    _check_shape(M, K)
+    X_bits = np.ascontiguousarray(X_bits, np.uint16)
+    N = X_bits.shape[0]
+    if X_bits.shape[1] != K:
+        raise ValueError("oracle.gemm: X must be [N, K]")
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint16)
+    Y = np.zeros((N, M), np.float64)
+    S = np.zeros((N, M), np.float64)
+    _load().oracle_gemm(_ptr(codes), _ptr(scales), M, K, _ptr(X_bits), N, _ptr(Y), _ptr(S))
+    return Y, S
+
+
+def argmax(y) -> int:
+    y = np.ascontiguousarray(y)
+    lib = _load()
+    if y.dtype == np.float64:
+        return int(lib.oracle_argmax_f64(_ptr(y), y.size))
+    if y.dtype == np.float32:
+        return int(lib.oracle_argmax_f32(_ptr(y), y.size))
+    raise TypeError("oracle.argmax: float32 or float64 only")
+
+
+def within_tolerance(y, y_ref, S, rel: float = 1e-3, abs_: float = 1e-5):
+    """The acceptance bound |y - y_ref| <= rel * S + abs_, element-wise.
+    Returns (ok, worst ratio of |y - y_ref| to the bound)."""
+    y = np.asarray(y, np.float64)
+    err = np.abs(y - y_ref)
+    bound = rel * S + abs_
+    ratio = err / bound
+    ok = bool(np.all(np.isfinite(y)) and np.all(err <= bound))
+    return ok, float(np.max(ratio)) if ratio.size else 0.0
+
+
+def _run_rows(n: int, threads: int, fn, status):
+    """Split [0, n) into `threads` contiguous ranges run on Python threads
+    (ctypes releases the GIL while the C code runs)."""
+    threads = max(1, min(int(threads), n if n > 0 else 1))
+    if threads == 1:
+        fn(0, n, status)
+        return
+    bounds = [n * t // threads for t in range(threads + 1)]
+    ts = []
+    slots = [[] for _ in range(threads)]
+    for t in range(threads):
+        th = threading.Thread(target=fn, args=(bounds[t], bounds[t + 1], slots[t]))
+        th.start()
+        ts.append(th)
+    for th in ts:
+        th.join()
+    for s in slots:
+        status.extend(s)

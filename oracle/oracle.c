@@ -1,0 +1,315 @@
+/*
+ * oracle.c -- plain, slow, obviously correct fp64 CPU oracle for the 4-bit
+ * 16-level NF4-style codebook GEMV  y = dequant(W) . x  and its small-N GEMM
+ * form  Y[n,:] = dequant(W) . X[n,:].
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call it; the
+ * HIP library is checked against it.  It shares no code, header, table or
+ * constant generator with the HIP library: the codebook here is computed
+ * from its construction, the library carries its own frozen bit patterns.
+ *
+ * Build with plain gcc, no -ffast-math (every comparison below relies on
+ * exact IEEE arithmetic).
+ *
+ * Where the pages fix a step it is cited by page and section; where they are
+ * silent the reading taken is stated at the step.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ *
+ * Codebook.
+ *
+ * The deep-fold "Decode V2" page (section 6, "Linear primitive") names the
+ * format NF4 and dequantises through "the 16-float table"; no page prints the
+ * 16 values.  Reading taken: the NormalFloat-4 construction of the QLoRA
+ * paper (Dettmers et al., 2023), asymmetric with an exact zero:
+ *   - 8 positive levels: the standard-normal quantiles at 8 equally spaced
+ *     probabilities running from 1 - delta down towards 1/2 (1/2 excluded);
+ *   - 7 negative levels: minus the quantiles at 7 equally spaced
+ *     probabilities over the same range (1/2 excluded);
+ *   - one exact 0;
+ *   - all divided by the largest quantile, so the extremes are -1 and +1;
+ *   - delta = (1/30 + 1/32) / 2.
+ * The levels are computed in fp64 and rounded once to fp32.
+ * ------------------------------------------------------------------ */
+
+/* Standard normal CDF written through erfc (no cancellation in the tails). */
+static double phi(double z) { return 0.5 * erfc(-z / sqrt(2.0)); }
+
+/* Upper tail 1 - phi(z), also through erfc. */
+static double phi_upper(double z) { return 0.5 * erfc(z / sqrt(2.0)); }
+
+double oracle_phi_inv(double p) {
+    /* Bisection: phi is strictly increasing; stop when the bracket can no
+     * longer shrink in fp64.  Above 1/2 the test is made on the upper tail,
+     * phi(z) < p  <=>  1 - phi(z) > 1 - p, where 1 - p is exact and the tail
+     * keeps full relative precision. */
+    const int upper = p > 0.5;
+    const double q = 1.0 - p; /* exact for p in [1/2, 1] */
+    double lo = -40.0, hi = 40.0;
+    for (int it = 0; it < 2000; ++it) {
+        double mid = 0.5 * (lo + hi);
+        if (mid <= lo || mid >= hi) break;
+        int below = upper ? (phi_upper(mid) > q) : (phi(mid) < p);
+        if (below)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return 0.5 * (lo + hi);
+}
+
+void oracle_codebook_f64(double out[16]) {
+    const double delta = 0.5 * (1.0 / 30.0 + 1.0 / 32.0);
+    const double p_top = 1.0 - delta;
+    const double top = oracle_phi_inv(p_top);
+    /* negative levels, most negative first: out[0..6] */
+    for (int j = 0; j < 7; ++j) {
+        double p = p_top - (double)j * (p_top - 0.5) / 7.0;
+        out[j] = -oracle_phi_inv(p) / top;
+    }
+    out[7] = 0.0;
+    /* positive levels, smallest first: out[8..15] */
+    for (int j = 0; j < 8; ++j) {
+        double p = p_top - (double)(7 - j) * (p_top - 0.5) / 8.0;
+        out[8 + j] = oracle_phi_inv(p) / top;
+    }
+    /* j == 0 on both sides divides the top quantile by itself: exactly -1
+     * and +1. */
+}
+
+void oracle_codebook_f32(float out[16]) {
+    double d[16];
+    oracle_codebook_f64(d);
+    for (int i = 0; i < 16; ++i) out[i] = (float)d[i];
+}
+
+/* ------------------------------------------------------------------ *
+ * Number formats.
+ *
+ * golang.design accel/tensor, func Cast: f32 -> f16 rounds to nearest-even,
+ * and a value outside the f16 range becomes an infinity; bf16 -> f32 is exact
+ * (bf16 is the top half of f32).
+ * ------------------------------------------------------------------ */
+
+void oracle_f32_to_f16_rne_array(const float *v, int64_t n, uint16_t *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_f16_rne(v[i]);
+}
+
+double oracle_f16_to_f64(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0x1f)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+    else
+        v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) 2^(e-15) */
+    return sign ? -v : v;
+}
+
+double oracle_bf16_to_f64(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+uint16_t oracle_f32_to_f16_rne(float v) {
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    if (isnan(v)) return (uint16_t)(sign | 0x7e00);
+    double a = fabs((double)v);
+    /* Halfway between the largest finite half (65504) and the next step
+     * (65536) is 65520; ties-to-even goes up there, so >= 65520 is inf. */
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7c00);
+    /* Spacing of representable halves around a: 2^-24 below 2^-14
+     * (subnormals), else 2^(floor(log2 a) - 10). */
+    double q;
+    if (a < ldexp(1.0, -14)) {
+        q = ldexp(1.0, -24);
+    } else {
+        int ex;
+        frexp(a, &ex); /* a = f 2^ex, f in [0.5, 1) => floor(log2 a) = ex-1 */
+        q = ldexp(1.0, ex - 1 - 10);
+    }
+    double n = a / q; /* exact: q is a power of two */
+    double fl = floor(n);
+    double frac = n - fl; /* exact */
+    double r;
+    if (frac > 0.5)
+        r = fl + 1.0;
+    else if (frac < 0.5)
+        r = fl;
+    else
+        r = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0; /* tie: to even */
+    double u = r * q; /* the rounded magnitude, exactly a half value */
+    if (u == 0.0) return sign;
+    if (u < ldexp(1.0, -14)) /* subnormal half: mantissa = u / 2^-24 */
+        return (uint16_t)(sign | (uint16_t)(u / ldexp(1.0, -24)));
+    int ex;
+    double f = frexp(u, &ex);          /* u = f 2^ex, f in [0.5,1) */
+    int E = ex - 1;                    /* u = (2f) 2^E, 2f in [1,2) */
+    int mant = (int)((2.0 * f - 1.0) * 1024.0); /* exact */
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)mant);
+}
+
+/* ------------------------------------------------------------------ *
+ * Quantisation (pack).
+ *
+ * Groups of 64 weights along K (deep-fold "Decode V2", section 2: hidden and
+ * intermediate sizes are multiples of 64, the NF4 group).  Reading taken for
+ * the unprinted steps:
+ *   - scale: the block's absolute maximum, stored as fp16 (round to nearest
+ *     even); blocks whose absmax rounds to fp16 infinity, and blocks holding
+ *     a non-finite weight, are refused (accel/tensor, func Cast: an
+ *     out-of-range value becomes infinity, and a silently clamped weight is
+ *     not allowed);
+ *   - the codes are chosen against the stored fp16 scale s: the level nearest
+ *     to w / s in exact arithmetic, an exact midpoint going to the lower
+ *     level; written without division as
+ *         code = #{ i in 0..14 : w > m_i * s },  m_i = (c_i + c_{i+1}) / 2,
+ *     every product and comparison exact in fp64 (m_i has at most 25
+ *     significant bits, s at most 11);
+ *   - a block whose scale is 0 gets code 7 (the exact zero level) throughout;
+ *   - packing: byte j of a row holds code 2j in its low nibble and code 2j+1
+ *     in its high nibble (accel/tensor, type Int4: low nibble first).
+ * ------------------------------------------------------------------ */
+
+int oracle_pack_rows(const float *W, int64_t M, int64_t K, int64_t row0,
+                     int64_t row1, uint8_t *codes, uint16_t *scales) {
+    (void)M;
+    float cb[16];
+    oracle_codebook_f32(cb);
+    double mid[15];
+    for (int i = 0; i < 15; ++i) mid[i] = ((double)cb[i] + (double)cb[i + 1]) / 2.0;
+
+    const int64_t nblk = K / 64;
+    int status = 0;
+    for (int64_t m = row0; m < row1; ++m) {
+        for (int64_t b = 0; b < nblk; ++b) {
+            const float *w = W + m * K + b * 64;
+            float amax = 0.0f;
+            int bad = 0;
+            for (int k = 0; k < 64; ++k) {
+                if (!isfinite(w[k])) bad = 1;
+                float aw = fabsf(w[k]);
+                if (aw > amax) amax = aw;
+            }
+            if (bad) {
+                status |= ORACLE_PACK_NONFINITE;
+                continue;
+            }
+            uint16_t s16 = oracle_f32_to_f16_rne(amax);
+            if (s16 == 0x7c00) {
+                status |= ORACLE_PACK_OVERFLOW;
+                continue;
+            }
+            scales[m * nblk + b] = s16;
+            double s = oracle_f16_to_f64(s16);
+            uint8_t code[64];
+            for (int k = 0; k < 64; ++k) {
+                if (s == 0.0) {
+                    code[k] = 7;
+                    continue;
+                }
+                int c = 0;
+                for (int i = 0; i < 15; ++i)
+                    if ((double)w[k] > mid[i] * s) ++c;
+                code[k] = (uint8_t)c;
+            }
+            uint8_t *dst = codes + m * (K / 2) + b * 32;
+            for (int j = 0; j < 32; ++j)
+                dst[j] = (uint8_t)(code[2 * j] | (code[2 * j + 1] << 4));
+        }
+    }
+    return status;
+}
+
+int oracle_pack(const float *W, int64_t M, int64_t K, uint8_t *codes,
+                uint16_t *scales) {
+    return oracle_pack_rows(W, M, K, 0, M, codes, scales);
+}
+
+/* ------------------------------------------------------------------ *
+ * Dequantisation and products.
+ *
+ * deep-fold "Decode V2", section 3 (CPU oracle): the NF4 linear is decode
+ * then matmul, Y = What @ x; section 6: the value of a weight is the table
+ * entry of its code times its group's scale.  Here every What = c * s is
+ * exact in fp64 (24 + 11 significant bits), x is bf16 widened exactly, every
+ * product What * x is exact (at most 43 bits), and the sum runs over
+ * ascending k in fp64.  S is the sum of |What * x|, the scale of the
+ * acceptance bound.
+ * ------------------------------------------------------------------ */
+
+static int code_at(const uint8_t *codes, int64_t K, int64_t m, int64_t k) {
+    uint8_t byte = codes[m * (K / 2) + k / 2];
+    return (k % 2 == 0) ? (byte & 0xf) : (byte >> 4);
+}
+
+void oracle_dequant(const uint8_t *codes, const uint16_t *scales, int64_t M,
+                    int64_t K, double *What) {
+    float cb[16];
+    oracle_codebook_f32(cb);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            double s = oracle_f16_to_f64(scales[m * (K / 64) + k / 64]);
+            What[m * K + k] = (double)cb[code_at(codes, K, m, k)] * s;
+        }
+}
+
+void oracle_gemv_rows(const uint8_t *codes, const uint16_t *scales, int64_t M,
+                      int64_t K, const uint16_t *x, int64_t row0, int64_t row1,
+                      double *y, double *S) {
+    (void)M;
+    float cb[16];
+    oracle_codebook_f32(cb);
+    for (int64_t m = row0; m < row1; ++m) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double s = oracle_f16_to_f64(scales[m * (K / 64) + k / 64]);
+            double w = (double)cb[code_at(codes, K, m, k)] * s;
+            double t = w * oracle_bf16_to_f64(x[k]);
+            acc += t;
+            mag += fabs(t);
+        }
+        y[m] = acc;
+        if (S) S[m] = mag;
+    }
+}
+
+void oracle_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M,
+                 int64_t K, const uint16_t *x, double *y, double *S) {
+    oracle_gemv_rows(codes, scales, M, K, x, 0, M, y, S);
+}
+
+void oracle_gemm(const uint8_t *codes, const uint16_t *scales, int64_t M,
+                 int64_t K, const uint16_t *X, int64_t N, double *Y, double *S) {
+    /* The prefill form is the same product for each of the N rows of X
+     * (accel/tensor, func Int4MatMul: the same representation and
+     * reconstruction as the vector form). */
+    for (int64_t n = 0; n < N; ++n)
+        oracle_gemv_rows(codes, scales, M, K, X + n * K, 0, M, Y + n * M,
+                         S ? S + n * M : (double *)0);
+}
+
+/* accel/tensor, func Argmax: the index of the largest value, ties to the
+ * lowest index. */
+int64_t oracle_argmax_f64(const double *y, int64_t n) {
+    int64_t best = -1;
+    for (int64_t i = 0; i < n; ++i)
+        if (!isnan(y[i]) && (best < 0 || y[i] > y[best])) best = i;
+    return best;
+}
+
+int64_t oracle_argmax_f32(const float *y, int64_t n) {
+    int64_t best = -1;
+    for (int64_t i = 0; i < n; ++i)
+        if (!isnan(y[i]) && (best < 0 || y[i] > y[best])) best = i;
+    return best;
+}

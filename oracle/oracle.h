@@ -1,0 +1,82 @@
+/*
+ * oracle.h -- declarations of the fp64 CPU oracle for the 4-bit, 16-level
+ * NF4-style codebook weight-only GEMV and its small-N GEMM form.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the slow, plain reference that the HIP
+ * library is checked against.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load it.  It shares no code, header,
+ * table or constant with the HIP library.
+ *
+ * Sources (the deep-fold "Decode V2 - resident executor" page unless noted):
+ *   - section 6 "Linear primitive": the GEMV dequantises with a 16-float table
+ *     times a per-group scale times x, fp32 on the GPU;
+ *   - section 2 "Synthetic models": quantisation groups are 64 weights long;
+ *   - section 3 "CPU oracle": the NF4 matmul is decode-then-matmul,
+ *     Y = What @ x;
+ *   - golang.design accel/tensor page, type Int4: nibbles are packed low
+ *     nibble first; func Cast: f32 -> f16 rounds to nearest-even and an
+ *     out-of-range value becomes infinity; bf16 -> f32 is exact;
+ *     func Argmax: ties go to the lowest index.
+ */
+#ifndef Q4_ORACLE_H
+#define Q4_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Pack status flags (OR-ed together over every block). */
+#define ORACLE_PACK_NONFINITE 1 /* some weight is NaN or +-inf            */
+#define ORACLE_PACK_OVERFLOW  2 /* some block absmax rounds to fp16 +inf  */
+
+/* The 16 levels in fp64 straight from the construction, ascending. */
+void oracle_codebook_f64(double out[16]);
+/* The same levels rounded once to fp32 (the frozen table). */
+void oracle_codebook_f32(float out[16]);
+/* Inverse standard normal CDF by bisection on erfc (exposed for pinning). */
+double oracle_phi_inv(double p);
+
+/* fp32 -> IEEE binary16 bits, round to nearest, ties to even; |v| >= 65520
+ * gives +-inf; NaN gives a quiet NaN. */
+uint16_t oracle_f32_to_f16_rne(float v);
+void oracle_f32_to_f16_rne_array(const float *v, int64_t n, uint16_t *out);
+double oracle_f16_to_f64(uint16_t h);
+/* bf16 bits -> value (exact widening). */
+double oracle_bf16_to_f64(uint16_t b);
+
+/* Quantise rows [row0,row1) of W[M,K] (fp32, row-major; K % 64 == 0).
+ * codes: M*K/2 bytes, byte (m,j) = code(m,2j) | code(m,2j+1) << 4.
+ * scales: fp16 bits, [M][K/64] row-major.
+ * Returns the OR of ORACLE_PACK_* flags over the rows (0 = ok); the output of
+ * a flagged block is unspecified. */
+int oracle_pack_rows(const float *W, int64_t M, int64_t K, int64_t row0,
+                     int64_t row1, uint8_t *codes, uint16_t *scales);
+int oracle_pack(const float *W, int64_t M, int64_t K, uint8_t *codes,
+                uint16_t *scales);
+
+/* What[M,K] in fp64 (exact: level times scale). */
+void oracle_dequant(const uint8_t *codes, const uint16_t *scales, int64_t M,
+                    int64_t K, double *What);
+
+/* y[m] = sum_k What[m,k] * x[k] (fp64, ascending k) and
+ * S[m] = sum_k |What[m,k] * x[k]| for m in [row0,row1); x is bf16 bits.
+ * y and S are indexed by m (full-length arrays). S may be NULL. */
+void oracle_gemv_rows(const uint8_t *codes, const uint16_t *scales, int64_t M,
+                      int64_t K, const uint16_t *x, int64_t row0, int64_t row1,
+                      double *y, double *S);
+void oracle_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M,
+                 int64_t K, const uint16_t *x, double *y, double *S);
+
+/* Y[n,m] = sum_k What[m,k] * X[n,k] for n < N (X bf16 bits [N,K]); S alike. */
+void oracle_gemm(const uint8_t *codes, const uint16_t *scales, int64_t M,
+                 int64_t K, const uint16_t *X, int64_t N, double *Y, double *S);
+
+/* First index of the maximum (NaN never wins); -1 if n == 0 or all NaN. */
+int64_t oracle_argmax_f64(const double *y, int64_t n);
+int64_t oracle_argmax_f32(const float *y, int64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,53 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies oracle.c, plants one plausible mistake (a swapped nibble, a
+wrong tie rule, a dropped scale, a wrong block index, ...), builds it with
+gcc on the CPU, and runs the pin suite against that build in a fresh
+process: the suite has to fail.  The real oracle is never modified.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "unpack_nibble_swap": ("(k % 2 == 0) ? (byte & 0xf) : (byte >> 4)",
+                           "(k % 2 == 0) ? (byte >> 4) : (byte & 0xf)"),
+    "pack_nibble_swap": ("(code[2 * j] | (code[2 * j + 1] << 4))",
+                         "(code[2 * j + 1] | (code[2 * j] << 4))"),
+    "tie_to_upper": ("if ((double)w[k] > mid[i] * s) ++c;",
+                     "if ((double)w[k] >= mid[i] * s) ++c;"),
+    "codes_against_fp32_absmax": ("if ((double)w[k] > mid[i] * s) ++c;",
+                                  "if ((double)w[k] > mid[i] * (double)amax) ++c;"),
+    "negative_grid_8": ("(p_top - 0.5) / 7.0", "(p_top - 0.5) / 8.0"),
+    "dropped_scale": ("double w = (double)cb[code_at(codes, K, m, k)] * s;",
+                      "double w = (double)cb[code_at(codes, K, m, k)];"),
+    "block_index_32": ("double s = oracle_f16_to_f64(scales[m * (K / 64) + k / 64]);\n            double w",
+                       "double s = oracle_f16_to_f64(scales[m * (K / 64) + k / 128]);\n            double w"),
+    "f16_tie_up": ("r = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "r = fl + 1.0;"),
+    "argmax_last_tie": ("if (!isnan(y[i]) && (best < 0 || y[i] > y[best])) best = i;\n    return best;\n}\n\nint64_t oracle_argmax_f32",
+                        "if (!isnan(y[i]) && (best < 0 || y[i] >= y[best])) best = i;\n    return best;\n}\n\nint64_t oracle_argmax_f32"),
+    "abs_sum_signed": ("mag += fabs(t);", "mag += t;"),
+    "zero_block_code_0": ("code[k] = 7;\n                    continue;", "code[k] = 0;\n                    continue;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mpath = tmp_path / "oracle_mutant.c"
+    mpath.write_text(src.replace(old, new))
+    lib = oracle.compile_source(str(mpath), str(tmp_path / "liboracle_mutant.so"))
+    env = dict(os.environ, Q4_ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"

@@ -1,0 +1,499 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test checks the oracle against an independent implementation (scipy's
+normal quantile, numpy's float16 conversion, numpy/BLAS products, Python's
+exact rationals), a closed form, an invariant, or a hand-built example whose
+answer follows from the pages' definitions:
+
+- deep-fold "Decode V2", section 6 (Linear primitive): 16-float table times
+  group scale times x; section 2: groups of 64 along K;
+- golang.design accel/tensor, type Int4 (low nibble first), func Cast
+  (f32 -> f16 nearest-even, overflow -> inf; bf16 -> f32 exact), func Argmax
+  (ties to the lowest index).
+
+No GPU is needed.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import ndtr, ndtri
+
+import workloads as wl
+
+DELTA = 0.5 * (1 / 30 + 1 / 32)
+
+
+# --------------------------------------------------------------------------
+# Codebook
+# --------------------------------------------------------------------------
+
+def _scipy_levels():
+    """NF4 levels from scipy's inverse normal CDF on numpy's linspace grids."""
+    top = 1 - DELTA
+    pos = ndtri(np.linspace(top, 0.5, 9)[:-1])
+    neg = -ndtri(np.linspace(top, 0.5, 8)[:-1])
+    v = np.sort(np.concatenate([pos, neg, [0.0]])) / ndtri(top)
+    return v
+
+
+def test_codebook_matches_scipy_construction(oracle_mod):
+    ours = oracle_mod.codebook_f32()
+    ref = _scipy_levels().astype(np.float32)
+    assert np.array_equal(ours.view(np.uint32), ref.view(np.uint32)), (ours, ref)
+    ours64 = oracle_mod.codebook_f64()
+    assert np.max(np.abs(ours64 - _scipy_levels())) < 1e-14
+
+
+def test_codebook_structure(oracle_mod):
+    c = oracle_mod.codebook_f32()
+    assert c.size == 16
+    assert c[0] == -1.0 and c[15] == 1.0
+    assert c.view(np.uint32)[7] == 0  # +0.0 exactly
+    assert np.all(np.diff(c.astype(np.float64)) > 0)
+    assert np.sum(c < 0) == 7 and np.sum(c > 0) == 8
+
+
+def test_codebook_levels_are_normal_quantiles(oracle_mod):
+    # Forward check with the CDF: level * Phi^-1(1-delta) sits at the grid
+    # probability the construction names.
+    c = oracle_mod.codebook_f64()
+    top = ndtri(1 - DELTA)
+    p_pos = ndtr(c[8:] * top)
+    grid_pos = (1 - DELTA) - np.arange(7, -1, -1) * ((1 - DELTA) - 0.5) / 8
+    assert np.allclose(p_pos, grid_pos, rtol=0, atol=1e-14)
+    p_neg = ndtr(-c[:7] * top)
+    grid_neg = (1 - DELTA) - np.arange(0, 7) * ((1 - DELTA) - 0.5) / 7
+    assert np.allclose(p_neg, grid_neg, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("p", [1e-12, 1e-6, 0.01, 0.2, 0.5, 0.5 + 1e-9, 0.7, 0.9677, 0.999, 1 - 1e-9])
+def test_phi_inv_against_scipy(oracle_mod, p):
+    z = oracle_mod.phi_inv(p)
+    assert abs(z - ndtri(p)) <= 1e-13 * max(1.0, abs(z))
+
+
+# --------------------------------------------------------------------------
+# Number formats
+# --------------------------------------------------------------------------
+
+def _f16_bits_numpy(v):
+    with np.errstate(over="ignore"):
+        return np.asarray(v, np.float32).astype(np.float16).view(np.uint16)
+
+
+def test_f32_to_f16_rne_matches_numpy_on_structured_values(oracle_mod):
+    all_h = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    hv = all_h.view(np.float16).astype(np.float32)
+    finite = np.isfinite(hv)
+    hv = hv[finite]
+    # every half value, its fp32 neighbours, and the midpoints between
+    # consecutive halves (the ties) with their fp32 neighbours
+    pos = np.sort(np.unique(np.abs(hv)))
+    mids = ((pos[:-1].astype(np.float64) + pos[1:].astype(np.float64)) / 2).astype(np.float32)
+    cand = np.concatenate([hv, mids, -mids])
+    cand = np.concatenate([cand, np.nextafter(cand, np.float32(np.inf)),
+                           np.nextafter(cand, np.float32(-np.inf))])
+    extra = np.array([0.0, -0.0, 65504, 65519.996, 65520, 65536, 1e38, np.inf, -np.inf,
+                      2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -26, 1e-30,
+                      2.0 ** -14, 2.0 ** -14 - 2.0 ** -25], np.float32)
+    cand = np.concatenate([cand, extra, -extra])
+    ours = oracle_mod.f32_to_f16_bits(cand)
+    ref = _f16_bits_numpy(cand)
+    bad = np.nonzero(ours != ref)[0]
+    assert bad.size == 0, [(float(cand[i]), hex(ours[i]), hex(ref[i])) for i in bad[:10]]
+
+
+def test_f32_to_f16_rne_matches_numpy_random(oracle_mod):
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    v = bits.view(np.float32)
+    v = v[~np.isnan(v)]
+    assert np.array_equal(oracle_mod.f32_to_f16_bits(v), _f16_bits_numpy(v))
+    # values concentrated in the half range, where rounding matters
+    v2 = (rng.standard_normal(1 << 20) * np.exp2(rng.integers(-26, 17, 1 << 20))).astype(np.float32)
+    assert np.array_equal(oracle_mod.f32_to_f16_bits(v2), _f16_bits_numpy(v2))
+
+
+def test_f32_to_f16_nan_stays_nan(oracle_mod):
+    h = oracle_mod.f32_to_f16_bits([np.nan])[0]
+    assert (h & 0x7c00) == 0x7c00 and (h & 0x3ff) != 0
+
+
+def test_f16_to_f64_all_patterns(oracle_mod):
+    h = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    ours = oracle_mod.f16_bits_to_f64(h)
+    ref = h.view(np.float16).astype(np.float64)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    m = ~np.isnan(ref)
+    assert np.array_equal(ours[m], ref[m])
+    assert np.array_equal(np.signbit(ours[m]), np.signbit(ref[m]))
+
+
+def test_bf16_to_f64_all_patterns(oracle_mod):
+    b = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    ours = oracle_mod.bf16_bits_to_f64(b)
+    ref = (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    m = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.array_equal(ours[m], ref[m])
+
+
+# --------------------------------------------------------------------------
+# Pack
+# --------------------------------------------------------------------------
+
+def _unpack_codes(codes, M, K):
+    """Codes [M, K] from the packed bytes, low nibble = even k (accel/tensor
+    type Int4)."""
+    lo = codes & 0xF
+    hi = codes >> 4
+    out = np.empty((M, K), np.int64)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out
+
+
+def _edge_matrix():
+    """64-row, 256-column matrix mixing ordinary and degenerate blocks."""
+    rng = np.random.default_rng(11)
+    W = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    W[0, :64] = 0.0                     # zero block
+    W[1, :64] = -0.0                    # negative-zero block
+    W[2, :64] = 1e-9                    # absmax below half the smallest fp16 subnormal
+    W[3, :64] = rng.standard_normal(64) * 1e-6   # subnormal fp16 scale
+    W[4, :64] = rng.standard_normal(64) * 1e3    # large scale
+    W[5, 64:128] = 65519.0              # rounds to 65504
+    W[6, :64] = rng.standard_normal(64).astype(np.float32) * np.float32(2.0 ** -14)
+    W[7, :] = np.exp2(rng.integers(-30, 10, 256)).astype(np.float32) * np.sign(rng.standard_normal(256)).astype(np.float32)
+    W[8, :64] = 0.0
+    W[8, 5] = 1.0                       # one nonzero in a block
+    W[9, :64] = 1.0                     # constant block
+    W[10, :64] = -1.0
+    return W
+
+
+def test_scale_is_fp16_rne_of_block_absmax(oracle_mod):
+    for W in (wl.weights(256, 512, 0), _edge_matrix()):
+        M, K = W.shape
+        _, scales, st = oracle_mod.pack(W)
+        assert st == 0
+        amax = np.abs(W.reshape(M, K // 64, 64)).max(axis=2)
+        assert np.array_equal(scales, _f16_bits_numpy(amax))
+
+
+def _nearest_check(W, codes, scales, cb):
+    """Every chosen level is a nearest level to w/s (exact arithmetic decides
+    near-ties); an exact midpoint goes to the lower level."""
+    M, K = W.shape
+    code = _unpack_codes(codes, M, K)
+    s = np.repeat(scales.view(np.float16).astype(np.float64), 64, axis=1)
+    w = W.astype(np.float64)
+    lv = cb.astype(np.float64)
+    d = np.abs(w[..., None] - lv[None, None, :] * s[..., None])  # [M,K,16]
+    chosen = np.take_along_axis(d, code[..., None], axis=2)[..., 0]
+    best = d.min(axis=2)
+    zero_s = s == 0
+    assert np.all(code[zero_s] == 7)
+    suspicious = np.nonzero(~zero_s & (chosen > best * (1 + 1e-9)))
+    assert suspicious[0].size == 0, "chosen level is not nearest"
+    # near-ties: settle exactly with rationals
+    close = np.nonzero(~zero_s & (np.sort(d, axis=2)[..., 1] <= best * (1 + 1e-9)))
+    for m, k in zip(*close):
+        wf = Fraction(float(W[m, k]))
+        sf = Fraction(float(s[m, k]))
+        dist = [abs(wf - Fraction(float(c)) * sf) for c in cb]
+        dmin = min(dist)
+        nearest = [j for j in range(16) if dist[j] == dmin]
+        assert code[m, k] == min(nearest), (m, k, nearest, code[m, k])
+
+
+def test_pack_chooses_nearest_level_brute_force(oracle_mod):
+    cb = oracle_mod.codebook_f32()
+    for W in (wl.weights(256, 512, 0), _edge_matrix()):
+        codes, scales, st = oracle_mod.pack(W)
+        assert st == 0
+        _nearest_check(W, codes, scales, cb)
+
+
+def test_pack_tie_goes_to_lower_level(oracle_mod):
+    cb = oracle_mod.codebook_f32().astype(np.float64)
+    tried = 0
+    for i in range(15):
+        mid = Fraction(float(cb[i])) / 2 + Fraction(float(cb[i + 1])) / 2
+        mf = np.float32(float(mid))
+        if Fraction(float(mf)) != mid:
+            continue  # midpoint not representable in fp32 at scale 1
+        tried += 1
+        W = np.zeros((1, 64), np.float32)
+        W[0, 0] = 1.0          # pins the scale to exactly 1.0
+        W[0, 1] = mf
+        W[0, 2] = np.nextafter(mf, np.float32(np.inf))
+        W[0, 3] = np.nextafter(mf, np.float32(-np.inf))
+        codes, scales, st = oracle_mod.pack(W)
+        code = _unpack_codes(codes, 1, 64)[0]
+        assert scales[0, 0] == 0x3C00
+        assert code[1] == i and code[2] == i + 1 and code[3] == i
+    assert tried >= 3
+
+
+def test_pack_nibble_order_and_layout_hand_built(oracle_mod):
+    # Weights placed exactly on levels (scale 1) so every code is known; the
+    # expected bytes are written from the rule: byte j = code 2j | code 2j+1 << 4.
+    cb = oracle_mod.codebook_f32()
+    M, K = 3, 192
+    want = np.zeros((M, K), np.int64)
+    for m in range(M):
+        for k in range(K):
+            want[m, k] = (3 * m + 5 * k + (k // 64)) % 16
+        for b in range(K // 64):
+            want[m, b * 64] = 15  # absmax 1.0 in every block -> scale exactly 1
+    W = cb[want].astype(np.float32)
+    codes, scales, st = oracle_mod.pack(W)
+    assert st == 0
+    assert np.all(scales == 0x3C00)
+    for m in range(M):
+        for j in range(K // 2):
+            assert codes[m, j] == (want[m, 2 * j] | (want[m, 2 * j + 1] << 4))
+    # one concrete byte spelled out: codes 3 then 12 give 0xC3
+    W2 = np.zeros((1, 64), np.float32)
+    W2[0, 0], W2[0, 1], W2[0, 2] = cb[3], cb[12], 1.0
+    c2, _, _ = oracle_mod.pack(W2)
+    assert c2[0, 0] == 0xC3 and c2[0, 1] == 0x7F
+
+
+def test_pack_zero_and_degenerate_blocks(oracle_mod):
+    W = _edge_matrix()
+    codes, scales, st = oracle_mod.pack(W)
+    assert st == 0
+    for m in (0, 1, 2):
+        assert scales[m, 0] == 0
+        assert np.all(codes[m, :32] == 0x77)
+    assert 0 < scales[3, 0] < 0x0400  # subnormal fp16 scale
+    assert scales[5, 1] == 0x7BFF       # 65519 -> 65504
+    # a lone nonzero in a zero block: it is the absmax, so level +1, the rest 0
+    code = _unpack_codes(codes, 64, 256)
+    assert code[8, 5] == 15 and np.all(np.delete(code[8, :64], 5) == 7)
+    assert np.all(code[9, :64] == 15) and np.all(code[10, :64] == 0)
+
+
+def test_pack_refuses_nonfinite_and_overflow(oracle_mod):
+    W = np.zeros((2, 128), np.float32)
+    W[0, 3] = np.nan
+    assert oracle_mod.pack(W)[2] == oracle_mod.PACK_NONFINITE
+    W[0, 3] = np.inf
+    assert oracle_mod.pack(W)[2] == oracle_mod.PACK_NONFINITE
+    W[0, 3] = 0
+    W[1, 100] = -65520.0
+    assert oracle_mod.pack(W)[2] == oracle_mod.PACK_OVERFLOW
+    W[0, 3] = -np.inf
+    assert oracle_mod.pack(W)[2] == oracle_mod.PACK_NONFINITE | oracle_mod.PACK_OVERFLOW
+    W[:] = 0
+    W[1, 100] = 65519.99
+    assert oracle_mod.pack(W)[2] == 0
+
+
+def test_pack_idempotent_through_dequant(oracle_mod):
+    for W in (wl.weights(256, 512, 0), _edge_matrix()):
+        M, K = W.shape
+        codes, scales, _ = oracle_mod.pack(W)
+        W2 = oracle_mod.dequant(codes, scales, M, K).astype(np.float32)
+        codes2, scales2, st = oracle_mod.pack(W2)
+        assert st == 0
+        assert np.array_equal(codes, codes2) and np.array_equal(scales, scales2)
+
+
+@pytest.mark.parametrize("j", [-3, -1, 1, 4])
+def test_pack_scale_linearity(oracle_mod, j):
+    W = wl.weights(64, 512, 5)
+    codes, scales, _ = oracle_mod.pack(W)
+    codes2, scales2, st = oracle_mod.pack((W * np.float32(2.0 ** j)).astype(np.float32))
+    assert st == 0
+    assert np.array_equal(codes, codes2)
+    s1 = scales.view(np.float16).astype(np.float64)
+    s2 = scales2.view(np.float16).astype(np.float64)
+    assert np.array_equal(s2, s1 * 2.0 ** j)
+
+
+def test_pack_error_bound_closed_form(oracle_mod):
+    # |w - What| is at most half the widest gap between neighbouring levels,
+    # times s, plus the amount by which |w| may exceed s after rounding.
+    cb = oracle_mod.codebook_f32().astype(np.float64)
+    half_gap = np.max(np.diff(cb)) / 2
+    assert abs(half_gap - (cb[1] - cb[0]) / 2) < 1e-15  # widest gap is the first
+    W = wl.weights(256, 2048, 6)
+    M, K = W.shape
+    codes, scales, _ = oracle_mod.pack(W)
+    What = oracle_mod.dequant(codes, scales, M, K)
+    s = np.repeat(scales.view(np.float16).astype(np.float64), 64, axis=1)
+    err = np.abs(W.astype(np.float64) - What)
+    bound = half_gap * s + np.maximum(0.0, np.abs(W) - s)
+    assert np.all(err <= bound * (1 + 1e-12))
+    assert np.max(err / s) > 0.9 * half_gap  # and the bound is nearly attained
+
+
+def test_pack_row_ranges_compose(oracle_mod):
+    W = wl.weights(97, 256, 9)
+    c1, s1, _ = oracle_mod.pack(W, threads=1)
+    c4, s4, _ = oracle_mod.pack(W, threads=4)
+    assert np.array_equal(c1, c4) and np.array_equal(s1, s4)
+
+
+# --------------------------------------------------------------------------
+# Dequant, GEMV, GEMM
+# --------------------------------------------------------------------------
+
+def test_dequant_hand_built_bytes(oracle_mod):
+    cb = oracle_mod.codebook_f32().astype(np.float64)
+    codes = np.zeros((2, 64), np.uint8)
+    codes[0, 0] = 0xC3
+    codes[1, 33] = 0x5A
+    scales = np.array([[0x3C00, 0x4000], [0x3800, 0xC000]], np.uint16)  # 1, 2, 0.5, -2
+    What = oracle_mod.dequant(codes, scales, 2, 128)
+    assert What[0, 0] == cb[3] * 1.0 and What[0, 1] == cb[12] * 1.0
+    assert What[0, 2] == cb[0] * 1.0 and What[0, 64] == cb[0] * 2.0
+    assert What[1, 66] == cb[0xA] * -2.0 and What[1, 67] == cb[0x5] * -2.0
+    assert What[1, 0] == cb[0] * 0.5
+
+
+def _fixture(M, K, seed, xrec="normal"):
+    W = wl.weights(M, K, seed)
+    x = wl.activation(K, seed, xrec)
+    return W, x
+
+
+def test_gemv_matches_blas_on_dequant(oracle_mod):
+    for (M, K, seed) in [(256, 512, 0), (37, 1280, 12), (5, 11008, 13)]:
+        W, x = _fixture(M, K, seed)
+        codes, scales, _ = oracle_mod.pack(W)
+        y, S = oracle_mod.gemv(codes, scales, M, K, x)
+        What = oracle_mod.dequant(codes, scales, M, K)
+        xv = wl.bf16_bits_to_f32(x).astype(np.float64)
+        ref = What @ xv
+        assert np.all(np.abs(y - ref) <= 1e-12 * np.abs(What) @ np.abs(xv))
+        assert np.allclose(S, np.abs(What) @ np.abs(xv), rtol=1e-12, atol=0)
+
+
+def test_gemv_exact_rational_tiny(oracle_mod):
+    M, K = 4, 128
+    W, x = _fixture(M, K, 21)
+    codes, scales, _ = oracle_mod.pack(W)
+    y, S = oracle_mod.gemv(codes, scales, M, K, x)
+    cb = oracle_mod.codebook_f32()
+    code = _unpack_codes(codes, M, K)
+    xv = wl.bf16_bits_to_f32(x)
+    for m in range(M):
+        exact = Fraction(0)
+        for k in range(K):
+            s = Fraction(float(scales[m, k // 64:k // 64 + 1].view(np.float16)[0]))
+            exact += Fraction(float(cb[code[m, k]])) * s * Fraction(float(xv[k]))
+        assert abs(Fraction(y[m]) - exact) <= Fraction(K * 2.0 ** -53) * Fraction(S[m])
+
+
+def test_gemv_one_hot_x_selects_column(oracle_mod):
+    M, K = 64, 256
+    W, _ = _fixture(M, K, 22)
+    codes, scales, _ = oracle_mod.pack(W)
+    What = oracle_mod.dequant(codes, scales, M, K)
+    for k in (0, 1, 63, 64, 201, 255):
+        x = np.zeros(K, np.uint16)
+        x[k] = 0x3F80  # bf16 1.0
+        y, _ = oracle_mod.gemv(codes, scales, M, K, x)
+        assert np.array_equal(y, What[:, k])
+
+
+def test_gemv_constant_code_closed_form(oracle_mod):
+    cb = oracle_mod.codebook_f32().astype(np.float64)
+    M, K = 16, 256
+    rng = np.random.default_rng(3)
+    scales = _f16_bits_numpy(rng.uniform(0.01, 2, (M, K // 64)))
+    x = np.full(K, 0x3F80, np.uint16)
+    for j in (0, 3, 7, 12, 15):
+        codes = np.full((M, K // 2), j | (j << 4), np.uint8)
+        y, _ = oracle_mod.gemv(codes, scales, M, K, x)
+        sums = scales.view(np.float16).astype(np.float64).sum(axis=1)
+        assert np.allclose(y, cb[j] * 64 * sums, rtol=1e-14, atol=0)
+        if j == 7:
+            assert np.all(y == 0)
+
+
+def test_gemv_zero_block_contributes_nothing(oracle_mod):
+    M, K = 32, 512
+    W, x = _fixture(M, K, 23)
+    codes, scales, _ = oracle_mod.pack(W)
+    y0, _ = oracle_mod.gemv(codes, scales, M, K, x)
+    W[:, 128:192] = 0
+    codes2, scales2, _ = oracle_mod.pack(W)
+    y1, _ = oracle_mod.gemv(codes2, scales2, M, K, x)
+    x2 = x.copy()
+    x2[128:192] = 0
+    y2, _ = oracle_mod.gemv(codes, scales, M, K, x2)
+    assert np.allclose(y1, y2, rtol=1e-13, atol=1e-15)
+    assert not np.allclose(y0, y1)
+
+
+def test_gemv_linearity_bit_exact(oracle_mod):
+    M, K = 64, 1024
+    W, x = _fixture(M, K, 24)
+    codes, scales, _ = oracle_mod.pack(W)
+    y, S = oracle_mod.gemv(codes, scales, M, K, x)
+    x2 = (x.astype(np.uint32) + (2 << 7)).astype(np.uint16)  # exponent + 2: x * 4 (normal x)
+    y2, S2 = oracle_mod.gemv(codes, scales, M, K, x2)
+    assert np.array_equal(y2, 4 * y) and np.array_equal(S2, 4 * S)
+    s2 = (scales.astype(np.uint32) + (1 << 10)).astype(np.uint16)  # scales * 2 (normal)
+    y3, _ = oracle_mod.gemv(codes, s2, M, K, x)
+    assert np.array_equal(y3, 2 * y)
+
+
+def test_gemv_row_range_and_list(oracle_mod):
+    M, K = 300, 256
+    W, x = _fixture(M, K, 25)
+    codes, scales, _ = oracle_mod.pack(W)
+    y, S = oracle_mod.gemv(codes, scales, M, K, x)
+    yt, St = oracle_mod.gemv(codes, scales, M, K, x, threads=3)
+    assert np.array_equal(y, yt) and np.array_equal(S, St)
+    rows = [299, 0, 17, 150]
+    yl, Sl = oracle_mod.gemv_row_list(codes, scales, M, K, x, rows)
+    assert np.array_equal(yl, y[rows]) and np.array_equal(Sl, S[rows])
+
+
+def test_gemm_matches_blas_and_gemv(oracle_mod):
+    M, K, N = 96, 640, 5
+    W = wl.weights(M, K, 26)
+    X = wl.activations(N, K, 26, "unit_rms")
+    codes, scales, _ = oracle_mod.pack(W)
+    Y, S = oracle_mod.gemm(codes, scales, M, K, X)
+    What = oracle_mod.dequant(codes, scales, M, K)
+    Xv = wl.bf16_bits_to_f32(X).astype(np.float64)
+    ref = Xv @ What.T
+    assert np.all(np.abs(Y - ref) <= 1e-12 * (np.abs(Xv) @ np.abs(What).T))
+    for n in range(N):
+        yn, Sn = oracle_mod.gemv(codes, scales, M, K, X[n])
+        assert np.array_equal(Y[n], yn) and np.array_equal(S[n], Sn)
+
+
+# --------------------------------------------------------------------------
+# Argmax and the acceptance bound
+# --------------------------------------------------------------------------
+
+def test_argmax_ties_lowest_index_and_nan(oracle_mod):
+    y = np.array([1.0, 3.0, 2.0, 3.0, 3.0], np.float64)
+    assert oracle_mod.argmax(y) == 1
+    assert oracle_mod.argmax(y.astype(np.float32)) == 1
+    y = np.array([np.nan, -5.0, np.nan, -5.0], np.float32)
+    assert oracle_mod.argmax(y) == 1
+    assert oracle_mod.argmax(np.zeros(0)) == -1
+    rng = np.random.default_rng(1)
+    for _ in range(20):
+        v = rng.integers(0, 7, 1000).astype(np.float64)  # many ties
+        assert oracle_mod.argmax(v) == int(np.argmax(v))
+
+
+def test_within_tolerance_bound():
+    import oracle
+    ok, r = oracle.within_tolerance([1.0 + 1e-5], np.array([1.0]), np.array([10.0]))
+    assert ok and r < 1
+    ok, r = oracle.within_tolerance([1.0 + 0.02], np.array([1.0]), np.array([10.0]))
+    assert not ok and r > 1
+    ok, _ = oracle.within_tolerance([np.nan], np.array([1.0]), np.array([10.0]))
+    assert not ok
