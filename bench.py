@@ -1,0 +1,238 @@
+"""Benchmark of the 4-bit codebook GEMV on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--copies R] [--no-secondary]
+
+A step is one q4_gemv call on the lm_head workload (M x K = 151936 x 2048,
+x bf16 unit-RMS, y fp32): the projection the metric is quoted on.  Inputs are
+resident in HBM before timing starts.  Each step reads a different one of R
+packed copies of the matrix, so that the 256 MB Infinity Cache and the L2
+cannot serve the weights (R * 166 MB >= 600 MB).
+
+Byte model (deep-fold "Decode V2", section 6 bench: GB/s = packed + scale +
+x over the median time; the y write is added here):
+    bytes = M*K/2 (codes) + M*K/32 (fp16 scales) + 2K (x) + 4M (y).
+
+Output: one JSON line with the metric, the per-launch kernel time measured
+with HIP events on the launch stream, the HBM roofline fraction against the
+8 TB/s peak, secondary workloads (down-projection GEMV, small-N GEMM), and the
+fp64 oracle timed on the host cores as a CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemv_bytes(M, K, N=1):
+    return M * K // 2 + M * K // 32 + 2 * K * N + 4 * M * N
+
+
+def _upload_bits(torch, a, dtype, dev):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(dtype)
+
+
+def prepare(torch, q4, wl, name, dev, copies, n_tokens=None):
+    """Generate the seeded workload, pack it on the GPU, replicate it."""
+    c = wl.CONFIGS[name]
+    M, K = c["M"], c["K"]
+    t = time.time()
+    W = wl.weights(M, K, c["seed"])
+    log(f"{name}: generated W {M}x{K} in {time.time() - t:.1f}s")
+    Wd = torch.from_numpy(W).to(dev)
+    codes, scales, status = q4.q4_pack(Wd)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"q4_pack flagged the {name} weights: {int(status.item())}")
+    del Wd
+    reps = [(codes, scales)]
+    for _ in range(copies - 1):
+        reps.append((codes.clone(), scales.clone()))
+    N = c["N"] if n_tokens is None else n_tokens
+    if N == 1:
+        xb = wl.activation(K, c["seed"], c["x"])
+        x = _upload_bits(torch, xb, torch.bfloat16, dev)
+    else:
+        xb = wl.activations(N, K, c["seed"], c["x"])
+        x = _upload_bits(torch, xb, torch.bfloat16, dev)
+    torch.cuda.synchronize()
+    return W, xb, reps, x
+
+
+def time_calls(torch, fn, reps, steps, warmup):
+    """Warm up, then time `steps` calls (rotating over the copies) with one
+    event pair per launch on the launch stream.  Returns (wall ms per step,
+    mean kernel ms, median kernel ms)."""
+    for i in range(warmup):
+        fn(*reps[i % len(reps)])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        fn(*reps[(warmup + i) % len(reps)])
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ks = np.array([a.elapsed_time(b) for a, b in ev])
+    return wall_ms, float(ks.mean()), float(np.median(ks))
+
+
+def cpu_baseline(oracle, wl, W, xb, name):
+    """The oracle's fp64 GEMV over the whole matrix on the host cores, as it
+    stands: rows split over threads, repeated until ~10 s have passed."""
+    c = wl.CONFIGS[name]
+    M, K = c["M"], c["K"]
+    threads = min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count() or 1)
+    codes, scales, st = oracle.pack(W, threads=threads)
+    assert st == 0
+    times = []
+    y_ref = S = None
+    t_start = time.time()
+    while True:
+        t = time.perf_counter()
+        y_ref, S = oracle.gemv(codes, scales, M, K, xb, threads=threads)
+        times.append(time.perf_counter() - t)
+        if time.time() - t_start > 10.0 or len(times) >= 50:
+            break
+    sec = float(np.median(times))
+    return {
+        "value": round(gemv_bytes(M, K) / sec / 1e9, 3),
+        "unit": "GB/s",
+        "us_per_call": round(sec * 1e6, 1),
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"full {name} GEMV {M}x{K} (fp64 oracle, rows split over {threads} threads), "
+                  f"{len(times)} calls in {time.time() - t_start:.1f}s, median",
+    }, y_ref, S
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the path is measured on one MI355X; "
+              f"--gpus {args.gpus} is not supported (row-sharded multi-GPU use is a design note, not built).",
+              flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import bit_weight_gemv_amd as q4
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    q4.lib()
+
+    name = "lm_head"
+    c = wl.CONFIGS[name]
+    M, K = c["M"], c["K"]
+    W, xb, reps, x = prepare(torch, q4, wl, name, dev, args.copies)
+    y = torch.empty(M, dtype=torch.float32, device=dev)
+
+    def step(codes, scales):
+        q4.q4_gemv(codes, scales, x, y)
+
+    wall_ms, k_mean_ms, k_med_ms = time_calls(torch, step, reps, args.steps, args.warmup)
+    nbytes = gemv_bytes(M, K)
+    value = nbytes / (wall_ms * 1e-3) / 1e9
+    achieved = nbytes / (k_mean_ms * 1e-3) / 1e9
+    log(f"lm_head: wall {wall_ms * 1e3:.2f} us/step, kernel mean {k_mean_ms * 1e3:.2f} us "
+        f"(median {k_med_ms * 1e3:.2f}), {achieved:.0f} GB/s")
+
+    # y of the last call for the argmax check against the oracle
+    q4.q4_gemv(reps[0][0], reps[0][1], x, y)
+    y_gpu = y.cpu().numpy()
+
+    secondary = []
+    if not args.no_secondary:
+        del reps
+        torch.cuda.empty_cache()
+        for sname, ncopies, ntok in (("down", 50, None), ("smalln", 45, 32), ("gateup", 25, None)):
+            sc = wl.CONFIGS[sname]
+            _, _, sreps, sx = prepare(torch, q4, wl, sname, dev, ncopies, n_tokens=ntok)
+            if ntok is None:
+                sy = torch.empty(sc["M"], dtype=torch.float32, device=dev)
+
+                def sstep(cd, sl, sx=sx, sy=sy):
+                    q4.q4_gemv(cd, sl, sx, sy)
+                N = 1
+            else:
+                sy = torch.empty((ntok, sc["M"]), dtype=torch.float32, device=dev)
+
+                def sstep(cd, sl, sx=sx, sy=sy):
+                    q4.q4_gemm_smalln(cd, sl, sx, sy)
+                N = ntok
+            sw, skm, skmed = time_calls(torch, sstep, sreps, args.steps, args.warmup)
+            sb = gemv_bytes(sc["M"], sc["K"], N)
+            secondary.append({
+                "workload": f"{sname} {sc['M']}x{sc['K']} N={N}",
+                "us_per_call_kernel": round(skm * 1e3, 3),
+                "us_per_step_wall": round(sw * 1e3, 3),
+                "achieved_GBs": round(sb / (skm * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak": round(sb / (skm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "bytes": sb,
+            })
+            log(f"{sname}: kernel mean {skm * 1e3:.2f} us, {sb / (skm * 1e-3) / 1e9:.0f} GB/s")
+            del sreps, sx, sy
+            torch.cuda.empty_cache()
+
+    result = {
+        "metric": "4-bit GEMV us/call + achieved HBM GB/s (% of peak), MxK=151936x2048, N=1",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "us_per_call": round(k_mean_ms * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "dtype_note": "4-bit codes, fp16 table x fp16-converted bf16 x via v_dot2_f32_f16, fp32 accumulate",
+        "data": "synthetic (seeded SplitMix64 normals; W ~ N(0, 0.02^2), x unit-RMS bf16)",
+        "config": {"workload": "lm_head GEMV 151936x2048, N=1", "M": M, "K": K, "N": 1,
+                   "copies_rotated": args.copies, "bytes_per_call": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "q4::gemv_kernel<4,1>", "kernel_us_mean": round(k_mean_ms * 1e3, 3),
+                     "kernel_us_median": round(k_med_ms * 1e3, 3)},
+        "secondary": secondary,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        cb, y_ref, S = cpu_baseline(oracle, wl, W, xb, name)
+        result["cpu_baseline"] = cb
+        ok, ratio = oracle.within_tolerance(y_gpu, y_ref, S)
+        result["parity"] = {"within_tolerance": ok, "worst_ratio": round(ratio, 4),
+                            "argmax_gpu": oracle.argmax(y_gpu), "argmax_oracle": oracle.argmax(y_ref)}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

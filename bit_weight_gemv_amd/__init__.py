@@ -1,0 +1,189 @@
+"""Python binding of libq4 (4-bit NF4-style codebook GEMV / small-N GEMM for
+MI355X).  Argument marshalling only: every step runs in the HIP kernels of
+libq4.so, reached through its C ABI (include/q4.h).  PyTorch supplies device
+memory and the stream.
+
+    codes, scales, status = q4_pack(W)            # W: fp32 [M, K] on the GPU
+    y = q4_gemv(codes, scales, x)                 # x: bf16 [K]     -> fp32 [M]
+    Y = q4_gemm_smalln(codes, scales, X)          # X: bf16 [N, K]  -> fp32 [N, M]
+
+There is no fallback: if libq4.so is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libq4.so")
+
+Q4_OK = 0
+Q4_ERR_NULL = 1
+Q4_ERR_SHAPE = 2
+Q4_ERR_ALIGN = 3
+Q4_ERR_OVERLAP = 4
+Q4_ERR_DEVICE = 5
+Q4_MAX_K = 131072
+Q4_MAX_N = 32
+Q4_PACK_NONFINITE = 1
+Q4_PACK_OVERFLOW = 2
+
+EXPORTED = ("q4_codes_bytes", "q4_scales_bytes", "q4_codebook", "q4_status_string",
+            "q4_pack", "q4_gemv", "q4_gemm_smalln")
+
+_lib = None
+_lock = threading.Lock()
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libq4.so with argument types set (raises if it is absent)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libq4.so not built ({LIB_PATH}); run python -m bit_weight_gemv_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.q4_codes_bytes.argtypes = [I64, I64]
+        L.q4_codes_bytes.restype = ctypes.c_size_t
+        L.q4_scales_bytes.argtypes = [I64, I64]
+        L.q4_scales_bytes.restype = ctypes.c_size_t
+        L.q4_codebook.argtypes = [P]
+        L.q4_codebook.restype = None
+        L.q4_status_string.argtypes = [I32]
+        L.q4_status_string.restype = ctypes.c_char_p
+        L.q4_pack.argtypes = [P, I64, I64, P, P, P, P]
+        L.q4_pack.restype = I32
+        L.q4_gemv.argtypes = [P, P, I64, I64, P, P, P]
+        L.q4_gemv.restype = I32
+        L.q4_gemm_smalln.argtypes = [P, P, I64, I64, P, I64, P, P]
+        L.q4_gemm_smalln.restype = I32
+        _lib = L
+        return L
+
+
+def status_string(status: int) -> str:
+    return lib().q4_status_string(int(status)).decode()
+
+
+def codebook():
+    """The 16 frozen levels (fp32) as a Python list."""
+    out = (ctypes.c_float * 16)()
+    lib().q4_codebook(out)
+    return list(out)
+
+
+def codes_bytes(M: int, K: int) -> int:
+    return int(lib().q4_codes_bytes(M, K))
+
+
+def scales_bytes(M: int, K: int) -> int:
+    return int(lib().q4_scales_bytes(M, K))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(t, name, dtype, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def q4_pack(W, codes=None, scales=None, status=None, stream=None):
+    """Quantise fp32 W [M, K] -> (codes uint8 [M, K/2], scales fp16 [M, K/64],
+    status int32 [1]).  status holds Q4_PACK_* flags once the stream reaches it."""
+    torch = _torch()
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [M, K]")
+    M, K = W.shape
+    _check(W, "W", torch.float32, W.device)
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=W.device)
+    if scales is None:
+        scales = torch.empty((M, K // 64), dtype=torch.float16, device=W.device)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=W.device)
+    _check(codes, "codes", torch.uint8, W.device)
+    _check(scales, "scales", torch.float16, W.device)
+    _check(status, "status", torch.int32, W.device)
+    if codes.numel() * 2 != M * K or scales.numel() * 64 != M * K:
+        raise ValueError("codes/scales do not match W's shape")
+    st = lib().q4_pack(_ptr(W), M, K, _ptr(codes), _ptr(scales), _ptr(status), _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_pack")
+    return codes, scales, status
+
+
+def _mk(codes, scales):
+    torch = _torch()
+    if codes.dim() != 2 or scales.dim() != 2:
+        raise ValueError("codes must be [M, K/2] and scales [M, K/64]")
+    M, K = codes.shape[0], codes.shape[1] * 2
+    if scales.shape[0] != M or scales.shape[1] * 64 != K:
+        raise ValueError("codes and scales disagree on M, K")
+    _check(codes, "codes", torch.uint8, codes.device)
+    _check(scales, "scales", torch.float16, codes.device)
+    return M, K
+
+
+def q4_gemv(codes, scales, x, y=None, stream=None):
+    """y = dequant(W) . x for bf16 x [K]; returns fp32 y [M]."""
+    torch = _torch()
+    M, K = _mk(codes, scales)
+    if x.numel() != K:
+        raise ValueError(f"x must have K={K} entries")
+    _check(x, "x", torch.bfloat16, codes.device)
+    if y is None:
+        y = torch.empty(M, dtype=torch.float32, device=codes.device)
+    _check(y, "y", torch.float32, codes.device)
+    if y.numel() != M:
+        raise ValueError(f"y must have M={M} entries")
+    st = lib().q4_gemv(_ptr(codes), _ptr(scales), M, K, _ptr(x), _ptr(y), _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_gemv")
+    return y
+
+
+def q4_gemm_smalln(codes, scales, X, Y=None, stream=None):
+    """Y[n] = dequant(W) . X[n] for bf16 X [N, K], N <= 32; returns fp32 Y [N, M]."""
+    torch = _torch()
+    M, K = _mk(codes, scales)
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError(f"X must be [N, K={K}]")
+    N = X.shape[0]
+    _check(X, "X", torch.bfloat16, codes.device)
+    if Y is None:
+        Y = torch.empty((N, M), dtype=torch.float32, device=codes.device)
+    _check(Y, "Y", torch.float32, codes.device)
+    if Y.numel() != N * M:
+        raise ValueError("Y must be [N, M]")
+    st = lib().q4_gemm_smalln(_ptr(codes), _ptr(scales), M, K, _ptr(X), N, _ptr(Y), _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_gemm_smalln")
+    return Y

@@ -1,0 +1,115 @@
+// q4_api.cpp -- the exported C ABI (declared in include/q4.h): argument
+// checks on the host, then one launch on the caller's stream.
+//
+// Conventions (golang.design accel/tensor, Builder/Plan documentation): the
+// caller owns every buffer it names; everything is validated before anything
+// is launched, and a call refuses bad arguments instead of clamping them; the
+// counts are passed explicitly because a buffer's size cannot give them.
+#include "q4.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q4_device.h"
+#include "q4_internal.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void *p, uint64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return {a, a + (uintptr_t)bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+// K must be a positive multiple of 64 up to Q4_MAX_K; M >= 0 and M*K must
+// leave headroom in 64-bit byte counts.
+bool shape_ok(int64_t M, int64_t K) {
+    if (M < 0 || K <= 0 || K % 64 != 0 || K > Q4_MAX_K) return false;
+    if (M > (INT64_C(1) << 62) / K) return false;
+    return true;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+size_t q4_codes_bytes(int64_t M, int64_t K) { return shape_ok(M, K) ? (size_t)(M * (K / 2)) : 0; }
+
+size_t q4_scales_bytes(int64_t M, int64_t K) {
+    return shape_ok(M, K) ? (size_t)(M * (K / 64) * 2) : 0;
+}
+
+void q4_codebook(float out[16]) {
+    if (!out) return;
+    for (int i = 0; i < 16; ++i) out[i] = q4::level_f32(i);
+}
+
+const char *q4_status_string(int status) {
+    switch (status) {
+        case Q4_OK: return "Q4_OK";
+        case Q4_ERR_NULL: return "Q4_ERR_NULL: a required pointer is NULL";
+        case Q4_ERR_SHAPE: return "Q4_ERR_SHAPE: bad M, K or N";
+        case Q4_ERR_ALIGN: return "Q4_ERR_ALIGN: a pointer is not aligned as required";
+        case Q4_ERR_OVERLAP: return "Q4_ERR_OVERLAP: an output range overlaps another range";
+        case Q4_ERR_DEVICE: return "Q4_ERR_DEVICE: the HIP runtime refused the launch";
+        default: return "unknown q4 status";
+    }
+}
+
+int q4_pack(const float *W, int64_t M, int64_t K, uint8_t *codes, uint16_t *scales, int32_t *status,
+            void *stream) {
+    if (!shape_ok(M, K)) return Q4_ERR_SHAPE;
+    if (!W || !codes || !scales || !status) return Q4_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(status, 4))
+        return Q4_ERR_ALIGN;
+    const Range rw = range_of(W, (uint64_t)M * K * 4);
+    const Range rc = range_of(codes, (uint64_t)M * (K / 2));
+    const Range rs = range_of(scales, (uint64_t)M * (K / 64) * 2);
+    const Range rst = range_of(status, 4);
+    if (overlap(rc, rw) || overlap(rs, rw) || overlap(rst, rw) || overlap(rc, rs) || overlap(rc, rst) ||
+        overlap(rs, rst))
+        return Q4_ERR_OVERLAP;
+    // M == 0 still clears the status word: the call's contract is that
+    // *status holds the flags of this call.
+    return launch_status(q4::launch_pack(W, M, K, codes, scales, status, (hipStream_t)stream));
+}
+
+int q4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K, const uint16_t *x,
+            float *y, void *stream) {
+    if (!shape_ok(M, K)) return Q4_ERR_SHAPE;
+    if (M == 0) return Q4_OK;
+    if (!codes || !scales || !x || !y) return Q4_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(x, 16) || !aligned(y, 4))
+        return Q4_ERR_ALIGN;
+    const Range ry = range_of(y, (uint64_t)M * 4);
+    if (overlap(ry, range_of(codes, (uint64_t)M * (K / 2))) ||
+        overlap(ry, range_of(scales, (uint64_t)M * (K / 64) * 2)) || overlap(ry, range_of(x, (uint64_t)K * 2)))
+        return Q4_ERR_OVERLAP;
+    return launch_status(q4::launch_gemv(codes, scales, M, K, x, y, (hipStream_t)stream));
+}
+
+int q4_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K, const uint16_t *X,
+                   int64_t N, float *Y, void *stream) {
+    if (!shape_ok(M, K) || N < 0 || N > Q4_MAX_N) return Q4_ERR_SHAPE;
+    if (M == 0 || N == 0) return Q4_OK;
+    if (!codes || !scales || !X || !Y) return Q4_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(X, 16) || !aligned(Y, 4))
+        return Q4_ERR_ALIGN;
+    const Range ry = range_of(Y, (uint64_t)N * M * 4);
+    if (overlap(ry, range_of(codes, (uint64_t)M * (K / 2))) ||
+        overlap(ry, range_of(scales, (uint64_t)M * (K / 64) * 2)) ||
+        overlap(ry, range_of(X, (uint64_t)N * K * 2)))
+        return Q4_ERR_OVERLAP;
+    return launch_status(q4::launch_gemm_smalln(codes, scales, M, K, X, N, Y, (hipStream_t)stream));
+}
+
+}  // extern "C"

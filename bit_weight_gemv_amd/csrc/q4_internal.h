@@ -1,0 +1,18 @@
+// q4_internal.h -- launchers behind the C ABI (host side, not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+hipError_t launch_pack(const float *W, int64_t M, int64_t K, uint8_t *codes, uint16_t *scales,
+                       int32_t *status, hipStream_t stream);
+
+hipError_t launch_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                       const uint16_t *x, float *y, hipStream_t stream);
+
+hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                              const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
+
+}  // namespace q4

@@ -1,0 +1,128 @@
+/*
+ * q4.h -- C ABI of libq4: 4-bit, 16-level NF4-style codebook weight-only
+ * GEMV and small-N GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (deep-fold "Decode V2 - resident executor" page):
+ *   - section 6 "Linear primitive": a weight's value is the entry of a
+ *     16-float table picked by its 4-bit code, times the scale of its group,
+ *     and the GEMV accumulates table x scale x activation in fp32;
+ *   - section 2 "Synthetic models": groups are 64 weights along K;
+ *   - section 0 "Goals": the prefill form runs chunks of up to 32 tokens
+ *     (LIVE_MAX_N) through one dedicated product that reads the weights once
+ *     per chunk.
+ * Number formats (golang.design accel/tensor page): f32 -> f16 rounds to
+ * nearest even and an out-of-range value becomes an infinity (func Cast);
+ * bf16 -> f32 is exact (func Cast); products accumulate in f32 and return f32
+ * (func MatMul); 4-bit codes are packed low nibble first (type Int4).
+ *
+ * Packed format (identical on host and device, "canonical"):
+ *   codes  : uint8 [M][K/2], row-major; byte j of row m holds the code of
+ *            k = 2j in bits 0..3 and of k = 2j+1 in bits 4..7.
+ *   scales : IEEE binary16 bit patterns, uint16 [M][K/64], row-major; the
+ *            scale of block b of row m is the fp16 round-to-nearest-even of
+ *            max |W[m, 64b .. 64b+63]|.
+ *   value  : What[m,k] = level[code(m,k)] * scale[m][k/64], where level is the
+ *            frozen table returned by q4_codebook() (level[7] == 0 exactly).
+ *
+ * Conventions for every entry point:
+ *   - Data pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing and keeps no state between calls.
+ *   - All argument checks run on the host before anything is launched; a
+ *     call that returns an error has launched nothing and written nothing.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the legacy default
+ *     stream) and the call returns without waiting.  Calls are reentrant.
+ *   - The device current at call time must be a gfx950 GPU and must own the
+ *     pointers.
+ *   - M = 0 (or N = 0) is a valid no-op returning Q4_OK.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+typedef enum {
+    Q4_OK = 0,
+    Q4_ERR_NULL = 1,      /* a required pointer is NULL                       */
+    Q4_ERR_SHAPE = 2,     /* M < 0, K <= 0, K % 64 != 0, K > Q4_MAX_K, N < 0,
+                             N > Q4_MAX_N                                      */
+    Q4_ERR_ALIGN = 3,     /* a pointer breaks the alignment stated below      */
+    Q4_ERR_OVERLAP = 4,   /* an output range overlaps an input or another
+                             output range                                     */
+    Q4_ERR_DEVICE = 5     /* the HIP runtime refused the launch (no gfx950
+                             device current, bad stream, ...)                  */
+} q4_status;
+
+/* Largest K the kernels accept (a multiple of 64). */
+#define Q4_MAX_K 131072
+/* Largest token count of q4_gemm_smalln (LIVE_MAX_N of the deep-fold page). */
+#define Q4_MAX_N 32
+
+/* Flags OR-ed into q4_pack's device status word. */
+#define Q4_PACK_NONFINITE 1 /* some weight is NaN or infinite                  */
+#define Q4_PACK_OVERFLOW 2  /* some block's absmax rounds to fp16 infinity
+                               (|w| >= 65520)                                   */
+
+/* Bytes of the packed codes / scales of an M x K matrix (0 on bad shape). */
+size_t q4_codes_bytes(int64_t M, int64_t K);
+size_t q4_scales_bytes(int64_t M, int64_t K);
+
+/* Copy the 16 frozen codebook levels (fp32, ascending, level[0] = -1,
+ * level[7] = 0, level[15] = +1) into host memory `out`.  These are the
+ * NormalFloat-4 levels (QLoRA construction with an exact zero; the deep-fold
+ * page names the format NF4 and its 16-float table without printing it). */
+void q4_codebook(float out[16]);
+
+/* Human-readable name of a q4_status value. */
+const char *q4_status_string(int status);
+
+/*
+ * q4_pack -- quantise W (fp32, [M][K] row-major) into the packed format.
+ *   codes: q4_codes_bytes(M,K) bytes, 16-byte aligned.
+ *   scales: q4_scales_bytes(M,K) bytes, 2-byte aligned.
+ *   W: 16-byte aligned.
+ *   status: one int32 in device memory, 4-byte aligned.  It is cleared and
+ *     then receives the OR of Q4_PACK_* flags over all blocks.  A flagged
+ *     block's codes and scale are left unwritten; the rest are valid.
+ * Codes (reading of the unprinted step): the level nearest to w / scale in
+ * exact arithmetic, an exact midpoint taking the lower level; a block whose
+ * scale is 0 gets code 7 throughout.  The result is bit-exact: one answer.
+ * Ranges of W, codes, scales and status must not overlap.
+ */
+int q4_pack(const float *W, int64_t M, int64_t K, uint8_t *codes,
+            uint16_t *scales, int32_t *status, void *stream);
+
+/*
+ * q4_gemv -- y[m] = sum_k What[m,k] * x[k], m < M (the batch-1 decode
+ * projection).
+ *   codes/scales: a packed matrix (codes 16-byte aligned, scales 2-byte).
+ *   x: bf16 bit patterns [K], 16-byte aligned.
+ *   y: fp32 [M], 4-byte aligned; must not overlap codes, scales or x.
+ * Accuracy: |y - y_exact| <= 1e-3 * sum_k |What[m,k] x[k]| + 1e-5 for
+ * finite inputs with max|What| * max|x| below 1e4 (the fp16 rounding of the
+ * table costs at most 2^-11 relative per term; fp32 accumulation).
+ * Non-finite x propagate into y.
+ */
+int q4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+            const uint16_t *x, float *y, void *stream);
+
+/*
+ * q4_gemm_smalln -- Y[n][m] = sum_k What[m,k] * X[n][k], n < N <= 32, m < M
+ * (the prefill-chunk form; every weight is read once per call).
+ *   X: bf16 bit patterns [N][K] row-major, 16-byte aligned.
+ *   Y: fp32 [N][M] row-major, 4-byte aligned; must not overlap the inputs.
+ * Same accuracy statement as q4_gemv.
+ */
+int q4_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M,
+                   int64_t K, const uint16_t *X, int64_t N, float *Y,
+                   void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q4_H */

@@ -1,0 +1,150 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/q4.h declares, and refuses bad arguments on the host before any
+launch (golang.design accel/tensor conventions: validate everything first,
+refuse rather than clamp).  The pointers used here are never dereferenced:
+each call fails a host-side check first.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4.h")
+
+
+@pytest.fixture(scope="module")
+def q4():
+    import bit_weight_gemv_amd as q4
+    if not os.path.exists(q4.LIB_PATH):
+        from bit_weight_gemv_amd import build
+        build.build()
+    return q4
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("q4_pack", "q4_gemv", "q4_gemm_smalln", "q4_codebook", "q4_codes_bytes",
+              "q4_scales_bytes", "q4_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(q4):
+    L = q4.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), f"libq4.so does not export {name}"
+    assert set(_declared_functions()) == set(q4.EXPORTED)
+
+
+def test_codebook_is_the_oracles(q4, oracle_mod):
+    lib_levels = np.array(q4.codebook(), np.float32)
+    assert np.array_equal(lib_levels.view(np.uint32), oracle_mod.codebook_f32().view(np.uint32))
+
+
+def test_sizes(q4):
+    assert q4.codes_bytes(151936, 2048) == 151936 * 1024
+    assert q4.scales_bytes(151936, 2048) == 151936 * 32 * 2
+    assert q4.codes_bytes(3, 64) == 96 and q4.scales_bytes(3, 64) == 6
+    assert q4.codes_bytes(0, 64) == 0
+    assert q4.codes_bytes(4, 100) == 0 and q4.scales_bytes(-1, 64) == 0
+    assert q4.codes_bytes(1, q4.Q4_MAX_K + 64) == 0
+
+
+def test_status_strings(q4):
+    for s in range(6):
+        assert q4.status_string(s).startswith("Q4_")
+    assert "unknown" in q4.status_string(99)
+
+
+A = 0x10000000  # fake, aligned, never dereferenced
+B = 0x20000000
+C = 0x30000000
+D = 0x40000000
+
+
+def _gemv(q4, codes, scales, M, K, x, y):
+    return q4.lib().q4_gemv(codes, scales, M, K, x, y, None)
+
+
+def _gemm(q4, codes, scales, M, K, X, N, Y):
+    return q4.lib().q4_gemm_smalln(codes, scales, M, K, X, N, Y, None)
+
+
+def _pack(q4, W, M, K, codes, scales, status):
+    return q4.lib().q4_pack(W, M, K, codes, scales, status, None)
+
+
+def test_gemv_shape_errors(q4):
+    for M, K in [(-1, 64), (4, 0), (4, 63), (4, 100), (4, -64), (4, q4.Q4_MAX_K + 64), (1 << 60, 1024)]:
+        assert _gemv(q4, A, B, M, K, C, D) == q4.Q4_ERR_SHAPE, (M, K)
+
+
+def test_gemv_empty_is_noop(q4):
+    assert _gemv(q4, None, None, 0, 64, None, None) == q4.Q4_OK
+
+
+def test_gemv_null_and_alignment(q4):
+    M, K = 16, 128
+    assert _gemv(q4, None, B, M, K, C, D) == q4.Q4_ERR_NULL
+    assert _gemv(q4, A, None, M, K, C, D) == q4.Q4_ERR_NULL
+    assert _gemv(q4, A, B, M, K, None, D) == q4.Q4_ERR_NULL
+    assert _gemv(q4, A, B, M, K, C, None) == q4.Q4_ERR_NULL
+    assert _gemv(q4, A + 8, B, M, K, C, D) == q4.Q4_ERR_ALIGN
+    assert _gemv(q4, A, B + 1, M, K, C, D) == q4.Q4_ERR_ALIGN
+    assert _gemv(q4, A, B, M, K, C + 2, D) == q4.Q4_ERR_ALIGN
+    assert _gemv(q4, A, B, M, K, C, D + 2) == q4.Q4_ERR_ALIGN
+
+
+def test_gemv_overlap(q4):
+    M, K = 16, 128  # codes 1024 B, scales 64 B, x 256 B, y 64 B
+    assert _gemv(q4, A, B, M, K, C, A + 1020) == q4.Q4_ERR_OVERLAP   # y over codes tail
+    assert _gemv(q4, A, B, M, K, C, B) == q4.Q4_ERR_OVERLAP          # y on scales
+    assert _gemv(q4, A, B, M, K, C, C + 252) == q4.Q4_ERR_OVERLAP    # y over x tail
+    # every call here must fail a host check: a call that passed them all
+    # would launch on fake pointers
+    assert _gemv(q4, A, B, M, K, C + 2, A + 1024) == q4.Q4_ERR_ALIGN
+
+
+def test_gemm_shape_errors(q4):
+    assert _gemm(q4, A, B, 16, 128, C, 33, D) == q4.Q4_ERR_SHAPE
+    assert _gemm(q4, A, B, 16, 128, C, -1, D) == q4.Q4_ERR_SHAPE
+    assert _gemm(q4, A, B, 16, 96, C, 4, D) == q4.Q4_ERR_SHAPE
+    assert _gemm(q4, None, None, 16, 128, None, 0, None) == q4.Q4_OK
+    assert _gemm(q4, None, None, 0, 128, None, 5, None) == q4.Q4_OK
+
+
+def test_gemm_null_alignment_overlap(q4):
+    M, K, N = 16, 128, 4
+    assert _gemm(q4, A, B, M, K, None, N, D) == q4.Q4_ERR_NULL
+    assert _gemm(q4, A, B, M, K, C + 8, N, D) == q4.Q4_ERR_ALIGN
+    assert _gemm(q4, A, B, M, K, C, N, D + 1) == q4.Q4_ERR_ALIGN
+    assert _gemm(q4, A, B, M, K, C, N, C + 1020) == q4.Q4_ERR_OVERLAP  # Y over X's last word (X is 1 KB)
+
+
+def test_pack_errors(q4):
+    assert _pack(q4, A, 4, 100, B, C, D) == q4.Q4_ERR_SHAPE
+    assert _pack(q4, None, 4, 64, B, C, D) == q4.Q4_ERR_NULL
+    assert _pack(q4, A, 4, 64, B, C, None) == q4.Q4_ERR_NULL
+    assert _pack(q4, A + 4, 4, 64, B, C, D) == q4.Q4_ERR_ALIGN
+    assert _pack(q4, A, 4, 64, B + 8, C, D) == q4.Q4_ERR_ALIGN
+    assert _pack(q4, A, 4, 64, B, C + 1, D) == q4.Q4_ERR_ALIGN
+    assert _pack(q4, A, 4, 64, B, C, D + 2) == q4.Q4_ERR_ALIGN
+    assert _pack(q4, A, 4, 64, A + 512, C, D) == q4.Q4_ERR_OVERLAP  # codes inside W (1 KB)
+    assert _pack(q4, A, 4, 64, B, B + 64, D) == q4.Q4_ERR_OVERLAP   # scales inside codes
+    assert _pack(q4, A, 4, 64, B, C, C + 4) == q4.Q4_ERR_OVERLAP    # status inside scales
+
+
+def test_binding_refuses_without_library(tmp_path, monkeypatch):
+    import bit_weight_gemv_amd as q4
+    monkeypatch.setattr(q4, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(q4, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        q4.lib()

@@ -1,0 +1,388 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Acceptance (the bar of this library):
+  - q4_pack: codes and scale bits equal, bit for bit;
+  - q4_gemv / q4_gemm_smalln: |y - y_ref| <= 1e-3 * sum_k |What x| + 1e-5 per output;
+  - lm_head-shaped outputs: identical argmax (ties to the lowest index,
+    golang.design accel/tensor func Argmax).
+Inputs come from the seeded generators; the oracle never sees anything the
+GPU produced.  Without a GPU these tests SKIP; they never pass silently.
+"""
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import cases
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible: SKIP (not a pass)")
+    import bit_weight_gemv_amd as q4
+    q4.lib()  # raises if libq4.so is missing: no fallback exists
+    oracle.build(force=False)
+    return torch, q4, torch.device("cuda:0")
+
+
+def _gpu_pack(env, W):
+    torch, q4, dev = env
+    Wd = cases.to_dev(W, torch, dev)
+    codes, scales, status = q4.q4_pack(Wd)
+    torch.cuda.synchronize()
+    return codes, scales, int(status.item())
+
+
+def _upload_packed(env, codes, scales):
+    torch, q4, dev = env
+    c = cases.to_dev(codes, torch, dev)
+    s = cases.to_dev(scales.view(np.float16), torch, dev)
+    return c, s
+
+
+def _x_dev(env, x_bits):
+    torch, q4, dev = env
+    return cases.to_dev(x_bits.view(np.int16), torch, dev).view(torch.bfloat16)
+
+
+def _check(y_gpu, y_ref, S, what):
+    ok, ratio = oracle.within_tolerance(y_gpu, y_ref, S)
+    _log(f"{what}: worst |err|/bound = {ratio:.3g}")
+    assert ok, f"{what}: tolerance broken, worst ratio {ratio}"
+
+
+# ---------------------------------------------------------------------------
+# q4_pack
+# ---------------------------------------------------------------------------
+
+PACK_SHAPES = [(1, 64), (3, 128), (17, 192), (256, 512), (5, 4096), (33, 11008)]
+
+
+@pytest.mark.parametrize("M,K", PACK_SHAPES)
+def test_pack_bit_exact_random(env, M, K):
+    W = wl.weights(M, K, seed=100 + M + K)
+    c_ref, s_ref, st_ref = oracle.pack(W)
+    codes, scales, st = _gpu_pack(env, W)
+    assert st == st_ref == 0
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(cases.bits16(scales, env[0]), s_ref)
+
+
+def test_pack_bit_exact_edge_blocks(env):
+    W = cases.edge_matrix()
+    c_ref, s_ref, st_ref = oracle.pack(W)
+    codes, scales, st = _gpu_pack(env, W)
+    assert st == st_ref == 0
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(cases.bits16(scales, env[0]), s_ref)
+
+
+def test_pack_bit_exact_scaled_range(env):
+    # the same weights at many magnitudes, including fp16-subnormal scales
+    base = wl.weights(40, 256, seed=7)
+    W = np.concatenate([base * np.float32(2.0 ** j) for j in range(-30, 16, 3)]).astype(np.float32)
+    c_ref, s_ref, st_ref = oracle.pack(W)
+    codes, scales, st = _gpu_pack(env, W)
+    assert st == st_ref == 0
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(cases.bits16(scales, env[0]), s_ref)
+
+
+def test_pack_flags_and_valid_blocks(env):
+    W = wl.weights(8, 256, seed=3)
+    W[1, 70] = np.nan
+    W[2, 3] = np.inf
+    W[5, 200] = -70000.0
+    c_ref, s_ref, st_ref = oracle.pack(W)
+    codes, scales, st = _gpu_pack(env, W)
+    assert st == st_ref == (oracle.PACK_NONFINITE | oracle.PACK_OVERFLOW)
+    codes = codes.cpu().numpy()
+    scales = cases.bits16(scales, env[0])
+    good = np.ones((8, 4), bool)
+    good[1, 1] = good[2, 0] = good[5, 3] = False
+    for m in range(8):
+        for b in range(4):
+            if good[m, b]:
+                assert np.array_equal(codes[m, 32 * b:32 * b + 32], c_ref[m, 32 * b:32 * b + 32])
+                assert scales[m, b] == s_ref[m, b]
+    # a second clean call clears the word
+    _, _, st2 = _gpu_pack(env, wl.weights(8, 256, seed=3))
+    assert st2 == 0
+
+
+# ---------------------------------------------------------------------------
+# q4_gemv
+# ---------------------------------------------------------------------------
+
+# (M, K): several tiles and ragged tails for every launch shape:
+#   K <= 2048 (a wave per row), K <= 4096 (two chunks a lane),
+#   longer rows (a workgroup per row tile; 1, 2, 4, 8 chunks a lane).
+GEMV_SHAPES = [(1, 64), (2, 64), (7, 128), (257, 512), (1000, 1024), (4097, 2048), (31, 1984),
+               (300, 2112), (65, 4096), (129, 4160), (2048, 11008), (33, 11008), (9, 16384),
+               (5, 16448), (3, 32768), (2, 65536), (2, 131072)]
+
+
+@pytest.mark.parametrize("M,K", GEMV_SHAPES)
+def test_gemv_parity_shapes(env, M, K):
+    torch, q4, dev = env
+    seed = 1000 + M + K
+    W = wl.weights(M, K, seed)
+    x = wl.activation(K, seed, "normal")
+    codes, scales, st = oracle.pack(W)
+    assert st == 0
+    y_ref, S = oracle.gemv(codes, scales, M, K, x)
+    c, s = _upload_packed(env, codes, scales)
+    y = q4.q4_gemv(c, s, _x_dev(env, x))
+    torch.cuda.synchronize()
+    _check(y.cpu().numpy(), y_ref, S, f"gemv M={M} K={K}")
+
+
+def test_gemv_after_gpu_pack_matches_oracle_chain(env):
+    torch, q4, dev = env
+    M, K = 700, 2048
+    W = wl.weights(M, K, 5)
+    x = wl.activation(K, 5, "unit_rms")
+    c_ref, s_ref, _ = oracle.pack(W)
+    y_ref, S = oracle.gemv(c_ref, s_ref, M, K, x)
+    codes, scales, st = _gpu_pack(env, W)
+    y = q4.q4_gemv(codes, scales, _x_dev(env, x))
+    torch.cuda.synchronize()
+    _check(y.cpu().numpy(), y_ref, S, "pack+gemv")
+
+
+def _bf16_bits(v):
+    return wl.bf16_rne_bits(np.asarray(v, np.float64))
+
+
+@pytest.mark.parametrize("kind", ["huge", "tiny", "mixed", "zeros", "onehot", "fp16_edge"])
+def test_gemv_activation_ranges(env, kind):
+    torch, q4, dev = env
+    M, K = 130, 2048
+    W = wl.weights(M, K, 9)
+    codes, scales, _ = oracle.pack(W)
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal(K)
+    if kind == "huge":
+        v = z * 1e30
+    elif kind == "tiny":
+        v = z * 1e-30
+    elif kind == "mixed":
+        v = z * np.exp2(rng.integers(-60, 60, K))
+    elif kind == "zeros":
+        v = np.zeros(K)
+    elif kind == "onehot":
+        v = np.zeros(K)
+        v[777] = 1.0
+    else:  # values just above fp16 range and around its subnormals
+        v = np.where(rng.random(K) < 0.5, 70000.0, 3e-6) * np.sign(z)
+    x = _bf16_bits(v)
+    y_ref, S = oracle.gemv(codes, scales, M, K, x)
+    c, s = _upload_packed(env, codes, scales)
+    y = q4.q4_gemv(c, s, _x_dev(env, x))
+    torch.cuda.synchronize()
+    yg = y.cpu().numpy()
+    if kind in ("zeros",):
+        assert np.all(yg == 0)
+    _check(yg, y_ref, S, f"gemv x={kind}")
+
+
+def test_gemv_bit_exact_invariants(env):
+    torch, q4, dev = env
+    M, K = 1030, 2048
+    W = wl.weights(M, K, 12)
+    x = wl.activation(K, 12, "unit_rms")
+    codes, scales, _ = oracle.pack(W)
+    assert np.all(x & 0x7F80) and np.all(scales & 0x7C00)  # normal x and scales only
+    c, s = _upload_packed(env, codes, scales)
+    y = q4.q4_gemv(c, s, _x_dev(env, x)).cpu().numpy()
+    # x * 4 (bf16 exponent + 2): y * 4 exactly
+    x4 = (x.astype(np.uint32) + (2 << 7)).astype(np.uint16)
+    y4 = q4.q4_gemv(c, s, _x_dev(env, x4)).cpu().numpy()
+    assert np.array_equal(y4, 4 * y)
+    # scales * 2 (fp16 exponent + 1): y * 2 exactly
+    s2 = cases.to_dev((scales.astype(np.uint32) + (1 << 10)).astype(np.uint16).view(np.float16), torch, dev)
+    y2 = q4.q4_gemv(c, s2, _x_dev(env, x)).cpu().numpy()
+    assert np.array_equal(y2, 2 * y)
+    # a permutation of the rows permutes y exactly
+    perm = np.random.default_rng(0).permutation(M)
+    cp, sp = _upload_packed(env, codes[perm], scales[perm])
+    yp = q4.q4_gemv(cp, sp, _x_dev(env, x)).cpu().numpy()
+    assert np.array_equal(yp, y[perm])
+    # repeated calls are deterministic
+    assert np.array_equal(q4.q4_gemv(c, s, _x_dev(env, x)).cpu().numpy(), y)
+
+
+def test_gemv_no_allocation_growth(env):
+    torch, q4, dev = env
+    M, K = 4096, 2048
+    W = wl.weights(M, K, 13)
+    x = wl.activation(K, 13, "normal")
+    codes, scales, _ = oracle.pack(W)
+    c, s = _upload_packed(env, codes, scales)
+    xd = _x_dev(env, x)
+    y = torch.empty(M, dtype=torch.float32, device=dev)
+    q4.q4_gemv(c, s, xd, y)
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    for _ in range(32):
+        q4.q4_gemv(c, s, xd, y)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == before
+
+
+def test_gemv_on_side_stream(env):
+    torch, q4, dev = env
+    M, K = 512, 4096
+    W = wl.weights(M, K, 14)
+    x = wl.activation(K, 14, "normal")
+    codes, scales, _ = oracle.pack(W)
+    y_ref, S = oracle.gemv(codes, scales, M, K, x)
+    c, s = _upload_packed(env, codes, scales)
+    xd = _x_dev(env, x)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        y = torch.empty(M, dtype=torch.float32, device=dev)
+        q4.q4_gemv(c, s, xd, y, stream=st)
+    st.synchronize()
+    _check(y.cpu().numpy(), y_ref, S, "gemv side stream")
+
+
+def test_gemv_misaligned_device_pointer_refused(env):
+    torch, q4, dev = env
+    M, K = 8, 128
+    codes = torch.zeros(M * K // 2 + 16, dtype=torch.uint8, device=dev)
+    scales = torch.zeros((M, K // 64), dtype=torch.float16, device=dev)
+    x = torch.zeros(K, dtype=torch.bfloat16, device=dev)
+    bad = codes[8:8 + M * K // 2].view(M, K // 2)  # 8-byte offset
+    with pytest.raises(q4.Q4Error) as e:
+        q4.q4_gemv(bad, scales, x)
+    assert e.value.status == q4.Q4_ERR_ALIGN
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads (the shapes the benchmark times), sampled rows + argmax
+# ---------------------------------------------------------------------------
+
+_FULL = {}
+
+
+def _full_inputs(name):
+    if name not in _FULL:
+        c = wl.CONFIGS[name]
+        t = time.time()
+        W = wl.weights(c["M"], c["K"], c["seed"])
+        _log(f"{name}: generated W {c['M']}x{c['K']} in {time.time() - t:.1f}s")
+        t = time.time()
+        codes, scales, st = oracle.pack(W, threads=min(16, os.cpu_count() or 1))
+        _log(f"{name}: oracle pack in {time.time() - t:.1f}s")
+        assert st == 0
+        _FULL.clear()  # keep one full-size workload in memory at a time
+        _FULL[name] = (W, codes, scales)
+    return _FULL[name]
+
+
+def _sample_rows(M, n=1024, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([np.arange(min(64, M)), np.arange(max(0, M - 64), M),
+                                     rng.integers(0, M, n)]))
+    return rows
+
+
+@pytest.mark.parametrize("name", ["down", "gateup", "lm_head"])
+def test_full_size_pack_and_gemv(env, name):
+    torch, q4, dev = env
+    c = wl.CONFIGS[name]
+    M, K = c["M"], c["K"]
+    W, c_ref, s_ref = _full_inputs(name)
+    x = wl.activation(K, c["seed"], c["x"])
+    t = time.time()
+    codes, scales, st = _gpu_pack(env, W)
+    assert st == 0
+    assert np.array_equal(codes.cpu().numpy(), c_ref), "pack codes differ"
+    assert np.array_equal(cases.bits16(scales, torch), s_ref), "pack scales differ"
+    _log(f"{name}: GPU pack bit-exact ({time.time() - t:.1f}s incl. upload)")
+    y = q4.q4_gemv(codes, scales, _x_dev(env, x)).cpu().numpy()
+    rows = _sample_rows(M)
+    y_ref, S = oracle.gemv_row_list(c_ref, s_ref, M, K, x, rows)
+    _check(y[rows], y_ref, S, f"{name} sampled rows ({rows.size})")
+    if name == "lm_head":
+        t = time.time()
+        y_full, S_full = oracle.gemv(c_ref, s_ref, M, K, x, threads=min(16, os.cpu_count() or 1))
+        _log(f"lm_head: full oracle GEMV in {time.time() - t:.1f}s")
+        _check(y, y_full, S_full, "lm_head all rows")
+        a_ref = oracle.argmax(y_full)
+        a_gpu = oracle.argmax(y)
+        top = np.sort(y_full)[-2:]
+        _log(f"lm_head argmax gpu={a_gpu} oracle={a_ref} top-2 gap={top[1] - top[0]:.4g}")
+        assert a_gpu == a_ref
+
+
+# ---------------------------------------------------------------------------
+# q4_gemm_smalln
+# ---------------------------------------------------------------------------
+
+GEMM_SHAPES = [(1, 64, 1), (40, 128, 2), (100, 512, 3), (64, 2048, 4), (97, 1024, 8),
+               (33, 2048, 16), (200, 2048, 17), (65, 4096, 31), (160, 2048, 32), (70, 11008, 32)]
+
+
+@pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
+def test_gemm_smalln_parity(env, M, K, N):
+    torch, q4, dev = env
+    seed = 3000 + M + K + N
+    W = wl.weights(M, K, seed)
+    X = wl.activations(N, K, seed, "unit_rms")
+    codes, scales, _ = oracle.pack(W)
+    Y_ref, S = oracle.gemm(codes, scales, M, K, X)
+    c, s = _upload_packed(env, codes, scales)
+    Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+    Y = q4.q4_gemm_smalln(c, s, Xd)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, S, f"gemm M={M} K={K} N={N}")
+
+
+def test_gemm_rows_match_gemv(env):
+    torch, q4, dev = env
+    M, K, N = 300, 2048, 5
+    W = wl.weights(M, K, 41)
+    X = wl.activations(N, K, 41, "normal")
+    codes, scales, _ = oracle.pack(W)
+    c, s = _upload_packed(env, codes, scales)
+    Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+    Y = q4.q4_gemm_smalln(c, s, Xd).cpu().numpy()
+    for n in range(N):
+        y = q4.q4_gemv(c, s, Xd[n].contiguous()).cpu().numpy()
+        _, Sn = oracle.gemv(codes, scales, M, K, X[n])
+        assert np.all(np.abs(Y[n] - y) <= 2e-3 * Sn + 2e-5)
+
+
+def test_gemm_smalln_full_size_sampled(env):
+    torch, q4, dev = env
+    c = wl.CONFIGS["smalln"]
+    M, K, N = c["M"], c["K"], c["N"]
+    W = wl.weights(M, K, c["seed"])
+    X = wl.activations(N, K, c["seed"], c["x"])
+    codes, scales, st = _gpu_pack(env, W)
+    assert st == 0
+    Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+    c_ref, s_ref, _ = oracle.pack(W, threads=min(16, os.cpu_count() or 1))
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    for n_tok in (32, 16, 8, 4, 2, 1):
+        Y = q4.q4_gemm_smalln(codes, scales, Xd[:n_tok].contiguous()).cpu().numpy()
+        rows = _sample_rows(M, n=256, seed=n_tok)
+        for n in range(n_tok):
+            y_ref, S = oracle.gemv_row_list(c_ref, s_ref, M, K, X[n], rows)
+            _check(Y[n, rows], y_ref, S, f"smalln N={n_tok} token {n}")

@@ -19,6 +19,9 @@ silu(a) * b with a, b ~ N(0,1) (the input of a down projection).
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 _GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -93,15 +96,28 @@ def bf16_bits_to_f32(bits) -> np.ndarray:
     return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def weights(M: int, K: int, seed: int, std: float = 0.02) -> np.ndarray:
-    """W fp32 [M, K] ~ N(0, std^2)."""
+def weights(M: int, K: int, seed: int, std: float = 0.02, threads: int | None = None) -> np.ndarray:
+    """W fp32 [M, K] ~ N(0, std^2).  Chunks are independent (counter-based
+    stream), so they are drawn on several threads; the result does not depend
+    on the thread count."""
     W = np.empty((M, K), np.float32)
     flat = W.reshape(-1)
     n = M * K
     step = 1 << 20
-    for s in range(0, n, step):
+
+    def fill(s):
         e = min(n, s + step)
         flat[s:e] = (std * normal(seed, e - s, start=s)).astype(np.float32)
+
+    if threads is None:
+        threads = min(16, os.cpu_count() or 1)
+    starts = range(0, n, step)
+    if threads <= 1 or n <= step:
+        for s in starts:
+            fill(s)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill, starts))
     return W
 
 
