@@ -39,11 +39,42 @@ typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
-// fp16 bit pattern of level i (round to nearest even), built from the fp32
-// table.  Used only while filling lookup tables.
+// Raw buffer resource over `bytes` bytes at `base` (CDNA dword-3 format,
+// no swizzle, no stride).  Loads through it take a wave-uniform base in
+// SGPRs, a 32-bit per-lane offset and a uniform SGPR offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Cache-policy operand of buffer loads: non-temporal (streamed once).
+constexpr int kLoadNonTemporal = 2;
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Mark a wave-uniform 64-bit value as such (lives in SGPRs afterwards).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// fp16 bit pattern of level i (round to nearest even, folded at compile
+// time from the fp32 table).
+__host__ __device__ constexpr uint32_t level_f16_bits_c(int i) {
+    return (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)level_f32(i));
+}
+
+// The same for a wave-uniform index, as a chain of scalar selects between
+// literals: no memory access (a table load at kernel start would queue
+// behind the first weight loads).
 __device__ __forceinline__ uint32_t level_f16_bits(int i) {
-    _Float16 h = (_Float16)level_f32(i);
-    return (uint32_t)__builtin_bit_cast(unsigned short, h);
+    uint32_t v = level_f16_bits_c(0);
+#define Q4_LEVEL_SEL(k) v = (i == k) ? level_f16_bits_c(k) : v;
+    Q4_LEVEL_SEL(1) Q4_LEVEL_SEL(2) Q4_LEVEL_SEL(3) Q4_LEVEL_SEL(4) Q4_LEVEL_SEL(5)
+    Q4_LEVEL_SEL(6) Q4_LEVEL_SEL(7) Q4_LEVEL_SEL(8) Q4_LEVEL_SEL(9) Q4_LEVEL_SEL(10)
+    Q4_LEVEL_SEL(11) Q4_LEVEL_SEL(12) Q4_LEVEL_SEL(13) Q4_LEVEL_SEL(14) Q4_LEVEL_SEL(15)
+#undef Q4_LEVEL_SEL
+    return v;
 }
 
 // DPP row operations (gfx9 encodings).
@@ -56,6 +87,69 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
     return __builtin_bit_cast(
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float keep, float send) {
+    return keep + dpp_f<CTRL>(send);
+}
+
+// DPP row_ror:n (rotate right by n lanes within each row of 16).
+constexpr int dpp_row_ror(int n) { return 0x120 + n; }
+
+// v + the value of lane (i ^ 16) (ds_swizzle bit mode: and 0x1f, xor 0x10).
+__device__ __forceinline__ float add_xor16(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+
+// v + the value of lane (i ^ 32) (ds_bpermute through __shfl_xor).
+__device__ __forceinline__ float add_xor32(float v) { return v + __shfl_xor(v, 32); }
+
+template <int L>
+__device__ __forceinline__ float ror_pow2(float v) {
+    if constexpr (L == 0) return dpp_f<dpp_row_ror(1)>(v);
+    else if constexpr (L == 1) return dpp_f<dpp_row_ror(2)>(v);
+    else if constexpr (L == 2) return dpp_f<dpp_row_ror(4)>(v);
+    else return dpp_f<dpp_row_ror(8)>(v);
+}
+
+// One pairing level of reduce_rows: rows 2j and 2j+1 become row j.  Lane i
+// receives from lane i - 2^L (DPP row_ror, same lower bits, opposite bit L);
+// a lane whose bit L is 0 keeps the sum of row 2j, otherwise of row 2j+1.
+template <int L, int N>
+__device__ __forceinline__ void pair_level(float (&v)[N], bool hi) {
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+        const float even = v[2 * j] + ror_pow2<L>(v[2 * j]);
+        const float odd = v[2 * j + 1] + ror_pow2<L>(v[2 * j + 1]);
+        v[j] = hi ? odd : even;
+    }
+}
+
+// Reduce NR per-lane values (one per row) over the 64 lanes of a wave.  On
+// return lane i holds the total of row i % NR.  log2(NR) pairing levels
+// (three VALU operations per pair) leave each lane one row; lanes with equal
+// i % NR are then summed (DPP row_ror within rows of 16, ds_swizzle across
+// 16, ds_bpermute across 32).  NR = 16 costs about 50 VALU operations for 16
+// rows instead of 16 full wave reductions.
+template <int NR>
+__device__ __forceinline__ float reduce_rows(const float (&a)[NR]) {
+    static_assert(NR == 1 || NR == 2 || NR == 4 || NR == 8 || NR == 16, "NR must be a power of two <= 16");
+    const unsigned lane = __lane_id();
+    float v[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) v[r] = a[r];
+    if constexpr (NR >= 2) pair_level<0, NR>(v, lane & 1u);
+    if constexpr (NR >= 4) pair_level<1, NR>(v, (lane >> 1) & 1u);
+    if constexpr (NR >= 8) pair_level<2, NR>(v, (lane >> 2) & 1u);
+    if constexpr (NR >= 16) pair_level<3, NR>(v, (lane >> 3) & 1u);
+    float t = v[0];
+    if constexpr (NR <= 1) t += dpp_f<dpp_row_ror(1)>(t);
+    if constexpr (NR <= 2) t += dpp_f<dpp_row_ror(2)>(t);
+    if constexpr (NR <= 4) t += dpp_f<dpp_row_ror(4)>(t);
+    if constexpr (NR <= 8) t += dpp_f<dpp_row_ror(8)>(t);
+    t = add_xor16(t);
+    return add_xor32(t);
 }
 
 // Sum over the 64 lanes of a wave; every lane gets the total.

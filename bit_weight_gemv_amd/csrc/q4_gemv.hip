@@ -27,7 +27,7 @@
 //  * Scale.  The dot over a 32-weight chunk is multiplied by its block
 //    scale once (fp32 FMA).
 //  * Reduction.  DPP row ops + ds_swizzle + readlane inside the wave; an LDS
-//    exchange across the waves of a workgroup when one row spans several
+//xchange across the waves of a workgroup when one row spans several
 //    waves (long K).
 //  * Schedule.  Rows are split into contiguous ranges, one per lane group
 //    (a wave, or a whole workgroup for long K); a group walks its range NR
@@ -45,17 +45,24 @@ constexpr int kLutCopies = 64;
 constexpr int kLutDwords = 256 * kLutCopies;  // 64 KB
 constexpr int kMaxWavesPerGroup = 8;
 
-// Dword i of the table holds entry i / 64 (a code byte) for lane slot
-// i % 64.  A wave writes 64 consecutive dwords of one entry, so the entry
-// index is wave-uniform.
+// Dword e * 64 + l of the table holds entry e (a code byte) for lane slot l.
+// Lane i of every wave computes the fp16 level i % 16 once (vector selects
+// between literals, no memory access); each wave then writes whole entries
+// (64 consecutive dwords, conflict-free), taking the two halves of an entry
+// from those lanes with v_readlane.
 __device__ __forceinline__ void fill_lut(uint32_t *lut) {
-    for (int i = threadIdx.x; i < kLutDwords; i += blockDim.x) {
-        const int e = __builtin_amdgcn_readfirstlane(i >> 6);
-        lut[i] = level_f16_bits(e & 15) | (level_f16_bits(e >> 4) << 16);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = blockDim.x >> 6;
+    const uint32_t mine = level_f16_bits(lane & 15);
+    for (int e = wave; e < 256; e += nw) {
+        const uint32_t lo = __builtin_amdgcn_readlane(mine, e & 15);
+        const uint32_t hi = __builtin_amdgcn_readlane(mine, e >> 4);
+        lut[e * 64 + lane] = lo | (hi << 16);
     }
 }
 
-// Table value for byte `b` (0..3) of a code word.
+// Table value for byte `B` (0..3) of a code word.
 template <int B>
 __device__ __forceinline__ half2_t lut_pair(const uint32_t *lut, uint32_t word, uint32_t laneoff) {
     constexpr uint32_t sel = 0x0C0C0000u | ((4u + B) << 8);  // [laneoff, byte B, 0, 0]
@@ -65,117 +72,187 @@ __device__ __forceinline__ half2_t lut_pair(const uint32_t *lut, uint32_t word, 
 }
 
 // Dot of one 16-byte chunk (32 weights) with the lane's fp16 activations.
+// All 16 lookups are issued before the first product so their LDS latencies
+// overlap.
 __device__ __forceinline__ float chunk_dot(const uint32_t *lut, uint4 q, const half2_t *xh,
                                            uint32_t laneoff) {
-    float p = 0.0f;
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    half2_t v[16];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        p = __builtin_amdgcn_fdot2(lut_pair<0>(lut, w[d], laneoff), xh[4 * d + 0], p, false);
-        p = __builtin_amdgcn_fdot2(lut_pair<1>(lut, w[d], laneoff), xh[4 * d + 1], p, false);
-        p = __builtin_amdgcn_fdot2(lut_pair<2>(lut, w[d], laneoff), xh[4 * d + 2], p, false);
-        p = __builtin_amdgcn_fdot2(lut_pair<3>(lut, w[d], laneoff), xh[4 * d + 3], p, false);
+        v[4 * d + 0] = lut_pair<0>(lut, w[d], laneoff);
+        v[4 * d + 1] = lut_pair<1>(lut, w[d], laneoff);
+        v[4 * d + 2] = lut_pair<2>(lut, w[d], laneoff);
+        v[4 * d + 3] = lut_pair<3>(lut, w[d], laneoff);
     }
+    float p = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) p = __builtin_amdgcn_fdot2(v[j], xh[j], p, false);
     return p;
 }
 
-// Load the lane's activation chunks and convert them to fp16 scaled by a
-// power of two; returns the inverse scale.
+// Load the lane's activation chunks and convert them to fp16, scaled by a
+// wave-uniform power of two chosen from the wave's largest bf16 magnitude so
+// that no value can overflow fp16.  Returns the inverse scale (exact).  With
+// several chunks per lane the maximum is taken in a first pass and the
+// chunks are re-read (from cache) for the conversion, so the raw and the
+// converted copies are never live together.
+__device__ __forceinline__ void load_chunk_x(const uint16_t *__restrict__ x, int c, bool valid,
+                                             uint32_t (&raw)[16]) {
+    if (valid) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(x + (int64_t)c * kChunkWeights);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const uint4 t = src[v];
+            raw[4 * v + 0] = t.x;
+            raw[4 * v + 1] = t.y;
+            raw[4 * v + 2] = t.z;
+            raw[4 * v + 3] = t.w;
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) raw[v] = 0;
+    }
+}
+
+__device__ __forceinline__ void convert_chunk_x(const uint32_t (&raw)[16], float up, half2_t (&xh)[16]) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const float lo = __builtin_bit_cast(float, raw[v] << 16);
+        const float hi = __builtin_bit_cast(float, raw[v] & 0xFFFF0000u);
+        half2_t h;
+        h.x = (_Float16)(lo * up);
+        h.y = (_Float16)(hi * up);
+        xh[v] = h;
+    }
+}
+
 template <int CPL>
 __device__ __forceinline__ float load_x(const uint16_t *__restrict__ x, const int (&cidx)[CPL],
                                         const bool (&cvalid)[CPL], half2_t (&xh)[CPL][16]) {
-    uint32_t raw[CPL][16];
     u16x2_t mx = {0, 0};
+    uint32_t raw[16];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        if (cvalid[i]) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(x + (int64_t)cidx[i] * kChunkWeights);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint4 t = src[v];
-                raw[i][4 * v + 0] = t.x;
-                raw[i][4 * v + 1] = t.y;
-                raw[i][4 * v + 2] = t.z;
-                raw[i][4 * v + 3] = t.w;
-            }
-        } else {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) raw[i][v] = 0;
-        }
+        load_chunk_x(x, cidx[i], cvalid[i], raw);
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, raw[i][v] & 0x7FFF7FFFu));
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, raw[v] & 0x7FFF7FFFu));
+        if (CPL == 1) break;
     }
-    // Largest bf16 magnitude -> its biased exponent E; scale by 2^(141-E) so
-    // the largest value lands in [2^14, 2^15), inside fp16's range.
-    int E = (int)((mx.x > mx.y ? mx.x : mx.y) >> 7);
+    // Largest bf16 magnitude bits of the wave (integer max: bf16 magnitudes
+    // order like their bit patterns).
+    int m = (int)(mx.x > mx.y ? mx.x : mx.y);
+    m = __builtin_amdgcn_readfirstlane(__reduce_max_sync(~0ull, m));
+    // Its biased exponent E; scale by 2^(141-E) so the largest value lands in
+    // [2^14, 2^15), inside fp16's range.
+    int E = m >> 7;
     if (E < 1) E = 1;
     int e = 141 - E;
     e = e > 126 ? 126 : (e < -126 ? -126 : e);
     const float up = exp2i(e);
 #pragma unroll
-    for (int i = 0; i < CPL; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float lo = __builtin_bit_cast(float, raw[i][v] << 16);
-            const float hi = __builtin_bit_cast(float, raw[i][v] & 0xFFFF0000u);
-            half2_t h;
-            h.x = (_Float16)(lo * up);
-            h.y = (_Float16)(hi * up);
-            xh[i][v] = h;
-        }
+    for (int i = 0; i < CPL; ++i) {
+        if (CPL > 1) load_chunk_x(x, cidx[i], cvalid[i], raw);
+        convert_chunk_x(raw, up, xh[i]);
+    }
     return exp2i(-e);
 }
 
-template <int NR, int CPL>
-__global__ __launch_bounds__(512) void gemv_kernel(const uint8_t *__restrict__ codes,
+// One lane group (P lanes: a wave, or a whole workgroup for long rows) owns
+// a contiguous range of rows and walks it NR rows (a tile) at a time.  Tiles
+// t+1 .. t+S are in flight while tile t is consumed: buffer s of the ring
+// holds tile t0+s and is reloaded with tile t0+s+S+1 once it is consumed.
+// Register budget: one chunk per lane keeps 4 waves per SIMD (128 VGPRs);
+// longer rows trade occupancy for the extra activation registers.  Groups
+// spanning several waves use workgroups of at most 512 lanes.
+constexpr int gemv_min_waves(int cpl) { return cpl == 1 ? 4 : 2; }
+constexpr int gemv_max_block(bool multi, int cpl) { return (multi || cpl > 1) ? 512 : 1024; }
+
+template <int NR, int CPL, int S, int RG, bool MULTI>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
+                          amdgpu_waves_per_eu(gemv_min_waves(CPL), 8))) void gemv_kernel(const uint8_t *__restrict__ codes,
                                                    const uint16_t *__restrict__ scales, int64_t M,
                                                    int K, const uint16_t *__restrict__ x,
                                                    float *__restrict__ y, int P) {
     __shared__ uint32_t lut[kLutDwords];
-    __shared__ float red[kMaxWavesPerGroup][NR];
+    __shared__ float red[kMaxWavesPerGroup][RG];
 
-    const int C = K >> 5;        // 16-byte chunks per row
-    const int nsb = K >> 6;      // scale blocks per row
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wpg = MULTI ? (P >> 6) : 1;      // waves per group
+    const int G = (int)(blockDim.x >> 6) / wpg;  // groups per workgroup
+    const int wig = wave % wpg;                // wave within its group
+    const int lig = wig * 64 + lane;           // lane within its group
+    const int C = K >> 5;                      // 16-byte chunks per row
+    const int nsb = K >> 6;                    // scale blocks per row
     const int64_t row_bytes = K >> 1;
-    const int G = blockDim.x / P;  // lane groups per workgroup
-    const int lig = threadIdx.x % P;
     const int64_t ngroups = (int64_t)gridDim.x * G;
-    const int64_t gid = (int64_t)blockIdx.x * G + threadIdx.x / P;
-    const int64_t r_begin = gid * M / ngroups;
-    const int64_t r_end = (gid + 1) * M / ngroups;
+    const int64_t gid = (int64_t)blockIdx.x * G + wave / wpg;
+    // 64-bit division runs on the VALU; the results are wave-uniform, so move
+    // them back to SGPRs and keep all row addressing scalar.
+    const int64_t r_begin = uniform64(gid * M / ngroups);
+    const int64_t r_end = uniform64((gid + 1) * M / ngroups);
+    const int64_t ntiles = uniform64((r_end - r_begin + NR - 1) / NR);
 
+    // Chunk indices of this lane.  Lanes past the row's end load a valid
+    // chunk (the last one) and multiply it by zero activations, so every load
+    // is unconditional.
     int cidx[CPL];
     bool cvalid[CPL];
+    uint32_t coff[CPL];  // byte offset of the lane's chunk in a row
+    uint32_t soff[CPL];  // element offset of its scale in a row
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         cidx[i] = lig + i * P;
         cvalid[i] = cidx[i] < C;
+        const int c = cvalid[i] ? cidx[i] : C - 1;
+        coff[i] = (uint32_t)c * 16u;
+        soff[i] = (uint32_t)c >> 1;
     }
 
-    uint4 q[NR][CPL];
-    uint32_t sc[NR][CPL];
-    auto load_tile = [&](int64_t r0) {
+    uint4 q[S + 1][NR][CPL];
+    uint32_t sc[S + 1][NR][CPL];
+    // Tiles are loaded in order.  The next tile to load starts at row
+    // r_begin + NR * (tiles loaded so far); its pointers advance by one tile
+    // per load.  Rows past r_end repeat the last valid row (their results are
+    // not stored), so every access stays inside the matrix.  A tile past the
+    // last one is loaded through a buffer resource of zero records: the loads
+    // stay unconditional (no register merges in the ring) but return zeros
+    // without touching memory.
+    const uint8_t *next_codes = codes + r_begin * row_bytes;
+    const uint16_t *next_scales = scales + r_begin * nsb;
+    int64_t next_left = r_end - r_begin;  // rows from the next tile to r_end
+    auto load_tile = [&](int buf) {
+        const bool real = next_left > 0;
+        const int nvalid = next_left < NR ? (int)next_left : NR;
+        const __amdgpu_buffer_rsrc_t crs =
+            buffer_rsrc(next_codes, real ? (uint32_t)(NR * row_bytes) : 0u);
+        const __amdgpu_buffer_rsrc_t srs =
+            buffer_rsrc(next_scales, real ? (uint32_t)(NR * nsb * 2) : 0u);
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const int64_t row = (r0 + r < r_end) ? r0 + r : r_end - 1;
-            const uint8_t *crow = codes + row * row_bytes;
-            const uint16_t *srow = scales + row * nsb;
+            const int rr = r < nvalid ? r : (nvalid > 0 ? nvalid - 1 : 0);
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
-                if (cvalid[i]) {
-                    q[r][i] = *reinterpret_cast<const uint4 *>(crow + (int64_t)cidx[i] * 16);
-                    sc[r][i] = srow[cidx[i] >> 1];
-                } else {
-                    q[r][i] = make_uint4(0, 0, 0, 0);
-                    sc[r][i] = 0;
-                }
+                // Weights are read once: non-temporal loads keep them from
+                // displacing reusable lines.
+                const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+                    crs, (int)coff[i], (int)(rr * row_bytes), kLoadNonTemporal);
+                q[buf][r][i] = make_uint4(v.x, v.y, v.z, v.w);
+                sc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(srs, (int)(soff[i] * 2),
+                                                                      rr * nsb * 2, kLoadNonTemporal);
             }
         }
+        next_codes += NR * row_bytes;
+        next_scales += NR * nsb;
+        next_left -= NR;
     };
 
-    const bool has_rows = r_begin < r_end;
-    if (has_rows) load_tile(r_begin);  // first tile in flight during set-up
+    if (ntiles > 0) {  // first tiles in flight during set-up
+#pragma unroll
+        for (int s = 0; s <= S; ++s) load_tile(s);
+    }
 
     half2_t xh[CPL][16];
     const float down = load_x<CPL>(x, cidx, cvalid, xh);
@@ -183,48 +260,51 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t *__restrict__ c
     fill_lut(lut);
     __syncthreads();
 
-    const uint32_t laneoff = (lane_id() & 63u) << 2;
-    const int wave = lig >> 6;
-    const int nwaves = P >> 6;
+    const uint32_t laneoff = (uint32_t)lane << 2;
 
-    for (int64_t r0 = r_begin; r0 < r_end; r0 += NR) {
-        uint4 qc[NR][CPL];
-        uint32_t scc[NR][CPL];
+    // Rows are reduced across the wave RG at a time (RG/NR tiles): the fixed
+    // cost of the cross-lane reduction and of the store is paid once per RG
+    // rows.  Ring step: accumulate tile t from buffer `buf` into rows
+    // [j*NR, j*NR+NR) of the group (if t exists), then refill the buffer
+    // with tile t + S + 1 (unconditionally; past the end it reads nothing).
+    constexpr int TPG = RG / NR;  // tiles per reduction group
+    static_assert(RG % NR == 0 && TPG % (S + 1) == 0, "group must hold whole ring turns");
+    float acc[RG];
+    auto step = [&](int buf, int j, int64_t t) {
+        if (t < ntiles) {
 #pragma unroll
-        for (int r = 0; r < NR; ++r)
+            for (int r = 0; r < NR; ++r) {
+                float a = 0.0f;
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                qc[r][i] = q[r][i];
-                scc[r][i] = sc[r][i];
+                for (int i = 0; i < CPL; ++i) {
+                    const float p = chunk_dot(lut, q[buf][r][i], xh[i], laneoff);
+                    a = fmaf(p, f16_bits_to_f32(sc[buf][r][i]), a);
+                }
+                acc[j * NR + r] = a;
             }
-        if (r0 + NR < r_end) load_tile(r0 + NR);  // prefetch the next tile
-
-        float acc[NR];
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            acc[r] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const float p = chunk_dot(lut, qc[r][i], xh[i], laneoff);
-                acc[r] = fmaf(p, f16_bits_to_f32(scc[r][i]), acc[r]);
-            }
-            acc[r] = wave_sum(acc[r] * down);
-        }
-
-        if (nwaves == 1) {
-#pragma unroll
-            for (int r = 0; r < NR; ++r)
-                if (lig == r && r0 + r < r_end) y[r0 + r] = acc[r];
         } else {
-            if ((lig & 63) == 0) {
 #pragma unroll
-                for (int r = 0; r < NR; ++r) red[wave][r] = acc[r];
-            }
+            for (int r = 0; r < NR; ++r) acc[j * NR + r] = 0.0f;
+        }
+        load_tile(buf);  // tile t + S + 1
+    };
+
+    const int64_t nrows = r_end - r_begin;
+    for (int64_t g0 = 0; g0 < ntiles; g0 += TPG) {
+#pragma unroll
+        for (int j = 0; j < TPG; ++j) step(j % (S + 1), j, g0 + j);
+        // Lane l now holds the wave's total of group row (l % RG).
+        const float tot = reduce_rows<RG>(acc) * down;
+        const int64_t local = g0 * NR + lane;  // row index within the range
+        if (!MULTI) {
+            if (lane < RG && local < nrows) y[r_begin + local] = tot;
+        } else {
+            if (lane < RG) red[wig][lane] = tot;
             __syncthreads();
-            if (lig < NR && r0 + lig < r_end) {
-                float s = 0.0f;
-                for (int w = 0; w < nwaves; ++w) s += red[w][lig];
-                y[r0 + lig] = s;
+            if (wig == 0 && lane < RG && local < nrows) {
+                float sum = 0.0f;
+                for (int w = 0; w < wpg; ++w) sum += red[w][lane];
+                y[r_begin + local] = sum;
             }
             __syncthreads();
         }
@@ -246,7 +326,7 @@ int cu_count() {
     return cached[dev];
 }
 
-template <int NR, int CPL>
+template <int NR, int CPL, int S, int RG, bool MULTI>
 hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, int64_t M, int K,
                           const uint16_t *x, float *y, int P, int G, hipStream_t stream) {
     // Two workgroups fit a CU (64 KB of LDS each); one pass over the grid.
@@ -256,7 +336,7 @@ hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, int64_t 
     if (grid > max_wg) grid = max_wg;
     if (grid < 1) grid = 1;
     void *args[] = {&codes, &scales, &M, &K, &x, &y, &P};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_kernel<NR, CPL>), dim3((unsigned)grid),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_kernel<NR, CPL, S, RG, MULTI>), dim3((unsigned)grid),
                            dim3((unsigned)(P * G)), args, 0, stream);
 }
 
@@ -267,19 +347,19 @@ hipError_t launch_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, 
     const int C = (int)(K / kChunkWeights);
     const int k = (int)K;
     if (C <= 64)  // one wave covers a row: 8 independent waves per workgroup
-        return launch_variant<4, 1>(codes, scales, M, k, x, y, 64, 8, stream);
+        return launch_variant<4, 1, 1, 8, false>(codes, scales, M, k, x, y, 64, 8, stream);
     if (C <= 128)
-        return launch_variant<4, 2>(codes, scales, M, k, x, y, 64, 8, stream);
+        return launch_variant<2, 2, 1, 16, false>(codes, scales, M, k, x, y, 64, 8, stream);
     // Long rows: the whole workgroup (up to 8 waves) shares a row tile.
     int cpl = 1;
     while (C > cpl * 64 * kMaxWavesPerGroup) cpl *= 2;
     const int waves = (C + cpl * 64 - 1) / (cpl * 64);
     const int P = waves * 64;
     switch (cpl) {
-        case 1: return launch_variant<4, 1>(codes, scales, M, k, x, y, P, 1, stream);
-        case 2: return launch_variant<4, 2>(codes, scales, M, k, x, y, P, 1, stream);
-        case 4: return launch_variant<2, 4>(codes, scales, M, k, x, y, P, 1, stream);
-        default: return launch_variant<1, 8>(codes, scales, M, k, x, y, P, 1, stream);
+        case 1: return launch_variant<4, 1, 1, 8, true>(codes, scales, M, k, x, y, P, 1, stream);
+        case 2: return launch_variant<4, 2, 1, 8, true>(codes, scales, M, k, x, y, P, 1, stream);
+        case 4: return launch_variant<2, 4, 1, 4, true>(codes, scales, M, k, x, y, P, 1, stream);
+        default: return launch_variant<1, 8, 0, 2, true>(codes, scales, M, k, x, y, P, 1, stream);
     }
 }
 

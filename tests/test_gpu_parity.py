@@ -216,11 +216,13 @@ def test_gemv_bit_exact_invariants(env):
     s2 = cases.to_dev((scales.astype(np.uint32) + (1 << 10)).astype(np.uint16).view(np.float16), torch, dev)
     y2 = q4.q4_gemv(c, s2, _x_dev(env, x)).cpu().numpy()
     assert np.array_equal(y2, 2 * y)
-    # a permutation of the rows permutes y exactly
+    # a permutation of the rows permutes y (to the acceptance bound: a row's
+    # fp32 summation order depends on its slot in a row tile)
     perm = np.random.default_rng(0).permutation(M)
     cp, sp = _upload_packed(env, codes[perm], scales[perm])
     yp = q4.q4_gemv(cp, sp, _x_dev(env, x)).cpu().numpy()
-    assert np.array_equal(yp, y[perm])
+    _, S = oracle.gemv(codes, scales, M, K, x)
+    assert np.all(np.abs(yp - y[perm]) <= 2e-3 * S[perm] + 2e-5)
     # repeated calls are deterministic
     assert np.array_equal(q4.q4_gemv(c, s, _x_dev(env, x)).cpu().numpy(), y)
 
