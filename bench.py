@@ -6,7 +6,9 @@ A step is one q4_gemv call on the lm_head workload (M x K = 151936 x 2048,
 x bf16 unit-RMS, y fp32): the projection the metric is quoted on.  Inputs are
 resident in HBM before timing starts.  Each step reads a different one of R
 packed copies of the matrix, so that the 256 MB Infinity Cache and the L2
-cannot serve the weights (R * 166 MB >= 600 MB).
+cannot serve the weights (R * 166 MB >= 600 MB).  The K timed steps are
+captured in one HIP graph (as a decode step is) and replayed between two
+events on the replay stream; --eager adds the same calls launched one by one.
 
 Byte model (deep-fold "Decode V2", section 6 bench: GB/s = packed + scale +
 x over the median time; the y write is added here):
@@ -32,6 +34,35 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+COPY_PROBE_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_lm_head_hbm_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_weight_gemv_amd", "csrc", f) for f in ("q4_gemv.hip", "q4_device.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per lm_head GEMV call from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        return int(float(kv["hbm_bytes_per_call"]))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def log(msg):
@@ -91,30 +122,35 @@ def time_calls(torch, fn, reps, steps, warmup):
     return wall_ms, start.elapsed_time(end) / steps
 
 
-def time_graph(torch, fn, reps, steps):
-    """The same `steps` calls captured once in a HIP graph and replayed:
-    the host issues one launch, so the average per call is device time plus
-    the dispatch gap between consecutive kernels."""
+def time_graph(torch, fn, reps, steps, warmup):
+    """The timed region: `steps` calls (rotating over the copies) captured once
+    in a HIP graph and replayed, bracketed by two events on the replay stream
+    and by host synchronisation.  Warm-up replays the same graph until at
+    least `warmup` calls have run.  Returns (event ms per call, wall ms per
+    call)."""
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        fn(*reps[0])  # warm the stream before capture
+        fn(*reps[0])  # initialise the stream before capture
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=s):
             for i in range(steps):
                 fn(*reps[i % len(reps)])
-    torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    g.replay()
-    end.record()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        for _ in range(max(1, -(-warmup // steps))):
+            g.replay()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(s)
+        g.replay()
+        end.record(s)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ms = start.elapsed_time(end) / steps
     del g
-    return ms
+    return ms, wall_ms
 
 
 def cpu_baseline(oracle, wl, W, xb, name):
@@ -153,7 +189,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="also time the calls launched one by one from Python")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run 3 plain 256 MiB device copies first (calibrates rocprofv3 "
+                         "FETCH_SIZE/WRITE_SIZE against a copy of known size)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -172,6 +213,15 @@ def main():
     dev = torch.device("cuda:0")
     q4.lib()
 
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy probe: 3 x {COPY_PROBE_BYTES} B device copies")
+
     name = "lm_head"
     c = wl.CONFIGS[name]
     M, K = c["M"], c["K"]
@@ -181,13 +231,16 @@ def main():
     def step(codes, scales):
         q4.q4_gemv(codes, scales, x, y)
 
-    wall_ms, k_mean_ms = time_calls(torch, step, reps, args.steps, args.warmup)
-    g_ms = time_graph(torch, step, reps, args.steps)
+    k_mean_ms, wall_ms = time_graph(torch, step, reps, args.steps, args.warmup)
+    eager = None
+    if args.eager:
+        e_wall, e_ms = time_calls(torch, step, reps, args.steps, args.warmup)
+        eager = {"us_per_call_events": round(e_ms * 1e3, 3), "us_per_step_wall": round(e_wall * 1e3, 3)}
     nbytes = gemv_bytes(M, K)
     value = nbytes / (wall_ms * 1e-3) / 1e9
     achieved = nbytes / (k_mean_ms * 1e-3) / 1e9
-    log(f"lm_head: wall {wall_ms * 1e3:.2f} us/step, events {k_mean_ms * 1e3:.2f} us/call, "
-        f"graph {g_ms * 1e3:.2f} us/call, {achieved:.0f} GB/s")
+    log(f"lm_head: {k_mean_ms * 1e3:.2f} us/call (events), {wall_ms * 1e3:.2f} us/step (wall), "
+        f"{achieved:.0f} GB/s" + (f"; eager {eager}" if eager else ""))
 
     # y of the last call for the argmax check against the oracle
     q4.q4_gemv(reps[0][0], reps[0][1], x, y)
@@ -212,20 +265,17 @@ def main():
                 def sstep(cd, sl, sx=sx, sy=sy):
                     q4.q4_gemm_smalln(cd, sl, sx, sy)
                 N = ntok
-            sw, skm = time_calls(torch, sstep, sreps, args.steps, args.warmup)
-            sg = time_graph(torch, sstep, sreps, args.steps)
+            sg, sw = time_graph(torch, sstep, sreps, args.steps, args.warmup)
             sb = gemv_bytes(sc["M"], sc["K"], N)
             secondary.append({
                 "workload": f"{sname} {sc['M']}x{sc['K']} N={N}",
-                "us_per_call_graph": round(sg * 1e3, 3),
-                "us_per_call_events": round(skm * 1e3, 3),
+                "us_per_call": round(sg * 1e3, 3),
                 "us_per_step_wall": round(sw * 1e3, 3),
                 "achieved_GBs": round(sb / (sg * 1e-3) / 1e9, 1),
                 "frac_of_hbm_peak": round(sb / (sg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "bytes": sb,
             })
-            log(f"{sname}: graph {sg * 1e3:.2f} us/call, events {skm * 1e3:.2f} us/call, "
-                f"{sb / (sg * 1e-3) / 1e9:.0f} GB/s")
+            log(f"{sname}: {sg * 1e3:.2f} us/call, {sb / (sg * 1e-3) / 1e9:.0f} GB/s")
             del sreps, sx, sy
             torch.cuda.empty_cache()
 
@@ -247,9 +297,11 @@ def main():
         "config": {"workload": "lm_head GEMV 151936x2048, N=1", "M": M, "K": K, "N": 1,
                    "copies_rotated": args.copies, "bytes_per_call": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "q4::gemv_kernel<4,1,1,8,false>", "kernel_us_events": round(k_mean_ms * 1e3, 3),
-                     "kernel_us_graph": round(g_ms * 1e3, 3)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "kernel": "q4::gemv_kernel<4,1,1,8,false>",
+                     "kernel_us": round(k_mean_ms * 1e3, 3),
+                     "timing": "HIP graph of the timed calls, events on the replay stream"},
+        "eager": eager,
         "secondary": secondary,
     }
     if not args.no_cpu_baseline:

@@ -388,3 +388,41 @@ def test_gemm_smalln_full_size_sampled(env):
         for n in range(n_tok):
             y_ref, S = oracle.gemv_row_list(c_ref, s_ref, M, K, X[n], rows)
             _check(Y[n, rows], y_ref, S, f"smalln N={n_tok} token {n}")
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture (a decode step is captured once and replayed)
+# ---------------------------------------------------------------------------
+
+def test_graph_capture_replays_match_eager(env):
+    torch, q4, dev = env
+    M, K, N = 3000, 2048, 8
+    W = wl.weights(M, K, 51)
+    codes, scales, _ = oracle.pack(W)
+    c, s = _upload_packed(env, codes, scales)
+    x = _x_dev(env, wl.activation(K, 51, "unit_rms"))
+    X = cases.to_dev(wl.activations(N, K, 51, "normal").view(np.int16), torch, dev).view(torch.bfloat16)
+    y_eager = q4.q4_gemv(c, s, x).clone()
+    Y_eager = q4.q4_gemm_smalln(c, s, X).clone()
+    y = torch.full((M,), float("nan"), device=dev)
+    Y = torch.full((N, M), float("nan"), device=dev)
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            q4.q4_gemv(c, s, x, y, stream=st)
+            q4.q4_gemm_smalln(c, s, X, Y, stream=st)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y.fill_(float("nan"))
+        Y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"gemv replay {rep} differs from eager"
+        assert torch.equal(Y, Y_eager), f"gemm replay {rep} differs from eager"
+        # eager work in between replays
+        q4.q4_gemv(c, s, x)
+        torch.cuda.synchronize()
