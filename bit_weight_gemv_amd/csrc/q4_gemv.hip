@@ -46,19 +46,26 @@ constexpr int kLutDwords = 256 * kLutCopies;  // 64 KB
 constexpr int kMaxWavesPerGroup = 8;
 
 // Dword e * 64 + l of the table holds entry e (a code byte) for lane slot l.
-// Lane i of every wave computes the fp16 level i % 16 once (vector selects
-// between literals, no memory access); each wave then writes whole entries
-// (64 consecutive dwords, conflict-free), taking the two halves of an entry
-// from those lanes with v_readlane.
+// Lane l of every wave first builds the four entries l, l+64, l+128, l+192
+// (vector selects between fp16 literals, no memory access).  Each wave then
+// writes whole entries (64 consecutive dwords, conflict-free); an entry's
+// value is broadcast from the lane that built it by one v_readlane, so the
+// loop has no scalar arithmetic (the CU's scalar unit is shared by all its
+// waves).
 __device__ __forceinline__ void fill_lut(uint32_t *lut) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nw = blockDim.x >> 6;
-    const uint32_t mine = level_f16_bits(lane & 15);
-    for (int e = wave; e < 256; e += nw) {
-        const uint32_t lo = __builtin_amdgcn_readlane(mine, e & 15);
-        const uint32_t hi = __builtin_amdgcn_readlane(mine, e >> 4);
-        lut[e * 64 + lane] = lo | (hi << 16);
+    const uint32_t lo = level_f16_bits(lane & 15);
+    uint32_t mine[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mine[r] = lo | (level_f16_bits((lane >> 4) + 4 * r) << 16);
+    // Wave w writes entries w, w+nw, ...; quarter r covers entries 64r..64r+63.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int first = 64 * r > wave ? wave + (64 * r - wave + nw - 1) / nw * nw : wave;
+        for (int e = first; e < 64 * (r + 1); e += nw)
+            lut[e * 64 + lane] = __builtin_amdgcn_readlane(mine[r], e & 63);
     }
 }
 
@@ -127,18 +134,25 @@ __device__ __forceinline__ void convert_chunk_x(const uint32_t (&raw)[16], float
     }
 }
 
+// Activations: the lane's chunks are converted to fp16, scaled by a
+// wave-uniform power of two chosen from the wave's largest bf16 magnitude so
+// that no value can overflow fp16; the inverse scale (exact) is returned.
+// With one chunk per lane the raw words are loaded first (`raw`, before the
+// weight tiles, so the conversion does not wait behind them); with several,
+// the maximum is taken in a first pass and the chunks are re-read (from
+// cache) for the conversion, so the raw and the converted copies are never
+// live together.
 template <int CPL>
-__device__ __forceinline__ float load_x(const uint16_t *__restrict__ x, const int (&cidx)[CPL],
-                                        const bool (&cvalid)[CPL], half2_t (&xh)[CPL][16]) {
+__device__ __forceinline__ float convert_x(const uint16_t *__restrict__ x, const int (&cidx)[CPL],
+                                           const bool (&cvalid)[CPL], uint32_t (&raw)[16],
+                                           half2_t (&xh)[CPL][16]) {
     u16x2_t mx = {0, 0};
-    uint32_t raw[16];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        load_chunk_x(x, cidx[i], cvalid[i], raw);
+        if (CPL > 1) load_chunk_x(x, cidx[i], cvalid[i], raw);
 #pragma unroll
         for (int v = 0; v < 16; ++v)
             mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, raw[v] & 0x7FFF7FFFu));
-        if (CPL == 1) break;
     }
     // Largest bf16 magnitude bits of the wave (integer max: bf16 magnitudes
     // order like their bit patterns).
@@ -174,26 +188,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
                           amdgpu_waves_per_eu(gemv_min_waves(CPL), 8))) void gemv_kernel(const uint8_t *__restrict__ codes,
                                                    const uint16_t *__restrict__ scales, int64_t M,
                                                    int K, const uint16_t *__restrict__ x,
-                                                   float *__restrict__ y, int P) {
+                                                   float *__restrict__ y, int P, int64_t rows_q,
+                                                   int rows_rem) {
     __shared__ uint32_t lut[kLutDwords];
     __shared__ float red[kMaxWavesPerGroup][RG];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wpg = MULTI ? (P >> 6) : 1;      // waves per group
-    const int G = (int)(blockDim.x >> 6) / wpg;  // groups per workgroup
-    const int wig = wave % wpg;                // wave within its group
-    const int lig = wig * 64 + lane;           // lane within its group
+    // A group is one wave (MULTI == false) or the whole workgroup.
+    const int wpg = MULTI ? (P >> 6) : 1;     // waves per group
+    const int wig = MULTI ? wave : 0;         // wave within its group
+    const int lig = wig * 64 + lane;          // lane within its group
+    const int64_t gid = MULTI ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
     const int C = K >> 5;                      // 16-byte chunks per row
     const int nsb = K >> 6;                    // scale blocks per row
     const int64_t row_bytes = K >> 1;
-    const int64_t ngroups = (int64_t)gridDim.x * G;
-    const int64_t gid = (int64_t)blockIdx.x * G + wave / wpg;
-    // 64-bit division runs on the VALU; the results are wave-uniform, so move
-    // them back to SGPRs and keep all row addressing scalar.
-    const int64_t r_begin = uniform64(gid * M / ngroups);
-    const int64_t r_end = uniform64((gid + 1) * M / ngroups);
-    const int64_t ntiles = uniform64((r_end - r_begin + NR - 1) / NR);
+    // Rows are split evenly over the groups by the host: rows_q each, one
+    // more for the first rows_rem groups (no division on the device).
+    const int64_t r_begin = gid * rows_q + (gid < rows_rem ? gid : rows_rem);
+    const int64_t r_end = r_begin + rows_q + (gid < rows_rem ? 1 : 0);
+    const int64_t ntiles = (r_end - r_begin + NR - 1) / NR;
 
     // Chunk indices of this lane.  Lanes past the row's end load a valid
     // chunk (the last one) and multiply it by zero activations, so every load
@@ -249,15 +263,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
         next_left -= NR;
     };
 
-    if (ntiles > 0) {  // first tiles in flight during set-up
+    // Set-up order: activation loads, then the first weight tiles, then the
+    // table fill (no memory dependence, so it overlaps the load latency),
+    // then the activation conversion (which waits only for the activation
+    // loads: vector loads complete in order).
+    // The first tiles load unconditionally: an empty row range loads through
+    // zero-record resources (no memory access), and no branch makes the
+    // compiler's wait analysis assume the tile loads might be missing.
+    uint32_t xraw[16];
+    if (CPL == 1) load_chunk_x(x, cidx[0], cvalid[0], xraw);
 #pragma unroll
-        for (int s = 0; s <= S; ++s) load_tile(s);
-    }
-
-    half2_t xh[CPL][16];
-    const float down = load_x<CPL>(x, cidx, cvalid, xh);
-
+    for (int s = 0; s <= S; ++s) load_tile(s);
     fill_lut(lut);
+    half2_t xh[CPL][16];
+    const float down = convert_x<CPL>(x, cidx, cvalid, xraw, xh);
     __syncthreads();
 
     const uint32_t laneoff = (uint32_t)lane << 2;
@@ -335,7 +354,10 @@ hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, int64_t 
     int64_t grid = (tiles + G - 1) / G;
     if (grid > max_wg) grid = max_wg;
     if (grid < 1) grid = 1;
-    void *args[] = {&codes, &scales, &M, &K, &x, &y, &P};
+    const int64_t ngroups = grid * G;
+    int64_t rows_q = M / ngroups;
+    int rows_rem = (int)(M % ngroups);
+    void *args[] = {&codes, &scales, &M, &K, &x, &y, &P, &rows_q, &rows_rem};
     return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_kernel<NR, CPL, S, RG, MULTI>), dim3((unsigned)grid),
                            dim3((unsigned)(P * G)), args, 0, stream);
 }
