@@ -122,11 +122,14 @@ def time_calls(torch, fn, reps, steps, warmup):
     return wall_ms, start.elapsed_time(end) / steps
 
 
+WARMUP_SECONDS = 0.1
+
+
 def time_graph(torch, fn, reps, steps, warmup):
     """The timed region: `steps` calls (rotating over the copies) captured once
     in a HIP graph and replayed, bracketed by two events on the replay stream
     and by host synchronisation.  Warm-up replays the same graph until at
-    least `warmup` calls have run.  Returns (event ms per call, wall ms per
+    least `warmup` calls and WARMUP_SECONDS have passed.  Returns (event ms per call, wall ms per
     call)."""
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
@@ -138,8 +141,14 @@ def time_graph(torch, fn, reps, steps, warmup):
             for i in range(steps):
                 fn(*reps[i % len(reps)])
         torch.cuda.synchronize()
-        for _ in range(max(1, -(-warmup // steps))):
+        # Warm-up: at least `warmup` calls and at least WARMUP_SECONDS of
+        # replays (the GPU's clocks take some 20 ms of sustained load to
+        # settle; a shorter warm-up times the ramp).
+        done, t_w = 0, time.perf_counter()
+        while done < max(1, warmup) or time.perf_counter() - t_w < WARMUP_SECONDS:
             g.replay()
+            torch.cuda.synchronize()
+            done += steps
         torch.cuda.synchronize()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()

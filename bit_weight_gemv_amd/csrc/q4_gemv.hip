@@ -44,28 +44,39 @@ namespace q4 {
 constexpr int kLutCopies = 64;
 constexpr int kLutDwords = 256 * kLutCopies;  // 64 KB
 constexpr int kMaxWavesPerGroup = 8;
+// Row-per-wave variants cover rows of up to 128 chunks (K <= 4096): the LDS
+// copy of the activations is at most 8 KB (512 lanes x 16 bytes).
+constexpr int kSharedXUnits = 512;
 
-// Dword e * 64 + l of the table holds entry e (a code byte) for lane slot l.
-// Lane l of every wave first builds the four entries l, l+64, l+128, l+192
-// (vector selects between fp16 literals, no memory access).  Each wave then
-// writes whole entries (64 consecutive dwords, conflict-free); an entry's
-// value is broadcast from the lane that built it by one v_readlane, so the
-// loop has no scalar arithmetic (the CU's scalar unit is shared by all its
-// waves).
+// The 256 distinct table entries (1 KB), built at compile time: entry b is
+// the fp16 pair (level[b & 15], level[b >> 4]).  Kernels read it only with
+// wave-uniform scalar loads, as the source of the LDS copies; no lane ever
+// indexes it.
+struct PairTable {
+    uint32_t v[256];
+};
+constexpr PairTable make_pair_table() {
+    PairTable t{};
+    for (int b = 0; b < 256; ++b) t.v[b] = level_f16_bits_c(b & 15) | (level_f16_bits_c(b >> 4) << 16);
+    return t;
+}
+__device__ const PairTable kPairTable = make_pair_table();
+
+// Dword e * 64 + l of the LDS table holds entry e for lane slot l.  The 256
+// entries are written in 8 portions of 32; wave w writes portions w, w + nw,
+// ...: two 16-dword scalar loads fetch a portion's entries, and each entry is
+// written to its 64 slots by one lane each (ds_write2st64 pairs two entries
+// per instruction, conflict-free).  No per-entry index arithmetic and no
+// dependence on the weight loads in flight.
 __device__ __forceinline__ void fill_lut(uint32_t *lut) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nw = blockDim.x >> 6;
-    const uint32_t lo = level_f16_bits(lane & 15);
-    uint32_t mine[4];
+    for (int p = wave; p < 8; p += nw) {
+        const uint32_t *src = kPairTable.v + 32 * p;
+        uint32_t *dst = lut + (32 * kLutCopies) * p + lane;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) mine[r] = lo | (level_f16_bits((lane >> 4) + 4 * r) << 16);
-    // Wave w writes entries w, w+nw, ...; quarter r covers entries 64r..64r+63.
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int first = 64 * r > wave ? wave + (64 * r - wave + nw - 1) / nw * nw : wave;
-        for (int e = first; e < 64 * (r + 1); e += nw)
-            lut[e * 64 + lane] = __builtin_amdgcn_readlane(mine[r], e & 63);
+        for (int i = 0; i < 32; ++i) dst[kLutCopies * i] = src[i];
     }
 }
 
@@ -98,12 +109,8 @@ __device__ __forceinline__ float chunk_dot(const uint32_t *lut, uint4 q, const h
     return p;
 }
 
-// Load the lane's activation chunks and convert them to fp16, scaled by a
-// wave-uniform power of two chosen from the wave's largest bf16 magnitude so
-// that no value can overflow fp16.  Returns the inverse scale (exact).  With
-// several chunks per lane the maximum is taken in a first pass and the
-// chunks are re-read (from cache) for the conversion, so the raw and the
-// converted copies are never live together.
+// Raw activations of chunk c (16 dwords, two bf16 each) from global memory;
+// a lane past the row's end gets zeros.
 __device__ __forceinline__ void load_chunk_x(const uint16_t *__restrict__ x, int c, bool valid,
                                              uint32_t (&raw)[16]) {
     if (valid) {
@@ -122,6 +129,18 @@ __device__ __forceinline__ void load_chunk_x(const uint16_t *__restrict__ x, int
     }
 }
 
+// The same from the workgroup's LDS copy of the activations.
+__device__ __forceinline__ void load_chunk_x_lds(const uint4 *xs, int c, bool valid, uint32_t (&raw)[16]) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const uint4 t = valid ? xs[c * 4 + v] : make_uint4(0, 0, 0, 0);
+        raw[4 * v + 0] = t.x;
+        raw[4 * v + 1] = t.y;
+        raw[4 * v + 2] = t.z;
+        raw[4 * v + 3] = t.w;
+    }
+}
+
 __device__ __forceinline__ void convert_chunk_x(const uint32_t (&raw)[16], float up, half2_t (&xh)[16]) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -137,19 +156,18 @@ __device__ __forceinline__ void convert_chunk_x(const uint32_t (&raw)[16], float
 // Activations: the lane's chunks are converted to fp16, scaled by a
 // wave-uniform power of two chosen from the wave's largest bf16 magnitude so
 // that no value can overflow fp16; the inverse scale (exact) is returned.
-// With one chunk per lane the raw words are loaded first (`raw`, before the
-// weight tiles, so the conversion does not wait behind them); with several,
-// the maximum is taken in a first pass and the chunks are re-read (from
-// cache) for the conversion, so the raw and the converted copies are never
-// live together.
-template <int CPL>
-__device__ __forceinline__ float convert_x(const uint16_t *__restrict__ x, const int (&cidx)[CPL],
-                                           const bool (&cvalid)[CPL], uint32_t (&raw)[16],
-                                           half2_t (&xh)[CPL][16]) {
+// `load(i, raw)` fetches the raw words of the lane's chunk i.  With one chunk
+// per lane the caller passes them in `raw` (loaded early, so the conversion
+// does not wait behind the weight tiles); with several, the maximum is taken
+// in a first pass and the chunks are fetched again (from cache or LDS) for
+// the conversion, so the raw and the converted copies are never live
+// together.
+template <int CPL, bool PRELOADED, class Load>
+__device__ __forceinline__ float convert_x(Load load, uint32_t (&raw)[16], half2_t (&xh)[CPL][16]) {
     u16x2_t mx = {0, 0};
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        if (CPL > 1) load_chunk_x(x, cidx[i], cvalid[i], raw);
+        if (!PRELOADED || CPL > 1) load(i, raw);
 #pragma unroll
         for (int v = 0; v < 16; ++v)
             mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, raw[v] & 0x7FFF7FFFu));
@@ -167,7 +185,7 @@ __device__ __forceinline__ float convert_x(const uint16_t *__restrict__ x, const
     const float up = exp2i(e);
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        if (CPL > 1) load_chunk_x(x, cidx[i], cvalid[i], raw);
+        if (CPL > 1) load(i, raw);
         convert_chunk_x(raw, up, xh[i]);
     }
     return exp2i(-e);
@@ -192,6 +210,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
                                                    int rows_rem) {
     __shared__ uint32_t lut[kLutDwords];
     __shared__ float red[kMaxWavesPerGroup][RG];
+    // Groups of one wave all need the whole activation vector: it is read
+    // from global memory once per workgroup into LDS (raw bf16, 16 bytes per
+    // lane) and every wave takes its chunks from there.
+    __shared__ uint4 xs[MULTI ? 1 : kSharedXUnits];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -271,13 +293,29 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
     // zero-record resources (no memory access), and no branch makes the
     // compiler's wait analysis assume the tile loads might be missing.
     uint32_t xraw[16];
-    if (CPL == 1) load_chunk_x(x, cidx[0], cvalid[0], xraw);
+    u32x4_t xunit;  // this lane's 16 bytes of the shared activation copy
+    const int xunits = K >> 3;
+    if (MULTI) {
+        if (CPL == 1) load_chunk_x(x, cidx[0], cvalid[0], xraw);
+    } else {
+        // Bytes past the vector's end read as zero (buffer bounds).
+        xunit = __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(x, (uint32_t)K * 2u), (int)threadIdx.x * 16, 0, 0);
+    }
 #pragma unroll
     for (int s = 0; s <= S; ++s) load_tile(s);
     fill_lut(lut);
     half2_t xh[CPL][16];
-    const float down = convert_x<CPL>(x, cidx, cvalid, xraw, xh);
-    __syncthreads();
+    float down;
+    if constexpr (MULTI) {
+        down = convert_x<CPL, true>([&](int i, uint32_t(&r)[16]) { load_chunk_x(x, cidx[i], cvalid[i], r); },
+                                    xraw, xh);
+        __syncthreads();
+    } else {
+        if ((int)threadIdx.x < xunits) xs[threadIdx.x] = make_uint4(xunit.x, xunit.y, xunit.z, xunit.w);
+        __syncthreads();
+        down = convert_x<CPL, false>(
+            [&](int i, uint32_t(&r)[16]) { load_chunk_x_lds(xs, cidx[i], cvalid[i], r); }, xraw, xh);
+    }
 
     const uint32_t laneoff = (uint32_t)lane << 2;
 
@@ -347,13 +385,10 @@ int cu_count() {
 
 template <int NR, int CPL, int S, int RG, bool MULTI>
 hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, int64_t M, int K,
-                          const uint16_t *x, float *y, int P, int G, hipStream_t stream) {
-    // Two workgroups fit a CU (64 KB of LDS each); one pass over the grid.
-    const int64_t max_wg = 2LL * cu_count();
-    const int64_t tiles = (M + NR - 1) / NR;
-    int64_t grid = (tiles + G - 1) / G;
-    if (grid > max_wg) grid = max_wg;
-    if (grid < 1) grid = 1;
+                          const uint16_t *x, float *y, int P, int G, int64_t grid, hipStream_t stream) {
+    // The LDS copy of the activations of a row-per-wave variant is one
+    // 16-byte unit per lane of the workgroup.
+    if (!MULTI && (K / 8 > P * G || K / 8 > kSharedXUnits)) return hipErrorInvalidValue;
     const int64_t ngroups = grid * G;
     int64_t rows_q = M / ngroups;
     int rows_rem = (int)(M % ngroups);
@@ -362,26 +397,58 @@ hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, int64_t 
                            dim3((unsigned)(P * G)), args, 0, stream);
 }
 
+// Workgroups for `tiles` tiles of NR rows, G groups per workgroup: two
+// workgroups fit a CU (64 KB of LDS each), one pass over the grid.
+int64_t gemv_grid(int64_t tiles, int G) {
+    const int64_t max_wg = 2LL * cu_count();
+    int64_t grid = (tiles + G - 1) / G;
+    if (grid > max_wg) grid = max_wg;
+    return grid < 1 ? 1 : grid;
+}
+
 }  // namespace
 
+// Variant choice.  Every variant reads tiles of 4 rows (2 for 2-chunk
+// lanes).  Where a lane group gets at most two tiles (the whole matrix fits
+// one pass of the grid with a few rows per group) the ring has nothing to run
+// ahead of: the single-tile form (no ring, 4-row reduction groups) has the
+// shortest set-up.  Otherwise a ring of two tiles keeps the next tile's
+// loads in flight while the current one is reduced.
 hipError_t launch_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                        const uint16_t *x, float *y, hipStream_t stream) {
     const int C = (int)(K / kChunkWeights);
     const int k = (int)K;
-    if (C <= 64)  // one wave covers a row: 8 independent waves per workgroup
-        return launch_variant<4, 1, 1, 8, false>(codes, scales, M, k, x, y, 64, 8, stream);
-    if (C <= 128)
-        return launch_variant<2, 2, 1, 16, false>(codes, scales, M, k, x, y, 64, 8, stream);
+    const int64_t tiles4 = (M + 3) / 4;
+    if (C <= 64) {  // one wave covers a row: 8 independent waves per workgroup
+        const int64_t grid = gemv_grid(tiles4, 8);
+        if (tiles4 <= 2 * grid * 8)
+            return launch_variant<4, 1, 0, 4, false>(codes, scales, M, k, x, y, 64, 8, grid, stream);
+        return launch_variant<4, 1, 1, 8, false>(codes, scales, M, k, x, y, 64, 8, grid, stream);
+    }
+    if (C <= 128) {
+        const int64_t tiles2 = (M + 1) / 2;
+        return launch_variant<2, 2, 1, 16, false>(codes, scales, M, k, x, y, 64, 8, gemv_grid(tiles2, 8), stream);
+    }
     // Long rows: the whole workgroup (up to 8 waves) shares a row tile.
     int cpl = 1;
     while (C > cpl * 64 * kMaxWavesPerGroup) cpl *= 2;
     const int waves = (C + cpl * 64 - 1) / (cpl * 64);
     const int P = waves * 64;
+    const int64_t grid4 = gemv_grid(tiles4, 1);
+    const bool few = tiles4 <= 2 * grid4;
     switch (cpl) {
-        case 1: return launch_variant<4, 1, 1, 8, true>(codes, scales, M, k, x, y, P, 1, stream);
-        case 2: return launch_variant<4, 2, 1, 8, true>(codes, scales, M, k, x, y, P, 1, stream);
-        case 4: return launch_variant<2, 4, 1, 4, true>(codes, scales, M, k, x, y, P, 1, stream);
-        default: return launch_variant<1, 8, 0, 2, true>(codes, scales, M, k, x, y, P, 1, stream);
+        case 1:
+            if (few) return launch_variant<4, 1, 0, 4, true>(codes, scales, M, k, x, y, P, 1, grid4, stream);
+            return launch_variant<4, 1, 1, 8, true>(codes, scales, M, k, x, y, P, 1, grid4, stream);
+        case 2:
+            if (few) return launch_variant<4, 2, 0, 4, true>(codes, scales, M, k, x, y, P, 1, grid4, stream);
+            return launch_variant<4, 2, 1, 8, true>(codes, scales, M, k, x, y, P, 1, grid4, stream);
+        case 4: {
+            const int64_t tiles2 = (M + 1) / 2;
+            return launch_variant<2, 4, 1, 4, true>(codes, scales, M, k, x, y, P, 1, gemv_grid(tiles2, 1), stream);
+        }
+        default:
+            return launch_variant<1, 8, 0, 2, true>(codes, scales, M, k, x, y, P, 1, gemv_grid(M, 1), stream);
     }
 }
 
