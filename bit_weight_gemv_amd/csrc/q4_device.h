@@ -50,6 +50,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
 constexpr int kLoadNonTemporal = 2;
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // Mark a wave-uniform 64-bit value as such (lives in SGPRs afterwards).
 __device__ __forceinline__ int64_t uniform64(int64_t v) {

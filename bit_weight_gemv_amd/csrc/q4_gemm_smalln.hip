@@ -8,160 +8,290 @@
 // read once per chunk of tokens and the unpacking amortised over the chunk.
 //
 // gfx950 design:
-//  * One wave computes a 32(n) x 32(m) output tile with
-//    v_mfma_f32_32x32x16_bf16: operand A is 32 tokens x 16 k of X (bf16, as
-//    given), operand B is 16 k x 32 rows of dequantised weights.  Tokens
-//    n >= N are zero rows of A.
-//  * Dequantisation goes through an LDS table: a code byte (two weights)
-//    selects the bf16 pair of their levels (hi) and the bf16 pair of the
-//    levels' residuals (lo), so level = hi + lo to 2^-17 relative and two
-//    MFMAs (hi, lo) reproduce the fp32 table without rounding X.  The table is
-//    stored 32 times (copy = lane % 32, 8 bytes each) so every half-wave
-//    reads 32 distinct 8-byte slots: no bank conflicts for random codes.
-//  * Scales are per (row, 64-block): a block's four k-steps accumulate into a
-//    fresh tile, which is then added into the running tile times the scale of
-//    each lane's row (lane l holds column m = l % 32 of the output tile).
-//  * A lane's 16 code bytes are 32 consecutive k of one block; the four
-//    MFMAs of a block take k = 32h + 8t + (0..7) for lane half h and step t,
-//    and X is read with the same permutation of k.
-//  * The four waves of a workgroup split the blocks of K; their tiles are
-//    summed through LDS at the end.
+//  * Matrix cores.  v_mfma_f32_16x16x32_f16 multiplies a 16-token x 32-k
+//    slab of X (operand A) by a 32-k x 16-row slab of dequantised weights
+//    (operand B) into a 16 x 16 fp32 tile; chunks of 17..32 tokens take two
+//    MFMAs per slab of weights, so each dequantised weight feeds every token.
+//    Lane l of an operand holds row/token l % 16 and eight k of group l / 16;
+//    within a 64-block, k-group g of MFMA step s is k = 16g + 8s + (0..7)
+//    (a fixed permutation of k, the same for X and W), so a lane's codes for
+//    one block are 8 contiguous bytes.
+//  * Dequantisation.  The LDS byte -> fp16-pair table (one ds_read_b32 per
+//    two weights; the 64-copy layout keeps random codes conflict-free).  The
+//    fp32 result of a block's two MFMAs is multiplied by the block scale of
+//    the lane's weight row (fp32 FMA): levels round to fp16 (2^-11 relative)
+//    and nothing else is rounded below fp32.
+//  * Activations.  The workgroup's waves split K into slices of 256 (four
+//    blocks); a wave converts its slice of X to fp16 once, each token scaled
+//    by a power of two chosen from that token's largest magnitude in the
+//    slice (exact; no bf16 value can overflow), and keeps it in registers
+//    for every row tile it visits.  The inverse scale is applied to the
+//    wave's partial sums.
+//  * Schedule.  Row tiles of 16 rows are split into contiguous ranges, one
+//    per workgroup (one workgroup per CU); the waves walk the range in step
+//    with a ring of prefetched tiles (codes and scales of tile t+1 .. t+S are
+//    in flight while tile t is multiplied).  Per tile the waves' partial
+//    tiles are summed through LDS (double-buffered: one barrier per tile).
 #include "q4_device.h"
 #include "q4_internal.h"
+#include "q4_lut.h"
 
 namespace q4 {
 
-constexpr int kMmaLutCopies = 32;
-constexpr int kMmaLutDwords = 256 * kMmaLutCopies * 2;  // 64 KB
-constexpr int kSmallnWaves = 4;
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-    const uint32_t b = __builtin_bit_cast(uint32_t, f);
-    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
+constexpr int kGemmMaxWaves = 8;   // workgroup: up to 8 waves, one K slice each
+constexpr int kSliceBlocks = 4;    // 64-blocks per K slice (256 k)
+constexpr int kTileRows = 16;
 
-__device__ __forceinline__ void level_hi_lo(int i, uint32_t &hi, uint32_t &lo) {
-    const float c = level_f32(i);
-    hi = bf16_rne_bits(c);
-    const float rest = c - __builtin_bit_cast(float, hi << 16);  // exact
-    lo = bf16_rne_bits(rest);
-}
-
-// Dword i: entry e = i / 64 (wave-uniform), copy = (i % 64) / 2, part = i % 2
-// (0: hi pair, 1: lo pair).  Byte address of (e, copy) = e * 256 + copy * 8.
-__device__ __forceinline__ void fill_mma_lut(uint32_t *lut) {
-    for (int i = threadIdx.x; i < kMmaLutDwords; i += blockDim.x) {
-        const int e = __builtin_amdgcn_readfirstlane(i >> 6);
-        uint32_t h0, l0, h1, l1;
-        level_hi_lo(e & 15, h0, l0);
-        level_hi_lo(e >> 4, h1, l1);
-        lut[i] = (i & 1) ? (l0 | (l1 << 16)) : (h0 | (h1 << 16));
-    }
-}
-
-template <int B>
-__device__ __forceinline__ uint2 mma_lut_pair(const uint32_t *lut, uint32_t word, uint32_t laneoff) {
-    constexpr uint32_t sel = 0x0C0C0000u | ((4u + B) << 8);
-    const uint32_t addr = __builtin_amdgcn_perm(word, laneoff, sel);
-    return *reinterpret_cast<const uint2 *>(reinterpret_cast<const char *>(lut) + addr);
-}
-
-template <int PF>
-__global__ __launch_bounds__(256) void gemm_smalln_kernel(const uint8_t *__restrict__ codes,
-                                                          const uint16_t *__restrict__ scales,
-                                                          int64_t M, int K,
-                                                          const uint16_t *__restrict__ X, int N,
-                                                          float *__restrict__ Y) {
-    __shared__ uint32_t lut[kMmaLutDwords];
-
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int col = lane & 31;   // row of W / column of the output tile
-    const int half = lane >> 5;  // which 32 k of a 64-block
-    const int64_t m0 = (int64_t)blockIdx.x * 32;
-    const int64_t mrow = (m0 + col < M) ? m0 + col : M - 1;
-    const int nsb = K >> 6;
-    const int b_begin = wave * nsb / kSmallnWaves;
-    const int b_end = (wave + 1) * nsb / kSmallnWaves;
-    const bool xrow = col < N;  // this lane carries token n = col in operand A
-    const uint8_t *crow = codes + mrow * (int64_t)(K >> 1) + half * 16;
-    const uint16_t *srow = scales + mrow * nsb;
-    const uint16_t *xrow_ptr = X + (int64_t)(xrow ? col : 0) * K + half * 32;
-
-    fill_mma_lut(lut);
-    __syncthreads();
-
-    const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
-    float16_t acc = {};
-
-    for (int b0 = b_begin; b0 < b_end; b0 += PF) {
-        uint4 q[PF];
-        uint32_t sc[PF];
-        uint4 xa[PF][4];
+// Raw bf16 activations of one lane: token row `tok`, the 16 k of group g for
+// each block of the slice (two MFMA steps x 8 k).  Blocks past the row's end
+// and tokens past N read as zero (offsets past the buffer).
+template <int NT>
+__device__ __forceinline__ void load_x_slice(__amdgpu_buffer_rsrc_t xrs, int K, int nsb, int slice, int j, int g,
+                                             u32x4_t (&raw)[NT][kSliceBlocks][2]) {
 #pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int b = (b0 + p < b_end) ? b0 + p : b_end - 1;
-            q[p] = *reinterpret_cast<const uint4 *>(crow + (int64_t)b * 32);
-            sc[p] = srow[b];
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                xa[p][t] = xrow ? *reinterpret_cast<const uint4 *>(xrow_ptr + (int64_t)b * 64 + 8 * t)
-                                : make_uint4(0, 0, 0, 0);
-        }
+        for (int b = 0; b < kSliceBlocks; ++b) {
+            const int blk = slice * kSliceBlocks + b;
+            const int base = ((16 * t + j) * K + 64 * blk + 16 * g) * 2;
 #pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            if (b0 + p < b_end) {
-                float16_t tile = {};
-                const uint32_t w[4] = {q[p].x, q[p].y, q[p].z, q[p].w};
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const uint2 e0 = mma_lut_pair<0>(lut, w[t], laneoff);
-                    const uint2 e1 = mma_lut_pair<1>(lut, w[t], laneoff);
-                    const uint2 e2 = mma_lut_pair<2>(lut, w[t], laneoff);
-                    const uint2 e3 = mma_lut_pair<3>(lut, w[t], laneoff);
-                    const uint4 bh = make_uint4(e0.x, e1.x, e2.x, e3.x);
-                    const uint4 bl = make_uint4(e0.y, e1.y, e2.y, e3.y);
-                    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xa[p][t]);
-                    tile = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bh),
-                                                                   tile, 0, 0, 0);
-                    tile = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bl),
-                                                                   tile, 0, 0, 0);
-                }
-                const float s = f16_bits_to_f32(sc[p]);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] = fmaf(tile[r], s, acc[r]);
+            for (int s = 0; s < 2; ++s) {
+                const int off = blk < nsb ? base + 16 * s : 0x7FFFFFF0;
+                raw[t][b][s] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
             }
         }
     }
+}
 
-    // Sum the four waves' tiles through LDS (the table is no longer needed).
+// Convert the slice to fp16 per token: lanes j, j+16, j+32, j+48 hold token
+// j's values; their largest bf16 magnitude fixes the power of two.  Returns
+// in inv[t][r] the inverse scale of the token of output register r (token
+// 4g + r of half t).
+template <int NT>
+__device__ __forceinline__ void convert_x_slice(const u32x4_t (&raw)[NT][kSliceBlocks][2],
+                                                half8_t (&xa)[NT][kSliceBlocks][2], float (&inv)[NT][4]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        u16x2_t mx = {0, 0};
+#pragma unroll
+        for (int b = 0; b < kSliceBlocks; ++b)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, raw[t][b][s][c] & 0x7FFF7FFFu));
+        int m = (int)(mx.x > mx.y ? mx.x : mx.y);
+        m = max(m, __shfl_xor(m, 16));
+        m = max(m, __shfl_xor(m, 32));
+        // Biased exponent E of the token's largest magnitude; 2^(141-E) puts
+        // it in [2^14, 2^15).
+        int E = m >> 7;
+        if (E < 1) E = 1;
+        int e = 141 - E;
+        e = e > 126 ? 126 : (e < -126 ? -126 : e);
+        const float up = exp2i(e);
+#pragma unroll
+        for (int b = 0; b < kSliceBlocks; ++b)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                half8_t h;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t w = raw[t][b][s][c];
+                    h[2 * c] = (_Float16)(__builtin_bit_cast(float, w << 16) * up);
+                    h[2 * c + 1] = (_Float16)(__builtin_bit_cast(float, w & 0xFFFF0000u) * up);
+                }
+                xa[t][b][s] = h;
+            }
+        // Output register r of lane l belongs to token 4 (l / 16) + r, whose
+        // scale lane 4 (l / 16) + r computed.
+        const float down = exp2i(-e);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) inv[t][r] = __shfl(down, 4 * (lane >> 4) + r);
+    }
+}
+
+template <int NT, int S, bool XFIXED>
+__global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, int64_t M, int K,
+    const uint16_t *__restrict__ X, int N, float *__restrict__ Y, int64_t tiles_q, int tiles_rem) {
+    __shared__ uint32_t lut[kLutDwords];
+    __shared__ float red[2][kGemmMaxWaves][NT * 4][64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = blockDim.x >> 6;
+    const int j = lane & 15;  // token (operand A) / weight row (operand B) of this lane
+    const int g = lane >> 4;  // k group
+    const int nsb = K >> 6;
+    const int nslices = (nsb + kSliceBlocks - 1) / kSliceBlocks;
+    // Slices per wave: one when the waves cover K (XFIXED: the activations
+    // stay in registers), else several, reloaded per tile.
+    const int spw = XFIXED ? 1 : (nslices + nw - 1) / nw;
+    const int64_t row_bytes = K >> 1;
+    const int64_t wg = blockIdx.x;
+    const int64_t t_begin = wg * tiles_q + (wg < tiles_rem ? wg : tiles_rem);
+    const int64_t ntiles = tiles_q + (wg < tiles_rem ? 1 : 0);
+    const int64_t nunits = ntiles * spw;  // (tile, slice) pairs of this wave
+
+    const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(X, (uint32_t)N * (uint32_t)K * 2u);
+
+    // Ring of prefetched units: the codes (8 bytes per block) and scales of
+    // one tile over one K slice.  Units past the last load through
+    // zero-record resources (no memory access, unconditional loads).
+    uint2 qc[S + 1][kSliceBlocks];
+    uint32_t sc[S + 1][kSliceBlocks];
+    int64_t next_unit = 0;
+    auto load_unit = [&](int buf) {
+        const int64_t u = next_unit++;
+        const bool real = u < nunits;
+        const int64_t ti = spw == 1 ? u : u / spw;
+        const int slice = wave + nw * (spw == 1 ? 0 : (int)(u - ti * spw));
+        const int64_t m0 = (t_begin + (real ? ti : 0)) * kTileRows;
+        const int64_t left = M - m0;
+        const int rows = left < kTileRows ? (int)left : kTileRows;
+        const int jr = j < rows ? j : rows - 1;
+        const __amdgpu_buffer_rsrc_t crs =
+            buffer_rsrc(codes + m0 * row_bytes, real ? (uint32_t)(rows * row_bytes) : 0u);
+        const __amdgpu_buffer_rsrc_t srs =
+            buffer_rsrc(scales + m0 * nsb, real ? (uint32_t)(rows * nsb * 2) : 0u);
+#pragma unroll
+        for (int b = 0; b < kSliceBlocks; ++b) {
+            const int blk = slice * kSliceBlocks + b;
+            const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(
+                crs, (int)(jr * row_bytes) + 32 * blk + 8 * g, 0, kLoadNonTemporal);
+            qc[buf][b] = make_uint2(v.x, v.y);
+            sc[buf][b] = __builtin_amdgcn_raw_buffer_load_b16(srs, (jr * nsb + blk) * 2, 0, kLoadNonTemporal);
+        }
+    };
+
+    // Set-up: first tiles' loads, table fill, then this wave's activations
+    // (when the wave keeps one slice for the whole run).
+    u32x4_t raw[NT][kSliceBlocks][2];
+    if (XFIXED) load_x_slice<NT>(xrs, K, nsb, wave, j, g, raw);
+#pragma unroll
+    for (int s = 0; s <= S; ++s) load_unit(s);
+    fill_lut(lut);
+    half8_t xa[NT][kSliceBlocks][2];
+    float inv[NT][4];
+    if (XFIXED) convert_x_slice<NT>(raw, xa, inv);
     __syncthreads();
-    float *red = reinterpret_cast<float *>(lut);  // [wave][reg][lane]
+
+    const uint32_t laneoff = (uint32_t)lane << 2;
+    float acc[NT][4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[r];
-    __syncthreads();
-    // Wave w finishes registers 4w .. 4w+3.
-    const int64_t m = m0 + col;
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        const int r = wave * 4 + rr;
-        float s = 0.0f;
+        for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
+    int rbuf = 0;
+
+    auto consume = [&](int buf, int64_t u) {
+        const int64_t ti = spw == 1 ? u : u / spw;
+        const int si = spw == 1 ? 0 : (int)(u - ti * spw);
+        const int slice = wave + nw * si;
+        if (!XFIXED) {
+            load_x_slice<NT>(xrs, K, nsb, slice, j, g, raw);
+            convert_x_slice<NT>(raw, xa, inv);
+        }
+        float part[NT][4];
 #pragma unroll
-        for (int w = 0; w < kSmallnWaves; ++w) s += red[(w * 16 + r) * 64 + lane];
-        // Output layout of the 32x32 MFMA: register r of lane l is row
-        // 8 * (r / 4) + 4 * (l / 32) + r % 4, column l % 32.
-        const int n = 8 * (r >> 2) + 4 * half + (r & 3);
-        if (n < N && m < M) Y[(int64_t)n * M + m] = s;
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part[t][r] = 0.0f;
+#pragma unroll
+        for (int b = 0; b < kSliceBlocks; ++b) {
+            const int blk = slice * kSliceBlocks + b;
+            const float sb = blk < nsb ? f16_bits_to_f32(sc[buf][b]) : 0.0f;
+            float4_t tile[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) tile[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const uint32_t w = s ? qc[buf][b].y : qc[buf][b].x;
+                const half2_t p0 = lut_pair<0>(lut, w, laneoff);
+                const half2_t p1 = lut_pair<1>(lut, w, laneoff);
+                const half2_t p2 = lut_pair<2>(lut, w, laneoff);
+                const half2_t p3 = lut_pair<3>(lut, w, laneoff);
+                const half8_t bop = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    tile[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][b][s], bop, tile[t], 0, 0, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) part[t][r] = fmaf(tile[t][r], sb, part[t][r]);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(part[t][r], inv[t][r], acc[t][r]);
+
+        if (si == spw - 1) {
+            // Tile complete for this wave: sum the waves' partial tiles.
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    red[rbuf][wave][4 * t + r][lane] = acc[t][r];
+                    acc[t][r] = 0.0f;
+                }
+            __syncthreads();
+            const int64_t m0 = (t_begin + ti) * kTileRows;
+            for (int idx = threadIdx.x; idx < NT * 256; idx += blockDim.x) {
+                const int n = idx >> 4, mm = idx & 15;
+                const int t = n >> 4, r = n & 3;
+                const int l = ((n & 15) >> 2) * 16 + mm;
+                float sum = 0.0f;
+                for (int w = 0; w < nw; ++w) sum += red[rbuf][w][4 * t + r][l];
+                if (n < N && m0 + mm < M) Y[(int64_t)n * M + m0 + mm] = sum;
+            }
+            rbuf ^= 1;
+        }
+    };
+
+    for (int64_t u0 = 0; u0 < nunits; u0 += S + 1) {
+#pragma unroll
+        for (int s = 0; s <= S; ++s) {
+            if (u0 + s < nunits) consume(s, u0 + s);
+            load_unit(s);  // unit u0 + s + S + 1
+        }
     }
 }
 
 hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                               const uint16_t *X, int64_t N, float *Y, hipStream_t stream) {
-    const int64_t grid = (M + 31) / 32;
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    // One workgroup per CU (the table and the reduction buffers take 96 KB of
+    // LDS), each with one wave per K slice (at most 8).
+    const int64_t tiles = (M + kTileRows - 1) / kTileRows;
+    int64_t grid = tiles < cus[dev] ? tiles : cus[dev];
+    if (grid < 1) grid = 1;
+    int64_t tiles_q = tiles / grid;
+    int tiles_rem = (int)(tiles % grid);
+    const int nslices = (int)((K / 64 + kSliceBlocks - 1) / kSliceBlocks);
+    const int waves = nslices < kGemmMaxWaves ? nslices : kGemmMaxWaves;
     int k = (int)K, n = (int)N;
-    void *args[] = {&codes, &scales, &M, &k, &X, &n, &Y};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_smalln_kernel<4>), dim3((unsigned)grid),
-                           dim3(64 * kSmallnWaves), args, 0, stream);
+    void *args[] = {&codes, &scales, &M, &k, &X, &n, &Y, &tiles_q, &tiles_rem};
+    const void *fn;
+    if (nslices <= kGemmMaxWaves)
+        fn = N <= 16 ? reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 2, true>)
+                     : reinterpret_cast<const void *>(&gemm_smalln_kernel<2, 2, true>);
+    else
+        fn = N <= 16 ? reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 0, false>)
+                     : reinterpret_cast<const void *>(&gemm_smalln_kernel<2, 0, false>);
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)(64 * waves)), args, 0, stream);
 }
 
 }  // namespace q4
