@@ -44,24 +44,63 @@ constexpr int kGemmMaxWaves = 8;   // workgroup: up to 8 waves, one K slice each
 constexpr int kSliceBlocks = 4;    // 64-blocks per K slice (256 k)
 constexpr int kTileRows = 16;
 
-// Raw bf16 activations of one lane: token row `tok`, the 16 k of group g for
-// each block of the slice (two MFMA steps x 8 k).  Blocks past the row's end
-// and tokens past N read as zero (offsets past the buffer).
+// Loads are laid out for the memory pipeline, not for the MFMA: a load
+// instruction whose neighbouring lanes read neighbouring 16-byte pieces of
+// one row is served at full rate, while the operand layout (neighbouring
+// lanes on different rows) costs about one request per lane.  Activations
+// and codes are therefore loaded row-contiguously and regrouped into operand
+// order through a per-wave LDS area.
+
+// Per-wave LDS staging, in 16-byte units.  Activations: 16 tokens x 512 bytes
+// (one token half of a slice), row pitch 33 units; codes: 16 rows x 128
+// bytes (one tile of a slice), row pitch 9 units.  Pitches are odd so the
+// 16 rows of an operand read fall in different banks.
+constexpr int kXPitch = 33;
+constexpr int kXStageUnits = 16 * kXPitch;
+constexpr int kCPitch = 9;
+constexpr int kCStageUnits = 16 * kCPitch;
+
+// This wave's slice of X, row-contiguously: piece p = 64 i + lane (16 bytes)
+// is token p / 32, bytes 16 (p % 32) of the slice.  Tokens past N and blocks
+// past the row's end read as zero (offsets past the buffer).
 template <int NT>
-__device__ __forceinline__ void load_x_slice(__amdgpu_buffer_rsrc_t xrs, int K, int nsb, int slice, int j, int g,
-                                             u32x4_t (&raw)[NT][kSliceBlocks][2]) {
+__device__ __forceinline__ void load_x_linear(__amdgpu_buffer_rsrc_t xrs, int K, int nsb, int slice,
+                                              u32x4_t (&lin)[NT * 8]) {
+    const int lane = threadIdx.x & 63;
+    const int within = lane & 31;
+    const int blk = slice * kSliceBlocks + (within >> 3);
+#pragma unroll
+    for (int i = 0; i < NT * 8; ++i) {
+        const int tok = 2 * i + (lane >> 5);
+        const int off = blk < nsb ? (tok * K + 256 * slice + 8 * within) * 2 : 0x7FFFFFF0;
+        lin[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+    }
+}
+
+// Regroup through the wave's staging area into operand order: lane (j, g)
+// gets token 16t + j, k = 64b + 16g + 8s + (0..7) of the slice for block b,
+// step s.  One token half at a time; LDS operations of a wave complete in
+// order, so each half's reads finish before the next half's writes.
+template <int NT>
+__device__ __forceinline__ void regroup_x(uint4 *xs, const u32x4_t (&lin)[NT * 8],
+                                          u32x4_t (&raw)[NT][kSliceBlocks][2]) {
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int b = 0; b < kSliceBlocks; ++b) {
-            const int blk = slice * kSliceBlocks + b;
-            const int base = ((16 * t + j) * K + 64 * blk + 16 * g) * 2;
+        for (int i = 0; i < 8; ++i) {
+            const int tok = 2 * i + (lane >> 5);
+            const u32x4_t v = lin[8 * t + i];
+            xs[tok * kXPitch + (lane & 31)] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+#pragma unroll
+        for (int b = 0; b < kSliceBlocks; ++b)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const int off = blk < nsb ? base + 16 * s : 0x7FFFFFF0;
-                raw[t][b][s] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+                const uint4 v = xs[j * kXPitch + 8 * b + 2 * g + s];
+                raw[t][b][s] = u32x4_t{v.x, v.y, v.z, v.w};
             }
-        }
     }
 }
 
@@ -119,7 +158,13 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, int64_t M, int K,
     const uint16_t *__restrict__ X, int N, float *__restrict__ Y, int64_t tiles_q, int tiles_rem) {
     __shared__ uint32_t lut[kLutDwords];
-    __shared__ float red[2][kGemmMaxWaves][NT * 4][64];
+    // Activation staging (set-up only); afterwards the same bytes hold the
+    // double-buffered partial tiles of the cross-wave sum.
+    __shared__ uint4 xstage[kGemmMaxWaves * kXStageUnits];
+    __shared__ uint4 cstage[kGemmMaxWaves * kCStageUnits];
+    typedef float RedBuf[2][kGemmMaxWaves][NT * 4][64];
+    static_assert(sizeof(RedBuf) <= sizeof(xstage), "reduction buffer must fit the staging area");
+    RedBuf &red = *reinterpret_cast<RedBuf *>(xstage);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -136,14 +181,19 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
     const int64_t t_begin = wg * tiles_q + (wg < tiles_rem ? wg : tiles_rem);
     const int64_t ntiles = tiles_q + (wg < tiles_rem ? 1 : 0);
     const int64_t nunits = ntiles * spw;  // (tile, slice) pairs of this wave
+    uint4 *xs = xstage + wave * kXStageUnits;
+    uint4 *cs = cstage + wave * kCStageUnits;
 
     const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(X, (uint32_t)N * (uint32_t)K * 2u);
 
-    // Ring of prefetched units: the codes (8 bytes per block) and scales of
-    // one tile over one K slice.  Units past the last load through
-    // zero-record resources (no memory access, unconditional loads).
-    uint2 qc[S + 1][kSliceBlocks];
-    uint32_t sc[S + 1][kSliceBlocks];
+    // Ring of prefetched units: the codes and scales of one tile over one K
+    // slice.  Codes: 16 rows x 128 bytes, lane l takes row l / 8 (+ 8 for
+    // the second load), bytes 16 (l % 8).  Scales: lane l takes row l / 4,
+    // block l % 4 of the slice.  Rows past M repeat the last row (results not
+    // stored); units past the last load through zero-record resources (no
+    // memory access, unconditional loads).
+    u32x4_t qv[S + 1][2];
+    uint32_t sc[S + 1];
     int64_t next_unit = 0;
     auto load_unit = [&](int buf) {
         const int64_t u = next_unit++;
@@ -153,31 +203,38 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
         const int64_t m0 = (t_begin + (real ? ti : 0)) * kTileRows;
         const int64_t left = M - m0;
         const int rows = left < kTileRows ? (int)left : kTileRows;
-        const int jr = j < rows ? j : rows - 1;
         const __amdgpu_buffer_rsrc_t crs =
             buffer_rsrc(codes + m0 * row_bytes, real ? (uint32_t)(rows * row_bytes) : 0u);
         const __amdgpu_buffer_rsrc_t srs =
             buffer_rsrc(scales + m0 * nsb, real ? (uint32_t)(rows * nsb * 2) : 0u);
 #pragma unroll
-        for (int b = 0; b < kSliceBlocks; ++b) {
-            const int blk = slice * kSliceBlocks + b;
-            const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(
-                crs, (int)(jr * row_bytes) + 32 * blk + 8 * g, 0, kLoadNonTemporal);
-            qc[buf][b] = make_uint2(v.x, v.y);
-            sc[buf][b] = __builtin_amdgcn_raw_buffer_load_b16(srs, (jr * nsb + blk) * 2, 0, kLoadNonTemporal);
+        for (int q = 0; q < 2; ++q) {
+            const int r = (lane >> 3) + 8 * q;
+            const int rr = r < rows ? r : rows - 1;
+            qv[buf][q] = __builtin_amdgcn_raw_buffer_load_b128(
+                crs, (int)(rr * row_bytes) + 128 * slice + 16 * (lane & 7), 0, kLoadNonTemporal);
         }
+        const int rs = lane >> 2;
+        const int rsr = rs < rows ? rs : rows - 1;
+        sc[buf] = __builtin_amdgcn_raw_buffer_load_b16(srs, (rsr * nsb + slice * kSliceBlocks + (lane & 3)) * 2, 0,
+                                                       kLoadNonTemporal);
     };
 
-    // Set-up: first tiles' loads, table fill, then this wave's activations
-    // (when the wave keeps one slice for the whole run).
+    // Set-up: this wave's activations (when it keeps one slice for the whole
+    // run), the first units, the table fill, then the activation regrouping
+    // and conversion (which waits only for the activation loads).
+    u32x4_t lin[NT * 8];
     u32x4_t raw[NT][kSliceBlocks][2];
-    if (XFIXED) load_x_slice<NT>(xrs, K, nsb, wave, j, g, raw);
+    if (XFIXED) load_x_linear<NT>(xrs, K, nsb, wave, lin);
 #pragma unroll
     for (int s = 0; s <= S; ++s) load_unit(s);
     fill_lut(lut);
     half8_t xa[NT][kSliceBlocks][2];
     float inv[NT][4];
-    if (XFIXED) convert_x_slice<NT>(raw, xa, inv);
+    if (XFIXED) {
+        regroup_x<NT>(xs, lin, raw);
+        convert_x_slice<NT>(raw, xa, inv);
+    }
     __syncthreads();
 
     const uint32_t laneoff = (uint32_t)lane << 2;
@@ -193,9 +250,25 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
         const int si = spw == 1 ? 0 : (int)(u - ti * spw);
         const int slice = wave + nw * si;
         if (!XFIXED) {
-            load_x_slice<NT>(xrs, K, nsb, slice, j, g, raw);
+            // Long rows: this slice's activations, regrouped through the
+            // staging area's share of this wave; the reduction buffer shares
+            // those bytes, so the workgroup first leaves the previous tile's
+            // sum.
+            load_x_linear<NT>(xrs, K, nsb, slice, lin);
+            __syncthreads();
+            regroup_x<NT>(xs, lin, raw);
             convert_x_slice<NT>(raw, xa, inv);
+            __syncthreads();
         }
+        // Regroup the codes: lane (j, g) takes bytes 32b + 8g (8 bytes) of
+        // row j for block b; the scale of row j, block b is held by lane
+        // 4j + b.
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const u32x4_t v = qv[buf][q];
+            cs[((lane >> 3) + 8 * q) * kCPitch + (lane & 7)] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+        const char *crow = reinterpret_cast<const char *>(cs + j * kCPitch);
         float part[NT][4];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -204,13 +277,15 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
 #pragma unroll
         for (int b = 0; b < kSliceBlocks; ++b) {
             const int blk = slice * kSliceBlocks + b;
-            const float sb = blk < nsb ? f16_bits_to_f32(sc[buf][b]) : 0.0f;
+            const uint32_t sbits = __shfl(sc[buf], 4 * j + b);
+            const float sb = blk < nsb ? f16_bits_to_f32(sbits & 0xFFFFu) : 0.0f;
+            const uint2 qw = *reinterpret_cast<const uint2 *>(crow + 32 * b + 8 * g);
             float4_t tile[NT];
 #pragma unroll
             for (int t = 0; t < NT; ++t) tile[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const uint32_t w = s ? qc[buf][b].y : qc[buf][b].x;
+                const uint32_t w = s ? qw.y : qw.x;
                 const half2_t p0 = lut_pair<0>(lut, w, laneoff);
                 const half2_t p1 = lut_pair<1>(lut, w, laneoff);
                 const half2_t p2 = lut_pair<2>(lut, w, laneoff);
