@@ -69,10 +69,13 @@ __device__ __forceinline__ void load_x_linear(__amdgpu_buffer_rsrc_t xrs, int K,
     const int lane = threadIdx.x & 63;
     const int within = lane & 31;
     const int blk = slice * kSliceBlocks + (within >> 3);
+    // All ones for a block past the row's end: the offset then lies past the
+    // buffer (arithmetic, so the loads stay unconditional).
+    const int past = (nsb - 1 - blk) >> 31;
 #pragma unroll
     for (int i = 0; i < NT * 8; ++i) {
         const int tok = 2 * i + (lane >> 5);
-        const int off = blk < nsb ? (tok * K + 256 * slice + 8 * within) * 2 : 0x7FFFFFF0;
+        const int off = ((tok * K + 256 * slice + 8 * within) * 2) | (past & 0x7FFFFFF0);
         lin[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
     }
 }
@@ -157,67 +160,83 @@ template <int NT, int S, bool XFIXED>
 __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, int64_t M, int K,
     const uint16_t *__restrict__ X, int N, float *__restrict__ Y, int64_t tiles_q, int tiles_rem) {
-    __shared__ uint32_t lut[kLutDwords];
-    // Activation staging (set-up only); afterwards the same bytes hold the
-    // double-buffered partial tiles of the cross-wave sum.
-    __shared__ uint4 xstage[kGemmMaxWaves * kXStageUnits];
-    __shared__ uint4 cstage[kGemmMaxWaves * kCStageUnits];
-    typedef float RedBuf[2][kGemmMaxWaves][NT * 4][64];
-    static_assert(sizeof(RedBuf) <= sizeof(xstage), "reduction buffer must fit the staging area");
-    RedBuf &red = *reinterpret_cast<RedBuf *>(xstage);
+    // One block of LDS with the table at address 0, so a lookup address
+    // built by v_perm needs no base added (the 16-bit offset field of a DS
+    // instruction cannot hold a base past 64 KB).  Activation staging is
+    // used during set-up only (and per unit on the long-row path); the same
+    // bytes hold the double-buffered partial tiles of the cross-wave sum.
+    struct Smem {
+        uint32_t lut[kLutDwords];
+        uint4 xstage[kGemmMaxWaves * kXStageUnits];
+        uint4 cstage[kGemmMaxWaves * kCStageUnits];
+    };
+    __shared__ Smem sm;
+    uint32_t *lut = sm.lut;
+    // Partial tiles: [buffer][wave][lane][register], a lane's registers
+    // contiguous (written with 16-byte stores).
+    typedef float RedBuf[2][kGemmMaxWaves][64][NT * 4];
+    static_assert(sizeof(RedBuf) <= sizeof(sm.xstage), "reduction buffer must fit the staging area");
+    RedBuf &red = *reinterpret_cast<RedBuf *>(sm.xstage);
 
+    // Always kGemmMaxWaves waves; waves past the last K slice load nothing
+    // (zero-record resources, zero activations) and add exact zeros.
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nw = blockDim.x >> 6;
+    constexpr int nw = kGemmMaxWaves;
     const int j = lane & 15;  // token (operand A) / weight row (operand B) of this lane
     const int g = lane >> 4;  // k group
     const int nsb = K >> 6;
     const int nslices = (nsb + kSliceBlocks - 1) / kSliceBlocks;
     // Slices per wave: one when the waves cover K (XFIXED: the activations
-    // stay in registers), else several, reloaded per tile.
+    // stay in registers), else several, reloaded per unit.
     const int spw = XFIXED ? 1 : (nslices + nw - 1) / nw;
-    const int64_t row_bytes = K >> 1;
+    const int row_bytes = K >> 1;
     const int64_t wg = blockIdx.x;
     const int64_t t_begin = wg * tiles_q + (wg < tiles_rem ? wg : tiles_rem);
-    const int64_t ntiles = tiles_q + (wg < tiles_rem ? 1 : 0);
-    const int64_t nunits = ntiles * spw;  // (tile, slice) pairs of this wave
-    uint4 *xs = xstage + wave * kXStageUnits;
-    uint4 *cs = cstage + wave * kCStageUnits;
+    const int ntiles = (int)tiles_q + (wg < tiles_rem ? 1 : 0);
+    const int nunits = ntiles * spw;  // (tile, slice) pairs of this wave
+    uint4 *xs = sm.xstage + wave * kXStageUnits;
+    uint4 *cs = sm.cstage + wave * kCStageUnits;
 
     const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(X, (uint32_t)N * (uint32_t)K * 2u);
 
     // Ring of prefetched units: the codes and scales of one tile over one K
     // slice.  Codes: 16 rows x 128 bytes, lane l takes row l / 8 (+ 8 for
-    // the second load), bytes 16 (l % 8).  Scales: lane l takes row l / 4,
-    // block l % 4 of the slice.  Rows past M repeat the last row (results not
-    // stored); units past the last load through zero-record resources (no
-    // memory access, unconditional loads).
+    // the second load), bytes 16 (l % 8) of the slice.  Scales: lane l takes
+    // row l / 4, block l % 4 of the slice; a block past the row's end reads
+    // as zero.  The buffer resource of a unit starts at its tile and slice
+    // and ends at the last row of the matrix, so rows past M read as zero
+    // (their results are not stored); units past the last load through
+    // zero-record resources (no memory access, unconditional loads).
+    const int c_off = (lane >> 3) * row_bytes + 16 * (lane & 7);
+    const int s_row_off = ((lane >> 2) * nsb + (lane & 3)) * 2;
     u32x4_t qv[S + 1][2];
     uint32_t sc[S + 1];
-    int64_t next_unit = 0;
+    const uint8_t *ld_codes = codes + t_begin * kTileRows * row_bytes;
+    const uint16_t *ld_scales = scales + t_begin * kTileRows * nsb;
+    int64_t ld_rows = M - t_begin * kTileRows;  // rows from the next tile to load to M
+    int ld_unit = 0, ld_si = 0;
     auto load_unit = [&](int buf) {
-        const int64_t u = next_unit++;
-        const bool real = u < nunits;
-        const int64_t ti = spw == 1 ? u : u / spw;
-        const int slice = wave + nw * (spw == 1 ? 0 : (int)(u - ti * spw));
-        const int64_t m0 = (t_begin + (real ? ti : 0)) * kTileRows;
-        const int64_t left = M - m0;
-        const int rows = left < kTileRows ? (int)left : kTileRows;
+        const bool real = ld_unit < nunits;
+        const int slice = wave + nw * ld_si;
+        const int rows = ld_rows < kTileRows ? (int)ld_rows : kTileRows;
+        const bool live = real && slice < nslices;
         const __amdgpu_buffer_rsrc_t crs =
-            buffer_rsrc(codes + m0 * row_bytes, real ? (uint32_t)(rows * row_bytes) : 0u);
-        const __amdgpu_buffer_rsrc_t srs =
-            buffer_rsrc(scales + m0 * nsb, real ? (uint32_t)(rows * nsb * 2) : 0u);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int r = (lane >> 3) + 8 * q;
-            const int rr = r < rows ? r : rows - 1;
-            qv[buf][q] = __builtin_amdgcn_raw_buffer_load_b128(
-                crs, (int)(rr * row_bytes) + 128 * slice + 16 * (lane & 7), 0, kLoadNonTemporal);
-        }
-        const int rs = lane >> 2;
-        const int rsr = rs < rows ? rs : rows - 1;
-        sc[buf] = __builtin_amdgcn_raw_buffer_load_b16(srs, (rsr * nsb + slice * kSliceBlocks + (lane & 3)) * 2, 0,
+            buffer_rsrc(ld_codes + 128 * slice, live ? (uint32_t)(rows * row_bytes - 128 * slice) : 0u);
+        const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(ld_scales, live ? (uint32_t)(rows * nsb * 2) : 0u);
+        qv[buf][0] = __builtin_amdgcn_raw_buffer_load_b128(crs, c_off, 0, kLoadNonTemporal);
+        qv[buf][1] = __builtin_amdgcn_raw_buffer_load_b128(crs, c_off + 8 * row_bytes, 0, kLoadNonTemporal);
+        const int sblk = kSliceBlocks * slice + (lane & 3);
+        const int past = (nsb - 1 - sblk) >> 31;  // all ones past the row's end
+        sc[buf] = __builtin_amdgcn_raw_buffer_load_b16(srs, (s_row_off + 8 * slice) | (past & 0x7FFFFFF0), 0,
                                                        kLoadNonTemporal);
+        ++ld_unit;
+        if (XFIXED || ++ld_si == spw) {
+            ld_si = 0;
+            ld_codes += kTileRows * row_bytes;
+            ld_scales += kTileRows * nsb;
+            ld_rows -= kTileRows;
+        }
     };
 
     // Set-up: this wave's activations (when it keeps one slice for the whole
@@ -244,17 +263,24 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
     int rbuf = 0;
+    // Output of this thread in a tile's sum: token n = tid / 16, row
+    // tid % 16; it is register 4 (n / 16) + n % 4 of lane
+    // 16 ((n % 16) / 4) + row of every wave.
+    static_assert(NT * 256 <= 64 * nw, "one output per thread");
+    const int out_n = threadIdx.x >> 4, out_mm = threadIdx.x & 15;
+    const int out_v = 4 * (out_n >> 4) + (out_n & 3);
+    const int out_l = ((out_n & 15) >> 2) * 16 + out_mm;
+    const int64_t out_base = (int64_t)out_n * M + out_mm;
+    int cu_si = 0;               // slice index of the unit being consumed
+    int64_t cu_m0 = t_begin * kTileRows;  // first row of its tile
 
-    auto consume = [&](int buf, int64_t u) {
-        const int64_t ti = spw == 1 ? u : u / spw;
-        const int si = spw == 1 ? 0 : (int)(u - ti * spw);
-        const int slice = wave + nw * si;
+    auto consume = [&](int buf) {
         if (!XFIXED) {
             // Long rows: this slice's activations, regrouped through the
             // staging area's share of this wave; the reduction buffer shares
             // those bytes, so the workgroup first leaves the previous tile's
             // sum.
-            load_x_linear<NT>(xrs, K, nsb, slice, lin);
+            load_x_linear<NT>(xrs, K, nsb, wave + nw * cu_si, lin);
             __syncthreads();
             regroup_x<NT>(xs, lin, raw);
             convert_x_slice<NT>(raw, xa, inv);
@@ -262,13 +288,33 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
         }
         // Regroup the codes: lane (j, g) takes bytes 32b + 8g (8 bytes) of
         // row j for block b; the scale of row j, block b is held by lane
-        // 4j + b.
+        // 4j + b.  All lookups of the unit are issued before the first MFMA
+        // so the LDS latencies overlap.
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const u32x4_t v = qv[buf][q];
             cs[((lane >> 3) + 8 * q) * kCPitch + (lane & 7)] = make_uint4(v.x, v.y, v.z, v.w);
         }
         const char *crow = reinterpret_cast<const char *>(cs + j * kCPitch);
+        uint2 qw[kSliceBlocks];
+        float sb[kSliceBlocks];
+#pragma unroll
+        for (int b = 0; b < kSliceBlocks; ++b) {
+            qw[b] = *reinterpret_cast<const uint2 *>(crow + 32 * b + 8 * g);
+            sb[b] = f16_bits_to_f32(__shfl(sc[buf], 4 * j + b) & 0xFFFFu);
+        }
+        half8_t bop[kSliceBlocks][2];
+#pragma unroll
+        for (int b = 0; b < kSliceBlocks; ++b)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const uint32_t w = s ? qw[b].y : qw[b].x;
+                const half2_t p0 = lut_pair<0>(lut, w, laneoff);
+                const half2_t p1 = lut_pair<1>(lut, w, laneoff);
+                const half2_t p2 = lut_pair<2>(lut, w, laneoff);
+                const half2_t p3 = lut_pair<3>(lut, w, laneoff);
+                bop[b][s] = half8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+            }
         float part[NT][4];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -276,62 +322,49 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
             for (int r = 0; r < 4; ++r) part[t][r] = 0.0f;
 #pragma unroll
         for (int b = 0; b < kSliceBlocks; ++b) {
-            const int blk = slice * kSliceBlocks + b;
-            const uint32_t sbits = __shfl(sc[buf], 4 * j + b);
-            const float sb = blk < nsb ? f16_bits_to_f32(sbits & 0xFFFFu) : 0.0f;
-            const uint2 qw = *reinterpret_cast<const uint2 *>(crow + 32 * b + 8 * g);
             float4_t tile[NT];
 #pragma unroll
-            for (int t = 0; t < NT; ++t) tile[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const uint32_t w = s ? qw.y : qw.x;
-                const half2_t p0 = lut_pair<0>(lut, w, laneoff);
-                const half2_t p1 = lut_pair<1>(lut, w, laneoff);
-                const half2_t p2 = lut_pair<2>(lut, w, laneoff);
-                const half2_t p3 = lut_pair<3>(lut, w, laneoff);
-                const half8_t bop = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    tile[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][b][s], bop, tile[t], 0, 0, 0);
+            for (int t = 0; t < NT; ++t) {
+                tile[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][b][0], bop[b][0], float4_t{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                 0, 0, 0);
+                tile[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][b][1], bop[b][1], tile[t], 0, 0, 0);
             }
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) part[t][r] = fmaf(tile[t][r], sb, part[t][r]);
+                for (int r = 0; r < 4; ++r) part[t][r] = fmaf(tile[t][r], sb[b], part[t][r]);
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(part[t][r], inv[t][r], acc[t][r]);
 
-        if (si == spw - 1) {
+        if (XFIXED || ++cu_si == spw) {
+            cu_si = 0;
             // Tile complete for this wave: sum the waves' partial tiles.
+            float4_t *mine = reinterpret_cast<float4_t *>(&red[rbuf][wave][lane][0]);
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < NT; ++t) {
+                mine[t] = float4_t{acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    red[rbuf][wave][4 * t + r][lane] = acc[t][r];
-                    acc[t][r] = 0.0f;
-                }
+                for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
+            }
             __syncthreads();
-            const int64_t m0 = (t_begin + ti) * kTileRows;
-            for (int idx = threadIdx.x; idx < NT * 256; idx += blockDim.x) {
-                const int n = idx >> 4, mm = idx & 15;
-                const int t = n >> 4, r = n & 3;
-                const int l = ((n & 15) >> 2) * 16 + mm;
+            if (out_n < N) {
                 float sum = 0.0f;
-                for (int w = 0; w < nw; ++w) sum += red[rbuf][w][4 * t + r][l];
-                if (n < N && m0 + mm < M) Y[(int64_t)n * M + m0 + mm] = sum;
+#pragma unroll
+                for (int w = 0; w < nw; ++w) sum += red[rbuf][w][out_l][out_v];
+                if (cu_m0 + out_mm < M) Y[out_base + cu_m0] = sum;
             }
             rbuf ^= 1;
+            cu_m0 += kTileRows;
         }
     };
 
-    for (int64_t u0 = 0; u0 < nunits; u0 += S + 1) {
+    for (int u0 = 0; u0 < nunits; u0 += S + 1) {
 #pragma unroll
         for (int s = 0; s <= S; ++s) {
-            if (u0 + s < nunits) consume(s, u0 + s);
+            if (u0 + s < nunits) consume(s);
             load_unit(s);  // unit u0 + s + S + 1
         }
     }
@@ -348,15 +381,16 @@ hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int6
             n = 256;
         cus[dev] = n;
     }
-    // One workgroup per CU (the table and the reduction buffers take 96 KB of
-    // LDS), each with one wave per K slice (at most 8).
+    // One workgroup of 8 waves per CU (the table and the staging areas take
+    // 148 KB of LDS).  Chunks of up to 16 tokens take one MFMA per slab of
+    // weights, larger ones two.  Rows of up to 8 slices (K <= 2048) keep the
+    // activations in registers; longer rows reload them per tile.
     const int64_t tiles = (M + kTileRows - 1) / kTileRows;
     int64_t grid = tiles < cus[dev] ? tiles : cus[dev];
     if (grid < 1) grid = 1;
     int64_t tiles_q = tiles / grid;
     int tiles_rem = (int)(tiles % grid);
     const int nslices = (int)((K / 64 + kSliceBlocks - 1) / kSliceBlocks);
-    const int waves = nslices < kGemmMaxWaves ? nslices : kGemmMaxWaves;
     int k = (int)K, n = (int)N;
     void *args[] = {&codes, &scales, &M, &k, &X, &n, &Y, &tiles_q, &tiles_rem};
     const void *fn;
@@ -366,7 +400,7 @@ hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int6
     else
         fn = N <= 16 ? reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 0, false>)
                      : reinterpret_cast<const void *>(&gemm_smalln_kernel<2, 0, false>);
-    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)(64 * waves)), args, 0, stream);
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * kGemmMaxWaves), args, 0, stream);
 }
 
 }  // namespace q4
