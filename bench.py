@@ -1,6 +1,7 @@
 """Benchmark of the 4-bit codebook GEMV on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--copies R] [--no-secondary]
+                    [--secondary down,smalln,gateup]
 
 A step is one q4_gemv call on the lm_head workload (M x K = 151936 x 2048,
 x bf16 unit-RMS, y fp32): the projection the metric is quoted on.  Inputs are
@@ -36,7 +37,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 COPY_PROBE_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_lm_head_hbm_traffic.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "bit_weight_gemv_amd", "csrc", f) for f in ("q4_gemv.hip", "q4_device.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_weight_gemv_amd", "csrc", f)
+                  for f in ("q4_gemv.hip", "q4_lut.h", "q4_device.h")]
 
 
 def kernel_source_hash():
@@ -198,6 +200,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondary", default="down,smalln,gateup",
+                    help="comma-separated secondary workloads to time (down, smalln, gateup)")
     ap.add_argument("--eager", action="store_true",
                     help="also time the calls launched one by one from Python")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -259,7 +263,10 @@ def main():
     if not args.no_secondary:
         del reps
         torch.cuda.empty_cache()
+        chosen = [n.strip() for n in args.secondary.split(",") if n.strip()]
         for sname, ncopies, ntok in (("down", 50, None), ("smalln", 45, 32), ("gateup", 25, None)):
+            if sname not in chosen:
+                continue
             sc = wl.CONFIGS[sname]
             _, _, sreps, sx = prepare(torch, q4, wl, sname, dev, ncopies, n_tokens=ntok)
             if ntok is None:
