@@ -164,6 +164,35 @@ def time_graph(torch, fn, reps, steps, warmup):
     return ms, wall_ms
 
 
+def secondary_entry(sname, sc, N, g_ms, w_ms):
+    sb = gemv_bytes(sc["M"], sc["K"], N)
+    gbs = sb / (g_ms * 1e-3) / 1e9
+    log(f"{sname} N={N}: {g_ms * 1e3:.2f} us/call, {gbs:.0f} GB/s")
+    return {
+        "workload": f"{sname} {sc['M']}x{sc['K']} N={N}",
+        "us_per_call": round(g_ms * 1e3, 3),
+        "us_per_step_wall": round(w_ms * 1e3, 3),
+        "achieved_GBs": round(gbs, 1),
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "bytes": sb,
+    }
+
+
+def context_bandwidth(torch, dev, steps=20):
+    """Bandwidth context from a library-independent kernel: torch's device
+    copy of COPY_PROBE_BYTES, replayed as a graph; (read + written bytes) / s
+    in GB/s."""
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dsts = [torch.empty_like(src) for _ in range(2)]
+
+    def cp(d):
+        d.copy_(src)
+    ms, _ = time_graph(torch, cp, [(d,) for d in dsts], steps, 2)
+    del src, dsts
+    torch.cuda.empty_cache()
+    return 2 * COPY_PROBE_BYTES / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(oracle, wl, W, xb, name):
     """The oracle's fp64 GEMV over the whole matrix on the host cores, as it
     stands: rows split over threads, repeated until ~10 s have passed."""
@@ -282,16 +311,18 @@ def main():
                     q4.q4_gemm_smalln(cd, sl, sx, sy)
                 N = ntok
             sg, sw = time_graph(torch, sstep, sreps, args.steps, args.warmup)
-            sb = gemv_bytes(sc["M"], sc["K"], N)
-            secondary.append({
-                "workload": f"{sname} {sc['M']}x{sc['K']} N={N}",
-                "us_per_call": round(sg * 1e3, 3),
-                "us_per_step_wall": round(sw * 1e3, 3),
-                "achieved_GBs": round(sb / (sg * 1e-3) / 1e9, 1),
-                "frac_of_hbm_peak": round(sb / (sg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "bytes": sb,
-            })
-            log(f"{sname}: {sg * 1e3:.2f} us/call, {sb / (sg * 1e-3) / 1e9:.0f} GB/s")
+            secondary.append(secondary_entry(sname, sc, N, sg, sw))
+            if ntok is not None:
+                # The prefill sweep: the first n tokens of the same chunk.
+                for n in (16, 8, 4, 2, 1):
+                    sxn = sx[:n].contiguous()
+                    syn = torch.empty((n, sc["M"]), dtype=torch.float32, device=dev)
+
+                    def nstep(cd, sl, sxn=sxn, syn=syn):
+                        q4.q4_gemm_smalln(cd, sl, sxn, syn)
+                    ng, nw = time_graph(torch, nstep, sreps, args.steps, args.warmup)
+                    secondary.append(secondary_entry(sname, sc, n, ng, nw))
+                    del sxn, syn
             del sreps, sx, sy
             torch.cuda.empty_cache()
 
@@ -320,14 +351,23 @@ def main():
         "eager": eager,
         "secondary": secondary,
     }
+    if not args.no_secondary:
+        copy_gbs = context_bandwidth(torch, dev)
+        log(f"context: torch device copy {copy_gbs:.0f} GB/s (read + written)")
+        result["context"] = {
+            "torch_copy_GBs": round(copy_gbs, 1),
+            "lm_head_over_torch_copy": round(achieved / copy_gbs, 4),
+            "how": f"torch's {COPY_PROBE_BYTES >> 20} MiB device-to-device copy, graph-replayed"}
     if not args.no_cpu_baseline:
         import oracle
         oracle.build(force=False)
         cb, y_ref, S = cpu_baseline(oracle, wl, W, xb, name)
         result["cpu_baseline"] = cb
         ok, ratio = oracle.within_tolerance(y_gpu, y_ref, S)
+        top2 = np.sort(y_ref)[-2:]
         result["parity"] = {"within_tolerance": ok, "worst_ratio": round(ratio, 4),
-                            "argmax_gpu": oracle.argmax(y_gpu), "argmax_oracle": oracle.argmax(y_ref)}
+                            "argmax_gpu": oracle.argmax(y_gpu), "argmax_oracle": oracle.argmax(y_ref),
+                            "top2_gap_oracle": float(top2[1] - top2[0])}
     print(json.dumps(result), flush=True)
 
 

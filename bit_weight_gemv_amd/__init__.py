@@ -31,7 +31,7 @@ Q4_PACK_NONFINITE = 1
 Q4_PACK_OVERFLOW = 2
 
 EXPORTED = ("q4_codes_bytes", "q4_scales_bytes", "q4_codebook", "q4_status_string",
-            "q4_pack", "q4_gemv", "q4_gemm_smalln")
+            "q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln")
 
 _lib = None
 _lock = threading.Lock()
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.q4_status_string.restype = ctypes.c_char_p
         L.q4_pack.argtypes = [P, I64, I64, P, P, P, P]
         L.q4_pack.restype = I32
+        L.q4_unpack_canonical.argtypes = [P, P, I64, I64, P, P, P]
+        L.q4_unpack_canonical.restype = I32
         L.q4_gemv.argtypes = [P, P, I64, I64, P, P, P]
         L.q4_gemv.restype = I32
         L.q4_gemm_smalln.argtypes = [P, P, I64, I64, P, I64, P, P]
@@ -150,6 +152,26 @@ def _mk(codes, scales):
     _check(codes, "codes", torch.uint8, codes.device)
     _check(scales, "scales", torch.float16, codes.device)
     return M, K
+
+
+def q4_unpack_canonical(codes, scales, codes_out=None, scales_out=None, stream=None):
+    """The canonical layout of a packed matrix: (codes uint8 [M, K/2],
+    scales fp16 [M, K/64]) written into new (or the given) tensors."""
+    torch = _torch()
+    M, K = _mk(codes, scales)
+    if codes_out is None:
+        codes_out = torch.empty_like(codes)
+    if scales_out is None:
+        scales_out = torch.empty_like(scales)
+    _check(codes_out, "codes_out", torch.uint8, codes.device)
+    _check(scales_out, "scales_out", torch.float16, codes.device)
+    if codes_out.numel() != codes.numel() or scales_out.numel() != scales.numel():
+        raise ValueError("codes_out/scales_out do not match the packed matrix")
+    st = lib().q4_unpack_canonical(_ptr(codes), _ptr(scales), M, K, _ptr(codes_out), _ptr(scales_out),
+                                   _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_unpack_canonical")
+    return codes_out, scales_out
 
 
 def q4_gemv(codes, scales, x, y=None, stream=None):

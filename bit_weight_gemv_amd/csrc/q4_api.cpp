@@ -83,6 +83,26 @@ int q4_pack(const float *W, int64_t M, int64_t K, uint8_t *codes, uint16_t *scal
     return launch_status(q4::launch_pack(W, M, K, codes, scales, status, (hipStream_t)stream));
 }
 
+int q4_unpack_canonical(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K, uint8_t *codes_out,
+                        uint16_t *scales_out, void *stream) {
+    if (!shape_ok(M, K)) return Q4_ERR_SHAPE;
+    if (M == 0) return Q4_OK;
+    if (!codes || !scales || !codes_out || !scales_out) return Q4_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(codes_out, 16) || !aligned(scales_out, 2))
+        return Q4_ERR_ALIGN;
+    const uint64_t cb = (uint64_t)M * (K / 2), sb = (uint64_t)M * (K / 64) * 2;
+    const Range r[4] = {range_of(codes, cb), range_of(scales, sb), range_of(codes_out, cb),
+                        range_of(scales_out, sb)};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(r[i], r[j])) return Q4_ERR_OVERLAP;
+    // The device layout is the canonical layout: copy both arrays.
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(codes_out, codes, cb, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(scales_out, scales, sb, hipMemcpyDeviceToDevice, s);
+    return launch_status(e);
+}
+
 int q4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K, const uint16_t *x,
             float *y, void *stream) {
     if (!shape_ok(M, K)) return Q4_ERR_SHAPE;

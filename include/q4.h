@@ -98,6 +98,21 @@ int q4_pack(const float *W, int64_t M, int64_t K, uint8_t *codes,
             uint16_t *scales, int32_t *status, void *stream);
 
 /*
+ * q4_unpack_canonical -- write a packed matrix in the canonical layout
+ * described at the top of this file.  The library's device layout is the
+ * canonical one, so this is a device-to-device copy of both arrays on
+ * `stream`; it exists so that bit-exactness of q4_pack can always be judged
+ * on the canonical layout.
+ *   codes/scales: the packed matrix (codes 16-byte aligned, scales 2-byte).
+ *   codes_out: q4_codes_bytes(M,K) bytes, 16-byte aligned.
+ *   scales_out: q4_scales_bytes(M,K) bytes, 2-byte aligned.
+ * No two of the four ranges may overlap.
+ */
+int q4_unpack_canonical(const uint8_t *codes, const uint16_t *scales,
+                        int64_t M, int64_t K, uint8_t *codes_out,
+                        uint16_t *scales_out, void *stream);
+
+/*
  * q4_gemv -- y[m] = sum_k What[m,k] * x[k], m < M (the batch-1 decode
  * projection).
  *   codes/scales: a packed matrix (codes 16-byte aligned, scales 2-byte).

@@ -32,8 +32,8 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("q4_pack", "q4_gemv", "q4_gemm_smalln", "q4_codebook", "q4_codes_bytes",
-              "q4_scales_bytes", "q4_status_string"):
+    for n in ("q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_codebook",
+              "q4_codes_bytes", "q4_scales_bytes", "q4_status_string"):
         assert n in names
 
 
@@ -140,6 +140,24 @@ def test_pack_errors(q4):
     assert _pack(q4, A, 4, 64, A + 512, C, D) == q4.Q4_ERR_OVERLAP  # codes inside W (1 KB)
     assert _pack(q4, A, 4, 64, B, B + 64, D) == q4.Q4_ERR_OVERLAP   # scales inside codes
     assert _pack(q4, A, 4, 64, B, C, C + 4) == q4.Q4_ERR_OVERLAP    # status inside scales
+
+
+def _unpack(q4, codes, scales, M, K, co, so):
+    return q4.lib().q4_unpack_canonical(codes, scales, M, K, co, so, None)
+
+
+def test_unpack_errors(q4):
+    M, K = 4, 128  # codes 256 B, scales 16 B
+    assert _unpack(q4, A, B, 4, 100, C, D) == q4.Q4_ERR_SHAPE
+    assert _unpack(q4, None, None, 0, 64, None, None) == q4.Q4_OK
+    assert _unpack(q4, None, B, M, K, C, D) == q4.Q4_ERR_NULL
+    assert _unpack(q4, A, B, M, K, C, None) == q4.Q4_ERR_NULL
+    assert _unpack(q4, A + 8, B, M, K, C, D) == q4.Q4_ERR_ALIGN
+    assert _unpack(q4, A, B, M, K, C + 8, D) == q4.Q4_ERR_ALIGN
+    assert _unpack(q4, A, B, M, K, C, D + 1) == q4.Q4_ERR_ALIGN
+    assert _unpack(q4, A, B, M, K, A + 128, D) == q4.Q4_ERR_OVERLAP   # codes_out inside codes
+    assert _unpack(q4, A, B, M, K, C, B + 8) == q4.Q4_ERR_OVERLAP     # scales_out over scales
+    assert _unpack(q4, A, B, M, K, C, C + 16) == q4.Q4_ERR_OVERLAP    # scales_out inside codes_out
 
 
 def test_binding_refuses_without_library(tmp_path, monkeypatch):

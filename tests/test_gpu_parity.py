@@ -81,6 +81,20 @@ def test_pack_bit_exact_random(env, M, K):
     assert np.array_equal(cases.bits16(scales, env[0]), s_ref)
 
 
+@pytest.mark.parametrize("M,K", [(3, 128), (257, 512), (33, 11008)])
+def test_unpack_canonical_bit_exact(env, M, K):
+    torch, q4, dev = env
+    W = wl.weights(M, K, seed=700 + M + K)
+    c_ref, s_ref, _ = oracle.pack(W)
+    codes, scales, st = _gpu_pack(env, W)
+    assert st == 0
+    co, so = q4.q4_unpack_canonical(codes, scales)
+    torch.cuda.synchronize()
+    assert np.array_equal(co.cpu().numpy(), c_ref)
+    assert np.array_equal(cases.bits16(so, torch), s_ref)
+    assert co.data_ptr() != codes.data_ptr() and so.data_ptr() != scales.data_ptr()
+
+
 def test_pack_bit_exact_edge_blocks(env):
     W = cases.edge_matrix()
     c_ref, s_ref, st_ref = oracle.pack(W)
