@@ -73,6 +73,10 @@ def _load():
         lib.oracle_dequant.argtypes = [P, P, I64, I64, P]
         lib.oracle_gemv_rows.argtypes = [P, P, I64, I64, P, I64, I64, P, P]
         lib.oracle_gemm.argtypes = [P, P, I64, I64, P, I64, P, P]
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        lib.oracle_silu.restype = ctypes.c_double
+        lib.oracle_epilogue.argtypes = [P, P, P, P, P, I64, ctypes.c_int, P]
+        lib.oracle_epilogue.restype = None
         lib.oracle_argmax_f64.argtypes = [P, I64]
         lib.oracle_argmax_f64.restype = I64
         lib.oracle_argmax_f32.argtypes = [P, I64]
@@ -203,6 +207,39 @@ def gemm(codes, scales, M: int, K: int, X_bits):
     S = np.zeros((N, M), np.float64)
     _load().oracle_gemm(_ptr(codes), _ptr(scales), M, K, _ptr(X_bits), N, _ptr(Y), _ptr(S))
     return Y, S
+
+
+def silu(z: float) -> float:
+    """SiLU(z) = z / (1 + e^-z) in fp64."""
+    return float(_load().oracle_silu(float(z)))
+
+
+def epilogue(t0, t1=None, bias0=None, bias1=None, residual=None, swiglu: bool = False):
+    """The fused-projection epilogue in fp64 (see oracle_epilogue): t0, t1
+    fp64 products; bias0, bias1, residual fp32 or None."""
+    t0 = np.ascontiguousarray(t0, np.float64)
+    n = t0.size
+    if swiglu:
+        if t1 is None:
+            raise ValueError("oracle.epilogue: swiglu needs t1")
+        t1 = np.ascontiguousarray(t1, np.float64)
+        if t1.size != n:
+            raise ValueError("oracle.epilogue: t0 and t1 differ in length")
+
+    def f32(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a, np.float32)
+        if a.size != n:
+            raise ValueError("oracle.epilogue: bias/residual length differs from t0")
+        return a
+    b0, b1, r = f32(bias0), f32(bias1), f32(residual)
+    out = np.empty(n, np.float64)
+    nullp = ctypes.c_void_p(0)
+    _load().oracle_epilogue(_ptr(t0), _ptr(t1) if swiglu else nullp, _ptr(b0) if b0 is not None else nullp,
+                            _ptr(b1) if b1 is not None else nullp, _ptr(r) if r is not None else nullp,
+                            n, 1 if swiglu else 0, _ptr(out))
+    return out
 
 
 def argmax(y) -> int:

@@ -313,3 +313,26 @@ int64_t oracle_argmax_f32(const float *y, int64_t n) {
         if (!isnan(y[i]) && (best < 0 || y[i] > y[best])) best = i;
     return best;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Fused-projection epilogue (accel/tensor func Linear, func SiLU,           */
+/* func SwiGLU; deep-fold "Decode V2" bench notes).                          */
+/* ------------------------------------------------------------------------ */
+
+double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
+
+void oracle_epilogue(const double *t0, const double *t1, const float *bias0, const float *bias1,
+                     const float *residual, int64_t n, int swiglu, double *out) {
+    for (int64_t i = 0; i < n; ++i) {
+        double a = t0[i];
+        if (bias0) a += (double)bias0[i];
+        double v = a;
+        if (swiglu) {
+            double b = t1[i];
+            if (bias1) b += (double)bias1[i];
+            v = oracle_silu(a) * b;
+        }
+        if (residual) v += (double)residual[i];
+        out[i] = v;
+    }
+}

@@ -72,6 +72,24 @@ void oracle_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M,
 void oracle_gemm(const uint8_t *codes, const uint16_t *scales, int64_t M,
                  int64_t K, const uint16_t *X, int64_t N, double *Y, double *S);
 
+/* SiLU(z) = z * sigmoid(z) = z / (1 + e^-z), fp64 (golang.design accel/tensor
+ * page, func SiLU). */
+double oracle_silu(double z);
+
+/* The epilogue of a fused projection, fp64, for i < n (golang.design
+ * accel/tensor page: func Linear adds the bias to the product, func SwiGLU is
+ * SiLU(gate) * value; deep-fold "Decode V2" page, bench notes: q/k/v bias in
+ * the projection, silu(g) * u after the full reduction, residual added into
+ * y):
+ *   a = t0[i] + bias0[i]                        (bias0 may be NULL)
+ *   swiglu == 0: out[i] = a
+ *   swiglu != 0: out[i] = silu(a) * (t1[i] + bias1[i])   (bias1 may be NULL)
+ *   out[i] += residual[i]                       (residual may be NULL)
+ * bias and residual are fp32 values widened exactly. */
+void oracle_epilogue(const double *t0, const double *t1, const float *bias0,
+                     const float *bias1, const float *residual, int64_t n,
+                     int swiglu, double *out);
+
 /* First index of the maximum (NaN never wins); -1 if n == 0 or all NaN. */
 int64_t oracle_argmax_f64(const double *y, int64_t n);
 int64_t oracle_argmax_f32(const float *y, int64_t n);

@@ -35,6 +35,10 @@ MUTANTS = {
                         "if (!isnan(y[i]) && (best < 0 || y[i] >= y[best])) best = i;\n    return best;\n}\n\nint64_t oracle_argmax_f32"),
     "abs_sum_signed": ("mag += fabs(t);", "mag += t;"),
     "zero_block_code_0": ("code[k] = 7;\n                    continue;", "code[k] = 0;\n                    continue;"),
+    "silu_exponent_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "swiglu_operands_swapped": ("v = oracle_silu(a) * b;", "v = oracle_silu(b) * a;"),
+    "bias_after_silu": ("        double v = a;\n        if (swiglu) {", "        double v = a;\n        if (swiglu && bias0) a -= (double)bias0[i];\n        if (swiglu) {"),
+    "residual_dropped": ("if (residual) v += (double)residual[i];", "if (residual && !swiglu) v += (double)residual[i];"),
 }
 
 

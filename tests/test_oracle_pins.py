@@ -497,3 +497,75 @@ def test_within_tolerance_bound():
     assert not ok and r > 1
     ok, _ = oracle.within_tolerance([np.nan], np.array([1.0]), np.array([10.0]))
     assert not ok
+
+
+# --------------------------------------------------------------------------
+# Fused-projection epilogue: SiLU, SwiGLU, bias and residual
+# --------------------------------------------------------------------------
+
+def test_silu_odd_part_identity(oracle_mod):
+    # silu(z) - silu(-z) = z (sigma(z) + sigma(-z) = 1): fixes the sign of
+    # the exponent and which factor is the sigmoid.
+    for z in (0.25, 1.0, 2.5, -3.0, 7.0, 0.0):
+        assert abs((oracle_mod.silu(z) - oracle_mod.silu(-z)) - z) <= 4e-16 * max(1.0, abs(z))
+
+
+def test_silu_limits_and_minimum(oracle_mod):
+    assert oracle_mod.silu(0.0) == 0.0
+    assert oracle_mod.silu(40.0) == 40.0            # sigmoid(40) rounds to 1 in fp64
+    assert -1e-15 < oracle_mod.silu(-40.0) < 0.0    # -40 e^-40
+    # The minimum of z sigmoid(z) sits where 1 + z (1 - sigmoid z) = 0, i.e.
+    # sigmoid(z*) = 1 + 1/z*, so its value is v* = z* + 1 (z* about
+    # -1.27846).  The grid gives v* to O(h^2); z* = v* - 1 must then hit it.
+    zs = np.linspace(-1.4, -1.15, 25001)
+    v = np.array([oracle_mod.silu(z) for z in zs])
+    i = int(np.argmin(v))
+    assert 0 < i < zs.size - 1
+    z_star = v[i] - 1.0
+    assert abs(z_star + 1.2784645) < 2e-6
+    assert abs(oracle_mod.silu(z_star) - v[i]) < 1e-9
+
+
+def test_epilogue_exact_small_values(oracle_mod):
+    t0 = np.array([1.0, 2.0, 3.0, -4.0])
+    b0 = np.array([0.5, 0.25, -1.0, 0.0], np.float32)
+    r = np.array([0.0, -2.0, 8.0, 0.125], np.float32)
+    assert np.array_equal(oracle_mod.epilogue(t0), t0)
+    assert np.array_equal(oracle_mod.epilogue(t0, bias0=b0), [1.5, 2.25, 2.0, -4.0])
+    assert np.array_equal(oracle_mod.epilogue(t0, residual=r), [1.0, 0.0, 11.0, -3.875])
+    assert np.array_equal(oracle_mod.epilogue(t0, bias0=b0, residual=r), [1.5, 0.25, 10.0, -3.875])
+
+
+def test_swiglu_epilogue_structure(oracle_mod):
+    rng = np.random.default_rng(3)
+    g = rng.normal(size=64) * 3
+    u = rng.normal(size=64)
+    out = oracle_mod.epilogue(g, u, swiglu=True)
+    ones = oracle_mod.epilogue(g, np.ones(64), swiglu=True)
+    # value 1 gives silu(gate); the gate goes through SiLU, the value does not
+    assert np.array_equal(ones, [oracle_mod.silu(z) for z in g])
+    # linear in the value (powers of two are exact)
+    assert np.array_equal(oracle_mod.epilogue(g, 4 * u, swiglu=True), 4 * out)
+    # gate 0 gives 0 whatever the value
+    assert np.all(oracle_mod.epilogue(np.zeros(64), u, swiglu=True) == 0)
+    # biases act before SiLU / the product: shifting t by b equals adding b
+    b0 = np.full(64, 0.5, np.float32)
+    b1 = np.full(64, -0.25, np.float32)
+    assert np.array_equal(oracle_mod.epilogue(g, u, b0, b1, swiglu=True),
+                          oracle_mod.epilogue(g + 0.5, u - 0.25, swiglu=True))
+    # the residual is added after the product
+    r = np.full(64, 2.0, np.float32)
+    assert np.array_equal(oracle_mod.epilogue(g, u, residual=r, swiglu=True), out + 2.0)
+
+
+def test_swiglu_closed_form_on_constant_codes(oracle_mod):
+    # All codes 15 (level +1) with scale 1 and x = 1: every row of gate and
+    # up is K; silu(K) = K for K = 64 in fp64, so silu(g) * u = K * K.
+    M, K = 3, 64
+    codes = np.full((M, K // 2), 0xFF, np.uint8)
+    scales = np.full((M, K // 64), 0x3C00, np.uint16)   # fp16 1.0
+    x = np.full(K, 0x3F80, np.uint16)                    # bf16 1.0
+    g, _ = oracle_mod.gemv(codes, scales, M, K, x)
+    assert np.array_equal(g, [64.0] * M)
+    out = oracle_mod.epilogue(g, g, swiglu=True)
+    assert np.array_equal(out, [4096.0] * M)
