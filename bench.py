@@ -1,7 +1,7 @@
 """Benchmark of the 4-bit codebook GEMV on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--copies R] [--no-secondary]
-                    [--secondary down,smalln,gateup]
+                    [--secondary down,smalln,gateup,fused]
 
 A step is one q4_gemv call on the lm_head workload (M x K = 151936 x 2048,
 x bf16 unit-RMS, y fp32): the projection the metric is quoted on.  Inputs are
@@ -178,6 +178,98 @@ def secondary_entry(sname, sc, N, g_ms, w_ms):
     }
 
 
+# Fused decode projections (one x, the epilogue in the kernel) against the
+# same work unfused (q4_gemv per matrix, then torch's epilogue ops), both
+# graph-replayed over rotating copies.  Shapes of a decoder layer with
+# hidden 2048, 16 query and 2 key/value heads of 128, MLP width 11008.
+FUSED_WORKLOADS = {
+    "qkv_bias": dict(Ms=(2048, 256, 256), K=2048, seed=5, x="unit_rms", copies=220),
+    "gateup_swiglu": dict(Ms=(11008, 11008), K=2048, seed=2, x="unit_rms", copies=25),
+    "down_residual": dict(Ms=(2048,), K=11008, seed=1, x="swiglu", copies=50),
+}
+
+
+def fused_bytes(name, Ms, K):
+    w = sum(M * K // 2 + M * K // 32 for M in Ms) + 2 * K
+    if name == "qkv_bias":
+        return w + sum(8 * M for M in Ms)       # bias read + y written
+    if name == "gateup_swiglu":
+        return w + 4 * Ms[0]                     # y written
+    return w + 8 * Ms[0]                         # residual read + y written
+
+
+def fused_secondaries(torch, q4, wl, dev, steps, warmup):
+    out = []
+    for name, fc in FUSED_WORKLOADS.items():
+        Ms, K = fc["Ms"], fc["K"]
+        W = wl.weights(sum(Ms), K, fc["seed"])
+        Wd = torch.from_numpy(W).to(dev)
+        codes, scales, status = q4.q4_pack(Wd)
+        torch.cuda.synchronize()
+        if int(status.item()) != 0:
+            raise RuntimeError(f"q4_pack flagged the {name} weights")
+        del Wd, W
+        reps = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(fc["copies"] - 1)]
+        x = _upload_bits(torch, wl.activation(K, fc["seed"], fc["x"]), torch.bfloat16, dev)
+        g = torch.Generator(device="cpu").manual_seed(fc["seed"])
+        bias = [torch.randn(M, generator=g).to(dev) for M in Ms]
+        if name == "gateup_swiglu":
+            ys = [torch.empty(Ms[0], device=dev)]
+            yu = torch.empty(sum(Ms), device=dev)
+        else:
+            ys = [torch.empty(M, device=dev) for M in Ms]
+        res = torch.randn(Ms[0], generator=g).to(dev)
+
+        def split(cd, sl):
+            parts, r0 = [], 0
+            for M in Ms:
+                parts.append((cd[r0:r0 + M], sl[r0:r0 + M]))
+                r0 += M
+            return parts
+
+        if name == "qkv_bias":
+            def fused(cd, sl):
+                q4.q4_gemv_fused([(c, s, b) for (c, s), b in zip(split(cd, sl), bias)], x, "separate", ys)
+
+            def unfused(cd, sl):
+                for (c, s), b, y in zip(split(cd, sl), bias, ys):
+                    q4.q4_gemv(c, s, x, y)
+                    y.add_(b)
+        elif name == "gateup_swiglu":
+            def fused(cd, sl):
+                (cg, sg), (cu, su) = split(cd, sl)
+                q4.q4_gemv_fused([(cg, sg, None), (cu, su, None)], x, "swiglu", ys)
+
+            def unfused(cd, sl):
+                q4.q4_gemv(cd, sl, x, yu)  # gate and up as one [2M, K] GEMV
+                torch.mul(torch.nn.functional.silu(yu[:Ms[0]]), yu[Ms[0]:], out=ys[0])
+        else:
+            def fused(cd, sl):
+                q4.q4_gemv_fused([(cd, sl, None)], x, "separate", ys, [ys[0]])  # residual in place
+
+            def unfused(cd, sl):
+                q4.q4_gemv(cd, sl, x, res)
+                ys[0].add_(res)
+        f_ms, f_wall = time_graph(torch, fused, reps, steps, warmup)
+        u_ms, u_wall = time_graph(torch, unfused, reps, steps, warmup)
+        nb = fused_bytes(name, Ms, K)
+        gbs = nb / (f_ms * 1e-3) / 1e9
+        log(f"fused {name}: {f_ms * 1e3:.2f} us/call ({gbs:.0f} GB/s), unfused {u_ms * 1e3:.2f} us")
+        out.append({
+            "workload": f"fused {name} Ms={'+'.join(map(str, Ms))} K={K} N=1",
+            "us_per_call": round(f_ms * 1e3, 3),
+            "us_per_step_wall": round(f_wall * 1e3, 3),
+            "achieved_GBs": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes": nb,
+            "unfused_us_per_call": round(u_ms * 1e3, 3),
+            "speedup_vs_unfused": round(u_ms / f_ms, 3),
+        })
+        del reps, x, bias, ys, res
+        torch.cuda.empty_cache()
+    return out
+
+
 def context_bandwidth(torch, dev, steps=20):
     """Bandwidth context from a library-independent kernel: torch's device
     copy of COPY_PROBE_BYTES, replayed as a graph; (read + written bytes) / s
@@ -229,8 +321,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--secondary", default="down,smalln,gateup",
-                    help="comma-separated secondary workloads to time (down, smalln, gateup)")
+    ap.add_argument("--secondary", default="down,smalln,gateup,fused",
+                    help="comma-separated secondary workloads to time (down, smalln, gateup, fused)")
     ap.add_argument("--eager", action="store_true",
                     help="also time the calls launched one by one from Python")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -325,6 +417,8 @@ def main():
                     del sxn, syn
             del sreps, sx, sy
             torch.cuda.empty_cache()
+        if "fused" in chosen:
+            secondary.extend(fused_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
 
     result = {
         "metric": "4-bit GEMV us/call + achieved HBM GB/s (% of peak), MxK=151936x2048, N=1",

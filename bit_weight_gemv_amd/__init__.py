@@ -31,7 +31,18 @@ Q4_PACK_NONFINITE = 1
 Q4_PACK_OVERFLOW = 2
 
 EXPORTED = ("q4_codes_bytes", "q4_scales_bytes", "q4_codebook", "q4_status_string",
-            "q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln")
+            "q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused")
+
+Q4_MAX_FUSED = 4
+Q4_MAX_FUSED_K = 16384
+Q4_FUSE_SEPARATE = 0
+Q4_FUSE_SWIGLU = 1
+
+
+class Operand(ctypes.Structure):
+    """q4_operand of include/q4.h."""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("M", ctypes.c_int64),
+                ("bias", ctypes.c_void_p)]
 
 _lib = None
 _lock = threading.Lock()
@@ -69,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.q4_gemv.restype = I32
         L.q4_gemm_smalln.argtypes = [P, P, I64, I64, P, I64, P, P]
         L.q4_gemm_smalln.restype = I32
+        L.q4_gemv_fused.argtypes = [P, I32, I64, P, I32, P, P, P]
+        L.q4_gemv_fused.restype = I32
         _lib = L
         return L
 
@@ -209,3 +222,59 @@ def q4_gemm_smalln(codes, scales, X, Y=None, stream=None):
     if st != Q4_OK:
         raise Q4Error(st, "q4_gemm_smalln")
     return Y
+
+
+def q4_gemv_fused(ops, x, mode="separate", ys=None, residuals=None, stream=None):
+    """Several products of one bf16 x [K] in one launch.  ops: list of
+    (codes, scales, bias or None).  mode "separate": returns [y_i] with
+    y_i = W_i . x + bias_i (+ residuals[i]); mode "swiglu" (two ops, gate then
+    up): returns [y] with y = silu(W_0 . x + b_0) * (W_1 . x + b_1)
+    (+ residuals[0]).  residuals: None or a list of fp32 tensors / None; an
+    entry may be the output tensor itself (in-place add)."""
+    torch = _torch()
+    if mode not in ("separate", "swiglu"):
+        raise ValueError("mode must be 'separate' or 'swiglu'")
+    n = len(ops)
+    arr = (Operand * max(n, 1))()
+    K = None
+    keep = []
+    for i, (codes, scales, bias) in enumerate(ops):
+        M, Ki = _mk(codes, scales)
+        if K is not None and Ki != K:
+            raise ValueError("all matrices must have the same K")
+        K = Ki
+        if bias is not None:
+            _check(bias, f"bias[{i}]", torch.float32, codes.device)
+            if bias.numel() != M:
+                raise ValueError(f"bias[{i}] must have M={M} entries")
+        arr[i] = Operand(codes.data_ptr(), scales.data_ptr(), M, bias.data_ptr() if bias is not None else 0)
+        keep.append((codes, scales, bias))
+    dev = ops[0][0].device
+    _check(x, "x", torch.bfloat16, dev)
+    if x.numel() != K:
+        raise ValueError(f"x must have K={K} entries")
+    nout = 1 if mode == "swiglu" else n
+    if ys is None:
+        ys = [torch.empty(ops[i][0].shape[0], dtype=torch.float32, device=dev) for i in range(nout)]
+    if len(ys) != nout or (residuals is not None and len(residuals) != nout):
+        raise ValueError(f"mode {mode!r} with {n} matrices has {nout} outputs")
+    for i, yv in enumerate(ys):
+        _check(yv, f"y[{i}]", torch.float32, dev)
+        if yv.numel() != ops[i][0].shape[0]:
+            raise ValueError(f"y[{i}] must have M={ops[i][0].shape[0]} entries")
+    yp = (ctypes.c_void_p * nout)(*[yv.data_ptr() for yv in ys])
+    rp = None
+    if residuals is not None:
+        rp = (ctypes.c_void_p * nout)(*[(r.data_ptr() if r is not None else 0) for r in residuals])
+        for i, r in enumerate(residuals):
+            if r is not None:
+                _check(r, f"residual[{i}]", torch.float32, dev)
+                if r.numel() != ys[i].numel():
+                    raise ValueError(f"residual[{i}] must have as many entries as y[{i}]")
+    st = lib().q4_gemv_fused(ctypes.cast(arr, ctypes.c_void_p), n, K, _ptr(x),
+                             Q4_FUSE_SWIGLU if mode == "swiglu" else Q4_FUSE_SEPARATE,
+                             ctypes.cast(yp, ctypes.c_void_p), ctypes.cast(rp, ctypes.c_void_p) if rp is not None else None,
+                             _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_gemv_fused")
+    return ys

@@ -15,6 +15,7 @@
 
 namespace {
 
+// (A null pointer counts as aligned.)
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 struct Range {
@@ -130,6 +131,64 @@ int q4_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M, int6
         overlap(ry, range_of(X, (uint64_t)N * K * 2)))
         return Q4_ERR_OVERLAP;
     return launch_status(q4::launch_gemm_smalln(codes, scales, M, K, X, N, Y, (hipStream_t)stream));
+}
+
+int q4_gemv_fused(const q4_operand *ops, int count, int64_t K, const uint16_t *x, int mode, float *const *y,
+                  const float *const *residual, void *stream) {
+    if (mode != Q4_FUSE_SEPARATE && mode != Q4_FUSE_SWIGLU) return Q4_ERR_SHAPE;
+    if (count < 1 || count > Q4_MAX_FUSED) return Q4_ERR_SHAPE;
+    if (mode == Q4_FUSE_SWIGLU && count != 2) return Q4_ERR_SHAPE;
+    if (!ops) return Q4_ERR_NULL;
+    if (!shape_ok(0, K) || K > Q4_MAX_FUSED_K) return Q4_ERR_SHAPE;
+    for (int i = 0; i < count; ++i)
+        if (!shape_ok(ops[i].M, K)) return Q4_ERR_SHAPE;
+    if (mode == Q4_FUSE_SWIGLU && ops[0].M != ops[1].M) return Q4_ERR_SHAPE;
+    const int nout = mode == Q4_FUSE_SWIGLU ? 1 : count;
+    bool any = false;
+    for (int i = 0; i < count; ++i) any = any || ops[i].M > 0;
+    if (!any) return Q4_OK;
+    if (!x || !y) return Q4_ERR_NULL;
+    if (!aligned(x, 16)) return Q4_ERR_ALIGN;
+    // Inputs (read only; they may overlap each other).
+    Range in[3 * Q4_MAX_FUSED + 1];
+    int nin = 0;
+    in[nin++] = range_of(x, (uint64_t)K * 2);
+    for (int i = 0; i < count; ++i) {
+        if (ops[i].M == 0) continue;
+        if (!ops[i].codes || !ops[i].scales) return Q4_ERR_NULL;
+        if (!aligned(ops[i].codes, 16) || !aligned(ops[i].scales, 2) || !aligned(ops[i].bias, 4))
+            return Q4_ERR_ALIGN;
+        in[nin++] = range_of(ops[i].codes, (uint64_t)ops[i].M * (K / 2));
+        in[nin++] = range_of(ops[i].scales, (uint64_t)ops[i].M * (K / 64) * 2);
+        if (ops[i].bias) in[nin++] = range_of(ops[i].bias, (uint64_t)ops[i].M * 4);
+    }
+    // Output o has ops[o].M floats (for SWIGLU, the common M).
+    Range out[Q4_MAX_FUSED], res[Q4_MAX_FUSED];
+    for (int o = 0; o < nout; ++o) {
+        const uint64_t n = (uint64_t)ops[o].M * 4;
+        const float *r = residual ? residual[o] : nullptr;
+        out[o] = range_of(y[o], n);
+        res[o] = range_of(r, r ? n : 0);
+        if (n == 0) continue;
+        if (!y[o]) return Q4_ERR_NULL;
+        if (!aligned(y[o], 4) || !aligned(r, 4)) return Q4_ERR_ALIGN;
+    }
+    for (int o = 0; o < nout; ++o) {
+        if (ops[o].M == 0) continue;
+        for (int i = 0; i < nin; ++i)
+            if (overlap(out[o], in[i])) return Q4_ERR_OVERLAP;
+        // The residual may be the output itself, exactly; nothing else may
+        // overlap an output.
+        if (res[o].lo != out[o].lo && overlap(res[o], out[o])) return Q4_ERR_OVERLAP;
+        for (int p = 0; p < nout; ++p) {
+            if (p == o || ops[p].M == 0) continue;
+            if (overlap(out[o], out[p]) || overlap(out[o], res[p])) return Q4_ERR_OVERLAP;
+        }
+    }
+    q4::FusedOperand fo[Q4_MAX_FUSED];
+    for (int i = 0; i < count; ++i) fo[i] = {ops[i].codes, ops[i].scales, ops[i].M, ops[i].bias};
+    return launch_status(
+        q4::launch_gemv_fused(fo, count, mode == Q4_FUSE_SWIGLU, K, x, y, residual, (hipStream_t)stream));
 }
 
 }  // extern "C"

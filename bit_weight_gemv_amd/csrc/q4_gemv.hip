@@ -159,13 +159,45 @@ __device__ __forceinline__ float convert_x(Load load, uint32_t (&raw)[16], half2
 constexpr int gemv_min_waves(int cpl) { return cpl == 1 ? 4 : 2; }
 constexpr int gemv_max_block(bool multi, int cpl) { return (multi || cpl > 1) ? 512 : 1024; }
 
-template <int NR, int CPL, int S, int RG, bool MULTI>
-__global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
-                          amdgpu_waves_per_eu(gemv_min_waves(CPL), 8))) void gemv_kernel(const uint8_t *__restrict__ codes,
-                                                   const uint16_t *__restrict__ scales, int64_t M,
-                                                   int K, const uint16_t *__restrict__ x,
-                                                   float *__restrict__ y, int P, int64_t rows_q,
-                                                   int rows_rem) {
+// SiLU(z) = z * sigmoid(z) = z / (1 + e^-z) (golang.design accel/tensor,
+// func SiLU), fp32.
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+// One output segment of a launch.  The plain and affine forms read one
+// matrix (codes0/scales0); the SwiGLU form reads a gate matrix (codes0) and
+// an up matrix (codes1) of the same shape and writes silu(gate . x + bias0)
+// times (up . x + bias1).  Optional fp32 epilogue operands may be null.  The
+// host splits the segment's rows over its own range of workgroups.
+struct GemvSeg {
+    const uint8_t *codes0;
+    const uint16_t *scales0;
+    const uint8_t *codes1;
+    const uint16_t *scales1;
+    const float *bias0;
+    const float *bias1;
+    const float *residual;
+    float *y;
+    int64_t rows;      // outputs of the segment
+    int64_t rows_q;    // rows per lane group (quotient)
+    int32_t rows_rem;  // groups with one more row
+    int32_t wg_begin;  // first workgroup of the segment
+};
+constexpr int kMaxSegs = 4;
+struct GemvSegs {
+    GemvSeg s[kMaxSegs];
+    int32_t n;
+};
+enum { kModePlain = 0, kModeAffine = 1, kModeSwiglu = 2 };
+
+// The GEMV of one segment by one workgroup (index `wg` within the segment).
+// MODE kModePlain: y = W . x.  kModeAffine: y = W . x (+ bias0) (+ residual).
+// kModeSwiglu: each tile holds NR/2 gate rows and the NR/2 up rows of the
+// same outputs; after the full reduction lane pairs are brought together and
+// y = silu(g (+ bias0)) * (u (+ bias1)) (+ residual) -- SiLU only ever sees
+// a finished sum (deep-fold "Decode V2" page, bench notes).
+template <int NR, int CPL, int S, int RG, bool MULTI, int MODE>
+__device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16_t *__restrict__ x, int P,
+                                          int64_t wg) {
     __shared__ uint32_t lut[kLutDwords];
     __shared__ float red[kMaxWavesPerGroup][RG];
     // Groups of one wave all need the whole activation vector: it is read
@@ -173,13 +205,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
     // lane) and every wave takes its chunks from there.
     __shared__ uint4 xs[MULTI ? 1 : kSharedXUnits];
 
+    static_assert(MODE != kModeSwiglu || NR % 2 == 0, "a SwiGLU tile pairs gate and up rows");
+    constexpr int LPT = MODE == kModeSwiglu ? NR / 2 : NR;  // outputs per tile
+    const int64_t rows_q = sg.rows_q;
+    const int rows_rem = sg.rows_rem;
+
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // A group is one wave (MULTI == false) or the whole workgroup.
     const int wpg = MULTI ? (P >> 6) : 1;     // waves per group
     const int wig = MULTI ? wave : 0;         // wave within its group
     const int lig = wig * 64 + lane;          // lane within its group
-    const int64_t gid = MULTI ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+    const int64_t gid = MULTI ? wg : wg * (blockDim.x >> 6) + wave;
     const int C = K >> 5;                      // 16-byte chunks per row
     const int nsb = K >> 6;                    // scale blocks per row
     const int64_t row_bytes = K >> 1;
@@ -187,7 +224,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
     // more for the first rows_rem groups (no division on the device).
     const int64_t r_begin = gid * rows_q + (gid < rows_rem ? gid : rows_rem);
     const int64_t r_end = r_begin + rows_q + (gid < rows_rem ? 1 : 0);
-    const int64_t ntiles = (r_end - r_begin + NR - 1) / NR;
+    const int64_t ntiles = (r_end - r_begin + LPT - 1) / LPT;
 
     // Chunk indices of this lane.  Lanes past the row's end load a valid
     // chunk (the last one) and multiply it by zero activations, so every load
@@ -207,40 +244,54 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
 
     uint4 q[S + 1][NR][CPL];
     uint32_t sc[S + 1][NR][CPL];
-    // Tiles are loaded in order.  The next tile to load starts at row
-    // r_begin + NR * (tiles loaded so far); its pointers advance by one tile
+    // Tiles are loaded in order.  The next tile to load starts at output
+    // r_begin + LPT * (tiles loaded so far); its pointers advance by one tile
     // per load.  Rows past r_end repeat the last valid row (their results are
     // not stored), so every access stays inside the matrix.  A tile past the
     // last one is loaded through a buffer resource of zero records: the loads
     // stay unconditional (no register merges in the ring) but return zeros
-    // without touching memory.
-    const uint8_t *next_codes = codes + r_begin * row_bytes;
-    const uint16_t *next_scales = scales + r_begin * nsb;
-    int64_t next_left = r_end - r_begin;  // rows from the next tile to r_end
+    // without touching memory.  In the SwiGLU form rows LPT.. of a tile are
+    // the up rows of rows 0..LPT-1 and come from the up matrix.
+    const uint8_t *next_codes0 = sg.codes0 + r_begin * row_bytes;
+    const uint16_t *next_scales0 = sg.scales0 + r_begin * nsb;
+    const uint8_t *next_codes1 = MODE == kModeSwiglu ? sg.codes1 + r_begin * row_bytes : nullptr;
+    const uint16_t *next_scales1 = MODE == kModeSwiglu ? sg.scales1 + r_begin * nsb : nullptr;
+    int64_t next_left = r_end - r_begin;  // outputs from the next tile to r_end
     auto load_tile = [&](int buf) {
         const bool real = next_left > 0;
-        const int nvalid = next_left < NR ? (int)next_left : NR;
-        const __amdgpu_buffer_rsrc_t crs =
-            buffer_rsrc(next_codes, real ? (uint32_t)(NR * row_bytes) : 0u);
-        const __amdgpu_buffer_rsrc_t srs =
-            buffer_rsrc(next_scales, real ? (uint32_t)(NR * nsb * 2) : 0u);
+        const int nvalid = next_left < LPT ? (int)next_left : LPT;
+        const __amdgpu_buffer_rsrc_t crs0 =
+            buffer_rsrc(next_codes0, real ? (uint32_t)(LPT * row_bytes) : 0u);
+        const __amdgpu_buffer_rsrc_t srs0 =
+            buffer_rsrc(next_scales0, real ? (uint32_t)(LPT * nsb * 2) : 0u);
+        __amdgpu_buffer_rsrc_t crs1 = crs0, srs1 = srs0;
+        if constexpr (MODE == kModeSwiglu) {
+            crs1 = buffer_rsrc(next_codes1, real ? (uint32_t)(LPT * row_bytes) : 0u);
+            srs1 = buffer_rsrc(next_scales1, real ? (uint32_t)(LPT * nsb * 2) : 0u);
+        }
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const int rr = r < nvalid ? r : (nvalid > 0 ? nvalid - 1 : 0);
+            const int lr = r % LPT;
+            const int rr = lr < nvalid ? lr : (nvalid > 0 ? nvalid - 1 : 0);
+            const bool up = MODE == kModeSwiglu && r >= LPT;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 // Weights are read once: non-temporal loads keep them from
                 // displacing reusable lines.
                 const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
-                    crs, (int)coff[i], (int)(rr * row_bytes), kLoadNonTemporal);
+                    up ? crs1 : crs0, (int)coff[i], (int)(rr * row_bytes), kLoadNonTemporal);
                 q[buf][r][i] = make_uint4(v.x, v.y, v.z, v.w);
-                sc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(srs, (int)(soff[i] * 2),
+                sc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(up ? srs1 : srs0, (int)(soff[i] * 2),
                                                                       rr * nsb * 2, kLoadNonTemporal);
             }
         }
-        next_codes += NR * row_bytes;
-        next_scales += NR * nsb;
-        next_left -= NR;
+        next_codes0 += LPT * row_bytes;
+        next_scales0 += LPT * nsb;
+        if constexpr (MODE == kModeSwiglu) {
+            next_codes1 += LPT * row_bytes;
+            next_scales1 += LPT * nsb;
+        }
+        next_left -= LPT;
     };
 
     // Set-up order: activation loads, then the first weight tiles, then the
@@ -304,26 +355,89 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
         load_tile(buf);  // tile t + S + 1
     };
 
+    // Store of a reduction group whose first tile is g0; lane l holds the
+    // finished sum of group row l (l < RG).  Every lane of the wave calls it.
     const int64_t nrows = r_end - r_begin;
+    auto store = [&](float tot, int64_t g0) {
+        if constexpr (MODE == kModeSwiglu) {
+            // Output o of the group: tile o / LPT, gate row o % LPT of it and
+            // the up row LPT after.
+            const int o = lane < RG / 2 ? lane : 0;
+            const int gate_lane = (o / LPT) * NR + o % LPT;
+            const float g = __shfl(tot, gate_lane);
+            const float u = __shfl(tot, gate_lane + LPT);
+            const int64_t local = g0 * LPT + lane;
+            if (lane < RG / 2 && local < nrows) {
+                const int64_t row = r_begin + local;
+                const float a = sg.bias0 ? g + sg.bias0[row] : g;
+                const float b = sg.bias1 ? u + sg.bias1[row] : u;
+                float v = silu_f(a) * b;
+                if (sg.residual) v += sg.residual[row];
+                sg.y[row] = v;
+            }
+        } else {
+            const int64_t local = g0 * NR + lane;  // row index within the range
+            if (lane < RG && local < nrows) {
+                const int64_t row = r_begin + local;
+                float v = tot;
+                if (MODE == kModeAffine && sg.bias0) v += sg.bias0[row];
+                if (MODE == kModeAffine && sg.residual) v += sg.residual[row];
+                sg.y[row] = v;
+            }
+        }
+    };
+
     for (int64_t g0 = 0; g0 < ntiles; g0 += TPG) {
 #pragma unroll
         for (int j = 0; j < TPG; ++j) step(j % (S + 1), j, g0 + j);
         // Lane l now holds the wave's total of group row (l % RG).
         const float tot = reduce_rows<RG>(acc) * down;
-        const int64_t local = g0 * NR + lane;  // row index within the range
         if (!MULTI) {
-            if (lane < RG && local < nrows) y[r_begin + local] = tot;
+            store(tot, g0);
         } else {
             if (lane < RG) red[wig][lane] = tot;
             __syncthreads();
-            if (wig == 0 && lane < RG && local < nrows) {
+            if (wig == 0) {
                 float sum = 0.0f;
-                for (int w = 0; w < wpg; ++w) sum += red[w][lane];
-                y[r_begin + local] = sum;
+                if (lane < RG)
+                    for (int w = 0; w < wpg; ++w) sum += red[w][lane];
+                store(sum, g0);
             }
             __syncthreads();
         }
     }
+}
+
+template <int NR, int CPL, int S, int RG, bool MULTI>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
+                          amdgpu_waves_per_eu(gemv_min_waves(CPL), 8))) void gemv_kernel(const uint8_t *__restrict__ codes,
+                                                   const uint16_t *__restrict__ scales, int64_t M,
+                                                   int K, const uint16_t *__restrict__ x,
+                                                   float *__restrict__ y, int P, int64_t rows_q,
+                                                   int rows_rem) {
+    GemvSeg sg{};
+    sg.codes0 = codes;
+    sg.scales0 = scales;
+    sg.y = y;
+    sg.rows = M;
+    sg.rows_q = rows_q;
+    sg.rows_rem = rows_rem;
+    gemv_body<NR, CPL, S, RG, MULTI, kModePlain>(sg, K, x, P, (int64_t)blockIdx.x);
+}
+
+// Several segments in one launch: workgroup b belongs to the last segment
+// whose first workgroup is <= b.
+template <int NR, int CPL, int S, int RG, bool MULTI, int MODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
+                          amdgpu_waves_per_eu(gemv_min_waves(CPL), 8))) void gemv_fused_kernel(GemvSegs segs, int K,
+                                                   const uint16_t *__restrict__ x, int P) {
+    int si = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxSegs; ++i)
+        if (i < segs.n && (int)blockIdx.x >= segs.s[i].wg_begin) si = i;
+    si = __builtin_amdgcn_readfirstlane(si);
+    const GemvSeg &sg = segs.s[si];
+    gemv_body<NR, CPL, S, RG, MULTI, MODE>(sg, K, x, P, (int64_t)blockIdx.x - sg.wg_begin);
 }
 
 namespace {
@@ -364,7 +478,108 @@ int64_t gemv_grid(int64_t tiles, int G) {
     return grid < 1 ? 1 : grid;
 }
 
+// Workgroups per segment (in proportion to its tiles of `lpt` outputs, G
+// groups per workgroup, one pass over two workgroups per CU) and each
+// segment's row split.  Returns the grid; *tpg gets the largest number of
+// tiles a lane group walks.
+int64_t plan_segments(GemvSegs &segs, int lpt, int G, int64_t *tpg) {
+    const int64_t cap = 2LL * cu_count();
+    int64_t wg[kMaxSegs], total = 0;
+    for (int i = 0; i < segs.n; ++i) {
+        const int64_t tiles = (segs.s[i].rows + lpt - 1) / lpt;
+        wg[i] = (tiles + G - 1) / G;
+        if (wg[i] < 1) wg[i] = 1;
+        total += wg[i];
+    }
+    if (total > cap)
+        for (int i = 0; i < segs.n; ++i) {
+            wg[i] = wg[i] * cap / total;
+            if (wg[i] < 1) wg[i] = 1;
+        }
+    int64_t begin = 0, most = 0;
+    for (int i = 0; i < segs.n; ++i) {
+        const int64_t groups = wg[i] * G;
+        segs.s[i].rows_q = segs.s[i].rows / groups;
+        segs.s[i].rows_rem = (int32_t)(segs.s[i].rows % groups);
+        segs.s[i].wg_begin = (int32_t)begin;
+        const int64_t per = segs.s[i].rows_q + (segs.s[i].rows_rem ? 1 : 0);
+        const int64_t t = (per + lpt - 1) / lpt;
+        if (t > most) most = t;
+        begin += wg[i];
+    }
+    *tpg = most;
+    return begin;
+}
+
+template <int NR, int CPL, int S, int RG, bool MULTI, int MODE>
+hipError_t launch_fused_variant(GemvSegs segs, int K, const uint16_t *x, int P, int G, int64_t grid,
+                                hipStream_t stream) {
+    if (!MULTI && (K / 8 > P * G || K / 8 > kSharedXUnits)) return hipErrorInvalidValue;
+    void *args[] = {&segs, &K, &x, &P};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_fused_kernel<NR, CPL, S, RG, MULTI, MODE>),
+                           dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
+}
+
+// The variant for the row length, as launch_gemv chooses it (rows of up to
+// 512 chunks, K <= 16384).
+template <int MODE>
+hipError_t launch_fused_mode(GemvSegs segs, int K, const uint16_t *x, hipStream_t stream) {
+    const int C = K / kChunkWeights;
+    constexpr int half = MODE == kModeSwiglu ? 2 : 1;  // rows per output
+    int64_t tpg = 0;
+    if (C <= 64) {
+        const int64_t grid = plan_segments(segs, 4 / half, 8, &tpg);
+        if (tpg <= 2) return launch_fused_variant<4, 1, 0, 4, false, MODE>(segs, K, x, 64, 8, grid, stream);
+        return launch_fused_variant<4, 1, 1, 8, false, MODE>(segs, K, x, 64, 8, grid, stream);
+    }
+    if (C <= 128) {
+        const int64_t grid = plan_segments(segs, 2 / half, 8, &tpg);
+        return launch_fused_variant<2, 2, 1, 16, false, MODE>(segs, K, x, 64, 8, grid, stream);
+    }
+    if (C <= 64 * kMaxWavesPerGroup) {
+        const int P = ((C + 63) / 64) * 64;
+        const int64_t grid = plan_segments(segs, 4 / half, 1, &tpg);
+        if (tpg <= 2) return launch_fused_variant<4, 1, 0, 4, true, MODE>(segs, K, x, P, 1, grid, stream);
+        return launch_fused_variant<4, 1, 1, 8, true, MODE>(segs, K, x, P, 1, grid, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_gemv_fused(const FusedOperand *ops, int count, bool swiglu, int64_t K, const uint16_t *x,
+                             float *const *y, const float *const *residual, hipStream_t stream) {
+    GemvSegs segs{};
+    if (swiglu) {
+        if (count != 2 || ops[0].M != ops[1].M) return hipErrorInvalidValue;
+        if (ops[0].M == 0) return hipSuccess;
+        GemvSeg &g = segs.s[0];
+        g.codes0 = ops[0].codes;
+        g.scales0 = ops[0].scales;
+        g.bias0 = ops[0].bias;
+        g.codes1 = ops[1].codes;
+        g.scales1 = ops[1].scales;
+        g.bias1 = ops[1].bias;
+        g.residual = residual ? residual[0] : nullptr;
+        g.y = y[0];
+        g.rows = ops[0].M;
+        segs.n = 1;
+        return launch_fused_mode<kModeSwiglu>(segs, (int)K, x, stream);
+    }
+    if (count < 1 || count > kMaxSegs) return hipErrorInvalidValue;
+    for (int i = 0; i < count; ++i) {
+        if (ops[i].M == 0) continue;
+        GemvSeg &g = segs.s[segs.n++];
+        g.codes0 = ops[i].codes;
+        g.scales0 = ops[i].scales;
+        g.bias0 = ops[i].bias;
+        g.residual = residual ? residual[i] : nullptr;
+        g.y = y[i];
+        g.rows = ops[i].M;
+    }
+    if (segs.n == 0) return hipSuccess;
+    return launch_fused_mode<kModeAffine>(segs, (int)K, x, stream);
+}
 
 // Variant choice.  Every variant reads tiles of 4 rows (2 for 2-chunk
 // lanes).  Where a lane group gets at most two tiles (the whole matrix fits

@@ -12,6 +12,20 @@ hipError_t launch_pack(const float *W, int64_t M, int64_t K, uint8_t *codes, uin
 hipError_t launch_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                        const uint16_t *x, float *y, hipStream_t stream);
 
+// One matrix of a fused GEMV launch (sharing x with the others).
+struct FusedOperand {
+    const uint8_t *codes;
+    const uint16_t *scales;
+    int64_t M;
+    const float *bias;  // or null
+};
+
+// count matrices (at most 4) into y[i] (+ residual[i]), or, with swiglu,
+// silu(W0 . x + b0) * (W1 . x + b1) (+ residual[0]) into y[0] (count == 2,
+// equal M).  K <= 16384.  Arguments are validated by the caller.
+hipError_t launch_gemv_fused(const FusedOperand *ops, int count, bool swiglu, int64_t K, const uint16_t *x,
+                             float *const *y, const float *const *residual, hipStream_t stream);
+
 hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                               const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
 

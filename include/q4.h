@@ -137,6 +137,48 @@ int q4_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M,
                    int64_t K, const uint16_t *X, int64_t N, float *Y,
                    void *stream);
 
+/*
+ * Fused decode projections (deep-fold "Decode V2" page, bench notes: one
+ * grid over the q, k and v rows sharing x with the q/k/v bias added in that
+ * kernel; gate/up pairs writing silu(g) * u, SiLU only after the full
+ * reduction; the o/down residual added into y; golang.design accel/tensor:
+ * func Linear adds its bias in the product's kernel, func SwiGLU is
+ * SiLU(gate) * value).
+ */
+#define Q4_MAX_FUSED 4           /* matrices per q4_gemv_fused call          */
+#define Q4_MAX_FUSED_K 16384     /* longest rows q4_gemv_fused accepts       */
+#define Q4_FUSE_SEPARATE 0       /* one output per matrix                    */
+#define Q4_FUSE_SWIGLU 1         /* two matrices (gate, up) -> one output    */
+
+/* One packed matrix of a fused call. */
+typedef struct {
+    const uint8_t *codes;    /* packed codes [M][K/2], 16-byte aligned        */
+    const uint16_t *scales;  /* fp16 bits [M][K/64], 2-byte aligned           */
+    int64_t M;               /* rows (M >= 0)                                 */
+    const float *bias;       /* fp32 [M], 4-byte aligned, or NULL             */
+} q4_operand;
+
+/*
+ * q4_gemv_fused -- several products of one activation vector in one launch.
+ *   ops[0..count-1]: the matrices, all with K columns (K <= Q4_MAX_FUSED_K);
+ *     t_i = W_i . x + bias_i (fp32 accumulation, bias added to the sum).
+ *   mode Q4_FUSE_SEPARATE (1 <= count <= Q4_MAX_FUSED):
+ *     y[i][m] = t_i[m] + residual[i][m],  m < ops[i].M.
+ *   mode Q4_FUSE_SWIGLU (count == 2, ops[0].M == ops[1].M, gate then up):
+ *     y[0][m] = silu(t_0[m]) * t_1[m] + residual[0][m],  silu(z) = z / (1 + e^-z).
+ *   x: bf16 bits [K], 16-byte aligned.
+ *   y: host array of device pointers (count of them, or 1 for SWIGLU), each
+ *     fp32 and 4-byte aligned.
+ *   residual: NULL, or a host array like y whose entries are NULL or fp32
+ *     device vectors; residual[i] may be exactly y[i] (an in-place add) but
+ *     must not otherwise overlap an output.
+ * An output must not overlap any input or another output.  Matrices with
+ * M == 0 are skipped.  Accuracy: t_i as q4_gemv; the epilogue is fp32.
+ */
+int q4_gemv_fused(const q4_operand *ops, int count, int64_t K,
+                  const uint16_t *x, int mode, float *const *y,
+                  const float *const *residual, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

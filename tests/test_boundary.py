@@ -32,8 +32,8 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_codebook",
-              "q4_codes_bytes", "q4_scales_bytes", "q4_status_string"):
+    for n in ("q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused",
+              "q4_codebook", "q4_codes_bytes", "q4_scales_bytes", "q4_status_string"):
         assert n in names
 
 
@@ -158,6 +158,64 @@ def test_unpack_errors(q4):
     assert _unpack(q4, A, B, M, K, A + 128, D) == q4.Q4_ERR_OVERLAP   # codes_out inside codes
     assert _unpack(q4, A, B, M, K, C, B + 8) == q4.Q4_ERR_OVERLAP     # scales_out over scales
     assert _unpack(q4, A, B, M, K, C, C + 16) == q4.Q4_ERR_OVERLAP    # scales_out inside codes_out
+
+
+def _fused(q4, ops, K, x, mode, ys, res=None):
+    """ops: list of (codes, scales, M, bias) fake addresses; ys/res: lists."""
+    arr = (q4.Operand * max(len(ops), 1))(*[q4.Operand(c, s, M, b) for c, s, M, b in ops])
+    yp = (ctypes.c_void_p * max(len(ys), 1))(*ys) if ys is not None else None
+    rp = (ctypes.c_void_p * max(len(res), 1))(*res) if res is not None else None
+    return q4.lib().q4_gemv_fused(ctypes.cast(arr, ctypes.c_void_p) if ops else None, len(ops), K, x, mode,
+                                  ctypes.cast(yp, ctypes.c_void_p) if yp is not None else None,
+                                  ctypes.cast(rp, ctypes.c_void_p) if rp is not None else None, None)
+
+
+E = 0x50000000
+F = 0x60000000
+G = 0x70000000
+
+
+def test_fused_shape_and_mode_errors(q4):
+    SEP, SWI = q4.Q4_FUSE_SEPARATE, q4.Q4_FUSE_SWIGLU
+    op = (A, B, 16, 0)  # codes 1 KB at K=128, scales 64 B
+    assert _fused(q4, [op], 128, C, 2, [D]) == q4.Q4_ERR_SHAPE               # unknown mode
+    assert _fused(q4, [], 128, C, SEP, [D]) == q4.Q4_ERR_SHAPE                # no matrix
+    assert _fused(q4, [op] * 5, 128, C, SEP, [D] * 5) == q4.Q4_ERR_SHAPE      # more than Q4_MAX_FUSED
+    assert _fused(q4, [op] * 3, 128, C, SWI, [D]) == q4.Q4_ERR_SHAPE          # SwiGLU takes two
+    assert _fused(q4, [op, (E, F, 8, 0)], 128, C, SWI, [D]) == q4.Q4_ERR_SHAPE  # unequal M
+    assert _fused(q4, [op], q4.Q4_MAX_FUSED_K + 64, C, SEP, [D]) == q4.Q4_ERR_SHAPE
+    assert _fused(q4, [op], 100, C, SEP, [D]) == q4.Q4_ERR_SHAPE
+    assert _fused(q4, [(A, B, -1, 0)], 128, C, SEP, [D]) == q4.Q4_ERR_SHAPE
+    assert _fused(q4, [(0, 0, 0, 0), (0, 0, 0, 0)], 128, 0, SEP, [0, 0]) == q4.Q4_OK  # nothing to do
+
+
+def test_fused_null_and_alignment(q4):
+    SEP = q4.Q4_FUSE_SEPARATE
+    op = (A, B, 16, 0)
+    assert _fused(q4, [op], 128, 0, SEP, [D]) == q4.Q4_ERR_NULL              # x
+    assert _fused(q4, [op], 128, C, SEP, None) == q4.Q4_ERR_NULL             # y array
+    assert _fused(q4, [op], 128, C, SEP, [0]) == q4.Q4_ERR_NULL              # y[0]
+    assert _fused(q4, [(0, B, 16, 0)], 128, C, SEP, [D]) == q4.Q4_ERR_NULL   # codes
+    assert _fused(q4, [op], 128, C + 8, SEP, [D]) == q4.Q4_ERR_ALIGN
+    assert _fused(q4, [(A + 8, B, 16, 0)], 128, C, SEP, [D]) == q4.Q4_ERR_ALIGN
+    assert _fused(q4, [(A, B + 1, 16, 0)], 128, C, SEP, [D]) == q4.Q4_ERR_ALIGN
+    assert _fused(q4, [(A, B, 16, E + 2)], 128, C, SEP, [D]) == q4.Q4_ERR_ALIGN
+    assert _fused(q4, [op], 128, C, SEP, [D + 2]) == q4.Q4_ERR_ALIGN
+    assert _fused(q4, [op], 128, C, SEP, [D], [F + 2]) == q4.Q4_ERR_ALIGN
+
+
+def test_fused_overlap(q4):
+    SEP, SWI = q4.Q4_FUSE_SEPARATE, q4.Q4_FUSE_SWIGLU
+    op = (A, B, 16, E)  # codes 1 KB, scales 64 B, bias 64 B; y 64 B
+    assert _fused(q4, [op], 128, C, SEP, [A + 512]) == q4.Q4_ERR_OVERLAP       # y inside codes
+    assert _fused(q4, [op], 128, C, SEP, [C + 200]) == q4.Q4_ERR_OVERLAP       # y over x's tail (256 B)
+    assert _fused(q4, [op], 128, C, SEP, [E + 32]) == q4.Q4_ERR_OVERLAP        # y over the bias
+    assert _fused(q4, [op, (F, G, 16, 0)], 128, C, SEP, [D, D + 32]) == q4.Q4_ERR_OVERLAP  # y0 over y1
+    assert _fused(q4, [op], 128, C, SEP, [D], [D + 4]) == q4.Q4_ERR_OVERLAP    # residual shifted onto y
+    assert _fused(q4, [op, (F, G, 16, 0)], 128, C, SEP, [D, D + 4096], [0, D + 16]) == q4.Q4_ERR_OVERLAP
+    assert _fused(q4, [op, (F, G, 16, 0)], 128, C, SWI, [G + 16]) == q4.Q4_ERR_OVERLAP  # y over up scales
+    # every call above fails a host check; the exact-alias residual is legal
+    # and is exercised on the GPU, not here
 
 
 def test_binding_refuses_without_library(tmp_path, monkeypatch):

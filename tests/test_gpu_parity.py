@@ -449,3 +449,218 @@ def test_graph_capture_replays_match_eager(env):
         # eager work in between replays
         q4.q4_gemv(c, s, x)
         torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# q4_gemv_fused: several products of one x with the decode epilogues
+# ---------------------------------------------------------------------------
+
+EPS32 = 2.0 ** -24
+
+
+def _fused_ref(ts, Ss, biases, residuals, swiglu):
+    """Oracle outputs and per-element bounds for the fused epilogue.
+
+    Each product t_i carries the GEMV bound e_i = 1e-3 S_i + 1e-5; the fp32
+    adds of bias and residual each add at most one rounding (half an ulp,
+    counted here as a full EPS32 of the operands).  SwiGLU: silu has slope in
+    (-0.1, 1.1), so an error e_a in its argument moves silu by at most 1.1 e_a;
+    the product silu(a) * b then moves by 1.1 e_a (|b| + e_b) + |silu(a)| e_b,
+    and the fp32 exp, divide and multiplies add a few ulps of |silu(a) b|."""
+    f64 = lambda v: None if v is None else np.asarray(v, np.float64)
+    if swiglu:
+        y = oracle.epilogue(ts[0], ts[1], biases[0], biases[1], residuals[0], swiglu=True)
+        b0, b1 = f64(biases[0]), f64(biases[1])
+        a = ts[0] + (b0 if b0 is not None else 0.0)
+        b = ts[1] + (b1 if b1 is not None else 0.0)
+        ea = 1e-3 * Ss[0] + 1e-5 + EPS32 * np.abs(a)
+        eb = 1e-3 * Ss[1] + 1e-5 + EPS32 * np.abs(b)
+        sa = np.array([oracle.silu(v) for v in a]) if a.size <= 4096 else a / (1.0 + np.exp(-a))
+        r = f64(residuals[0])
+        bound = 1.1 * ea * (np.abs(b) + eb) + np.abs(sa) * eb + 8 * EPS32 * (
+            np.abs(sa * b) + (np.abs(r) if r is not None else 0.0))
+        return [y], [bound]
+    ys, bounds = [], []
+    for t, S, bias, res in zip(ts, Ss, biases, residuals):
+        ys.append(oracle.epilogue(t, bias0=bias, residual=res))
+        mag = np.abs(t) + (np.abs(f64(bias)) if bias is not None else 0.0) + (
+            np.abs(f64(res)) if res is not None else 0.0)
+        bounds.append(1e-3 * S + 1e-5 + 2 * EPS32 * mag)
+    return ys, bounds
+
+
+def _check_bound(y_gpu, y_ref, bound, what):
+    y_gpu = np.asarray(y_gpu, np.float64)
+    err = np.abs(y_gpu - y_ref)
+    ratio = float(np.max(err / bound)) if err.size else 0.0
+    _log(f"{what}: worst |err|/bound = {ratio:.3g}")
+    assert np.all(np.isfinite(y_gpu)), f"{what}: non-finite output"
+    assert np.all(err <= bound), f"{what}: tolerance broken, worst ratio {ratio}"
+
+
+def _fused_case(env, Ms, K, seed, swiglu=False, bias=True, residual=True, alias=(), x_recipe="unit_rms",
+                bias_scale=0.5):
+    """Packs len(Ms) matrices, runs q4_gemv_fused, checks every output against
+    the oracle and against the unfused q4_gemv followed by torch's epilogue."""
+    torch, q4, dev = env
+    x = wl.activation(K, seed, x_recipe)
+    xd = _x_dev(env, x)
+    ops, ts, Ss, biases, packed = [], [], [], [], []
+    rng = np.random.default_rng(seed)
+    for i, M in enumerate(Ms):
+        W = wl.weights(M, K, seed + 17 * i)
+        codes, scales, st = oracle.pack(W)
+        assert st == 0
+        t, S = oracle.gemv(codes, scales, M, K, x)
+        c, s = _upload_packed(env, codes, scales)
+        b = (rng.standard_normal(M) * bias_scale).astype(np.float32) if bias else None
+        bd = torch.from_numpy(b).to(dev) if b is not None else None
+        ops.append((c, s, bd))
+        ts.append(t)
+        Ss.append(S)
+        biases.append(b)
+        packed.append((c, s))
+    nout = 1 if swiglu else len(Ms)
+    res_h = [(rng.standard_normal(Ms[o]) * 2).astype(np.float32) if residual else None for o in range(nout)]
+    ys = [torch.full((Ms[o],), float("nan"), device=dev) for o in range(nout)]
+    res_d = []
+    for o in range(nout):
+        if res_h[o] is None:
+            res_d.append(None)
+        elif o in alias:  # in-place: the output buffer holds the residual
+            ys[o].copy_(torch.from_numpy(res_h[o]))
+            res_d.append(ys[o])
+        else:
+            res_d.append(torch.from_numpy(res_h[o]).to(dev))
+    q4.q4_gemv_fused(ops, xd, "swiglu" if swiglu else "separate", ys, res_d if residual else None)
+    torch.cuda.synchronize()
+    y_ref, bound = _fused_ref(ts, Ss, biases, res_h, swiglu)
+    what = f"fused {'swiglu' if swiglu else 'separate'} Ms={Ms} K={K}"
+    for o in range(nout):
+        _check_bound(ys[o].cpu().numpy(), y_ref[o], bound[o], f"{what} out {o}")
+    # Unfused: one q4_gemv per matrix, then torch's epilogue in fp32.
+    tg = [q4.q4_gemv(c, s, xd) for c, s in packed]
+    for i in range(len(tg)):
+        if biases[i] is not None:
+            tg[i] = tg[i] + ops[i][2]
+    if swiglu:
+        un = [torch.nn.functional.silu(tg[0]) * tg[1]]
+    else:
+        un = tg
+    for o in range(nout):
+        if res_h[o] is not None:
+            un[o] = un[o] + torch.from_numpy(res_h[o]).to(dev)
+        torch.cuda.synchronize()
+        # both sides are within `bound` of the oracle
+        _check_bound(ys[o].cpu().numpy(), un[o].cpu().numpy().astype(np.float64), 2 * bound[o],
+                     f"{what} out {o} vs unfused")
+    return ys
+
+
+# (Ms, K): the row-length classes of the launcher (one wave a row up to
+# K=2048, two chunks a lane to 4096, a workgroup a row to 16384), segments of
+# ragged and empty sizes, and single-tile and ring plans.
+FUSED_SEPARATE = [((2048, 256, 256), 2048), ((1, 65, 0, 300), 512), ((7,), 64), ((4096, 4096), 2048),
+                  ((33, 1000, 2), 4096), ((2048,), 11008), ((129, 5, 4100), 4160), ((40, 3), 16384),
+                  ((20000, 300), 1024)]
+
+
+@pytest.mark.parametrize("Ms,K", FUSED_SEPARATE)
+def test_fused_separate_bias_residual(env, Ms, K):
+    _fused_case(env, Ms, K, seed=5000 + K + sum(Ms))
+
+
+@pytest.mark.parametrize("bias,residual", [(False, False), (True, False), (False, True)])
+def test_fused_separate_optional_terms(env, bias, residual):
+    _fused_case(env, (300, 64, 1), 2048, seed=5100, bias=bias, residual=residual)
+
+
+def test_fused_residual_in_place(env):
+    # down projection with the residual stream updated in place, plus a
+    # second output that is not aliased
+    _fused_case(env, (2048, 77), 11008, seed=5200, alias=(0,))
+    _fused_case(env, (513, 1, 64), 2048, seed=5201, alias=(0, 2))
+
+
+# (M, K): gate/up pairs over the same row-length classes.
+FUSED_SWIGLU = [(11008, 2048), (1, 64), (77, 512), (5000, 2048), (300, 4096), (2048, 4160),
+                (129, 11008), (20, 16384), (20000, 1024)]
+
+
+@pytest.mark.parametrize("M,K", FUSED_SWIGLU)
+def test_fused_swiglu(env, M, K):
+    _fused_case(env, (M, M), K, seed=6000 + M + K, swiglu=True)
+
+
+@pytest.mark.parametrize("bias,residual,alias", [(False, False, ()), (True, False, ()), (False, True, (0,))])
+def test_fused_swiglu_optional_terms(env, bias, residual, alias):
+    _fused_case(env, (1100, 1100), 2048, seed=6100, swiglu=True, bias=bias, residual=residual, alias=alias)
+
+
+def test_fused_swiglu_wide_activations(env):
+    # gate biases of tens drive silu into both tails (e^-z overflows to inf
+    # for z < -88)
+    _fused_case(env, (500, 500), 2048, seed=6200, swiglu=True, x_recipe="normal", bias_scale=60.0)
+
+
+def test_fused_swiglu_halves_of_one_matrix(env):
+    """Gate and up packed as one [2M, K] matrix: the two operands are the
+    halves of one codes/scales buffer."""
+    torch, q4, dev = env
+    M, K = 1100, 2048
+    W = wl.weights(2 * M, K, 6300)
+    x = wl.activation(K, 6300, "unit_rms")
+    codes, scales, _ = oracle.pack(W)
+    t, S = oracle.gemv(codes, scales, 2 * M, K, x)
+    c, s = _upload_packed(env, codes, scales)
+    ops = [(c[:M], s[:M], None), (c[M:], s[M:], None)]
+    y = q4.q4_gemv_fused(ops, _x_dev(env, x), "swiglu")[0]
+    torch.cuda.synchronize()
+    y_ref, bound = _fused_ref([t[:M], t[M:]], [S[:M], S[M:]], [None, None], [None], True)
+    _check_bound(y.cpu().numpy(), y_ref[0], bound[0], "swiglu halves")
+
+
+def test_fused_graph_replays_match_eager(env):
+    torch, q4, dev = env
+    K = 2048
+    ops, packed = [], []
+    for i, M in enumerate((2048, 256, 256)):
+        codes, scales, _ = oracle.pack(wl.weights(M, K, 6400 + i))
+        c, s = _upload_packed(env, codes, scales)
+        ops.append((c, s, torch.randn(M, device=dev)))
+    x = _x_dev(env, wl.activation(K, 6400, "unit_rms"))
+    eager = [v.clone() for v in q4.q4_gemv_fused(ops, x)]
+    ys = [torch.full_like(v, float("nan")) for v in eager]
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            q4.q4_gemv_fused(ops, x, "separate", ys, stream=st)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in ys:
+            v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ys, eager):
+            assert torch.equal(a, b), f"fused replay {rep} differs from eager"
+        q4.q4_gemv_fused(ops, x)
+        torch.cuda.synchronize()
+
+
+def test_fused_rejects_through_binding(env):
+    torch, q4, dev = env
+    K = 128
+    codes, scales, _ = oracle.pack(wl.weights(8, K, 1))
+    c, s = _upload_packed(env, codes, scales)
+    x = _x_dev(env, wl.activation(K, 1, "unit_rms"))
+    with pytest.raises(q4.Q4Error):
+        q4.q4_gemv_fused([(c, s, None)] * 3, x, "swiglu")
+    y = torch.empty(8, device=dev)
+    with pytest.raises(q4.Q4Error):  # residual overlapping its output off by one element
+        big = torch.zeros(9, device=dev)
+        q4.q4_gemv_fused([(c, s, None)], x, "separate", [big[:8]], [big[1:]])
+    del y
