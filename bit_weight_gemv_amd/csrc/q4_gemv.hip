@@ -355,10 +355,33 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         load_tile(buf);  // tile t + S + 1
     };
 
+    // The epilogue operands of a reduction group (first tile g0): lane l
+    // reads those of the group's output l.  They are read when the group
+    // starts, behind its weight tiles and ahead of the ring's refills, so
+    // their latency hides under the group's arithmetic instead of following
+    // the reduction.
+    const int64_t nrows = r_end - r_begin;
+    struct Epi {
+        float b0, b1, r;
+    };
+    auto fetch_epi = [&](int64_t g0) {
+        Epi e{0.0f, 0.0f, 0.0f};
+        if constexpr (MODE != kModePlain) {
+            constexpr int OPG = MODE == kModeSwiglu ? RG / 2 : RG;  // outputs per group
+            const int64_t local = g0 * LPT + lane;
+            if ((!MULTI || wig == 0) && lane < OPG && local < nrows) {
+                const int64_t row = r_begin + local;
+                if (sg.bias0) e.b0 = sg.bias0[row];
+                if (MODE == kModeSwiglu && sg.bias1) e.b1 = sg.bias1[row];
+                if (sg.residual) e.r = sg.residual[row];
+            }
+        }
+        return e;
+    };
+
     // Store of a reduction group whose first tile is g0; lane l holds the
     // finished sum of group row l (l < RG).  Every lane of the wave calls it.
-    const int64_t nrows = r_end - r_begin;
-    auto store = [&](float tot, int64_t g0) {
+    auto store = [&](float tot, int64_t g0, const Epi &e) {
         if constexpr (MODE == kModeSwiglu) {
             // Output o of the group: tile o / LPT, gate row o % LPT of it and
             // the up row LPT after.
@@ -369,10 +392,10 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
             const int64_t local = g0 * LPT + lane;
             if (lane < RG / 2 && local < nrows) {
                 const int64_t row = r_begin + local;
-                const float a = sg.bias0 ? g + sg.bias0[row] : g;
-                const float b = sg.bias1 ? u + sg.bias1[row] : u;
+                const float a = sg.bias0 ? g + e.b0 : g;
+                const float b = sg.bias1 ? u + e.b1 : u;
                 float v = silu_f(a) * b;
-                if (sg.residual) v += sg.residual[row];
+                if (sg.residual) v += e.r;
                 sg.y[row] = v;
             }
         } else {
@@ -380,20 +403,21 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
             if (lane < RG && local < nrows) {
                 const int64_t row = r_begin + local;
                 float v = tot;
-                if (MODE == kModeAffine && sg.bias0) v += sg.bias0[row];
-                if (MODE == kModeAffine && sg.residual) v += sg.residual[row];
+                if (MODE == kModeAffine && sg.bias0) v += e.b0;
+                if (MODE == kModeAffine && sg.residual) v += e.r;
                 sg.y[row] = v;
             }
         }
     };
 
     for (int64_t g0 = 0; g0 < ntiles; g0 += TPG) {
+        const Epi epi = fetch_epi(g0);
 #pragma unroll
         for (int j = 0; j < TPG; ++j) step(j % (S + 1), j, g0 + j);
         // Lane l now holds the wave's total of group row (l % RG).
         const float tot = reduce_rows<RG>(acc) * down;
         if (!MULTI) {
-            store(tot, g0);
+            store(tot, g0, epi);
         } else {
             if (lane < RG) red[wig][lane] = tot;
             __syncthreads();
@@ -401,7 +425,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                 float sum = 0.0f;
                 if (lane < RG)
                     for (int w = 0; w < wpg; ++w) sum += red[w][lane];
-                store(sum, g0);
+                store(sum, g0, epi);
             }
             __syncthreads();
         }
@@ -438,6 +462,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
     si = __builtin_amdgcn_readfirstlane(si);
     const GemvSeg &sg = segs.s[si];
     gemv_body<NR, CPL, S, RG, MULTI, MODE>(sg, K, x, P, (int64_t)blockIdx.x - sg.wg_begin);
+}
+
+// The one-segment form (a SwiGLU pair, or a single matrix): the segment is
+// the kernel argument itself, so its fields arrive with the first scalar
+// reads instead of after a lookup of the workgroup's segment.
+template <int NR, int CPL, int S, int RG, bool MULTI, int MODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
+                          amdgpu_waves_per_eu(gemv_min_waves(CPL), 8))) void gemv_fused1_kernel(GemvSeg sg, int K,
+                                                   const uint16_t *__restrict__ x, int P) {
+    gemv_body<NR, CPL, S, RG, MULTI, MODE>(sg, K, x, P, (int64_t)blockIdx.x);
 }
 
 namespace {
@@ -515,9 +549,17 @@ template <int NR, int CPL, int S, int RG, bool MULTI, int MODE>
 hipError_t launch_fused_variant(GemvSegs segs, int K, const uint16_t *x, int P, int G, int64_t grid,
                                 hipStream_t stream) {
     if (!MULTI && (K / 8 > P * G || K / 8 > kSharedXUnits)) return hipErrorInvalidValue;
-    void *args[] = {&segs, &K, &x, &P};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_fused_kernel<NR, CPL, S, RG, MULTI, MODE>),
-                           dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
+    if (MODE == kModeSwiglu || segs.n == 1) {
+        void *args[] = {&segs.s[0], &K, &x, &P};
+        return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_fused1_kernel<NR, CPL, S, RG, MULTI, MODE>),
+                               dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
+    }
+    if constexpr (MODE != kModeSwiglu) {
+        void *args[] = {&segs, &K, &x, &P};
+        return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_fused_kernel<NR, CPL, S, RG, MULTI, MODE>),
+                               dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 // The variant for the row length, as launch_gemv chooses it (rows of up to
