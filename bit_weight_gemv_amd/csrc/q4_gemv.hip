@@ -194,7 +194,7 @@ enum { kModePlain = 0, kModeAffine = 1, kModeSwiglu = 2 };
 // kModeSwiglu: each tile holds NR/2 gate rows and the NR/2 up rows of the
 // same outputs; after the full reduction lane pairs are brought together and
 // y = silu(g (+ bias0)) * (u (+ bias1)) (+ residual) -- SiLU only ever sees
-// a finished sum (deep-fold "Decode V2" page, bench notes).
+// a finished sum (deep-fold "Decode V2" page, section 6 Linear primitive).
 template <int NR, int CPL, int S, int RG, bool MULTI, int MODE>
 __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16_t *__restrict__ x, int P,
                                           int64_t wg) {

@@ -138,7 +138,7 @@ int q4_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M,
                    void *stream);
 
 /*
- * Fused decode projections (deep-fold "Decode V2" page, bench notes: one
+ * Fused decode projections (deep-fold "Decode V2" page, section 6 Linear primitive: one
  * grid over the q, k and v rows sharing x with the q/k/v bias added in that
  * kernel; gate/up pairs writing silu(g) * u, SiLU only after the full
  * reduction; the o/down residual added into y; golang.design accel/tensor:
@@ -174,6 +174,12 @@ typedef struct {
  *     must not otherwise overlap an output.
  * An output must not overlap any input or another output.  Matrices with
  * M == 0 are skipped.  Accuracy: t_i as q4_gemv; the epilogue is fp32.
+ * Errors (nothing is launched): Q4_ERR_SHAPE for an unknown mode, a count
+ * out of range, SWIGLU with count != 2 or unequal M, K not a positive
+ * multiple of 64 or above Q4_MAX_FUSED_K, or M < 0; Q4_ERR_NULL for a missing
+ * ops, x, y or y[i], codes or scales of a non-empty matrix; Q4_ERR_ALIGN;
+ * Q4_ERR_OVERLAP; Q4_ERR_DEVICE if the launch fails.  With every M == 0 the
+ * call returns Q4_OK without looking at x, y or residual.
  */
 int q4_gemv_fused(const q4_operand *ops, int count, int64_t K,
                   const uint16_t *x, int mode, float *const *y,

@@ -316,7 +316,7 @@ int64_t oracle_argmax_f32(const float *y, int64_t n) {
 
 /* ------------------------------------------------------------------------ */
 /* Fused-projection epilogue (accel/tensor func Linear, func SiLU,           */
-/* func SwiGLU; deep-fold "Decode V2" bench notes).                          */
+/* func SwiGLU; deep-fold "Decode V2", section 6 Linear primitive).                          */
 /* ------------------------------------------------------------------------ */
 
 double oracle_silu(double z) { return z / (1.0 + exp(-z)); }

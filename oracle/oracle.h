@@ -78,7 +78,7 @@ double oracle_silu(double z);
 
 /* The epilogue of a fused projection, fp64, for i < n (golang.design
  * accel/tensor page: func Linear adds the bias to the product, func SwiGLU is
- * SiLU(gate) * value; deep-fold "Decode V2" page, bench notes: q/k/v bias in
+ * SiLU(gate) * value; deep-fold "Decode V2" page, section 6 Linear primitive: q/k/v bias in
  * the projection, silu(g) * u after the full reduction, residual added into
  * y):
  *   a = t0[i] + bias0[i]                        (bias0 may be NULL)
