@@ -81,6 +81,10 @@ def _load():
         lib.oracle_argmax_f64.restype = I64
         lib.oracle_argmax_f32.argtypes = [P, I64]
         lib.oracle_argmax_f32.restype = I64
+        lib.oracle_f64_to_bf16_rne.argtypes = [ctypes.c_double]
+        lib.oracle_f64_to_bf16_rne.restype = ctypes.c_uint16
+        lib.oracle_gather_rows.argtypes = [P, P, I64, I64, P, I64, ctypes.c_int, P]
+        lib.oracle_gather_rows.restype = ctypes.c_int32
         _lib = lib
         return lib
 
@@ -240,6 +244,30 @@ def epilogue(t0, t1=None, bias0=None, bias1=None, residual=None, swiglu: bool = 
                             _ptr(b1) if b1 is not None else nullp, _ptr(r) if r is not None else nullp,
                             n, 1 if swiglu else 0, _ptr(out))
     return out
+
+
+GATHER_BAD_ID = 1
+
+
+def f64_to_bf16_bits(v: float) -> int:
+    """One rounding of a finite double to bfloat16 bits, nearest-even."""
+    return int(_load().oracle_f64_to_bf16_rne(float(v)))
+
+
+def gather_rows(codes, scales, M: int, K: int, ids, bf16: bool = False, out=None):
+    """(out, flags): out[i] = What[ids[i]] rounded once to fp32 (or bf16 bits,
+    uint16); rows of ids outside [0, M) keep what `out` held (NaN / 0xFFFF
+    when out is None) and set GATHER_BAD_ID in flags."""
+    _check_shape(M, K)
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint16)
+    ids = np.ascontiguousarray(ids, np.int32)
+    n = ids.size
+    if out is None:
+        out = np.full((n, K), 0xFFFF, np.uint16) if bf16 else np.full((n, K), np.nan, np.float32)
+    flags = _load().oracle_gather_rows(_ptr(codes), _ptr(scales), M, K, _ptr(ids), n, 1 if bf16 else 0,
+                                       _ptr(out))
+    return out, int(flags)
 
 
 def argmax(y) -> int:

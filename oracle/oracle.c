@@ -336,3 +336,69 @@ void oracle_epilogue(const double *t0, const double *t1, const float *bias0, con
         out[i] = v;
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Packed row gather (deep-fold "Decode V2" page, run notes of section 6:    */
+/* the embedding stays packed, its rows are dequantised into the arena, and  */
+/* a tied embedding shares the lm_head's packed matrix; golang.design        */
+/* accel/tensor, func QuantGatherRows: rows gathered from a quantized table). */
+/* ------------------------------------------------------------------------ */
+
+/* A finite double -> bfloat16 bits, rounded once to nearest, ties to even.
+ * bf16 keeps 8 significant bits and the fp32 exponent range: the spacing of
+ * representable values around a normal a is 2^(floor(log2 a) - 7), and
+ * 2^-133 below 2^-126.  Magnitudes that round past the largest finite bf16
+ * become infinity. */
+uint16_t oracle_f64_to_bf16_rne(double v) {
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    if (isnan(v)) return (uint16_t)(sign | 0x7fc0);
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    double q;
+    if (a < ldexp(1.0, -126)) {
+        q = ldexp(1.0, -133);
+    } else {
+        int ex;
+        frexp(a, &ex); /* floor(log2 a) = ex - 1 */
+        q = ldexp(1.0, ex - 1 - 7);
+    }
+    double n = a / q; /* exact: q is a power of two */
+    double fl = floor(n);
+    double frac = n - fl;
+    double r;
+    if (frac > 0.5)
+        r = fl + 1.0;
+    else if (frac < 0.5)
+        r = fl;
+    else
+        r = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+    double u = r * q; /* the rounded magnitude */
+    if (u >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7f80);
+    float f = (float)u; /* exact: u has at most 8 significant bits */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    return (uint16_t)(sign | (uint16_t)(bits >> 16));
+}
+
+int32_t oracle_gather_rows(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                           const int32_t *ids, int64_t n, int bf16, void *out) {
+    float cb[16];
+    oracle_codebook_f32(cb);
+    int32_t flags = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t m = ids[i];
+        if (m < 0 || m >= M) {
+            flags |= ORACLE_GATHER_BAD_ID;
+            continue; /* the row of a refused id is left as it was */
+        }
+        for (int64_t k = 0; k < K; ++k) {
+            const double sc = oracle_f16_to_f64(scales[m * (K / 64) + k / 64]);
+            const double w = (double)cb[code_at(codes, K, m, k)] * sc; /* exact */
+            if (bf16)
+                ((uint16_t *)out)[i * K + k] = oracle_f64_to_bf16_rne(w);
+            else
+                ((float *)out)[i * K + k] = (float)w; /* one rounding, nearest-even */
+        }
+    }
+    return flags;
+}

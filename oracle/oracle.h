@@ -90,6 +90,22 @@ void oracle_epilogue(const double *t0, const double *t1, const float *bias0,
                      const float *bias1, const float *residual, int64_t n,
                      int swiglu, double *out);
 
+/* A finite double -> bfloat16 bits, one rounding to nearest, ties to even
+ * (gizai tensor/lazy page, Lazy.roundedBf16: round to nearest even). */
+uint16_t oracle_f64_to_bf16_rne(double v);
+
+/* Packed row gather (deep-fold "Decode V2" page, section 6 run notes: the
+ * embedding is kept as packed rows dequantised into the arena, and a tied
+ * embedding reads the lm_head's packed matrix; golang.design accel/tensor
+ * page, func QuantGatherRows).  For i < n with 0 <= ids[i] < M:
+ *   out[i][k] = What[ids[i], k] rounded once to fp32 (bf16 == 0) or to bf16
+ *               bits (bf16 != 0), nearest-even; What = c * s is exact.
+ * Rows of ids outside [0, M) are left untouched and ORACLE_GATHER_BAD_ID is
+ * returned in the flags. */
+#define ORACLE_GATHER_BAD_ID 1
+int32_t oracle_gather_rows(const uint8_t *codes, const uint16_t *scales, int64_t M,
+                           int64_t K, const int32_t *ids, int64_t n, int bf16, void *out);
+
 /* First index of the maximum (NaN never wins); -1 if n == 0 or all NaN. */
 int64_t oracle_argmax_f64(const double *y, int64_t n);
 int64_t oracle_argmax_f32(const float *y, int64_t n);

@@ -30,7 +30,7 @@ MUTANTS = {
                       "double w = (double)cb[code_at(codes, K, m, k)];"),
     "block_index_32": ("double s = oracle_f16_to_f64(scales[m * (K / 64) + k / 64]);\n            double w",
                        "double s = oracle_f16_to_f64(scales[m * (K / 64) + k / 128]);\n            double w"),
-    "f16_tie_up": ("r = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "r = fl + 1.0;"),
+    "f16_tie_up": ("r = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0; /* tie: to even */", "r = fl + 1.0;"),
     "argmax_last_tie": ("if (!isnan(y[i]) && (best < 0 || y[i] > y[best])) best = i;\n    return best;\n}\n\nint64_t oracle_argmax_f32",
                         "if (!isnan(y[i]) && (best < 0 || y[i] >= y[best])) best = i;\n    return best;\n}\n\nint64_t oracle_argmax_f32"),
     "abs_sum_signed": ("mag += fabs(t);", "mag += t;"),
@@ -38,6 +38,15 @@ MUTANTS = {
     "silu_exponent_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
     "swiglu_operands_swapped": ("v = oracle_silu(a) * b;", "v = oracle_silu(b) * a;"),
     "bias_after_silu": ("        double v = a;\n        if (swiglu) {", "        double v = a;\n        if (swiglu && bias0) a -= (double)bias0[i];\n        if (swiglu) {"),
+    "bf16_precision_7_bits": ("q = ldexp(1.0, ex - 1 - 7);", "q = ldexp(1.0, ex - 1 - 6);"),
+    "bf16_tie_away": ("r = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;\n    double u = r * q; /* the rounded magnitude */",
+                      "r = fl + 1.0;\n    double u = r * q; /* the rounded magnitude */"),
+    "bf16_truncate": ("    if (frac > 0.5)\n        r = fl + 1.0;\n    else if (frac < 0.5)\n        r = fl;\n    else\n        r = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;\n    double u = r * q; /* the rounded magnitude */",
+                      "    r = fl;\n    double u = r * q; /* the rounded magnitude */"),
+    "gather_ignores_ids": ("const int64_t m = ids[i];", "const int64_t m = i;"),
+    "gather_accepts_id_M": ("if (m < 0 || m >= M) {", "if (m < 0 || m > M) {"),
+    "gather_fp32_via_bf16": ("((float *)out)[i * K + k] = (float)w;",
+                             "((float *)out)[i * K + k] = (float)oracle_bf16_to_f64(oracle_f64_to_bf16_rne(w));"),
     "residual_dropped": ("if (residual) v += (double)residual[i];", "if (residual && !swiglu) v += (double)residual[i];"),
 }
 

@@ -569,3 +569,115 @@ def test_swiglu_closed_form_on_constant_codes(oracle_mod):
     assert np.array_equal(g, [64.0] * M)
     out = oracle_mod.epilogue(g, g, swiglu=True)
     assert np.array_equal(out, [4096.0] * M)
+
+
+# ---------------------------------------------------------------------------
+# Packed row gather and the bf16 rounding it uses
+# ---------------------------------------------------------------------------
+
+def _bf16_value(bits):
+    return Fraction(float((np.array([bits], np.uint32) << np.uint32(16)).view(np.float32)[0]))
+
+
+def _bf16_brute(v):
+    """Nearest bf16 pattern to the double v by bisection over the ordered
+    positive finite patterns 0x0000..0x7F7F, exact rational distances, ties
+    to the even pattern."""
+    x = Fraction(v)
+    sign = 0x8000 if v < 0 or (v == 0 and np.signbit(v)) else 0
+    a = abs(x)
+    lo, hi = 0, 0x7F7F
+    if a >= _bf16_value(hi):
+        lo = hi
+    else:
+        while hi - lo > 1:  # invariant: value(lo) <= a < value(hi)
+            mid = (lo + hi) // 2
+            if _bf16_value(mid) <= a:
+                lo = mid
+            else:
+                hi = mid
+    if _bf16_value(lo) == a or lo == 0x7F7F and a >= _bf16_value(lo):
+        best = lo
+    else:
+        dl, dh = a - _bf16_value(lo), _bf16_value(hi) - a
+        best = lo if dl < dh else hi if dh < dl else (lo if lo % 2 == 0 else hi)
+    return sign | best
+
+
+def test_f64_to_bf16_brute_force(oracle_mod):
+    rng = np.random.default_rng(7)
+    vals = list(rng.standard_normal(300) * np.exp2(rng.integers(-30, 30, 300)))
+    # exact ties, one ulp either side of them, and the subnormal range
+    for m in (1, 3, 5, 127, 255):
+        for e in (-20, 0, 7):
+            t = (1 + (2 * m - 1) * 2.0 ** -8) * 2.0 ** e if m < 128 else (1 + m * 2.0 ** -8) * 2.0 ** e
+            vals += [t, -t, np.nextafter(t, 0), np.nextafter(t, np.inf)]
+    vals += [2.0 ** -130, 3 * 2.0 ** -134, 2.0 ** -133 * 1.5, 65504.0, -0.0, 0.0]
+    for v in vals:
+        assert oracle_mod.f64_to_bf16_bits(v) == _bf16_brute(v), v
+
+
+def _gather_inputs(oracle_mod, M, K, seed):
+    W = wl.weights(M, K, seed, std=0.5)
+    codes, scales, st = oracle_mod.pack(W)
+    assert st == 0
+    return codes, scales
+
+
+def test_gather_fp32_is_numpy_cast_of_dequant(oracle_mod):
+    M, K = 37, 192
+    codes, scales = _gather_inputs(oracle_mod, M, K, 11)
+    ids = np.array([5, 0, 36, 5, 17, 2], np.int32)
+    out, flags = oracle_mod.gather_rows(codes, scales, M, K, ids)
+    assert flags == 0
+    What = oracle_mod.dequant(codes, scales, M, K)
+    assert np.array_equal(out, What[ids].astype(np.float32))
+
+
+def test_gather_bf16_brute_force(oracle_mod):
+    M, K = 9, 128
+    codes, scales = _gather_inputs(oracle_mod, M, K, 12)
+    ids = np.array([8, 3, 3, 0], np.int32)
+    out, flags = oracle_mod.gather_rows(codes, scales, M, K, ids, bf16=True)
+    assert flags == 0
+    What = oracle_mod.dequant(codes, scales, M, K)
+    for i, m in enumerate(ids):
+        for k in range(0, K, 3):
+            assert out[i, k] == _bf16_brute(What[m, k]), (i, k)
+
+
+def test_gather_ties_closed_form(oracle_mod):
+    """Rows whose blocks hold +s, -s and 0 pack to codes 15, 0, 7 with scale s
+    exactly, so the gathered values are +-s and 0: fp32 exact, bf16 the
+    nearest-even rounding of s, which for these s is an exact tie."""
+    K = 64
+    cases = {1 + 2.0 ** -8: 0x3F80, 1 + 3 * 2.0 ** -8: 0x3F82, 2 + 2.0 ** -7: 0x4000,
+             0.5 + 3 * 2.0 ** -9: 0x3F02}
+    W = np.zeros((len(cases), K), np.float32)
+    for r, s in enumerate(cases):
+        W[r, 0::3] = s
+        W[r, 1::3] = -s
+    codes, scales, st = oracle_mod.pack(W)
+    assert st == 0
+    ids = np.arange(len(cases), dtype=np.int32)
+    f32, _ = oracle_mod.gather_rows(codes, scales, len(cases), K, ids)
+    b16, _ = oracle_mod.gather_rows(codes, scales, len(cases), K, ids, bf16=True)
+    for r, (s, bits) in enumerate(cases.items()):
+        assert np.all(f32[r, 0::3] == np.float32(s)) and np.all(f32[r, 1::3] == -np.float32(s))
+        assert np.all(f32[r, 2::3] == 0.0)
+        assert np.all(b16[r, 0::3] == bits) and np.all(b16[r, 1::3] == (bits | 0x8000))
+        assert np.all(b16[r, 2::3] == 0)
+
+
+def test_gather_refuses_out_of_range_ids(oracle_mod):
+    M, K = 6, 64
+    codes, scales = _gather_inputs(oracle_mod, M, K, 13)
+    ids = np.array([-1, M, 2, 2**31 - 1, 0], np.int32)
+    out, flags = oracle_mod.gather_rows(codes, scales, M, K, ids)
+    assert flags == oracle_mod.GATHER_BAD_ID
+    assert np.all(np.isnan(out[[0, 1, 3]]))
+    What = oracle_mod.dequant(codes, scales, M, K)
+    assert np.array_equal(out[2], What[2].astype(np.float32))
+    assert np.array_equal(out[4], What[0].astype(np.float32))
+    ok, flags = oracle_mod.gather_rows(codes, scales, M, K, np.array([], np.int32))
+    assert flags == 0 and ok.shape == (0, K)
