@@ -1,7 +1,7 @@
 """Benchmark of the 4-bit codebook GEMV on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--copies R] [--no-secondary]
-                    [--secondary down,smalln,gateup,fused]
+                    [--secondary down,smalln,gateup,fused,gather]
 
 A step is one q4_gemv call on the lm_head workload (M x K = 151936 x 2048,
 x bf16 unit-RMS, y fp32): the projection the metric is quoted on.  Inputs are
@@ -270,6 +270,38 @@ def fused_secondaries(torch, q4, wl, dev, steps, warmup):
     return out
 
 
+def gather_secondaries(torch, q4, wl, dev, steps, warmup):
+    """The packed row gather on the tied-embedding table (the lm_head matrix,
+    151936 x 2048): one decode token and a 32-token chunk, fp32 and bf16
+    rows; ids drawn afresh for every call from a seeded stream."""
+    c = wl.CONFIGS["lm_head"]
+    M, K = c["M"], c["K"]
+    W = torch.from_numpy(wl.weights(M, K, c["seed"])).to(dev)
+    codes, scales, status = q4.q4_pack(W)
+    torch.cuda.synchronize()
+    del W
+    torch.cuda.empty_cache()
+    g = torch.Generator(device="cpu").manual_seed(9)
+    out = []
+    for n in (1, 32):
+        idsets = [(torch.randint(0, M, (n,), generator=g, dtype=torch.int32).to(dev),) for _ in range(64)]
+        for dt, name, elt in ((torch.float32, "f32", 4), (torch.bfloat16, "bf16", 2)):
+            o = torch.empty((n, K), dtype=dt, device=dev)
+            st = torch.empty(1, dtype=torch.int32, device=dev)
+
+            def fn(ids, o=o, st=st):
+                q4.q4_gather_rows(codes, scales, ids, dt, o, st)
+            ms, wall = time_graph(torch, fn, idsets, steps, warmup)
+            nb = n * (K // 2 + K // 32 + 4) + n * K * elt
+            log(f"gather {name} n={n}: {ms * 1e3:.2f} us/call")
+            out.append({"workload": f"gather rows of the tied lm_head table {M}x{K}, n={n}, out {name}",
+                        "us_per_call": round(ms * 1e3, 3), "us_per_step_wall": round(wall * 1e3, 3),
+                        "bytes": nb, "achieved_GBs": round(nb / (ms * 1e-3) / 1e9, 2)})
+    del codes, scales
+    torch.cuda.empty_cache()
+    return out
+
+
 def context_bandwidth(torch, dev, steps=20):
     """Bandwidth context from a library-independent kernel: torch's device
     copy of COPY_PROBE_BYTES, replayed as a graph; (read + written bytes) / s
@@ -321,8 +353,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--secondary", default="down,smalln,gateup,fused",
-                    help="comma-separated secondary workloads to time (down, smalln, gateup, fused)")
+    ap.add_argument("--secondary", default="down,smalln,gateup,fused,gather",
+                    help="comma-separated secondary workloads to time (down, smalln, gateup, fused, gather)")
     ap.add_argument("--eager", action="store_true",
                     help="also time the calls launched one by one from Python")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -419,6 +451,8 @@ def main():
             torch.cuda.empty_cache()
         if "fused" in chosen:
             secondary.extend(fused_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
+        if "gather" in chosen:
+            secondary.extend(gather_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
 
     result = {
         "metric": "4-bit GEMV us/call + achieved HBM GB/s (% of peak), MxK=151936x2048, N=1",

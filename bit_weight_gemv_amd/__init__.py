@@ -31,7 +31,12 @@ Q4_PACK_NONFINITE = 1
 Q4_PACK_OVERFLOW = 2
 
 EXPORTED = ("q4_codes_bytes", "q4_scales_bytes", "q4_codebook", "q4_status_string",
-            "q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused")
+            "q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused",
+            "q4_gather_rows")
+
+Q4_OUT_F32 = 0
+Q4_OUT_BF16 = 1
+Q4_GATHER_BAD_ID = 1
 
 Q4_MAX_FUSED = 4
 Q4_MAX_FUSED_K = 16384
@@ -82,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.q4_gemm_smalln.restype = I32
         L.q4_gemv_fused.argtypes = [P, I32, I64, P, I32, P, P, P]
         L.q4_gemv_fused.restype = I32
+        L.q4_gather_rows.argtypes = [P, P, I64, I64, P, I64, I32, P, P, P]
+        L.q4_gather_rows.restype = I32
         _lib = L
         return L
 
@@ -278,3 +285,32 @@ def q4_gemv_fused(ops, x, mode="separate", ys=None, residuals=None, stream=None)
     if st != Q4_OK:
         raise Q4Error(st, "q4_gemv_fused")
     return ys
+
+
+def q4_gather_rows(codes, scales, ids, out_dtype=None, out=None, status=None, stream=None):
+    """Rows ids (int32 [n]) of a packed matrix, dequantised: returns (out
+    [n, K] fp32 or bf16, status int32 [1]).  status is 0, or Q4_GATHER_BAD_ID
+    when some id is outside [0, M); the rows of such ids are not written."""
+    torch = _torch()
+    M, K = _mk(codes, scales)
+    dev = codes.device
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    _check(ids, "ids", torch.int32, dev)
+    n = ids.numel()
+    if out is None:
+        out = torch.empty((n, K), dtype=out_dtype, device=dev)
+    _check(out, "out", out_dtype, dev)
+    if out.numel() != n * K:
+        raise ValueError(f"out must hold n*K = {n * K} values")
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(status, "status", torch.int32, dev)
+    st = lib().q4_gather_rows(_ptr(codes), _ptr(scales), M, K, _ptr(ids) if n else None, n,
+                              Q4_OUT_BF16 if out_dtype == torch.bfloat16 else Q4_OUT_F32,
+                              _ptr(out) if n else None, _ptr(status), _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_gather_rows")
+    return out, status

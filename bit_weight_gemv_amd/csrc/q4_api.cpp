@@ -191,4 +191,30 @@ int q4_gemv_fused(const q4_operand *ops, int count, int64_t K, const uint16_t *x
         q4::launch_gemv_fused(fo, count, mode == Q4_FUSE_SWIGLU, K, x, y, residual, (hipStream_t)stream));
 }
 
+int q4_gather_rows(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K, const int32_t *ids,
+                   int64_t n, int out_type, void *out, int32_t *status, void *stream) {
+    if (!shape_ok(M, K) || n < 0) return Q4_ERR_SHAPE;
+    if (out_type != Q4_OUT_F32 && out_type != Q4_OUT_BF16) return Q4_ERR_SHAPE;
+    const bool bf16 = out_type == Q4_OUT_BF16;
+    const int64_t elt = bf16 ? 2 : 4;
+    // The grid is n times the workgroups of one row; the output must also
+    // leave headroom in 64-bit byte counts.
+    if (n > (INT64_C(1) << 31) / q4::gather_blocks_per_row(K, bf16) || n > (INT64_C(1) << 62) / (K * elt))
+        return Q4_ERR_SHAPE;
+    if (!status) return Q4_ERR_NULL;
+    if (n > 0 && (!ids || !out)) return Q4_ERR_NULL;
+    if (n > 0 && M > 0 && (!codes || !scales)) return Q4_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(ids, 4) || !aligned(out, 16) || !aligned(status, 4))
+        return Q4_ERR_ALIGN;
+    const Range ro = range_of(out, (uint64_t)n * K * elt);
+    const Range rs = range_of(status, 4);
+    const Range in[3] = {range_of(codes, (uint64_t)M * (K / 2)), range_of(scales, (uint64_t)M * (K / 64) * 2),
+                         range_of(ids, (uint64_t)n * 4)};
+    for (const Range &r : in)
+        if (overlap(ro, r) || overlap(rs, r)) return Q4_ERR_OVERLAP;
+    if (overlap(ro, rs)) return Q4_ERR_OVERLAP;
+    return launch_status(q4::launch_gather_rows(codes, scales, M, K, ids, n, bf16, out, status,
+                                                (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -29,4 +29,12 @@ hipError_t launch_gemv_fused(const FusedOperand *ops, int count, bool swiglu, in
 hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                               const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
 
+// Rows ids[0..n) of a packed matrix into fp32 or bf16 rows; workgroup 0
+// writes *status.  Arguments are validated by the caller.
+hipError_t launch_gather_rows(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                              const int32_t *ids, int64_t n, bool bf16, void *out, int32_t *status,
+                              hipStream_t stream);
+// Workgroups one output row takes (the grid is n times this).
+int64_t gather_blocks_per_row(int64_t K, bool bf16);
+
 }  // namespace q4

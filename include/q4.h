@@ -185,6 +185,38 @@ int q4_gemv_fused(const q4_operand *ops, int count, int64_t K,
                   const uint16_t *x, int mode, float *const *y,
                   const float *const *residual, void *stream);
 
+/*
+ * Packed row gather (deep-fold "Decode V2" page, run notes of section 6: the
+ * embedding is kept as packed rows and the rows a step needs are dequantised
+ * into its arena, with no dense vocabulary table; a tied embedding shares
+ * the lm_head's packed matrix; golang.design accel/tensor page, func
+ * QuantGatherRows: rows gathered from a quantized table).
+ */
+#define Q4_OUT_F32 0            /* fp32 output rows                           */
+#define Q4_OUT_BF16 1           /* bf16 output rows (bit patterns, uint16)    */
+#define Q4_GATHER_BAD_ID 1      /* status flag: some id outside [0, M)        */
+
+/*
+ * q4_gather_rows -- out[i][k] = What[ids[i], k] for i < n, rounded once to
+ * nearest even (ties to even) from the exact What = level * scale into
+ * out_type (Q4_OUT_F32 or Q4_OUT_BF16).
+ *   codes, scales: the packed M x K matrix (16- and 2-byte aligned).
+ *   ids: int32 [n] device array of row indices (4-byte aligned).
+ *   out: [n][K] fp32 or bf16, 16-byte aligned.
+ *   status: device int32 word, 4-byte aligned; set to 0, or to
+ *     Q4_GATHER_BAD_ID if some ids[i] is outside [0, M).  The row of such an
+ *     id is not written (refused, never clamped).  With n == 0 the call only
+ *     clears *status.
+ * Errors (nothing is launched): Q4_ERR_SHAPE for a bad M, K, n < 0, an
+ * unknown out_type or an output larger than the grid can cover;
+ * Q4_ERR_NULL for a missing status, or ids / out with n > 0, or codes /
+ * scales with n > 0 and M > 0; Q4_ERR_ALIGN; Q4_ERR_OVERLAP if out or status
+ * overlaps an input or each other; Q4_ERR_DEVICE if the launch fails.
+ */
+int q4_gather_rows(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                   const int32_t *ids, int64_t n, int out_type, void *out,
+                   int32_t *status, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused",
-              "q4_codebook", "q4_codes_bytes", "q4_scales_bytes", "q4_status_string"):
+              "q4_gather_rows", "q4_codebook", "q4_codes_bytes", "q4_scales_bytes", "q4_status_string"):
         assert n in names
 
 
@@ -216,6 +216,34 @@ def test_fused_overlap(q4):
     assert _fused(q4, [op, (F, G, 16, 0)], 128, C, SWI, [G + 16]) == q4.Q4_ERR_OVERLAP  # y over up scales
     # every call above fails a host check; the exact-alias residual is legal
     # and is exercised on the GPU, not here
+
+
+def _gather(q4, codes, scales, M, K, ids, n, out_type, out, status):
+    return q4.lib().q4_gather_rows(codes, scales, M, K, ids, n, out_type, out, status, None)
+
+
+def test_gather_errors(q4):
+    F32, BF = q4.Q4_OUT_F32, q4.Q4_OUT_BF16
+    # codes A (M=16, K=128: 1 KB), scales B (64 B), ids C (n=4: 16 B), out D, status E
+    assert _gather(q4, A, B, 16, 100, C, 4, F32, D, E) == q4.Q4_ERR_SHAPE
+    assert _gather(q4, A, B, -1, 128, C, 4, F32, D, E) == q4.Q4_ERR_SHAPE
+    assert _gather(q4, A, B, 16, 128, C, -1, F32, D, E) == q4.Q4_ERR_SHAPE
+    assert _gather(q4, A, B, 16, 128, C, 4, 2, D, E) == q4.Q4_ERR_SHAPE
+    assert _gather(q4, A, B, 16, 128, C, 1 << 40, F32, D, E) == q4.Q4_ERR_SHAPE  # grid too large
+    assert _gather(q4, A, B, 16, 128, C, 4, F32, D, 0) == q4.Q4_ERR_NULL
+    assert _gather(q4, A, B, 16, 128, 0, 4, F32, D, E) == q4.Q4_ERR_NULL
+    assert _gather(q4, A, B, 16, 128, C, 4, F32, 0, E) == q4.Q4_ERR_NULL
+    assert _gather(q4, 0, B, 16, 128, C, 4, F32, D, E) == q4.Q4_ERR_NULL
+    assert _gather(q4, A + 8, B, 16, 128, C, 4, F32, D, E) == q4.Q4_ERR_ALIGN
+    assert _gather(q4, A, B + 1, 16, 128, C, 4, F32, D, E) == q4.Q4_ERR_ALIGN
+    assert _gather(q4, A, B, 16, 128, C + 2, 4, F32, D, E) == q4.Q4_ERR_ALIGN
+    assert _gather(q4, A, B, 16, 128, C, 4, BF, D + 8, E) == q4.Q4_ERR_ALIGN
+    assert _gather(q4, A, B, 16, 128, C, 4, F32, D, E + 2) == q4.Q4_ERR_ALIGN
+    assert _gather(q4, A, B, 16, 128, C, 4, F32, A + 512, E) == q4.Q4_ERR_OVERLAP   # out over codes
+    assert _gather(q4, A, B, 16, 128, C, 4, F32, D, C + 4) == q4.Q4_ERR_OVERLAP     # status over ids
+    assert _gather(q4, A, B, 16, 128, C, 4, BF, D, D + 1020) == q4.Q4_ERR_OVERLAP   # status in out (1 KB)
+    assert _gather(q4, A, B, 16, 128, C, 4, F32, C - 2032, E) == q4.Q4_ERR_OVERLAP  # out's tail over ids
+    # every call above fails a host check and launches nothing
 
 
 def test_binding_refuses_without_library(tmp_path, monkeypatch):

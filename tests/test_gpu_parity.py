@@ -664,3 +664,122 @@ def test_fused_rejects_through_binding(env):
         big = torch.zeros(9, device=dev)
         q4.q4_gemv_fused([(c, s, None)], x, "separate", [big[:8]], [big[1:]])
     del y
+
+
+# ---------------------------------------------------------------------------
+# q4_gather_rows: packed rows dequantised (bit-exact: one rounding of the
+# exact level * scale on both sides)
+# ---------------------------------------------------------------------------
+
+# (M, K, n): one and several workgroups per row (K/4 or K/8 lanes of 256),
+# ragged last workgroups (K = 11008: 2752 / 1376 lanes), repeated ids.
+GATHER_SHAPES = [(1, 64, 1), (37, 192, 6), (300, 2048, 32), (257, 4160, 5), (64, 11008, 9), (9, 16384, 3)]
+
+
+def _gather_case(env, M, K, n, seed, dtype_name):
+    torch, q4, dev = env
+    bf16 = dtype_name == "bf16"
+    W = wl.weights(M, K, seed, std=0.5)
+    codes, scales, st = oracle.pack(W)
+    assert st == 0
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, M, n).astype(np.int32)
+    ref, flags = oracle.gather_rows(codes, scales, M, K, ids, bf16=bf16)
+    assert flags == 0
+    c, s = _upload_packed(env, codes, scales)
+    idd = torch.from_numpy(ids).to(dev)
+    out, status = q4.q4_gather_rows(c, s, idd, torch.bfloat16 if bf16 else torch.float32)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16) if bf16 else out.cpu().numpy()
+    if bf16:
+        assert np.array_equal(got, ref), f"gather bf16 M={M} K={K}: {np.count_nonzero(got != ref)} differ"
+    else:
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"gather f32 M={M} K={K}"
+    _log(f"gather {dtype_name} M={M} K={K} n={n}: bit-exact")
+
+
+@pytest.mark.parametrize("dtype_name", ["f32", "bf16"])
+@pytest.mark.parametrize("M,K,n", GATHER_SHAPES)
+def test_gather_rows_bit_exact(env, M, K, n, dtype_name):
+    _gather_case(env, M, K, n, 7000 + M + K + n, dtype_name)
+
+
+def test_gather_rows_bf16_ties(env):
+    """Rows of +s, -s and 0 with s an exact bf16 midpoint (the fp32 product
+    is exact, so the tie is decided by the even rule alone)."""
+    torch, q4, dev = env
+    K = 128
+    svals = [1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 2 + 2.0 ** -7, 0.5 + 3 * 2.0 ** -9]
+    W = np.zeros((len(svals), K), np.float32)
+    for r, sv in enumerate(svals):
+        W[r, 0::3] = sv
+        W[r, 1::3] = -sv
+    codes, scales, _ = oracle.pack(W)
+    ids = np.array([3, 2, 1, 0, 0], np.int32)
+    ref, _ = oracle.gather_rows(codes, scales, len(svals), K, ids, bf16=True)
+    c, s = _upload_packed(env, codes, scales)
+    out, status = q4.q4_gather_rows(c, s, torch.from_numpy(ids).to(dev), torch.bfloat16)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+
+
+@pytest.mark.parametrize("dtype_name", ["f32", "bf16"])
+def test_gather_rows_refuses_bad_ids(env, dtype_name):
+    torch, q4, dev = env
+    bf16 = dtype_name == "bf16"
+    M, K = 50, 2048
+    codes, scales, _ = oracle.pack(wl.weights(M, K, 7100, std=0.5))
+    ids = np.array([4, -1, M, 49, 2 ** 31 - 1, 0], np.int32)
+    ref, flags = oracle.gather_rows(codes, scales, M, K, ids, bf16=bf16)
+    assert flags == oracle.GATHER_BAD_ID
+    c, s = _upload_packed(env, codes, scales)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    out = torch.full((len(ids), K), float("nan"), dtype=dt, device=dev)
+    sentinel = out.clone()
+    out, status = q4.q4_gather_rows(c, s, torch.from_numpy(ids).to(dev), dt, out)
+    torch.cuda.synchronize()
+    assert int(status.item()) == q4.Q4_GATHER_BAD_ID
+    bad = [1, 2, 4]
+    good = [0, 3, 5]
+    assert torch.equal(out[bad].view(torch.int16 if bf16 else torch.int32),
+                       sentinel[bad].view(torch.int16 if bf16 else torch.int32)), "a refused row was written"
+    got = out[good].view(torch.int16).cpu().numpy().view(np.uint16) if bf16 else out[good].cpu().numpy()
+    exp = ref[good]
+    assert np.array_equal(got.view(np.uint16 if bf16 else np.uint32), exp.view(np.uint16 if bf16 else np.uint32))
+    # the next good call clears the flag; n == 0 clears it too
+    status.fill_(77)
+    q4.q4_gather_rows(c, s, torch.from_numpy(ids[[0, 3]]).to(dev), dt, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    status.fill_(77)
+    q4.q4_gather_rows(c, s, torch.empty(0, dtype=torch.int32, device=dev), dt, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+
+
+def test_gather_rows_tied_lm_head_full_size(env):
+    """The tied embedding: rows of the full lm_head matrix (151936 x 2048),
+    packed by the oracle, gathered for a 32-token chunk and one token."""
+    torch, q4, dev = env
+    cfg = wl.CONFIGS["lm_head"]
+    M, K = cfg["M"], cfg["K"]
+    W = wl.weights(M, K, cfg["seed"])
+    codes, scales, st = oracle.pack(W, threads=min(16, os.cpu_count() or 1))
+    assert st == 0
+    del W
+    c, s = _upload_packed(env, codes, scales)
+    rng = np.random.default_rng(7200)
+    for n in (32, 1):
+        ids = rng.integers(0, M, n).astype(np.int32)
+        ids[0] = M - 1
+        for bf16 in (False, True):
+            ref, _ = oracle.gather_rows(codes, scales, M, K, ids, bf16=bf16)
+            out, status = q4.q4_gather_rows(c, s, torch.from_numpy(ids).to(dev),
+                                            torch.bfloat16 if bf16 else torch.float32)
+            torch.cuda.synchronize()
+            assert int(status.item()) == 0
+            got = out.view(torch.int16).cpu().numpy().view(np.uint16) if bf16 else out.cpu().numpy().view(np.uint32)
+            assert np.array_equal(got, ref.view(np.uint16 if bf16 else np.uint32)), f"lm_head gather n={n} bf16={bf16}"
+    _log("gather lm_head 151936x2048: bit-exact for n=32 and n=1, fp32 and bf16")
