@@ -290,7 +290,7 @@ def q4_gemv_fused(ops, x, mode="separate", ys=None, residuals=None, stream=None)
 def q4_gather_rows(codes, scales, ids, out_dtype=None, out=None, status=None, stream=None):
     """Rows ids (int32 [n]) of a packed matrix, dequantised: returns (out
     [n, K] fp32 or bf16, status int32 [1]).  status is 0, or Q4_GATHER_BAD_ID
-    when some id is outside [0, M); the rows of such ids are not written."""
+    when some id is outside [0, M); the rows of such ids are zeros."""
     torch = _torch()
     M, K = _mk(codes, scales)
     dev = codes.device

@@ -16,6 +16,9 @@
 // wrongly when the first one moved the value onto the bf16 midpoint; the
 // exact remainder fma(c, s, -p) tells which side of the midpoint the exact
 // product lies on, so the bf16 result is one rounding of the exact value.
+// An id outside [0, M) is a caller error (accel/tensor func GatherRows): its
+// row is written as zeros, the table is not read, and the status word gets
+// Q4_GATHER_BAD_ID.
 //
 // Work split: one lane writes one 16-byte vector of a row (4 fp32 or 8 bf16
 // values) from 2 or 4 bytes of codes; consecutive lanes take consecutive
@@ -72,12 +75,20 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
     const int64_t i = blockIdx.x / bpr;  // output row
     if (i >= n) return;
     const int64_t id = ids[i];
-    if (id < 0 || id >= M) return;       // refused: the row is left as it was
     constexpr int kPer = BF16 ? 8 : 4;    // weights per lane
     const int units = K / kPer;
     const int u = (int)(blockIdx.x % bpr) * kGatherThreads + (int)threadIdx.x;
     if (u >= units) return;
     const int k0 = u * kPer;
+    if (id < 0 || id >= M) {
+        // A caller error: the row comes out as zeros (the table is never
+        // read outside its rows) and the status word carries the flag.
+        if constexpr (BF16)
+            *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + i * (int64_t)K + k0) = make_uint4(0, 0, 0, 0);
+        else
+            *reinterpret_cast<float4 *>(static_cast<float *>(out) + i * (int64_t)K + k0) = make_float4(0, 0, 0, 0);
+        return;
+    }
     const uint8_t *crow = codes + id * (int64_t)(K / 2);
     const float s = f16_bits_to_f32(scales[id * (int64_t)(K / 64) + k0 / 64]);
     if constexpr (BF16) {

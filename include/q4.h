@@ -204,8 +204,9 @@ int q4_gemv_fused(const q4_operand *ops, int count, int64_t K,
  *   ids: int32 [n] device array of row indices (4-byte aligned).
  *   out: [n][K] fp32 or bf16, 16-byte aligned.
  *   status: device int32 word, 4-byte aligned; set to 0, or to
- *     Q4_GATHER_BAD_ID if some ids[i] is outside [0, M).  The row of such an
- *     id is not written (refused, never clamped).  With n == 0 the call only
+ *     Q4_GATHER_BAD_ID if some ids[i] is outside [0, M).  Such an id is a
+ *     caller error (accel/tensor func GatherRows): its row is written as
+ *     zeros and the table is not read there.  With n == 0 the call only
  *     clears *status.
  * Errors (nothing is launched): Q4_ERR_SHAPE for a bad M, K, n < 0, an
  * unknown out_type or an output larger than the grid can cover;

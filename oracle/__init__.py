@@ -256,8 +256,8 @@ def f64_to_bf16_bits(v: float) -> int:
 
 def gather_rows(codes, scales, M: int, K: int, ids, bf16: bool = False, out=None):
     """(out, flags): out[i] = What[ids[i]] rounded once to fp32 (or bf16 bits,
-    uint16); rows of ids outside [0, M) keep what `out` held (NaN / 0xFFFF
-    when out is None) and set GATHER_BAD_ID in flags."""
+    uint16); rows of ids outside [0, M) are zeros and set GATHER_BAD_ID in
+    flags."""
     _check_shape(M, K)
     codes = np.ascontiguousarray(codes, np.uint8)
     scales = np.ascontiguousarray(scales, np.uint16)

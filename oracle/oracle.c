@@ -388,8 +388,17 @@ int32_t oracle_gather_rows(const uint8_t *codes, const uint16_t *scales, int64_t
     for (int64_t i = 0; i < n; ++i) {
         const int64_t m = ids[i];
         if (m < 0 || m >= M) {
+            /* accel/tensor func GatherRows: an out-of-range id is a caller
+             * error and its row comes out as zeros, never read from outside
+             * the table; the flag is the diagnostic. */
             flags |= ORACLE_GATHER_BAD_ID;
-            continue; /* the row of a refused id is left as it was */
+            for (int64_t k = 0; k < K; ++k) {
+                if (bf16)
+                    ((uint16_t *)out)[i * K + k] = 0;
+                else
+                    ((float *)out)[i * K + k] = 0.0f;
+            }
+            continue;
         }
         for (int64_t k = 0; k < K; ++k) {
             const double sc = oracle_f16_to_f64(scales[m * (K / 64) + k / 64]);

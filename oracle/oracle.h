@@ -100,8 +100,8 @@ uint16_t oracle_f64_to_bf16_rne(double v);
  * page, func QuantGatherRows).  For i < n with 0 <= ids[i] < M:
  *   out[i][k] = What[ids[i], k] rounded once to fp32 (bf16 == 0) or to bf16
  *               bits (bf16 != 0), nearest-even; What = c * s is exact.
- * Rows of ids outside [0, M) are left untouched and ORACLE_GATHER_BAD_ID is
- * returned in the flags. */
+ * An id outside [0, M) is a caller error (accel/tensor func GatherRows): its
+ * row is written as zeros and ORACLE_GATHER_BAD_ID is returned in the flags. */
 #define ORACLE_GATHER_BAD_ID 1
 int32_t oracle_gather_rows(const uint8_t *codes, const uint16_t *scales, int64_t M,
                            int64_t K, const int32_t *ids, int64_t n, int bf16, void *out);

@@ -44,6 +44,8 @@ MUTANTS = {
     "bf16_truncate": ("    if (frac > 0.5)\n        r = fl + 1.0;\n    else if (frac < 0.5)\n        r = fl;\n    else\n        r = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;\n    double u = r * q; /* the rounded magnitude */",
                       "    r = fl;\n    double u = r * q; /* the rounded magnitude */"),
     "gather_ignores_ids": ("const int64_t m = ids[i];", "const int64_t m = i;"),
+    "gather_bad_row_untouched": ("                    ((float *)out)[i * K + k] = 0.0f;",
+                                 "                    (void)0;"),
     "gather_accepts_id_M": ("if (m < 0 || m >= M) {", "if (m < 0 || m > M) {"),
     "gather_fp32_via_bf16": ("((float *)out)[i * K + k] = (float)w;",
                              "((float *)out)[i * K + k] = (float)oracle_bf16_to_f64(oracle_f64_to_bf16_rne(w));"),

@@ -675,7 +675,8 @@ def test_gather_refuses_out_of_range_ids(oracle_mod):
     ids = np.array([-1, M, 2, 2**31 - 1, 0], np.int32)
     out, flags = oracle_mod.gather_rows(codes, scales, M, K, ids)
     assert flags == oracle_mod.GATHER_BAD_ID
-    assert np.all(np.isnan(out[[0, 1, 3]]))
+    # accel/tensor func GatherRows: the row of an out-of-range id is zeros
+    assert np.all(out[[0, 1, 3]].view(np.uint32) == 0)
     What = oracle_mod.dequant(codes, scales, M, K)
     assert np.array_equal(out[2], What[2].astype(np.float32))
     assert np.array_equal(out[4], What[0].astype(np.float32))
