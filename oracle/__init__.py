@@ -81,6 +81,14 @@ def _load():
         lib.oracle_argmax_f64.restype = I64
         lib.oracle_argmax_f32.argtypes = [P, I64]
         lib.oracle_argmax_f32.restype = I64
+        lib.oracle_f64_to_f16_rne.argtypes = [ctypes.c_double]
+        lib.oracle_f64_to_f16_rne.restype = ctypes.c_uint16
+        lib.oracle_pack_affine_rows.argtypes = [P, I64, I64, I64, I64, P, P, P]
+        lib.oracle_pack_affine_rows.restype = ctypes.c_int
+        lib.oracle_dequant_affine.argtypes = [P, P, P, I64, I64, P]
+        lib.oracle_dequant_affine.restype = None
+        lib.oracle_gemv_affine_rows.argtypes = [P, P, P, I64, I64, P, I64, I64, P, P]
+        lib.oracle_gemv_affine_rows.restype = None
         lib.oracle_f64_to_bf16_rne.argtypes = [ctypes.c_double]
         lib.oracle_f64_to_bf16_rne.restype = ctypes.c_uint16
         lib.oracle_gather_rows.argtypes = [P, P, I64, I64, P, I64, ctypes.c_int, P]
@@ -244,6 +252,66 @@ def epilogue(t0, t1=None, bias0=None, bias1=None, residual=None, swiglu: bool = 
                             _ptr(b1) if b1 is not None else nullp, _ptr(r) if r is not None else nullp,
                             n, 1 if swiglu else 0, _ptr(out))
     return out
+
+
+def f64_to_f16_bits(v: float) -> int:
+    """One rounding of a double to IEEE binary16 bits, nearest-even."""
+    return int(_load().oracle_f64_to_f16_rne(float(v)))
+
+
+def pack_affine(W: np.ndarray, threads: int = 1):
+    """(codes uint8 [M, K/2], scales fp16 bits [M, K/64], zeros fp16 bits
+    [M, K/64], status) of the affine 4-bit format."""
+    W = np.ascontiguousarray(W, np.float32)
+    M, K = W.shape
+    _check_shape(M, K)
+    codes = np.zeros((M, K // 2), np.uint8)
+    scales = np.zeros((M, K // 64), np.uint16)
+    zeros = np.zeros((M, K // 64), np.uint16)
+    lib = _load()
+    status = [0]
+
+    def run(r0, r1, slot):
+        slot.append(lib.oracle_pack_affine_rows(_ptr(W), M, K, r0, r1, _ptr(codes), _ptr(scales), _ptr(zeros)))
+
+    _run_rows(M, threads, run, status)
+    st = 0
+    for v in status[1:]:
+        st |= v
+    return codes, scales, zeros, st
+
+
+def dequant_affine(codes, scales, zeros, M: int, K: int) -> np.ndarray:
+    _check_shape(M, K)
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint16)
+    zeros = np.ascontiguousarray(zeros, np.uint16)
+    out = np.zeros((M, K), np.float64)
+    _load().oracle_dequant_affine(_ptr(codes), _ptr(scales), _ptr(zeros), M, K, _ptr(out))
+    return out
+
+
+def gemv_affine(codes, scales, zeros, M: int, K: int, x_bits, rows=None, threads: int = 1):
+    """y, S (fp64, length M) of the affine format; rows=(r0, r1) restricts
+    the work (other entries NaN)."""
+    _check_shape(M, K)
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint16)
+    zeros = np.ascontiguousarray(zeros, np.uint16)
+    x_bits = np.ascontiguousarray(x_bits, np.uint16)
+    if x_bits.size != K:
+        raise ValueError("oracle.gemv_affine: x must have K entries")
+    y = np.full(M, np.nan)
+    S = np.full(M, np.nan)
+    lib = _load()
+    r0, r1 = (0, M) if rows is None else rows
+
+    def run(a, b, slot):
+        lib.oracle_gemv_affine_rows(_ptr(codes), _ptr(scales), _ptr(zeros), M, K, _ptr(x_bits), r0 + a, r0 + b,
+                                    _ptr(y), _ptr(S))
+
+    _run_rows(r1 - r0, threads, run, [0])
+    return y, S
 
 
 GATHER_BAD_ID = 1

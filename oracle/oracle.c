@@ -120,10 +120,12 @@ double oracle_bf16_to_f64(uint16_t b) {
     return (double)f;
 }
 
-uint16_t oracle_f32_to_f16_rne(float v) {
+uint16_t oracle_f32_to_f16_rne(float v) { return oracle_f64_to_f16_rne((double)v); }
+
+uint16_t oracle_f64_to_f16_rne(double v) {
     uint16_t sign = signbit(v) ? 0x8000 : 0;
     if (isnan(v)) return (uint16_t)(sign | 0x7e00);
-    double a = fabs((double)v);
+    double a = fabs(v);
     /* Halfway between the largest finite half (65504) and the next step
      * (65536) is 65520; ties-to-even goes up there, so >= 65520 is inf. */
     if (a >= 65520.0) return (uint16_t)(sign | 0x7c00);
@@ -410,4 +412,106 @@ int32_t oracle_gather_rows(const uint8_t *codes, const uint16_t *scales, int64_t
         }
     }
     return flags;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Affine 4-bit format (golang.design accel/tensor: type Int4 holds 4-bit    */
+/* codes, low nibble first, with an f16 scale and an f16 zero point per      */
+/* group; func Int4MatVec reconstructs a weight as (code - z) * s; the       */
+/* accuracy stated there is a group's range over 30).  Reading taken for the */
+/* quantiser, which the page does not print:                                 */
+/*   - groups of 64 weights along K, as the NF4 format;                      */
+/*   - the group's range [lo, hi] is widened to hold 0 (so the zero point is */
+/*     a code and an all-zero group is exact); s = fp16 RNE of              */
+/*     (hi - lo) / 15 (fp64 subtraction and division, one rounding each),    */
+/*     so the spacing of the levels is the range over 15 and the error at    */
+/*     most half of it: the range over 30;                                   */
+/*   - z = the integer nearest to -lo / s in 0..15, an exact midpoint going  */
+/*     down, written as #{ j in 0..14 : -lo > (j + 1/2) s }; stored as f16   */
+/*     (exact);                                                              */
+/*   - code = the level (j - z) s nearest to w, an exact midpoint going to   */
+/*     the lower code: #{ j in 0..14 : w > (j - z + 1/2) s }.  Every product */
+/*     and comparison is exact (a half-integer of at most 5 bits times an    */
+/*     11-bit s, against an fp32 w);                                         */
+/*   - s == 0 (the widened range is 0 or below the fp16 range): codes 0 and  */
+/*     z = 0, every weight reconstructs to 0;                                */
+/*   - refusals as the NF4 pack: a non-finite weight, or s rounding to       */
+/*     infinity.                                                             */
+/* ------------------------------------------------------------------------ */
+
+int oracle_pack_affine_rows(const float *W, int64_t M, int64_t K, int64_t row0, int64_t row1,
+                            uint8_t *codes, uint16_t *scales, uint16_t *zeros) {
+    (void)M;
+    const int64_t nblk = K / 64;
+    int status = 0;
+    for (int64_t m = row0; m < row1; ++m) {
+        for (int64_t b = 0; b < nblk; ++b) {
+            const float *w = W + m * K + b * 64;
+            float lo = 0.0f, hi = 0.0f;
+            int bad = 0;
+            for (int k = 0; k < 64; ++k) {
+                if (!isfinite(w[k])) bad = 1;
+                if (w[k] < lo) lo = w[k];
+                if (w[k] > hi) hi = w[k];
+            }
+            if (bad) {
+                status |= ORACLE_PACK_NONFINITE;
+                continue;
+            }
+            const uint16_t s16 = oracle_f64_to_f16_rne(((double)hi - (double)lo) / 15.0);
+            if (s16 == 0x7c00) {
+                status |= ORACLE_PACK_OVERFLOW;
+                continue;
+            }
+            const double s = oracle_f16_to_f64(s16);
+            int z = 0;
+            if (s > 0.0)
+                for (int j = 0; j < 15; ++j)
+                    if (-(double)lo > ((double)j + 0.5) * s) ++z;
+            scales[m * nblk + b] = s16;
+            zeros[m * nblk + b] = oracle_f64_to_f16_rne((double)z);
+            uint8_t code[64];
+            for (int k = 0; k < 64; ++k) {
+                int c = 0;
+                if (s > 0.0)
+                    for (int j = 0; j < 15; ++j)
+                        if ((double)w[k] > ((double)(j - z) + 0.5) * s) ++c;
+                code[k] = (uint8_t)c;
+            }
+            uint8_t *out = codes + m * (K / 2) + b * 32;
+            for (int j = 0; j < 32; ++j)
+                out[j] = (uint8_t)((code[2 * j + 1] << 4) | code[2 * j]); /* low nibble first */
+        }
+    }
+    return status;
+}
+
+void oracle_dequant_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
+                           int64_t K, double *What) {
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t g = m * (K / 64) + k / 64;
+            What[m * K + k] = ((double)code_at(codes, K, m, k) - oracle_f16_to_f64(zeros[g])) *
+                              oracle_f16_to_f64(scales[g]); /* exact */
+        }
+}
+
+/* y[m] = sum_k What[m,k] x[k] in fp64 over ascending k (each term exact), and
+ * S[m] = sum_k |What[m,k] x[k]|, for m in [row0, row1). */
+void oracle_gemv_affine_rows(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
+                             int64_t K, const uint16_t *x, int64_t row0, int64_t row1, double *y, double *S) {
+    (void)M;
+    for (int64_t m = row0; m < row1; ++m) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t g = m * (K / 64) + k / 64;
+            const double w = ((double)code_at(codes, K, m, k) - oracle_f16_to_f64(zeros[g])) *
+                             oracle_f16_to_f64(scales[g]);
+            const double term = w * oracle_bf16_to_f64(x[k]);
+            acc += term;
+            mag += fabs(term);
+        }
+        y[m] = acc;
+        if (S) S[m] = mag;
+    }
 }

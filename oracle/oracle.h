@@ -40,6 +40,8 @@ double oracle_phi_inv(double p);
 /* fp32 -> IEEE binary16 bits, round to nearest, ties to even; |v| >= 65520
  * gives +-inf; NaN gives a quiet NaN. */
 uint16_t oracle_f32_to_f16_rne(float v);
+/* The same rounding from a double (one rounding of the exact value). */
+uint16_t oracle_f64_to_f16_rne(double v);
 void oracle_f32_to_f16_rne_array(const float *v, int64_t n, uint16_t *out);
 double oracle_f16_to_f64(uint16_t h);
 /* bf16 bits -> value (exact widening). */
@@ -105,6 +107,20 @@ uint16_t oracle_f64_to_bf16_rne(double v);
 #define ORACLE_GATHER_BAD_ID 1
 int32_t oracle_gather_rows(const uint8_t *codes, const uint16_t *scales, int64_t M,
                            int64_t K, const int32_t *ids, int64_t n, int bf16, void *out);
+
+/* Affine 4-bit format (golang.design accel/tensor page: type Int4, func
+ * Int4MatVec: What = (code - z) * s with an f16 scale and an f16 zero point
+ * per group; the error is at most the group's range over 30).  Groups of 64
+ * along K; codes laid out as the NF4 format; scales and zeros fp16 bits
+ * [M][K/64].  The quantiser's steps are in oracle.c.  Returns the OR of
+ * ORACLE_PACK_* flags; a flagged block's output is unspecified. */
+int oracle_pack_affine_rows(const float *W, int64_t M, int64_t K, int64_t row0, int64_t row1,
+                            uint8_t *codes, uint16_t *scales, uint16_t *zeros);
+void oracle_dequant_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros,
+                           int64_t M, int64_t K, double *What);
+void oracle_gemv_affine_rows(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros,
+                             int64_t M, int64_t K, const uint16_t *x, int64_t row0, int64_t row1,
+                             double *y, double *S);
 
 /* First index of the maximum (NaN never wins); -1 if n == 0 or all NaN. */
 int64_t oracle_argmax_f64(const double *y, int64_t n);

@@ -49,6 +49,18 @@ MUTANTS = {
     "gather_accepts_id_M": ("if (m < 0 || m >= M) {", "if (m < 0 || m > M) {"),
     "gather_fp32_via_bf16": ("((float *)out)[i * K + k] = (float)w;",
                              "((float *)out)[i * K + k] = (float)oracle_bf16_to_f64(oracle_f64_to_bf16_rne(w));"),
+    "affine_zero_sign": ("What[m * K + k] = ((double)code_at(codes, K, m, k) - oracle_f16_to_f64(zeros[g])) *",
+                         "What[m * K + k] = ((double)code_at(codes, K, m, k) + oracle_f16_to_f64(zeros[g])) *"),
+    "affine_range_without_zero": ("float lo = 0.0f, hi = 0.0f;", "float lo = w[0], hi = w[0];"),
+    "affine_scale_over_16": ("((double)hi - (double)lo) / 15.0", "((double)hi - (double)lo) / 16.0"),
+    "affine_zero_tie_up": ("if (-(double)lo > ((double)j + 0.5) * s) ++z;",
+                           "if (-(double)lo >= ((double)j + 0.5) * s) ++z;"),
+    "affine_code_tie_up": ("if ((double)w[k] > ((double)(j - z) + 0.5) * s) ++c;",
+                           "if ((double)w[k] >= ((double)(j - z) + 0.5) * s) ++c;"),
+    "affine_gemv_ignores_zero": ("const double w = ((double)code_at(codes, K, m, k) - oracle_f16_to_f64(zeros[g])) *",
+                                 "const double w = ((double)code_at(codes, K, m, k)) *"),
+    "f16_via_f32": ("    if (isnan(v)) return (uint16_t)(sign | 0x7e00);\n    double a = fabs(v);",
+                    "    if (isnan(v)) return (uint16_t)(sign | 0x7e00);\n    double a = fabs((double)(float)v);"),
     "residual_dropped": ("if (residual) v += (double)residual[i];", "if (residual && !swiglu) v += (double)residual[i];"),
 }
 

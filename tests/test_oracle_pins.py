@@ -682,3 +682,163 @@ def test_gather_refuses_out_of_range_ids(oracle_mod):
     assert np.array_equal(out[4], What[0].astype(np.float32))
     ok, flags = oracle_mod.gather_rows(codes, scales, M, K, np.array([], np.int32))
     assert flags == 0 and ok.shape == (0, K)
+
+
+# ---------------------------------------------------------------------------
+# Affine 4-bit format: What = (code - z) * s per 64-block
+# ---------------------------------------------------------------------------
+
+def test_f64_to_f16_matches_numpy_single_rounding(oracle_mod):
+    rng = np.random.default_rng(21)
+    vals = list(rng.standard_normal(3000) * np.exp2(rng.integers(-30, 17, 3000)))
+    # just beyond fp16 ties, where a detour through fp32 would round wrongly
+    vals += [1 + 2.0 ** -11 + 2.0 ** -40, 1 + 2.0 ** -11 - 2.0 ** -40, 3 * 2.0 ** -25 + 2.0 ** -60,
+             65519.99, 65520.0, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11]
+    for v in vals:
+        with np.errstate(over="ignore"):
+            ref = int(np.array([np.float16(v)]).view(np.uint16)[0])
+        assert oracle_mod.f64_to_f16_bits(v) == ref, v
+
+
+def _affine_block_params(w):
+    """(s, z) of one block from the reading, written independently with exact
+    rationals: range widened to hold 0, s = fp16 RNE of range/15 (numpy's
+    single rounding of the fp64 quotient), z = nearest integer to -lo/s in
+    0..15 with a midpoint going down."""
+    lo = min(0.0, float(np.min(w)))
+    hi = max(0.0, float(np.max(w)))
+    s = float(np.float16((hi - lo) / 15.0))
+    if s == 0.0:
+        return 0.0, 0
+    t = Fraction(-lo) / Fraction(s)
+    z = int(t)  # floor (t >= 0)
+    if t - z > Fraction(1, 2):
+        z += 1
+    return s, min(z, 15)
+
+
+def _affine_unpack(codes, M, K):
+    c = np.zeros((M, K), np.int64)
+    c[:, 0::2] = codes & 0xF
+    c[:, 1::2] = codes >> 4
+    return c
+
+
+def test_affine_pack_brute_force(oracle_mod):
+    M, K = 6, 256
+    W = wl.weights(M, K, 31, std=0.7)
+    W[1, 64:128] += 3.0          # a block far from zero (z = 0 side)
+    W[2, 0:64] -= 2.0            # and the other side (z = 15)
+    W[3, 128:192] = 0.0          # all zero: s = 0
+    W[4, 192:256] = 0.25         # constant positive
+    codes, scales, zeros, st = oracle_mod.pack_affine(W)
+    assert st == 0
+    c = _affine_unpack(codes, M, K)
+    for m in range(M):
+        for b in range(K // 64):
+            w = W[m, 64 * b:64 * b + 64].astype(np.float64)
+            s, z = _affine_block_params(w)
+            assert scales[m, b] == np.array([np.float16(s)]).view(np.uint16)[0]
+            assert zeros[m, b] == np.array([np.float16(z)]).view(np.uint16)[0]
+            lv = (np.arange(16) - z) * s
+            for k in range(64):
+                code = c[m, 64 * b + k]
+                if s == 0.0:
+                    assert code == 0
+                    continue
+                d = np.abs(lv - w[k])
+                best = int(np.flatnonzero(d == d.min())[0])  # lowest code on a tie
+                assert code == best, (m, b, k)
+
+
+def test_affine_closed_forms(oracle_mod):
+    K = 64
+    W = np.zeros((4, K), np.float32)
+    W[0, :] = 0.25                       # [0, 0.25]: z = 0, codes 15
+    W[1, :] = -1.5                       # [-1.5, 0]: s = 0.1, z = 15, codes 0
+    W[2, 0::2], W[2, 1::2] = 1.5, -1.5   # [-1.5, 1.5]: s = 0.2, z = 7.5 -> 7 (midpoint down)
+    codes, scales, zeros, st = oracle_mod.pack_affine(W)
+    assert st == 0
+    s = scales.view(np.float16).astype(np.float64)
+    z = zeros.view(np.float16).astype(np.float64)
+    c = _affine_unpack(codes, 4, K)
+    assert s[0, 0] == np.float16(0.25 / 15) and z[0, 0] == 0 and np.all(c[0] == 15)
+    assert s[1, 0] == np.float16(0.1) and z[1, 0] == 15 and np.all(c[1] == 0)
+    assert s[2, 0] == np.float16(0.2)
+    assert z[2, 0] == (7 if 1.5 / float(np.float16(0.2)) <= 7.5 else 8)  # fp16(0.2) < 0.2: 8
+    assert np.all(s[3] == 0) and np.all(z[3] == 0) and np.all(c[3] == 0)
+    What = oracle_mod.dequant_affine(codes, scales, zeros, 4, K)
+    assert np.all(What[3] == 0.0)
+    assert np.all(What[0] == 15 * s[0, 0]) and np.all(What[1] == -15 * s[1, 0])
+
+
+def test_affine_error_is_at_most_range_over_30(oracle_mod):
+    M, K = 64, 512
+    W = wl.weights(M, K, 32, std=1.0) + np.float32(0.3)
+    codes, scales, zeros, st = oracle_mod.pack_affine(W)
+    assert st == 0
+    What = oracle_mod.dequant_affine(codes, scales, zeros, M, K)
+    s = np.repeat(scales.view(np.float16).astype(np.float64), 64, axis=1)
+    err = np.abs(What - W)
+    # half a level step, plus the fp16 rounding of s stretched over 15 steps
+    assert np.all(err <= s * (0.5 + 15 * 2.0 ** -11) + 1e-12)
+    blk = W.reshape(M, K // 64, 64).astype(np.float64)
+    rng_ = np.maximum(blk.max(2), 0) - np.minimum(blk.min(2), 0)
+    assert np.all(err.reshape(M, K // 64, 64).max(2) <= rng_ / 30 * (1 + 2.0 ** -9) + 1e-12)
+
+
+def test_affine_refuses_nonfinite_and_overflow(oracle_mod):
+    W = np.zeros((3, 128), np.float32)
+    W[0, 3] = np.nan
+    W[1, 70] = np.inf
+    _, _, _, st = oracle_mod.pack_affine(W[:2])
+    assert st == oracle_mod.PACK_NONFINITE
+    W2 = np.zeros((1, 64), np.float32)
+    W2[0, 0], W2[0, 1] = 6.0e5, -6.0e5  # range / 15 = 8e4 >= 65520
+    assert oracle_mod.pack_affine(W2)[3] == oracle_mod.PACK_OVERFLOW
+    W2[0, 0], W2[0, 1] = 4.0e5, -4.0e5  # 53333: fits
+    assert oracle_mod.pack_affine(W2)[3] == 0
+
+
+def test_affine_dequant_hand_built(oracle_mod):
+    K = 64
+    codes = np.zeros((1, 32), np.uint8)
+    codes[0, 0] = 0x5A  # k=0 -> code 10, k=1 -> code 5
+    codes[0, 1] = 0xF0  # k=2 -> 0, k=3 -> 15
+    scales = np.array([[np.float16(0.5)]]).view(np.uint16)
+    zeros = np.array([[np.float16(6.0)]]).view(np.uint16)
+    What = oracle_mod.dequant_affine(codes, scales, zeros, 1, K)
+    assert list(What[0, :4]) == [2.0, -0.5, -3.0, 4.5]
+    assert np.all(What[0, 4:] == -3.0)
+
+
+def test_affine_gemv_matches_blas_and_one_hot(oracle_mod):
+    M, K = 33, 320
+    W = wl.weights(M, K, 33, std=0.5)
+    codes, scales, zeros, st = oracle_mod.pack_affine(W)
+    x = wl.activation(K, 33, "normal")
+    y, S = oracle_mod.gemv_affine(codes, scales, zeros, M, K, x)
+    What = oracle_mod.dequant_affine(codes, scales, zeros, M, K)
+    xv = wl.bf16_bits_to_f32(x).astype(np.float64)
+    assert np.allclose(y, What @ xv, rtol=1e-12, atol=1e-12)
+    assert np.allclose(S, np.abs(What) @ np.abs(xv), rtol=1e-12)
+    for k in (0, 63, 64, 319):
+        e = np.zeros(K, np.uint16)
+        e[k] = 0x3F80  # bf16 1.0
+        yk, _ = oracle_mod.gemv_affine(codes, scales, zeros, M, K, e)
+        assert np.array_equal(yk, What[:, k])
+
+
+def test_affine_exact_ties_go_down(oracle_mod):
+    """s = 0.125 exactly (range 1.875 / 15) and -lo / s = 7.5 exactly: z takes
+    the lower integer 7; weights on a level midpoint take the lower code."""
+    W = np.zeros((1, 64), np.float32)
+    W[0, :4] = [0.9375, -0.9375, 0.0625, -0.0625]
+    W[0, 4] = 0.1875  # midpoint of levels 1*s and 2*s above z
+    codes, scales, zeros, st = oracle_mod.pack_affine(W)
+    assert st == 0
+    assert scales.view(np.float16)[0, 0] == 0.125 and zeros.view(np.float16)[0, 0] == 7.0
+    c = _affine_unpack(codes, 1, 64)
+    assert list(c[0, :5]) == [14, 0, 7, 6, 8]
+    What = oracle_mod.dequant_affine(codes, scales, zeros, 1, 64)
+    assert list(What[0, :5]) == [0.875, -0.875, 0.0, -0.125, 0.125]
