@@ -32,7 +32,7 @@ Q4_PACK_OVERFLOW = 2
 
 EXPORTED = ("q4_codes_bytes", "q4_scales_bytes", "q4_codebook", "q4_status_string",
             "q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused",
-            "q4_gather_rows")
+            "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine")
 
 Q4_OUT_F32 = 0
 Q4_OUT_BF16 = 1
@@ -89,6 +89,10 @@ def lib() -> ctypes.CDLL:
         L.q4_gemv_fused.restype = I32
         L.q4_gather_rows.argtypes = [P, P, I64, I64, P, I64, I32, P, P, P]
         L.q4_gather_rows.restype = I32
+        L.q4_pack_affine.argtypes = [P, I64, I64, P, P, P, P, P]
+        L.q4_pack_affine.restype = I32
+        L.q4_gemv_affine.argtypes = [P, P, P, I64, I64, P, P, P]
+        L.q4_gemv_affine.restype = I32
         _lib = L
         return L
 
@@ -314,3 +318,53 @@ def q4_gather_rows(codes, scales, ids, out_dtype=None, out=None, status=None, st
     if st != Q4_OK:
         raise Q4Error(st, "q4_gather_rows")
     return out, status
+
+
+def q4_pack_affine(W, codes=None, scales=None, zeros=None, status=None, stream=None):
+    """Quantise fp32 W [M, K] into the affine format -> (codes uint8 [M, K/2],
+    scales fp16 [M, K/64], zeros fp16 [M, K/64], status int32 [1])."""
+    torch = _torch()
+    if W.dim() != 2:
+        raise ValueError("W must be [M, K]")
+    M, K = W.shape
+    dev = W.device
+    _check(W, "W", torch.float32, dev)
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((M, K // 64), dtype=torch.float16, device=dev)
+    if zeros is None:
+        zeros = torch.empty((M, K // 64), dtype=torch.float16, device=dev)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(codes, "codes", torch.uint8, dev)
+    _check(scales, "scales", torch.float16, dev)
+    _check(zeros, "zeros", torch.float16, dev)
+    _check(status, "status", torch.int32, dev)
+    if codes.numel() * 2 != M * K or scales.numel() * 64 != M * K or zeros.numel() * 64 != M * K:
+        raise ValueError("codes / scales / zeros sizes do not match W")
+    st = lib().q4_pack_affine(_ptr(W), M, K, _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(status), _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_pack_affine")
+    return codes, scales, zeros, status
+
+
+def q4_gemv_affine(codes, scales, zeros, x, y=None, stream=None):
+    """y fp32 [M] = W . x for an affine-format W and bf16 x [K]."""
+    torch = _torch()
+    M, K = _mk(codes, scales)
+    _check(zeros, "zeros", torch.float16, codes.device)
+    if tuple(zeros.shape) != tuple(scales.shape):
+        raise ValueError("zeros must have the shape of scales")
+    _check(x, "x", torch.bfloat16, codes.device)
+    if x.numel() != K:
+        raise ValueError(f"x must have K={K} entries")
+    if y is None:
+        y = torch.empty(M, dtype=torch.float32, device=codes.device)
+    _check(y, "y", torch.float32, codes.device)
+    if y.numel() != M:
+        raise ValueError(f"y must have M={M} entries")
+    st = lib().q4_gemv_affine(_ptr(codes), _ptr(scales), _ptr(zeros), M, K, _ptr(x), _ptr(y), _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_gemv_affine")
+    return y

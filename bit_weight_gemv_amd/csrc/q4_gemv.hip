@@ -171,6 +171,7 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z));
 struct GemvSeg {
     const uint8_t *codes0;
     const uint16_t *scales0;
+    const uint16_t *zeros0;  // affine format only: fp16 zero points [rows][K/64]
     const uint8_t *codes1;
     const uint16_t *scales1;
     const float *bias0;
@@ -187,15 +188,24 @@ struct GemvSegs {
     GemvSeg s[kMaxSegs];
     int32_t n;
 };
-enum { kModePlain = 0, kModeAffine = 1, kModeSwiglu = 2 };
+enum { kModePlain = 0, kModeEpi = 1, kModeSwiglu = 2 };
+// Weight formats: the NF4 codebook (level[code] * s), or the affine format
+// ((code - z) * s with an fp16 zero point per 64-block; golang.design
+// accel/tensor, type Int4 and func Int4MatVec).
+enum { kFmtNf4 = 0, kFmtAffine = 1 };
 
 // The GEMV of one segment by one workgroup (index `wg` within the segment).
-// MODE kModePlain: y = W . x.  kModeAffine: y = W . x (+ bias0) (+ residual).
+// MODE kModePlain: y = W . x.  kModeEpi: y = W . x (+ bias0) (+ residual).
 // kModeSwiglu: each tile holds NR/2 gate rows and the NR/2 up rows of the
 // same outputs; after the full reduction lane pairs are brought together and
 // y = silu(g (+ bias0)) * (u (+ bias1)) (+ residual) -- SiLU only ever sees
 // a finished sum (deep-fold "Decode V2" page, section 6 Linear primitive).
-template <int NR, int CPL, int S, int RG, bool MULTI, int MODE>
+//
+// FMT kFmtAffine: the table holds code - 8 and each chunk's dot d is turned
+// into s * (d - (z - 8) * xsum), xsum being the sum of the lane's 32
+// activations of that chunk (the same scaled fp16 values the dot uses), so
+// the zero point costs one load and two operations per chunk.
+template <int NR, int CPL, int S, int RG, bool MULTI, int MODE, int FMT = kFmtNf4>
 __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16_t *__restrict__ x, int P,
                                           int64_t wg) {
     __shared__ uint32_t lut[kLutDwords];
@@ -244,6 +254,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
 
     uint4 q[S + 1][NR][CPL];
     uint32_t sc[S + 1][NR][CPL];
+    uint32_t zc[FMT == kFmtAffine ? S + 1 : 1][NR][CPL];  // zero-point bits (affine only)
     // Tiles are loaded in order.  The next tile to load starts at output
     // r_begin + LPT * (tiles loaded so far); its pointers advance by one tile
     // per load.  Rows past r_end repeat the last valid row (their results are
@@ -254,6 +265,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     // the up rows of rows 0..LPT-1 and come from the up matrix.
     const uint8_t *next_codes0 = sg.codes0 + r_begin * row_bytes;
     const uint16_t *next_scales0 = sg.scales0 + r_begin * nsb;
+    const uint16_t *next_zeros0 = FMT == kFmtAffine ? sg.zeros0 + r_begin * nsb : nullptr;
     const uint8_t *next_codes1 = MODE == kModeSwiglu ? sg.codes1 + r_begin * row_bytes : nullptr;
     const uint16_t *next_scales1 = MODE == kModeSwiglu ? sg.scales1 + r_begin * nsb : nullptr;
     int64_t next_left = r_end - r_begin;  // outputs from the next tile to r_end
@@ -264,6 +276,9 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
             buffer_rsrc(next_codes0, real ? (uint32_t)(LPT * row_bytes) : 0u);
         const __amdgpu_buffer_rsrc_t srs0 =
             buffer_rsrc(next_scales0, real ? (uint32_t)(LPT * nsb * 2) : 0u);
+        __amdgpu_buffer_rsrc_t zrs0 = srs0;
+        if constexpr (FMT == kFmtAffine)
+            zrs0 = buffer_rsrc(next_zeros0, real ? (uint32_t)(LPT * nsb * 2) : 0u);
         __amdgpu_buffer_rsrc_t crs1 = crs0, srs1 = srs0;
         if constexpr (MODE == kModeSwiglu) {
             crs1 = buffer_rsrc(next_codes1, real ? (uint32_t)(LPT * row_bytes) : 0u);
@@ -283,10 +298,14 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                 q[buf][r][i] = make_uint4(v.x, v.y, v.z, v.w);
                 sc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(up ? srs1 : srs0, (int)(soff[i] * 2),
                                                                       rr * nsb * 2, kLoadNonTemporal);
+                if constexpr (FMT == kFmtAffine)
+                    zc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(zrs0, (int)(soff[i] * 2), rr * nsb * 2,
+                                                                          kLoadNonTemporal);
             }
         }
         next_codes0 += LPT * row_bytes;
         next_scales0 += LPT * nsb;
+        if constexpr (FMT == kFmtAffine) next_zeros0 += LPT * nsb;
         if constexpr (MODE == kModeSwiglu) {
             next_codes1 += LPT * row_bytes;
             next_scales1 += LPT * nsb;
@@ -312,7 +331,10 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     }
 #pragma unroll
     for (int s = 0; s <= S; ++s) load_tile(s);
-    fill_lut(lut);
+    if constexpr (FMT == kFmtAffine)
+        fill_lut_from(lut, kAffinePairTable);
+    else
+        fill_lut(lut);
     half2_t xh[CPL][16];
     float down;
     if constexpr (MULTI) {
@@ -327,6 +349,20 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     }
 
     const uint32_t laneoff = (uint32_t)lane << 2;
+
+    // Affine format: the sum of each chunk's 32 activations (zero for chunks
+    // past the row's end, whose activations are zero).
+    float xsum[FMT == kFmtAffine ? CPL : 1];
+    if constexpr (FMT == kFmtAffine) {
+        const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            float t = 0.0f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) t = __builtin_amdgcn_fdot2(xh[i][v], one, t, false);
+            xsum[i] = t;
+        }
+    }
 
     // Rows are reduced across the wave RG at a time (RG/NR tiles): the fixed
     // cost of the cross-lane reduction and of the store is paid once per RG
@@ -343,7 +379,9 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                 float a = 0.0f;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
-                    const float p = chunk_dot(lut, q[buf][r][i], xh[i], laneoff);
+                    float p = chunk_dot(lut, q[buf][r][i], xh[i], laneoff);
+                    if constexpr (FMT == kFmtAffine)
+                        p = fmaf(8.0f - f16_bits_to_f32(zc[buf][r][i]), xsum[i], p);
                     a = fmaf(p, f16_bits_to_f32(sc[buf][r][i]), a);
                 }
                 acc[j * NR + r] = a;
@@ -403,8 +441,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
             if (lane < RG && local < nrows) {
                 const int64_t row = r_begin + local;
                 float v = tot;
-                if (MODE == kModeAffine && sg.bias0) v += e.b0;
-                if (MODE == kModeAffine && sg.residual) v += e.r;
+                if (MODE == kModeEpi && sg.bias0) v += e.b0;
+                if (MODE == kModeEpi && sg.residual) v += e.r;
                 sg.y[row] = v;
             }
         }
@@ -449,6 +487,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
     gemv_body<NR, CPL, S, RG, MULTI, kModePlain>(sg, K, x, P, (int64_t)blockIdx.x);
 }
 
+// The affine format's GEMV (y = W . x with W = (code - z) * s).
+template <int NR, int CPL, int S, int RG, bool MULTI>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
+                          amdgpu_waves_per_eu(gemv_min_waves(CPL), 8))) void gemv_affine_kernel(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    int64_t M, int K, const uint16_t *__restrict__ x, float *__restrict__ y, int P, int64_t rows_q, int rows_rem) {
+    GemvSeg sg{};
+    sg.codes0 = codes;
+    sg.scales0 = scales;
+    sg.zeros0 = zeros;
+    sg.y = y;
+    sg.rows = M;
+    sg.rows_q = rows_q;
+    sg.rows_rem = rows_rem;
+    gemv_body<NR, CPL, S, RG, MULTI, kModePlain, kFmtAffine>(sg, K, x, P, (int64_t)blockIdx.x);
+}
+
 // Several segments in one launch: workgroup b belongs to the last segment
 // whose first workgroup is <= b.
 template <int NR, int CPL, int S, int RG, bool MULTI, int MODE>
@@ -489,8 +544,8 @@ int cu_count() {
     return cached[dev];
 }
 
-template <int NR, int CPL, int S, int RG, bool MULTI>
-hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, int64_t M, int K,
+template <int NR, int CPL, int S, int RG, bool MULTI, int FMT>
+hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M, int K,
                           const uint16_t *x, float *y, int P, int G, int64_t grid, hipStream_t stream) {
     // The LDS copy of the activations of a row-per-wave variant is one
     // 16-byte unit per lane of the workgroup.
@@ -498,9 +553,16 @@ hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, int64_t 
     const int64_t ngroups = grid * G;
     int64_t rows_q = M / ngroups;
     int rows_rem = (int)(M % ngroups);
-    void *args[] = {&codes, &scales, &M, &K, &x, &y, &P, &rows_q, &rows_rem};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_kernel<NR, CPL, S, RG, MULTI>), dim3((unsigned)grid),
-                           dim3((unsigned)(P * G)), args, 0, stream);
+    if constexpr (FMT == kFmtAffine) {
+        void *args[] = {&codes, &scales, &zeros, &M, &K, &x, &y, &P, &rows_q, &rows_rem};
+        return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_affine_kernel<NR, CPL, S, RG, MULTI>),
+                               dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
+    } else {
+        (void)zeros;
+        void *args[] = {&codes, &scales, &M, &K, &x, &y, &P, &rows_q, &rows_rem};
+        return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_kernel<NR, CPL, S, RG, MULTI>),
+                               dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
+    }
 }
 
 // Workgroups for `tiles` tiles of NR rows, G groups per workgroup: two
@@ -620,7 +682,7 @@ hipError_t launch_gemv_fused(const FusedOperand *ops, int count, bool swiglu, in
         g.rows = ops[i].M;
     }
     if (segs.n == 0) return hipSuccess;
-    return launch_fused_mode<kModeAffine>(segs, (int)K, x, stream);
+    return launch_fused_mode<kModeEpi>(segs, (int)K, x, stream);
 }
 
 // Variant choice.  Every variant reads tiles of 4 rows (2 for 2-chunk
@@ -629,20 +691,21 @@ hipError_t launch_gemv_fused(const FusedOperand *ops, int count, bool swiglu, in
 // ahead of: the single-tile form (no ring, 4-row reduction groups) has the
 // shortest set-up.  Otherwise a ring of two tiles keeps the next tile's
 // loads in flight while the current one is reduced.
-hipError_t launch_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
-                       const uint16_t *x, float *y, hipStream_t stream) {
+template <int FMT>
+hipError_t launch_gemv_fmt(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
+                           int64_t K, const uint16_t *x, float *y, hipStream_t stream) {
     const int C = (int)(K / kChunkWeights);
     const int k = (int)K;
     const int64_t tiles4 = (M + 3) / 4;
     if (C <= 64) {  // one wave covers a row: 8 independent waves per workgroup
         const int64_t grid = gemv_grid(tiles4, 8);
         if (tiles4 <= 2 * grid * 8)
-            return launch_variant<4, 1, 0, 4, false>(codes, scales, M, k, x, y, 64, 8, grid, stream);
-        return launch_variant<4, 1, 1, 8, false>(codes, scales, M, k, x, y, 64, 8, grid, stream);
+            return launch_variant<4, 1, 0, 4, false, FMT>(codes, scales, zeros, M, k, x, y, 64, 8, grid, stream);
+        return launch_variant<4, 1, 1, 8, false, FMT>(codes, scales, zeros, M, k, x, y, 64, 8, grid, stream);
     }
     if (C <= 128) {
         const int64_t tiles2 = (M + 1) / 2;
-        return launch_variant<2, 2, 1, 16, false>(codes, scales, M, k, x, y, 64, 8, gemv_grid(tiles2, 8), stream);
+        return launch_variant<2, 2, 1, 16, false, FMT>(codes, scales, zeros, M, k, x, y, 64, 8, gemv_grid(tiles2, 8), stream);
     }
     // Long rows: the whole workgroup (up to 8 waves) shares a row tile.
     int cpl = 1;
@@ -653,18 +716,28 @@ hipError_t launch_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, 
     const bool few = tiles4 <= 2 * grid4;
     switch (cpl) {
         case 1:
-            if (few) return launch_variant<4, 1, 0, 4, true>(codes, scales, M, k, x, y, P, 1, grid4, stream);
-            return launch_variant<4, 1, 1, 8, true>(codes, scales, M, k, x, y, P, 1, grid4, stream);
+            if (few) return launch_variant<4, 1, 0, 4, true, FMT>(codes, scales, zeros, M, k, x, y, P, 1, grid4, stream);
+            return launch_variant<4, 1, 1, 8, true, FMT>(codes, scales, zeros, M, k, x, y, P, 1, grid4, stream);
         case 2:
-            if (few) return launch_variant<4, 2, 0, 4, true>(codes, scales, M, k, x, y, P, 1, grid4, stream);
-            return launch_variant<4, 2, 1, 8, true>(codes, scales, M, k, x, y, P, 1, grid4, stream);
+            if (few) return launch_variant<4, 2, 0, 4, true, FMT>(codes, scales, zeros, M, k, x, y, P, 1, grid4, stream);
+            return launch_variant<4, 2, 1, 8, true, FMT>(codes, scales, zeros, M, k, x, y, P, 1, grid4, stream);
         case 4: {
             const int64_t tiles2 = (M + 1) / 2;
-            return launch_variant<2, 4, 1, 4, true>(codes, scales, M, k, x, y, P, 1, gemv_grid(tiles2, 1), stream);
+            return launch_variant<2, 4, 1, 4, true, FMT>(codes, scales, zeros, M, k, x, y, P, 1, gemv_grid(tiles2, 1), stream);
         }
         default:
-            return launch_variant<1, 8, 0, 2, true>(codes, scales, M, k, x, y, P, 1, gemv_grid(M, 1), stream);
+            return launch_variant<1, 8, 0, 2, true, FMT>(codes, scales, zeros, M, k, x, y, P, 1, gemv_grid(M, 1), stream);
     }
+}
+
+hipError_t launch_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K, const uint16_t *x,
+                       float *y, hipStream_t stream) {
+    return launch_gemv_fmt<kFmtNf4>(codes, scales, nullptr, M, K, x, y, stream);
+}
+
+hipError_t launch_gemv_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
+                              int64_t K, const uint16_t *x, float *y, hipStream_t stream) {
+    return launch_gemv_fmt<kFmtAffine>(codes, scales, zeros, M, K, x, y, stream);
 }
 
 }  // namespace q4

@@ -12,6 +12,12 @@ hipError_t launch_pack(const float *W, int64_t M, int64_t K, uint8_t *codes, uin
 hipError_t launch_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                        const uint16_t *x, float *y, hipStream_t stream);
 
+// The affine format ((code - z) * s per 64-block).
+hipError_t launch_pack_affine(const float *W, int64_t M, int64_t K, uint8_t *codes, uint16_t *scales,
+                              uint16_t *zeros, int32_t *status, hipStream_t stream);
+hipError_t launch_gemv_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
+                              int64_t K, const uint16_t *x, float *y, hipStream_t stream);
+
 // One matrix of a fused GEMV launch (sharing x with the others).
 struct FusedOperand {
     const uint8_t *codes;

@@ -32,23 +32,44 @@ constexpr PairTable make_pair_table() {
 }
 __device__ const PairTable kPairTable = make_pair_table();
 
+// fp16 bits of a small integer (|v| <= 15), exact.
+constexpr uint32_t small_int_f16_bits(int v) {
+    if (v == 0) return 0;
+    const uint32_t sign = v < 0 ? 0x8000u : 0u;
+    const int a = v < 0 ? -v : v;
+    int e = 0;
+    while ((2 << e) <= a) ++e;  // a = 2^e * (1 + f)
+    return sign | (uint32_t)(e + 15) << 10 | (uint32_t)((a - (1 << e)) << (10 - e));
+}
+// The affine format's table: entry b is the pair (lo - 8, hi - 8) of the
+// byte's two codes, centred so that the zero-point term subtracted later is
+// (z - 8) times the activation sum (less cancellation than z times it).
+constexpr PairTable make_affine_pair_table() {
+    PairTable t{};
+    for (int b = 0; b < 256; ++b)
+        t.v[b] = small_int_f16_bits((b & 15) - 8) | (small_int_f16_bits((b >> 4) - 8) << 16);
+    return t;
+}
+__device__ const PairTable kAffinePairTable = make_affine_pair_table();
+
 // Dword e * 64 + l of the LDS table holds entry e for lane slot l.  The 256
 // entries are written in 8 portions of 32; wave w writes portions w, w + nw,
 // ...: two 16-dword scalar loads fetch a portion's entries, and each entry is
 // written to its 64 slots by one lane each (ds_write2st64 pairs two entries
 // per instruction, conflict-free).  No per-entry index arithmetic and no
 // dependence on the weight loads in flight.
-__device__ __forceinline__ void fill_lut(uint32_t *lut) {
+__device__ __forceinline__ void fill_lut_from(uint32_t *lut, const PairTable &table) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nw = blockDim.x >> 6;
     for (int p = wave; p < 8; p += nw) {
-        const uint32_t *src = kPairTable.v + 32 * p;
+        const uint32_t *src = table.v + 32 * p;
         uint32_t *dst = lut + (32 * kLutCopies) * p + lane;
 #pragma unroll
         for (int i = 0; i < 32; ++i) dst[kLutCopies * i] = src[i];
     }
 }
+__device__ __forceinline__ void fill_lut(uint32_t *lut) { fill_lut_from(lut, kPairTable); }
 
 // Table value for byte `B` (0..3) of a code word.
 template <int B>

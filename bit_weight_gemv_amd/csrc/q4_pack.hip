@@ -69,6 +69,110 @@ __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ W, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Affine 4-bit format (golang.design accel/tensor, type Int4 and func
+// Int4MatVec: What = (code - z) * s with an fp16 scale and an fp16 zero point
+// per group; the error is at most the group's range over 30).  The page does
+// not print its quantiser; the steps taken:
+//   range [lo, hi] of the 64-block widened to hold 0; s = fp16 nearest-even
+//   of (hi - lo) / 15, the subtraction and the division in fp64 (IEEE, as
+//   on any host), the fp64 -> fp16 rounding done once (below);
+//   z = #{ j in 0..14 : -lo > (j + 1/2) s }: the integer nearest to -lo / s,
+//   a midpoint going down;
+//   code = #{ j in 0..14 : w > (j - z + 1/2) s }: the nearest level, a
+//   midpoint going to the lower code.
+// (j + 1/2) and (j - z + 1/2) are half-integers of at most 5 bits and s has
+// 11, so every product is exact in fp32 and every comparison decides as it
+// would in exact arithmetic.  s == 0: codes and z are 0.
+// ---------------------------------------------------------------------------
+
+// fp64 -> fp16 with one rounding to nearest even: round to odd into fp32
+// (truncate, then set the last bit when anything was cut off), then let the
+// hardware round fp32 -> fp16 to nearest even.  With 13 more bits in fp32
+// than in fp16 the two steps round exactly as one would.
+__device__ __forceinline__ uint32_t f64_to_f16_bits_rne(double d) {
+    float f = (float)d;
+    if ((double)f != d) {
+        uint32_t b = __builtin_bit_cast(uint32_t, f);
+        if (fabs((double)f) > fabs(d)) b -= 1;  // one step toward zero: the truncation
+        f = __builtin_bit_cast(float, b | 1u);
+    }
+    return __builtin_bit_cast(unsigned short, (_Float16)f);
+}
+
+__global__ __launch_bounds__(256) void pack_affine_kernel(const float *__restrict__ W, int64_t nblocks,
+                                                          uint8_t *__restrict__ codes,
+                                                          uint16_t *__restrict__ scales,
+                                                          uint16_t *__restrict__ zeros,
+                                                          int32_t *__restrict__ status) {
+    const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nblocks * 16; t += nthreads) {
+        const int64_t blk = t >> 4;
+        const int j = (int)(t & 15);
+        const float4 w4 = *reinterpret_cast<const float4 *>(W + blk * kBlock + 4 * j);
+        const float w[4] = {w4.x, w4.y, w4.z, w4.w};
+        float hi = 0.0f, nlo = 0.0f, bad = 0.0f;  // nlo = -lo
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (!__builtin_isfinite(w[i])) bad = 1.0f;
+            hi = fmaxf(hi, w[i]);
+            nlo = fmaxf(nlo, -w[i]);
+        }
+        hi = row16_max(hi);
+        nlo = row16_max(nlo);
+        bad = row16_max(bad);
+        if (bad != 0.0f) {
+            if (j == 0) atomicOr(status, 1);
+            continue;
+        }
+        const uint32_t s16_bits = f64_to_f16_bits_rne(((double)hi + (double)nlo) / 15.0);
+        if (s16_bits == 0x7C00u) {
+            if (j == 0) atomicOr(status, 2);
+            continue;
+        }
+        const float s = f16_bits_to_f32(s16_bits);
+        int z = 0;
+        if (s > 0.0f) {
+#pragma unroll
+            for (int q = 0; q < 15; ++q) z += (nlo > ((float)q + 0.5f) * s) ? 1 : 0;
+        }
+        uint32_t code[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t c = 0;
+            if (s > 0.0f) {
+#pragma unroll
+                for (int q = 0; q < 15; ++q) c += (w[i] > ((float)(q - z) + 0.5f) * s) ? 1u : 0u;
+            }
+            code[i] = c;
+        }
+        const uint16_t two_bytes =
+            (uint16_t)(code[0] | (code[1] << 4) | (code[2] << 8) | (code[3] << 12));
+        *reinterpret_cast<uint16_t *>(codes + blk * (kBlock / 2) + 2 * j) = two_bytes;
+        if (j == 0) {
+            scales[blk] = (uint16_t)s16_bits;
+            zeros[blk] = __builtin_bit_cast(unsigned short, (_Float16)(float)z);
+        }
+    }
+}
+
+hipError_t launch_pack_affine(const float *W, int64_t M, int64_t K, uint8_t *codes, uint16_t *scales,
+                              uint16_t *zeros, int32_t *status, hipStream_t stream) {
+    hipError_t e;
+    {
+        void *args[] = {&status};
+        e = hipLaunchKernel(reinterpret_cast<const void *>(&clear_word_kernel), dim3(1), dim3(1), args, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    int64_t nblocks = M * (K / kBlock);
+    int64_t grid = (nblocks * 16 + 255) / 256;
+    if (grid > 65536) grid = 65536;
+    if (grid < 1) grid = 1;
+    void *args[] = {&W, &nblocks, &codes, &scales, &zeros, &status};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&pack_affine_kernel), dim3((unsigned)grid), dim3(256),
+                           args, 0, stream);
+}
+
 hipError_t launch_pack(const float *W, int64_t M, int64_t K, uint8_t *codes, uint16_t *scales,
                        int32_t *status, hipStream_t stream) {
     hipError_t e;

@@ -186,6 +186,44 @@ int q4_gemv_fused(const q4_operand *ops, int count, int64_t K,
                   const float *const *residual, void *stream);
 
 /*
+ * Affine 4-bit format (golang.design accel/tensor page: type Int4 stores
+ * 4-bit codes, low nibble first, with an f16 scale and an f16 zero point per
+ * group; func Int4MatVec reconstructs What = (code - z) * s, and states the
+ * error as at most a group's range over 30).  Here a group is 64 weights
+ * along K, and codes are laid out as in the NF4 format above; scales and
+ * zeros are fp16 bits [M][K/64] (q4_scales_bytes each).  The page does not
+ * print its quantiser; q4_pack_affine does this:
+ *   - lo, hi: the block's minimum and maximum, widened to hold 0;
+ *   - s = fp16 nearest-even of (hi - lo) / 15 (fp64 arithmetic, one rounding
+ *     to fp16);
+ *   - z = the integer nearest to -lo / s in 0..15 (a midpoint goes down);
+ *   - code = the level (j - z) * s nearest to w (a midpoint goes to the lower
+ *     code); with s == 0 every code and z are 0.
+ * Each decision is an exact comparison, so the result is bit-exact.
+ */
+
+/*
+ * q4_pack_affine -- quantise W [M][K] (fp32, 16-byte aligned) into codes,
+ * scales and zeros (fp16 bits, 2-byte aligned).  *status as q4_pack
+ * (Q4_PACK_NONFINITE, Q4_PACK_OVERFLOW when (hi - lo) / 15 rounds to fp16
+ * infinity); a flagged block's output is unspecified.  No two of W, codes,
+ * scales, zeros and status may overlap.
+ */
+int q4_pack_affine(const float *W, int64_t M, int64_t K, uint8_t *codes,
+                   uint16_t *scales, uint16_t *zeros, int32_t *status,
+                   void *stream);
+
+/*
+ * q4_gemv_affine -- y[m] = sum_k (code(m,k) - z[m][k/64]) * s[m][k/64] * x[k],
+ * fp32 accumulation; x bf16 bits [K] (16-byte aligned), y fp32 [M]
+ * (4-byte aligned, overlapping no input).  Accuracy as q4_gemv: within
+ * 1e-3 * sum_k |What x| + 1e-5 of the exact value.  Errors as q4_gemv.
+ */
+int q4_gemv_affine(const uint8_t *codes, const uint16_t *scales,
+                   const uint16_t *zeros, int64_t M, int64_t K,
+                   const uint16_t *x, float *y, void *stream);
+
+/*
  * Packed row gather (deep-fold "Decode V2" page, run notes of section 6: the
  * embedding is kept as packed rows and the rows a step needs are dequantised
  * into its arena, with no dense vocabulary table; a tied embedding shares

@@ -33,7 +33,8 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused",
-              "q4_gather_rows", "q4_codebook", "q4_codes_bytes", "q4_scales_bytes", "q4_status_string"):
+              "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_codebook", "q4_codes_bytes",
+              "q4_scales_bytes", "q4_status_string"):
         assert n in names
 
 
@@ -243,6 +244,23 @@ def test_gather_errors(q4):
     assert _gather(q4, A, B, 16, 128, C, 4, F32, D, C + 4) == q4.Q4_ERR_OVERLAP     # status over ids
     assert _gather(q4, A, B, 16, 128, C, 4, BF, D, D + 1020) == q4.Q4_ERR_OVERLAP   # status in out (1 KB)
     assert _gather(q4, A, B, 16, 128, C, 4, F32, C - 2032, E) == q4.Q4_ERR_OVERLAP  # out's tail over ids
+    # every call above fails a host check and launches nothing
+
+
+def test_affine_errors(q4):
+    L = q4.lib()
+    # W A (M=16, K=128 fp32: 8 KB), codes B (1 KB), scales C (64 B), zeros D, status E
+    assert L.q4_pack_affine(A, 16, 100, B, C, D, E, None) == q4.Q4_ERR_SHAPE
+    assert L.q4_pack_affine(A, 16, 128, B, C, 0, E, None) == q4.Q4_ERR_NULL
+    assert L.q4_pack_affine(A, 16, 128, B, C, D + 1, E, None) == q4.Q4_ERR_ALIGN
+    assert L.q4_pack_affine(A, 16, 128, B, C, C + 32, E, None) == q4.Q4_ERR_OVERLAP   # zeros over scales
+    assert L.q4_pack_affine(A, 16, 128, B, C, A + 4096, E, None) == q4.Q4_ERR_OVERLAP  # zeros inside W
+    # gemv: codes A, scales B, zeros C, x D (256 B), y E (64 B)
+    assert L.q4_gemv_affine(A, B, C, 16, 100, D, E, None) == q4.Q4_ERR_SHAPE
+    assert L.q4_gemv_affine(A, B, C, 0, 128, 0, 0, None) == q4.Q4_OK
+    assert L.q4_gemv_affine(A, B, 0, 16, 128, D, E, None) == q4.Q4_ERR_NULL
+    assert L.q4_gemv_affine(A, B, C + 1, 16, 128, D, E, None) == q4.Q4_ERR_ALIGN
+    assert L.q4_gemv_affine(A, B, C, 16, 128, D, C + 16, None) == q4.Q4_ERR_OVERLAP  # y over zeros
     # every call above fails a host check and launches nothing
 
 

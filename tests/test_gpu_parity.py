@@ -781,3 +781,99 @@ def test_gather_rows_tied_lm_head_full_size(env):
             got = out.view(torch.int16).cpu().numpy().view(np.uint16) if bf16 else out.cpu().numpy().view(np.uint32)
             assert np.array_equal(got, ref.view(np.uint16 if bf16 else np.uint32)), f"lm_head gather n={n} bf16={bf16}"
     _log("gather lm_head 151936x2048: bit-exact for n=32 and n=1, fp32 and bf16")
+
+
+# ---------------------------------------------------------------------------
+# Affine format: q4_pack_affine (bit-exact) and q4_gemv_affine
+# ---------------------------------------------------------------------------
+
+def _affine_upload(env, codes, scales, zeros):
+    torch, q4, dev = env
+    c, s = _upload_packed(env, codes, scales)
+    z = cases.to_dev(zeros.view(np.float16), torch, dev)
+    return c, s, z
+
+
+@pytest.mark.parametrize("M,K", [(1, 64), (17, 192), (256, 512), (5, 4096), (33, 11008)])
+def test_affine_pack_bit_exact(env, M, K):
+    torch, q4, dev = env
+    W = wl.weights(M, K, 8000 + M + K, std=0.6)
+    W[:, :64] += np.float32(0.7)        # blocks off zero
+    if M > 2:
+        W[1, 64:128] = 0.0 if K > 64 else W[1, 64:128]
+        W[2, :64] = np.float32(-0.3)    # constant negative block
+    c_ref, s_ref, z_ref, st_ref = oracle.pack_affine(W)
+    codes, scales, zeros, status = q4.q4_pack_affine(cases.to_dev(W, torch, dev))
+    torch.cuda.synchronize()
+    assert int(status.item()) == st_ref == 0
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(scales.view(torch.int16).cpu().numpy().view(np.uint16), s_ref)
+    assert np.array_equal(zeros.view(torch.int16).cpu().numpy().view(np.uint16), z_ref)
+
+
+def test_affine_pack_exact_ties_and_flags(env):
+    torch, q4, dev = env
+    W = np.zeros((3, 128), np.float32)
+    W[0, :5] = [0.9375, -0.9375, 0.0625, -0.0625, 0.1875]   # s = 0.125, z = 7.5 -> 7, midpoint codes
+    W[1, 64:70] = [1e-30, -1e-30, 3e-8, 0, 0, 0]              # below the fp16 range: s == 0
+    W[2, 0], W[2, 1] = 4.0e5, -4.0e5                          # large but finite scale
+    c_ref, s_ref, z_ref, st = oracle.pack_affine(W)
+    assert st == 0
+    codes, scales, zeros, status = q4.q4_pack_affine(cases.to_dev(W, torch, dev))
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(scales.view(torch.int16).cpu().numpy().view(np.uint16), s_ref)
+    assert np.array_equal(zeros.view(torch.int16).cpu().numpy().view(np.uint16), z_ref)
+    for bad, flag in ((np.nan, q4.Q4_PACK_NONFINITE), (6.0e5, q4.Q4_PACK_OVERFLOW)):
+        Wb = W.copy()
+        Wb[1, 3] = bad
+        if flag == q4.Q4_PACK_OVERFLOW:
+            Wb[1, 4] = -6.0e5
+        _, _, _, st_b = oracle.pack_affine(Wb)
+        assert st_b == flag
+        _, _, _, sb = q4.q4_pack_affine(cases.to_dev(Wb, torch, dev))
+        torch.cuda.synchronize()
+        assert int(sb.item()) == flag
+
+
+AFFINE_GEMV_SHAPES = [(1, 64), (7, 128), (1000, 1024), (4097, 2048), (40001, 64), (300, 2112), (65, 4096),
+                      (129, 4160), (2048, 11008), (4101, 16448), (3, 32768), (2, 131072)]
+
+
+@pytest.mark.parametrize("M,K", AFFINE_GEMV_SHAPES)
+def test_affine_gemv_parity(env, M, K):
+    torch, q4, dev = env
+    seed = 8100 + M + K
+    W = wl.weights(M, K, seed, std=0.5) + np.float32(0.05)
+    x = wl.activation(K, seed, "normal")
+    codes, scales, zeros, st = oracle.pack_affine(W)
+    assert st == 0
+    y_ref, S = oracle.gemv_affine(codes, scales, zeros, M, K, x)
+    c, s, z = _affine_upload(env, codes, scales, zeros)
+    y = q4.q4_gemv_affine(c, s, z, _x_dev(env, x))
+    torch.cuda.synchronize()
+    _check(y.cpu().numpy(), y_ref, S, f"affine gemv M={M} K={K}")
+
+
+def test_affine_full_size_gateup(env):
+    """The gate/up shape (22016 x 2048): GPU pack bit-exact with the oracle,
+    then the GEMV on every row against the oracle."""
+    torch, q4, dev = env
+    c_cfg = wl.CONFIGS["gateup"]
+    M, K = c_cfg["M"], c_cfg["K"]
+    W = wl.weights(M, K, c_cfg["seed"])
+    x = wl.activation(K, c_cfg["seed"], c_cfg["x"])
+    threads = min(16, os.cpu_count() or 1)
+    c_ref, s_ref, z_ref, st = oracle.pack_affine(W, threads=threads)
+    assert st == 0
+    codes, scales, zeros, status = q4.q4_pack_affine(cases.to_dev(W, torch, dev))
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(scales.view(torch.int16).cpu().numpy().view(np.uint16), s_ref)
+    assert np.array_equal(zeros.view(torch.int16).cpu().numpy().view(np.uint16), z_ref)
+    y = q4.q4_gemv_affine(codes, scales, zeros, _x_dev(env, x))
+    torch.cuda.synchronize()
+    y_ref, S = oracle.gemv_affine(c_ref, s_ref, z_ref, M, K, x, threads=threads)
+    _check(y.cpu().numpy(), y_ref, S, "affine gemv gate/up 22016x2048")
