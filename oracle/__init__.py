@@ -89,6 +89,18 @@ def _load():
         lib.oracle_dequant_affine.restype = None
         lib.oracle_gemv_affine_rows.argtypes = [P, P, P, I64, I64, P, I64, I64, P, P]
         lib.oracle_gemv_affine_rows.restype = None
+        lib.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_to_f64.restype = ctypes.c_double
+        lib.oracle_e2m1_to_f64.argtypes = [ctypes.c_uint8]
+        lib.oracle_e2m1_to_f64.restype = ctypes.c_double
+        lib.oracle_nvfp4_tensor_scale.argtypes = [P, I64, P]
+        lib.oracle_nvfp4_tensor_scale.restype = ctypes.c_float
+        lib.oracle_pack_nvfp4_rows.argtypes = [P, I64, I64, I64, I64, ctypes.c_float, P, P]
+        lib.oracle_pack_nvfp4_rows.restype = ctypes.c_int
+        lib.oracle_dequant_nvfp4.argtypes = [P, P, ctypes.c_float, I64, I64, P]
+        lib.oracle_dequant_nvfp4.restype = None
+        lib.oracle_gemv_nvfp4_rows.argtypes = [P, P, ctypes.c_float, I64, I64, P, I64, I64, P, P]
+        lib.oracle_gemv_nvfp4_rows.restype = None
         lib.oracle_f64_to_bf16_rne.argtypes = [ctypes.c_double]
         lib.oracle_f64_to_bf16_rne.restype = ctypes.c_uint16
         lib.oracle_gather_rows.argtypes = [P, P, I64, I64, P, I64, ctypes.c_int, P]
@@ -309,6 +321,67 @@ def gemv_affine(codes, scales, zeros, M: int, K: int, x_bits, rows=None, threads
     def run(a, b, slot):
         lib.oracle_gemv_affine_rows(_ptr(codes), _ptr(scales), _ptr(zeros), M, K, _ptr(x_bits), r0 + a, r0 + b,
                                     _ptr(y), _ptr(S))
+
+    _run_rows(r1 - r0, threads, run, [0])
+    return y, S
+
+
+def e4m3_to_f64(b: int) -> float:
+    return float(_load().oracle_e4m3_to_f64(int(b)))
+
+
+def e2m1_to_f64(c: int) -> float:
+    return float(_load().oracle_e2m1_to_f64(int(c)))
+
+
+def pack_nvfp4(W: np.ndarray, threads: int = 1):
+    """(codes uint8 [M, K/2], scales E4M3 bytes uint8 [M, K/16], tensor scale
+    (float), status) of the NVFP4-style format."""
+    W = np.ascontiguousarray(W, np.float32)
+    M, K = W.shape
+    _check_shape(M, K)
+    lib = _load()
+    st0 = ctypes.c_int(0)
+    s = float(lib.oracle_nvfp4_tensor_scale(_ptr(W), W.size, ctypes.byref(st0)))
+    codes = np.zeros((M, K // 2), np.uint8)
+    scales = np.zeros((M, K // 16), np.uint8)
+    status = [0]
+
+    def run(r0, r1, slot):
+        slot.append(lib.oracle_pack_nvfp4_rows(_ptr(W), M, K, r0, r1, s, _ptr(codes), _ptr(scales)))
+
+    _run_rows(M, threads, run, status)
+    st = st0.value
+    for v in status[1:]:
+        st |= v
+    return codes, scales, s, st
+
+
+def dequant_nvfp4(codes, scales, s: float, M: int, K: int) -> np.ndarray:
+    _check_shape(M, K)
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    out = np.zeros((M, K), np.float64)
+    _load().oracle_dequant_nvfp4(_ptr(codes), _ptr(scales), float(s), M, K, _ptr(out))
+    return out
+
+
+def gemv_nvfp4(codes, scales, s: float, M: int, K: int, x_bits, rows=None, threads: int = 1):
+    """y, S (fp64, length M) of the NVFP4-style format."""
+    _check_shape(M, K)
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    x_bits = np.ascontiguousarray(x_bits, np.uint16)
+    if x_bits.size != K:
+        raise ValueError("oracle.gemv_nvfp4: x must have K entries")
+    y = np.full(M, np.nan)
+    S = np.full(M, np.nan)
+    lib = _load()
+    r0, r1 = (0, M) if rows is None else rows
+
+    def run(a, b, slot):
+        lib.oracle_gemv_nvfp4_rows(_ptr(codes), _ptr(scales), float(s), M, K, _ptr(x_bits), r0 + a, r0 + b,
+                                   _ptr(y), _ptr(S))
 
     _run_rows(r1 - r0, threads, run, [0])
     return y, S

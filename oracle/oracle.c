@@ -515,3 +515,138 @@ void oracle_gemv_affine_rows(const uint8_t *codes, const uint16_t *scales, const
         if (S) S[m] = mag;
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* NVFP4-style format (gizai tensor/lazy page, fp4Blocks: E2M1 codes, two to */
+/* a byte with the first in the low half; one E4M3 scale per 16 values along */
+/* k; a tensor scale s = max |t| / (6 * 448) in f32; a value is its E2M1    */
+/* times its block's scale times s).  Reading taken for the steps the page   */
+/* leaves open:                                                              */
+/*   - s = the f32 rounding of the fp64 quotient max|W| / 2688;             */
+/*   - a block's scale is the E4M3 value nearest to amax_b / (6 s), ties to  */
+/*     the even pattern, at most 448 (s == 0: scale 0);                      */
+/*   - a weight's code is the E2M1 magnitude nearest to |w| / (scale * s),   */
+/*     ties to the even pattern, at most 6, with w's sign bit; a block whose */
+/*     scale is 0 is all code 0;                                             */
+/*   - every decision compares against a midpoint times 6 s or scale * s:    */
+/*     midpoints of at most 5 significant bits, 6 of 2, an E4M3 of 4 and s   */
+/*     of 24, so each product and comparison is exact in fp64;               */
+/*   - scales are stored row-major, [M][K/16] (not the page's tensor-core   */
+/*     interleave).                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* The value of an E4M3 (OCP E4M3FN: bias 7, no infinities, 0x7F NaN) byte. */
+double oracle_e4m3_to_f64(uint8_t b) {
+    const int sign = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9); /* (m / 8) 2^-6 */
+    else
+        v = ldexp(8.0 + m, e - 10); /* (1 + m / 8) 2^(e - 7) */
+    return sign ? -v : v;
+}
+
+/* The value of an E2M1 code (sign bit 3): 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+double oracle_e2m1_to_f64(uint8_t c) {
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    const double v = mag[c & 7];
+    return (c & 8) ? -v : v;
+}
+
+/* Nearest of the ascending grid g[0..n-1] to a >= 0 scaled by u (a against
+ * g[i] * u), ties to the even index; a above the grid saturates. */
+static int nearest_on_grid(double a, const double *g, int n, double u) {
+    int i = 0;
+    while (i + 1 < n) {
+        const double mid = (g[i] + g[i + 1]) / 2.0 * u; /* exact */
+        if (a > mid || (a == mid && (i & 1))) {
+            ++i;
+            continue;
+        }
+        break;
+    }
+    return i;
+}
+
+float oracle_nvfp4_tensor_scale(const float *W, int64_t n, int *status) {
+    double amax = 0.0;
+    *status = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (!isfinite(W[i])) {
+            *status |= ORACLE_PACK_NONFINITE;
+            continue;
+        }
+        if (fabs((double)W[i]) > amax) amax = fabs((double)W[i]);
+    }
+    return (float)(amax / 2688.0);
+}
+
+int oracle_pack_nvfp4_rows(const float *W, int64_t M, int64_t K, int64_t row0, int64_t row1, float s,
+                           uint8_t *codes, uint8_t *scales) {
+    (void)M;
+    static double e4m3[127]; /* positive E4M3 values, ascending (0x00 .. 0x7E) */
+    static const double e2m1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    for (int b = 0; b < 127; ++b) e4m3[b] = oracle_e4m3_to_f64((uint8_t)b);
+    int status = 0;
+    const int64_t nblk = K / 16;
+    for (int64_t m = row0; m < row1; ++m) {
+        for (int64_t b = 0; b < nblk; ++b) {
+            const float *w = W + m * K + b * 16;
+            double amax = 0.0;
+            int bad = 0;
+            for (int k = 0; k < 16; ++k) {
+                if (!isfinite(w[k])) bad = 1;
+                else if (fabs((double)w[k]) > amax) amax = fabs((double)w[k]);
+            }
+            if (bad) {
+                status |= ORACLE_PACK_NONFINITE;
+                continue;
+            }
+            const int sb = (s > 0.0f) ? nearest_on_grid(amax, e4m3, 127, 6.0 * (double)s) : 0;
+            scales[m * nblk + b] = (uint8_t)sb;
+            const double unit = e4m3[sb] * (double)s; /* exact */
+            for (int k = 0; k < 16; k += 2) {
+                uint8_t c[2];
+                for (int h = 0; h < 2; ++h) {
+                    const double wv = (double)w[k + h];
+                    if (unit == 0.0) {
+                        c[h] = 0;
+                        continue;
+                    }
+                    const int mag = nearest_on_grid(fabs(wv), e2m1, 8, unit);
+                    c[h] = (uint8_t)(mag | (signbit(wv) ? 8 : 0));
+                }
+                codes[m * (K / 2) + b * 8 + k / 2] = (uint8_t)(c[0] | (c[1] << 4));
+            }
+        }
+    }
+    return status;
+}
+
+/* What[m,k] = E2M1(code) * E4M3(scale) * s, exact in fp64. */
+void oracle_dequant_nvfp4(const uint8_t *codes, const uint8_t *scales, float s, int64_t M, int64_t K,
+                          double *What) {
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k)
+            What[m * K + k] = oracle_e2m1_to_f64((uint8_t)code_at(codes, K, m, k)) *
+                              oracle_e4m3_to_f64(scales[m * (K / 16) + k / 16]) * (double)s;
+}
+
+void oracle_gemv_nvfp4_rows(const uint8_t *codes, const uint8_t *scales, float s, int64_t M, int64_t K,
+                            const uint16_t *x, int64_t row0, int64_t row1, double *y, double *S) {
+    (void)M;
+    for (int64_t m = row0; m < row1; ++m) {
+        double sum = 0.0, absum = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double wq = oracle_e2m1_to_f64((uint8_t)code_at(codes, K, m, k)) *
+                              oracle_e4m3_to_f64(scales[m * (K / 16) + k / 16]) * (double)s;
+            const double prod = wq * oracle_bf16_to_f64(x[k]); /* exact */
+            sum += prod;
+            absum += fabs(prod);
+        }
+        y[m] = sum;
+        if (S) S[m] = absum;
+    }
+}

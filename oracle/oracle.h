@@ -122,6 +122,22 @@ void oracle_gemv_affine_rows(const uint8_t *codes, const uint16_t *scales, const
                              int64_t M, int64_t K, const uint16_t *x, int64_t row0, int64_t row1,
                              double *y, double *S);
 
+/* NVFP4-style format (gizai tensor/lazy page, fp4Blocks): E2M1 codes (low
+ * half first), one E4M3 scale per 16 values along K (row-major [M][K/16]
+ * here), an f32 tensor scale s = max|W| / (6 * 448).  What = E2M1 * E4M3 * s.
+ * The rounding steps the page leaves open are in oracle.c. */
+double oracle_e4m3_to_f64(uint8_t b);
+double oracle_e2m1_to_f64(uint8_t c);
+/* s of W[0..n) (non-finite values are skipped and flagged in *status). */
+float oracle_nvfp4_tensor_scale(const float *W, int64_t n, int *status);
+int oracle_pack_nvfp4_rows(const float *W, int64_t M, int64_t K, int64_t row0, int64_t row1,
+                           float s, uint8_t *codes, uint8_t *scales);
+void oracle_dequant_nvfp4(const uint8_t *codes, const uint8_t *scales, float s, int64_t M,
+                          int64_t K, double *What);
+void oracle_gemv_nvfp4_rows(const uint8_t *codes, const uint8_t *scales, float s, int64_t M,
+                            int64_t K, const uint16_t *x, int64_t row0, int64_t row1,
+                            double *y, double *S);
+
 /* First index of the maximum (NaN never wins); -1 if n == 0 or all NaN. */
 int64_t oracle_argmax_f64(const double *y, int64_t n);
 int64_t oracle_argmax_f32(const float *y, int64_t n);

@@ -61,6 +61,16 @@ MUTANTS = {
                                  "const double w = ((double)code_at(codes, K, m, k)) *"),
     "f16_via_f32": ("    if (isnan(v)) return (uint16_t)(sign | 0x7e00);\n    double a = fabs(v);",
                     "    if (isnan(v)) return (uint16_t)(sign | 0x7e00);\n    double a = fabs((double)(float)v);"),
+    "e4m3_bias_8": ("v = ldexp(8.0 + m, e - 10); /* (1 + m / 8) 2^(e - 7) */", "v = ldexp(8.0 + m, e - 11);"),
+    "e2m1_top_5": ("{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};\n    const double v = mag[c & 7];",
+                   "{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 5.0};\n    const double v = mag[c & 7];"),
+    "grid_ties_to_odd": ("if (a > mid || (a == mid && (i & 1))) {", "if (a > mid || (a == mid && !(i & 1))) {"),
+    "tensor_scale_2048": ("return (float)(amax / 2688.0);", "return (float)(amax / 2048.0);"),
+    "nvfp4_sign_dropped": ("c[h] = (uint8_t)(mag | (signbit(wv) ? 8 : 0));", "c[h] = (uint8_t)mag;"),
+    "nvfp4_block_32": ("oracle_e4m3_to_f64(scales[m * (K / 16) + k / 16]) * (double)s;\n}",
+                       "oracle_e4m3_to_f64(scales[m * (K / 16) + k / 32]) * (double)s;\n}"),
+    "nvfp4_gemv_drops_tensor_scale": ("oracle_e4m3_to_f64(scales[m * (K / 16) + k / 16]) * (double)s;\n            const double prod",
+                                      "oracle_e4m3_to_f64(scales[m * (K / 16) + k / 16]);\n            const double prod"),
     "residual_dropped": ("if (residual) v += (double)residual[i];", "if (residual && !swiglu) v += (double)residual[i];"),
 }
 

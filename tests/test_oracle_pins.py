@@ -842,3 +842,128 @@ def test_affine_exact_ties_go_down(oracle_mod):
     assert list(c[0, :5]) == [14, 0, 7, 6, 8]
     What = oracle_mod.dequant_affine(codes, scales, zeros, 1, 64)
     assert list(What[0, :5]) == [0.875, -0.875, 0.0, -0.125, 0.125]
+
+
+# ---------------------------------------------------------------------------
+# NVFP4-style format: E2M1 codes, E4M3 scale per 16 along K, f32 tensor scale
+# ---------------------------------------------------------------------------
+
+def _e4m3_exact(b):
+    """E4M3FN from its definition (bias 7, subnormals (m/8) 2^-6, 0x7F NaN)."""
+    s, e, m = b >> 7, (b >> 3) & 15, b & 7
+    if e == 15 and m == 7:
+        return None
+    v = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+    return -v if s else v
+
+
+_E2M1 = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4), Fraction(6)]
+_E4M3_POS = [_e4m3_exact(b) for b in range(127)]
+
+
+def test_e4m3_and_e2m1_values(oracle_mod):
+    import torch
+    tv = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    for b in range(256):
+        v = oracle_mod.e4m3_to_f64(b)
+        ref = _e4m3_exact(b)
+        if ref is None:
+            assert np.isnan(v) and np.isnan(tv[b])
+        else:
+            assert Fraction(v) == ref and v == tv[b], b
+    # E2M1 from its definition: bias 1, e = 0 -> m / 2, else 2^(e-1) (1 + m/2)
+    for c in range(16):
+        e, m = (c >> 1) & 3, c & 1
+        mag = Fraction(m, 2) if e == 0 else Fraction(2) ** (e - 1) * (1 + Fraction(m, 2))
+        assert Fraction(oracle_mod.e2m1_to_f64(c)) == (-mag if c & 8 else mag), c
+
+
+def _nearest_even(a, grid):
+    """Index of the grid value nearest to the rational a >= 0, ties to the even
+    index, saturating at the top."""
+    best = None
+    for i, g in enumerate(grid):
+        d = abs(a - g)
+        if best is None or d < best[0] or (d == best[0] and i % 2 == 0):
+            best = (d, i)
+    return best[1]
+
+
+def test_nvfp4_pack_brute_force(oracle_mod):
+    M, K = 5, 128
+    W = wl.weights(M, K, 41, std=0.5)
+    W[1, 16:32] *= 1e-4                 # a small block (subnormal E4M3 scale)
+    W[2, 32:48] = 0.0                   # a zero block
+    W[3, 0] = -0.0
+    codes, scales, s, st = oracle_mod.pack_nvfp4(W)
+    assert st == 0
+    assert s == np.float32(np.max(np.abs(W)).astype(np.float64) / 2688.0)
+    S = Fraction(float(s))
+    for m in range(M):
+        for b in range(K // 16):
+            w = W[m, 16 * b:16 * b + 16]
+            amax = Fraction(float(np.max(np.abs(w))))
+            sb = _nearest_even(amax / (6 * S), _E4M3_POS)
+            assert scales[m, b] == sb, (m, b)
+            unit = _E4M3_POS[sb] * S
+            for k in range(16):
+                byte = codes[m, 8 * b + k // 2]
+                c = (byte >> 4) if k % 2 else (byte & 15)
+                wk = float(w[k])
+                if unit == 0:
+                    assert c == 0
+                    continue
+                mag = _nearest_even(abs(Fraction(wk)) / unit, _E2M1)
+                assert c == (mag | (8 if np.signbit(wk) else 0)), (m, b, k)
+
+
+def test_nvfp4_closed_forms_and_ties(oracle_mod):
+    """max |W| = 2688 makes s = 1; a block with amax 6 gets scale 1.0 (0x38)
+    and values on the E2M1 grid and on its midpoints (ties to the even code);
+    amax 6.375 = 6 * 1.0625 is the midpoint of E4M3 1.0 and 1.125: scale 1.0,
+    and 6.375 itself saturates to 6."""
+    W = np.zeros((1, 64), np.float32)
+    W[0, 0] = 2688.0
+    W[0, 16:32] = [6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, -0.25, -5, 0.5, 3, 0, -6, 4, 1.5]
+    W[0, 32:34] = [6.375, 1.0]
+    codes, scales, s, st = oracle_mod.pack_nvfp4(W)
+    assert st == 0 and s == 1.0
+    assert scales[0, 0] == 0x7E  # 2688 / 6 = 448
+    assert scales[0, 1] == 0x38 and scales[0, 2] == 0x38
+    c = np.zeros(64, np.int64)
+    c[0::2], c[1::2] = codes[0] & 15, codes[0] >> 4
+    assert list(c[16:32]) == [7, 0, 2, 2, 4, 4, 6, 6, 8, 14, 1, 5, 0, 15, 6, 3]
+    assert list(c[32:34]) == [7, 2]
+    What = oracle_mod.dequant_nvfp4(codes, scales, s, 1, 64)
+    assert What[0, 32] == 6.0 and What[0, 0] == 2688.0
+
+
+def test_nvfp4_zero_tensor_and_refusal(oracle_mod):
+    W = np.zeros((2, 64), np.float32)
+    codes, scales, s, st = oracle_mod.pack_nvfp4(W)
+    assert st == 0 and s == 0.0 and not codes.any() and not scales.any()
+    W[1, 5] = np.inf
+    assert oracle_mod.pack_nvfp4(W)[3] == oracle_mod.PACK_NONFINITE
+
+
+def test_nvfp4_gemv_matches_blas_and_one_hot(oracle_mod):
+    M, K = 21, 192
+    W = wl.weights(M, K, 43, std=0.5)
+    codes, scales, s, st = oracle_mod.pack_nvfp4(W)
+    x = wl.activation(K, 43, "normal")
+    y, S = oracle_mod.gemv_nvfp4(codes, scales, s, M, K, x)
+    What = oracle_mod.dequant_nvfp4(codes, scales, s, M, K)
+    xv = wl.bf16_bits_to_f32(x).astype(np.float64)
+    assert np.allclose(y, What @ xv, rtol=1e-12, atol=1e-12)
+    assert np.allclose(S, np.abs(What) @ np.abs(xv), rtol=1e-12)
+    for k in (0, 15, 16, 191):
+        e = np.zeros(K, np.uint16)
+        e[k] = 0x3F80
+        yk, _ = oracle_mod.gemv_nvfp4(codes, scales, s, M, K, e)
+        assert np.array_equal(yk, What[:, k])
+    # a hand-built element: code 0xB (-1.5) with scale 0x30 (0.5) and s
+    cb = np.zeros((1, 32), np.uint8)
+    cb[0, 0] = 0xB0  # k=0 code 0, k=1 code 0xB
+    sc = np.full((1, 4), 0x30, np.uint8)
+    Wh = oracle_mod.dequant_nvfp4(cb, sc, np.float32(0.25), 1, 64)
+    assert Wh[0, 0] == 0.0 and Wh[0, 1] == -1.5 * 0.5 * 0.25
