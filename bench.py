@@ -1,7 +1,7 @@
 """Benchmark of the 4-bit codebook GEMV on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--copies R] [--no-secondary]
-                    [--secondary down,smalln,gateup,fused,gather,affine]
+                    [--secondary down,smalln,gateup,fused,gather,affine,nvfp4]
 
 A step is one q4_gemv call on the lm_head workload (M x K = 151936 x 2048,
 x bf16 unit-RMS, y fp32): the projection the metric is quoted on.  Inputs are
@@ -333,6 +333,37 @@ def affine_secondaries(torch, q4, wl, dev, steps, warmup):
     return out
 
 
+def nvfp4_secondaries(torch, q4, wl, dev, steps, warmup):
+    """The NVFP4-style format's GEMV (E2M1 codes, an E4M3 scale per 16
+    weights, an f32 tensor scale) on the lm_head and down shapes."""
+    out = []
+    for name, copies in (("lm_head", 4), ("down", 50)):
+        c = wl.CONFIGS[name]
+        M, K = c["M"], c["K"]
+        W = torch.from_numpy(wl.weights(M, K, c["seed"])).to(dev)
+        codes, scales, ts, status = q4.q4_pack_nvfp4(W)
+        torch.cuda.synchronize()
+        if int(status.item()) != 0:
+            raise RuntimeError(f"q4_pack_nvfp4 flagged the {name} weights")
+        del W
+        reps = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(copies - 1)]
+        x = _upload_bits(torch, wl.activation(K, c["seed"], c["x"]), torch.bfloat16, dev)
+        y = torch.empty(M, dtype=torch.float32, device=dev)
+
+        def fn(cd, sl):
+            q4.q4_gemv_nvfp4(cd, sl, ts, x, y)
+        ms, wall = time_graph(torch, fn, reps, steps, warmup)
+        nb = M * K // 2 + M * K // 16 + 4 + 2 * K + 4 * M
+        gbs = nb / (ms * 1e-3) / 1e9
+        log(f"nvfp4 {name}: {ms * 1e3:.2f} us/call, {gbs:.0f} GB/s")
+        out.append({"workload": f"NVFP4-style GEMV {name} {M}x{K} N=1", "us_per_call": round(ms * 1e3, 3),
+                    "us_per_step_wall": round(wall * 1e3, 3), "achieved_GBs": round(gbs, 1),
+                    "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": nb})
+        del reps, codes, scales, ts, x, y
+        torch.cuda.empty_cache()
+    return out
+
+
 def context_bandwidth(torch, dev, steps=20):
     """Bandwidth context from a library-independent kernel: torch's device
     copy of COPY_PROBE_BYTES, replayed as a graph; (read + written bytes) / s
@@ -384,8 +415,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--secondary", default="down,smalln,gateup,fused,gather,affine",
-                    help="comma-separated secondary workloads to time (down, smalln, gateup, fused, gather, affine)")
+    ap.add_argument("--secondary", default="down,smalln,gateup,fused,gather,affine,nvfp4",
+                    help="comma-separated secondary workloads to time "
+                         "(down, smalln, gateup, fused, gather, affine, nvfp4)")
     ap.add_argument("--eager", action="store_true",
                     help="also time the calls launched one by one from Python")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -486,6 +518,8 @@ def main():
             secondary.extend(gather_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
         if "affine" in chosen:
             secondary.extend(affine_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
+        if "nvfp4" in chosen:
+            secondary.extend(nvfp4_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
 
     result = {
         "metric": "4-bit GEMV us/call + achieved HBM GB/s (% of peak), MxK=151936x2048, N=1",

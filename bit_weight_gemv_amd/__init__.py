@@ -32,7 +32,7 @@ Q4_PACK_OVERFLOW = 2
 
 EXPORTED = ("q4_codes_bytes", "q4_scales_bytes", "q4_codebook", "q4_status_string",
             "q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused",
-            "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine")
+            "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_pack_nvfp4", "q4_gemv_nvfp4")
 
 Q4_OUT_F32 = 0
 Q4_OUT_BF16 = 1
@@ -93,6 +93,10 @@ def lib() -> ctypes.CDLL:
         L.q4_pack_affine.restype = I32
         L.q4_gemv_affine.argtypes = [P, P, P, I64, I64, P, P, P]
         L.q4_gemv_affine.restype = I32
+        L.q4_pack_nvfp4.argtypes = [P, I64, I64, P, P, P, P, P]
+        L.q4_pack_nvfp4.restype = I32
+        L.q4_gemv_nvfp4.argtypes = [P, P, P, I64, I64, P, P, P]
+        L.q4_gemv_nvfp4.restype = I32
         _lib = L
         return L
 
@@ -367,4 +371,60 @@ def q4_gemv_affine(codes, scales, zeros, x, y=None, stream=None):
     st = lib().q4_gemv_affine(_ptr(codes), _ptr(scales), _ptr(zeros), M, K, _ptr(x), _ptr(y), _stream(stream))
     if st != Q4_OK:
         raise Q4Error(st, "q4_gemv_affine")
+    return y
+
+
+def q4_pack_nvfp4(W, codes=None, scales=None, tscale=None, status=None, stream=None):
+    """Quantise fp32 W [M, K] into the NVFP4-style format -> (codes uint8
+    [M, K/2], scales E4M3 bytes uint8 [M, K/16], tensor scale fp32 [1],
+    status int32 [1])."""
+    torch = _torch()
+    if W.dim() != 2:
+        raise ValueError("W must be [M, K]")
+    M, K = W.shape
+    dev = W.device
+    _check(W, "W", torch.float32, dev)
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    if tscale is None:
+        tscale = torch.empty(1, dtype=torch.float32, device=dev)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    for t, n, dt in ((codes, "codes", torch.uint8), (scales, "scales", torch.uint8),
+                     (tscale, "tscale", torch.float32), (status, "status", torch.int32)):
+        _check(t, n, dt, dev)
+    if codes.numel() * 2 != M * K or scales.numel() * 16 != M * K:
+        raise ValueError("codes / scales sizes do not match W")
+    st = lib().q4_pack_nvfp4(_ptr(W), M, K, _ptr(codes), _ptr(scales), _ptr(tscale), _ptr(status), _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_pack_nvfp4")
+    return codes, scales, tscale, status
+
+
+def q4_gemv_nvfp4(codes, scales, tscale, x, y=None, stream=None):
+    """y fp32 [M] = W . x for an NVFP4-style W (codes [M, K/2], scales uint8
+    [M, K/16], tensor scale fp32 [1]) and bf16 x [K]."""
+    torch = _torch()
+    dev = codes.device
+    if codes.dim() != 2 or scales.dim() != 2:
+        raise ValueError("codes must be [M, K/2] and scales [M, K/16]")
+    M, K = codes.shape[0], codes.shape[1] * 2
+    if scales.shape[0] != M or scales.shape[1] * 16 != K:
+        raise ValueError("codes and scales disagree on M, K")
+    _check(codes, "codes", torch.uint8, dev)
+    _check(scales, "scales", torch.uint8, dev)
+    _check(tscale, "tscale", torch.float32, dev)
+    _check(x, "x", torch.bfloat16, dev)
+    if x.numel() != K:
+        raise ValueError(f"x must have K={K} entries")
+    if y is None:
+        y = torch.empty(M, dtype=torch.float32, device=dev)
+    _check(y, "y", torch.float32, dev)
+    if y.numel() != M:
+        raise ValueError(f"y must have M={M} entries")
+    st = lib().q4_gemv_nvfp4(_ptr(codes), _ptr(scales), _ptr(tscale), M, K, _ptr(x), _ptr(y), _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_gemv_nvfp4")
     return y

@@ -148,6 +148,34 @@ int q4_gemv_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t 
     return launch_status(q4::launch_gemv_affine(codes, scales, zeros, M, K, x, y, (hipStream_t)stream));
 }
 
+int q4_pack_nvfp4(const float *W, int64_t M, int64_t K, uint8_t *codes, uint8_t *scales, float *tscale,
+                  int32_t *status, void *stream) {
+    if (!shape_ok(M, K)) return Q4_ERR_SHAPE;
+    if (!W || !codes || !scales || !tscale || !status) return Q4_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(tscale, 4) || !aligned(status, 4))
+        return Q4_ERR_ALIGN;
+    const Range r[5] = {range_of(W, (uint64_t)M * K * 4), range_of(codes, (uint64_t)M * (K / 2)),
+                        range_of(scales, (uint64_t)M * (K / 16)), range_of(tscale, 4), range_of(status, 4)};
+    for (int i = 0; i < 5; ++i)
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(r[i], r[j])) return Q4_ERR_OVERLAP;
+    return launch_status(q4::launch_pack_nvfp4(W, M, K, codes, scales, tscale, status, (hipStream_t)stream));
+}
+
+int q4_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscale, int64_t M, int64_t K,
+                  const uint16_t *x, float *y, void *stream) {
+    if (!shape_ok(M, K)) return Q4_ERR_SHAPE;
+    if (M == 0) return Q4_OK;
+    if (!codes || !scales || !tscale || !x || !y) return Q4_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(tscale, 4) || !aligned(x, 16) || !aligned(y, 4))
+        return Q4_ERR_ALIGN;
+    const Range ry = range_of(y, (uint64_t)M * 4);
+    if (overlap(ry, range_of(codes, (uint64_t)M * (K / 2))) || overlap(ry, range_of(scales, (uint64_t)M * (K / 16))) ||
+        overlap(ry, range_of(tscale, 4)) || overlap(ry, range_of(x, (uint64_t)K * 2)))
+        return Q4_ERR_OVERLAP;
+    return launch_status(q4::launch_gemv_nvfp4(codes, scales, tscale, M, K, x, y, (hipStream_t)stream));
+}
+
 int q4_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K, const uint16_t *X,
                    int64_t N, float *Y, void *stream) {
     if (!shape_ok(M, K) || N < 0 || N > Q4_MAX_N) return Q4_ERR_SHAPE;

@@ -67,6 +67,36 @@ __device__ __forceinline__ float chunk_dot(const uint32_t *lut, uint4 q, const h
     return p;
 }
 
+// The same dot split at the chunk's middle: p0 over its first 16 weights
+// (bytes 0..7), p1 over the last 16, for formats with a scale per 16 weights.
+__device__ __forceinline__ void chunk_dot_halves(const uint32_t *lut, uint4 q, const half2_t *xh,
+                                                 uint32_t laneoff, float &p0, float &p1) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    half2_t v[16];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        v[4 * d + 0] = lut_pair<0>(lut, w[d], laneoff);
+        v[4 * d + 1] = lut_pair<1>(lut, w[d], laneoff);
+        v[4 * d + 2] = lut_pair<2>(lut, w[d], laneoff);
+        v[4 * d + 3] = lut_pair<3>(lut, w[d], laneoff);
+    }
+    p0 = 0.0f;
+    p1 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        p0 = __builtin_amdgcn_fdot2(v[j], xh[j], p0, false);
+        p1 = __builtin_amdgcn_fdot2(v[j + 8], xh[j + 8], p1, false);
+    }
+}
+
+// An E4M3 scale byte (sign clear) as fp32: its 7 magnitude bits placed at
+// fp32's exponent/mantissa boundary give 2^(e-127) (1 + m/8) for e > 0 and
+// the denormal m 2^-129 for e == 0; times 2^120 that is exactly
+// 2^(e-7) (1 + m/8), or (m/8) 2^-6 (fp32 denormals are kept).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    return __builtin_bit_cast(float, (b & 0x7Fu) << 20) * 0x1p120f;
+}
+
 // Raw activations of chunk c (16 dwords, two bf16 each) from global memory;
 // a lane past the row's end gets zeros.
 __device__ __forceinline__ void load_chunk_x(const uint16_t *__restrict__ x, int c, bool valid,
@@ -172,6 +202,7 @@ struct GemvSeg {
     const uint8_t *codes0;
     const uint16_t *scales0;
     const uint16_t *zeros0;  // affine format only: fp16 zero points [rows][K/64]
+    const float *tscale;     // NVFP4-style format only: the f32 tensor scale
     const uint8_t *codes1;
     const uint16_t *scales1;
     const float *bias0;
@@ -189,10 +220,12 @@ struct GemvSegs {
     int32_t n;
 };
 enum { kModePlain = 0, kModeEpi = 1, kModeSwiglu = 2 };
-// Weight formats: the NF4 codebook (level[code] * s), or the affine format
+// Weight formats: the NF4 codebook (level[code] * s), the affine format
 // ((code - z) * s with an fp16 zero point per 64-block; golang.design
-// accel/tensor, type Int4 and func Int4MatVec).
-enum { kFmtNf4 = 0, kFmtAffine = 1 };
+// accel/tensor, type Int4 and func Int4MatVec), or the NVFP4-style format
+// (E2M1 * E4M3 scale per 16 weights * an f32 tensor scale; gizai tensor/lazy,
+// fp4Blocks).
+enum { kFmtNf4 = 0, kFmtAffine = 1, kFmtNvfp4 = 2 };
 
 // The GEMV of one segment by one workgroup (index `wg` within the segment).
 // MODE kModePlain: y = W . x.  kModeEpi: y = W . x (+ bias0) (+ residual).
@@ -228,7 +261,10 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     const int lig = wig * 64 + lane;          // lane within its group
     const int64_t gid = MULTI ? wg : wg * (blockDim.x >> 6) + wave;
     const int C = K >> 5;                      // 16-byte chunks per row
-    const int nsb = K >> 6;                    // scale blocks per row
+    const int nsb = K >> 6;                    // 64-blocks per row
+    // Scale row stride in 16-bit units: one fp16 per 64-block, or (NVFP4)
+    // two E4M3 bytes per 32-weight chunk.
+    const int sst = FMT == kFmtNvfp4 ? (K >> 5) : nsb;
     const int64_t row_bytes = K >> 1;
     // Rows are split evenly over the groups by the host: rows_q each, one
     // more for the first rows_rem groups (no division on the device).
@@ -242,14 +278,14 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     int cidx[CPL];
     bool cvalid[CPL];
     uint32_t coff[CPL];  // byte offset of the lane's chunk in a row
-    uint32_t soff[CPL];  // element offset of its scale in a row
+    uint32_t soff[CPL];  // 16-bit offset of its scale(s) in a row
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         cidx[i] = lig + i * P;
         cvalid[i] = cidx[i] < C;
         const int c = cvalid[i] ? cidx[i] : C - 1;
         coff[i] = (uint32_t)c * 16u;
-        soff[i] = (uint32_t)c >> 1;
+        soff[i] = FMT == kFmtNvfp4 ? (uint32_t)c : (uint32_t)c >> 1;
     }
 
     uint4 q[S + 1][NR][CPL];
@@ -264,7 +300,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     // without touching memory.  In the SwiGLU form rows LPT.. of a tile are
     // the up rows of rows 0..LPT-1 and come from the up matrix.
     const uint8_t *next_codes0 = sg.codes0 + r_begin * row_bytes;
-    const uint16_t *next_scales0 = sg.scales0 + r_begin * nsb;
+    const uint16_t *next_scales0 = sg.scales0 + r_begin * sst;
     const uint16_t *next_zeros0 = FMT == kFmtAffine ? sg.zeros0 + r_begin * nsb : nullptr;
     const uint8_t *next_codes1 = MODE == kModeSwiglu ? sg.codes1 + r_begin * row_bytes : nullptr;
     const uint16_t *next_scales1 = MODE == kModeSwiglu ? sg.scales1 + r_begin * nsb : nullptr;
@@ -275,7 +311,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         const __amdgpu_buffer_rsrc_t crs0 =
             buffer_rsrc(next_codes0, real ? (uint32_t)(LPT * row_bytes) : 0u);
         const __amdgpu_buffer_rsrc_t srs0 =
-            buffer_rsrc(next_scales0, real ? (uint32_t)(LPT * nsb * 2) : 0u);
+            buffer_rsrc(next_scales0, real ? (uint32_t)(LPT * sst * 2) : 0u);
         __amdgpu_buffer_rsrc_t zrs0 = srs0;
         if constexpr (FMT == kFmtAffine)
             zrs0 = buffer_rsrc(next_zeros0, real ? (uint32_t)(LPT * nsb * 2) : 0u);
@@ -297,14 +333,14 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                     up ? crs1 : crs0, (int)coff[i], (int)(rr * row_bytes), kLoadNonTemporal);
                 q[buf][r][i] = make_uint4(v.x, v.y, v.z, v.w);
                 sc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(up ? srs1 : srs0, (int)(soff[i] * 2),
-                                                                      rr * nsb * 2, kLoadNonTemporal);
+                                                                      rr * sst * 2, kLoadNonTemporal);
                 if constexpr (FMT == kFmtAffine)
                     zc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(zrs0, (int)(soff[i] * 2), rr * nsb * 2,
                                                                           kLoadNonTemporal);
             }
         }
         next_codes0 += LPT * row_bytes;
-        next_scales0 += LPT * nsb;
+        next_scales0 += LPT * sst;
         if constexpr (FMT == kFmtAffine) next_zeros0 += LPT * nsb;
         if constexpr (MODE == kModeSwiglu) {
             next_codes1 += LPT * row_bytes;
@@ -333,6 +369,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     for (int s = 0; s <= S; ++s) load_tile(s);
     if constexpr (FMT == kFmtAffine)
         fill_lut_from(lut, kAffinePairTable);
+    else if constexpr (FMT == kFmtNvfp4)
+        fill_lut_from(lut, kE2m1PairTable);
     else
         fill_lut(lut);
     half2_t xh[CPL][16];
@@ -349,6 +387,9 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     }
 
     const uint32_t laneoff = (uint32_t)lane << 2;
+    // NVFP4-style format: the tensor scale joins the activations' inverse
+    // power of two (both multiply every finished sum).
+    if constexpr (FMT == kFmtNvfp4) down *= *sg.tscale;
 
     // Affine format: the sum of each chunk's 32 activations (zero for chunks
     // past the row's end, whose activations are zero).
@@ -379,10 +420,17 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                 float a = 0.0f;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
-                    float p = chunk_dot(lut, q[buf][r][i], xh[i], laneoff);
-                    if constexpr (FMT == kFmtAffine)
-                        p = fmaf(8.0f - f16_bits_to_f32(zc[buf][r][i]), xsum[i], p);
-                    a = fmaf(p, f16_bits_to_f32(sc[buf][r][i]), a);
+                    if constexpr (FMT == kFmtNvfp4) {
+                        float p0, p1;
+                        chunk_dot_halves(lut, q[buf][r][i], xh[i], laneoff, p0, p1);
+                        a = fmaf(p0, e4m3_to_f32(sc[buf][r][i]), a);
+                        a = fmaf(p1, e4m3_to_f32(sc[buf][r][i] >> 8), a);
+                    } else {
+                        float p = chunk_dot(lut, q[buf][r][i], xh[i], laneoff);
+                        if constexpr (FMT == kFmtAffine)
+                            p = fmaf(8.0f - f16_bits_to_f32(zc[buf][r][i]), xsum[i], p);
+                        a = fmaf(p, f16_bits_to_f32(sc[buf][r][i]), a);
+                    }
                 }
                 acc[j * NR + r] = a;
             }
@@ -504,6 +552,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
     gemv_body<NR, CPL, S, RG, MULTI, kModePlain, kFmtAffine>(sg, K, x, P, (int64_t)blockIdx.x);
 }
 
+// The NVFP4-style format's GEMV (y = s * sum E2M1 * E4M3 * x).
+template <int NR, int CPL, int S, int RG, bool MULTI>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
+                          amdgpu_waves_per_eu(gemv_min_waves(CPL), 8))) void gemv_nvfp4_kernel(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, const float *__restrict__ tscale,
+    int64_t M, int K, const uint16_t *__restrict__ x, float *__restrict__ y, int P, int64_t rows_q, int rows_rem) {
+    GemvSeg sg{};
+    sg.codes0 = codes;
+    sg.scales0 = scales;
+    sg.tscale = tscale;
+    sg.y = y;
+    sg.rows = M;
+    sg.rows_q = rows_q;
+    sg.rows_rem = rows_rem;
+    gemv_body<NR, CPL, S, RG, MULTI, kModePlain, kFmtNvfp4>(sg, K, x, P, (int64_t)blockIdx.x);
+}
+
 // Several segments in one launch: workgroup b belongs to the last segment
 // whose first workgroup is <= b.
 template <int NR, int CPL, int S, int RG, bool MULTI, int MODE>
@@ -545,7 +610,9 @@ int cu_count() {
 }
 
 template <int NR, int CPL, int S, int RG, bool MULTI, int FMT>
-hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M, int K,
+// `extra` is the format's third operand: the affine zero points, or the
+// NVFP4-style tensor scale (unused for NF4).
+hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, const void *extra, int64_t M, int K,
                           const uint16_t *x, float *y, int P, int G, int64_t grid, hipStream_t stream) {
     // The LDS copy of the activations of a row-per-wave variant is one
     // 16-byte unit per lane of the workgroup.
@@ -554,11 +621,17 @@ hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, const ui
     int64_t rows_q = M / ngroups;
     int rows_rem = (int)(M % ngroups);
     if constexpr (FMT == kFmtAffine) {
+        const uint16_t *zeros = static_cast<const uint16_t *>(extra);
         void *args[] = {&codes, &scales, &zeros, &M, &K, &x, &y, &P, &rows_q, &rows_rem};
         return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_affine_kernel<NR, CPL, S, RG, MULTI>),
                                dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
+    } else if constexpr (FMT == kFmtNvfp4) {
+        const float *tscale = static_cast<const float *>(extra);
+        void *args[] = {&codes, &scales, &tscale, &M, &K, &x, &y, &P, &rows_q, &rows_rem};
+        return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_nvfp4_kernel<NR, CPL, S, RG, MULTI>),
+                               dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
     } else {
-        (void)zeros;
+        (void)extra;
         void *args[] = {&codes, &scales, &M, &K, &x, &y, &P, &rows_q, &rows_rem};
         return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_kernel<NR, CPL, S, RG, MULTI>),
                                dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
@@ -692,7 +765,7 @@ hipError_t launch_gemv_fused(const FusedOperand *ops, int count, bool swiglu, in
 // shortest set-up.  Otherwise a ring of two tiles keeps the next tile's
 // loads in flight while the current one is reduced.
 template <int FMT>
-hipError_t launch_gemv_fmt(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
+hipError_t launch_gemv_fmt(const uint8_t *codes, const uint16_t *scales, const void *extra, int64_t M,
                            int64_t K, const uint16_t *x, float *y, hipStream_t stream) {
     const int C = (int)(K / kChunkWeights);
     const int k = (int)K;
@@ -700,12 +773,12 @@ hipError_t launch_gemv_fmt(const uint8_t *codes, const uint16_t *scales, const u
     if (C <= 64) {  // one wave covers a row: 8 independent waves per workgroup
         const int64_t grid = gemv_grid(tiles4, 8);
         if (tiles4 <= 2 * grid * 8)
-            return launch_variant<4, 1, 0, 4, false, FMT>(codes, scales, zeros, M, k, x, y, 64, 8, grid, stream);
-        return launch_variant<4, 1, 1, 8, false, FMT>(codes, scales, zeros, M, k, x, y, 64, 8, grid, stream);
+            return launch_variant<4, 1, 0, 4, false, FMT>(codes, scales, extra, M, k, x, y, 64, 8, grid, stream);
+        return launch_variant<4, 1, 1, 8, false, FMT>(codes, scales, extra, M, k, x, y, 64, 8, grid, stream);
     }
     if (C <= 128) {
         const int64_t tiles2 = (M + 1) / 2;
-        return launch_variant<2, 2, 1, 16, false, FMT>(codes, scales, zeros, M, k, x, y, 64, 8, gemv_grid(tiles2, 8), stream);
+        return launch_variant<2, 2, 1, 16, false, FMT>(codes, scales, extra, M, k, x, y, 64, 8, gemv_grid(tiles2, 8), stream);
     }
     // Long rows: the whole workgroup (up to 8 waves) shares a row tile.
     int cpl = 1;
@@ -716,17 +789,17 @@ hipError_t launch_gemv_fmt(const uint8_t *codes, const uint16_t *scales, const u
     const bool few = tiles4 <= 2 * grid4;
     switch (cpl) {
         case 1:
-            if (few) return launch_variant<4, 1, 0, 4, true, FMT>(codes, scales, zeros, M, k, x, y, P, 1, grid4, stream);
-            return launch_variant<4, 1, 1, 8, true, FMT>(codes, scales, zeros, M, k, x, y, P, 1, grid4, stream);
+            if (few) return launch_variant<4, 1, 0, 4, true, FMT>(codes, scales, extra, M, k, x, y, P, 1, grid4, stream);
+            return launch_variant<4, 1, 1, 8, true, FMT>(codes, scales, extra, M, k, x, y, P, 1, grid4, stream);
         case 2:
-            if (few) return launch_variant<4, 2, 0, 4, true, FMT>(codes, scales, zeros, M, k, x, y, P, 1, grid4, stream);
-            return launch_variant<4, 2, 1, 8, true, FMT>(codes, scales, zeros, M, k, x, y, P, 1, grid4, stream);
+            if (few) return launch_variant<4, 2, 0, 4, true, FMT>(codes, scales, extra, M, k, x, y, P, 1, grid4, stream);
+            return launch_variant<4, 2, 1, 8, true, FMT>(codes, scales, extra, M, k, x, y, P, 1, grid4, stream);
         case 4: {
             const int64_t tiles2 = (M + 1) / 2;
-            return launch_variant<2, 4, 1, 4, true, FMT>(codes, scales, zeros, M, k, x, y, P, 1, gemv_grid(tiles2, 1), stream);
+            return launch_variant<2, 4, 1, 4, true, FMT>(codes, scales, extra, M, k, x, y, P, 1, gemv_grid(tiles2, 1), stream);
         }
         default:
-            return launch_variant<1, 8, 0, 2, true, FMT>(codes, scales, zeros, M, k, x, y, P, 1, gemv_grid(M, 1), stream);
+            return launch_variant<1, 8, 0, 2, true, FMT>(codes, scales, extra, M, k, x, y, P, 1, gemv_grid(M, 1), stream);
     }
 }
 
@@ -738,6 +811,13 @@ hipError_t launch_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, 
 hipError_t launch_gemv_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
                               int64_t K, const uint16_t *x, float *y, hipStream_t stream) {
     return launch_gemv_fmt<kFmtAffine>(codes, scales, zeros, M, K, x, y, stream);
+}
+
+hipError_t launch_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscale, int64_t M,
+                             int64_t K, const uint16_t *x, float *y, hipStream_t stream) {
+    // Two E4M3 bytes per 32-weight chunk are read as one 16-bit value.
+    return launch_gemv_fmt<kFmtNvfp4>(codes, reinterpret_cast<const uint16_t *>(scales), tscale, M, K, x, y,
+                                      stream);
 }
 
 }  // namespace q4

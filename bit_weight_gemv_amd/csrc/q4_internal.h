@@ -18,6 +18,12 @@ hipError_t launch_pack_affine(const float *W, int64_t M, int64_t K, uint8_t *cod
 hipError_t launch_gemv_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
                               int64_t K, const uint16_t *x, float *y, hipStream_t stream);
 
+// The NVFP4-style format (E2M1 * E4M3 per 16 * f32 tensor scale).
+hipError_t launch_pack_nvfp4(const float *W, int64_t M, int64_t K, uint8_t *codes, uint8_t *scales,
+                             float *tscale, int32_t *status, hipStream_t stream);
+hipError_t launch_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscale, int64_t M,
+                             int64_t K, const uint16_t *x, float *y, hipStream_t stream);
+
 // One matrix of a fused GEMV launch (sharing x with the others).
 struct FusedOperand {
     const uint8_t *codes;

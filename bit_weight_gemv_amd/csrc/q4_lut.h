@@ -52,6 +52,20 @@ constexpr PairTable make_affine_pair_table() {
 }
 __device__ const PairTable kAffinePairTable = make_affine_pair_table();
 
+// fp16 bits of an E2M1 code (sign bit 3; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4,
+// 6, all exact in fp16).
+constexpr uint32_t e2m1_f16_bits(int c) {
+    constexpr uint32_t mag[8] = {0x0000u, 0x3800u, 0x3C00u, 0x3E00u, 0x4000u, 0x4200u, 0x4400u, 0x4600u};
+    return mag[c & 7] | ((c & 8) ? 0x8000u : 0u);
+}
+// The E2M1 format's table: entry b is the pair of the byte's two E2M1 values.
+constexpr PairTable make_e2m1_pair_table() {
+    PairTable t{};
+    for (int b = 0; b < 256; ++b) t.v[b] = e2m1_f16_bits(b & 15) | (e2m1_f16_bits(b >> 4) << 16);
+    return t;
+}
+__device__ const PairTable kE2m1PairTable = make_e2m1_pair_table();
+
 // Dword e * 64 + l of the LDS table holds entry e for lane slot l.  The 256
 // entries are written in 8 portions of 32; wave w writes portions w, w + nw,
 // ...: two 16-dword scalar loads fetch a portion's entries, and each entry is

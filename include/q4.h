@@ -224,6 +224,43 @@ int q4_gemv_affine(const uint8_t *codes, const uint16_t *scales,
                    const uint16_t *x, float *y, void *stream);
 
 /*
+ * NVFP4-style format (gizai tensor/lazy page, fp4Blocks: E2M1 codes, two to a
+ * byte with the first in the low half; one E4M3 scale per 16 values along K;
+ * an f32 tensor scale s = max|W| / (6 * 448); a weight is its E2M1 value
+ * times its block's E4M3 scale times s).  Codes are laid out as the NF4
+ * format; scales are E4M3 bytes [M][K/16], row-major (the page interleaves
+ * them for NVIDIA tensor-core tiles; a row-per-wave GEMV wants one row's
+ * scales contiguous).  The page leaves the rounding steps open;
+ * q4_pack_nvfp4 does this:
+ *   - s = the f32 rounding of the fp64 quotient max|W| / 2688;
+ *   - a block's scale: the E4M3 value nearest to amax_block / (6 s), ties to
+ *     the even pattern, at most 448 (s == 0: 0);
+ *   - a code: the E2M1 magnitude nearest to |w| / (scale * s), ties to the
+ *     even pattern, at most 6, with w's sign bit; a block of scale 0 is all
+ *     code 0.
+ * Every decision is an exact comparison, so the result is bit-exact.
+ */
+
+/*
+ * q4_pack_nvfp4 -- quantise W [M][K] (fp32, 16-byte aligned): codes
+ * (16-byte aligned), scales (2-byte aligned), the tensor scale (one float,
+ * 4-byte aligned) and *status (Q4_PACK_NONFINITE if W holds a NaN or an
+ * infinity: the blocks holding one are unspecified, s is taken over the
+ * finite values).  Four launches on `stream`.  No two buffers may overlap.
+ */
+int q4_pack_nvfp4(const float *W, int64_t M, int64_t K, uint8_t *codes,
+                  uint8_t *scales, float *tscale, int32_t *status, void *stream);
+
+/*
+ * q4_gemv_nvfp4 -- y[m] = s * sum_k E2M1(code(m,k)) * E4M3(scale[m][k/16])
+ * * x[k], fp32 accumulation; the tensor scale is read from device memory
+ * (tscale) when the kernel runs.  Accuracy and errors as q4_gemv.
+ */
+int q4_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales,
+                  const float *tscale, int64_t M, int64_t K,
+                  const uint16_t *x, float *y, void *stream);
+
+/*
  * Packed row gather (deep-fold "Decode V2" page, run notes of section 6: the
  * embedding is kept as packed rows and the rows a step needs are dequantised
  * into its arena, with no dense vocabulary table; a tied embedding shares

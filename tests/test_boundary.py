@@ -33,7 +33,8 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused",
-              "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_codebook", "q4_codes_bytes",
+              "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_pack_nvfp4", "q4_gemv_nvfp4",
+              "q4_codebook", "q4_codes_bytes",
               "q4_scales_bytes", "q4_status_string"):
         assert n in names
 
@@ -261,6 +262,24 @@ def test_affine_errors(q4):
     assert L.q4_gemv_affine(A, B, 0, 16, 128, D, E, None) == q4.Q4_ERR_NULL
     assert L.q4_gemv_affine(A, B, C + 1, 16, 128, D, E, None) == q4.Q4_ERR_ALIGN
     assert L.q4_gemv_affine(A, B, C, 16, 128, D, C + 16, None) == q4.Q4_ERR_OVERLAP  # y over zeros
+    # every call above fails a host check and launches nothing
+
+
+def test_nvfp4_errors(q4):
+    L = q4.lib()
+    # W A (M=16, K=128 fp32: 8 KB), codes B (1 KB), scales C (128 B), tscale D, status E
+    assert L.q4_pack_nvfp4(A, 16, 100, B, C, D, E, None) == q4.Q4_ERR_SHAPE
+    assert L.q4_pack_nvfp4(A, 16, 128, B, C, 0, E, None) == q4.Q4_ERR_NULL
+    assert L.q4_pack_nvfp4(A, 16, 128, B, C + 1, D, E, None) == q4.Q4_ERR_ALIGN
+    assert L.q4_pack_nvfp4(A, 16, 128, B, C, D + 2, E, None) == q4.Q4_ERR_ALIGN
+    assert L.q4_pack_nvfp4(A, 16, 128, B, C, C + 124, E, None) == q4.Q4_ERR_OVERLAP  # tscale in scales
+    # gemv: codes A, scales B (128 B), tscale C, x D (256 B), y E (64 B)
+    assert L.q4_gemv_nvfp4(A, B, C, 16, 100, D, E, None) == q4.Q4_ERR_SHAPE
+    assert L.q4_gemv_nvfp4(A, B, C, 0, 128, 0, 0, None) == q4.Q4_OK
+    assert L.q4_gemv_nvfp4(A, B, 0, 16, 128, D, E, None) == q4.Q4_ERR_NULL
+    assert L.q4_gemv_nvfp4(A, B + 1, C, 16, 128, D, E, None) == q4.Q4_ERR_ALIGN
+    assert L.q4_gemv_nvfp4(A, B, C, 16, 128, D, B + 64, None) == q4.Q4_ERR_OVERLAP  # y over scales
+    assert L.q4_gemv_nvfp4(A, B, C, 16, 128, D, C - 32, None) == q4.Q4_ERR_OVERLAP  # y over tscale
     # every call above fails a host check and launches nothing
 
 

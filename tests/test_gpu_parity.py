@@ -877,3 +877,92 @@ def test_affine_full_size_gateup(env):
     torch.cuda.synchronize()
     y_ref, S = oracle.gemv_affine(c_ref, s_ref, z_ref, M, K, x, threads=threads)
     _check(y.cpu().numpy(), y_ref, S, "affine gemv gate/up 22016x2048")
+
+
+# ---------------------------------------------------------------------------
+# NVFP4-style format: q4_pack_nvfp4 (bit-exact) and q4_gemv_nvfp4
+# ---------------------------------------------------------------------------
+
+def _nvfp4_gpu_pack(env, W):
+    torch, q4, dev = env
+    codes, scales, ts, status = q4.q4_pack_nvfp4(cases.to_dev(W, torch, dev))
+    torch.cuda.synchronize()
+    return codes, scales, ts, int(status.item())
+
+
+def _nvfp4_check_pack(env, W):
+    c_ref, s_ref, ts_ref, st_ref = oracle.pack_nvfp4(W)
+    codes, scales, ts, st = _nvfp4_gpu_pack(env, W)
+    assert st == st_ref == 0
+    assert np.float32(ts.item()).view(np.uint32) == np.float32(ts_ref).view(np.uint32)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    return c_ref, s_ref, ts_ref
+
+
+@pytest.mark.parametrize("M,K", [(1, 64), (17, 192), (256, 512), (5, 4096), (33, 11008)])
+def test_nvfp4_pack_bit_exact(env, M, K):
+    W = wl.weights(M, K, 9000 + M + K, std=0.5)
+    if M > 2:
+        W[1, 16:32] *= 1e-4      # subnormal E4M3 block scale
+        W[2, 32:48] = 0.0        # zero block
+        W[0, 5] = -0.0
+    _nvfp4_check_pack(env, W)
+
+
+def test_nvfp4_pack_ties_and_flags(env):
+    torch, q4, dev = env
+    W = np.zeros((2, 64), np.float32)
+    W[0, 0] = 2688.0
+    W[0, 16:32] = [6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, -0.25, -5, 0.5, 3, 0, -6, 4, 1.5]
+    W[0, 32:34] = [6.375, 1.0]
+    W[1, 0:16] = 1e-6            # tiny against the tensor scale: scale 0 or subnormal
+    _nvfp4_check_pack(env, W)
+    _nvfp4_check_pack(env, np.zeros((3, 128), np.float32))  # s == 0
+    Wb = W.copy()
+    Wb[1, 40] = np.nan
+    _, _, _, st = _nvfp4_gpu_pack(env, Wb)
+    assert st == q4.Q4_PACK_NONFINITE == oracle.pack_nvfp4(Wb)[3]
+
+
+NVFP4_GEMV_SHAPES = [(1, 64), (7, 128), (1000, 1024), (4097, 2048), (40001, 64), (300, 2112), (65, 4096),
+                     (129, 4160), (2048, 11008), (4101, 16448), (3, 32768), (2, 131072)]
+
+
+@pytest.mark.parametrize("M,K", NVFP4_GEMV_SHAPES)
+def test_nvfp4_gemv_parity(env, M, K):
+    torch, q4, dev = env
+    seed = 9100 + M + K
+    W = wl.weights(M, K, seed, std=0.5)
+    if M > 3:
+        W[3, :64] *= 1e-4                 # subnormal block scales in the product
+    x = wl.activation(K, seed, "normal")
+    codes, scales, ts, st = oracle.pack_nvfp4(W)
+    assert st == 0
+    y_ref, S = oracle.gemv_nvfp4(codes, scales, ts, M, K, x)
+    c = cases.to_dev(codes, torch, dev)
+    s = cases.to_dev(scales, torch, dev)
+    t = torch.tensor([ts], dtype=torch.float32, device=dev)
+    y = q4.q4_gemv_nvfp4(c, s, t, _x_dev(env, x))
+    torch.cuda.synchronize()
+    _check(y.cpu().numpy(), y_ref, S, f"nvfp4 gemv M={M} K={K}")
+
+
+def test_nvfp4_full_size_gateup(env):
+    """The gate/up shape: GPU pack bit-exact with the oracle, then the GEMV on
+    every row (reading the tensor scale the pack wrote) against the oracle."""
+    torch, q4, dev = env
+    c_cfg = wl.CONFIGS["gateup"]
+    M, K = c_cfg["M"], c_cfg["K"]
+    W = wl.weights(M, K, c_cfg["seed"])
+    x = wl.activation(K, c_cfg["seed"], c_cfg["x"])
+    threads = min(16, os.cpu_count() or 1)
+    c_ref, s_ref, ts_ref, st = oracle.pack_nvfp4(W, threads=threads)
+    assert st == 0
+    codes, scales, ts, st_g = _nvfp4_gpu_pack(env, W)
+    assert st_g == 0 and ts.item() == ts_ref
+    assert np.array_equal(codes.cpu().numpy(), c_ref) and np.array_equal(scales.cpu().numpy(), s_ref)
+    y = q4.q4_gemv_nvfp4(codes, scales, ts, _x_dev(env, x))
+    torch.cuda.synchronize()
+    y_ref, S = oracle.gemv_nvfp4(c_ref, s_ref, ts_ref, M, K, x, threads=threads)
+    _check(y.cpu().numpy(), y_ref, S, "nvfp4 gemv gate/up 22016x2048")
