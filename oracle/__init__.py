@@ -101,6 +101,12 @@ def _load():
         lib.oracle_dequant_nvfp4.restype = None
         lib.oracle_gemv_nvfp4_rows.argtypes = [P, P, ctypes.c_float, I64, I64, P, I64, I64, P, P]
         lib.oracle_gemv_nvfp4_rows.restype = None
+        lib.oracle_quantize_x8.argtypes = [P, I64, ctypes.c_int, P, P, P]
+        lib.oracle_quantize_x8.restype = None
+        lib.oracle_dequantize_x8.argtypes = [P, P, P, I64, P]
+        lib.oracle_dequantize_x8.restype = None
+        lib.oracle_gemv_affine_x8_rows.argtypes = [P, P, P, I64, I64, P, P, P, I64, I64, P, P]
+        lib.oracle_gemv_affine_x8_rows.restype = None
         lib.oracle_f64_to_bf16_rne.argtypes = [ctypes.c_double]
         lib.oracle_f64_to_bf16_rne.restype = ctypes.c_uint16
         lib.oracle_gather_rows.argtypes = [P, P, I64, I64, P, I64, ctypes.c_int, P]
@@ -384,6 +390,49 @@ def gemv_nvfp4(codes, scales, s: float, M: int, K: int, x_bits, rows=None, threa
                                    _ptr(y), _ptr(S))
 
     _run_rows(r1 - r0, threads, run, [0])
+    return y, S
+
+
+def quantize_x8(x_bits, words: int = 2):
+    """(q1 int8 [K], q2 int8 [K] or None, d fp32 [K/32]) of bf16 x."""
+    x_bits = np.ascontiguousarray(x_bits, np.uint16)
+    K = x_bits.size
+    if K % 32 != 0 or words not in (1, 2):
+        raise ValueError("oracle.quantize_x8: K % 32 == 0 and words in (1, 2)")
+    q1 = np.zeros(K, np.int8)
+    q2 = np.zeros(K, np.int8) if words == 2 else None
+    d = np.zeros(K // 32, np.float32)
+    _load().oracle_quantize_x8(_ptr(x_bits), K, words, _ptr(q1), _ptr(q2) if q2 is not None else None, _ptr(d))
+    return q1, q2, d
+
+
+def dequantize_x8(q1, q2, d) -> np.ndarray:
+    q1 = np.ascontiguousarray(q1, np.int8)
+    d = np.ascontiguousarray(d, np.float32)
+    out = np.zeros(q1.size, np.float64)
+    q2c = np.ascontiguousarray(q2, np.int8) if q2 is not None else None
+    _load().oracle_dequantize_x8(_ptr(q1), _ptr(q2c) if q2c is not None else None, _ptr(d), q1.size, _ptr(out))
+    return out
+
+
+def gemv_affine_x8(codes, scales, zeros, M: int, K: int, q1, q2, d, threads: int = 1):
+    """y, S (fp64) of the affine format's GEMV on int8 activations."""
+    _check_shape(M, K)
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint16)
+    zeros = np.ascontiguousarray(zeros, np.uint16)
+    q1 = np.ascontiguousarray(q1, np.int8)
+    q2c = np.ascontiguousarray(q2, np.int8) if q2 is not None else None
+    d = np.ascontiguousarray(d, np.float32)
+    y = np.full(M, np.nan)
+    S = np.full(M, np.nan)
+    lib = _load()
+
+    def run(a, b, slot):
+        lib.oracle_gemv_affine_x8_rows(_ptr(codes), _ptr(scales), _ptr(zeros), M, K, _ptr(q1),
+                                       _ptr(q2c) if q2c is not None else None, _ptr(d), a, b, _ptr(y), _ptr(S))
+
+    _run_rows(M, threads, run, [0])
     return y, S
 
 

@@ -650,3 +650,87 @@ void oracle_gemv_nvfp4_rows(const uint8_t *codes, const uint8_t *scales, float s
         if (S) S[m] = absum;
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* int8 activations for the integer-code (affine) format (deep-fold page's  */
+/* lane knobs, section "The lane": a projection's activation may be one     */
+/* int8 word, as llama.cpp does, or two int8 words of about 14 bits, the    */
+/* default).  Reading taken:                                                 */
+/*   - blocks of 32 activations along K (one 16-byte code chunk);           */
+/*   - d = the f32 rounding of the fp64 quotient max|x_block| / 127;        */
+/*   - q1 = the integer nearest to x / d, ties to even, within +-127;       */
+/*   - two words: r = x - q1 d (exact) and q2 = the integer nearest to      */
+/*     128 r / d, ties to even, within +-127 (|r| <= d/2 keeps it in +-64);   */
+/*   - the value carried is xq = d (q1 + q2 / 128) (q2 = 0 for one word);   */
+/*   - every decision compares |x| (or |r|) with (j + 1/2) d (or / 128),    */
+/*     exact in fp64, so any implementation decides alike.                  */
+/* The product then uses xq in place of x: the GEMV tolerance applies to    */
+/* sum What xq, and |x - xq| <= d / 2 (one word) or d / 256 (two words).    */
+/* ------------------------------------------------------------------------ */
+
+/* Nearest integer to a / u (a >= 0, u > 0) in 0..127, ties to even, by
+ * comparisons with (j + 1/2) u. */
+static int nearest_int_127(double a, double u) {
+    int j = 0;
+    while (j < 127) {
+        const double mid = ((double)j + 0.5) * u;
+        if (a > mid || (a == mid && (j & 1))) ++j;
+        else break;
+    }
+    return j;
+}
+
+void oracle_quantize_x8(const uint16_t *x, int64_t K, int words, int8_t *q1, int8_t *q2, float *d) {
+    for (int64_t b = 0; b < K / 32; ++b) {
+        double amax = 0.0;
+        for (int k = 0; k < 32; ++k) {
+            const double v = fabs(oracle_bf16_to_f64(x[b * 32 + k]));
+            if (v > amax) amax = v;
+        }
+        const float db = (float)(amax / 127.0);
+        d[b] = db;
+        for (int k = 0; k < 32; ++k) {
+            const int64_t i = b * 32 + k;
+            const double v = oracle_bf16_to_f64(x[i]);
+            int a1 = 0, a2 = 0;
+            if (db > 0.0f) {
+                a1 = nearest_int_127(fabs(v), (double)db);
+                if (v < 0) a1 = -a1;
+                if (words == 2) {
+                    const double r = v - (double)a1 * (double)db; /* exact */
+                    a2 = nearest_int_127(fabs(r), (double)db / 128.0);
+                    if (r < 0) a2 = -a2;
+                }
+            }
+            q1[i] = (int8_t)a1;
+            if (words == 2) q2[i] = (int8_t)a2;
+        }
+    }
+}
+
+/* xq[k] = d (q1 + q2 / 128), exact in fp64 (q2 NULL: one word). */
+void oracle_dequantize_x8(const int8_t *q1, const int8_t *q2, const float *d, int64_t K, double *xq) {
+    for (int64_t k = 0; k < K; ++k)
+        xq[k] = (double)d[k / 32] * ((double)q1[k] + (q2 ? (double)q2[k] / 128.0 : 0.0));
+}
+
+/* The affine format's GEMV on int8 activations: y[m] = sum_k What[m,k] xq[k]
+ * (each term exact in fp64, ascending k), S[m] = sum_k |What[m,k] xq[k]|. */
+void oracle_gemv_affine_x8_rows(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
+                                int64_t K, const int8_t *q1, const int8_t *q2, const float *d, int64_t row0,
+                                int64_t row1, double *y, double *S) {
+    (void)M;
+    for (int64_t m = row0; m < row1; ++m) {
+        double total = 0.0, size = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t g = m * (K / 64) + k / 64;
+            const double wv = ((double)code_at(codes, K, m, k) - oracle_f16_to_f64(zeros[g])) *
+                              oracle_f16_to_f64(scales[g]);
+            const double xv = (double)d[k / 32] * ((double)q1[k] + (q2 ? (double)q2[k] / 128.0 : 0.0));
+            total += wv * xv;
+            size += fabs(wv * xv);
+        }
+        y[m] = total;
+        if (S) S[m] = size;
+    }
+}

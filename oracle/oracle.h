@@ -138,6 +138,18 @@ void oracle_gemv_nvfp4_rows(const uint8_t *codes, const uint8_t *scales, float s
                             int64_t K, const uint16_t *x, int64_t row0, int64_t row1,
                             double *y, double *S);
 
+/* int8 activations (deep-fold page, "The lane": one int8 word per
+ * activation, or two of about 14 bits): per 32-block of x (bf16 bits [K]),
+ * d = f32(max|x| / 127), q1 = nearest(x / d), q2 = nearest(128 (x - q1 d) / d)
+ * (two words; q2 may be NULL for one), ties to even, within +-127.  The
+ * carried value is xq = d (q1 + q2 / 128). */
+void oracle_quantize_x8(const uint16_t *x, int64_t K, int words, int8_t *q1, int8_t *q2, float *d);
+void oracle_dequantize_x8(const int8_t *q1, const int8_t *q2, const float *d, int64_t K, double *xq);
+/* The affine format's GEMV on xq (q2 NULL: one word). */
+void oracle_gemv_affine_x8_rows(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros,
+                                int64_t M, int64_t K, const int8_t *q1, const int8_t *q2,
+                                const float *d, int64_t row0, int64_t row1, double *y, double *S);
+
 /* First index of the maximum (NaN never wins); -1 if n == 0 or all NaN. */
 int64_t oracle_argmax_f64(const double *y, int64_t n);
 int64_t oracle_argmax_f32(const float *y, int64_t n);

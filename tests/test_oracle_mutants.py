@@ -71,6 +71,13 @@ MUTANTS = {
                        "oracle_e4m3_to_f64(scales[m * (K / 16) + k / 32]) * (double)s;\n}"),
     "nvfp4_gemv_drops_tensor_scale": ("oracle_e4m3_to_f64(scales[m * (K / 16) + k / 16]) * (double)s;\n            const double prod",
                                       "oracle_e4m3_to_f64(scales[m * (K / 16) + k / 16]);\n            const double prod"),
+    "x8_ties_up": ("if (a > mid || (a == mid && (j & 1))) ++j;", "if (a >= mid) ++j;"),
+    "x8_scale_128": ("const float db = (float)(amax / 127.0);", "const float db = (float)(amax / 128.0);"),
+    "x8_second_word_256": ("a2 = nearest_int_127(fabs(r), (double)db / 128.0);",
+                           "a2 = nearest_int_127(fabs(r), (double)db / 256.0);"),
+    "x8_second_word_sign": ("if (r < 0) a2 = -a2;", "if (v < 0) a2 = -a2;"),
+    "x8_gemv_second_word_256": ("const double xv = (double)d[k / 32] * ((double)q1[k] + (q2 ? (double)q2[k] / 128.0 : 0.0));",
+                                "const double xv = (double)d[k / 32] * ((double)q1[k] + (q2 ? (double)q2[k] / 256.0 : 0.0));"),
     "residual_dropped": ("if (residual) v += (double)residual[i];", "if (residual && !swiglu) v += (double)residual[i];"),
 }
 

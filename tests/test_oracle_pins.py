@@ -967,3 +967,87 @@ def test_nvfp4_gemv_matches_blas_and_one_hot(oracle_mod):
     sc = np.full((1, 4), 0x30, np.uint8)
     Wh = oracle_mod.dequant_nvfp4(cb, sc, np.float32(0.25), 1, 64)
     assert Wh[0, 0] == 0.0 and Wh[0, 1] == -1.5 * 0.5 * 0.25
+
+
+# ---------------------------------------------------------------------------
+# int8 activations (one or two words) and the affine GEMV on them
+# ---------------------------------------------------------------------------
+
+def _nearest_int_even(t):
+    """Nearest integer to the rational t >= 0, ties to even, at most 127."""
+    j = int(t)
+    f = t - j
+    if f > Fraction(1, 2) or (f == Fraction(1, 2) and j % 2 == 1):
+        j += 1
+    return min(j, 127)
+
+
+def _bf16_from_values(vals):
+    b = np.array(vals, np.float32).view(np.uint32)
+    assert np.all(b & 0xFFFF == 0), "fixture values must be bf16"
+    return (b >> 16).astype(np.uint16)
+
+
+def test_quantize_x8_brute_force(oracle_mod):
+    x = wl.activation(256, 51, "normal")
+    x[40] = 0x8000  # -0.0
+    for words in (1, 2):
+        q1, q2, d = oracle_mod.quantize_x8(x, words)
+        xv = wl.bf16_bits_to_f32(x).astype(np.float64)
+        for b in range(8):
+            blk = xv[32 * b:32 * b + 32]
+            assert d[b] == np.float32(np.max(np.abs(blk)) / 127.0)
+            D = Fraction(float(d[b]))
+            for k in range(32):
+                v = Fraction(float(blk[k]))
+                a1 = _nearest_int_even(abs(v) / D) * (1 if v >= 0 else -1)
+                assert q1[32 * b + k] == a1
+                if words == 2:
+                    r = v - a1 * D
+                    a2 = _nearest_int_even(abs(r) * 128 / D) * (1 if r >= 0 else -1)
+                    assert q2[32 * b + k] == a2
+
+
+def test_quantize_x8_ties_and_bounds(oracle_mod):
+    vals = np.zeros(32, np.float32)
+    vals[:6] = [127.0, 2.5, 3.5, -2.5, 0.5, 0.50390625]  # d = 1: ties to 2, 4, -2, 0, and 1 + (-63.5 -> -64)/128
+    x = _bf16_from_values(vals)
+    q1, q2, d = oracle_mod.quantize_x8(x, 2)
+    assert d[0] == 1.0
+    assert list(q1[:6]) == [127, 2, 4, -2, 0, 1]
+    assert q2[5] == -64 and q2[4] == 64
+    # the bounds |x - xq| <= d/2 (one word) and d/256 (two words)
+    xr = wl.activation(4096, 52, "normal")
+    xv = wl.bf16_bits_to_f32(xr).astype(np.float64)
+    for words, lim in ((1, 0.5), (2, 1.0 / 256)):
+        a, b2, dd = oracle_mod.quantize_x8(xr, words)
+        xq = oracle_mod.dequantize_x8(a, b2, dd)
+        assert np.all(np.abs(xq - xv) <= lim * np.repeat(dd.astype(np.float64), 32))
+    z = np.zeros(64, np.uint16)
+    a, b2, dd = oracle_mod.quantize_x8(z, 2)
+    assert not a.any() and not b2.any() and not dd.any()
+
+
+def test_affine_x8_gemv_matches_blas_and_exact_case(oracle_mod):
+    M, K = 19, 256
+    W = wl.weights(M, K, 53, std=0.5)
+    codes, scales, zeros, st = oracle_mod.pack_affine(W)
+    x = wl.activation(K, 53, "normal")
+    for words in (1, 2):
+        q1, q2, d = oracle_mod.quantize_x8(x, words)
+        y, S = oracle_mod.gemv_affine_x8(codes, scales, zeros, M, K, q1, q2, d)
+        What = oracle_mod.dequant_affine(codes, scales, zeros, M, K)
+        xq = oracle_mod.dequantize_x8(q1, q2, d)
+        assert np.allclose(y, What @ xq, rtol=1e-12, atol=1e-12)
+        assert np.allclose(S, np.abs(What) @ np.abs(xq), rtol=1e-12)
+    # integer activations with each block's maximum 127: d = 1, xq == x, so
+    # the product equals the bf16 GEMV bit for bit
+    rng = np.random.default_rng(54)
+    iv = rng.integers(-127, 128, K).astype(np.float32)
+    iv[::32] = 127.0
+    xi = _bf16_from_values(iv)
+    q1, q2, d = oracle_mod.quantize_x8(xi, 2)
+    assert np.all(d == 1.0) and not q2.any()
+    y8, _ = oracle_mod.gemv_affine_x8(codes, scales, zeros, M, K, q1, q2, d)
+    yb, _ = oracle_mod.gemv_affine(codes, scales, zeros, M, K, xi)
+    assert np.array_equal(y8, yb)
