@@ -1,7 +1,7 @@
 """Benchmark of the 4-bit codebook GEMV on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--copies R] [--no-secondary]
-                    [--secondary down,smalln,gateup,fused,gather,affine,nvfp4]
+                    [--secondary down,smalln,gateup,fused,gather,affine,nvfp4,x8]
 
 A step is one q4_gemv call on the lm_head workload (M x K = 151936 x 2048,
 x bf16 unit-RMS, y fp32): the projection the metric is quoted on.  Inputs are
@@ -364,6 +364,43 @@ def nvfp4_secondaries(torch, q4, wl, dev, steps, warmup):
     return out
 
 
+def x8_secondaries(torch, q4, wl, dev, steps, warmup):
+    """The affine format's GEMV on int8 activations (one and two words) on
+    the lm_head shape; the activation quantisation timed as its own call."""
+    out = []
+    c = wl.CONFIGS["lm_head"]
+    M, K = c["M"], c["K"]
+    W = torch.from_numpy(wl.weights(M, K, c["seed"])).to(dev)
+    codes, scales, zeros, status = q4.q4_pack_affine(W)
+    torch.cuda.synchronize()
+    del W
+    reps = [(codes, scales, zeros)] + [(codes.clone(), scales.clone(), zeros.clone()) for _ in range(3)]
+    x = _upload_bits(torch, wl.activation(K, c["seed"], c["x"]), torch.bfloat16, dev)
+    y = torch.empty(M, dtype=torch.float32, device=dev)
+    for words in (1, 2):
+        q1, q2, d = q4.q4_quantize_x8(x, words)
+
+        def fn(cd, sl, zr, q1=q1, q2=q2, d=d):
+            q4.q4_gemv_affine_x8(cd, sl, zr, q1, q2, d, y)
+        ms, wall = time_graph(torch, fn, reps, steps, warmup)
+        nb = gemv_bytes(M, K) + M * K // 32 - 2 * K + K * words + K // 8
+        gbs = nb / (ms * 1e-3) / 1e9
+        log(f"affine x8 ({words} word) lm_head: {ms * 1e3:.2f} us/call, {gbs:.0f} GB/s")
+        out.append({"workload": f"affine-format GEMV on int8 activations ({words} word) lm_head {M}x{K} N=1",
+                    "us_per_call": round(ms * 1e3, 3), "us_per_step_wall": round(wall * 1e3, 3),
+                    "achieved_GBs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": nb})
+
+        def qfn(xx, words=words, q1=q1, q2=q2, d=d):
+            q4.q4_quantize_x8(xx, words, q1, q2, d)
+        qms, qwall = time_graph(torch, qfn, [(x,)], steps, warmup)
+        log(f"quantize x8 ({words} word) K={K}: {qms * 1e3:.2f} us/call")
+        out.append({"workload": f"activation quantisation to int8 ({words} word) K={K}",
+                    "us_per_call": round(qms * 1e3, 3), "us_per_step_wall": round(qwall * 1e3, 3)})
+    del reps, codes, scales, zeros, x, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def context_bandwidth(torch, dev, steps=20):
     """Bandwidth context from a library-independent kernel: torch's device
     copy of COPY_PROBE_BYTES, replayed as a graph; (read + written bytes) / s
@@ -415,9 +452,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--secondary", default="down,smalln,gateup,fused,gather,affine,nvfp4",
+    ap.add_argument("--secondary", default="down,smalln,gateup,fused,gather,affine,nvfp4,x8",
                     help="comma-separated secondary workloads to time "
-                         "(down, smalln, gateup, fused, gather, affine, nvfp4)")
+                         "(down, smalln, gateup, fused, gather, affine, nvfp4, x8)")
     ap.add_argument("--eager", action="store_true",
                     help="also time the calls launched one by one from Python")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -520,6 +557,8 @@ def main():
             secondary.extend(affine_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
         if "nvfp4" in chosen:
             secondary.extend(nvfp4_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
+        if "x8" in chosen:
+            secondary.extend(x8_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
 
     result = {
         "metric": "4-bit GEMV us/call + achieved HBM GB/s (% of peak), MxK=151936x2048, N=1",

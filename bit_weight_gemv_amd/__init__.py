@@ -32,7 +32,8 @@ Q4_PACK_OVERFLOW = 2
 
 EXPORTED = ("q4_codes_bytes", "q4_scales_bytes", "q4_codebook", "q4_status_string",
             "q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused",
-            "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_pack_nvfp4", "q4_gemv_nvfp4")
+            "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_pack_nvfp4", "q4_gemv_nvfp4",
+            "q4_quantize_x8", "q4_gemv_affine_x8")
 
 Q4_OUT_F32 = 0
 Q4_OUT_BF16 = 1
@@ -97,6 +98,10 @@ def lib() -> ctypes.CDLL:
         L.q4_pack_nvfp4.restype = I32
         L.q4_gemv_nvfp4.argtypes = [P, P, P, I64, I64, P, P, P]
         L.q4_gemv_nvfp4.restype = I32
+        L.q4_quantize_x8.argtypes = [P, I64, I32, P, P, P, P]
+        L.q4_quantize_x8.restype = I32
+        L.q4_gemv_affine_x8.argtypes = [P, P, P, I64, I64, P, P, P, P, P]
+        L.q4_gemv_affine_x8.restype = I32
         _lib = L
         return L
 
@@ -427,4 +432,52 @@ def q4_gemv_nvfp4(codes, scales, tscale, x, y=None, stream=None):
     st = lib().q4_gemv_nvfp4(_ptr(codes), _ptr(scales), _ptr(tscale), M, K, _ptr(x), _ptr(y), _stream(stream))
     if st != Q4_OK:
         raise Q4Error(st, "q4_gemv_nvfp4")
+    return y
+
+
+def q4_quantize_x8(x, words=2, q1=None, q2=None, d=None, stream=None):
+    """bf16 x [K] -> (q1 int8 [K], q2 int8 [K] or None, d fp32 [K/32])."""
+    torch = _torch()
+    dev = x.device
+    _check(x, "x", torch.bfloat16, dev)
+    K = x.numel()
+    if words not in (1, 2):
+        raise ValueError("words must be 1 or 2")
+    if q1 is None:
+        q1 = torch.empty(K, dtype=torch.int8, device=dev)
+    if q2 is None and words == 2:
+        q2 = torch.empty(K, dtype=torch.int8, device=dev)
+    if d is None:
+        d = torch.empty(K // 32, dtype=torch.float32, device=dev)
+    _check(q1, "q1", torch.int8, dev)
+    _check(d, "d", torch.float32, dev)
+    if words == 2:
+        _check(q2, "q2", torch.int8, dev)
+    st = lib().q4_quantize_x8(_ptr(x), K, words, _ptr(q1), _ptr(q2) if words == 2 else None, _ptr(d),
+                              _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_quantize_x8")
+    return q1, (q2 if words == 2 else None), d
+
+
+def q4_gemv_affine_x8(codes, scales, zeros, q1, q2, d, y=None, stream=None):
+    """y fp32 [M] = W . xq for an affine-format W and int8 activations from
+    q4_quantize_x8 (q2 None: one word)."""
+    torch = _torch()
+    M, K = _mk(codes, scales)
+    dev = codes.device
+    _check(zeros, "zeros", torch.float16, dev)
+    _check(q1, "q1", torch.int8, dev)
+    _check(d, "d", torch.float32, dev)
+    if q2 is not None:
+        _check(q2, "q2", torch.int8, dev)
+    if q1.numel() != K or d.numel() != K // 32 or (q2 is not None and q2.numel() != K):
+        raise ValueError("activation words do not match K")
+    if y is None:
+        y = torch.empty(M, dtype=torch.float32, device=dev)
+    _check(y, "y", torch.float32, dev)
+    st = lib().q4_gemv_affine_x8(_ptr(codes), _ptr(scales), _ptr(zeros), M, K, _ptr(q1),
+                                 _ptr(q2) if q2 is not None else None, _ptr(d), _ptr(y), _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_gemv_affine_x8")
     return y

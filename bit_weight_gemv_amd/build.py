@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libq4.so")
-SOURCES = ["q4_api.cpp", "q4_pack.hip", "q4_gemv.hip", "q4_gemm_smalln.hip", "q4_gather.hip"]
+SOURCES = ["q4_api.cpp", "q4_pack.hip", "q4_gemv.hip", "q4_gemm_smalln.hip", "q4_gather.hip", "q4_quant.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -148,6 +148,34 @@ int q4_gemv_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t 
     return launch_status(q4::launch_gemv_affine(codes, scales, zeros, M, K, x, y, (hipStream_t)stream));
 }
 
+int q4_quantize_x8(const uint16_t *x, int64_t K, int words, int8_t *q1, int8_t *q2, float *d, void *stream) {
+    if (!shape_ok(0, K) || (words != 1 && words != 2)) return Q4_ERR_SHAPE;
+    if (!x || !q1 || !d || (words == 2 && !q2)) return Q4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(q1, 16) || !aligned(q2, 16) || !aligned(d, 4)) return Q4_ERR_ALIGN;
+    const Range rx = range_of(x, (uint64_t)K * 2), r1 = range_of(q1, (uint64_t)K),
+                r2 = range_of(words == 2 ? q2 : nullptr, words == 2 ? (uint64_t)K : 0), rd = range_of(d, (uint64_t)K / 8);
+    if (overlap(rx, r1) || overlap(rx, r2) || overlap(rx, rd) || overlap(r1, r2) || overlap(r1, rd) || overlap(r2, rd))
+        return Q4_ERR_OVERLAP;
+    return launch_status(q4::launch_quantize_x8(x, K, words, q1, words == 2 ? q2 : nullptr, d, (hipStream_t)stream));
+}
+
+int q4_gemv_affine_x8(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M, int64_t K,
+                      const int8_t *q1, const int8_t *q2, const float *d, float *y, void *stream) {
+    if (!shape_ok(M, K)) return Q4_ERR_SHAPE;
+    if (M == 0) return Q4_OK;
+    if (!codes || !scales || !zeros || !q1 || !d || !y) return Q4_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2) || !aligned(q1, 16) || !aligned(q2, 16) ||
+        !aligned(d, 4) || !aligned(y, 4))
+        return Q4_ERR_ALIGN;
+    const Range ry = range_of(y, (uint64_t)M * 4);
+    const uint64_t sb = (uint64_t)M * (K / 64) * 2;
+    if (overlap(ry, range_of(codes, (uint64_t)M * (K / 2))) || overlap(ry, range_of(scales, sb)) ||
+        overlap(ry, range_of(zeros, sb)) || overlap(ry, range_of(q1, (uint64_t)K)) ||
+        overlap(ry, range_of(q2, q2 ? (uint64_t)K : 0)) || overlap(ry, range_of(d, (uint64_t)K / 8)))
+        return Q4_ERR_OVERLAP;
+    return launch_status(q4::launch_gemv_affine_x8(codes, scales, zeros, M, K, q1, q2, d, y, (hipStream_t)stream));
+}
+
 int q4_pack_nvfp4(const float *W, int64_t M, int64_t K, uint8_t *codes, uint8_t *scales, float *tscale,
                   int32_t *status, void *stream) {
     if (!shape_ok(M, K)) return Q4_ERR_SHAPE;

@@ -203,6 +203,9 @@ struct GemvSeg {
     const uint16_t *scales0;
     const uint16_t *zeros0;  // affine format only: fp16 zero points [rows][K/64]
     const float *tscale;     // NVFP4-style format only: the f32 tensor scale
+    const int8_t *xq1;       // int8-activation forms: first words [K]
+    const int8_t *xq2;       //   second words [K] (two-word form)
+    const float *xd;         //   block scales [K/32]
     const uint8_t *codes1;
     const uint16_t *scales1;
     const float *bias0;
@@ -225,7 +228,18 @@ enum { kModePlain = 0, kModeEpi = 1, kModeSwiglu = 2 };
 // accel/tensor, type Int4 and func Int4MatVec), or the NVFP4-style format
 // (E2M1 * E4M3 scale per 16 weights * an f32 tensor scale; gizai tensor/lazy,
 // fp4Blocks).
-enum { kFmtNf4 = 0, kFmtAffine = 1, kFmtNvfp4 = 2 };
+// kFmtAffineX8 / kFmtAffineX8x2: the affine format with int8 activations of
+// one or two words (the deep-fold page's lane: one int8 word as llama.cpp
+// does, or two of about 14 bits): integer dot products, no table.
+enum { kFmtNf4 = 0, kFmtAffine = 1, kFmtNvfp4 = 2, kFmtAffineX8 = 3, kFmtAffineX8x2 = 4 };
+
+// Host-side operands of the int8-activation forms.
+struct X8Args {
+    const uint16_t *zeros;
+    const int8_t *q1;
+    const int8_t *q2;  // null for one word
+    const float *d;
+};
 
 // The GEMV of one segment by one workgroup (index `wg` within the segment).
 // MODE kModePlain: y = W . x.  kModeEpi: y = W . x (+ bias0) (+ residual).
@@ -241,12 +255,15 @@ enum { kFmtNf4 = 0, kFmtAffine = 1, kFmtNvfp4 = 2 };
 template <int NR, int CPL, int S, int RG, bool MULTI, int MODE, int FMT = kFmtNf4>
 __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16_t *__restrict__ x, int P,
                                           int64_t wg) {
-    __shared__ uint32_t lut[kLutDwords];
+    constexpr bool X8 = FMT == kFmtAffineX8 || FMT == kFmtAffineX8x2;
+    constexpr bool X8TWO = FMT == kFmtAffineX8x2;
+    constexpr bool ZEROS = FMT == kFmtAffine || X8;  // zero-point plane
+    __shared__ uint32_t lut[X8 ? 1 : kLutDwords];
     __shared__ float red[kMaxWavesPerGroup][RG];
     // Groups of one wave all need the whole activation vector: it is read
     // from global memory once per workgroup into LDS (raw bf16, 16 bytes per
     // lane) and every wave takes its chunks from there.
-    __shared__ uint4 xs[MULTI ? 1 : kSharedXUnits];
+    __shared__ uint4 xs[(MULTI || X8) ? 1 : kSharedXUnits];
 
     static_assert(MODE != kModeSwiglu || NR % 2 == 0, "a SwiGLU tile pairs gate and up rows");
     constexpr int LPT = MODE == kModeSwiglu ? NR / 2 : NR;  // outputs per tile
@@ -290,7 +307,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
 
     uint4 q[S + 1][NR][CPL];
     uint32_t sc[S + 1][NR][CPL];
-    uint32_t zc[FMT == kFmtAffine ? S + 1 : 1][NR][CPL];  // zero-point bits (affine only)
+    uint32_t zc[ZEROS ? S + 1 : 1][NR][CPL];  // zero-point bits (affine codes only)
     // Tiles are loaded in order.  The next tile to load starts at output
     // r_begin + LPT * (tiles loaded so far); its pointers advance by one tile
     // per load.  Rows past r_end repeat the last valid row (their results are
@@ -301,7 +318,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     // the up rows of rows 0..LPT-1 and come from the up matrix.
     const uint8_t *next_codes0 = sg.codes0 + r_begin * row_bytes;
     const uint16_t *next_scales0 = sg.scales0 + r_begin * sst;
-    const uint16_t *next_zeros0 = FMT == kFmtAffine ? sg.zeros0 + r_begin * nsb : nullptr;
+    const uint16_t *next_zeros0 = ZEROS ? sg.zeros0 + r_begin * nsb : nullptr;
     const uint8_t *next_codes1 = MODE == kModeSwiglu ? sg.codes1 + r_begin * row_bytes : nullptr;
     const uint16_t *next_scales1 = MODE == kModeSwiglu ? sg.scales1 + r_begin * nsb : nullptr;
     int64_t next_left = r_end - r_begin;  // outputs from the next tile to r_end
@@ -313,7 +330,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         const __amdgpu_buffer_rsrc_t srs0 =
             buffer_rsrc(next_scales0, real ? (uint32_t)(LPT * sst * 2) : 0u);
         __amdgpu_buffer_rsrc_t zrs0 = srs0;
-        if constexpr (FMT == kFmtAffine)
+        if constexpr (ZEROS)
             zrs0 = buffer_rsrc(next_zeros0, real ? (uint32_t)(LPT * nsb * 2) : 0u);
         __amdgpu_buffer_rsrc_t crs1 = crs0, srs1 = srs0;
         if constexpr (MODE == kModeSwiglu) {
@@ -334,14 +351,14 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                 q[buf][r][i] = make_uint4(v.x, v.y, v.z, v.w);
                 sc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(up ? srs1 : srs0, (int)(soff[i] * 2),
                                                                       rr * sst * 2, kLoadNonTemporal);
-                if constexpr (FMT == kFmtAffine)
+                if constexpr (ZEROS)
                     zc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(zrs0, (int)(soff[i] * 2), rr * nsb * 2,
                                                                           kLoadNonTemporal);
             }
         }
         next_codes0 += LPT * row_bytes;
         next_scales0 += LPT * sst;
-        if constexpr (FMT == kFmtAffine) next_zeros0 += LPT * nsb;
+        if constexpr (ZEROS) next_zeros0 += LPT * nsb;
         if constexpr (MODE == kModeSwiglu) {
             next_codes1 += LPT * row_bytes;
             next_scales1 += LPT * nsb;
@@ -359,11 +376,38 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     uint32_t xraw[16];
     u32x4_t xunit;  // this lane's 16 bytes of the shared activation copy
     const int xunits = K >> 3;
-    if (MULTI) {
-        if (CPL == 1) load_chunk_x(x, cidx[0], cvalid[0], xraw);
-    } else {
-        // Bytes past the vector's end read as zero (buffer bounds).
-        xunit = __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(x, (uint32_t)K * 2u), (int)threadIdx.x * 16, 0, 0);
+    if constexpr (!X8) {
+        if (MULTI) {
+            if (CPL == 1) load_chunk_x(x, cidx[0], cvalid[0], xraw);
+        } else {
+            // Bytes past the vector's end read as zero (buffer bounds).
+            xunit = __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(x, (uint32_t)K * 2u), (int)threadIdx.x * 16, 0, 0);
+        }
+    }
+    // int8-activation forms: each lane reads the 32 words (and the block
+    // scale) of its own chunks; a chunk past the row's end reads past the
+    // buffer bounds and gets zeros.
+    u32x4_t q1raw[X8 ? CPL : 1][2], q2raw[X8TWO ? CPL : 1][2];
+    float dch[X8 ? CPL : 1];
+    if constexpr (X8) {
+        const __amdgpu_buffer_rsrc_t r1 = buffer_rsrc(sg.xq1, (uint32_t)K);
+        const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(sg.xd, (uint32_t)K / 8u);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int off = cvalid[i] ? cidx[i] * 32 : K;
+            q1raw[i][0] = __builtin_amdgcn_raw_buffer_load_b128(r1, off, 0, 0);
+            q1raw[i][1] = __builtin_amdgcn_raw_buffer_load_b128(r1, off + 16, 0, 0);
+            dch[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, off / 8, 0, 0));
+        }
+        if constexpr (X8TWO) {
+            const __amdgpu_buffer_rsrc_t r2 = buffer_rsrc(sg.xq2, (uint32_t)K);
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int off = cvalid[i] ? cidx[i] * 32 : K;
+                q2raw[i][0] = __builtin_amdgcn_raw_buffer_load_b128(r2, off, 0, 0);
+                q2raw[i][1] = __builtin_amdgcn_raw_buffer_load_b128(r2, off + 16, 0, 0);
+            }
+        }
     }
 #pragma unroll
     for (int s = 0; s <= S; ++s) load_tile(s);
@@ -371,11 +415,13 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         fill_lut_from(lut, kAffinePairTable);
     else if constexpr (FMT == kFmtNvfp4)
         fill_lut_from(lut, kE2m1PairTable);
-    else
+    else if constexpr (!X8)
         fill_lut(lut);
-    half2_t xh[CPL][16];
-    float down;
-    if constexpr (MULTI) {
+    half2_t xh[X8 ? 1 : CPL][16];
+    float down = 1.0f;
+    if constexpr (X8) {
+        // (no table and no shared activation copy to wait for)
+    } else if constexpr (MULTI) {
         down = convert_x<CPL, true>([&](int i, uint32_t(&r)[16]) { load_chunk_x(x, cidx[i], cvalid[i], r); },
                                     xraw, xh);
         __syncthreads();
@@ -384,6 +430,45 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         __syncthreads();
         down = convert_x<CPL, false>(
             [&](int i, uint32_t(&r)[16]) { load_chunk_x_lds(xs, cidx[i], cvalid[i], r); }, xraw, xh);
+    }
+
+    // int8-activation forms: the words regrouped to match the code nibbles
+    // (code dword d holds weights 8d .. 8d+7, even ones in the low nibbles):
+    // E[d] = words 8d, 8d+2, 8d+4, 8d+6 and O[d] = words 8d+1, ..., 8d+7;
+    // the chunk's word sums (for the zero point); d / 2048 per chunk (the
+    // integer dot below carries a factor 16 * 128).
+    uint32_t E1[X8 ? CPL : 1][4], O1[X8 ? CPL : 1][4], E2[X8TWO ? CPL : 1][4], O2[X8TWO ? CPL : 1][4];
+    int qs1[X8 ? CPL : 1], qs2[X8TWO ? CPL : 1];
+    float dsc[X8 ? CPL : 1];
+    if constexpr (X8) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const uint32_t v[8] = {q1raw[i][0].x, q1raw[i][0].y, q1raw[i][0].z, q1raw[i][0].w,
+                                   q1raw[i][1].x, q1raw[i][1].y, q1raw[i][1].z, q1raw[i][1].w};
+            int t = 0;
+#pragma unroll
+            for (int dd = 0; dd < 4; ++dd) {
+                E1[i][dd] = __builtin_amdgcn_perm(v[2 * dd + 1], v[2 * dd], 0x06040200u);
+                O1[i][dd] = __builtin_amdgcn_perm(v[2 * dd + 1], v[2 * dd], 0x07050301u);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) t = __builtin_amdgcn_sdot4((int)v[j], 0x01010101, t, false);
+            qs1[i] = t;
+            dsc[i] = dch[i] * 0x1p-11f;
+            if constexpr (X8TWO) {
+                const uint32_t u[8] = {q2raw[i][0].x, q2raw[i][0].y, q2raw[i][0].z, q2raw[i][0].w,
+                                       q2raw[i][1].x, q2raw[i][1].y, q2raw[i][1].z, q2raw[i][1].w};
+                int t2 = 0;
+#pragma unroll
+                for (int dd = 0; dd < 4; ++dd) {
+                    E2[i][dd] = __builtin_amdgcn_perm(u[2 * dd + 1], u[2 * dd], 0x06040200u);
+                    O2[i][dd] = __builtin_amdgcn_perm(u[2 * dd + 1], u[2 * dd], 0x07050301u);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) t2 = __builtin_amdgcn_sdot4((int)u[j], 0x01010101, t2, false);
+                qs2[i] = t2;
+            }
+        }
     }
 
     const uint32_t laneoff = (uint32_t)lane << 2;
@@ -420,7 +505,30 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                 float a = 0.0f;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
-                    if constexpr (FMT == kFmtNvfp4) {
+                    if constexpr (X8) {
+                        // Nibble c of a code byte, XOR 8, placed in a byte's
+                        // high half reads as the signed byte 16 (c - 8): even
+                        // weights by a shift, odd ones in place.
+                        const uint32_t w[4] = {q[buf][r][i].x, q[buf][r][i].y, q[buf][r][i].z, q[buf][r][i].w};
+                        int t1 = 0, t2 = 0;
+#pragma unroll
+                        for (int dd = 0; dd < 4; ++dd) {
+                            const uint32_t f = w[dd] ^ 0x88888888u;
+                            const int ev = (int)((f << 4) & 0xF0F0F0F0u), od = (int)(f & 0xF0F0F0F0u);
+                            t1 = __builtin_amdgcn_sdot4(ev, (int)E1[i][dd], t1, false);
+                            t1 = __builtin_amdgcn_sdot4(od, (int)O1[i][dd], t1, false);
+                            if constexpr (X8TWO) {
+                                t2 = __builtin_amdgcn_sdot4(ev, (int)E2[i][dd], t2, false);
+                                t2 = __builtin_amdgcn_sdot4(od, (int)O2[i][dd], t2, false);
+                            }
+                        }
+                        // 16 sum (c - z) q = 16 sum (c - 8) q - 16 (z - 8) sum q:
+                        // exact integers (|.| < 2^20; times 128 < 2^27).
+                        const int zi = (int)f16_bits_to_f32(zc[buf][r][i]) - 8;
+                        int tot = 128 * (t1 - 16 * zi * qs1[i]);
+                        if constexpr (X8TWO) tot += t2 - 16 * zi * qs2[i];
+                        a = fmaf((float)tot, f16_bits_to_f32(sc[buf][r][i]) * dsc[i], a);
+                    } else if constexpr (FMT == kFmtNvfp4) {
                         float p0, p1;
                         chunk_dot_halves(lut, q[buf][r][i], xh[i], laneoff, p0, p1);
                         a = fmaf(p0, e4m3_to_f32(sc[buf][r][i]), a);
@@ -569,6 +677,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
     gemv_body<NR, CPL, S, RG, MULTI, kModePlain, kFmtNvfp4>(sg, K, x, P, (int64_t)blockIdx.x);
 }
 
+// The affine format's GEMV on int8 activations (one or two words).
+template <int NR, int CPL, int S, int RG, bool MULTI, int FMT>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
+                          amdgpu_waves_per_eu(gemv_min_waves(CPL), 8))) void gemv_affine_x8_kernel(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    const int8_t *__restrict__ q1, const int8_t *__restrict__ q2, const float *__restrict__ d, int64_t M, int K,
+    float *__restrict__ y, int P, int64_t rows_q, int rows_rem) {
+    GemvSeg sg{};
+    sg.codes0 = codes;
+    sg.scales0 = scales;
+    sg.zeros0 = zeros;
+    sg.xq1 = q1;
+    sg.xq2 = q2;
+    sg.xd = d;
+    sg.y = y;
+    sg.rows = M;
+    sg.rows_q = rows_q;
+    sg.rows_rem = rows_rem;
+    gemv_body<NR, CPL, S, RG, MULTI, kModePlain, FMT>(sg, K, nullptr, P, (int64_t)blockIdx.x);
+}
+
 // Several segments in one launch: workgroup b belongs to the last segment
 // whose first workgroup is <= b.
 template <int NR, int CPL, int S, int RG, bool MULTI, int MODE>
@@ -624,6 +753,14 @@ hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, const vo
         const uint16_t *zeros = static_cast<const uint16_t *>(extra);
         void *args[] = {&codes, &scales, &zeros, &M, &K, &x, &y, &P, &rows_q, &rows_rem};
         return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_affine_kernel<NR, CPL, S, RG, MULTI>),
+                               dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
+    } else if constexpr (FMT == kFmtAffineX8 || FMT == kFmtAffineX8x2) {
+        const X8Args *xa = static_cast<const X8Args *>(extra);
+        const uint16_t *zeros = xa->zeros;
+        const int8_t *q1 = xa->q1, *q2 = xa->q2;
+        const float *d = xa->d;
+        void *args[] = {&codes, &scales, &zeros, &q1, &q2, &d, &M, &K, &y, &P, &rows_q, &rows_rem};
+        return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_affine_x8_kernel<NR, CPL, S, RG, MULTI, FMT>),
                                dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
     } else if constexpr (FMT == kFmtNvfp4) {
         const float *tscale = static_cast<const float *>(extra);
@@ -811,6 +948,14 @@ hipError_t launch_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, 
 hipError_t launch_gemv_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
                               int64_t K, const uint16_t *x, float *y, hipStream_t stream) {
     return launch_gemv_fmt<kFmtAffine>(codes, scales, zeros, M, K, x, y, stream);
+}
+
+hipError_t launch_gemv_affine_x8(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
+                                 int64_t K, const int8_t *q1, const int8_t *q2, const float *d, float *y,
+                                 hipStream_t stream) {
+    const X8Args xa{zeros, q1, q2, d};
+    if (q2) return launch_gemv_fmt<kFmtAffineX8x2>(codes, scales, &xa, M, K, nullptr, y, stream);
+    return launch_gemv_fmt<kFmtAffineX8>(codes, scales, &xa, M, K, nullptr, y, stream);
 }
 
 hipError_t launch_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscale, int64_t M,

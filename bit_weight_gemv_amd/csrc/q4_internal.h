@@ -18,6 +18,14 @@ hipError_t launch_pack_affine(const float *W, int64_t M, int64_t K, uint8_t *cod
 hipError_t launch_gemv_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
                               int64_t K, const uint16_t *x, float *y, hipStream_t stream);
 
+// int8 activations (one or two words, f32 scale per 32-block) and the affine
+// format's GEMV on them (q2 null: one word).
+hipError_t launch_quantize_x8(const uint16_t *x, int64_t K, int words, int8_t *q1, int8_t *q2, float *d,
+                              hipStream_t stream);
+hipError_t launch_gemv_affine_x8(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
+                                 int64_t K, const int8_t *q1, const int8_t *q2, const float *d, float *y,
+                                 hipStream_t stream);
+
 // The NVFP4-style format (E2M1 * E4M3 per 16 * f32 tensor scale).
 hipError_t launch_pack_nvfp4(const float *W, int64_t M, int64_t K, uint8_t *codes, uint8_t *scales,
                              float *tscale, int32_t *status, hipStream_t stream);

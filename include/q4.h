@@ -224,6 +224,39 @@ int q4_gemv_affine(const uint8_t *codes, const uint16_t *scales,
                    const uint16_t *x, float *y, void *stream);
 
 /*
+ * int8 activations for the integer-code (affine) format (deep-fold "Decode
+ * V2" page, the lane's knobs: a projection's activation may be one int8
+ * word, as llama.cpp does, or two int8 words of about 14 bits, the page's
+ * default).  Per block of 32 activations along K:
+ *   d  = the f32 rounding of the fp64 quotient max|x| / 127;
+ *   q1 = the integer nearest to x / d, ties to even, within +-127;
+ *   q2 = (two words) the integer nearest to 128 (x - q1 d) / d, same rule;
+ * the value carried is xq = d (q1 + q2 / 128); |x - xq| <= d / 2 (one word)
+ * or d / 256 (two words).  Decisions are exact comparisons: bit-exact.
+ */
+
+/*
+ * q4_quantize_x8 -- x bf16 bits [K] (16-byte aligned) -> q1 int8 [K] and,
+ * for words == 2, q2 int8 [K] (16-byte aligned; q2 may be NULL for one
+ * word), d fp32 [K/32] (4-byte aligned).  K as the products (a positive
+ * multiple of 64).  No two ranges may overlap.
+ */
+int q4_quantize_x8(const uint16_t *x, int64_t K, int words, int8_t *q1,
+                   int8_t *q2, float *d, void *stream);
+
+/*
+ * q4_gemv_affine_x8 -- the affine format's GEMV on int8 activations:
+ * y[m] = sum_k (code - z) * s * xq[k], with xq from q4_quantize_x8 (q2 NULL:
+ * one word).  The dot products are exact integer sums (v_dot4_i32_i8), then
+ * one fp32 scaling per 32 weights: within 1e-3 * sum_k |What xq| + 1e-5 of
+ * the exact value (the bound restated on xq).  Errors as q4_gemv_affine.
+ */
+int q4_gemv_affine_x8(const uint8_t *codes, const uint16_t *scales,
+                      const uint16_t *zeros, int64_t M, int64_t K,
+                      const int8_t *q1, const int8_t *q2, const float *d,
+                      float *y, void *stream);
+
+/*
  * NVFP4-style format (gizai tensor/lazy page, fp4Blocks: E2M1 codes, two to a
  * byte with the first in the low half; one E4M3 scale per 16 values along K;
  * an f32 tensor scale s = max|W| / (6 * 448); a weight is its E2M1 value

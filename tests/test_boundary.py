@@ -34,6 +34,7 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused",
               "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_pack_nvfp4", "q4_gemv_nvfp4",
+              "q4_quantize_x8", "q4_gemv_affine_x8",
               "q4_codebook", "q4_codes_bytes",
               "q4_scales_bytes", "q4_status_string"):
         assert n in names
@@ -280,6 +281,24 @@ def test_nvfp4_errors(q4):
     assert L.q4_gemv_nvfp4(A, B + 1, C, 16, 128, D, E, None) == q4.Q4_ERR_ALIGN
     assert L.q4_gemv_nvfp4(A, B, C, 16, 128, D, B + 64, None) == q4.Q4_ERR_OVERLAP  # y over scales
     assert L.q4_gemv_nvfp4(A, B, C, 16, 128, D, C - 32, None) == q4.Q4_ERR_OVERLAP  # y over tscale
+    # every call above fails a host check and launches nothing
+
+
+def test_x8_errors(q4):
+    L = q4.lib()
+    # x A (K=128: 256 B), q1 B (128 B), q2 C, d D (16 B)
+    assert L.q4_quantize_x8(A, 100, 2, B, C, D, None) == q4.Q4_ERR_SHAPE
+    assert L.q4_quantize_x8(A, 128, 3, B, C, D, None) == q4.Q4_ERR_SHAPE
+    assert L.q4_quantize_x8(A, 128, 2, B, 0, D, None) == q4.Q4_ERR_NULL
+    assert L.q4_quantize_x8(A, 128, 2, B + 8, C, D, None) == q4.Q4_ERR_ALIGN
+    assert L.q4_quantize_x8(A, 128, 2, B, B + 64, D, None) == q4.Q4_ERR_OVERLAP
+    assert L.q4_quantize_x8(A, 128, 1, B, 0, A + 128, None) == q4.Q4_ERR_OVERLAP   # d inside x
+    # gemv: codes A, scales B, zeros C, q1 D, q2 E, d F, y G
+    assert L.q4_gemv_affine_x8(A, B, C, 16, 100, D, E, F, G, None) == q4.Q4_ERR_SHAPE
+    assert L.q4_gemv_affine_x8(A, B, C, 0, 128, 0, 0, 0, 0, None) == q4.Q4_OK
+    assert L.q4_gemv_affine_x8(A, B, C, 16, 128, 0, E, F, G, None) == q4.Q4_ERR_NULL
+    assert L.q4_gemv_affine_x8(A, B, C, 16, 128, D, E + 4, F, G, None) == q4.Q4_ERR_ALIGN
+    assert L.q4_gemv_affine_x8(A, B, C, 16, 128, D, E, F, D + 64, None) == q4.Q4_ERR_OVERLAP  # y over q1
     # every call above fails a host check and launches nothing
 
 

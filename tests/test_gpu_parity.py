@@ -966,3 +966,85 @@ def test_nvfp4_full_size_gateup(env):
     torch.cuda.synchronize()
     y_ref, S = oracle.gemv_nvfp4(c_ref, s_ref, ts_ref, M, K, x, threads=threads)
     _check(y.cpu().numpy(), y_ref, S, "nvfp4 gemv gate/up 22016x2048")
+
+
+# ---------------------------------------------------------------------------
+# int8 activations: q4_quantize_x8 (bit-exact) and q4_gemv_affine_x8
+# ---------------------------------------------------------------------------
+
+def _x8_dev(env, q1, q2, d):
+    torch, q4, dev = env
+    t1 = cases.to_dev(q1, torch, dev)
+    t2 = cases.to_dev(q2, torch, dev) if q2 is not None else None
+    return t1, t2, cases.to_dev(d, torch, dev)
+
+
+@pytest.mark.parametrize("words", [1, 2])
+@pytest.mark.parametrize("K,recipe", [(64, "normal"), (2048, "unit_rms"), (11008, "swiglu"), (131072, "normal")])
+def test_quantize_x8_bit_exact(env, K, recipe, words):
+    torch, q4, dev = env
+    x = wl.activation(K, 9500 + K, recipe)
+    if K >= 128:
+        x[64:96] = 0                                   # a zero block
+        x[96:128] = wl.bf16_rne_bits(np.full(32, 1e-30))  # a block of tiny values
+        x[32:38] = wl.bf16_rne_bits(np.array([127.0, 2.5, 3.5, -2.5, 0.5, 0.50390625]))
+        x[38:64] = 0
+    q1r, q2r, dr = oracle.quantize_x8(x, words)
+    q1, q2, d = q4.q4_quantize_x8(_x_dev(env, x), words)
+    torch.cuda.synchronize()
+    assert np.array_equal(d.cpu().numpy().view(np.uint32), dr.view(np.uint32))
+    assert np.array_equal(q1.cpu().numpy(), q1r)
+    if words == 2:
+        assert np.array_equal(q2.cpu().numpy(), q2r)
+
+
+X8_GEMV_SHAPES = [(1, 64), (7, 128), (1000, 1024), (4097, 2048), (40001, 64), (300, 2112), (65, 4096),
+                  (129, 4160), (2048, 11008), (4101, 16448), (3, 32768), (2, 131072)]
+
+
+@pytest.mark.parametrize("words", [1, 2])
+@pytest.mark.parametrize("M,K", X8_GEMV_SHAPES)
+def test_affine_x8_gemv_parity(env, M, K, words):
+    torch, q4, dev = env
+    seed = 9600 + M + K
+    W = wl.weights(M, K, seed, std=0.5) + np.float32(0.05)
+    x = wl.activation(K, seed, "normal")
+    codes, scales, zeros, st = oracle.pack_affine(W)
+    assert st == 0
+    q1, q2, d = oracle.quantize_x8(x, words)
+    y_ref, S = oracle.gemv_affine_x8(codes, scales, zeros, M, K, q1, q2, d)
+    c, s, z = _affine_upload(env, codes, scales, zeros)
+    t1, t2, td = _x8_dev(env, q1, q2, d)
+    y = q4.q4_gemv_affine_x8(c, s, z, t1, t2, td)
+    torch.cuda.synchronize()
+    _check(y.cpu().numpy(), y_ref, S, f"affine x8 ({words} word) gemv M={M} K={K}")
+
+
+def test_affine_x8_chain_full_size_down(env):
+    """The down shape (2048 x 11008, SwiGLU-like x): GPU pack, GPU quantise
+    and the GEMV against the oracle's pack, quantise and GEMV; the bf16
+    product and the two-word product stay within the restated bound of
+    each other (|x - xq| <= d / 256)."""
+    torch, q4, dev = env
+    c_cfg = wl.CONFIGS["down"]
+    M, K = c_cfg["M"], c_cfg["K"]
+    W = wl.weights(M, K, c_cfg["seed"])
+    x = wl.activation(K, c_cfg["seed"], c_cfg["x"])
+    codes, scales, zeros, st = q4.q4_pack_affine(cases.to_dev(W, torch, dev))
+    c_ref, s_ref, z_ref, _ = oracle.pack_affine(W, threads=min(16, os.cpu_count() or 1))
+    for words in (2, 1):
+        q1, q2, d = q4.q4_quantize_x8(_x_dev(env, x), words)
+        y = q4.q4_gemv_affine_x8(codes, scales, zeros, q1, q2, d)
+        torch.cuda.synchronize()
+        r1, r2, rd = oracle.quantize_x8(x, words)
+        y_ref, S = oracle.gemv_affine_x8(c_ref, s_ref, z_ref, M, K, r1, r2, rd, threads=min(16, os.cpu_count() or 1))
+        _check(y.cpu().numpy(), y_ref, S, f"affine x8 chain down ({words} word)")
+    # restated against the bf16 product: |y(xq) - y(x)| <= sum |What| |x - xq|
+    yb, _ = oracle.gemv_affine(c_ref, s_ref, z_ref, M, K, x)
+    r1, r2, rd = oracle.quantize_x8(x, 2)
+    xq = oracle.dequantize_x8(r1, r2, rd)
+    xv = wl.bf16_bits_to_f32(x).astype(np.float64)
+    What = oracle.dequant_affine(c_ref, s_ref, z_ref, M, K)
+    bound = np.abs(What) @ np.abs(xq - xv)
+    y2, _ = oracle.gemv_affine_x8(c_ref, s_ref, z_ref, M, K, r1, r2, rd)
+    assert np.all(np.abs(y2 - yb) <= bound * (1 + 1e-9) + 1e-12)
