@@ -1048,3 +1048,50 @@ def test_affine_x8_chain_full_size_down(env):
     bound = np.abs(What) @ np.abs(xq - xv)
     y2, _ = oracle.gemv_affine_x8(c_ref, s_ref, z_ref, M, K, r1, r2, rd)
     assert np.all(np.abs(y2 - yb) <= bound * (1 + 1e-9) + 1e-12)
+
+
+def test_graph_capture_other_entry_points(env):
+    """Gather, affine, NVFP4-style, int8 quantisation and int8 GEMV captured
+    in one graph; every replay (with eager work in between) equals eager."""
+    torch, q4, dev = env
+    M, K = 3000, 2048
+    W = wl.weights(M, K, 7300)
+    Wd = cases.to_dev(W, torch, dev)
+    xd = _x_dev(env, wl.activation(K, 7300, "unit_rms"))
+    codes, scales, _ = oracle.pack(W)
+    c, s = _upload_packed(env, codes, scales)
+    ac, asc, az, _ = q4.q4_pack_affine(Wd)
+    nc, ns, nt, _ = q4.q4_pack_nvfp4(Wd)
+    torch.cuda.synchronize()
+    ids = torch.tensor([5, 0, M - 1, 17], dtype=torch.int32, device=dev)
+
+    def run(outs=None):
+        o = outs or {}
+        g, st = q4.q4_gather_rows(c, s, ids, torch.bfloat16, o.get("g"), o.get("gs"))
+        ya = q4.q4_gemv_affine(ac, asc, az, xd, o.get("ya"))
+        yn = q4.q4_gemv_nvfp4(nc, ns, nt, xd, o.get("yn"))
+        q1, q2, d = q4.q4_quantize_x8(xd, 2, o.get("q1"), o.get("q2"), o.get("d"))
+        y8 = q4.q4_gemv_affine_x8(ac, asc, az, q1, q2, d, o.get("y8"))
+        return {"g": g, "gs": st, "ya": ya, "yn": yn, "q1": q1, "q2": q2, "d": d, "y8": y8}
+
+    eager = {k: v.clone() for k, v in run().items()}
+    torch.cuda.synchronize()
+    outs = {k: torch.empty_like(v) for k, v in eager.items()}
+    gr = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr, stream=stream):
+            run(outs)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in outs.values():
+            v.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        for k in eager:
+            assert torch.equal(outs[k].view(torch.uint8), eager[k].view(torch.uint8)), f"replay {rep}: {k} differs"
+        run()  # eager work between replays
+        torch.cuda.synchronize()
