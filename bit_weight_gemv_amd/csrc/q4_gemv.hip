@@ -46,6 +46,11 @@ constexpr int kMaxWavesPerGroup = 8;
 // Row-per-wave variants cover rows of up to 128 chunks (K <= 4096): the LDS
 // copy of the activations is at most 8 KB (512 lanes x 16 bytes).
 constexpr int kSharedXUnits = 512;
+// Rows of the first tile whose loads are issued before the table fill:
+// variants that walk a long ring of row tiles issue their first tiles whole
+// (their start-up is amortised, and the early tiles keep the HBM busy);
+// short row ranges issue two rows, so the set-up behind them is not held up.
+constexpr int pre_rows(int nr, int s, bool multi) { return (!multi && s >= 1) ? nr : (nr < 2 ? nr : 2); }
 
 // Dot of one 16-byte chunk (32 weights) with the lane's fp16 activations.
 // All 16 lookups are issued before the first product so their LDS latencies
@@ -322,7 +327,9 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     const uint8_t *next_codes1 = MODE == kModeSwiglu ? sg.codes1 + r_begin * row_bytes : nullptr;
     const uint16_t *next_scales1 = MODE == kModeSwiglu ? sg.scales1 + r_begin * nsb : nullptr;
     int64_t next_left = r_end - r_begin;  // outputs from the next tile to r_end
-    auto load_tile = [&](int buf) {
+    // Rows [r0, r1) of the next tile into ring buffer `buf`; advance() then
+    // moves the pointers to the tile after it.
+    auto load_rows = [&](int buf, int r0, int r1) {
         const bool real = next_left > 0;
         const int nvalid = next_left < LPT ? (int)next_left : LPT;
         const __amdgpu_buffer_rsrc_t crs0 =
@@ -338,7 +345,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
             srs1 = buffer_rsrc(next_scales1, real ? (uint32_t)(LPT * nsb * 2) : 0u);
         }
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
+        for (int r = r0; r < r1; ++r) {
             const int lr = r % LPT;
             const int rr = lr < nvalid ? lr : (nvalid > 0 ? nvalid - 1 : 0);
             const bool up = MODE == kModeSwiglu && r >= LPT;
@@ -356,6 +363,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                                                                           kLoadNonTemporal);
             }
         }
+    };
+    auto advance = [&]() {
         next_codes0 += LPT * row_bytes;
         next_scales0 += LPT * sst;
         if constexpr (ZEROS) next_zeros0 += LPT * nsb;
@@ -365,11 +374,18 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         }
         next_left -= LPT;
     };
+    auto load_tile = [&](int buf) {
+        load_rows(buf, 0, NR);
+        advance();
+    };
 
-    // Set-up order: activation loads, then the first weight tiles, then the
-    // table fill (no memory dependence, so it overlaps the load latency),
-    // then the activation conversion (which waits only for the activation
-    // loads: vector loads complete in order).
+    // Set-up order: activation loads, then the first PRE rows of the first
+    // tile, then the table fill (no memory dependence, so it overlaps the
+    // load latency), then the activation copy or conversion (which waits
+    // only for the activation loads: vector loads complete in order) and the
+    // barrier, and only then the rest of the ring.  A wave that issued its
+    // whole ring first would stall in the memory pipeline until the HBM
+    // returned data, and the set-up behind the loads would wait with it.
     // The first tiles load unconditionally: an empty row range loads through
     // zero-record resources (no memory access), and no branch makes the
     // compiler's wait analysis assume the tile loads might be missing.
@@ -409,8 +425,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
             }
         }
     }
-#pragma unroll
-    for (int s = 0; s <= S; ++s) load_tile(s);
+    constexpr int PRE = pre_rows(NR, S, MULTI);
+    load_rows(0, 0, PRE);
     if constexpr (FMT == kFmtAffine)
         fill_lut_from(lut, kAffinePairTable);
     else if constexpr (FMT == kFmtNvfp4)
@@ -428,9 +444,14 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     } else {
         if ((int)threadIdx.x < xunits) xs[threadIdx.x] = make_uint4(xunit.x, xunit.y, xunit.z, xunit.w);
         __syncthreads();
+    }
+    load_rows(0, PRE, NR);
+    advance();
+#pragma unroll
+    for (int s = 1; s <= S; ++s) load_tile(s);
+    if constexpr (!X8 && !MULTI)
         down = convert_x<CPL, false>(
             [&](int i, uint32_t(&r)[16]) { load_chunk_x_lds(xs, cidx[i], cvalid[i], r); }, xraw, xh);
-    }
 
     // int8-activation forms: the words regrouped to match the code nibbles
     // (code dword d holds weights 8d .. 8d+7, even ones in the low nibbles):
