@@ -64,7 +64,7 @@ constexpr int kCStageUnits = 16 * kCPitch;
 // is token p / 32, bytes 16 (p % 32) of the slice.  Tokens past N and blocks
 // past the row's end read as zero (offsets past the buffer).
 template <int NT>
-__device__ __forceinline__ void load_x_linear(__amdgpu_buffer_rsrc_t xrs, int K, int nsb, int slice,
+__device__ __forceinline__ void load_x_linear(__amdgpu_buffer_rsrc_t xrs, int K, int N, int nsb, int slice,
                                               u32x4_t (&lin)[NT * 8]) {
     const int lane = threadIdx.x & 63;
     const int within = lane & 31;
@@ -172,11 +172,22 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
     };
     __shared__ Smem sm;
     uint32_t *lut = sm.lut;
-    // Partial tiles: [buffer][wave][lane][register], a lane's registers
-    // contiguous (written with 16-byte stores).
+    // Partial tiles of the cross-wave sum.  Activations kept in registers
+    // (XFIXED): each wave writes the partial tiles of up to kGroupTiles
+    // consecutive tiles into its own staging area, [tile][lane][register],
+    // and the workgroup sums them once per group (one barrier per group, not
+    // per tile, so the waves run through a group's tiles independently).
+    // Long rows restage activations per tile in that area, so they use a
+    // double-buffered [buffer][wave][lane][register] sum per tile instead.
+    constexpr int kGroupTiles = XFIXED ? (NT == 1 ? 8 : 4) : 1;
+    typedef float WavePart[kGroupTiles][64][NT * 4];
+    static_assert(sizeof(WavePart) <= kXStageUnits * sizeof(uint4), "partial tiles must fit a wave's staging area");
     typedef float RedBuf[2][kGemmMaxWaves][64][NT * 4];
     static_assert(sizeof(RedBuf) <= sizeof(sm.xstage), "reduction buffer must fit the staging area");
     RedBuf &red = *reinterpret_cast<RedBuf *>(sm.xstage);
+    auto wave_part = [&](int w) -> WavePart & {
+        return *reinterpret_cast<WavePart *>(sm.xstage + w * kXStageUnits);
+    };
 
     // Always kGemmMaxWaves waves; waves past the last K slice load nothing
     // (zero-record resources, zero activations) and add exact zeros.
@@ -241,10 +252,13 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
 
     // Set-up: this wave's activations (when it keeps one slice for the whole
     // run), the first units, the table fill, then the activation regrouping
-    // and conversion (which waits only for the activation loads).
+    // and conversion (which waits only for the activation loads: vector
+    // loads complete in order) and the barrier that publishes the table.
+    // (Measured on the 11008 x 2048 shape: issuing weight units ahead of the
+    // activations, or the barrier before the conversion, is slower.)
     u32x4_t lin[NT * 8];
     u32x4_t raw[NT][kSliceBlocks][2];
-    if (XFIXED) load_x_linear<NT>(xrs, K, nsb, wave, lin);
+    if (XFIXED) load_x_linear<NT>(xrs, K, N, nsb, wave, lin);
 #pragma unroll
     for (int s = 0; s <= S; ++s) load_unit(s);
     fill_lut(lut);
@@ -273,6 +287,24 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
     const int64_t out_base = (int64_t)out_n * M + out_mm;
     int cu_si = 0;               // slice index of the unit being consumed
     int64_t cu_m0 = t_begin * kTileRows;  // first row of its tile
+    int gslot = 0;               // XFIXED: tile slot within the current group
+    int tiles_done = 0;
+
+    // XFIXED: the sums of the group's `nslot` tiles, whose first row is m0.
+    // Thread (n, row) adds the eight waves' partials of its output in each
+    // tile; every wave has written its partials before the barrier.
+    auto sum_group = [&](int nslot, int64_t m0) {
+        __syncthreads();
+        if (out_n < N) {
+            for (int t = 0; t < nslot; ++t) {
+                float sum = 0.0f;
+#pragma unroll
+                for (int w = 0; w < nw; ++w) sum += wave_part(w)[t][out_l][out_v];
+                const int64_t m = m0 + (int64_t)t * kTileRows + out_mm;
+                if (m < M) Y[(int64_t)out_n * M + m] = sum;
+            }
+        }
+    };
 
     auto consume = [&](int buf) {
         if (!XFIXED) {
@@ -280,7 +312,7 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
             // staging area's share of this wave; the reduction buffer shares
             // those bytes, so the workgroup first leaves the previous tile's
             // sum.
-            load_x_linear<NT>(xrs, K, nsb, wave + nw * cu_si, lin);
+            load_x_linear<NT>(xrs, K, N, nsb, wave + nw * cu_si, lin);
             __syncthreads();
             regroup_x<NT>(xs, lin, raw);
             convert_x_slice<NT>(raw, xa, inv);
@@ -339,7 +371,27 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(part[t][r], inv[t][r], acc[t][r]);
 
-        if (XFIXED || ++cu_si == spw) {
+        if (XFIXED) {
+            // Tile complete for this wave: its partial goes to the group's
+            // next slot; the group is summed when full or at the last tile.
+            float4_t *mine = reinterpret_cast<float4_t *>(&wave_part(wave)[gslot][lane][0]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                mine[t] = float4_t{acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
+            }
+            ++gslot;
+            ++tiles_done;
+            if (gslot == kGroupTiles || tiles_done == ntiles) {
+                sum_group(gslot, cu_m0 - (int64_t)(gslot - 1) * kTileRows);
+                // The slots are rewritten by the next group only after
+                // every thread has read them.
+                if (tiles_done < ntiles) __syncthreads();
+                gslot = 0;
+            }
+            cu_m0 += kTileRows;
+        } else if (++cu_si == spw) {
             cu_si = 0;
             // Tile complete for this wave: sum the waves' partial tiles.
             float4_t *mine = reinterpret_cast<float4_t *>(&red[rbuf][wave][lane][0]);
@@ -372,6 +424,12 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
 
 hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                               const uint16_t *X, int64_t N, float *Y, hipStream_t stream) {
+    // A chunk of one token is the GEMV (measured on the 11008 x 2048 prefill
+    // shape: 5.3 us against 7.1 us for the matrix-core kernel, whose set-up
+    // and 16-token tiles do not pay for one token).  A row-per-wave kernel
+    // sharing each lookup among 2..4 tokens measured slower than the
+    // matrix-core kernel (7.5 and 11.1 us at N = 2 and 4).
+    if (N == 1) return launch_gemv(codes, scales, M, K, X, Y, stream);
     static int cus[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;

@@ -358,10 +358,14 @@ def test_full_size_pack_and_gemv(env, name):
 # (M, K, N): ragged row tiles (16 rows), K slices of 256 (partial last
 # slices; up to 8 slices the activations stay in registers, beyond that each
 # wave reloads its slices per tile), one or two 16-token halves, and enough
-# tiles per workgroup (20000 rows) that the prefetch ring wraps.
+# tiles per workgroup (20000 rows) that the prefetch ring wraps; 40000 rows
+# give each workgroup several groups of tiles between the cross-wave sums.
 GEMM_SHAPES = [(1, 64, 1), (40, 128, 2), (100, 512, 3), (64, 2048, 4), (97, 1024, 8),
                (33, 2048, 16), (200, 2048, 17), (65, 4096, 31), (160, 2048, 32), (70, 11008, 32),
-               (300, 1600, 20), (50, 2112, 32), (20000, 256, 9), (20000, 192, 32)]
+               (300, 1600, 20), (50, 2112, 32), (20000, 256, 9), (20000, 192, 32),
+               (40000, 64, 5), (40000, 128, 24),
+               # one token takes the GEMV kernels (short and long rows)
+               (7, 2048, 1), (3000, 2112, 1), (600, 11008, 1)]
 
 
 @pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
