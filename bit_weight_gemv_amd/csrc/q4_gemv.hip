@@ -805,12 +805,38 @@ int64_t gemv_grid(int64_t tiles, int G) {
     return grid < 1 ? 1 : grid;
 }
 
+// Rows of one wave (at most 64 chunks): the most tiles one pass of the
+// one-tile-per-wave form covers (two workgroups of 16 waves per CU).
+int64_t one_tile_limit() { return 2LL * 16 * cu_count(); }
+
+// Workgroup shape of the one-tile-per-wave form for `tiles` row tiles: one
+// wave per tile, in one workgroup per CU while that takes at most 12 waves,
+// else two; at least enough threads for the workgroup's copy of the
+// activations (one 16-byte unit per thread).  Measured on 11008 x 2048 and
+// 22016 x 2048: 4.7 and 7.0 us against 5.2 and 7.2 us for 8-wave workgroups
+// at two per CU, which leave a third of the waves two tiles in sequence
+// (11008 rows: 344 workgroups, two on some CUs and one on others).
+struct OneTileShape {
+    int G;          // waves per workgroup
+    int64_t cap;    // most workgroups
+};
+OneTileShape one_tile_shape(int64_t tiles, int K) {
+    const int64_t cus = cu_count();
+    const int64_t per_cu = tiles <= 12 * cus ? 1 : 2;
+    int64_t G = (tiles + per_cu * cus - 1) / (per_cu * cus);
+    const int64_t gmin = (K / 8 + 63) / 64;
+    if (G < gmin) G = gmin;
+    if (G < 1) G = 1;
+    if (G > 16) G = 16;
+    return {(int)G, per_cu * cus};
+}
+
 // Workgroups per segment (in proportion to its tiles of `lpt` outputs, G
-// groups per workgroup, one pass over two workgroups per CU) and each
-// segment's row split.  Returns the grid; *tpg gets the largest number of
-// tiles a lane group walks.
-int64_t plan_segments(GemvSegs &segs, int lpt, int G, int64_t *tpg) {
-    const int64_t cap = 2LL * cu_count();
+// groups per workgroup, one pass over at most `cap` workgroups, by default
+// two per CU) and each segment's row split.  Returns the grid; *tpg gets the
+// largest number of tiles a lane group walks.
+int64_t plan_segments(GemvSegs &segs, int lpt, int G, int64_t *tpg, int64_t cap = 0) {
+    if (cap <= 0) cap = 2LL * cu_count();
     int64_t wg[kMaxSegs], total = 0;
     for (int i = 0; i < segs.n; ++i) {
         const int64_t tiles = (segs.s[i].rows + lpt - 1) / lpt;
@@ -863,8 +889,15 @@ hipError_t launch_fused_mode(GemvSegs segs, int K, const uint16_t *x, hipStream_
     constexpr int half = MODE == kModeSwiglu ? 2 : 1;  // rows per output
     int64_t tpg = 0;
     if (C <= 64) {
-        const int64_t grid = plan_segments(segs, 4 / half, 8, &tpg);
-        if (tpg <= 2) return launch_fused_variant<4, 1, 0, 4, false, MODE>(segs, K, x, 64, 8, grid, stream);
+        const int lpt = 4 / half;
+        int64_t tiles = 0;
+        for (int i = 0; i < segs.n; ++i) tiles += (segs.s[i].rows + lpt - 1) / lpt;
+        if (tiles <= one_tile_limit()) {
+            const OneTileShape sh = one_tile_shape(tiles, K);
+            const int64_t grid = plan_segments(segs, lpt, sh.G, &tpg, sh.cap);
+            return launch_fused_variant<4, 1, 0, 4, false, MODE>(segs, K, x, 64, sh.G, grid, stream);
+        }
+        const int64_t grid = plan_segments(segs, lpt, 8, &tpg);
         return launch_fused_variant<4, 1, 1, 8, false, MODE>(segs, K, x, 64, 8, grid, stream);
     }
     if (C <= 128) {
@@ -928,11 +961,15 @@ hipError_t launch_gemv_fmt(const uint8_t *codes, const uint16_t *scales, const v
     const int C = (int)(K / kChunkWeights);
     const int k = (int)K;
     const int64_t tiles4 = (M + 3) / 4;
-    if (C <= 64) {  // one wave covers a row: 8 independent waves per workgroup
-        const int64_t grid = gemv_grid(tiles4, 8);
-        if (tiles4 <= 2 * grid * 8)
-            return launch_variant<4, 1, 0, 4, false, FMT>(codes, scales, extra, M, k, x, y, 64, 8, grid, stream);
-        return launch_variant<4, 1, 1, 8, false, FMT>(codes, scales, extra, M, k, x, y, 64, 8, grid, stream);
+    if (C <= 64) {  // one wave covers a row: independent waves
+        if (tiles4 <= one_tile_limit()) {
+            const OneTileShape sh = one_tile_shape(tiles4, k);
+            int64_t grid = (tiles4 + sh.G - 1) / sh.G;
+            if (grid > sh.cap) grid = sh.cap;
+            return launch_variant<4, 1, 0, 4, false, FMT>(codes, scales, extra, M, k, x, y, 64, sh.G, grid, stream);
+        }
+        return launch_variant<4, 1, 1, 8, false, FMT>(codes, scales, extra, M, k, x, y, 64, 8, gemv_grid(tiles4, 8),
+                                                      stream);
     }
     if (C <= 128) {
         const int64_t tiles2 = (M + 1) / 2;
