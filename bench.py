@@ -18,7 +18,10 @@ x over the median time; the y write is added here):
 Output: one JSON line with the metric, the per-launch kernel time measured
 with HIP events on the launch stream, the HBM roofline fraction against the
 8 TB/s peak, secondary workloads (down-projection GEMV, small-N GEMM), and the
-fp64 oracle timed on the host cores as a CPU baseline.
+fp64 oracle timed on the host cores as a CPU baseline.  For context it also
+times library-independent references the same way: an empty one-element
+kernel (the per-launch floor of a graph-replayed kernel) and torch's device
+copy of each workload's code plane (its bytes read once and written once).
 """
 from __future__ import annotations
 
@@ -416,6 +419,30 @@ def context_bandwidth(torch, dev, steps=20):
     return 2 * COPY_PROBE_BYTES / (ms * 1e-3) / 1e9
 
 
+def code_plane_copy_us(torch, reps, steps, warmup):
+    """Bandwidth context from a library-independent kernel: torch's device
+    copy of the same code plane (every byte read once and written once, so
+    twice the GEMV's code bytes), graph-replayed over the same rotating
+    copies, each into a destination of its own; microseconds per call."""
+    pairs = [(cd, torch.empty_like(cd)) for cd, _ in reps]
+
+    def cp(cd, dst):
+        dst.copy_(cd)
+    ms, _ = time_graph(torch, cp, pairs, steps, warmup)
+    del pairs
+    return ms * 1e3
+
+
+def empty_kernel_us(torch, dev, steps, warmup):
+    """Launch floor: one one-element torch kernel per call, graph-replayed."""
+    t = torch.zeros(1, device=dev)
+
+    def one(_):
+        t.add_(1.0)
+    ms, _ = time_graph(torch, one, [(None,)], steps, warmup)
+    return ms * 1e3
+
+
 def cpu_baseline(oracle, wl, W, xb, name):
     """The oracle's fp64 GEMV over the whole matrix on the host cores, as it
     stands: rows split over threads, repeated until ~10 s have passed."""
@@ -511,6 +538,11 @@ def main():
     # y of the last call for the argmax check against the oracle
     q4.q4_gemv(reps[0][0], reps[0][1], x, y)
     y_gpu = y.cpu().numpy()
+    floors = None
+    if not args.no_secondary:
+        floors = {"empty_kernel_us": round(empty_kernel_us(torch, dev, args.steps, args.warmup), 3),
+                  "lm_head_code_plane_copy_us": round(code_plane_copy_us(torch, reps, args.steps, args.warmup), 3)}
+        log(f"floors: {floors}")
 
     secondary = []
     if not args.no_secondary:
@@ -536,6 +568,7 @@ def main():
                 N = ntok
             sg, sw = time_graph(torch, sstep, sreps, args.steps, args.warmup)
             secondary.append(secondary_entry(sname, sc, N, sg, sw))
+            secondary[-1]["code_plane_copy_us"] = round(code_plane_copy_us(torch, sreps, args.steps, args.warmup), 3)
             if ntok is not None:
                 # The prefill sweep: the first n tokens of the same chunk.
                 for n in (16, 8, 4, 2, 1):
@@ -591,7 +624,12 @@ def main():
         result["context"] = {
             "torch_copy_GBs": round(copy_gbs, 1),
             "lm_head_over_torch_copy": round(achieved / copy_gbs, 4),
-            "how": f"torch's {COPY_PROBE_BYTES >> 20} MiB device-to-device copy, graph-replayed"}
+            "how": f"torch's {COPY_PROBE_BYTES >> 20} MiB device-to-device copy, graph-replayed",
+            "floors": floors,
+            "floors_how": "empty_kernel_us: a one-element torch kernel per call (the launch floor); "
+                          "*code_plane_copy_us (also per secondary workload): torch's device copy of the "
+                          "same code plane (its bytes read and written once each); both graph-replayed "
+                          "over the same rotating copies"}
     if not args.no_cpu_baseline:
         import oracle
         oracle.build(force=False)
