@@ -62,10 +62,14 @@ constexpr int kCStageUnits = 16 * kCPitch;
 
 // This wave's slice of X, row-contiguously: piece p = 64 i + lane (16 bytes)
 // is token p / 32, bytes 16 (p % 32) of the slice.  Tokens past N and blocks
-// past the row's end read as zero (offsets past the buffer).
-template <int NT>
-__device__ __forceinline__ void load_x_linear(__amdgpu_buffer_rsrc_t xrs, int K, int N, int nsb, int slice,
+// past the row's end read as zero (offsets past the buffer).  Only the first
+// XP token pairs are loaded (XP covers N, fixed at compile time so the wait
+// counts stay static); the rest are zero without a load, so a small chunk
+// does not queue dead requests in the memory pipeline.
+template <int NT, int XP>
+__device__ __forceinline__ void load_x_linear(__amdgpu_buffer_rsrc_t xrs, int K, int nsb, int slice,
                                               u32x4_t (&lin)[NT * 8]) {
+    static_assert(XP >= 1 && XP <= NT * 8, "token pairs loaded");
     const int lane = threadIdx.x & 63;
     const int within = lane & 31;
     const int blk = slice * kSliceBlocks + (within >> 3);
@@ -76,7 +80,7 @@ __device__ __forceinline__ void load_x_linear(__amdgpu_buffer_rsrc_t xrs, int K,
     for (int i = 0; i < NT * 8; ++i) {
         const int tok = 2 * i + (lane >> 5);
         const int off = ((tok * K + 256 * slice + 8 * within) * 2) | (past & 0x7FFFFFF0);
-        lin[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+        lin[i] = i < XP ? __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0) : u32x4_t{0u, 0u, 0u, 0u};
     }
 }
 
@@ -156,7 +160,7 @@ __device__ __forceinline__ void convert_x_slice(const u32x4_t (&raw)[NT][kSliceB
     }
 }
 
-template <int NT, int S, bool XFIXED>
+template <int NT, int S, bool XFIXED, int XP>
 __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, int64_t M, int K,
     const uint16_t *__restrict__ X, int N, float *__restrict__ Y, int64_t tiles_q, int tiles_rem) {
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
     // activations, or the barrier before the conversion, is slower.)
     u32x4_t lin[NT * 8];
     u32x4_t raw[NT][kSliceBlocks][2];
-    if (XFIXED) load_x_linear<NT>(xrs, K, N, nsb, wave, lin);
+    if (XFIXED) load_x_linear<NT, XP>(xrs, K, nsb, wave, lin);
 #pragma unroll
     for (int s = 0; s <= S; ++s) load_unit(s);
     fill_lut(lut);
@@ -312,7 +316,7 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
             // staging area's share of this wave; the reduction buffer shares
             // those bytes, so the workgroup first leaves the previous tile's
             // sum.
-            load_x_linear<NT>(xrs, K, N, nsb, wave + nw * cu_si, lin);
+            load_x_linear<NT, XP>(xrs, K, nsb, wave + nw * cu_si, lin);
             __syncthreads();
             regroup_x<NT>(xs, lin, raw);
             convert_x_slice<NT>(raw, xa, inv);
@@ -451,13 +455,24 @@ hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int6
     const int nslices = (int)((K / 64 + kSliceBlocks - 1) / kSliceBlocks);
     int k = (int)K, n = (int)N;
     void *args[] = {&codes, &scales, &M, &k, &X, &n, &Y, &tiles_q, &tiles_rem};
+    // Token pairs loaded: the smallest of 1, 2, 4, 8 (one 16-token half) or
+    // 12, 16 (two halves) that covers N.
     const void *fn;
-    if (nslices <= kGemmMaxWaves)
-        fn = N <= 16 ? reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 2, true>)
-                     : reinterpret_cast<const void *>(&gemm_smalln_kernel<2, 2, true>);
-    else
-        fn = N <= 16 ? reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 0, false>)
-                     : reinterpret_cast<const void *>(&gemm_smalln_kernel<2, 0, false>);
+    if (nslices <= kGemmMaxWaves) {
+        if (N <= 2) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 2, true, 1>);
+        else if (N <= 4) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 2, true, 2>);
+        else if (N <= 8) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 2, true, 4>);
+        else if (N <= 16) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 2, true, 8>);
+        else if (N <= 24) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<2, 2, true, 12>);
+        else fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<2, 2, true, 16>);
+    } else {
+        if (N <= 2) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 0, false, 1>);
+        else if (N <= 4) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 0, false, 2>);
+        else if (N <= 8) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 0, false, 4>);
+        else if (N <= 16) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 0, false, 8>);
+        else if (N <= 24) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<2, 0, false, 12>);
+        else fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<2, 0, false, 16>);
+    }
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * kGemmMaxWaves), args, 0, stream);
 }
 
