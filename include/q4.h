@@ -128,10 +128,14 @@ int q4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
 
 /*
  * q4_gemm_smalln -- Y[n][m] = sum_k What[m,k] * X[n][k], n < N <= 32, m < M
- * (the prefill-chunk form; every weight is read once per call).
+ * (the prefill-chunk form: deep-fold "Decode V2" page, section 0 Goals, a
+ * prompt runs as chunks of up to 32 tokens through one product; golang.design
+ * accel/tensor, func Int4MatMul: the matrix is read once per tile of tokens.
+ * Every weight is read once per call).
  *   X: bf16 bit patterns [N][K] row-major, 16-byte aligned.
  *   Y: fp32 [N][M] row-major, 4-byte aligned; must not overlap the inputs.
- * Same accuracy statement as q4_gemv.
+ * Same accuracy statement as q4_gemv.  A chunk of one token is computed by
+ * the q4_gemv kernels (Y[0] is then bit-identical to q4_gemv of X[0]).
  */
 int q4_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M,
                    int64_t K, const uint16_t *X, int64_t N, float *Y,

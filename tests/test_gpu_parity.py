@@ -383,6 +383,21 @@ def test_gemm_smalln_parity(env, M, K, N):
     _check(Y.cpu().numpy(), Y_ref, S, f"gemm M={M} K={K} N={N}")
 
 
+def test_gemm_one_token_is_the_gemv(env):
+    """A one-token chunk runs the GEMV kernels: bit-identical to q4_gemv."""
+    torch, q4, dev = env
+    for M, K in ((300, 2048), (257, 11008)):
+        W = wl.weights(M, K, 43)
+        X = wl.activations(1, K, 43, "unit_rms")
+        codes, scales, _ = oracle.pack(W)
+        c, s = _upload_packed(env, codes, scales)
+        Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+        Y = q4.q4_gemm_smalln(c, s, Xd)
+        y = q4.q4_gemv(c, s, Xd[0].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(Y[0], y), f"M={M} K={K}"
+
+
 def test_gemm_rows_match_gemv(env):
     torch, q4, dev = env
     M, K, N = 300, 2048, 5
