@@ -1,7 +1,7 @@
 """Benchmark of the 4-bit codebook GEMV on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--copies R] [--no-secondary]
-                    [--secondary down,smalln,gateup,fused,gather,affine,nvfp4,x8]
+                    [--secondary down,smalln,gateup,fused,gather,affine,nvfp4,x8,pages]
 
 A step is one q4_gemv call on the lm_head workload (M x K = 151936 x 2048,
 x bf16 unit-RMS, y fp32): the projection the metric is quoted on.  Inputs are
@@ -273,6 +273,74 @@ def fused_secondaries(torch, q4, wl, dev, steps, warmup):
     return out
 
 
+PAGES_TABLE = os.path.join(ROOT, "tests", "golden", "decode_v2_linear_bench.tsv")
+COLD_BYTES = 640 << 20   # rotated copies per shape: past the 256 MB Infinity Cache
+
+
+def pages_table():
+    """The per-launch GEMV bench table of the deep-fold "Decode V2" page
+    (section 6): kind, M, K, median us and GB/s on the page's consumer NVIDIA
+    card, as transcribed in the golden fixture."""
+    rows = []
+    with open(PAGES_TABLE) as fh:
+        for line in fh:
+            if line.strip() and not line.startswith("#"):
+                kind, M, K, us, gbs = line.split("\t")
+                rows.append((kind, int(M), int(K), float(us), float(gbs)))
+    return rows
+
+
+def pages_secondaries(torch, q4, wl, dev, steps, warmup):
+    """The GEMV on every shape of the page's bench table (but lm_head, the
+    headline): W ~ N(0, 0.02^2) seeded per shape, x unit-RMS (SwiGLU-like for
+    the down projections, K of 11008 or 27648), enough packed copies (views
+    of one buffer) that the timed graph reads past the Infinity Cache; the
+    graph holds at least one call per copy.  The page's own figures ride
+    along as context (other hardware, their GB/s omits y)."""
+    out = []
+    for i, (kind, M, K, p_us, p_gbs) in enumerate(pages_table()):
+        if kind == "lm_head":
+            continue
+        seed = 100 + i
+        W = torch.from_numpy(wl.weights(M, K, seed)).to(dev)
+        codes, scales, status = q4.q4_pack(W)
+        torch.cuda.synchronize()
+        del W
+        if int(status.item()) != 0:
+            raise RuntimeError(f"q4_pack flagged the {kind} weights")
+        wbytes = codes.numel() + 2 * scales.numel()
+        R = max(1, min(4096, -(-COLD_BYTES // wbytes)))
+        big_c = torch.empty((R,) + tuple(codes.shape), dtype=codes.dtype, device=dev)
+        big_s = torch.empty((R,) + tuple(scales.shape), dtype=scales.dtype, device=dev)
+        big_c[:] = codes
+        big_s[:] = scales
+        del codes, scales
+        reps = [(big_c[r], big_s[r]) for r in range(R)]
+        x = _upload_bits(torch, wl.activation(K, seed, "swiglu" if K in (11008, 27648) else "unit_rms"),
+                         torch.bfloat16, dev)
+        y = torch.empty(M, dtype=torch.float32, device=dev)
+
+        def fn(cd, sl, x=x, y=y):
+            q4.q4_gemv(cd, sl, x, y)
+        n_calls = max(steps, R)
+        ms, wall = time_graph(torch, fn, reps, n_calls, warmup)
+        nb = gemv_bytes(M, K)
+        pb = nb - 4 * M  # the page's convention: packed + scale + x
+        log(f"pages {kind} {M}x{K}: {ms * 1e3:.2f} us/call, {nb / (ms * 1e-3) / 1e9:.0f} GB/s "
+            f"(page: {p_us} us, {p_gbs} GB/s)")
+        out.append({"workload": f"pages table {kind} {M}x{K} N=1", "us_per_call": round(ms * 1e3, 3),
+                    "us_per_step_wall": round(wall * 1e3, 3), "bytes": nb,
+                    "achieved_GBs": round(nb / (ms * 1e-3) / 1e9, 1),
+                    "frac_of_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "pages_convention_GBs": round(pb / (ms * 1e-3) / 1e9, 1),
+                    "copies_rotated": R, "calls_per_graph": n_calls,
+                    "page_us": p_us, "page_GBs": p_gbs,
+                    "page_hardware": "consumer NVIDIA card of the page's lab log (context only)"})
+        del reps, big_c, big_s, x, y
+        torch.cuda.empty_cache()
+    return out
+
+
 def gather_secondaries(torch, q4, wl, dev, steps, warmup):
     """The packed row gather on the tied-embedding table (the lm_head matrix,
     151936 x 2048): one decode token and a 32-token chunk, fp32 and bf16
@@ -479,9 +547,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--secondary", default="down,smalln,gateup,fused,gather,affine,nvfp4,x8",
+    ap.add_argument("--secondary", default="down,smalln,gateup,fused,gather,affine,nvfp4,x8,pages",
                     help="comma-separated secondary workloads to time "
-                         "(down, smalln, gateup, fused, gather, affine, nvfp4, x8)")
+                         "(down, smalln, gateup, fused, gather, affine, nvfp4, x8, pages)")
     ap.add_argument("--eager", action="store_true",
                     help="also time the calls launched one by one from Python")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -592,6 +660,8 @@ def main():
             secondary.extend(nvfp4_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
         if "x8" in chosen:
             secondary.extend(x8_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
+        if "pages" in chosen:
+            secondary.extend(pages_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
 
     result = {
         "metric": "4-bit GEMV us/call + achieved HBM GB/s (% of peak), MxK=151936x2048, N=1",

@@ -43,6 +43,7 @@
 namespace q4 {
 
 constexpr int kMaxWavesPerGroup = 8;
+constexpr int kMaxWavesPerBlock = 16;
 // Row-per-wave variants cover rows of up to 128 chunks (K <= 4096): the LDS
 // copy of the activations is at most 8 KB (512 lanes x 16 bytes).
 constexpr int kSharedXUnits = 512;
@@ -192,7 +193,7 @@ __device__ __forceinline__ float convert_x(Load load, uint32_t (&raw)[16], half2
 // longer rows trade occupancy for the extra activation registers.  Groups
 // spanning several waves use workgroups of at most 512 lanes.
 constexpr int gemv_min_waves(int cpl) { return cpl == 1 ? 4 : 2; }
-constexpr int gemv_max_block(bool multi, int cpl) { return (multi || cpl > 1) ? 512 : 1024; }
+constexpr int gemv_max_block(bool multi, int cpl) { return cpl > 1 ? 512 : 1024; }
 
 // SiLU(z) = z * sigmoid(z) = z / (1 + e^-z) (golang.design accel/tensor,
 // func SiLU), fp32.
@@ -264,7 +265,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     constexpr bool X8TWO = FMT == kFmtAffineX8x2;
     constexpr bool ZEROS = FMT == kFmtAffine || X8;  // zero-point plane
     __shared__ uint32_t lut[X8 ? 1 : kLutDwords];
-    __shared__ float red[kMaxWavesPerGroup][RG];
+    __shared__ float red[kMaxWavesPerBlock][RG];
     // Groups of one wave all need the whole activation vector: it is read
     // from global memory once per workgroup into LDS (raw bf16, 16 bytes per
     // lane) and every wave takes its chunks from there.
@@ -277,11 +278,13 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // A group is one wave (MULTI == false) or the whole workgroup.
+    // A group is one wave (MULTI == false) or P / 64 waves of the
+    // workgroup (MULTI; a workgroup holds blockDim.x / P groups).
     const int wpg = MULTI ? (P >> 6) : 1;     // waves per group
-    const int wig = MULTI ? wave : 0;         // wave within its group
+    const int grp = MULTI ? wave / wpg : 0;   // group within the workgroup
+    const int wig = MULTI ? wave - grp * wpg : 0;  // wave within its group
     const int lig = wig * 64 + lane;          // lane within its group
-    const int64_t gid = MULTI ? wg : wg * (blockDim.x >> 6) + wave;
+    const int64_t gid = MULTI ? wg * (int64_t)(blockDim.x / P) + grp : wg * (blockDim.x >> 6) + wave;
     const int C = K >> 5;                      // 16-byte chunks per row
     const int nsb = K >> 6;                    // 64-blocks per row
     // Scale row stride in 16-bit units: one fp16 per 64-block, or (NVFP4)
@@ -293,6 +296,11 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     const int64_t r_begin = gid * rows_q + (gid < rows_rem ? gid : rows_rem);
     const int64_t r_end = r_begin + rows_q + (gid < rows_rem ? 1 : 0);
     const int64_t ntiles = (r_end - r_begin + LPT - 1) / LPT;
+    // Groups spanning several waves meet at workgroup barriers in every
+    // reduction group, so all groups of the grid walk the same number of
+    // tiles: the most any group has (a group past its own range works on
+    // tiles that load nothing and store nothing).
+    const int64_t nsteps = MULTI ? (rows_q + (rows_rem > 0 ? 1 : 0) + LPT - 1) / LPT : ntiles;
 
     // Chunk indices of this lane.  Lanes past the row's end load a valid
     // chunk (the last one) and multiply it by zero activations, so every load
@@ -625,7 +633,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         }
     };
 
-    for (int64_t g0 = 0; g0 < ntiles; g0 += TPG) {
+    for (int64_t g0 = 0; g0 < nsteps; g0 += TPG) {
         const Epi epi = fetch_epi(g0);
 #pragma unroll
         for (int j = 0; j < TPG; ++j) step(j % (S + 1), j, g0 + j);
@@ -634,12 +642,12 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         if (!MULTI) {
             store(tot, g0, epi);
         } else {
-            if (lane < RG) red[wig][lane] = tot;
+            if (lane < RG) red[wave][lane] = tot;
             __syncthreads();
             if (wig == 0) {
                 float sum = 0.0f;
                 if (lane < RG)
-                    for (int w = 0; w < wpg; ++w) sum += red[w][lane];
+                    for (int w = 0; w < wpg; ++w) sum += red[grp * wpg + w][lane];
                 store(sum, g0, epi);
             }
             __syncthreads();
@@ -817,7 +825,7 @@ int64_t one_tile_limit() { return 2LL * 16 * cu_count(); }
 // at two per CU, which leave a third of the waves two tiles in sequence
 // (11008 rows: 344 workgroups, two on some CUs and one on others).
 struct OneTileShape {
-    int G;          // waves per workgroup
+    int G;          // lane groups per workgroup (waves, for rows of one wave)
     int64_t cap;    // most workgroups
 };
 OneTileShape one_tile_shape(int64_t tiles, int K) {
@@ -828,6 +836,27 @@ OneTileShape one_tile_shape(int64_t tiles, int K) {
     if (G < gmin) G = gmin;
     if (G < 1) G = 1;
     if (G > 16) G = 16;
+    return {(int)G, per_cu * cus};
+}
+
+// Groups per workgroup for rows spanning `wpg` waves (one chunk a lane, at
+// most 512 chunks): up to about 16 waves per CU, in one workgroup per CU
+// when that covers every tile once, else in two.  Each group takes one 4-row
+// tile at a time.  Measured (lab sweep of the group count and the ring, same run):
+// 2048 x 11008 5.50 -> 5.21 us (2 groups of 6 waves), 5120 x 5120 7.61 ->
+// 5.75 (5 of 3), 27648 x 5120 18.9 -> 16.2 (2 of 3, two per CU), 8192 x 8192
+// 9.28 -> 8.82 (2 of 4), 4096 x 14336 8.54 -> 8.55 (1 of 7); a ring of two
+// tiles per group, or 24-32 waves per CU, was slower on every shape.
+OneTileShape multi_shape(int64_t tiles, int wpg) {
+    const int64_t cus = cu_count();
+    const int gmax = 16 / wpg > 0 ? 16 / wpg : 1;
+    const int64_t per_cu = tiles <= cus * gmax ? 1 : 2;
+    // No more groups per workgroup than the tiles need: a small matrix keeps
+    // one workgroup on every CU it can reach.
+    int64_t G = gmax / per_cu;
+    const int64_t need = (tiles + per_cu * cus - 1) / (per_cu * cus);
+    if (G > need) G = need;
+    if (G < 1) G = 1;
     return {(int)G, per_cu * cus};
 }
 
@@ -905,10 +934,13 @@ hipError_t launch_fused_mode(GemvSegs segs, int K, const uint16_t *x, hipStream_
         return launch_fused_variant<2, 2, 1, 16, false, MODE>(segs, K, x, 64, 8, grid, stream);
     }
     if (C <= 64 * kMaxWavesPerGroup) {
-        const int P = ((C + 63) / 64) * 64;
-        const int64_t grid = plan_segments(segs, 4 / half, 1, &tpg);
-        if (tpg <= 2) return launch_fused_variant<4, 1, 0, 4, true, MODE>(segs, K, x, P, 1, grid, stream);
-        return launch_fused_variant<4, 1, 1, 8, true, MODE>(segs, K, x, P, 1, grid, stream);
+        const int wpg = (C + 63) / 64;
+        const int lpt = 4 / half;
+        int64_t tiles = 0;
+        for (int i = 0; i < segs.n; ++i) tiles += (segs.s[i].rows + lpt - 1) / lpt;
+        const OneTileShape sh = multi_shape(tiles, wpg);
+        const int64_t grid = plan_segments(segs, lpt, sh.G, &tpg, sh.cap);
+        return launch_fused_variant<4, 1, 0, 4, true, MODE>(segs, K, x, wpg * 64, sh.G, grid, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -975,7 +1007,8 @@ hipError_t launch_gemv_fmt(const uint8_t *codes, const uint16_t *scales, const v
         const int64_t tiles2 = (M + 1) / 2;
         return launch_variant<2, 2, 1, 16, false, FMT>(codes, scales, extra, M, k, x, y, 64, 8, gemv_grid(tiles2, 8), stream);
     }
-    // Long rows: the whole workgroup (up to 8 waves) shares a row tile.
+    // Long rows: a group of up to 8 waves shares a row tile; one chunk a
+    // lane for rows of up to 512 chunks, in several groups per workgroup.
     int cpl = 1;
     while (C > cpl * 64 * kMaxWavesPerGroup) cpl *= 2;
     const int waves = (C + cpl * 64 - 1) / (cpl * 64);
@@ -983,9 +1016,12 @@ hipError_t launch_gemv_fmt(const uint8_t *codes, const uint16_t *scales, const v
     const int64_t grid4 = gemv_grid(tiles4, 1);
     const bool few = tiles4 <= 2 * grid4;
     switch (cpl) {
-        case 1:
-            if (few) return launch_variant<4, 1, 0, 4, true, FMT>(codes, scales, extra, M, k, x, y, P, 1, grid4, stream);
-            return launch_variant<4, 1, 1, 8, true, FMT>(codes, scales, extra, M, k, x, y, P, 1, grid4, stream);
+        case 1: {
+            const OneTileShape sh = multi_shape(tiles4, waves);
+            int64_t grid = (tiles4 + sh.G - 1) / sh.G;
+            if (grid > sh.cap) grid = sh.cap;
+            return launch_variant<4, 1, 0, 4, true, FMT>(codes, scales, extra, M, k, x, y, P, sh.G, grid, stream);
+        }
         case 2:
             if (few) return launch_variant<4, 2, 0, 4, true, FMT>(codes, scales, extra, M, k, x, y, P, 1, grid4, stream);
             return launch_variant<4, 2, 1, 8, true, FMT>(codes, scales, extra, M, k, x, y, P, 1, grid4, stream);

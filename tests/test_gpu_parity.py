@@ -150,7 +150,10 @@ def test_pack_flags_and_valid_blocks(env):
 GEMV_SHAPES = [(1, 64), (2, 64), (7, 128), (257, 512), (1000, 1024), (4097, 2048), (31, 1984),
                (32771, 192), (40001, 64),
                (300, 2112), (65, 4096), (129, 4160), (2048, 11008), (33, 11008), (9, 16384),
-               (4099, 4160), (5, 16448), (4101, 16448), (3, 32768), (2, 65536), (2, 131072)]
+               (4099, 4160), (5, 16448), (4101, 16448), (3, 32768), (2, 65536), (2, 131072),
+               # long rows in two workgroups per CU, several groups each, some
+               # groups one tile short of the others
+               (8197, 6208)]
 
 
 @pytest.mark.parametrize("M,K", GEMV_SHAPES)
