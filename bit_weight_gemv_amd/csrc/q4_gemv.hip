@@ -850,7 +850,9 @@ OneTileShape one_tile_shape(int64_t tiles, int K) {
 OneTileShape multi_shape(int64_t tiles, int wpg) {
     const int64_t cus = cu_count();
     const int gmax = 16 / wpg > 0 ? 16 / wpg : 1;
-    const int64_t per_cu = tiles <= cus * gmax ? 1 : 2;
+    // Groups of more than 8 waves stay one workgroup per CU (28 waves per CU
+    // measured slower than 14 on 5120 x 27648: 17.1 against 15.5 us).
+    const int64_t per_cu = (tiles <= cus * gmax || 2 * wpg > 16) ? 1 : 2;
     // No more groups per workgroup than the tiles need: a small matrix keeps
     // one workgroup on every CU it can reach.
     int64_t G = gmax / per_cu;
@@ -1007,14 +1009,15 @@ hipError_t launch_gemv_fmt(const uint8_t *codes, const uint16_t *scales, const v
         const int64_t tiles2 = (M + 1) / 2;
         return launch_variant<2, 2, 1, 16, false, FMT>(codes, scales, extra, M, k, x, y, 64, 8, gemv_grid(tiles2, 8), stream);
     }
-    // Long rows: a group of up to 8 waves shares a row tile; one chunk a
-    // lane for rows of up to 512 chunks, in several groups per workgroup.
+    // Long rows: a group of waves shares a row tile.  One chunk a lane for
+    // rows of up to 1024 chunks (groups of up to 16 waves, several groups per
+    // workgroup when they are small); longer rows take 2, 4 or 8 chunks a
+    // lane in groups of up to 8 waves.
     int cpl = 1;
-    while (C > cpl * 64 * kMaxWavesPerGroup) cpl *= 2;
+    if (C > 64 * kMaxWavesPerBlock)
+        while (C > cpl * 64 * kMaxWavesPerGroup) cpl *= 2;
     const int waves = (C + cpl * 64 - 1) / (cpl * 64);
     const int P = waves * 64;
-    const int64_t grid4 = gemv_grid(tiles4, 1);
-    const bool few = tiles4 <= 2 * grid4;
     switch (cpl) {
         case 1: {
             const OneTileShape sh = multi_shape(tiles4, waves);
@@ -1022,9 +1025,6 @@ hipError_t launch_gemv_fmt(const uint8_t *codes, const uint16_t *scales, const v
             if (grid > sh.cap) grid = sh.cap;
             return launch_variant<4, 1, 0, 4, true, FMT>(codes, scales, extra, M, k, x, y, P, sh.G, grid, stream);
         }
-        case 2:
-            if (few) return launch_variant<4, 2, 0, 4, true, FMT>(codes, scales, extra, M, k, x, y, P, 1, grid4, stream);
-            return launch_variant<4, 2, 1, 8, true, FMT>(codes, scales, extra, M, k, x, y, P, 1, grid4, stream);
         case 4: {
             const int64_t tiles2 = (M + 1) / 2;
             return launch_variant<2, 4, 1, 4, true, FMT>(codes, scales, extra, M, k, x, y, P, 1, gemv_grid(tiles2, 1), stream);
