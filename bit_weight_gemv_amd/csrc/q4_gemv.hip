@@ -931,10 +931,6 @@ hipError_t launch_fused_mode(GemvSegs segs, int K, const uint16_t *x, hipStream_
         const int64_t grid = plan_segments(segs, lpt, 8, &tpg);
         return launch_fused_variant<4, 1, 1, 8, false, MODE>(segs, K, x, 64, 8, grid, stream);
     }
-    if (C <= 128) {
-        const int64_t grid = plan_segments(segs, 2 / half, 8, &tpg);
-        return launch_fused_variant<2, 2, 1, 16, false, MODE>(segs, K, x, 64, 8, grid, stream);
-    }
     if (C <= 64 * kMaxWavesPerGroup) {
         const int wpg = (C + 63) / 64;
         const int lpt = 4 / half;
@@ -983,12 +979,13 @@ hipError_t launch_gemv_fused(const FusedOperand *ops, int count, bool swiglu, in
     return launch_fused_mode<kModeEpi>(segs, (int)K, x, stream);
 }
 
-// Variant choice.  Every variant reads tiles of 4 rows (2 for 2-chunk
-// lanes).  Where a lane group gets at most two tiles (the whole matrix fits
-// one pass of the grid with a few rows per group) the ring has nothing to run
-// ahead of: the single-tile form (no ring, 4-row reduction groups) has the
-// shortest set-up.  Otherwise a ring of two tiles keeps the next tile's
-// loads in flight while the current one is reduced.
+// Variant choice (by measurement).  Rows of one wave (K <= 2048): one 4-row
+// tile per wave while the grid covers the matrix in one pass, else a ring of
+// two tiles per wave keeps the next tile's loads in flight while the current
+// one is reduced (the lm_head shape).  Longer rows: groups of waves share
+// 4-row tiles, one tile at a time, sized by multi_shape; the longest rows
+// take several chunks a lane (4-row tiles in a ring of two at 4 chunks, one
+// row at a time at 8).
 template <int FMT>
 hipError_t launch_gemv_fmt(const uint8_t *codes, const uint16_t *scales, const void *extra, int64_t M,
                            int64_t K, const uint16_t *x, float *y, hipStream_t stream) {
@@ -1005,14 +1002,12 @@ hipError_t launch_gemv_fmt(const uint8_t *codes, const uint16_t *scales, const v
         return launch_variant<4, 1, 1, 8, false, FMT>(codes, scales, extra, M, k, x, y, 64, 8, gemv_grid(tiles4, 8),
                                                       stream);
     }
-    if (C <= 128) {
-        const int64_t tiles2 = (M + 1) / 2;
-        return launch_variant<2, 2, 1, 16, false, FMT>(codes, scales, extra, M, k, x, y, 64, 8, gemv_grid(tiles2, 8), stream);
-    }
-    // Long rows: a group of waves shares a row tile.  One chunk a lane for
+    // Longer rows: a group of waves shares a row tile.  One chunk a lane for
     // rows of up to 1024 chunks (groups of up to 16 waves, several groups per
-    // workgroup when they are small); longer rows take 2, 4 or 8 chunks a
-    // lane in groups of up to 8 waves.
+    // workgroup when they are small; for rows of 65..128 chunks this measured
+    // 8.4 against 11.7 us on 14336 x 4096 and 4.6 against 7.3 us on
+    // 4096 x 4096 for one wave per row at two chunks a lane); longer rows take
+    // 4 or 8 chunks a lane in groups of up to 8 waves.
     int cpl = 1;
     if (C > 64 * kMaxWavesPerBlock)
         while (C > cpl * 64 * kMaxWavesPerGroup) cpl *= 2;
