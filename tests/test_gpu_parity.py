@@ -153,7 +153,10 @@ GEMV_SHAPES = [(1, 64), (2, 64), (7, 128), (257, 512), (1000, 1024), (4097, 2048
                (4099, 4160), (5, 16448), (4101, 16448), (3, 32768), (2, 65536), (2, 131072),
                # long rows in two workgroups per CU, several groups each, some
                # groups one tile short of the others
-               (8197, 6208)]
+               (8197, 6208),
+               # rows of one wave dealt to the waves in turn (more than 16
+               # tiles per CU), with ragged last tiles
+               (16389, 1024), (20011, 2048)]
 
 
 @pytest.mark.parametrize("M,K", GEMV_SHAPES)
