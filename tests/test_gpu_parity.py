@@ -442,6 +442,40 @@ def test_gemm_smalln_full_size_sampled(env):
 # HIP graph capture (a decode step is captured once and replayed)
 # ---------------------------------------------------------------------------
 
+def test_graph_capture_strided_and_grouped_launches(env):
+    """The strided short-row launch (more than 16 tiles per CU) and the
+    grouped long-row launch, captured in one graph: every replay equals the
+    eager result bit for bit."""
+    torch, q4, dev = env
+    outs, calls = [], []
+    for M, K in ((40000, 2048), (3000, 5120)):
+        W = wl.weights(M, K, 52)
+        codes, scales, _ = oracle.pack(W)
+        c, s = _upload_packed(env, codes, scales)
+        x = _x_dev(env, wl.activation(K, 52, "unit_rms"))
+        y_eager = q4.q4_gemv(c, s, x).clone()
+        y = torch.full((M,), float("nan"), device=dev)
+        outs.append((y, y_eager))
+        calls.append((c, s, x, y))
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            for c, s, x, y in calls:
+                q4.q4_gemv(c, s, x, y, stream=st)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for y, _ in outs:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (y, y_eager) in enumerate(outs):
+            assert torch.equal(y, y_eager), f"launch {i} replay {rep} differs from eager"
+
+
 def test_graph_capture_replays_match_eager(env):
     torch, q4, dev = env
     M, K, N = 3000, 2048, 8
