@@ -511,6 +511,18 @@ def empty_kernel_us(torch, dev, steps, warmup):
     return ms * 1e3
 
 
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(oracle, wl, W, xb, name):
     """The oracle's fp64 GEMV over the whole matrix on the host cores, as it
     stands: rows split over threads, repeated until ~10 s have passed."""
@@ -529,11 +541,20 @@ def cpu_baseline(oracle, wl, W, xb, name):
         if time.time() - t_start > 10.0 or len(times) >= 400:
             break
     sec = float(np.median(times))
+    # The same call on one thread (identical sums: rows are only split),
+    # median of three.
+    t1 = []
+    for _ in range(3):
+        t = time.perf_counter()
+        oracle.gemv(codes, scales, M, K, xb, threads=1)
+        t1.append(time.perf_counter() - t)
     return {
         "value": round(gemv_bytes(M, K) / sec / 1e9, 3),
         "unit": "GB/s",
         "us_per_call": round(sec * 1e6, 1),
+        "us_per_call_1_thread": round(float(np.median(t1)) * 1e6, 1),
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"full {name} GEMV {M}x{K} (fp64 oracle, rows split over {threads} threads), "
                   f"{len(times)} calls in {time.time() - t_start:.1f}s, median",
@@ -687,6 +708,8 @@ def main():
                      "timing": "HIP graph of the timed calls, events on the replay stream"},
         "eager": eager,
         "secondary": secondary,
+        "machine": {"gpu": torch.cuda.get_device_name(dev), "hip": torch.version.hip,
+                    "torch": torch.__version__},
     }
     if not args.no_secondary:
         copy_gbs = context_bandwidth(torch, dev)

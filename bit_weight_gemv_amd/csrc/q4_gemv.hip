@@ -192,11 +192,23 @@ __device__ __forceinline__ float convert_x(Load load, uint32_t (&raw)[16], half2
 // Register budget: one chunk per lane keeps 4 waves per SIMD (128 VGPRs);
 // longer rows trade occupancy for the extra activation registers.  Groups
 // spanning several waves use workgroups of at most 512 lanes.
-constexpr int gemv_min_waves(int cpl) { return cpl == 1 ? 4 : 2; }
+// The one-load-per-tile scale path (TS) asks for six (at most 80 VGPRs): the
+// one-tile-per-wave launches put up to 16 waves on a CU.
+constexpr int gemv_min_waves(int cpl, bool ts = false) { return ts ? 6 : (cpl == 1 ? 4 : 2); }
 constexpr int gemv_max_block(bool multi, int cpl) { return cpl > 1 ? 512 : 1024; }
 
 // SiLU(z) = z * sigmoid(z) = z / (1 + e^-z) (golang.design accel/tensor,
 // func SiLU), fp32.
+// Lane l of each quad's value, in every lane of the quad (DPP quad_perm).
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v, int l) {
+    switch (l) {
+        case 0: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xF, 0xF, false);
+        case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xF, 0xF, false);
+        case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xAA, 0xF, 0xF, false);
+        default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xFF, 0xF, 0xF, false);
+    }
+}
+
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
 // One output segment of a launch.  The plain and affine forms read one
@@ -258,7 +270,15 @@ struct X8Args {
 // into s * (d - (z - 8) * xsum), xsum being the sum of the lane's 32
 // activations of that chunk (the same scaled fp16 values the dot uses), so
 // the zero point costs one load and two operations per chunk.
-template <int NR, int CPL, int S, int RG, bool MULTI, int MODE, int FMT = kFmtNf4, bool STRIDED = false>
+//
+// TS (rows of one wave, one chunk a lane, NF4 scales on a dword-aligned plane
+// with an even number a row, as the host checks): a tile's scales are one
+// contiguous run per matrix (LPT rows of K/64 values, at most 256 bytes),
+// read with one dword load per lane and handed to the lanes that need them by
+// quad broadcasts (DPP): one load instruction per tile and matrix instead of
+// one 2-byte load per row.
+template <int NR, int CPL, int S, int RG, bool MULTI, int MODE, int FMT = kFmtNf4, bool STRIDED = false,
+          bool TS = false>
 __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16_t *__restrict__ x, int P,
                                           int64_t wg) {
     constexpr bool X8 = FMT == kFmtAffineX8 || FMT == kFmtAffineX8x2;
@@ -273,6 +293,9 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
 
     static_assert(MODE != kModeSwiglu || NR % 2 == 0, "a SwiGLU tile pairs gate and up rows");
     constexpr int LPT = MODE == kModeSwiglu ? NR / 2 : NR;  // outputs per tile
+    static_assert(!TS || (!MULTI && CPL == 1 && S == 0 && FMT == kFmtNf4 && LPT <= 4),
+                  "one scale run per tile and matrix");
+    constexpr int NPART = MODE == kModeSwiglu ? 2 : 1;  // matrices a tile reads
     const int64_t rows_q = sg.rows_q;
     const int rows_rem = sg.rows_rem;
 
@@ -329,8 +352,21 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         soff[i] = FMT == kFmtNvfp4 ? (uint32_t)c : (uint32_t)c >> 1;
     }
 
+    // TS: the four lanes of quad Q hold chunks 4Q .. 4Q+3, i.e. 64-blocks 2Q
+    // and 2Q+1 of each row: the low and high halves of dword Q of the row's
+    // scales.  Lane 4Q+r reads that dword of tile row r (rows r % LPT of each
+    // matrix when LPT < 4), so row r's scales reach the quad by a broadcast of
+    // its lane r.  Quads past the row's end read past every run (zeros).
+    uint32_t ts_off = 0, ts_sh = 0;
+    if constexpr (TS) {
+        const int quad = lane >> 2;
+        ts_off = quad < (C >> 2) ? (uint32_t)((((lane & 3) % LPT) * (nsb >> 1) + quad) * 4) : 0x40000000u;
+        ts_sh = (uint32_t)((lane >> 1) & 1) << 4;
+    }
+
     uint4 q[S + 1][NR][CPL];
-    uint32_t sc[S + 1][NR][CPL];
+    uint32_t sc[TS ? 1 : S + 1][NR][CPL];
+    uint32_t tsc[TS ? S + 1 : 1][NPART];  // TS: this lane's dword of each run
     uint32_t zc[ZEROS ? S + 1 : 1][NR][CPL];  // zero-point bits (affine codes only)
     // Tiles are loaded in order.  The next tile to load starts at output
     // r_begin + LPT * (tiles loaded so far); its pointers advance by one tile
@@ -365,6 +401,18 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
             crs1 = buffer_rsrc(next_codes1, real ? (uint32_t)(LPT * row_bytes) : 0u);
             srs1 = buffer_rsrc(next_scales1, real ? (uint32_t)(LPT * nsb * 2) : 0u);
         }
+        if constexpr (TS) {
+            // The run of the tile's valid rows (whole dwords: an even number
+            // of scales a row); lanes past it read zeros.
+            const uint32_t run = (uint32_t)((real ? nvalid : 0) * nsb * 2);
+            if (r0 == 0)
+                tsc[buf][0] = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(next_scales0, run), (int)ts_off, 0,
+                                                                   kLoadNonTemporal);
+            if constexpr (MODE == kModeSwiglu)
+                if (r0 <= LPT && LPT < r1)
+                    tsc[buf][NPART - 1] = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(next_scales1, run),
+                                                                               (int)ts_off, 0, kLoadNonTemporal);
+        }
 #pragma unroll
         for (int r = r0; r < r1; ++r) {
             const int lr = r % LPT;
@@ -377,8 +425,9 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                 const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
                     up ? crs1 : crs0, (int)coff[i], (int)(rr * row_bytes), kLoadNonTemporal);
                 q[buf][r][i] = make_uint4(v.x, v.y, v.z, v.w);
-                sc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(up ? srs1 : srs0, (int)(soff[i] * 2),
-                                                                      rr * sst * 2, kLoadNonTemporal);
+                if constexpr (!TS)
+                    sc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(up ? srs1 : srs0, (int)(soff[i] * 2),
+                                                                          rr * sst * 2, kLoadNonTemporal);
                 if constexpr (ZEROS)
                     zc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(zrs0, (int)(soff[i] * 2), rr * nsb * 2,
                                                                           kLoadNonTemporal);
@@ -542,6 +591,12 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     float acc[RG];
     auto step = [&](int buf, int j, int64_t t) {
         if (t < ntiles) {
+            // TS: row r's scale dword, broadcast in each quad from its lane r % LPT.
+            uint32_t tsb[TS ? NR : 1];
+            if constexpr (TS) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r) tsb[r] = quad_bcast(tsc[buf][r < LPT ? 0 : NPART - 1], r % LPT);
+            }
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 float a = 0.0f;
@@ -579,7 +634,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                         float p = chunk_dot(lut, q[buf][r][i], xh[i], laneoff);
                         if constexpr (FMT == kFmtAffine)
                             p = fmaf(8.0f - f16_bits_to_f32(zc[buf][r][i]), xsum[i], p);
-                        a = fmaf(p, f16_bits_to_f32(sc[buf][r][i]), a);
+                        const uint32_t sbits = TS ? tsb[r] >> ts_sh : sc[buf][r][i];
+                        a = fmaf(p, f16_bits_to_f32(sbits), a);
                     }
                 }
                 acc[j * NR + r] = a;
@@ -675,9 +731,9 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     }
 }
 
-template <int NR, int CPL, int S, int RG, bool MULTI, bool STRIDED = false>
+template <int NR, int CPL, int S, int RG, bool MULTI, bool STRIDED = false, bool TS = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
-                          amdgpu_waves_per_eu(gemv_min_waves(CPL), 8))) void gemv_kernel(const uint8_t *__restrict__ codes,
+                          amdgpu_waves_per_eu(gemv_min_waves(CPL, TS), 8))) void gemv_kernel(const uint8_t *__restrict__ codes,
                                                    const uint16_t *__restrict__ scales, int64_t M,
                                                    int K, const uint16_t *__restrict__ x,
                                                    float *__restrict__ y, int P, int64_t rows_q,
@@ -689,7 +745,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
     sg.rows = M;
     sg.rows_q = rows_q;
     sg.rows_rem = rows_rem;
-    gemv_body<NR, CPL, S, RG, MULTI, kModePlain, kFmtNf4, STRIDED>(sg, K, x, P, (int64_t)blockIdx.x);
+    gemv_body<NR, CPL, S, RG, MULTI, kModePlain, kFmtNf4, STRIDED, TS>(sg, K, x, P, (int64_t)blockIdx.x);
 }
 
 // The affine format's GEMV (y = W . x with W = (code - z) * s).
@@ -765,11 +821,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
 // The one-segment form (a SwiGLU pair, or a single matrix): the segment is
 // the kernel argument itself, so its fields arrive with the first scalar
 // reads instead of after a lookup of the workgroup's segment.
-template <int NR, int CPL, int S, int RG, bool MULTI, int MODE, bool STRIDED = false>
+template <int NR, int CPL, int S, int RG, bool MULTI, int MODE, bool STRIDED = false, bool TS = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
-                          amdgpu_waves_per_eu(gemv_min_waves(CPL), 8))) void gemv_fused1_kernel(GemvSeg sg, int K,
+                          amdgpu_waves_per_eu(gemv_min_waves(CPL, TS), 8))) void gemv_fused1_kernel(GemvSeg sg, int K,
                                                    const uint16_t *__restrict__ x, int P) {
-    gemv_body<NR, CPL, S, RG, MULTI, MODE, kFmtNf4, STRIDED>(sg, K, x, P, (int64_t)blockIdx.x);
+    gemv_body<NR, CPL, S, RG, MULTI, MODE, kFmtNf4, STRIDED, TS>(sg, K, x, P, (int64_t)blockIdx.x);
 }
 
 namespace {
@@ -785,6 +841,19 @@ int cu_count() {
         cached[dev] = n;
     }
     return cached[dev];
+}
+
+// Whether every tile's run of scales starts on a dword, so that the
+// one-load-per-tile scale path may read whole dwords: the scale planes
+// dword-aligned and an even number of scales a row (a contiguous row range
+// may start at any row).  The path serves the one-tile-per-wave launches
+// only: measured on 11008 x 2048 4.62 against 4.80 us, while in the strided
+// order it was no faster (151936 x 2048 27.9-28.2 against 27.4-27.7 us,
+// 22016 x 2048 6.48-6.54 against 6.45-6.47, same run).
+bool scale_runs_aligned(const uint16_t *scales0, const uint16_t *scales1, int K) {
+    const bool planes = (reinterpret_cast<uintptr_t>(scales0) & 3) == 0 &&
+                        (reinterpret_cast<uintptr_t>(scales1) & 3) == 0;
+    return planes && (K / 64) % 2 == 0;  // K / 64 scales a row
 }
 
 template <int NR, int CPL, int S, int RG, bool MULTI, int FMT, bool STRIDED = false>
@@ -819,8 +888,11 @@ hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, const vo
     } else {
         (void)extra;
         void *args[] = {&codes, &scales, &M, &K, &x, &y, &P, &rows_q, &rows_rem};
-        return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_kernel<NR, CPL, S, RG, MULTI, STRIDED>),
-                               dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
+        const void *fn = reinterpret_cast<const void *>(&gemv_kernel<NR, CPL, S, RG, MULTI, STRIDED>);
+        if constexpr (!MULTI && CPL == 1 && S == 0 && NR <= 4)
+            if (scale_runs_aligned(scales, nullptr, K))
+                fn = reinterpret_cast<const void *>(&gemv_kernel<NR, CPL, S, RG, MULTI, STRIDED, true>);
+        return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
     }
 }
 
@@ -932,9 +1004,11 @@ hipError_t launch_fused_variant(GemvSegs segs, int K, const uint16_t *x, int P, 
     if (!MULTI && (K / 8 > P * G || K / 8 > kSharedXUnits)) return hipErrorInvalidValue;
     if (MODE == kModeSwiglu || segs.n == 1) {
         void *args[] = {&segs.s[0], &K, &x, &P};
-        return hipLaunchKernel(
-            reinterpret_cast<const void *>(&gemv_fused1_kernel<NR, CPL, S, RG, MULTI, MODE, STRIDED>),
-            dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
+        const void *fn = reinterpret_cast<const void *>(&gemv_fused1_kernel<NR, CPL, S, RG, MULTI, MODE, STRIDED>);
+        if constexpr (!MULTI && CPL == 1 && S == 0 && NR <= 4)
+            if (scale_runs_aligned(segs.s[0].scales0, segs.s[0].scales1, K))
+                fn = reinterpret_cast<const void *>(&gemv_fused1_kernel<NR, CPL, S, RG, MULTI, MODE, STRIDED, true>);
+        return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
     }
     if (STRIDED) return hipErrorInvalidValue;  // the strided order serves one matrix
     if constexpr (MODE != kModeSwiglu) {

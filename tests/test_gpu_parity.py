@@ -174,6 +174,61 @@ def test_gemv_parity_shapes(env, M, K):
     _check(y.cpu().numpy(), y_ref, S, f"gemv M={M} K={K}")
 
 
+def _scales_at(env, scales, shift):
+    """The scales on the device at a 2-byte offset of `shift` units from a
+    fresh (256-byte aligned) allocation: shift 1 leaves the plane 2 mod 4."""
+    torch, q4, dev = env
+    buf = torch.zeros(scales.size + shift, dtype=torch.float16, device=dev)
+    buf[shift:].copy_(torch.from_numpy(scales.reshape(-1).view(np.float16)))
+    return buf[shift:].view(scales.shape)
+
+
+# (M, K) with odd and even scale counts per row (K / 64), in the row ranges of
+# one tile per wave (at most 4096 four-row tiles) and in the strided order
+# (more): rows of one wave read a tile's scales with one dword load per lane
+# (handed on by quad broadcasts) when the plane is dword-aligned and a row
+# holds an even number of scales, else one 2-byte load per row; both are
+# checked on a dword-aligned and on a 2 mod 4 scale plane.
+SCALE_RUN_SHAPES = [(37, 64), (1001, 192), (257, 576), (130, 1984), (1001, 128), (300, 1024), (129, 2048),
+                    (16411, 64), (17003, 576), (16389, 1984), (20011, 2048)]
+
+
+@pytest.mark.parametrize("shift", [0, 1])
+@pytest.mark.parametrize("M,K", SCALE_RUN_SHAPES)
+def test_gemv_scale_runs_every_alignment(env, M, K, shift):
+    torch, q4, dev = env
+    seed = 2000 + M + K
+    W = wl.weights(M, K, seed)
+    x = wl.activation(K, seed, "unit_rms")
+    codes, scales, st = oracle.pack(W)
+    assert st == 0
+    y_ref, S = oracle.gemv(codes, scales, M, K, x)
+    c, _ = _upload_packed(env, codes, scales)
+    s = _scales_at(env, scales, shift)
+    assert s.data_ptr() % 4 == 2 * shift
+    y = q4.q4_gemv(c, s, _x_dev(env, x))
+    torch.cuda.synchronize()
+    _check(y.cpu().numpy(), y_ref, S, f"gemv M={M} K={K} scale plane +{2 * shift} B")
+
+
+# SwiGLU pairs as the halves of one packed matrix: with an odd number of
+# scales per row and an odd M the up half's plane is 2 mod 4.
+@pytest.mark.parametrize("M,K", [(1101, 576), (1100, 576), (1100, 1024), (9001, 192), (9000, 192), (9000, 2048)])
+def test_fused_swiglu_scale_plane_alignment(env, M, K):
+    torch, q4, dev = env
+    W = wl.weights(2 * M, K, 6500 + M)
+    x = wl.activation(K, 6500 + M, "unit_rms")
+    codes, scales, _ = oracle.pack(W)
+    t, S = oracle.gemv(codes, scales, 2 * M, K, x)
+    c, s = _upload_packed(env, codes, scales)
+    _log(f"swiglu M={M} K={K}: up scales at {s[M:].data_ptr() % 4} mod 4")
+    ops = [(c[:M], s[:M], None), (c[M:], s[M:], None)]
+    y = q4.q4_gemv_fused(ops, _x_dev(env, x), "swiglu")[0]
+    torch.cuda.synchronize()
+    y_ref, bound = _fused_ref([t[:M], t[M:]], [S[:M], S[M:]], [None, None], [None], True)
+    _check_bound(y.cpu().numpy(), y_ref[0], bound[0], f"swiglu halves M={M} K={K}")
+
+
 def test_gemv_after_gpu_pack_matches_oracle_chain(env):
     torch, q4, dev = env
     M, K = 700, 2048
