@@ -271,12 +271,12 @@ struct X8Args {
 // activations of that chunk (the same scaled fp16 values the dot uses), so
 // the zero point costs one load and two operations per chunk.
 //
-// TS (rows of one wave, one chunk a lane, NF4 scales on a dword-aligned plane
-// with an even number a row, as the host checks): a tile's scales are one
-// contiguous run per matrix (LPT rows of K/64 values, at most 256 bytes),
-// read with one dword load per lane and handed to the lanes that need them by
-// quad broadcasts (DPP): one load instruction per tile and matrix instead of
-// one 2-byte load per row.
+// TS (one chunk a lane, NF4 scales on a dword-aligned plane with an even
+// number a row, as the host checks): a tile's scales are one contiguous run
+// per matrix (LPT rows of K/64 values), read with one dword load per lane of
+// the group and handed to the lanes that need them by quad broadcasts (DPP,
+// inside each wave): one load instruction per tile and matrix instead of one
+// 2-byte load per row.
 template <int NR, int CPL, int S, int RG, bool MULTI, int MODE, int FMT = kFmtNf4, bool STRIDED = false,
           bool TS = false>
 __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16_t *__restrict__ x, int P,
@@ -293,7 +293,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
 
     static_assert(MODE != kModeSwiglu || NR % 2 == 0, "a SwiGLU tile pairs gate and up rows");
     constexpr int LPT = MODE == kModeSwiglu ? NR / 2 : NR;  // outputs per tile
-    static_assert(!TS || (!MULTI && CPL == 1 && S == 0 && FMT == kFmtNf4 && LPT <= 4),
+    static_assert(!TS || (CPL == 1 && S == 0 && FMT == kFmtNf4 && LPT <= 4),
                   "one scale run per tile and matrix");
     constexpr int NPART = MODE == kModeSwiglu ? 2 : 1;  // matrices a tile reads
     const int64_t rows_q = sg.rows_q;
@@ -352,14 +352,14 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         soff[i] = FMT == kFmtNvfp4 ? (uint32_t)c : (uint32_t)c >> 1;
     }
 
-    // TS: the four lanes of quad Q hold chunks 4Q .. 4Q+3, i.e. 64-blocks 2Q
+    // TS: the four lanes of quad Q of the group hold chunks 4Q .. 4Q+3, i.e. 64-blocks 2Q
     // and 2Q+1 of each row: the low and high halves of dword Q of the row's
     // scales.  Lane 4Q+r reads that dword of tile row r (rows r % LPT of each
     // matrix when LPT < 4), so row r's scales reach the quad by a broadcast of
     // its lane r.  Quads past the row's end read past every run (zeros).
     uint32_t ts_off = 0, ts_sh = 0;
     if constexpr (TS) {
-        const int quad = lane >> 2;
+        const int quad = lig >> 2;
         ts_off = quad < (C >> 2) ? (uint32_t)((((lane & 3) % LPT) * (nsb >> 1) + quad) * 4) : 0x40000000u;
         ts_sh = (uint32_t)((lane >> 1) & 1) << 4;
     }
@@ -889,7 +889,7 @@ hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, const vo
         (void)extra;
         void *args[] = {&codes, &scales, &M, &K, &x, &y, &P, &rows_q, &rows_rem};
         const void *fn = reinterpret_cast<const void *>(&gemv_kernel<NR, CPL, S, RG, MULTI, STRIDED>);
-        if constexpr (!MULTI && CPL == 1 && S == 0 && NR <= 4)
+        if constexpr (CPL == 1 && S == 0 && NR <= 4)
             if (scale_runs_aligned(scales, nullptr, K))
                 fn = reinterpret_cast<const void *>(&gemv_kernel<NR, CPL, S, RG, MULTI, STRIDED, true>);
         return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
@@ -1005,7 +1005,7 @@ hipError_t launch_fused_variant(GemvSegs segs, int K, const uint16_t *x, int P, 
     if (MODE == kModeSwiglu || segs.n == 1) {
         void *args[] = {&segs.s[0], &K, &x, &P};
         const void *fn = reinterpret_cast<const void *>(&gemv_fused1_kernel<NR, CPL, S, RG, MULTI, MODE, STRIDED>);
-        if constexpr (!MULTI && CPL == 1 && S == 0 && NR <= 4)
+        if constexpr (CPL == 1 && S == 0 && NR <= 4)
             if (scale_runs_aligned(segs.s[0].scales0, segs.s[0].scales1, K))
                 fn = reinterpret_cast<const void *>(&gemv_fused1_kernel<NR, CPL, S, RG, MULTI, MODE, STRIDED, true>);
         return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);

@@ -184,13 +184,16 @@ def _scales_at(env, scales, shift):
 
 
 # (M, K) with odd and even scale counts per row (K / 64), in the row ranges of
-# one tile per wave (at most 4096 four-row tiles) and in the strided order
-# (more): rows of one wave read a tile's scales with one dword load per lane
+# one tile per wave (at most 4096 four-row tiles), in the strided order
+# (more) and in rows spanning several waves: with one chunk a lane the
+# GEMV reads a tile's scales with one dword load per lane
 # (handed on by quad broadcasts) when the plane is dword-aligned and a row
 # holds an even number of scales, else one 2-byte load per row; both are
 # checked on a dword-aligned and on a 2 mod 4 scale plane.
 SCALE_RUN_SHAPES = [(37, 64), (1001, 192), (257, 576), (130, 1984), (1001, 128), (300, 1024), (129, 2048),
-                    (16411, 64), (17003, 576), (16389, 1984), (20011, 2048)]
+                    (16411, 64), (17003, 576), (16389, 1984), (20011, 2048),
+                    # rows spanning several waves (one chunk a lane)
+                    (2053, 11008), (517, 5120), (1001, 4224), (33, 6208), (3001, 2112)]
 
 
 @pytest.mark.parametrize("shift", [0, 1])
