@@ -271,12 +271,12 @@ struct X8Args {
 // activations of that chunk (the same scaled fp16 values the dot uses), so
 // the zero point costs one load and two operations per chunk.
 //
-// TS (one chunk a lane, NF4 scales on a dword-aligned plane with an even
-// number a row, as the host checks): a tile's scales are one contiguous run
-// per matrix (LPT rows of K/64 values), read with one dword load per lane of
-// the group and handed to the lanes that need them by quad broadcasts (DPP,
-// inside each wave): one load instruction per tile and matrix instead of one
-// 2-byte load per row.
+// TS (one chunk a lane, 16-bit scales (and zero points) on dword-aligned
+// planes with an even number a row, as the host checks): a tile's scales are
+// one contiguous run per matrix (LPT rows of K/64 values), read with one
+// dword load per lane of the group and handed to the lanes that need them by
+// quad broadcasts (DPP, inside each wave): one load instruction per tile and
+// plane instead of one 2-byte load per row.
 template <int NR, int CPL, int S, int RG, bool MULTI, int MODE, int FMT = kFmtNf4, bool STRIDED = false,
           bool TS = false>
 __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16_t *__restrict__ x, int P,
@@ -293,7 +293,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
 
     static_assert(MODE != kModeSwiglu || NR % 2 == 0, "a SwiGLU tile pairs gate and up rows");
     constexpr int LPT = MODE == kModeSwiglu ? NR / 2 : NR;  // outputs per tile
-    static_assert(!TS || (CPL == 1 && S == 0 && FMT == kFmtNf4 && LPT <= 4),
+    static_assert(!TS || (CPL == 1 && S == 0 && FMT != kFmtNvfp4 && LPT <= 4),
                   "one scale run per tile and matrix");
     constexpr int NPART = MODE == kModeSwiglu ? 2 : 1;  // matrices a tile reads
     const int64_t rows_q = sg.rows_q;
@@ -367,7 +367,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     uint4 q[S + 1][NR][CPL];
     uint32_t sc[TS ? 1 : S + 1][NR][CPL];
     uint32_t tsc[TS ? S + 1 : 1][NPART];  // TS: this lane's dword of each run
-    uint32_t zc[ZEROS ? S + 1 : 1][NR][CPL];  // zero-point bits (affine codes only)
+    uint32_t zc[ZEROS && !TS ? S + 1 : 1][NR][CPL];  // zero-point bits (affine codes only)
+    uint32_t tzc[ZEROS && TS ? S + 1 : 1];           // TS: this lane's dword of the zero points
     // Tiles are loaded in order.  The next tile to load starts at output
     // r_begin + LPT * (tiles loaded so far); its pointers advance by one tile
     // per load.  Rows past r_end repeat the last valid row (their results are
@@ -405,9 +406,13 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
             // The run of the tile's valid rows (whole dwords: an even number
             // of scales a row); lanes past it read zeros.
             const uint32_t run = (uint32_t)((real ? nvalid : 0) * nsb * 2);
-            if (r0 == 0)
+            if (r0 == 0) {
                 tsc[buf][0] = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(next_scales0, run), (int)ts_off, 0,
                                                                    kLoadNonTemporal);
+                if constexpr (ZEROS)
+                    tzc[buf] = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(next_zeros0, run), (int)ts_off, 0,
+                                                                    kLoadNonTemporal);
+            }
             if constexpr (MODE == kModeSwiglu)
                 if (r0 <= LPT && LPT < r1)
                     tsc[buf][NPART - 1] = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(next_scales1, run),
@@ -428,7 +433,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                 if constexpr (!TS)
                     sc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(up ? srs1 : srs0, (int)(soff[i] * 2),
                                                                           rr * sst * 2, kLoadNonTemporal);
-                if constexpr (ZEROS)
+                if constexpr (ZEROS && !TS)
                     zc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(zrs0, (int)(soff[i] * 2), rr * nsb * 2,
                                                                           kLoadNonTemporal);
             }
@@ -592,10 +597,13 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     auto step = [&](int buf, int j, int64_t t) {
         if (t < ntiles) {
             // TS: row r's scale dword, broadcast in each quad from its lane r % LPT.
-            uint32_t tsb[TS ? NR : 1];
+            uint32_t tsb[TS ? NR : 1], tzb[TS && ZEROS ? NR : 1];
             if constexpr (TS) {
 #pragma unroll
-                for (int r = 0; r < NR; ++r) tsb[r] = quad_bcast(tsc[buf][r < LPT ? 0 : NPART - 1], r % LPT);
+                for (int r = 0; r < NR; ++r) {
+                    tsb[r] = quad_bcast(tsc[buf][r < LPT ? 0 : NPART - 1], r % LPT);
+                    if constexpr (ZEROS) tzb[r] = quad_bcast(tzc[buf], r);
+                }
             }
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
@@ -621,10 +629,10 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                         }
                         // 16 sum (c - z) q = 16 sum (c - 8) q - 16 (z - 8) sum q:
                         // exact integers (|.| < 2^20; times 128 < 2^27).
-                        const int zi = (int)f16_bits_to_f32(zc[buf][r][i]) - 8;
+                        const int zi = (int)f16_bits_to_f32(TS ? tzb[r] >> ts_sh : zc[buf][r][i]) - 8;
                         int tot = 128 * (t1 - 16 * zi * qs1[i]);
                         if constexpr (X8TWO) tot += t2 - 16 * zi * qs2[i];
-                        a = fmaf((float)tot, f16_bits_to_f32(sc[buf][r][i]) * dsc[i], a);
+                        a = fmaf((float)tot, f16_bits_to_f32(TS ? tsb[r] >> ts_sh : sc[buf][r][i]) * dsc[i], a);
                     } else if constexpr (FMT == kFmtNvfp4) {
                         float p0, p1;
                         chunk_dot_halves(lut, q[buf][r][i], xh[i], laneoff, p0, p1);
@@ -633,7 +641,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                     } else {
                         float p = chunk_dot(lut, q[buf][r][i], xh[i], laneoff);
                         if constexpr (FMT == kFmtAffine)
-                            p = fmaf(8.0f - f16_bits_to_f32(zc[buf][r][i]), xsum[i], p);
+                            p = fmaf(8.0f - f16_bits_to_f32(TS ? tzb[r] >> ts_sh : zc[buf][r][i]), xsum[i], p);
                         const uint32_t sbits = TS ? tsb[r] >> ts_sh : sc[buf][r][i];
                         a = fmaf(p, f16_bits_to_f32(sbits), a);
                     }
@@ -749,9 +757,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
 }
 
 // The affine format's GEMV (y = W . x with W = (code - z) * s).
-template <int NR, int CPL, int S, int RG, bool MULTI, bool STRIDED = false>
+template <int NR, int CPL, int S, int RG, bool MULTI, bool STRIDED = false, bool TS = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
-                          amdgpu_waves_per_eu(gemv_min_waves(CPL), 8))) void gemv_affine_kernel(
+                          amdgpu_waves_per_eu(gemv_min_waves(CPL, TS), 8))) void gemv_affine_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     int64_t M, int K, const uint16_t *__restrict__ x, float *__restrict__ y, int P, int64_t rows_q, int rows_rem) {
     GemvSeg sg{};
@@ -762,7 +770,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
     sg.rows = M;
     sg.rows_q = rows_q;
     sg.rows_rem = rows_rem;
-    gemv_body<NR, CPL, S, RG, MULTI, kModePlain, kFmtAffine, STRIDED>(sg, K, x, P, (int64_t)blockIdx.x);
+    gemv_body<NR, CPL, S, RG, MULTI, kModePlain, kFmtAffine, STRIDED, TS>(sg, K, x, P, (int64_t)blockIdx.x);
 }
 
 // The NVFP4-style format's GEMV (y = s * sum E2M1 * E4M3 * x).
@@ -783,9 +791,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
 }
 
 // The affine format's GEMV on int8 activations (one or two words).
-template <int NR, int CPL, int S, int RG, bool MULTI, int FMT, bool STRIDED = false>
+template <int NR, int CPL, int S, int RG, bool MULTI, int FMT, bool STRIDED = false, bool TS = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
-                          amdgpu_waves_per_eu(gemv_min_waves(CPL), 8))) void gemv_affine_x8_kernel(
+                          amdgpu_waves_per_eu(gemv_min_waves(CPL, TS), 8))) void gemv_affine_x8_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     const int8_t *__restrict__ q1, const int8_t *__restrict__ q2, const float *__restrict__ d, int64_t M, int K,
     float *__restrict__ y, int P, int64_t rows_q, int rows_rem) {
@@ -800,7 +808,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
     sg.rows = M;
     sg.rows_q = rows_q;
     sg.rows_rem = rows_rem;
-    gemv_body<NR, CPL, S, RG, MULTI, kModePlain, FMT, STRIDED>(sg, K, nullptr, P, (int64_t)blockIdx.x);
+    gemv_body<NR, CPL, S, RG, MULTI, kModePlain, FMT, STRIDED, TS>(sg, K, nullptr, P, (int64_t)blockIdx.x);
 }
 
 // Several segments in one launch: workgroup b belongs to the last segment
@@ -844,9 +852,10 @@ int cu_count() {
 }
 
 // Whether every tile's run of scales starts on a dword, so that the
-// one-load-per-tile scale path may read whole dwords: the scale planes
-// dword-aligned and an even number of scales a row (a contiguous row range
-// may start at any row).  The path serves the one-tile-per-wave launches
+// one-load-per-tile scale path may read whole dwords: the scale planes (the
+// second is the up matrix's scales or the zero points, or null) dword-aligned
+// and an even number of scales a row (a contiguous row range may start at any
+// row).  The path serves the one-tile-per-wave launches
 // only: measured on 11008 x 2048 4.62 against 4.80 us, while in the strided
 // order it was no faster (151936 x 2048 27.9-28.2 against 27.4-27.7 us,
 // 22016 x 2048 6.48-6.54 against 6.45-6.47, same run).
@@ -870,16 +879,24 @@ hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, const vo
     if constexpr (FMT == kFmtAffine) {
         const uint16_t *zeros = static_cast<const uint16_t *>(extra);
         void *args[] = {&codes, &scales, &zeros, &M, &K, &x, &y, &P, &rows_q, &rows_rem};
-        return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_affine_kernel<NR, CPL, S, RG, MULTI, STRIDED>),
-                               dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
+        // (In the strided order the affine format's two planes were slower
+        // this way: lm_head 29.30 against 28.83 us; down 5.39 against 5.65.)
+        const void *fn = reinterpret_cast<const void *>(&gemv_affine_kernel<NR, CPL, S, RG, MULTI, STRIDED>);
+        if constexpr (CPL == 1 && S == 0 && NR <= 4 && !STRIDED)
+            if (scale_runs_aligned(scales, zeros, K))
+                fn = reinterpret_cast<const void *>(&gemv_affine_kernel<NR, CPL, S, RG, MULTI, STRIDED, true>);
+        return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
     } else if constexpr (FMT == kFmtAffineX8 || FMT == kFmtAffineX8x2) {
         const X8Args *xa = static_cast<const X8Args *>(extra);
         const uint16_t *zeros = xa->zeros;
         const int8_t *q1 = xa->q1, *q2 = xa->q2;
         const float *d = xa->d;
         void *args[] = {&codes, &scales, &zeros, &q1, &q2, &d, &M, &K, &y, &P, &rows_q, &rows_rem};
-        return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_affine_x8_kernel<NR, CPL, S, RG, MULTI, FMT, STRIDED>),
-                               dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
+        const void *fn = reinterpret_cast<const void *>(&gemv_affine_x8_kernel<NR, CPL, S, RG, MULTI, FMT, STRIDED>);
+        if constexpr (CPL == 1 && S == 0 && NR <= 4 && !STRIDED)
+            if (scale_runs_aligned(scales, zeros, K))
+                fn = reinterpret_cast<const void *>(&gemv_affine_x8_kernel<NR, CPL, S, RG, MULTI, FMT, STRIDED, true>);
+        return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
     } else if constexpr (FMT == kFmtNvfp4) {
         const float *tscale = static_cast<const float *>(extra);
         void *args[] = {&codes, &scales, &tscale, &M, &K, &x, &y, &P, &rows_q, &rows_rem};

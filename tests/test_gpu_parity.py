@@ -1137,6 +1137,34 @@ def test_affine_x8_gemv_parity(env, M, K, words):
     _check(y.cpu().numpy(), y_ref, S, f"affine x8 ({words} word) gemv M={M} K={K}")
 
 
+# The affine format reads a tile's scales and zero points with one dword load
+# each per lane when both planes are dword-aligned (an even number a row),
+# else one 2-byte load per row each; a 2 mod 4 zero-point plane takes the
+# second path, in every launch shape of one chunk a lane.
+@pytest.mark.parametrize("shift", [0, 1])
+@pytest.mark.parametrize("M,K", [(1001, 1024), (20011, 2048), (2053, 11008)])
+def test_affine_zero_point_plane_alignment(env, M, K, shift):
+    torch, q4, dev = env
+    seed = 9900 + M + K
+    W = wl.weights(M, K, seed, std=0.5) + np.float32(0.05)
+    x = wl.activation(K, seed, "normal")
+    codes, scales, zeros, st = oracle.pack_affine(W)
+    assert st == 0
+    c, s, _ = _affine_upload(env, codes, scales, zeros)
+    z = _scales_at(env, zeros, shift)
+    assert z.data_ptr() % 4 == 2 * shift
+    y_ref, S = oracle.gemv_affine(codes, scales, zeros, M, K, x)
+    y = q4.q4_gemv_affine(c, s, z, _x_dev(env, x))
+    torch.cuda.synchronize()
+    _check(y.cpu().numpy(), y_ref, S, f"affine gemv M={M} K={K} zeros +{2 * shift} B")
+    q1, q2, d = oracle.quantize_x8(x, 2)
+    y8_ref, S8 = oracle.gemv_affine_x8(codes, scales, zeros, M, K, q1, q2, d)
+    t1, t2, td = _x8_dev(env, q1, q2, d)
+    y8 = q4.q4_gemv_affine_x8(c, s, z, t1, t2, td)
+    torch.cuda.synchronize()
+    _check(y8.cpu().numpy(), y8_ref, S8, f"affine x8 gemv M={M} K={K} zeros +{2 * shift} B")
+
+
 def test_affine_x8_chain_full_size_down(env):
     """The down shape (2048 x 11008, SwiGLU-like x): GPU pack, GPU quantise
     and the GEMV against the oracle's pack, quantise and GEMV; the bf16
