@@ -939,8 +939,8 @@ int strided_waves(int64_t tiles) { return tiles <= one_tile_limit() ? 8 : 12; }
 
 // Workgroup shape of the one-tile-per-wave form for `tiles` row tiles: one
 // wave per tile, in one workgroup per CU while that takes at most 12 waves,
-// else two; at least enough threads for the workgroup's copy of the
-// activations (one 16-byte unit per thread).  Measured on 11008 x 2048 and
+// else two; at least 4 waves and enough threads for the workgroup's copy of
+// the activations (one 16-byte unit per thread).  Measured on 11008 x 2048 and
 // 22016 x 2048: 4.7 and 7.0 us against 5.2 and 7.2 us for 8-wave workgroups
 // at two per CU, which leave a third of the waves two tiles in sequence
 // (11008 rows: 344 workgroups, two on some CUs and one on others).
@@ -952,7 +952,11 @@ OneTileShape one_tile_shape(int64_t tiles, int K) {
     const int64_t cus = cu_count();
     const int64_t per_cu = tiles <= 12 * cus ? 1 : 2;
     int64_t G = (tiles + per_cu * cus - 1) / (per_cu * cus);
-    const int64_t gmin = (K / 8 + 63) / 64;
+    // At least 4 waves a workgroup: each workgroup fills the whole 64 KB
+    // table, and one or two waves alone take longer to fill it than the rest
+    // of a small launch (256 x 512: 4.61 us with 1 wave, 3.78 with 2, 3.58
+    // with 4; 1024 x 1024: 3.85 with 2, 3.66 with 4; lab, same run).
+    const int64_t gmin = (K / 8 + 63) / 64 > 4 ? (K / 8 + 63) / 64 : 4;
     if (G < gmin) G = gmin;
     if (G < 1) G = 1;
     if (G > 16) G = 16;
@@ -978,6 +982,11 @@ OneTileShape multi_shape(int64_t tiles, int wpg) {
     int64_t G = gmax / per_cu;
     const int64_t need = (tiles + per_cu * cus - 1) / (per_cu * cus);
     if (G > need) G = need;
+    // ... but at least 4 waves a workgroup, which share the table fill
+    // (1024 x 4096: 4.22 -> 3.98 us, 300 x 4096: 4.14 -> 3.91 with two groups
+    // of 2 waves instead of one; lab, same run).
+    const int64_t gmin = (4 + wpg - 1) / wpg;
+    if (G < gmin) G = gmin < gmax ? gmin : gmax;
     if (G < 1) G = 1;
     return {(int)G, per_cu * cus};
 }
