@@ -434,6 +434,7 @@ hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int6
     // sharing each lookup among 2..4 tokens measured slower than the
     // matrix-core kernel (7.5 and 11.1 us at N = 2 and 4).
     if (N == 1) return launch_gemv(codes, scales, M, K, X, Y, stream);
+    if (gemv_tokens_fits(M, K, N)) return launch_gemv_tokens(codes, scales, M, K, X, N, Y, stream);
     static int cus[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;

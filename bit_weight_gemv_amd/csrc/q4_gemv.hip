@@ -73,6 +73,28 @@ __device__ __forceinline__ float chunk_dot(const uint32_t *lut, uint4 q, const h
     return p;
 }
 
+// The chunk's weights against NTOK tokens' activations: each table lookup
+// serves every token.
+template <int NTOK>
+__device__ __forceinline__ void chunk_dot_n(const uint32_t *lut, uint4 q, const half2_t (&xh)[NTOK][1][16],
+                                            uint32_t laneoff, float (&p)[NTOK]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) p[t] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        half2_t v[4];
+        v[0] = lut_pair<0>(lut, w[d], laneoff);
+        v[1] = lut_pair<1>(lut, w[d], laneoff);
+        v[2] = lut_pair<2>(lut, w[d], laneoff);
+        v[3] = lut_pair<3>(lut, w[d], laneoff);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int t = 0; t < NTOK; ++t) p[t] = __builtin_amdgcn_fdot2(v[b], xh[t][0][4 * d + b], p[t], false);
+    }
+}
+
 // The same dot split at the chunk's middle: p0 over its first 16 weights
 // (bytes 0..7), p1 over the last 16, for formats with a scale per 16 weights.
 __device__ __forceinline__ void chunk_dot_halves(const uint32_t *lut, uint4 q, const half2_t *xh,
@@ -277,8 +299,12 @@ struct X8Args {
 // dword load per lane of the group and handed to the lanes that need them by
 // quad broadcasts (DPP, inside each wave): one load instruction per tile and
 // plane instead of one 2-byte load per row.
+//
+// NTOK > 1 (rows of one wave, one tile per wave, plain NF4): x is NTOK
+// tokens, [NTOK][K] bf16, and y is [NTOK][rows]; every table lookup serves
+// all tokens (a prefill chunk of 2 or 3 tokens).
 template <int NR, int CPL, int S, int RG, bool MULTI, int MODE, int FMT = kFmtNf4, bool STRIDED = false,
-          bool TS = false>
+          bool TS = false, int NTOK = 1>
 __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16_t *__restrict__ x, int P,
                                           int64_t wg) {
     constexpr bool X8 = FMT == kFmtAffineX8 || FMT == kFmtAffineX8x2;
@@ -289,7 +315,9 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     // Groups of one wave all need the whole activation vector: it is read
     // from global memory once per workgroup into LDS (raw bf16, 16 bytes per
     // lane) and every wave takes its chunks from there.
-    __shared__ uint4 xs[(MULTI || X8) ? 1 : kSharedXUnits];
+    __shared__ uint4 xs[(MULTI || X8) ? 1 : kSharedXUnits * NTOK];
+    static_assert(NTOK == 1 || (!MULTI && MODE == kModePlain && FMT == kFmtNf4 && CPL == 1 && S == 0),
+                  "several tokens: rows of one wave, plain NF4, one chunk a lane");
 
     static_assert(MODE != kModeSwiglu || NR % 2 == 0, "a SwiGLU tile pairs gate and up rows");
     constexpr int LPT = MODE == kModeSwiglu ? NR / 2 : NR;  // outputs per tile
@@ -465,14 +493,17 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     // zero-record resources (no memory access), and no branch makes the
     // compiler's wait analysis assume the tile loads might be missing.
     uint32_t xraw[16];
-    u32x4_t xunit;  // this lane's 16 bytes of the shared activation copy
+    u32x4_t xunit[NTOK];  // this lane's 16 bytes of the shared activation copy, per token
     const int xunits = K >> 3;
     if constexpr (!X8) {
         if (MULTI) {
             if (CPL == 1) load_chunk_x(x, cidx[0], cvalid[0], xraw);
         } else {
             // Bytes past the vector's end read as zero (buffer bounds).
-            xunit = __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(x, (uint32_t)K * 2u), (int)threadIdx.x * 16, 0, 0);
+#pragma unroll
+            for (int t = 0; t < NTOK; ++t)
+                xunit[t] = __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(x, (uint32_t)K * 2u * NTOK),
+                                                                 t * K * 2 + (int)threadIdx.x * 16, 0, 0);
         }
     }
     // int8-activation forms: each lane reads the 32 words (and the block
@@ -508,8 +539,11 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         fill_lut_from(lut, kE2m1PairTable);
     else if constexpr (!X8)
         fill_lut(lut);
-    half2_t xh[X8 ? 1 : CPL][16];
-    float down = 1.0f;
+    half2_t xhn[NTOK][X8 ? 1 : CPL][16];
+    float downn[NTOK];
+    auto &xh = xhn[0];
+    float &down = downn[0];
+    down = 1.0f;
     if constexpr (X8) {
         // (no table and no shared activation copy to wait for)
     } else if constexpr (MULTI) {
@@ -517,7 +551,10 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                                     xraw, xh);
         __syncthreads();
     } else {
-        if ((int)threadIdx.x < xunits) xs[threadIdx.x] = make_uint4(xunit.x, xunit.y, xunit.z, xunit.w);
+        if ((int)threadIdx.x < xunits)
+#pragma unroll
+            for (int t = 0; t < NTOK; ++t)
+                xs[t * xunits + threadIdx.x] = make_uint4(xunit[t].x, xunit[t].y, xunit[t].z, xunit[t].w);
         __syncthreads();
     }
     load_rows(0, PRE, NR);
@@ -525,8 +562,11 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
 #pragma unroll
     for (int s = 1; s <= S; ++s) load_tile(s);
     if constexpr (!X8 && !MULTI)
-        down = convert_x<CPL, false>(
-            [&](int i, uint32_t(&r)[16]) { load_chunk_x_lds(xs, cidx[i], cvalid[i], r); }, xraw, xh);
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t)
+            downn[t] = convert_x<CPL, false>(
+                [&](int i, uint32_t(&r)[16]) { load_chunk_x_lds(xs + t * xunits, cidx[i], cvalid[i], r); }, xraw,
+                xhn[t]);
 
     // int8-activation forms: the words regrouped to match the code nibbles
     // (code dword d holds weights 8d .. 8d+7, even ones in the low nibbles):
@@ -593,7 +633,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     // with tile t + S + 1 (unconditionally; past the end it reads nothing).
     constexpr int TPG = RG / NR;  // tiles per reduction group
     static_assert(RG % NR == 0 && TPG % (S + 1) == 0, "group must hold whole ring turns");
-    float acc[RG];
+    float accn[NTOK][RG];
+    auto &acc = accn[0];
     auto step = [&](int buf, int j, int64_t t) {
         if (t < ntiles) {
             // TS: row r's scale dword, broadcast in each quad from its lane r % LPT.
@@ -638,6 +679,13 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                         chunk_dot_halves(lut, q[buf][r][i], xh[i], laneoff, p0, p1);
                         a = fmaf(p0, e4m3_to_f32(sc[buf][r][i]), a);
                         a = fmaf(p1, e4m3_to_f32(sc[buf][r][i] >> 8), a);
+                    } else if constexpr (NTOK > 1) {
+                        float pn[NTOK];
+                        chunk_dot_n<NTOK>(lut, q[buf][r][i], xhn, laneoff, pn);
+                        const float sf = f16_bits_to_f32(TS ? tsb[r] >> ts_sh : sc[buf][r][i]);
+#pragma unroll
+                        for (int t = 1; t < NTOK; ++t) accn[t][j * NR + r] = pn[t] * sf;
+                        a = fmaf(pn[0], sf, a);
                     } else {
                         float p = chunk_dot(lut, q[buf][r][i], xh[i], laneoff);
                         if constexpr (FMT == kFmtAffine)
@@ -650,7 +698,9 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
             }
         } else {
 #pragma unroll
-            for (int r = 0; r < NR; ++r) acc[j * NR + r] = 0.0f;
+            for (int t = 0; t < NTOK; ++t)
+#pragma unroll
+                for (int r = 0; r < NR; ++r) accn[t][j * NR + r] = 0.0f;
         }
         load_tile(buf);  // tile t + S + 1
     };
@@ -690,7 +740,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
 
     // Store of a reduction group whose first tile is g0; lane l holds the
     // finished sum of group row l (l < RG).  Every lane of the wave calls it.
-    auto store = [&](float tot, int64_t g0, const Epi &e) {
+    auto store = [&](float tot, int64_t g0, const Epi &e, int tok = 0) {
         if constexpr (MODE == kModeSwiglu) {
             // Output o of the group: tile o / LPT, gate row o % LPT of it and
             // the up row LPT after.
@@ -712,7 +762,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                 float v = tot;
                 if (MODE == kModeEpi && sg.bias0) v += e.b0;
                 if (MODE == kModeEpi && sg.residual) v += e.r;
-                sg.y[row] = v;
+                sg.y[tok * sg.rows + row] = v;
             }
         }
     };
@@ -725,6 +775,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         const float tot = reduce_rows<RG>(acc) * down;
         if (!MULTI) {
             store(tot, g0, epi);
+#pragma unroll
+            for (int t = 1; t < NTOK; ++t) store(reduce_rows<RG>(accn[t]) * downn[t], g0, epi, t);
         } else {
             if (lane < RG) red[wave][lane] = tot;
             __syncthreads();
@@ -754,6 +806,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
     sg.rows_q = rows_q;
     sg.rows_rem = rows_rem;
     gemv_body<NR, CPL, S, RG, MULTI, kModePlain, kFmtNf4, STRIDED, TS>(sg, K, x, P, (int64_t)blockIdx.x);
+}
+
+// A prefill chunk of NTOK = 2 or 3 tokens on rows of one wave: Y [NTOK][M] =
+// W . X^T with X [NTOK][K] bf16, one 4-row tile per wave.
+template <int NTOK, bool TS>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 768), amdgpu_waves_per_eu(3, 8))) void gemv_tokens_kernel(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, int64_t M, int K,
+    const uint16_t *__restrict__ X, float *__restrict__ Y, int P, int64_t rows_q, int rows_rem) {
+    GemvSeg sg{};
+    sg.codes0 = codes;
+    sg.scales0 = scales;
+    sg.y = Y;
+    sg.rows = M;
+    sg.rows_q = rows_q;
+    sg.rows_rem = rows_rem;
+    gemv_body<4, 1, 0, 4, false, kModePlain, kFmtNf4, false, TS, NTOK>(sg, K, X, P, (int64_t)blockIdx.x);
 }
 
 // The affine format's GEMV (y = W . x with W = (code - z) * s).
@@ -1166,6 +1234,40 @@ hipError_t launch_gemv_fmt(const uint8_t *codes, const uint16_t *scales, const v
         default:
             return launch_variant<1, 8, 0, 2, true, FMT>(codes, scales, extra, M, k, x, y, P, 1, gemv_grid(M, 1), stream);
     }
+}
+
+// Chunks of 2 or 3 tokens on rows of one wave, in one workgroup of at most
+// 12 waves per CU (the table and the activations take up to 88 KB of LDS;
+// a wave holds 16 VGPRs of activations per token; 4 tokens spill).
+bool gemv_tokens_fits(int64_t M, int64_t K, int64_t N) {
+    return N >= 2 && N <= 3 && K <= 64 * kChunkWeights && (M + 3) / 4 <= 12LL * cu_count();
+}
+
+namespace {
+template <int NTOK>
+const void *gemv_tokens_fn(bool ts) {
+    return ts ? reinterpret_cast<const void *>(&gemv_tokens_kernel<NTOK, true>)
+              : reinterpret_cast<const void *>(&gemv_tokens_kernel<NTOK, false>);
+}
+}  // namespace
+
+hipError_t launch_gemv_tokens(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                              const uint16_t *X, int64_t N, float *Y, hipStream_t stream) {
+    if (!gemv_tokens_fits(M, K, N)) return hipErrorInvalidValue;
+    int k = (int)K;
+    const int64_t tiles4 = (M + 3) / 4;
+    const OneTileShape sh = one_tile_shape(tiles4, k);
+    int64_t grid = (tiles4 + sh.G - 1) / sh.G;
+    if (grid > sh.cap) grid = sh.cap;
+    int P = 64;
+    if (k / 8 > P * sh.G || sh.G > 12) return hipErrorInvalidValue;  // at most 768 threads
+    const int64_t ngroups = grid * sh.G;
+    int64_t rows_q = M / ngroups;
+    int rows_rem = (int)(M % ngroups);
+    const bool ts = scale_runs_aligned(scales, nullptr, k);
+    const void *fn = N == 2 ? gemv_tokens_fn<2>(ts) : gemv_tokens_fn<3>(ts);
+    void *args[] = {&codes, &scales, &M, &k, &X, &Y, &P, &rows_q, &rows_rem};
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)(P * sh.G)), args, 0, stream);
 }
 
 hipError_t launch_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K, const uint16_t *x,

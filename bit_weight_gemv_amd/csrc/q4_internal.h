@@ -9,6 +9,11 @@ namespace q4 {
 hipError_t launch_pack(const float *W, int64_t M, int64_t K, uint8_t *codes, uint16_t *scales,
                        int32_t *status, hipStream_t stream);
 
+// A chunk of 2 or 3 tokens on short rows (K <= 2048, at most 12 four-row
+// tiles per CU): the GEMV with every table lookup serving all tokens.
+bool gemv_tokens_fits(int64_t M, int64_t K, int64_t N);
+hipError_t launch_gemv_tokens(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                              const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
 hipError_t launch_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                        const uint16_t *x, float *y, hipStream_t stream);
 

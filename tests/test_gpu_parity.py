@@ -429,7 +429,11 @@ GEMM_SHAPES = [(1, 64, 1), (40, 128, 2), (100, 512, 3), (64, 2048, 4), (97, 1024
                (300, 1600, 20), (50, 2112, 32), (20000, 256, 9), (20000, 192, 32),
                (40000, 64, 5), (40000, 128, 24),
                # one token takes the GEMV kernels (short and long rows)
-               (7, 2048, 1), (3000, 2112, 1), (600, 11008, 1)]
+               (7, 2048, 1), (3000, 2112, 1), (600, 11008, 1),
+               # two or three tokens on short rows take the GEMV with shared
+               # lookups (up to 12 four-row tiles per CU), beyond that the
+               # matrix-core kernel
+               (11008, 2048, 2), (3001, 1984, 3), (5, 64, 2), (1001, 576, 3), (12289, 2048, 3)]
 
 
 @pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
