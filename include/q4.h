@@ -135,7 +135,10 @@ int q4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
  *   X: bf16 bit patterns [N][K] row-major, 16-byte aligned.
  *   Y: fp32 [N][M] row-major, 4-byte aligned; must not overlap the inputs.
  * Same accuracy statement as q4_gemv.  A chunk of one token is computed by
- * the q4_gemv kernels (Y[0] is then bit-identical to q4_gemv of X[0]).
+ * the q4_gemv kernels (Y[0] is then bit-identical to q4_gemv of X[0]);
+ * chunks of two or three tokens on rows of at most 2048 weights (and at most
+ * 12 four-row tiles per compute unit) by the same kernels with each table
+ * lookup serving every token.
  */
 int q4_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M,
                    int64_t K, const uint16_t *X, int64_t N, float *Y,
