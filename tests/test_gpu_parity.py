@@ -546,10 +546,13 @@ def test_graph_capture_replays_match_eager(env):
     c, s = _upload_packed(env, codes, scales)
     x = _x_dev(env, wl.activation(K, 51, "unit_rms"))
     X = cases.to_dev(wl.activations(N, K, 51, "normal").view(np.int16), torch, dev).view(torch.bfloat16)
+    X2 = X[:2].contiguous()  # two tokens: the GEMV with shared lookups
     y_eager = q4.q4_gemv(c, s, x).clone()
     Y_eager = q4.q4_gemm_smalln(c, s, X).clone()
+    Y2_eager = q4.q4_gemm_smalln(c, s, X2).clone()
     y = torch.full((M,), float("nan"), device=dev)
     Y = torch.full((N, M), float("nan"), device=dev)
+    Y2 = torch.full((2, M), float("nan"), device=dev)
     g = torch.cuda.CUDAGraph()
     st = torch.cuda.Stream()
     st.wait_stream(torch.cuda.current_stream())
@@ -558,15 +561,18 @@ def test_graph_capture_replays_match_eager(env):
         with torch.cuda.graph(g, stream=st):
             q4.q4_gemv(c, s, x, y, stream=st)
             q4.q4_gemm_smalln(c, s, X, Y, stream=st)
+            q4.q4_gemm_smalln(c, s, X2, Y2, stream=st)
     torch.cuda.synchronize()
     for rep in range(4):
         y.fill_(float("nan"))
         Y.fill_(float("nan"))
+        Y2.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, y_eager), f"gemv replay {rep} differs from eager"
         assert torch.equal(Y, Y_eager), f"gemm replay {rep} differs from eager"
+        assert torch.equal(Y2, Y2_eager), f"two-token gemm replay {rep} differs from eager"
         # eager work in between replays
         q4.q4_gemv(c, s, x)
         torch.cuda.synchronize()
