@@ -923,10 +923,16 @@ int cu_count() {
 // one-load-per-tile scale path may read whole dwords: the scale planes (the
 // second is the up matrix's scales or the zero points, or null) dword-aligned
 // and an even number of scales a row (a contiguous row range may start at any
-// row).  The path serves the one-tile-per-wave launches
-// only: measured on 11008 x 2048 4.62 against 4.80 us, while in the strided
-// order it was no faster (151936 x 2048 27.9-28.2 against 27.4-27.7 us,
-// 22016 x 2048 6.48-6.54 against 6.45-6.47, same run).
+// row).  Every NF4 launch with one chunk a lane takes the path when this
+// holds (one tile per wave, the strided order, rows spanning several waves,
+// the fused form of one matrix or a SwiGLU pair); the affine forms take it
+// outside the strided order, and
+// the NVFP4-style format (two scale bytes a chunk) never.  Measured against the
+// 2-byte loads (lab, same run): 151936 x 2048 27.29-27.38 against
+// 27.54-27.62 us, 22016 x 2048 6.24-6.29 against 6.50-6.58, 11008 x 2048
+// 4.56-4.60 against 4.78-4.83, 2048 x 11008 4.98 against 5.17.  The affine
+// format keeps the 2-byte loads in the strided order, where its two planes
+// read this way were slower (151936 x 2048 29.30 against 28.83 us).
 bool scale_runs_aligned(const uint16_t *scales0, const uint16_t *scales1, int K) {
     const bool planes = (reinterpret_cast<uintptr_t>(scales0) & 3) == 0 &&
                         (reinterpret_cast<uintptr_t>(scales1) & 3) == 0;

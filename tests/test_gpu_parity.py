@@ -142,11 +142,10 @@ def test_pack_flags_and_valid_blocks(env):
 # ---------------------------------------------------------------------------
 
 # (M, K): several tiles and ragged tails for every launch shape:
-#   K <= 2048 (a wave per row), K <= 4096 (two chunks a lane),
-#   longer rows (a workgroup per row tile; 1, 2, 4, 8 chunks a lane).
-# With 256 CUs the single-tile forms serve up to 32768 rows (K <= 2048) and
-# 4096 rows (longer rows); the shapes just past those bounds take the
-# two-tile ring.
+#   K <= 2048: a wave per row, one 4-row tile per wave up to 16 tiles per CU
+#     (16384 rows with 256 CUs), tiles dealt to the waves in turn beyond;
+#   K <= 32768: a group of waves per row tile, one chunk a lane;
+#   longer rows: 4 chunks a lane (K <= 65536), else 8.
 GEMV_SHAPES = [(1, 64), (2, 64), (7, 128), (257, 512), (1000, 1024), (4097, 2048), (31, 1984),
                (32771, 192), (40001, 64),
                (300, 2112), (65, 4096), (129, 4160), (2048, 11008), (33, 11008), (9, 16384),
