@@ -511,24 +511,51 @@ def empty_kernel_us(torch, dev, steps, warmup):
     return ms * 1e3
 
 
-def cpu_model():
-    """The host CPU's model name, from /proc/cpuinfo."""
+def cpu_info():
+    """The host CPU as /proc/cpuinfo describes it: the model string plus the
+    vendor, family / model / stepping numbers, clock and cache fields (a
+    virtualised host may print a short model string), and the CPU counts."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if fields:
+                        break  # the first processor's block is enough
+                    continue
+                k, v = (t.strip() for t in line.split(":", 1))
+                if k in ("model name", "vendor_id", "cpu family", "model", "stepping", "cpu MHz",
+                         "cache size", "siblings", "cpu cores") and k not in fields:
+                    fields[k] = v
     except OSError:
         pass
-    return None
+    desc = fields.get("model name")
+    extra = ", ".join(f"{k} {fields[k]}" for k in ("vendor_id", "cpu family", "model", "stepping",
+                                                    "cpu MHz", "cache size") if k in fields)
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"cpu_model": desc, "cpu_detail": extra or None, "host_logical_cpus": os.cpu_count(),
+            "affinity_cpus": affinity}
+
+
+def cpu_threads():
+    """Threads for the oracle: every CPU this process may run on, or the
+    CPU share the environment grants when OMP_NUM_THREADS names a smaller one
+    (on a shared GPU host that is the share of one GPU)."""
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and 0 < int(share) < aff:
+        return int(share), f"OMP_NUM_THREADS={share} (the CPU share granted to this process)"
+    return aff, "every CPU in the process's affinity mask"
 
 
 def cpu_baseline(oracle, wl, W, xb, name):
     """The oracle's fp64 GEMV over the whole matrix on the host cores, as it
-    stands: rows split over threads, repeated until ~10 s have passed."""
+    stands: rows split over T threads (T = the CPUs granted to the process),
+    repeated for about 10 s, median; and the same call on one thread, median
+    of three (identical sums: rows are only split)."""
     c = wl.CONFIGS[name]
     M, K = c["M"], c["K"]
-    threads = min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count() or 1)
+    threads, why = cpu_threads()
     codes, scales, st = oracle.pack(W, threads=threads)
     assert st == 0
     times = []
@@ -541,24 +568,26 @@ def cpu_baseline(oracle, wl, W, xb, name):
         if time.time() - t_start > 10.0 or len(times) >= 400:
             break
     sec = float(np.median(times))
-    # The same call on one thread (identical sums: rows are only split),
-    # median of three.
     t1 = []
     for _ in range(3):
         t = time.perf_counter()
         oracle.gemv(codes, scales, M, K, xb, threads=1)
         t1.append(time.perf_counter() - t)
-    return {
+    sec1 = float(np.median(t1))
+    out = {
         "value": round(gemv_bytes(M, K) / sec / 1e9, 3),
         "unit": "GB/s",
         "us_per_call": round(sec * 1e6, 1),
-        "us_per_call_1_thread": round(float(np.median(t1)) * 1e6, 1),
         "cores": threads,
-        "cpu_model": cpu_model(),
+        "threads_rule": why,
+        "value_1_thread": round(gemv_bytes(M, K) / sec1 / 1e9, 4),
+        "us_per_call_1_thread": round(sec1 * 1e6, 1),
         "kind": "oracle",
         "sample": f"full {name} GEMV {M}x{K} (fp64 oracle, rows split over {threads} threads), "
-                  f"{len(times)} calls in {time.time() - t_start:.1f}s, median",
-    }, y_ref, S
+                  f"{len(times)} calls in {time.time() - t_start:.1f}s, median; one thread: median of 3",
+    }
+    out.update(cpu_info())
+    return out, y_ref, S
 
 
 def main():

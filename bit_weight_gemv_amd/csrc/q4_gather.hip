@@ -34,8 +34,6 @@
 
 namespace q4 {
 
-constexpr int kGatherThreads = 256;
-
 __device__ __forceinline__ uint32_t bf16_of_product(float c, float s) {
     const float p = c * s;
     const float r = fmaf(c, s, -p);  // exact: c * s - p
@@ -111,11 +109,6 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
         v.w = lv[(q >> 12) & 0xF] * s;
         *reinterpret_cast<float4 *>(static_cast<float *>(out) + i * (int64_t)K + k0) = v;
     }
-}
-
-int64_t gather_blocks_per_row(int64_t K, bool bf16) {
-    const int64_t units = K / (bf16 ? 8 : 4);
-    return (units + kGatherThreads - 1) / kGatherThreads;
 }
 
 hipError_t launch_gather_rows(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,

@@ -59,7 +59,13 @@ hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int6
 hipError_t launch_gather_rows(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                               const int32_t *ids, int64_t n, bool bf16, void *out, int32_t *status,
                               hipStream_t stream);
-// Workgroups one output row takes (the grid is n times this).
-int64_t gather_blocks_per_row(int64_t K, bool bf16);
+// Workgroups one output row takes (the grid is n times this): one lane per
+// 16-byte output vector (4 fp32 or 8 bf16 values), kGatherThreads lanes a
+// workgroup.
+constexpr int kGatherThreads = 256;
+inline int64_t gather_blocks_per_row(int64_t K, bool bf16) {
+    const int64_t units = K / (bf16 ? 8 : 4);
+    return (units + kGatherThreads - 1) / kGatherThreads;
+}
 
 }  // namespace q4
