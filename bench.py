@@ -501,6 +501,41 @@ def code_plane_copy_us(torch, reps, steps, warmup):
     return ms * 1e3
 
 
+_FLOOR_LIB = None
+FLOOR_GRIDS = ((256, 256), (512, 256), (1024, 256), (2048, 256), (4096, 256), (1024, 512), (2048, 512))
+
+
+def read_floor_us(torch, reps, steps, warmup):
+    """The plain streaming read of the same bytes (each copy's code plane and
+    scale plane once, no arithmetic; libq4floor.so, a reference kernel kept
+    out of libq4), graph-replayed over the same rotating copies; the best of
+    a sweep of grid shapes.  Returns (microseconds per call, grid, block)."""
+    import ctypes
+    global _FLOOR_LIB
+    if _FLOOR_LIB is None:
+        from bit_weight_gemv_amd import build as b
+        if not os.path.exists(b.FLOOR_LIB):
+            raise RuntimeError("libq4floor.so not built; run python -m bit_weight_gemv_amd.build")
+        L = ctypes.CDLL(b.FLOOR_LIB)
+        L.q4floor_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
+                                   ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.q4floor_read.restype = ctypes.c_int
+        _FLOOR_LIB = L
+    out = torch.zeros(256, dtype=torch.int32, device=reps[0][0].device)
+    best = None
+    for grid, block in FLOOR_GRIDS:
+        def rd(cd, sl, grid=grid, block=block):
+            rc = _FLOOR_LIB.q4floor_read(cd.data_ptr(), cd.numel() * cd.element_size(), sl.data_ptr(),
+                                         sl.numel() * sl.element_size(), out.data_ptr(), grid, block,
+                                         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"q4floor_read returned {rc}")
+        ms, _ = time_graph(torch, rd, reps, steps, warmup)
+        if best is None or ms < best[0]:
+            best = (ms, grid, block)
+    return best[0] * 1e3, best[1], best[2]
+
+
 def empty_kernel_us(torch, dev, steps, warmup):
     """Launch floor: one one-element torch kernel per call, graph-replayed."""
     t = torch.zeros(1, device=dev)
@@ -658,8 +693,12 @@ def main():
     y_gpu = y.cpu().numpy()
     floors = None
     if not args.no_secondary:
+        rf_us, rf_grid, rf_block = read_floor_us(torch, reps, args.steps, args.warmup)
         floors = {"empty_kernel_us": round(empty_kernel_us(torch, dev, args.steps, args.warmup), 3),
-                  "lm_head_code_plane_copy_us": round(code_plane_copy_us(torch, reps, args.steps, args.warmup), 3)}
+                  "lm_head_code_plane_copy_us": round(code_plane_copy_us(torch, reps, args.steps, args.warmup), 3),
+                  "lm_head_read_floor_us": round(rf_us, 3),
+                  "lm_head_read_floor_grid": f"{rf_grid}x{rf_block}",
+                  "lm_head_gemv_over_read_floor": round(k_mean_ms * 1e3 / rf_us, 4)}
         log(f"floors: {floors}")
 
     secondary = []
@@ -689,6 +728,11 @@ def main():
             sg, sw = time_graph(torch, sstep, sreps, args.steps, args.warmup)
             secondary.append(secondary_entry(sname, sc, N, sg, sw))
             secondary[-1]["code_plane_copy_us"] = round(code_plane_copy_us(torch, sreps, args.steps, args.warmup), 3)
+            rf_us, rf_grid, rf_block = read_floor_us(torch, sreps, args.steps, args.warmup)
+            secondary[-1]["read_floor_us"] = round(rf_us, 3)
+            secondary[-1]["read_floor_grid"] = f"{rf_grid}x{rf_block}"
+            secondary[-1]["over_read_floor"] = round(sg * 1e3 / rf_us, 4)
+            log(f"{sname}: read floor {rf_us:.2f} us ({rf_grid}x{rf_block})")
             if ntok is not None:
                 # The prefill sweep: the first n tokens of the same chunk.
                 for n in (16, 8, 4, 2, 1):
@@ -728,7 +772,11 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
-        "dtype_note": "4-bit codes, fp16 table x fp16-converted bf16 x via v_dot2_f32_f16, fp32 accumulate",
+        "dtype_note": "fp16 table, fp32 accumulate: 4-bit codes; levels held as fp16 (rounded by at most "
+                      "2^-11 relative); bf16 x converted exactly to fp16 under a power of two (or widened to "
+                      "fp32 when a wave's activations span more than 2^31); products exact in "
+                      "v_dot2_f32_f16; sums in fp32. A reading of the page's 'FP32 LUT x scale x x' that "
+                      "stays inside the acceptance bound by proof",
         "data": "synthetic (seeded SplitMix64 normals; W ~ N(0, 0.02^2), x unit-RMS bf16)",
         "config": {"workload": "lm_head GEMV 151936x2048, N=1", "M": M, "K": K, "N": 1,
                    "copies_rotated": args.copies, "bytes_per_call": nbytes},
@@ -752,8 +800,10 @@ def main():
             "floors": floors,
             "floors_how": "empty_kernel_us: a one-element torch kernel per call (the launch floor); "
                           "*code_plane_copy_us (also per secondary workload): torch's device copy of the "
-                          "same code plane (its bytes read and written once each); both graph-replayed "
-                          "over the same rotating copies"}
+                          "same code plane (its bytes read and written once each); *read_floor_us (also "
+                          "per secondary workload): libq4floor.so's plain streaming read of the code and "
+                          "scale planes, best of a sweep of grid shapes; all graph-replayed over the same "
+                          "rotating copies"}
     if not args.no_cpu_baseline:
         import oracle
         oracle.build(force=False)

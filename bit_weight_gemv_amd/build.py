@@ -17,6 +17,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libq4.so")
+# A measurement reference kept out of libq4: the plain streaming read of a
+# packed matrix's bytes (bench.py times it beside each GEMV).
+FLOOR_SOURCE = "q4_floor.hip"
+FLOOR_LIB = os.path.join(HERE, "libq4floor.so")
 SOURCES = ["q4_api.cpp", "q4_pack.hip", "q4_gemv.hip", "q4_gemm_smalln.hip", "q4_gather.hip", "q4_quant.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -48,6 +52,15 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("link of libq4.so failed")
     os.replace(tmp, LIB)
+    tmp = FLOOR_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, "-shared", "-x", "hip", os.path.join(CSRC, FLOOR_SOURCE), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("build of libq4floor.so failed")
+    os.replace(tmp, FLOOR_LIB)
     return LIB
 
 

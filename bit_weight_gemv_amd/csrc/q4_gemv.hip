@@ -21,9 +21,15 @@
 //    LDS address of lane l for byte b is (b << 8) | (l << 2), assembled by
 //    one v_perm_b32 from the code word.
 //  * Activations.  Each lane converts its own 32*CPL activations once from
-//    bf16 to fp16, after scaling them by a power of two chosen from their
-//    largest magnitude so that no bf16 value can overflow fp16; the lane's
-//    partial sum is scaled back by the inverse power of two (exact).
+//    bf16 to fp16, after scaling them by a power of two chosen from the
+//    wave's largest magnitude so that no bf16 value can overflow fp16; the
+//    partial sums are scaled back by the inverse power of two (exact).  The
+//    conversion is exact while no nonzero activation of the wave lies more
+//    than 2^31 below that largest one.  A wave whose activations span more
+//    runs a plain loop instead (the exact loop in gemv_body) that
+//    multiplies the raw bf16 activations, widened exactly to fp32, with the
+//    table levels in fp32 FMAs: slower, same accuracy bound, for any finite
+//    bf16 input.
 //  * Scale.  The dot over a 32-weight chunk is multiplied by its block
 //    scale once (fp32 FMA).
 //  * Reduction.  DPP row ops + ds_swizzle + readlane inside the wave; an LDS
@@ -55,9 +61,12 @@ constexpr int pre_rows(int nr, int s, bool multi) { return (!multi && s >= 1) ? 
 
 // Dot of one 16-byte chunk (32 weights) with the lane's fp16 activations.
 // All 16 lookups are issued before the first product so their LDS latencies
-// overlap.
-__device__ __forceinline__ float chunk_dot(const uint32_t *lut, uint4 q, const half2_t *xh,
-                                           uint32_t laneoff) {
+// overlap.  ZOFF (the affine format): `zz` (z - 8 in both halves) is taken
+// from each looked-up pair of code - 8 values, one packed fp16 subtract,
+// exact for these small integers, so every product is (code - z) x.
+template <bool ZOFF = false>
+__device__ __forceinline__ float chunk_dot(const uint32_t *lut, uint4 q, const half2_t *xh, uint32_t laneoff,
+                                           half2_t zz = half2_t{(_Float16)0.0f, (_Float16)0.0f}) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
     half2_t v[16];
 #pragma unroll
@@ -69,7 +78,7 @@ __device__ __forceinline__ float chunk_dot(const uint32_t *lut, uint4 q, const h
     }
     float p = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) p = __builtin_amdgcn_fdot2(v[j], xh[j], p, false);
+    for (int j = 0; j < 16; ++j) p = __builtin_amdgcn_fdot2(ZOFF ? v[j] - zz : v[j], xh[j], p, false);
     return p;
 }
 
@@ -115,6 +124,34 @@ __device__ __forceinline__ void chunk_dot_halves(const uint32_t *lut, uint4 q, c
         p0 = __builtin_amdgcn_fdot2(v[j], xh[j], p0, false);
         p1 = __builtin_amdgcn_fdot2(v[j + 8], xh[j + 8], p1, false);
     }
+}
+
+// The exact forms of the dots above, for activations that span too wide a
+// range for one fp16 scale.  `xw` holds the raw bf16 activations of one code
+// word of the chunk (4 dwords, two each); each is widened exactly to fp32
+// and multiplied with a table level (fp16, widened exactly) in an fp32 FMA:
+// the product is exact (11 + 8 significant bits), only the sums round.
+// ZOFF (the affine format): `zoff` = z - 8 is taken from each table value of
+// code - 8 first, so each term is (code - z) x exactly.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+template <bool ZOFF>
+__device__ __forceinline__ float dot_word_exact(const uint32_t *lut, uint32_t w, u32x4_t xw, uint32_t laneoff,
+                                                float p, float zoff) {
+    const half2_t v0 = lut_pair<0>(lut, w, laneoff);
+    const half2_t v1 = lut_pair<1>(lut, w, laneoff);
+    const half2_t v2 = lut_pair<2>(lut, w, laneoff);
+    const half2_t v3 = lut_pair<3>(lut, w, laneoff);
+    auto lv = [&](_Float16 h) { return ZOFF ? (float)h - zoff : (float)h; };
+    p = fmaf(lv(v0.x), bf16_lo(xw.x), p);
+    p = fmaf(lv(v0.y), bf16_hi(xw.x), p);
+    p = fmaf(lv(v1.x), bf16_lo(xw.y), p);
+    p = fmaf(lv(v1.y), bf16_hi(xw.y), p);
+    p = fmaf(lv(v2.x), bf16_lo(xw.z), p);
+    p = fmaf(lv(v2.y), bf16_hi(xw.z), p);
+    p = fmaf(lv(v3.x), bf16_lo(xw.w), p);
+    return fmaf(lv(v3.y), bf16_hi(xw.w), p);
 }
 
 // An E4M3 scale byte (sign clear) as fp32: its 7 magnitude bits placed at
@@ -178,20 +215,41 @@ __device__ __forceinline__ void convert_chunk_x(const uint32_t (&raw)[16], float
 // in a first pass and the chunks are fetched again (from cache or LDS) for
 // the conversion, so the raw and the converted copies are never live
 // together.
+//
+// `exact` is set (wave-uniform) when the conversion loses nothing: every
+// nonzero magnitude has a biased exponent of at least E - 31, E being the
+// largest one's.  A bf16 value of exponent e has 7 fraction bits, so its
+// scaled copy is a multiple of 2^(e - 134 + 141 - E) >= 2^-24, fp16's
+// finest step (subnormals included), and the scaled largest value is below
+// 2^15.  (A bf16 subnormal counts as exponent 0; it passes only when
+// E <= 31, where the scale is at least 2^110 and its step 2^-133 becomes at
+// least 2^-23.)
 template <int CPL, bool PRELOADED, class Load>
-__device__ __forceinline__ float convert_x(Load load, uint32_t (&raw)[16], half2_t (&xh)[CPL][16]) {
+__device__ __forceinline__ float convert_x(Load load, uint32_t (&raw)[16], half2_t (&xh)[CPL][16], bool &exact) {
     u16x2_t mx = {0, 0};
+    // Smallest nonzero magnitude minus one (a zero wraps to 0xFFFF).
+    u16x2_t mn = {0xFFFF, 0xFFFF};
+    const u16x2_t one = {1, 1};
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         if (!PRELOADED || CPL > 1) load(i, raw);
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, raw[v] & 0x7FFF7FFFu));
+        for (int v = 0; v < 16; ++v) {
+            const u16x2_t mag = __builtin_bit_cast(u16x2_t, raw[v] & 0x7FFF7FFFu);
+            mx = __builtin_elementwise_max(mx, mag);
+            mn = __builtin_elementwise_min(mn, mag - one);
+        }
     }
     // Largest bf16 magnitude bits of the wave (integer max: bf16 magnitudes
     // order like their bit patterns).
     int m = (int)(mx.x > mx.y ? mx.x : mx.y);
     m = __builtin_amdgcn_readfirstlane(__reduce_max_sync(~0ull, m));
+    // Each lane tests its own smallest nonzero magnitude against the wave's
+    // threshold; one ballot makes the answer wave-uniform.
+    const int emax = m >> 7;
+    const int lo = (int)(mn.x < mn.y ? mn.x : mn.y);
+    const bool lane_ok = emax <= 31 || lo == 0xFFFF || lo + 1 >= ((emax - 31) << 7);
+    exact = __builtin_amdgcn_ballot_w64(!lane_ok) == 0;
     // Its biased exponent E; scale by 2^(141-E) so the largest value lands in
     // [2^14, 2^15), inside fp16's range.
     int E = m >> 7;
@@ -215,8 +273,15 @@ __device__ __forceinline__ float convert_x(Load load, uint32_t (&raw)[16], half2
 // longer rows trade occupancy for the extra activation registers.  Groups
 // spanning several waves use workgroups of at most 512 lanes.
 // The one-load-per-tile scale path (TS) asks for six (at most 80 VGPRs): the
-// one-tile-per-wave launches put up to 16 waves on a CU.
-constexpr int gemv_min_waves(int cpl, bool ts = false) { return ts ? 6 : (cpl == 1 ? 4 : 2); }
+// one-tile-per-wave launches put up to 16 waves on a CU.  Its plain
+// (epilogue-free) kernels ask for eight (at most 64): their main loop fits
+// in 64 without spilling, and without the bound the register budget of the
+// exact-activation loop (which runs only for activations the fp16 copy
+// cannot hold) would lower the occupancy the main loop is scheduled for;
+// with it, that loop's few spills stay in the rarely taken branch.
+constexpr int gemv_min_waves(int cpl, bool ts = false, bool plain = false) {
+    return ts ? (plain ? 8 : 6) : (cpl == 1 ? 4 : 2);
+}
 constexpr int gemv_max_block(bool multi, int cpl) { return cpl > 1 ? 512 : 1024; }
 
 // SiLU(z) = z * sigmoid(z) = z / (1 + e^-z) (golang.design accel/tensor,
@@ -288,10 +353,12 @@ struct X8Args {
 // y = silu(g (+ bias0)) * (u (+ bias1)) (+ residual) -- SiLU only ever sees
 // a finished sum (deep-fold "Decode V2" page, section 6 Linear primitive).
 //
-// FMT kFmtAffine: the table holds code - 8 and each chunk's dot d is turned
-// into s * (d - (z - 8) * xsum), xsum being the sum of the lane's 32
-// activations of that chunk (the same scaled fp16 values the dot uses), so
-// the zero point costs one load and two operations per chunk.
+// FMT kFmtAffine: the table holds code - 8 (centred, exact in fp16) and
+// z - 8 is taken from each looked-up pair before its product, so every term
+// is (code - z) x itself: the zero point costs one load per chunk and one
+// packed subtract per code byte.  (Applying it afterwards as (z - 8) times
+// the chunk's activation sum would cancel when a large activation meets a
+// weight of code z, and break the per-output bound.)
 //
 // TS (one chunk a lane, 16-bit scales (and zero points) on dword-aligned
 // planes with an even number a row, as the host checks): a tile's scales are
@@ -544,11 +611,16 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     auto &xh = xhn[0];
     float &down = downn[0];
     down = 1.0f;
+    // Whether the conversion of every token was exact (wave-uniform).  For
+    // groups of waves each wave decides alone: the main loop and the exact
+    // loop meet the same workgroup barriers in the same order, so waves of
+    // one workgroup may take different loops.
+    bool xexact = true;
     if constexpr (X8) {
         // (no table and no shared activation copy to wait for)
     } else if constexpr (MULTI) {
         down = convert_x<CPL, true>([&](int i, uint32_t(&r)[16]) { load_chunk_x(x, cidx[i], cvalid[i], r); },
-                                    xraw, xh);
+                                    xraw, xh, xexact);
         __syncthreads();
     } else {
         if ((int)threadIdx.x < xunits)
@@ -563,10 +635,13 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     for (int s = 1; s <= S; ++s) load_tile(s);
     if constexpr (!X8 && !MULTI)
 #pragma unroll
-        for (int t = 0; t < NTOK; ++t)
+        for (int t = 0; t < NTOK; ++t) {
+            bool ex = true;
             downn[t] = convert_x<CPL, false>(
                 [&](int i, uint32_t(&r)[16]) { load_chunk_x_lds(xs + t * xunits, cidx[i], cvalid[i], r); }, xraw,
-                xhn[t]);
+                xhn[t], ex);
+            xexact = xexact && ex;
+        }
 
     // int8-activation forms: the words regrouped to match the code nibbles
     // (code dword d holds weights 8d .. 8d+7, even ones in the low nibbles):
@@ -611,20 +686,6 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     // NVFP4-style format: the tensor scale joins the activations' inverse
     // power of two (both multiply every finished sum).
     if constexpr (FMT == kFmtNvfp4) down *= *sg.tscale;
-
-    // Affine format: the sum of each chunk's 32 activations (zero for chunks
-    // past the row's end, whose activations are zero).
-    float xsum[FMT == kFmtAffine ? CPL : 1];
-    if constexpr (FMT == kFmtAffine) {
-        const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            float t = 0.0f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) t = __builtin_amdgcn_fdot2(xh[i][v], one, t, false);
-            xsum[i] = t;
-        }
-    }
 
     // Rows are reduced across the wave RG at a time (RG/NR tiles): the fixed
     // cost of the cross-lane reduction and of the store is paid once per RG
@@ -687,9 +748,14 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                         for (int t = 1; t < NTOK; ++t) accn[t][j * NR + r] = pn[t] * sf;
                         a = fmaf(pn[0], sf, a);
                     } else {
-                        float p = chunk_dot(lut, q[buf][r][i], xh[i], laneoff);
-                        if constexpr (FMT == kFmtAffine)
-                            p = fmaf(8.0f - f16_bits_to_f32(TS ? tzb[r] >> ts_sh : zc[buf][r][i]), xsum[i], p);
+                        float p;
+                        if constexpr (FMT == kFmtAffine) {
+                            const _Float16 zo =
+                                (_Float16)(f16_bits_to_f32(TS ? tzb[r] >> ts_sh : zc[buf][r][i]) - 8.0f);
+                            p = chunk_dot<true>(lut, q[buf][r][i], xh[i], laneoff, half2_t{zo, zo});
+                        } else {
+                            p = chunk_dot(lut, q[buf][r][i], xh[i], laneoff);
+                        }
                         const uint32_t sbits = TS ? tsb[r] >> ts_sh : sc[buf][r][i];
                         a = fmaf(p, f16_bits_to_f32(sbits), a);
                     }
@@ -767,6 +833,110 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         }
     };
 
+    // The exact loop: the same tiles, rows, reductions, barriers and stores
+    // as the main loop below, for a wave whose activations the fp16
+    // conversion would not hold exactly.  Each row's chunks are read
+    // directly (no prefetch ring) and multiplied with the raw activations
+    // (exact_row); it is kept plain so that it needs fewer registers than
+    // the main loop and leaves that loop's code and register budget as they
+    // are.  Rare inputs only: its speed is not a concern.
+    if constexpr (!X8) {
+        if (__builtin_expect(!xexact, 0)) {
+            // The lane's values, derived again from an index the compiler
+            // cannot trace back to the set-up, so that nothing per-lane of
+            // the set-up stays live into this loop (its registers are then
+            // free for the loop's own values).
+            int tid = (int)threadIdx.x;
+            __asm__ volatile("" : "+v"(tid));
+            const int e_lig = MULTI ? tid - grp * P : (tid & 63);
+            const uint32_t e_laneoff = (uint32_t)(tid & 63) << 2;
+            // Raw activations of token `tok`'s chunk c (valid: c < C), code
+            // word d; a chunk past the row's end has zero activations.
+            auto raw_word = [&](int tok, int c, bool valid, int d) -> u32x4_t {
+                if (!valid) return u32x4_t{0u, 0u, 0u, 0u};
+                uint4 v;
+                if constexpr (MULTI)
+                    v = reinterpret_cast<const uint4 *>(x)[c * 4 + d];
+                else
+                    v = xs[tok * xunits + c * 4 + d];
+                return u32x4_t{v.x, v.y, v.z, v.w};
+            };
+            // The lane's part of row `row` of one matrix for token `tok`.
+            auto exact_row = [&](int tok, const uint8_t *cbase, const uint16_t *sbase, int64_t row) -> float {
+                float a = 0.0f;
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) {
+                    const int ci = e_lig + i * P;
+                    const bool valid = ci < C;
+                    const int c = valid ? ci : C - 1;
+                    const uint32_t so = FMT == kFmtNvfp4 ? (uint32_t)c : (uint32_t)c >> 1;
+                    const uint4 qv = *reinterpret_cast<const uint4 *>(cbase + row * row_bytes + c * 16);
+                    const uint32_t sbits = sbase[row * sst + so];
+                    float zoff = 0.0f;
+                    if constexpr (FMT == kFmtAffine) zoff = f16_bits_to_f32(sg.zeros0[row * nsb + so]) - 8.0f;
+                    float p0 = 0.0f, p1 = 0.0f;
+#pragma clang loop unroll(disable)
+                    for (int d = 0; d < 4; ++d) {
+                        const uint32_t w = d == 0 ? qv.x : (d == 1 ? qv.y : (d == 2 ? qv.z : qv.w));
+                        const float t = dot_word_exact<FMT == kFmtAffine>(lut, w, raw_word(tok, c, valid, d),
+                                                                          e_laneoff, 0.0f, zoff);
+                        if (d < 2) p0 += t; else p1 += t;
+                    }
+                    if constexpr (FMT == kFmtNvfp4) {
+                        a = fmaf(p0, e4m3_to_f32(sbits), a);
+                        a = fmaf(p1, e4m3_to_f32(sbits >> 8), a);
+                    } else {
+                        a = fmaf(p0 + p1, f16_bits_to_f32(sbits), a);
+                    }
+                }
+                return a;
+            };
+            const float tsc = FMT == kFmtNvfp4 ? *sg.tscale : 1.0f;
+            for (int64_t g0 = 0; g0 < nsteps; g0 += TPG) {
+                const Epi epi = fetch_epi(g0);
+                // Lane l gets the total of group row l % RG, as reduce_rows
+                // leaves it in the main loop; the rows are taken one at a
+                // time (a rolled loop) and summed over the wave at once.
+                float tot[NTOK];
+#pragma unroll
+                for (int tk = 0; tk < NTOK; ++tk) tot[tk] = 0.0f;
+#pragma clang loop unroll(disable)
+                for (int gr = 0; gr < RG; ++gr) {
+                    // Group row gr is row r of tile j: output (tile, r % LPT);
+                    // a SwiGLU tile's rows LPT.. are the up rows of the same
+                    // outputs.
+                    const int j = gr / NR, r = gr % NR;
+                    const int64_t row = g0 + j < ntiles ? out_row((g0 + j) * LPT + r % LPT) : -1;
+                    const bool up = MODE == kModeSwiglu && r >= LPT;
+#pragma unroll
+                    for (int tk = 0; tk < NTOK; ++tk) {
+                        const float v = row < 0 ? 0.0f
+                                                : exact_row(tk, up ? sg.codes1 : sg.codes0,
+                                                            up ? sg.scales1 : sg.scales0, row);
+                        const float sum = wave_sum(v);
+                        if ((tid & 63) % RG == gr) tot[tk] = sum;
+                    }
+                }
+                if (!MULTI) {
+                    store(tot[0] * tsc, g0, epi);
+#pragma unroll
+                    for (int tk = 1; tk < NTOK; ++tk) store(tot[tk], g0, epi, tk);
+                } else {
+                    if (lane < RG) red[wave][lane] = tot[0] * tsc;
+                    __syncthreads();
+                    if (wig == 0) {
+                        float sum = 0.0f;
+                        if (lane < RG)
+                            for (int w = 0; w < wpg; ++w) sum += red[grp * wpg + w][lane];
+                        store(sum, g0, epi);
+                    }
+                    __syncthreads();
+                }
+            }
+            return;
+        }
+    }
+
     for (int64_t g0 = 0; g0 < nsteps; g0 += TPG) {
         const Epi epi = fetch_epi(g0);
 #pragma unroll
@@ -793,7 +963,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
 
 template <int NR, int CPL, int S, int RG, bool MULTI, bool STRIDED = false, bool TS = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
-                          amdgpu_waves_per_eu(gemv_min_waves(CPL, TS), 8))) void gemv_kernel(const uint8_t *__restrict__ codes,
+                          amdgpu_waves_per_eu(gemv_min_waves(CPL, TS, true), 8))) void gemv_kernel(const uint8_t *__restrict__ codes,
                                                    const uint16_t *__restrict__ scales, int64_t M,
                                                    int K, const uint16_t *__restrict__ x,
                                                    float *__restrict__ y, int P, int64_t rows_q,
@@ -827,7 +997,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 768), amdgpu_waves_per
 // The affine format's GEMV (y = W . x with W = (code - z) * s).
 template <int NR, int CPL, int S, int RG, bool MULTI, bool STRIDED = false, bool TS = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
-                          amdgpu_waves_per_eu(gemv_min_waves(CPL, TS), 8))) void gemv_affine_kernel(
+                          amdgpu_waves_per_eu(gemv_min_waves(CPL, TS, true), 8))) void gemv_affine_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     int64_t M, int K, const uint16_t *__restrict__ x, float *__restrict__ y, int P, int64_t rows_q, int rows_rem) {
     GemvSeg sg{};

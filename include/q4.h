@@ -118,10 +118,12 @@ int q4_unpack_canonical(const uint8_t *codes, const uint16_t *scales,
  *   codes/scales: a packed matrix (codes 16-byte aligned, scales 2-byte).
  *   x: bf16 bit patterns [K], 16-byte aligned.
  *   y: fp32 [M], 4-byte aligned; must not overlap codes, scales or x.
- * Accuracy: |y - y_exact| <= 1e-3 * sum_k |What[m,k] x[k]| + 1e-5 for
- * finite inputs with max|What| * max|x| below 1e4 (the fp16 rounding of the
- * table costs at most 2^-11 relative per term; fp32 accumulation).
- * Non-finite x propagate into y.
+ * Accuracy: |y - y_exact| <= 1e-3 * sum_k |What[m,k] x[k]| + 1e-5 for any
+ * finite x and any packed matrix, while that sum stays inside fp32's range.
+ * The fp16 rounding of the table costs at most 2^-11 relative per term;
+ * every activation enters its product exactly (as fp16 under a power of two,
+ * or widened to fp32 where the values one wave holds span more than 2^31);
+ * sums are fp32.  Non-finite x propagate into y.
  */
 int q4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
             const uint16_t *x, float *y, void *stream);
@@ -134,8 +136,13 @@ int q4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
  * Every weight is read once per call).
  *   X: bf16 bit patterns [N][K] row-major, 16-byte aligned.
  *   Y: fp32 [N][M] row-major, 4-byte aligned; must not overlap the inputs.
- * Same accuracy statement as q4_gemv.  A chunk of one token is computed by
- * the q4_gemv kernels (Y[0] is then bit-identical to q4_gemv of X[0]);
+ * Same accuracy statement as q4_gemv, with one exception: chunks of four or
+ * more tokens take a token's activations exactly only while, within each
+ * 256-weight slice of K, none that is nonzero lies more than 2^31 below the
+ * slice's largest magnitude (smaller ones are rounded to fp16 subnormals, an
+ * absolute error of at most 2^-39 of that largest magnitude each).  A chunk
+ * of one token is computed by the q4_gemv kernels (Y[0] is then
+ * bit-identical to q4_gemv of X[0]);
  * chunks of two or three tokens on rows of at most 2048 weights (and at most
  * 12 four-row tiles per compute unit) by the same kernels with each table
  * lookup serving every token.

@@ -280,6 +280,121 @@ def test_gemv_activation_ranges(env, kind):
     _check(yg, y_ref, S, f"gemv x={kind}")
 
 
+# ---------------------------------------------------------------------------
+# Activations of any range.  An fp16 copy of a wave's activations under one
+# power of two is exact only while they span at most 2^31; beyond that the
+# kernels take the raw bf16 values.  Each case puts a huge activation where
+# it meets only zero weights (a zero 64-block, or a column of code 7), so
+# the row sums come entirely from activations far below it: a conversion
+# that flushed them would give y = 0.  spread_31 / spread_32 sit on the
+# exactness threshold with activations 1 + 2^-7 (8 significant bits), which
+# the one-scale conversion would round by up to 2^-7 relative if it were
+# taken one binade too far.
+# ---------------------------------------------------------------------------
+
+WIDE_KINDS = ["zero_block_2^60", "code7_column_2^60", "spread_31", "spread_32", "tiny_run", "many_windows"]
+K_ZERO_BLOCK, K_ZERO_COL = 64 * 3 + 5, 1000
+
+
+def _wide_x(kind, K, seed):
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal(K)
+    sgn = np.where(z < 0, -1.0, 1.0)
+    if kind == "zero_block_2^60":
+        v = z.copy()
+        v[K_ZERO_BLOCK] = 2.0 ** 60
+    elif kind == "code7_column_2^60":
+        v = z.copy()
+        v[K_ZERO_COL] = -(2.0 ** 60)
+    elif kind in ("spread_31", "spread_32"):
+        v = sgn * (1.0 + 2.0 ** -7)
+        v[K_ZERO_COL] = 2.0 ** int(kind[-2:])
+    elif kind == "tiny_run":
+        v = z.copy()
+        v[100:140] *= 2.0 ** -100
+        v[K_ZERO_COL] = 2.0 ** 50
+    else:  # many_windows: magnitudes over 160 binades (five windows), every weight nonzero
+        v = sgn * (1.0 + 0.5 * rng.random(K)) * np.exp2(rng.integers(-120, 41, K).astype(np.float64))
+    return _bf16_bits(v)
+
+
+def _wide_w(W):
+    W = W.copy()
+    b = K_ZERO_BLOCK // 64
+    W[:, 64 * b:64 * b + 64] = 0.0
+    W[:, K_ZERO_COL] = 0.0
+    return W
+
+
+WIDE_GEMV_SHAPES = [(300, 2048), (20011, 2048), (77, 11008), (64, 4096), (5, 40960), (3, 98304)]
+
+
+@pytest.mark.parametrize("kind", WIDE_KINDS)
+@pytest.mark.parametrize("M,K", WIDE_GEMV_SHAPES)
+def test_gemv_wide_range_activations(env, M, K, kind):
+    torch, q4, dev = env
+    seed = 7300 + M + K
+    W = _wide_w(wl.weights(M, K, seed))
+    x = _wide_x(kind, K, seed)
+    codes, scales, _ = oracle.pack(W)
+    y_ref, S = oracle.gemv(codes, scales, M, K, x, threads=min(16, os.cpu_count() or 1))
+    c, s = _upload_packed(env, codes, scales)
+    y = q4.q4_gemv(c, s, _x_dev(env, x))
+    torch.cuda.synchronize()
+    yg = y.cpu().numpy()
+    assert np.all(np.isfinite(yg))
+    _check(yg, y_ref, S, f"gemv wide x={kind} M={M} K={K}")
+
+
+@pytest.mark.parametrize("kind", WIDE_KINDS)
+@pytest.mark.parametrize("M,K", [(300, 2048), (77, 11008)])
+def test_affine_and_nvfp4_wide_range_activations(env, M, K, kind):
+    torch, q4, dev = env
+    seed = 7400 + M + K
+    W = _wide_w(wl.weights(M, K, seed, std=0.5))
+    x = _wide_x(kind, K, seed)
+    codes, scales, zeros, st = oracle.pack_affine(W)
+    assert st == 0
+    y_ref, S = oracle.gemv_affine(codes, scales, zeros, M, K, x)
+    c, s, z = _affine_upload(env, codes, scales, zeros)
+    y = q4.q4_gemv_affine(c, s, z, _x_dev(env, x))
+    torch.cuda.synchronize()
+    _check(y.cpu().numpy(), y_ref, S, f"affine gemv wide x={kind} M={M} K={K}")
+    ncodes, nscales, ts, st = oracle.pack_nvfp4(W)
+    assert st == 0
+    y_ref, S = oracle.gemv_nvfp4(ncodes, nscales, ts, M, K, x)
+    t = torch.tensor([ts], dtype=torch.float32, device=dev)
+    y = q4.q4_gemv_nvfp4(cases.to_dev(ncodes, torch, dev), cases.to_dev(nscales, torch, dev), t, _x_dev(env, x))
+    torch.cuda.synchronize()
+    _check(y.cpu().numpy(), y_ref, S, f"nvfp4 gemv wide x={kind} M={M} K={K}")
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 2048, 2), (300, 2048, 3), (3001, 1984, 3), (600, 11008, 1)])
+def test_gemm_smalln_wide_range_activations(env, M, K, N):
+    """Each token of the chunk takes a different wide-range recipe."""
+    torch, q4, dev = env
+    seed = 7500 + M + K + N
+    W = _wide_w(wl.weights(M, K, seed))
+    X = np.stack([_wide_x(WIDE_KINDS[(n + seed) % len(WIDE_KINDS)], K, seed + n) for n in range(N)])
+    codes, scales, _ = oracle.pack(W)
+    Y_ref, S = oracle.gemm(codes, scales, M, K, X)
+    c, s = _upload_packed(env, codes, scales)
+    Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+    Y = q4.q4_gemm_smalln(c, s, Xd)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, S, f"gemm wide M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("kind", ["code7_column_2^60", "spread_32", "many_windows"])
+@pytest.mark.parametrize("swiglu,Ms,K", [(False, (2048, 256, 256), 2048), (False, (300, 40), 11008),
+                                         (True, (1000, 1000), 2048), (True, (300, 300), 4160)])
+def test_fused_wide_range_activations(env, swiglu, Ms, K, kind):
+    seed = 7600 + K + sum(Ms)
+    # Bias and residual small next to the products, so the products' bound
+    # is what is tested.
+    _fused_case(env, Ms, K, seed, swiglu=swiglu, x=_wide_x(kind, K, seed), w_hook=_wide_w, bias_scale=1e-3)
+
+
 def test_gemv_bit_exact_invariants(env):
     torch, q4, dev = env
     M, K = 1030, 2048
@@ -625,16 +740,21 @@ def _check_bound(y_gpu, y_ref, bound, what):
 
 
 def _fused_case(env, Ms, K, seed, swiglu=False, bias=True, residual=True, alias=(), x_recipe="unit_rms",
-                bias_scale=0.5):
+                bias_scale=0.5, x=None, w_hook=None):
     """Packs len(Ms) matrices, runs q4_gemv_fused, checks every output against
-    the oracle and against the unfused q4_gemv followed by torch's epilogue."""
+    the oracle and against the unfused q4_gemv followed by torch's epilogue.
+    `x` (bf16 bits) replaces the recipe's activations; `w_hook(W)` edits each
+    fp32 matrix before it is packed."""
     torch, q4, dev = env
-    x = wl.activation(K, seed, x_recipe)
+    if x is None:
+        x = wl.activation(K, seed, x_recipe)
     xd = _x_dev(env, x)
     ops, ts, Ss, biases, packed = [], [], [], [], []
     rng = np.random.default_rng(seed)
     for i, M in enumerate(Ms):
         W = wl.weights(M, K, seed + 17 * i)
+        if w_hook is not None:
+            W = w_hook(W)
         codes, scales, st = oracle.pack(W)
         assert st == 0
         t, S = oracle.gemv(codes, scales, M, K, x)
