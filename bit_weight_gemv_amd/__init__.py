@@ -33,7 +33,7 @@ Q4_PACK_OVERFLOW = 2
 EXPORTED = ("q4_codes_bytes", "q4_scales_bytes", "q4_codebook", "q4_status_string",
             "q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused",
             "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_pack_nvfp4", "q4_gemv_nvfp4",
-            "q4_quantize_x8", "q4_gemv_affine_x8")
+            "q4_quantize_x8", "q4_gemv_affine_x8", "q4_gemm_smalln_affine", "q4_gemm_smalln_nvfp4")
 
 Q4_OUT_F32 = 0
 Q4_OUT_BF16 = 1
@@ -102,6 +102,10 @@ def lib() -> ctypes.CDLL:
         L.q4_quantize_x8.restype = I32
         L.q4_gemv_affine_x8.argtypes = [P, P, P, I64, I64, P, P, P, P, P]
         L.q4_gemv_affine_x8.restype = I32
+        L.q4_gemm_smalln_affine.argtypes = [P, P, P, I64, I64, P, I64, P, P]
+        L.q4_gemm_smalln_affine.restype = I32
+        L.q4_gemm_smalln_nvfp4.argtypes = [P, P, P, I64, I64, P, I64, P, P]
+        L.q4_gemm_smalln_nvfp4.restype = I32
         _lib = L
         return L
 
@@ -433,6 +437,57 @@ def q4_gemv_nvfp4(codes, scales, tscale, x, y=None, stream=None):
     if st != Q4_OK:
         raise Q4Error(st, "q4_gemv_nvfp4")
     return y
+
+
+def _smalln_out(X, K, M, Y, dev):
+    torch = _torch()
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError(f"X must be [N, K={K}]")
+    N = X.shape[0]
+    _check(X, "X", torch.bfloat16, dev)
+    if Y is None:
+        Y = torch.empty((N, M), dtype=torch.float32, device=dev)
+    _check(Y, "Y", torch.float32, dev)
+    if Y.numel() != N * M:
+        raise ValueError("Y must be [N, M]")
+    return N, Y
+
+
+def q4_gemm_smalln_affine(codes, scales, zeros, X, Y=None, stream=None):
+    """Y[n] = W . X[n] for an affine-format W and bf16 X [N, K], N <= 32;
+    returns fp32 Y [N, M]."""
+    torch = _torch()
+    M, K = _mk(codes, scales)
+    _check(zeros, "zeros", torch.float16, codes.device)
+    if tuple(zeros.shape) != tuple(scales.shape):
+        raise ValueError("zeros must have the shape of scales")
+    N, Y = _smalln_out(X, K, M, Y, codes.device)
+    st = lib().q4_gemm_smalln_affine(_ptr(codes), _ptr(scales), _ptr(zeros), M, K, _ptr(X), N, _ptr(Y),
+                                     _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_gemm_smalln_affine")
+    return Y
+
+
+def q4_gemm_smalln_nvfp4(codes, scales, tscale, X, Y=None, stream=None):
+    """Y[n] = W . X[n] for an NVFP4-style W (codes [M, K/2], scales uint8
+    [M, K/16], tensor scale fp32 [1]) and bf16 X [N, K], N <= 32."""
+    torch = _torch()
+    dev = codes.device
+    if codes.dim() != 2 or scales.dim() != 2:
+        raise ValueError("codes must be [M, K/2] and scales [M, K/16]")
+    M, K = codes.shape[0], codes.shape[1] * 2
+    if scales.shape[0] != M or scales.shape[1] * 16 != K:
+        raise ValueError("codes and scales disagree on M, K")
+    _check(codes, "codes", torch.uint8, dev)
+    _check(scales, "scales", torch.uint8, dev)
+    _check(tscale, "tscale", torch.float32, dev)
+    N, Y = _smalln_out(X, K, M, Y, dev)
+    st = lib().q4_gemm_smalln_nvfp4(_ptr(codes), _ptr(scales), _ptr(tscale), M, K, _ptr(X), N, _ptr(Y),
+                                    _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_gemm_smalln_nvfp4")
+    return Y
 
 
 def q4_quantize_x8(x, words=2, q1=None, q2=None, d=None, stream=None):

@@ -219,6 +219,35 @@ int q4_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M, int6
     return launch_status(q4::launch_gemm_smalln(codes, scales, M, K, X, N, Y, (hipStream_t)stream));
 }
 
+int q4_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M, int64_t K,
+                          const uint16_t *X, int64_t N, float *Y, void *stream) {
+    if (!shape_ok(M, K) || N < 0 || N > Q4_MAX_N) return Q4_ERR_SHAPE;
+    if (M == 0 || N == 0) return Q4_OK;
+    if (!codes || !scales || !zeros || !X || !Y) return Q4_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2) || !aligned(X, 16) || !aligned(Y, 4))
+        return Q4_ERR_ALIGN;
+    const Range ry = range_of(Y, (uint64_t)N * M * 4);
+    const uint64_t sb = (uint64_t)M * (K / 64) * 2;
+    if (overlap(ry, range_of(codes, (uint64_t)M * (K / 2))) || overlap(ry, range_of(scales, sb)) ||
+        overlap(ry, range_of(zeros, sb)) || overlap(ry, range_of(X, (uint64_t)N * K * 2)))
+        return Q4_ERR_OVERLAP;
+    return launch_status(q4::launch_gemm_smalln_affine(codes, scales, zeros, M, K, X, N, Y, (hipStream_t)stream));
+}
+
+int q4_gemm_smalln_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscale, int64_t M, int64_t K,
+                         const uint16_t *X, int64_t N, float *Y, void *stream) {
+    if (!shape_ok(M, K) || N < 0 || N > Q4_MAX_N) return Q4_ERR_SHAPE;
+    if (M == 0 || N == 0) return Q4_OK;
+    if (!codes || !scales || !tscale || !X || !Y) return Q4_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(tscale, 4) || !aligned(X, 16) || !aligned(Y, 4))
+        return Q4_ERR_ALIGN;
+    const Range ry = range_of(Y, (uint64_t)N * M * 4);
+    if (overlap(ry, range_of(codes, (uint64_t)M * (K / 2))) || overlap(ry, range_of(scales, (uint64_t)M * (K / 16))) ||
+        overlap(ry, range_of(tscale, 4)) || overlap(ry, range_of(X, (uint64_t)N * K * 2)))
+        return Q4_ERR_OVERLAP;
+    return launch_status(q4::launch_gemm_smalln_nvfp4(codes, scales, tscale, M, K, X, N, Y, (hipStream_t)stream));
+}
+
 int q4_gemv_fused(const q4_operand *ops, int count, int64_t K, const uint16_t *x, int mode, float *const *y,
                   const float *const *residual, void *stream) {
     if (mode != Q4_FUSE_SEPARATE && mode != Q4_FUSE_SWIGLU) return Q4_ERR_SHAPE;

@@ -1,11 +1,14 @@
-// q4_gemm_smalln.hip -- Y[n][m] = sum_k level[code(m,k)] * scale[m][k/64] * X[n][k]
-// for a prefill chunk of N <= 32 tokens.
+// q4_gemm_smalln.hip -- Y[n][m] = sum_k What[m,k] * X[n][k] for a prefill chunk of N <= 32 tokens,
+// for the NF4 codebook format and the affine and NVFP4-style formats.
 //
 // What is computed: the prefill form of the deep-fold "Decode V2" page
 // (section 0: prompts run as chunks of up to 32 tokens through a dedicated
 // matrix-core product) -- the same representation and reconstruction as the
 // vector form (golang.design accel/tensor, func Int4MatMul), with the matrix
 // read once per chunk of tokens and the unpacking amortised over the chunk.
+// The affine format is accel/tensor's type Int4 (What = (code - z) * s per
+// 64-block); the NVFP4-style format is gizai tensor/lazy's fp4Blocks (E2M1
+// codes, one E4M3 scale per 16 values, an f32 tensor scale).
 //
 // gfx950 design:
 //  * Matrix cores.  v_mfma_f32_16x16x32_f16 multiplies a 16-token x 32-k
@@ -17,21 +20,36 @@
 //    (a fixed permutation of k, the same for X and W), so a lane's codes for
 //    one block are 8 contiguous bytes.
 //  * Dequantisation.  The LDS byte -> fp16-pair table (one ds_read_b32 per
-//    two weights; the 64-copy layout keeps random codes conflict-free).  The
-//    fp32 result of a block's two MFMAs is multiplied by the block scale of
-//    the lane's weight row (fp32 FMA): levels round to fp16 (2^-11 relative)
-//    and nothing else is rounded below fp32.
+//    two weights; the 64-copy layout keeps random codes conflict-free).
+//    NF4: the fp32 result of a block's two MFMAs is multiplied by the block
+//    scale of the lane's weight row (fp32 FMA): levels round to fp16 (2^-11
+//    relative) and nothing else is rounded below fp32.  Affine: the table
+//    holds code - 8 and z - 8 is subtracted from every pair before the MFMA
+//    (a packed fp16 subtract of small integers, exact), so each term is
+//    (code - z) x; then the block scale as for NF4.  NVFP4: each E2M1 pair
+//    is multiplied by its 16-block's E4M3 scale in fp16 before the MFMA
+//    (E2M1 has at most 2 and E4M3 at most 4 significant bits, so the
+//    product is exact and within fp16's normal range), the tiles accumulate
+//    across blocks, and the tensor scale multiplies the finished sums.
 //  * Activations.  The workgroup's waves split K into slices of 256 (four
 //    blocks); a wave converts its slice of X to fp16 once, each token scaled
 //    by a power of two chosen from that token's largest magnitude in the
-//    slice (exact; no bf16 value can overflow), and keeps it in registers
-//    for every row tile it visits.  The inverse scale is applied to the
-//    wave's partial sums.
+//    slice, and keeps it in registers for every row tile it visits.  The
+//    inverse scale is applied to the wave's partial sums.  The conversion is
+//    exact while no nonzero value of a token's slice lies more than 2^31
+//    below that token's largest (each lane tests its own values; one ballot
+//    decides for the wave).  A wave whose slice is not held exactly keeps
+//    the raw bf16 values instead and multiplies them with
+//    v_mfma_f32_16x16x4_f32 (fp32 operands, exact products): eight such
+//    MFMAs per 32-k slab, the same accumulator layout.  Slower, and only for
+//    inputs that need it.
 //  * Schedule.  Row tiles of 16 rows are split into contiguous ranges, one
 //    per workgroup (one workgroup per CU); the waves walk the range in step
 //    with a ring of prefetched tiles (codes and scales of tile t+1 .. t+S are
 //    in flight while tile t is multiplied).  Per tile the waves' partial
-//    tiles are summed through LDS (double-buffered: one barrier per tile).
+//    tiles are summed through LDS.
+#include <type_traits>
+
 #include "q4_device.h"
 #include "q4_internal.h"
 #include "q4_lut.h"
@@ -39,6 +57,8 @@
 namespace q4 {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+enum { kGemmNf4 = 0, kGemmAffine = 1, kGemmNvfp4 = 2 };
 
 constexpr int kGemmMaxWaves = 8;   // workgroup: up to 8 waves, one K slice each
 constexpr int kSliceBlocks = 4;    // 64-blocks per K slice (256 k)
@@ -111,64 +131,129 @@ __device__ __forceinline__ void regroup_x(uint4 *xs, const u32x4_t (&lin)[NT * 8
     }
 }
 
-// Convert the slice to fp16 per token: lanes j, j+16, j+32, j+48 hold token
-// j's values; their largest bf16 magnitude fixes the power of two.  Returns
-// in inv[t][r] the inverse scale of the token of output register r (token
-// 4g + r of half t).
+// Prepare the slice's activations per token: lanes j, j+16, j+32, j+48 hold
+// token j's values; their largest bf16 magnitude fixes the power of two 2^e
+// that puts it in [2^14, 2^15).  A bf16 value (8 significant bits) scaled by
+// 2^e is exact in fp16 when its biased exponent is at least 110 - e (its
+// last bit then lies at or above fp16's subnormal spacing 2^-24); each lane
+// tests its nonzero values against that (the smallest nonzero magnitude is
+// found as 1 + the minimum of magnitude - 1 taken modulo 2^16, so zeros do
+// not count), and one ballot makes the decision for the wave.  Exact: xa
+// holds the scaled fp16 values and inv[t][r] the inverse power of two of the
+// token of output register r (token 4g + r of half t), times `post`.
+// Otherwise xa keeps the raw bf16 bits and inv[t][r] = post.  Returns
+// whether the fp16 form is exact.
 template <int NT>
-__device__ __forceinline__ void convert_x_slice(const u32x4_t (&raw)[NT][kSliceBlocks][2],
-                                                half8_t (&xa)[NT][kSliceBlocks][2], float (&inv)[NT][4]) {
+__device__ __forceinline__ bool prepare_x_slice(const u32x4_t (&raw)[NT][kSliceBlocks][2],
+                                                half8_t (&xa)[NT][kSliceBlocks][2], float (&inv)[NT][4],
+                                                float post) {
     const int lane = threadIdx.x & 63;
+    int ex[NT];
+    bool ok = true;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         u16x2_t mx = {0, 0};
+        u16x2_t mn = {0xFFFF, 0xFFFF};
 #pragma unroll
         for (int b = 0; b < kSliceBlocks; ++b)
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, raw[t][b][s][c] & 0x7FFF7FFFu));
+                for (int c = 0; c < 4; ++c) {
+                    const u16x2_t mag = __builtin_bit_cast(u16x2_t, raw[t][b][s][c] & 0x7FFF7FFFu);
+                    mx = __builtin_elementwise_max(mx, mag);
+                    mn = __builtin_elementwise_min(mn, mag - u16x2_t{1, 1});
+                }
         int m = (int)(mx.x > mx.y ? mx.x : mx.y);
         m = max(m, __shfl_xor(m, 16));
         m = max(m, __shfl_xor(m, 32));
-        // Biased exponent E of the token's largest magnitude; 2^(141-E) puts
-        // it in [2^14, 2^15).
         int E = m >> 7;
         if (E < 1) E = 1;
         int e = 141 - E;
         e = e > 126 ? 126 : (e < -126 ? -126 : e);
-        const float up = exp2i(e);
+        ex[t] = e;
+        const uint32_t lo = mn.x < mn.y ? mn.x : mn.y;
+        const int thr = 110 - e;
+        ok = ok && (lo == 0xFFFFu || thr <= 0 || lo + 1u >= ((uint32_t)thr << 7));
+    }
+    const bool exact = __builtin_amdgcn_ballot_w64(!ok) == 0;
 #pragma unroll
-        for (int b = 0; b < kSliceBlocks; ++b)
+    for (int t = 0; t < NT; ++t) {
+        float down = post;
+        if (exact) {
+            const float up = exp2i(ex[t]);
+            down *= exp2i(-ex[t]);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                half8_t h;
+            for (int b = 0; b < kSliceBlocks; ++b)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const uint32_t w = raw[t][b][s][c];
-                    h[2 * c] = (_Float16)(__builtin_bit_cast(float, w << 16) * up);
-                    h[2 * c + 1] = (_Float16)(__builtin_bit_cast(float, w & 0xFFFF0000u) * up);
+                for (int s = 0; s < 2; ++s) {
+                    half8_t h;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint32_t w = raw[t][b][s][c];
+                        h[2 * c] = (_Float16)(__builtin_bit_cast(float, w << 16) * up);
+                        h[2 * c + 1] = (_Float16)(__builtin_bit_cast(float, w & 0xFFFF0000u) * up);
+                    }
+                    xa[t][b][s] = h;
                 }
-                xa[t][b][s] = h;
-            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < kSliceBlocks; ++b)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) xa[t][b][s] = __builtin_bit_cast(half8_t, raw[t][b][s]);
+        }
         // Output register r of lane l belongs to token 4 (l / 16) + r, whose
         // scale lane 4 (l / 16) + r computed.
-        const float down = exp2i(-e);
 #pragma unroll
         for (int r = 0; r < 4; ++r) inv[t][r] = __shfl(down, 4 * (lane >> 4) + r);
     }
+    return exact;
 }
 
-template <int NT, int S, bool XFIXED, int XP>
+// One 32-k slab: acc + X (16 tokens x 32 k) . W (32 k x 16 rows).  EXACT:
+// the fp16 MFMA.  Otherwise x holds raw bf16 bits: element e of every lane
+// (k = 8 (l / 16) + e of the slab) is widened to fp32, as is the weight, and
+// v_mfma_f32_16x16x4_f32 adds the products over the four k groups; the
+// eight such products cover the slab (exact: 8 x 11 significant bits).
+template <bool EXACT>
+__device__ __forceinline__ float4_t slab_mfma(const half8_t &x, const half8_t &w, float4_t acc) {
+    if constexpr (EXACT) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, w, acc, 0, 0, 0);
+    } else {
+        // (Each dword is passed through an empty asm so that its widening is
+        // redone per use: the activations are loop-invariant, and widening
+        // them all once would hold 8 registers per slab across the loop.)
+        const u32x4_t xr = __builtin_bit_cast(u32x4_t, x);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint32_t d = xr[c];
+            __asm__ volatile("" : "+v"(d));
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, d << 16), (float)w[2 * c], acc, 0,
+                                                       0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, d & 0xFFFF0000u), (float)w[2 * c + 1],
+                                                       acc, 0, 0, 0);
+        }
+        return acc;
+    }
+}
+
+// An E4M3 scale byte (sign clear) as fp32: its 7 magnitude bits placed at
+// fp32's exponent/mantissa boundary read as 2^(e-127) (1 + m/8), or for
+// e == 0 the denormal m 2^-129; times 2^120 that is the E4M3 value.
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+    return __builtin_bit_cast(float, (b & 0x7Fu) << 20) * 0x1p120f;
+}
+
+template <int NT, int S, bool XFIXED, int XP, int FMT>
 __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
-    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, int64_t M, int K,
-    const uint16_t *__restrict__ X, int N, float *__restrict__ Y, int64_t tiles_q, int tiles_rem) {
+    const uint8_t *__restrict__ codes, const void *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    const float *__restrict__ tscale, int64_t M, int K, const uint16_t *__restrict__ X, int N,
+    float *__restrict__ Y, int64_t tiles_q, int tiles_rem) {
     // One block of LDS with the table at address 0, so a lookup address
     // built by v_perm needs no base added (the 16-bit offset field of a DS
     // instruction cannot hold a base past 64 KB).  Activation staging is
     // used during set-up only (and per unit on the long-row path); the same
-    // bytes hold the double-buffered partial tiles of the cross-wave sum.
+    // bytes hold the partial tiles of the cross-wave sum.
     struct Smem {
         uint32_t lut[kLutDwords];
         uint4 xstage[kGemmMaxWaves * kXStageUnits];
@@ -206,29 +291,42 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
     // stay in registers), else several, reloaded per unit.
     const int spw = XFIXED ? 1 : (nslices + nw - 1) / nw;
     const int row_bytes = K >> 1;
+    // Scale plane: fp16 per 64-block (NF4, affine: also the zero points), or
+    // one E4M3 byte per 16-block (NVFP4).
+    const int sc_row_bytes = FMT == kGemmNvfp4 ? (K >> 4) : (nsb * 2);
     const int64_t wg = blockIdx.x;
     const int64_t t_begin = wg * tiles_q + (wg < tiles_rem ? wg : tiles_rem);
     const int ntiles = (int)tiles_q + (wg < tiles_rem ? 1 : 0);
     const int nunits = ntiles * spw;  // (tile, slice) pairs of this wave
     uint4 *xs = sm.xstage + wave * kXStageUnits;
     uint4 *cs = sm.cstage + wave * kCStageUnits;
+    // NVFP4: the tensor scale multiplies every finished sum (with the
+    // activations' inverse power of two).
+    const float post = FMT == kGemmNvfp4 ? *tscale : 1.0f;
 
     const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(X, (uint32_t)N * (uint32_t)K * 2u);
 
-    // Ring of prefetched units: the codes and scales of one tile over one K
-    // slice.  Codes: 16 rows x 128 bytes, lane l takes row l / 8 (+ 8 for
-    // the second load), bytes 16 (l % 8) of the slice.  Scales: lane l takes
-    // row l / 4, block l % 4 of the slice; a block past the row's end reads
-    // as zero.  The buffer resource of a unit starts at its tile and slice
-    // and ends at the last row of the matrix, so rows past M read as zero
-    // (their results are not stored); units past the last load through
-    // zero-record resources (no memory access, unconditional loads).
+    // Ring of prefetched units: the scales (and zero points) and codes of
+    // one tile over one K slice, issued in that order.  Codes: 16 rows x 128
+    // bytes, lane l takes row l / 8 (+ 8 for the second load), bytes
+    // 16 (l % 8) of the slice.  Scales: one load per lane (the address
+    // unit's cost is per instruction, so the unit's scales come in a single
+    // one and lane shuffles hand them out): lane l takes row l / 4, 64-block
+    // 4 slice + l % 4 -- its fp16 scale (NF4, affine; likewise the zero
+    // point), or the dword of that block's four E4M3 bytes (NVFP4, one per
+    // 16 k).  A block past the row's end reads past the buffer and gets 0.
+    // The buffer resource of a unit starts at its tile and ends at the last
+    // row of the matrix, so rows past M read as zero (their results are not
+    // stored); units past the last load through zero-record resources (no
+    // memory access, unconditional loads).
     const int c_off = (lane >> 3) * row_bytes + 16 * (lane & 7);
-    const int s_row_off = ((lane >> 2) * nsb + (lane & 3)) * 2;
+    const int s_row_off = (lane >> 2) * sc_row_bytes + (FMT == kGemmNvfp4 ? 4 : 2) * (lane & 3);
     u32x4_t qv[S + 1][2];
     uint32_t sc[S + 1];
+    uint32_t zc[FMT == kGemmAffine ? S + 1 : 1];
     const uint8_t *ld_codes = codes + t_begin * kTileRows * row_bytes;
-    const uint16_t *ld_scales = scales + t_begin * kTileRows * nsb;
+    const uint8_t *ld_scales = static_cast<const uint8_t *>(scales) + t_begin * kTileRows * sc_row_bytes;
+    const uint8_t *ld_zeros = reinterpret_cast<const uint8_t *>(zeros) + t_begin * kTileRows * sc_row_bytes;
     int64_t ld_rows = M - t_begin * kTileRows;  // rows from the next tile to load to M
     int ld_unit = 0, ld_si = 0;
     auto load_unit = [&](int buf) {
@@ -236,27 +334,38 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
         const int slice = wave + nw * ld_si;
         const int rows = ld_rows < kTileRows ? (int)ld_rows : kTileRows;
         const bool live = real && slice < nslices;
-        const __amdgpu_buffer_rsrc_t crs =
-            buffer_rsrc(ld_codes + 128 * slice, live ? (uint32_t)(rows * row_bytes - 128 * slice) : 0u);
-        const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(ld_scales, live ? (uint32_t)(rows * nsb * 2) : 0u);
-        qv[buf][0] = __builtin_amdgcn_raw_buffer_load_b128(crs, c_off, 0, kLoadNonTemporal);
-        qv[buf][1] = __builtin_amdgcn_raw_buffer_load_b128(crs, c_off + 8 * row_bytes, 0, kLoadNonTemporal);
+        const uint32_t sbytes = live ? (uint32_t)(rows * sc_row_bytes) : 0u;
         const int sblk = kSliceBlocks * slice + (lane & 3);
         const int past = (nsb - 1 - sblk) >> 31;  // all ones past the row's end
-        sc[buf] = __builtin_amdgcn_raw_buffer_load_b16(srs, (s_row_off + 8 * slice) | (past & 0x7FFFFFF0), 0,
-                                                       kLoadNonTemporal);
+        const int s_off = (s_row_off + (FMT == kGemmNvfp4 ? 16 : 8) * slice) | (past & 0x7FFFFFF0);
+        if constexpr (FMT == kGemmNvfp4) {
+            sc[buf] = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(ld_scales, sbytes), s_off, 0, kLoadNonTemporal);
+        } else {
+            sc[buf] = __builtin_amdgcn_raw_buffer_load_b16(buffer_rsrc(ld_scales, sbytes), s_off, 0, kLoadNonTemporal);
+            if constexpr (FMT == kGemmAffine)
+                zc[buf] = __builtin_amdgcn_raw_buffer_load_b16(buffer_rsrc(ld_zeros, sbytes), s_off, 0,
+                                                               kLoadNonTemporal);
+        }
+        const __amdgpu_buffer_rsrc_t crs =
+            buffer_rsrc(ld_codes + 128 * slice, live ? (uint32_t)(rows * row_bytes - 128 * slice) : 0u);
+        qv[buf][0] = __builtin_amdgcn_raw_buffer_load_b128(crs, c_off, 0, kLoadNonTemporal);
+        qv[buf][1] = __builtin_amdgcn_raw_buffer_load_b128(crs, c_off + 8 * row_bytes, 0, kLoadNonTemporal);
+        // Keep the unit's loads together and in this order: the wait for a
+        // unit's codes then covers its scales, and never a later unit's.
+        __builtin_amdgcn_sched_barrier(0);
         ++ld_unit;
         if (XFIXED || ++ld_si == spw) {
             ld_si = 0;
             ld_codes += kTileRows * row_bytes;
-            ld_scales += kTileRows * nsb;
+            ld_scales += kTileRows * sc_row_bytes;
+            ld_zeros += kTileRows * sc_row_bytes;
             ld_rows -= kTileRows;
         }
     };
 
     // Set-up: this wave's activations (when it keeps one slice for the whole
     // run), the first units, the table fill, then the activation regrouping
-    // and conversion (which waits only for the activation loads: vector
+    // and preparation (which waits only for the activation loads: vector
     // loads complete in order) and the barrier that publishes the table.
     // (Measured on the 11008 x 2048 shape: issuing weight units ahead of the
     // activations, or the barrier before the conversion, is slower.)
@@ -265,12 +374,18 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
     if (XFIXED) load_x_linear<NT, XP>(xrs, K, nsb, wave, lin);
 #pragma unroll
     for (int s = 0; s <= S; ++s) load_unit(s);
-    fill_lut(lut);
+    if constexpr (FMT == kGemmAffine)
+        fill_lut_from(lut, kAffinePairTable);
+    else if constexpr (FMT == kGemmNvfp4)
+        fill_lut_from(lut, kE2m1PairTable);
+    else
+        fill_lut(lut);
     half8_t xa[NT][kSliceBlocks][2];
     float inv[NT][4];
+    bool xexact = true;
     if (XFIXED) {
         regroup_x<NT>(xs, lin, raw);
-        convert_x_slice<NT>(raw, xa, inv);
+        xexact = prepare_x_slice<NT>(raw, xa, inv, post);
     }
     __syncthreads();
 
@@ -310,6 +425,93 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
         }
     };
 
+    // The unit's dequantised weights, then its MFMAs: EXACT selects the fp16
+    // product or the exact fp32 one (activations held as raw bf16).
+    auto multiply = [&](auto exact_tag, int buf, float (&part)[NT][4]) {
+        constexpr bool EXACT = decltype(exact_tag)::value;
+        // Regroup the codes: lane (j, g) takes bytes 32b + 8g (8 bytes) of
+        // row j for block b.  All lookups of the unit are issued before the
+        // first MFMA so the LDS latencies overlap.
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const u32x4_t v = qv[buf][q];
+            cs[((lane >> 3) + 8 * q) * kCPitch + (lane & 7)] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+        const char *crow = reinterpret_cast<const char *>(cs + j * kCPitch);
+        uint2 qw[kSliceBlocks];
+#pragma unroll
+        for (int b = 0; b < kSliceBlocks; ++b) qw[b] = *reinterpret_cast<const uint2 *>(crow + 32 * b + 8 * g);
+        half8_t bop[kSliceBlocks][2];
+#pragma unroll
+        for (int b = 0; b < kSliceBlocks; ++b) {
+            // Per-block adjustment of the table pairs: affine subtracts
+            // z - 8, NVFP4 multiplies by the lane's E4M3 scale (both exact
+            // in fp16).
+            // (The values of row j, block b sit in lane 4j + b.)
+            half2_t adj = {0, 0};
+            if constexpr (FMT == kGemmAffine) {
+                const _Float16 z = (_Float16)(f16_bits_to_f32(__shfl(zc[buf], 4 * j + b) & 0xFFFFu) - 8.0f);
+                adj = half2_t{z, z};
+            } else if constexpr (FMT == kGemmNvfp4) {
+                const uint32_t d = __shfl(sc[buf], 4 * j + b);
+                const _Float16 v = (_Float16)e4m3_value(d >> (8 * g));
+                adj = half2_t{v, v};
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const uint32_t w = s ? qw[b].y : qw[b].x;
+                half2_t p0 = lut_pair<0>(lut, w, laneoff);
+                half2_t p1 = lut_pair<1>(lut, w, laneoff);
+                half2_t p2 = lut_pair<2>(lut, w, laneoff);
+                half2_t p3 = lut_pair<3>(lut, w, laneoff);
+                if constexpr (FMT == kGemmAffine) {
+                    p0 -= adj; p1 -= adj; p2 -= adj; p3 -= adj;
+                } else if constexpr (FMT == kGemmNvfp4) {
+                    p0 *= adj; p1 *= adj; p2 *= adj; p3 *= adj;
+                }
+                bop[b][s] = half8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+            }
+        }
+        if constexpr (FMT == kGemmNvfp4) {
+            // Scales already in the weights: one accumulation over the slice.
+            float4_t tile[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) tile[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int b = 0; b < kSliceBlocks; ++b)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    tile[t] = slab_mfma<EXACT>(xa[t][b][0], bop[b][0], tile[t]);
+                    tile[t] = slab_mfma<EXACT>(xa[t][b][1], bop[b][1], tile[t]);
+                }
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) part[t][r] = tile[t][r];
+        } else {
+            float sb[kSliceBlocks];
+#pragma unroll
+            for (int b = 0; b < kSliceBlocks; ++b) sb[b] = f16_bits_to_f32(__shfl(sc[buf], 4 * j + b) & 0xFFFFu);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) part[t][r] = 0.0f;
+#pragma unroll
+            for (int b = 0; b < kSliceBlocks; ++b) {
+                float4_t tile[NT];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    tile[t] = slab_mfma<EXACT>(xa[t][b][0], bop[b][0], float4_t{0.0f, 0.0f, 0.0f, 0.0f});
+                    tile[t] = slab_mfma<EXACT>(xa[t][b][1], bop[b][1], tile[t]);
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) part[t][r] = fmaf(tile[t][r], sb[b], part[t][r]);
+            }
+        }
+    };
+
     auto consume = [&](int buf) {
         if (!XFIXED) {
             // Long rows: this slice's activations, regrouped through the
@@ -319,57 +521,14 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
             load_x_linear<NT, XP>(xrs, K, nsb, wave + nw * cu_si, lin);
             __syncthreads();
             regroup_x<NT>(xs, lin, raw);
-            convert_x_slice<NT>(raw, xa, inv);
+            xexact = prepare_x_slice<NT>(raw, xa, inv, post);
             __syncthreads();
         }
-        // Regroup the codes: lane (j, g) takes bytes 32b + 8g (8 bytes) of
-        // row j for block b; the scale of row j, block b is held by lane
-        // 4j + b.  All lookups of the unit are issued before the first MFMA
-        // so the LDS latencies overlap.
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const u32x4_t v = qv[buf][q];
-            cs[((lane >> 3) + 8 * q) * kCPitch + (lane & 7)] = make_uint4(v.x, v.y, v.z, v.w);
-        }
-        const char *crow = reinterpret_cast<const char *>(cs + j * kCPitch);
-        uint2 qw[kSliceBlocks];
-        float sb[kSliceBlocks];
-#pragma unroll
-        for (int b = 0; b < kSliceBlocks; ++b) {
-            qw[b] = *reinterpret_cast<const uint2 *>(crow + 32 * b + 8 * g);
-            sb[b] = f16_bits_to_f32(__shfl(sc[buf], 4 * j + b) & 0xFFFFu);
-        }
-        half8_t bop[kSliceBlocks][2];
-#pragma unroll
-        for (int b = 0; b < kSliceBlocks; ++b)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const uint32_t w = s ? qw[b].y : qw[b].x;
-                const half2_t p0 = lut_pair<0>(lut, w, laneoff);
-                const half2_t p1 = lut_pair<1>(lut, w, laneoff);
-                const half2_t p2 = lut_pair<2>(lut, w, laneoff);
-                const half2_t p3 = lut_pair<3>(lut, w, laneoff);
-                bop[b][s] = half8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-            }
         float part[NT][4];
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) part[t][r] = 0.0f;
-#pragma unroll
-        for (int b = 0; b < kSliceBlocks; ++b) {
-            float4_t tile[NT];
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                tile[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][b][0], bop[b][0], float4_t{0.0f, 0.0f, 0.0f, 0.0f},
-                                                                 0, 0, 0);
-                tile[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][b][1], bop[b][1], tile[t], 0, 0, 0);
-            }
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) part[t][r] = fmaf(tile[t][r], sb[b], part[t][r]);
-        }
+        if (__builtin_expect(xexact, 1))
+            multiply(std::true_type{}, buf, part);
+        else
+            multiply(std::false_type{}, buf, part);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -426,15 +585,28 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
     }
 }
 
-hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
-                              const uint16_t *X, int64_t N, float *Y, hipStream_t stream) {
-    // A chunk of one token is the GEMV (measured on the 11008 x 2048 prefill
-    // shape: 5.3 us against 7.1 us for the matrix-core kernel, whose set-up
-    // and 16-token tiles do not pay for one token).  A row-per-wave kernel
-    // sharing each lookup among 2..4 tokens measured slower than the
-    // matrix-core kernel (7.5 and 11.1 us at N = 2 and 4).
-    if (N == 1) return launch_gemv(codes, scales, M, K, X, Y, stream);
-    if (gemv_tokens_fits(M, K, N)) return launch_gemv_tokens(codes, scales, M, K, X, N, Y, stream);
+namespace {
+
+// The kernel for a chunk of N tokens (2 <= N <= 32).  Token pairs loaded:
+// the smallest of 1, 2, 4, 8 (one 16-token half) or 12, 16 (two halves)
+// that covers N for the NF4 format; the extra formats take 4, 8 or 16.
+template <int FMT, bool XF>
+const void *smalln_kernel_for(int64_t N) {
+    if constexpr (FMT == kGemmNf4) {
+        if (N <= 2) return reinterpret_cast<const void *>(&gemm_smalln_kernel<1, XF ? 2 : 0, XF, 1, FMT>);
+        if (N <= 4) return reinterpret_cast<const void *>(&gemm_smalln_kernel<1, XF ? 2 : 0, XF, 2, FMT>);
+        if (N <= 8) return reinterpret_cast<const void *>(&gemm_smalln_kernel<1, XF ? 2 : 0, XF, 4, FMT>);
+        if (N <= 16) return reinterpret_cast<const void *>(&gemm_smalln_kernel<1, XF ? 2 : 0, XF, 8, FMT>);
+        if (N <= 24) return reinterpret_cast<const void *>(&gemm_smalln_kernel<2, XF ? 2 : 0, XF, 12, FMT>);
+        return reinterpret_cast<const void *>(&gemm_smalln_kernel<2, XF ? 2 : 0, XF, 16, FMT>);
+    } else {
+        if (N <= 8) return reinterpret_cast<const void *>(&gemm_smalln_kernel<1, XF ? 2 : 0, XF, 4, FMT>);
+        if (N <= 16) return reinterpret_cast<const void *>(&gemm_smalln_kernel<1, XF ? 2 : 0, XF, 8, FMT>);
+        return reinterpret_cast<const void *>(&gemm_smalln_kernel<2, XF ? 2 : 0, XF, 16, FMT>);
+    }
+}
+
+int device_cus() {
     static int cus[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -444,37 +616,53 @@ hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int6
             n = 256;
         cus[dev] = n;
     }
-    // One workgroup of 8 waves per CU (the table and the staging areas take
-    // 148 KB of LDS).  Chunks of up to 16 tokens take one MFMA per slab of
-    // weights, larger ones two.  Rows of up to 8 slices (K <= 2048) keep the
-    // activations in registers; longer rows reload them per tile.
+    return cus[dev];
+}
+
+// One workgroup of 8 waves per CU (the table and the staging areas take
+// 148 KB of LDS).  Chunks of up to 16 tokens take one MFMA per slab of
+// weights, larger ones two.  Rows of up to 8 slices (K <= 2048) keep the
+// activations in registers; longer rows reload them per tile.
+template <int FMT>
+hipError_t launch_matrix_core(const uint8_t *codes, const void *scales, const uint16_t *zeros,
+                              const float *tscale, int64_t M, int64_t K, const uint16_t *X, int64_t N, float *Y,
+                              hipStream_t stream) {
     const int64_t tiles = (M + kTileRows - 1) / kTileRows;
-    int64_t grid = tiles < cus[dev] ? tiles : cus[dev];
+    const int cus = device_cus();
+    int64_t grid = tiles < cus ? tiles : cus;
     if (grid < 1) grid = 1;
     int64_t tiles_q = tiles / grid;
     int tiles_rem = (int)(tiles % grid);
     const int nslices = (int)((K / 64 + kSliceBlocks - 1) / kSliceBlocks);
     int k = (int)K, n = (int)N;
-    void *args[] = {&codes, &scales, &M, &k, &X, &n, &Y, &tiles_q, &tiles_rem};
-    // Token pairs loaded: the smallest of 1, 2, 4, 8 (one 16-token half) or
-    // 12, 16 (two halves) that covers N.
-    const void *fn;
-    if (nslices <= kGemmMaxWaves) {
-        if (N <= 2) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 2, true, 1>);
-        else if (N <= 4) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 2, true, 2>);
-        else if (N <= 8) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 2, true, 4>);
-        else if (N <= 16) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 2, true, 8>);
-        else if (N <= 24) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<2, 2, true, 12>);
-        else fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<2, 2, true, 16>);
-    } else {
-        if (N <= 2) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 0, false, 1>);
-        else if (N <= 4) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 0, false, 2>);
-        else if (N <= 8) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 0, false, 4>);
-        else if (N <= 16) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<1, 0, false, 8>);
-        else if (N <= 24) fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<2, 0, false, 12>);
-        else fn = reinterpret_cast<const void *>(&gemm_smalln_kernel<2, 0, false, 16>);
-    }
+    void *args[] = {&codes, &scales, &zeros, &tscale, &M, &k, &X, &n, &Y, &tiles_q, &tiles_rem};
+    const void *fn = nslices <= kGemmMaxWaves ? smalln_kernel_for<FMT, true>(N) : smalln_kernel_for<FMT, false>(N);
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * kGemmMaxWaves), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                              const uint16_t *X, int64_t N, float *Y, hipStream_t stream) {
+    // A chunk of one token is the GEMV (measured on the 11008 x 2048 prefill
+    // shape: 5.3 us against 7.1 us for the matrix-core kernel, whose set-up
+    // and 16-token tiles do not pay for one token).  Two or three tokens on
+    // short rows share each table lookup in the GEMV kernels.
+    if (N == 1) return launch_gemv(codes, scales, M, K, X, Y, stream);
+    if (gemv_tokens_fits(M, K, N)) return launch_gemv_tokens(codes, scales, M, K, X, N, Y, stream);
+    return launch_matrix_core<kGemmNf4>(codes, scales, nullptr, nullptr, M, K, X, N, Y, stream);
+}
+
+hipError_t launch_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
+                                     int64_t K, const uint16_t *X, int64_t N, float *Y, hipStream_t stream) {
+    if (N == 1) return launch_gemv_affine(codes, scales, zeros, M, K, X, Y, stream);
+    return launch_matrix_core<kGemmAffine>(codes, scales, zeros, nullptr, M, K, X, N, Y, stream);
+}
+
+hipError_t launch_gemm_smalln_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscale, int64_t M,
+                                    int64_t K, const uint16_t *X, int64_t N, float *Y, hipStream_t stream) {
+    if (N == 1) return launch_gemv_nvfp4(codes, scales, tscale, M, K, X, Y, stream);
+    return launch_matrix_core<kGemmNvfp4>(codes, scales, nullptr, tscale, M, K, X, N, Y, stream);
 }
 
 }  // namespace q4

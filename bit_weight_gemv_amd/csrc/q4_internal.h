@@ -53,6 +53,12 @@ hipError_t launch_gemv_fused(const FusedOperand *ops, int count, bool swiglu, in
 
 hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                               const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
+// The prefill product of the affine and NVFP4-style formats (N == 1: their
+// GEMV).  Arguments are validated by the caller.
+hipError_t launch_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
+                                     int64_t K, const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
+hipError_t launch_gemm_smalln_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscale, int64_t M,
+                                    int64_t K, const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
 
 // Rows ids[0..n) of a packed matrix into fp32 or bf16 rows; workgroup 0
 // writes *status.  Arguments are validated by the caller.

@@ -42,8 +42,8 @@ constexpr uint32_t small_int_f16_bits(int v) {
     return sign | (uint32_t)(e + 15) << 10 | (uint32_t)((a - (1 << e)) << (10 - e));
 }
 // The affine format's table: entry b is the pair (lo - 8, hi - 8) of the
-// byte's two codes, centred so that the zero-point term subtracted later is
-// (z - 8) times the activation sum (less cancellation than z times it).
+// byte's two codes (exact small integers); the product subtracts z - 8 from
+// each before it multiplies, so every term is (code - z) x.
 constexpr PairTable make_affine_pair_table() {
     PairTable t{};
     for (int b = 0; b < 256; ++b)

@@ -136,11 +136,10 @@ int q4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
  * Every weight is read once per call).
  *   X: bf16 bit patterns [N][K] row-major, 16-byte aligned.
  *   Y: fp32 [N][M] row-major, 4-byte aligned; must not overlap the inputs.
- * Same accuracy statement as q4_gemv, with one exception: chunks of four or
- * more tokens take a token's activations exactly only while, within each
- * 256-weight slice of K, none that is nonzero lies more than 2^31 below the
- * slice's largest magnitude (smaller ones are rounded to fp16 subnormals, an
- * absolute error of at most 2^-39 of that largest magnitude each).  A chunk
+ * Same accuracy statement as q4_gemv, for every finite X: chunks of four or
+ * more tokens take each token's activations exactly as fp16 under a power
+ * of two per 256-weight slice of K, or as fp32 where the slice's nonzero
+ * values span more than 2^31 (a slower path for such inputs only).  A chunk
  * of one token is computed by the q4_gemv kernels (Y[0] is then
  * bit-identical to q4_gemv of X[0]);
  * chunks of two or three tokens on rows of at most 2048 weights (and at most
@@ -306,6 +305,37 @@ int q4_pack_nvfp4(const float *W, int64_t M, int64_t K, uint8_t *codes,
 int q4_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales,
                   const float *tscale, int64_t M, int64_t K,
                   const uint16_t *x, float *y, void *stream);
+
+/*
+ * The prefill-chunk forms of the two formats above (as q4_gemm_smalln: the
+ * deep-fold "Decode V2" page, section 0 Goals, runs a prompt as chunks of up
+ * to 32 tokens through one product; accel/tensor func Int4MatMul reads the
+ * matrix once per tile of tokens).  Every weight is read once per call.
+ *   X: bf16 bits [N][K] row-major, 16-byte aligned; 0 <= N <= Q4_MAX_N.
+ *   Y: fp32 [N][M] row-major, 4-byte aligned; must not overlap the inputs.
+ * N == 1 runs the format's GEMV (Y[0] is bit-identical to it); N == 0 is a
+ * no-op.  Accuracy as q4_gemv, for every finite X: each token's activations
+ * enter exactly (fp16 under a power of two per 256-weight slice, or as fp32
+ * where a slice spans more than 2^31).  Errors as q4_gemm_smalln.
+ *
+ * q4_gemm_smalln_affine -- Y[n][m] = sum_k (code(m,k) - z[m][k/64])
+ * * s[m][k/64] * X[n][k]; codes, scales and zeros as q4_gemv_affine.
+ */
+int q4_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scales,
+                          const uint16_t *zeros, int64_t M, int64_t K,
+                          const uint16_t *X, int64_t N, float *Y,
+                          void *stream);
+
+/*
+ * q4_gemm_smalln_nvfp4 -- Y[n][m] = s * sum_k E2M1(code(m,k))
+ * * E4M3(scale[m][k/16]) * X[n][k]; codes, scales and tscale as
+ * q4_gemv_nvfp4, except that scales must be 4-byte aligned (the four scale
+ * bytes of a 64-block are read as one dword).
+ */
+int q4_gemm_smalln_nvfp4(const uint8_t *codes, const uint8_t *scales,
+                         const float *tscale, int64_t M, int64_t K,
+                         const uint16_t *X, int64_t N, float *Y,
+                         void *stream);
 
 /*
  * Packed row gather (deep-fold "Decode V2" page, run notes of section 6: the

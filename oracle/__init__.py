@@ -332,6 +332,21 @@ def gemv_affine(codes, scales, zeros, M: int, K: int, x_bits, rows=None, threads
     return y, S
 
 
+def gemm_affine(codes, scales, zeros, M: int, K: int, X_bits, threads: int = 1):
+    """Y, S fp64 [N, M] of the affine format for X bf16 bits [N, K]: the
+    prefill product is, by definition, one GEMV per token (accel/tensor
+    func Int4MatMul: Y[n] = W . X[n])."""
+    X_bits = np.ascontiguousarray(X_bits, np.uint16)
+    if X_bits.ndim != 2 or X_bits.shape[1] != K:
+        raise ValueError("oracle.gemm_affine: X must be [N, K]")
+    N = X_bits.shape[0]
+    Y = np.zeros((N, M), np.float64)
+    S = np.zeros((N, M), np.float64)
+    for n in range(N):
+        Y[n], S[n] = gemv_affine(codes, scales, zeros, M, K, X_bits[n], threads=threads)
+    return Y, S
+
+
 def e4m3_to_f64(b: int) -> float:
     return float(_load().oracle_e4m3_to_f64(int(b)))
 
@@ -391,6 +406,20 @@ def gemv_nvfp4(codes, scales, s: float, M: int, K: int, x_bits, rows=None, threa
 
     _run_rows(r1 - r0, threads, run, [0])
     return y, S
+
+
+def gemm_nvfp4(codes, scales, s: float, M: int, K: int, X_bits, threads: int = 1):
+    """Y, S fp64 [N, M] of the NVFP4-style format for X bf16 bits [N, K]:
+    one GEMV per token, as gemm_affine."""
+    X_bits = np.ascontiguousarray(X_bits, np.uint16)
+    if X_bits.ndim != 2 or X_bits.shape[1] != K:
+        raise ValueError("oracle.gemm_nvfp4: X must be [N, K]")
+    N = X_bits.shape[0]
+    Y = np.zeros((N, M), np.float64)
+    S = np.zeros((N, M), np.float64)
+    for n in range(N):
+        Y[n], S[n] = gemv_nvfp4(codes, scales, s, M, K, X_bits[n], threads=threads)
+    return Y, S
 
 
 def quantize_x8(x_bits, words: int = 2):

@@ -72,6 +72,14 @@ hipError_t launch_gemm_smalln(const uint8_t *, const uint16_t *, int64_t M, int6
                               float *, hipStream_t) {
     return note("gemm_smalln M=%lld K=%lld N=%lld", M, K, N);
 }
+hipError_t launch_gemm_smalln_affine(const uint8_t *, const uint16_t *, const uint16_t *, int64_t M, int64_t K,
+                                     const uint16_t *, int64_t N, float *, hipStream_t) {
+    return note("gemm_smalln_affine M=%lld K=%lld N=%lld", M, K, N);
+}
+hipError_t launch_gemm_smalln_nvfp4(const uint8_t *, const uint8_t *, const float *, int64_t M, int64_t K,
+                                    const uint16_t *, int64_t N, float *, hipStream_t) {
+    return note("gemm_smalln_nvfp4 M=%lld K=%lld N=%lld", M, K, N);
+}
 hipError_t launch_gather_rows(const uint8_t *, const uint16_t *, int64_t M, int64_t K, const int32_t *, int64_t n,
                               bool bf16, void *, int32_t *, hipStream_t) {
     return note(bf16 ? "gather_rows_bf16 M=%lld K=%lld n=%lld" : "gather_rows_f32 M=%lld K=%lld n=%lld", M, K, n);

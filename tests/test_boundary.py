@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused",
               "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_pack_nvfp4", "q4_gemv_nvfp4",
-              "q4_quantize_x8", "q4_gemv_affine_x8",
+              "q4_quantize_x8", "q4_gemv_affine_x8", "q4_gemm_smalln_affine", "q4_gemm_smalln_nvfp4",
               "q4_codebook", "q4_codes_bytes",
               "q4_scales_bytes", "q4_status_string"):
         assert n in names
@@ -282,6 +282,37 @@ def test_nvfp4_errors(q4):
     assert L.q4_gemv_nvfp4(A, B, C, 16, 128, D, B + 64, None) == q4.Q4_ERR_OVERLAP  # y over scales
     assert L.q4_gemv_nvfp4(A, B, C, 16, 128, D, C - 32, None) == q4.Q4_ERR_OVERLAP  # y over tscale
     # every call above fails a host check and launches nothing
+
+
+def test_gemm_formats_errors(q4):
+    L = q4.lib()
+    E = 0x50000000
+    M, K, N = 16, 128, 4  # codes 1 KB, scales/zeros 64 B, NVFP4 scales 128 B, X 1 KB, Y 256 B
+    aff = lambda c, s, z, m, k, x, n, y: L.q4_gemm_smalln_affine(c, s, z, m, k, x, n, y, None)
+    nv = lambda c, s, t, m, k, x, n, y: L.q4_gemm_smalln_nvfp4(c, s, t, m, k, x, n, y, None)
+    for f in (aff, nv):
+        assert f(A, B, C, M, K, D, 33, E) == q4.Q4_ERR_SHAPE
+        assert f(A, B, C, M, K, D, -1, E) == q4.Q4_ERR_SHAPE
+        assert f(A, B, C, M, 96, D, N, E) == q4.Q4_ERR_SHAPE
+        assert f(None, None, None, M, K, None, 0, None) == q4.Q4_OK
+        assert f(None, None, None, 0, K, None, N, None) == q4.Q4_OK
+        assert f(None, B, C, M, K, D, N, E) == q4.Q4_ERR_NULL
+        assert f(A, None, C, M, K, D, N, E) == q4.Q4_ERR_NULL
+        assert f(A, B, None, M, K, D, N, E) == q4.Q4_ERR_NULL
+        assert f(A, B, C, M, K, None, N, E) == q4.Q4_ERR_NULL
+        assert f(A, B, C, M, K, D, N, None) == q4.Q4_ERR_NULL
+        assert f(A + 8, B, C, M, K, D, N, E) == q4.Q4_ERR_ALIGN
+        assert f(A, B + 1, C, M, K, D, N, E) == q4.Q4_ERR_ALIGN
+        assert f(A, B, C, M, K, D + 8, N, E) == q4.Q4_ERR_ALIGN
+        assert f(A, B, C, M, K, D, N, E + 2) == q4.Q4_ERR_ALIGN
+        assert f(A, B, C, M, K, D, N, A + 1020) == q4.Q4_ERR_OVERLAP  # Y over the codes' tail
+        assert f(A, B, C, M, K, D, N, D + 1020) == q4.Q4_ERR_OVERLAP  # Y over X's tail
+    assert aff(A, B, C + 1, M, K, D, N, E) == q4.Q4_ERR_ALIGN
+    assert aff(A, B, C, M, K, D, N, C + 60) == q4.Q4_ERR_OVERLAP      # Y over the zeros' tail
+    assert nv(A, B, C + 2, M, K, D, N, E) == q4.Q4_ERR_ALIGN
+    assert nv(A, B + 2, C, M, K, D, N, E) == q4.Q4_ERR_ALIGN          # NVFP4 scales: 4-byte aligned
+    assert nv(A, B, C, M, K, D, N, B + 124) == q4.Q4_ERR_OVERLAP      # Y over the NVFP4 scales' tail
+    assert nv(A, B, C, M, K, D, N, C) == q4.Q4_ERR_OVERLAP            # Y on the tensor scale
 
 
 def test_x8_errors(q4):

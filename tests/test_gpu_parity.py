@@ -369,7 +369,9 @@ def test_affine_and_nvfp4_wide_range_activations(env, M, K, kind):
     _check(y.cpu().numpy(), y_ref, S, f"nvfp4 gemv wide x={kind} M={M} K={K}")
 
 
-@pytest.mark.parametrize("M,K,N", [(300, 2048, 2), (300, 2048, 3), (3001, 1984, 3), (600, 11008, 1)])
+@pytest.mark.parametrize("M,K,N", [(300, 2048, 2), (300, 2048, 3), (3001, 1984, 3), (600, 11008, 1),
+                                   (300, 2048, 4), (300, 2048, 17), (3001, 1984, 32), (77, 4160, 17),
+                                   (70, 11008, 32)])
 def test_gemm_smalln_wide_range_activations(env, M, K, N):
     """Each token of the chunk takes a different wide-range recipe."""
     torch, q4, dev = env
@@ -393,6 +395,65 @@ def test_fused_wide_range_activations(env, swiglu, Ms, K, kind):
     # Bias and residual small next to the products, so the products' bound
     # is what is tested.
     _fused_case(env, Ms, K, seed, swiglu=swiglu, x=_wide_x(kind, K, seed), w_hook=_wide_w, bias_scale=1e-3)
+
+
+# The prefill product of the affine and NVFP4-style formats: one token (the
+# format's GEMV), two and three tokens, one and two 16-token halves,
+# activations in registers (K <= 2048, ragged last slice) and reloaded per
+# tile (longer rows), many tiles per workgroup.
+FMT_GEMM_CASES = [(300, 2048, 1), (300, 2048, 2), (1000, 1984, 3), (77, 4160, 17), (300, 2048, 32),
+                  (20000, 192, 5), (50, 2112, 20), (70, 11008, 32), (1, 64, 2)]
+
+
+def _nvfp4_upload(env, codes, scales, ts):
+    torch, q4, dev = env
+    return (cases.to_dev(codes, torch, dev), cases.to_dev(scales, torch, dev),
+            torch.tensor([ts], dtype=torch.float32, device=dev))
+
+
+def _gemm_formats_case(env, M, K, N, W, X, what):
+    torch, q4, dev = env
+    Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+    codes, scales, zeros, st = oracle.pack_affine(W)
+    assert st == 0
+    Y_ref, S = oracle.gemm_affine(codes, scales, zeros, M, K, X)
+    c, s, z = _affine_upload(env, codes, scales, zeros)
+    Y = q4.q4_gemm_smalln_affine(c, s, z, Xd)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, S, f"affine gemm {what} M={M} K={K} N={N}")
+    if N == 1:
+        y = q4.q4_gemv_affine(c, s, z, Xd[0].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(Y[0], y)
+    ncodes, nscales, ts, st = oracle.pack_nvfp4(W)
+    assert st == 0
+    Y_ref, S = oracle.gemm_nvfp4(ncodes, nscales, ts, M, K, X)
+    c, s, t = _nvfp4_upload(env, ncodes, nscales, ts)
+    Y = q4.q4_gemm_smalln_nvfp4(c, s, t, Xd)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, S, f"nvfp4 gemm {what} M={M} K={K} N={N}")
+    if N == 1:
+        y = q4.q4_gemv_nvfp4(c, s, t, Xd[0].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(Y[0], y)
+
+
+@pytest.mark.parametrize("M,K,N", FMT_GEMM_CASES)
+def test_gemm_smalln_formats_parity(env, M, K, N):
+    seed = 9500 + M + K + N
+    W = wl.weights(M, K, seed, std=0.5) + np.float32(0.03)
+    if M > 3:
+        W[3, :64] *= 1e-4   # subnormal NVFP4 block scales in the product
+    X = wl.activations(N, K, seed, "unit_rms")
+    _gemm_formats_case(env, M, K, N, W, X, "")
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 2048, 2), (300, 2048, 17), (77, 4160, 32)])
+def test_gemm_smalln_formats_wide_range_activations(env, M, K, N):
+    seed = 9600 + M + K + N
+    W = _wide_w(wl.weights(M, K, seed, std=0.5))
+    X = np.stack([_wide_x(WIDE_KINDS[(n + seed) % len(WIDE_KINDS)], K, seed + n) for n in range(N)])
+    _gemm_formats_case(env, M, K, N, W, X, "wide")
 
 
 def test_gemv_bit_exact_invariants(env):
@@ -493,13 +554,6 @@ def _full_inputs(name):
     return _FULL[name]
 
 
-def _sample_rows(M, n=1024, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([np.arange(min(64, M)), np.arange(max(0, M - 64), M),
-                                     rng.integers(0, M, n)]))
-    return rows
-
-
 @pytest.mark.parametrize("name", ["down", "gateup", "lm_head"])
 def test_full_size_pack_and_gemv(env, name):
     torch, q4, dev = env
@@ -514,14 +568,11 @@ def test_full_size_pack_and_gemv(env, name):
     assert np.array_equal(cases.bits16(scales, torch), s_ref), "pack scales differ"
     _log(f"{name}: GPU pack bit-exact ({time.time() - t:.1f}s incl. upload)")
     y = q4.q4_gemv(codes, scales, _x_dev(env, x)).cpu().numpy()
-    rows = _sample_rows(M)
-    y_ref, S = oracle.gemv_row_list(c_ref, s_ref, M, K, x, rows)
-    _check(y[rows], y_ref, S, f"{name} sampled rows ({rows.size})")
+    t = time.time()
+    y_full, S_full = oracle.gemv(c_ref, s_ref, M, K, x, threads=min(16, os.cpu_count() or 1))
+    _log(f"{name}: full oracle GEMV in {time.time() - t:.1f}s")
+    _check(y, y_full, S_full, f"{name} all {M} rows")
     if name == "lm_head":
-        t = time.time()
-        y_full, S_full = oracle.gemv(c_ref, s_ref, M, K, x, threads=min(16, os.cpu_count() or 1))
-        _log(f"lm_head: full oracle GEMV in {time.time() - t:.1f}s")
-        _check(y, y_full, S_full, "lm_head all rows")
         a_ref = oracle.argmax(y_full)
         a_gpu = oracle.argmax(y)
         top = np.sort(y_full)[-2:]
@@ -547,7 +598,13 @@ GEMM_SHAPES = [(1, 64, 1), (40, 128, 2), (100, 512, 3), (64, 2048, 4), (97, 1024
                # two or three tokens on short rows take the GEMV with shared
                # lookups (up to 12 four-row tiles per CU), beyond that the
                # matrix-core kernel
-               (11008, 2048, 2), (3001, 1984, 3), (5, 64, 2), (1001, 576, 3), (12289, 2048, 3)]
+               (11008, 2048, 2), (3001, 1984, 3), (5, 64, 2), (1001, 576, 3), (12289, 2048, 3),
+               # every matrix-core instantiation: two tokens past the
+               # shared-lookup GEMV's limit (activations in registers, one
+               # token pair loaded), and long rows with 1, 2, 4, 8 token pairs
+               # in one half and 12 in two halves
+               (12293, 2048, 2), (70, 11008, 2), (65, 4096, 3), (97, 4160, 8), (33, 11008, 16),
+               (50, 2112, 20)]
 
 
 @pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
@@ -595,7 +652,9 @@ def test_gemm_rows_match_gemv(env):
         assert np.all(np.abs(Y[n] - y) <= 2e-3 * Sn + 2e-5)
 
 
-def test_gemm_smalln_full_size_sampled(env):
+def test_gemm_smalln_full_size(env):
+    """The prefill shape (11008 x 2048), chunks of 32 .. 1 tokens, every
+    output against the oracle."""
     torch, q4, dev = env
     c = wl.CONFIGS["smalln"]
     M, K, N = c["M"], c["K"], c["N"]
@@ -606,12 +665,12 @@ def test_gemm_smalln_full_size_sampled(env):
     Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
     c_ref, s_ref, _ = oracle.pack(W, threads=min(16, os.cpu_count() or 1))
     assert np.array_equal(codes.cpu().numpy(), c_ref)
-    for n_tok in (32, 16, 8, 4, 2, 1):
+    t = time.time()
+    Y_ref, S = oracle.gemm(c_ref, s_ref, M, K, X)
+    _log(f"smalln: oracle product of {N} tokens in {time.time() - t:.1f}s")
+    for n_tok in (32, 17, 16, 8, 4, 3, 2, 1):
         Y = q4.q4_gemm_smalln(codes, scales, Xd[:n_tok].contiguous()).cpu().numpy()
-        rows = _sample_rows(M, n=256, seed=n_tok)
-        for n in range(n_tok):
-            y_ref, S = oracle.gemv_row_list(c_ref, s_ref, M, K, X[n], rows)
-            _check(Y[n, rows], y_ref, S, f"smalln N={n_tok} token {n}")
+        _check(Y, Y_ref[:n_tok], S[:n_tok], f"smalln N={n_tok} all {M} rows")
 
 
 # ---------------------------------------------------------------------------

@@ -829,6 +829,22 @@ def test_affine_gemv_matches_blas_and_one_hot(oracle_mod):
         assert np.array_equal(yk, What[:, k])
 
 
+def test_affine_gemm_matches_blas(oracle_mod):
+    """The prefill product of the affine format against a BLAS product of
+    the dequantised matrix (an independent path: the matrix is built by
+    oracle_dequant_affine, the product by numpy)."""
+    M, K, N = 40, 320, 5
+    W = wl.weights(M, K, 61)
+    X = wl.activations(N, K, 61, "unit_rms")
+    codes, scales, zeros, st = oracle_mod.pack_affine(W)
+    assert st == 0
+    Y, S = oracle_mod.gemm_affine(codes, scales, zeros, M, K, X)
+    What = oracle_mod.dequant_affine(codes, scales, zeros, M, K)
+    Xv = wl.bf16_bits_to_f32(X).astype(np.float64)
+    assert np.all(np.abs(Y - Xv @ What.T) <= 1e-12 * (np.abs(Xv) @ np.abs(What).T))
+    assert np.allclose(S, np.abs(Xv) @ np.abs(What).T, rtol=1e-12, atol=0)
+
+
 def test_affine_exact_ties_go_down(oracle_mod):
     """s = 0.125 exactly (range 1.875 / 15) and -lo / s = 7.5 exactly: z takes
     the lower integer 7; weights on a level midpoint take the lower code."""
@@ -936,6 +952,21 @@ def test_nvfp4_closed_forms_and_ties(oracle_mod):
     assert list(c[32:34]) == [7, 2]
     What = oracle_mod.dequant_nvfp4(codes, scales, s, 1, 64)
     assert What[0, 32] == 6.0 and What[0, 0] == 2688.0
+
+
+def test_nvfp4_gemm_matches_blas(oracle_mod):
+    """The NVFP4-style prefill product against a BLAS product of the
+    dequantised matrix."""
+    M, K, N = 40, 320, 5
+    W = wl.weights(M, K, 62)
+    X = wl.activations(N, K, 62, "swiglu")
+    codes, scales, s, st = oracle_mod.pack_nvfp4(W)
+    assert st == 0
+    Y, S = oracle_mod.gemm_nvfp4(codes, scales, s, M, K, X)
+    What = oracle_mod.dequant_nvfp4(codes, scales, s, M, K)
+    Xv = wl.bf16_bits_to_f32(X).astype(np.float64)
+    assert np.all(np.abs(Y - Xv @ What.T) <= 1e-12 * (np.abs(Xv) @ np.abs(What).T))
+    assert np.allclose(S, np.abs(Xv) @ np.abs(What).T, rtol=1e-12, atol=0)
 
 
 def test_nvfp4_zero_tensor_and_refusal(oracle_mod):
