@@ -401,6 +401,32 @@ def affine_secondaries(torch, q4, wl, dev, steps, warmup):
                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": nb})
         del reps, codes, scales, zeros, x, y
         torch.cuda.empty_cache()
+    # The prefill product on the prefill shape (11008 x 2048), chunks of 32
+    # and 16 tokens.
+    c = wl.CONFIGS["smalln"]
+    M, K = c["M"], c["K"]
+    W = torch.from_numpy(wl.weights(M, K, c["seed"])).to(dev)
+    codes, scales, zeros, status = q4.q4_pack_affine(W)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError("q4_pack_affine flagged the prefill weights")
+    del W
+    reps = [(codes, scales, zeros)] + [(codes.clone(), scales.clone(), zeros.clone()) for _ in range(44)]
+    X = _upload_bits(torch, wl.activations(32, K, c["seed"], c["x"]), torch.bfloat16, dev)
+    for n in (32, 16):
+        Xn = X[:n].contiguous()
+        Y = torch.empty((n, M), dtype=torch.float32, device=dev)
+
+        def fn(cd, sl, zr, Xn=Xn, Y=Y):
+            q4.q4_gemm_smalln_affine(cd, sl, zr, Xn, Y)
+        ms, wall = time_graph(torch, fn, reps, steps, warmup)
+        nb = gemv_bytes(M, K, n) + M * K // 32
+        log(f"affine prefill N={n}: {ms * 1e3:.2f} us/call")
+        out.append({"workload": f"affine-format prefill {M}x{K} N={n}", "us_per_call": round(ms * 1e3, 3),
+                    "us_per_step_wall": round(wall * 1e3, 3), "achieved_GBs": round(nb / (ms * 1e-3) / 1e9, 1),
+                    "bytes": nb})
+    del reps, codes, scales, zeros, X
+    torch.cuda.empty_cache()
     return out
 
 
@@ -432,6 +458,32 @@ def nvfp4_secondaries(torch, q4, wl, dev, steps, warmup):
                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": nb})
         del reps, codes, scales, ts, x, y
         torch.cuda.empty_cache()
+    # The prefill product on the prefill shape (11008 x 2048), chunks of 32
+    # and 16 tokens.
+    c = wl.CONFIGS["smalln"]
+    M, K = c["M"], c["K"]
+    W = torch.from_numpy(wl.weights(M, K, c["seed"])).to(dev)
+    codes, scales, ts, status = q4.q4_pack_nvfp4(W)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError("q4_pack_nvfp4 flagged the prefill weights")
+    del W
+    reps = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(44)]
+    X = _upload_bits(torch, wl.activations(32, K, c["seed"], c["x"]), torch.bfloat16, dev)
+    for n in (32, 16):
+        Xn = X[:n].contiguous()
+        Y = torch.empty((n, M), dtype=torch.float32, device=dev)
+
+        def fn(cd, sl, Xn=Xn, Y=Y):
+            q4.q4_gemm_smalln_nvfp4(cd, sl, ts, Xn, Y)
+        ms, wall = time_graph(torch, fn, reps, steps, warmup)
+        nb = M * K // 2 + M * K // 16 + 4 + 2 * K * n + 4 * M * n
+        log(f"nvfp4 prefill N={n}: {ms * 1e3:.2f} us/call")
+        out.append({"workload": f"NVFP4-style prefill {M}x{K} N={n}", "us_per_call": round(ms * 1e3, 3),
+                    "us_per_step_wall": round(wall * 1e3, 3), "achieved_GBs": round(nb / (ms * 1e-3) / 1e9, 1),
+                    "bytes": nb})
+    del reps, codes, scales, ts, X
+    torch.cuda.empty_cache()
     return out
 
 
