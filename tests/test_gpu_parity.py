@@ -604,7 +604,10 @@ GEMM_SHAPES = [(1, 64, 1), (40, 128, 2), (100, 512, 3), (64, 2048, 4), (97, 1024
                # token pair loaded), and long rows with 1, 2, 4, 8 token pairs
                # in one half and 12 in two halves
                (12293, 2048, 2), (70, 11008, 2), (65, 4096, 3), (97, 4160, 8), (33, 11008, 16),
-               (50, 2112, 20)]
+               (50, 2112, 20),
+               # odd blocks a row with a last tile reaching past M, and 15
+               # tiles a workgroup
+               (3000, 1984, 32), (3000, 1984, 4), (3001, 1984, 17), (3001, 1984, 4), (60000, 2048, 8)]
 
 
 @pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
