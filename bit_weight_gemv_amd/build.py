@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libq4.so")
 # packed matrix's bytes (bench.py times it beside each GEMV).
 FLOOR_SOURCE = "q4_floor.hip"
 FLOOR_LIB = os.path.join(HERE, "libq4floor.so")
-SOURCES = ["q4_api.cpp", "q4_pack.hip", "q4_gemv.hip", "q4_gemm_smalln.hip", "q4_gather.hip", "q4_quant.hip"]
+SOURCES = ["q4_api.cpp", "q4_pack.hip", "q4_gemv.hip", "q4_gemm_smalln.hip", "q4_gemm_rows4.hip", "q4_gather.hip", "q4_quant.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

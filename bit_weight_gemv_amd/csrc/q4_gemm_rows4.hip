@@ -1,0 +1,409 @@
+// q4_gemm_rows4.hip -- the prefill product Y[n][m] = sum_k What[m,k] * X[n][k]
+// for chunks of 2..8 tokens on rows of at most 2048 weights (NF4 codebook
+// format), one 4-row tile per wave.
+//
+// What is computed: the same product as q4_gemm_smalln (the prefill form of
+// the deep-fold "Decode V2" page, section 0; accel/tensor func Int4MatMul's
+// reconstruction What = level[code] * s per 64-block), for the smallest
+// chunks.
+//
+// gfx950 design:
+//  * Tiles.  A chunk of a few tokens has as few rows per CU as the GEMV
+//    (11008 rows: 43 a CU), too few for 16-row matrix-core tiles to keep a
+//    CU's waves busy without splitting K between waves.  The 16-block
+//    v_mfma_f32_4x4x4_16b_f16 works on 4 x 4 blocks instead: block q (lanes
+//    4q .. 4q+3) multiplies 4 tokens by the 4 weight rows of the tile over
+//    4 k of its own, lane 4q + i supplying token i's activations (operand A)
+//    and row i's weights (operand B), and lane 4q + j receiving the 4
+//    tokens' sums of row j.  So each wave takes one tile of 4 rows and all
+//    of K, as the GEMV does, and the 16 blocks' sums are added across lanes
+//    at the end.  Chunks of 5..8 tokens take two groups of 4 tokens: two
+//    MFMAs per step on the same dequantised weights.
+//  * Loads.  Load p of a tile gives lane l row l % 4, bytes 16 (16p + l / 4)
+//    of the row: 16 lanes read 256 contiguous bytes of each of the 4 rows
+//    (measured at the speed of the GEMV's row-by-row order on 11008 x 2048).
+//    Lane group q therefore holds chunks 16p + q (32 k each) of all 4 rows.
+//  * Scales.  One dword per lane (two block scales of one row), handed to the
+//    lanes that need them by lane shuffles: a lane needs, per load p, the
+//    scale of its row for the block of chunk 16p + l / 4.  The scale
+//    multiplies the chunk's 4 x 4 fp32 sums (one per load p and lane).
+//  * Activations.  The workgroup converts the chunk's tokens once into an
+//    fp16 copy in LDS: one wave per (token, 512-k range), that range scaled
+//    by the power of two that puts its largest bf16 magnitude in
+//    [2^14, 2^15); the inverse joins the block scale of the chunks of that
+//    range.  A wave issues loads only for the pairs it converts: a load
+//    through a range that reads nothing still costs the CU's address unit
+//    as much as one that reads (on 11008 x 2048, issuing every wave the
+//    same number of loads, most reading nothing, took 5.8-6.0 us against
+//    5.1-5.3 us for 2..4 tokens).  The conversion is exact while no nonzero
+//    value of a range lies more than 2^31 below its largest (tested per
+//    lane, decided per wave).  If any range of the chunk fails the test the
+//    whole workgroup takes the exact loop instead: raw bf16 activations read
+//    per lane and widened to fp32, the fp16 levels widened likewise, and
+//    v_mfma_f32_4x4x1_16b_f32 (products exact, sums fp32).
+//  * Dequantisation.  The LDS byte -> fp16-pair table shared with the GEMV
+//    (64 bank-private copies; one ds_read_b32 per two weights).
+//  * Measured (11008 x 2048, A/B in one process against the kernels it
+//    replaces): 2 tokens 5.1 us (shared-lookup GEMV 6.3), 3 tokens 5.3
+//    (8.2), 4 tokens 5.3 (16-row matrix-core kernel 7.2), 8 tokens 7.3
+//    (7.5); the GEMV takes 4.9 us for one.  A third and fourth token group
+//    (9..16 tokens) measured slower than the 16-row kernel (10.7 against
+//    7.8 us at 16): every wave reads all of the chunk's activations from
+//    LDS and runs 8 MFMAs per 32 k and group, and the conversion grows with
+//    the chunk.
+#include "q4_device.h"
+#include "q4_internal.h"
+#include "q4_lut.h"
+
+namespace q4 {
+
+namespace {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kR4MaxK = 2048;
+constexpr int kR4Ranges = kR4MaxK / 512;  // 512-k ranges: one activation scale per token and range
+// Bytes per token of the fp16 copy: 16 bytes of padding put the four tokens
+// of a lane group's reads in different banks.
+constexpr int kR4Pitch = 2 * kR4MaxK + 16;
+constexpr int kR4MaxWaves = 12;
+constexpr int kR4MaxTokens = 8;
+
+// Pairs a wave converts at most: the launch gives NTG token groups at least
+// 4 NTG waves (at most 12).
+constexpr int rows4_min_waves(int ntg) { return 4 * ntg < kR4MaxWaves ? 4 * ntg : kR4MaxWaves; }
+constexpr int rows4_pairs_per_wave(int ntg) {
+    return ((16 * ntg + rows4_min_waves(ntg) - 1) / rows4_min_waves(ntg) + 1) / 2 * 2;
+}
+
+// A byte of the exponent table meaning "this range is not held exactly".
+constexpr int kR4Inexact = -128;
+
+// Lane l of the reduction receives from lane l - 2^L of its row of 16.
+template <int L>
+__device__ __forceinline__ float ror_lanes(float v) {
+    return dpp_f<dpp_row_ror(1 << L)>(v);
+}
+
+}  // namespace
+
+// NTG groups of 4 tokens (chunks of up to 4 NTG tokens), NTG = 1 or 2.
+template <int NTG>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) void gemm_rows4_kernel(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, int64_t M, int K,
+    const uint16_t *__restrict__ X, int N, float *__restrict__ Y) {
+    constexpr int NTOK = 4 * NTG;             // tokens the kernel holds
+    constexpr int kPairs = NTOK * kR4Ranges;  // (token, range) pairs at most
+    constexpr int kPPW = rows4_pairs_per_wave(NTG);
+    // The activation copy has one more row and the exponent table one more
+    // dword: a wave's batch of pairs may end past the chunk's last pair, and
+    // those (zero) results go there.
+    struct Smem {
+        uint32_t lut[kLutDwords];
+        uint4 xh[(NTOK + 1) * kR4Pitch / 16];
+        uint32_t meta[kPairs / 4 + 1];
+    };
+    __shared__ Smem sm;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = blockDim.x >> 6;
+    const int64_t tile = (int64_t)blockIdx.x * nw + wave;
+    const int64_t tiles = (M + 3) >> 2;
+    const int row_bytes = K >> 1;
+    const int nsb = K >> 6;       // 64-blocks (scales) a row
+    const int nch = K >> 5;       // 32-weight chunks a row
+    const int row = lane & 3;     // weight row (operand B) and token within a group (operand A) of this lane
+    const int grp = lane >> 2;    // lane group: chunk 16p + grp of load p
+
+    // Activations of the wave's (token, range) pairs: pair P = 4 t + r is
+    // token t, k = 512 r + 8 lane .. +7 for this lane, for P = wave + nw i
+    // below 4 N.  k past K and pairs past the last read zeros (offsets past
+    // the buffer).
+    const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(X, (uint32_t)N * (uint32_t)K * 2u);
+    const int npairs = 4 * N;
+    u32x4_t xraw[kPPW];
+#pragma unroll
+    for (int i = 0; i < kPPW; ++i) {
+        const int P = wave + nw * i;
+        const int t = P >> 2, k0 = 512 * (P & 3) + 8 * lane;
+        // (A wave with fewer pairs issues fewer loads: every load costs the
+        // CU's address unit time, whether or not it reads memory.)
+        if (P < npairs)
+            xraw[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, k0 < K ? (t * K + k0) * 2 : 0x7FFFFFF0, 0, 0);
+        else
+            xraw[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+
+    // The tile's scales, then its codes (rows past M and chunks past the
+    // row's end read zeros).  Scales: lane L reads dword L % 16 of row L / 16
+    // (the scales of blocks 2 (L % 16) and 2 (L % 16) + 1); issued first, so
+    // that waiting for them does not wait for the codes.
+    const bool live = tile < tiles;
+    const int64_t row0 = uniform64(live ? tile * 4 : 0);
+    const int rows = live ? (int)(M - row0 < 4 ? M - row0 : 4) : 0;
+    const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(scales + row0 * nsb, (uint32_t)(rows * nsb * 2));
+    const int sdw = lane & 15;
+    const uint32_t sdword = __builtin_amdgcn_raw_buffer_load_b32(
+        srs, 2 * sdw < nsb ? (lane >> 4) * nsb * 2 + 4 * sdw : 0x7FFFFFF0, 0, kLoadNonTemporal);
+    const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(codes + row0 * row_bytes, (uint32_t)(rows * row_bytes));
+    u32x4_t q[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int c = 16 * p + grp;
+        q[p] = __builtin_amdgcn_raw_buffer_load_b128(crs, c < nch ? row * row_bytes + 16 * c : 0x7FFFFFF0, 0,
+                                                     kLoadNonTemporal);
+    }
+
+    fill_lut(sm.lut);
+
+    // Convert the wave's pairs, two at a time (their cross-lane steps
+    // overlap): the range's largest magnitude (over the wave) fixes its power
+    // of two 2^e; each lane checks that its nonzero values stay exact under
+    // it (biased exponent >= 110 - e, the last bit then at or above fp16's
+    // subnormal spacing), and one ballot decides.
+#pragma unroll
+    for (int i0 = 0; i0 < kPPW; i0 += 2) {
+        if (wave + nw * i0 >= npairs) break;
+        float m[2];
+        uint32_t lo[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            u16x2_t mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const u16x2_t mag = __builtin_bit_cast(u16x2_t, xraw[i0 + b][c] & 0x7FFF7FFFu);
+                mx = __builtin_elementwise_max(mx, mag);
+                mn = __builtin_elementwise_min(mn, mag - u16x2_t{1, 1});
+            }
+            // Magnitude bits as fp32 values (bf16 bits shifted up) keep
+            // their order, so the float max of the DPP helpers finds the
+            // largest.
+            m[b] = __builtin_bit_cast(float, (uint32_t)(mx.x > mx.y ? mx.x : mx.y) << 16);
+            lo[b] = mn.x < mn.y ? mn.x : mn.y;
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) m[b] = row16_max(m[b]);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            m[b] = fmaxf(m[b], __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, m[b]),
+                                                                                     0x401F)));
+#pragma unroll
+        for (int b = 0; b < 2; ++b) m[b] = fmaxf(m[b], __shfl_xor(m[b], 32));
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int P = wave + nw * (i0 + b);
+            int E = __builtin_amdgcn_readfirstlane((int)(__builtin_bit_cast(uint32_t, m[b]) >> 23));
+            if (E < 1) E = 1;
+            int e = 141 - E;
+            e = e > 126 ? 126 : (e < -126 ? -126 : e);
+            const int thr = 110 - e;
+            const bool ok = lo[b] == 0xFFFFu || thr <= 0 || lo[b] + 1u >= ((uint32_t)thr << 7);
+            const bool exact = __builtin_amdgcn_ballot_w64(!ok) == 0;
+            const float up = exp2i(e);
+            half2_t h[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t w = xraw[i0 + b][c];
+                h[c] = half2_t{(_Float16)(__builtin_bit_cast(float, w << 16) * up),
+                               (_Float16)(__builtin_bit_cast(float, w & 0xFFFF0000u) * up)};
+            }
+            const bool real = P < npairs;
+            const int t = real ? P >> 2 : NTOK, r = P & 3;
+            sm.xh[(t * kR4Pitch + (512 * r + 8 * lane) * 2) / 16] = make_uint4(
+                __builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
+                __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3]));
+            if (lane == 0) reinterpret_cast<int8_t *>(sm.meta)[real ? P : kPairs] = (int8_t)(exact ? e : kR4Inexact);
+        }
+    }
+    __syncthreads();
+
+    // Per (token, range): the exponent e (its inverse power of two joins the
+    // block scale); any inexact range of a token in the chunk sends the
+    // workgroup to the exact loop.
+    int eb[NTOK];
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) eb[t] = __builtin_amdgcn_readfirstlane((int)sm.meta[t]);
+    bool all_exact = true;
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t)
+#pragma unroll
+        for (int r = 0; r < kR4Ranges; ++r)
+            all_exact = all_exact && ((int)(int8_t)(eb[t] >> (8 * r)) != kR4Inexact || t >= N);
+
+    // The scale of this lane's row for the block of chunk 16p + grp: dword
+    // (8p + grp / 2) / 2 of the row, held by lane 16 row + 4p + grp / 4.
+    float sc[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t d = (uint32_t)__shfl((int)sdword, 16 * row + 4 * p + (grp >> 2));
+        sc[p] = f16_bits_to_f32((d >> (16 * ((grp >> 1) & 1))) & 0xFFFFu);
+    }
+
+    const uint32_t laneoff = (uint32_t)lane << 2;
+    // acc[4 g + t]: token 4 g + t of row `row`, summed over this lane group's
+    // chunks.
+    float acc[NTOK];
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) acc[t] = 0.0f;
+    if (__builtin_expect(all_exact, 1)) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const u32x4_t w = q[p];
+            half4_t wb[8];  // this lane's 32 weights of chunk 16p + grp, 4 a step
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const half2_t p0 = lut_pair<0>(sm.lut, w[d], laneoff);
+                const half2_t p1 = lut_pair<1>(sm.lut, w[d], laneoff);
+                const half2_t p2 = lut_pair<2>(sm.lut, w[d], laneoff);
+                const half2_t p3 = lut_pair<3>(sm.lut, w[d], laneoff);
+                wb[2 * d] = half4_t{p0.x, p0.y, p1.x, p1.y};
+                wb[2 * d + 1] = half4_t{p2.x, p2.y, p3.x, p3.y};
+            }
+#pragma unroll
+            for (int g = 0; g < NTG; ++g) {
+                // Token 4g + row's fp16 activations of chunk 16p + grp (64 bytes).
+                const uint4 *xp = sm.xh + ((4 * g + row) * kR4Pitch + 64 * (16 * p + grp)) / 16;
+                float4_t D = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint4 xv = xp[d];
+                    D = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, uint2{xv.x, xv.y}), wb[2 * d],
+                                                           D, 0, 0, 0);
+                    D = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, uint2{xv.z, xv.w}),
+                                                           wb[2 * d + 1], D, 0, 0, 0);
+                }
+                // (D times the block scale first: the product stays finite,
+                // and a zero sum stays zero under the largest inverse power
+                // of two.)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int e = (int)(int8_t)(eb[4 * g + t] >> (8 * p));
+                    acc[4 * g + t] = fmaf(D[t] * sc[p], exp2i(-e), acc[4 * g + t]);
+                }
+            }
+        }
+    } else {
+        // Exact loop: raw bf16 activations of token 4g + row (zeros past N
+        // and past K), one k per MFMA.
+#pragma unroll 1
+        for (int p = 0; p < 4; ++p) {
+            const int c = 16 * p + grp;
+            const u32x4_t w = q[p];
+            half2_t pr[16];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                pr[4 * d] = lut_pair<0>(sm.lut, w[d], laneoff);
+                pr[4 * d + 1] = lut_pair<1>(sm.lut, w[d], laneoff);
+                pr[4 * d + 2] = lut_pair<2>(sm.lut, w[d], laneoff);
+                pr[4 * d + 3] = lut_pair<3>(sm.lut, w[d], laneoff);
+            }
+#pragma unroll 1
+            for (int g = 0; g < NTG; ++g) {
+                const int t = 4 * g + row;
+                const bool ok = t < N && c < nch;
+                u32x4_t xr[4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    xr[d] = __builtin_amdgcn_raw_buffer_load_b128(
+                        xrs, ok ? (t * K + 32 * c) * 2 + 16 * d : 0x7FFFFFF0, 0, 0);
+                float4_t D = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        // k = 8d + 2b and 8d + 2b + 1 of the chunk
+                        uint32_t xw = xr[d][b];
+                        __asm__ volatile("" : "+v"(xw));
+                        D = __builtin_amdgcn_mfma_f32_4x4x1f32(__builtin_bit_cast(float, xw << 16),
+                                                               (float)pr[4 * d + b].x, D, 0, 0, 0);
+                        D = __builtin_amdgcn_mfma_f32_4x4x1f32(__builtin_bit_cast(float, xw & 0xFFFF0000u),
+                                                               (float)pr[4 * d + b].y, D, 0, 0, 0);
+                    }
+                // (acc is indexed at run time here; the loop over groups is
+                // kept rolled to hold the exact loop's registers down.)
+#pragma unroll
+                for (int gg = 0; gg < NTG; ++gg)
+                    if (gg == g)
+#pragma unroll
+                        for (int tt = 0; tt < 4; ++tt) acc[4 * gg + tt] = fmaf(D[tt], sc[p], acc[4 * gg + tt]);
+            }
+        }
+    }
+
+    // Sum the 16 lane groups.  Pairing levels over lane bits 2 and 3 (DPP
+    // row rotations by 4 and 8) leave each lane one token of each group,
+    // (l / 4) % 4, summed over its row of 16 for weight row l % 4; levels
+    // over bit 4 (lanes l ^ 16) then picks the group (two groups) or adds
+    // the other rows (one group), and lanes l ^ 32 are added.  Lane l ends
+    // with token 4 (l / 16 % NTG) + (l / 4) % 4 of row l % 4.
+    const bool b2 = (lane >> 2) & 1, b3 = (lane >> 3) & 1, b4 = (lane >> 4) & 1;
+    float u[2 * NTG];
+#pragma unroll
+    for (int j = 0; j < 2 * NTG; ++j) {
+        const float e = acc[2 * j] + ror_lanes<2>(acc[2 * j]), o = acc[2 * j + 1] + ror_lanes<2>(acc[2 * j + 1]);
+        u[j] = b2 ? o : e;
+    }
+    float v[NTG];
+#pragma unroll
+    for (int j = 0; j < NTG; ++j) {
+        const float e = u[2 * j] + ror_lanes<3>(u[2 * j]), o = u[2 * j + 1] + ror_lanes<3>(u[2 * j + 1]);
+        v[j] = b3 ? o : e;
+    }
+    // (Every lane runs every cross-lane step; only the selection after it
+    // depends on the lane.)
+    float tot;
+    if constexpr (NTG == 1) {
+        tot = add_xor32(add_xor16(v[0]));
+    } else {
+        const float s0 = add_xor16(v[0]), s1 = add_xor16(v[1]);
+        tot = add_xor32(b4 ? s1 : s0);
+    }
+    const int tok = 4 * ((lane >> 4) & (NTG - 1)) + ((lane >> 2) & 3);
+    const int64_t m = row0 + row;
+    if (live && lane < 16 * NTG && tok < N && m < M) Y[(int64_t)tok * M + m] = tot;
+}
+
+namespace {
+
+int rows4_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+}  // namespace
+
+bool gemm_rows4_fits(const uint16_t *scales, int64_t M, int64_t K, int64_t N) {
+    return N >= 2 && N <= kR4MaxTokens && K <= kR4MaxK && K % 128 == 0 &&
+           (reinterpret_cast<uintptr_t>(scales) & 3) == 0 && (M + 3) / 4 <= (int64_t)kR4MaxWaves * rows4_cus();
+}
+
+// One tile per wave, G waves a workgroup (one workgroup per CU: the table
+// and the activation copy take 81 KB of LDS), at least 4 so that the table
+// fill is shared.
+hipError_t launch_gemm_rows4(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K, const uint16_t *X,
+                             int64_t N, float *Y, hipStream_t stream) {
+    if (!gemm_rows4_fits(scales, M, K, N)) return hipErrorInvalidValue;
+    const int64_t tiles = (M + 3) / 4;
+    const int64_t cus = rows4_cus();
+    int64_t G = (tiles + cus - 1) / cus;
+    const int ntg = N <= 4 ? 1 : 2;
+    if (G < rows4_min_waves(ntg)) G = rows4_min_waves(ntg);
+    if (G > kR4MaxWaves) G = kR4MaxWaves;
+    const int64_t grid = (tiles + G - 1) / G;
+    int k = (int)K, n = (int)N;
+    void *args[] = {&codes, &scales, &M, &k, &X, &n, &Y};
+    const void *fn = N <= 4 ? reinterpret_cast<const void *>(&gemm_rows4_kernel<1>)
+                            : reinterpret_cast<const void *>(&gemm_rows4_kernel<2>);
+    return hipLaunchKernel(fn, dim3((unsigned)grid),
+                           dim3((unsigned)(64 * G)), args, 0, stream);
+}
+
+}  // namespace q4

@@ -646,9 +646,12 @@ hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int6
                               const uint16_t *X, int64_t N, float *Y, hipStream_t stream) {
     // A chunk of one token is the GEMV (measured on the 11008 x 2048 prefill
     // shape: 5.3 us against 7.1 us for the matrix-core kernel, whose set-up
-    // and 16-token tiles do not pay for one token).  Two or three tokens on
-    // short rows share each table lookup in the GEMV kernels.
+    // and 16-token tiles do not pay for one token).  Two to eight tokens on
+    // short rows take one 4-row tile per wave (q4_gemm_rows4.hip); where
+    // that kernel's layout conditions fail, two or three tokens share each
+    // table lookup in the GEMV kernels.
     if (N == 1) return launch_gemv(codes, scales, M, K, X, Y, stream);
+    if (gemm_rows4_fits(scales, M, K, N)) return launch_gemm_rows4(codes, scales, M, K, X, N, Y, stream);
     if (gemv_tokens_fits(M, K, N)) return launch_gemv_tokens(codes, scales, M, K, X, N, Y, stream);
     return launch_matrix_core<kGemmNf4>(codes, scales, nullptr, nullptr, M, K, X, N, Y, stream);
 }

@@ -371,7 +371,7 @@ def test_affine_and_nvfp4_wide_range_activations(env, M, K, kind):
 
 @pytest.mark.parametrize("M,K,N", [(300, 2048, 2), (300, 2048, 3), (3001, 1984, 3), (600, 11008, 1),
                                    (300, 2048, 4), (300, 2048, 17), (3001, 1984, 32), (77, 4160, 17),
-                                   (70, 11008, 32)])
+                                   (70, 11008, 32), (300, 2048, 8), (300, 2048, 16), (3001, 1920, 11)])
 def test_gemm_smalln_wide_range_activations(env, M, K, N):
     """Each token of the chunk takes a different wide-range recipe."""
     torch, q4, dev = env
@@ -595,9 +595,9 @@ GEMM_SHAPES = [(1, 64, 1), (40, 128, 2), (100, 512, 3), (64, 2048, 4), (97, 1024
                (40000, 64, 5), (40000, 128, 24),
                # one token takes the GEMV kernels (short and long rows)
                (7, 2048, 1), (3000, 2112, 1), (600, 11008, 1),
-               # two or three tokens on short rows take the GEMV with shared
-               # lookups (up to 12 four-row tiles per CU), beyond that the
-               # matrix-core kernel
+               # two to eight tokens on short rows take 4-row tiles (up to
+               # 12 a CU; K % 128 == 0), two or three with K % 128 == 64 the
+               # GEMV with shared lookups, beyond that the matrix-core kernel
                (11008, 2048, 2), (3001, 1984, 3), (5, 64, 2), (1001, 576, 3), (12289, 2048, 3),
                # every matrix-core instantiation: two tokens past the
                # shared-lookup GEMV's limit (activations in registers, one
@@ -607,7 +607,16 @@ GEMM_SHAPES = [(1, 64, 1), (40, 128, 2), (100, 512, 3), (64, 2048, 4), (97, 1024
                (50, 2112, 20),
                # odd blocks a row with a last tile reaching past M, and 15
                # tiles a workgroup
-               (3000, 1984, 32), (3000, 1984, 4), (3001, 1984, 17), (3001, 1984, 4), (60000, 2048, 8)]
+               (3000, 1984, 32), (3000, 1984, 4), (3001, 1984, 17), (3001, 1984, 4), (60000, 2048, 8),
+               # 2..4 tokens on 4-row tiles: rows not a multiple of 4, K not
+               # a multiple of 512 (a partial activation range), one row,
+               # the most tiles a launch takes (12 a CU), the fewest waves
+               (3001, 1920, 4), (12288, 2048, 4), (1, 128, 2), (13, 640, 3), (4099, 1152, 2),
+               (3001, 1920, 2),
+               # 5..8 tokens on 4-row tiles (two token groups), and 9..16
+               # tokens on the same shapes (the 16-row matrix-core kernel)
+               (3001, 1920, 8), (12288, 2048, 7), (13, 640, 7), (4099, 1152, 6), (2, 256, 5),
+               (3001, 1920, 16), (12288, 2048, 13), (2, 256, 16)]
 
 
 @pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
