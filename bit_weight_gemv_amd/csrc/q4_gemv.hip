@@ -1363,9 +1363,10 @@ hipError_t launch_gemv_fused(const FusedOperand *ops, int count, bool swiglu, in
 }
 
 // Variant choice (by measurement).  Rows of one wave (K <= 2048): one 4-row
-// tile per wave while the grid covers the matrix in one pass, else a ring of
-// two tiles per wave keeps the next tile's loads in flight while the current
-// one is reduced (the lm_head shape).  Longer rows: groups of waves share
+// tile per wave while the grid covers the matrix in one pass, else 4-row
+// tiles dealt to the waves in turn, one at a time (the strided order: the
+// grid reads one moving stretch of the matrix; the lm_head and gate/up
+// shapes).  Longer rows: groups of waves share
 // 4-row tiles, one tile at a time, sized by multi_shape; the longest rows
 // take several chunks a lane (4-row tiles in a ring of two at 4 chunks, one
 // row at a time at 8).
