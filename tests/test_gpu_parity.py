@@ -634,6 +634,27 @@ def test_gemm_smalln_parity(env, M, K, N):
     _check(Y.cpu().numpy(), Y_ref, S, f"gemm M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("shift", [0, 1])
+@pytest.mark.parametrize("M,K,N", [(1001, 2048, 2), (300, 1024, 3), (4099, 1152, 4), (257, 2048, 8)])
+def test_gemm_smalln_scale_plane_alignment(env, M, K, N, shift):
+    """2..8 tokens with the scale plane dword-aligned (4-row tiles) and at
+    2 mod 4 (the 4-row-tile kernel needs dword-aligned scales: the chunk
+    then takes the shared-lookup GEMV or the matrix-core kernel)."""
+    torch, q4, dev = env
+    seed = 3500 + M + K + N
+    W = wl.weights(M, K, seed)
+    X = wl.activations(N, K, seed, "unit_rms")
+    codes, scales, _ = oracle.pack(W)
+    Y_ref, S = oracle.gemm(codes, scales, M, K, X)
+    c, _ = _upload_packed(env, codes, scales)
+    s = _scales_at(env, scales, shift)
+    assert s.data_ptr() % 4 == 2 * shift
+    Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+    Y = q4.q4_gemm_smalln(c, s, Xd)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, S, f"gemm M={M} K={K} N={N} scale plane +{2 * shift} B")
+
+
 def test_gemm_one_token_is_the_gemv(env):
     """A one-token chunk runs the GEMV kernels: bit-identical to q4_gemv."""
     torch, q4, dev = env
@@ -725,19 +746,23 @@ def test_graph_capture_strided_and_grouped_launches(env):
 
 def test_graph_capture_replays_match_eager(env):
     torch, q4, dev = env
-    M, K, N = 3000, 2048, 8
+    M, K, N = 3000, 2048, 16
     W = wl.weights(M, K, 51)
     codes, scales, _ = oracle.pack(W)
     c, s = _upload_packed(env, codes, scales)
     x = _x_dev(env, wl.activation(K, 51, "unit_rms"))
     X = cases.to_dev(wl.activations(N, K, 51, "normal").view(np.int16), torch, dev).view(torch.bfloat16)
-    X2 = X[:2].contiguous()  # two tokens: the GEMV with shared lookups
+    X2 = X[:2].contiguous()  # two tokens: 4-row tiles, one token group
+    X8 = X[:8].contiguous()  # eight tokens: 4-row tiles, two token groups
+    # (sixteen tokens: the 16-row matrix-core kernel)
     y_eager = q4.q4_gemv(c, s, x).clone()
     Y_eager = q4.q4_gemm_smalln(c, s, X).clone()
     Y2_eager = q4.q4_gemm_smalln(c, s, X2).clone()
+    Y8_eager = q4.q4_gemm_smalln(c, s, X8).clone()
     y = torch.full((M,), float("nan"), device=dev)
     Y = torch.full((N, M), float("nan"), device=dev)
     Y2 = torch.full((2, M), float("nan"), device=dev)
+    Y8 = torch.full((8, M), float("nan"), device=dev)
     g = torch.cuda.CUDAGraph()
     st = torch.cuda.Stream()
     st.wait_stream(torch.cuda.current_stream())
@@ -747,17 +772,20 @@ def test_graph_capture_replays_match_eager(env):
             q4.q4_gemv(c, s, x, y, stream=st)
             q4.q4_gemm_smalln(c, s, X, Y, stream=st)
             q4.q4_gemm_smalln(c, s, X2, Y2, stream=st)
+            q4.q4_gemm_smalln(c, s, X8, Y8, stream=st)
     torch.cuda.synchronize()
     for rep in range(4):
         y.fill_(float("nan"))
         Y.fill_(float("nan"))
         Y2.fill_(float("nan"))
+        Y8.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, y_eager), f"gemv replay {rep} differs from eager"
         assert torch.equal(Y, Y_eager), f"gemm replay {rep} differs from eager"
         assert torch.equal(Y2, Y2_eager), f"two-token gemm replay {rep} differs from eager"
+        assert torch.equal(Y8, Y8_eager), f"eight-token gemm replay {rep} differs from eager"
         # eager work in between replays
         q4.q4_gemv(c, s, x)
         torch.cuda.synchronize()
