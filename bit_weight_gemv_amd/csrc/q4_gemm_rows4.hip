@@ -117,8 +117,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
 
     // Activations of the wave's (token, range) pairs: pair P = 4 t + r is
     // token t, k = 512 r + 8 lane .. +7 for this lane, for P = wave + nw i
-    // below 4 N.  k past K and pairs past the last read zeros (offsets past
-    // the buffer).
+    // below 4 N.  k past K reads zeros (an offset past the buffer).  The
+    // rows of tokens N .. 4 NTG - 1 of the last group are never written:
+    // they only reach the sums of those tokens, which are not stored.
     const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(X, (uint32_t)N * (uint32_t)K * 2u);
     const int npairs = 4 * N;
     u32x4_t xraw[kPPW];
