@@ -1175,9 +1175,11 @@ int64_t one_tile_limit() { return 2LL * 16 * cu_count(); }
 // a time, in two workgroups of G waves per CU: G = 8 up to 32 tiles per CU,
 // else 12.  Measured (lab, same run): 22016 x 2048 7.10 -> 6.45 us (against
 // one tile per wave in 11-wave workgroups), 151936 x 2048 28.9 -> 27.7 us
-// (against a ring of two tiles over contiguous row ranges); a ring over the
-// strided order was far slower (48.6 us), and up to 16 tiles per CU one tile
-// per wave stays best (11008 x 2048 4.79 against 4.84-5.5 us strided).
+// (against a ring of two tiles over contiguous row ranges).  A ring of two
+// tiles over the strided order gained nothing (a spill-free lab kernel:
+// 151936 x 2048 27.2-27.65 against 27.0-27.7 us, 22016 x 2048 7.3-8.0
+// against 6.4), and up to 16 tiles per CU one tile per wave stays best
+// (11008 x 2048 4.79 against 4.84-5.5 us strided).
 int64_t strided_from() { return 2LL * 8 * cu_count(); }
 int strided_waves(int64_t tiles) { return tiles <= one_tile_limit() ? 8 : 12; }
 
