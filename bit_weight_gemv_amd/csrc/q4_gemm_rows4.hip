@@ -35,18 +35,23 @@
 //    through a range that reads nothing still costs the CU's address unit
 //    as much as one that reads (on 11008 x 2048, issuing every wave the
 //    same number of loads, most reading nothing, took 5.8-6.0 us against
-//    5.1-5.3 us for 2..4 tokens).  The conversion is exact while no nonzero
-//    value of a range lies more than 2^31 below its largest (tested per
-//    lane, decided per wave).  If any range of the chunk fails the test the
+//    5.1-5.3 us for 2..4 tokens).  The conversion is integer arithmetic on
+//    the bf16 bits (exponent rebased, mantissa widened), exact while every
+//    nonzero value of a range lies at most 2^28 below its largest (fp16
+//    normal numbers; tested per lane, decided per wave).  All waves convert
+//    at once before the barrier, so the conversion's instruction count is on
+//    the critical path: against an fp32 multiply and round per value it took
+//    2 / 4 / 8 tokens from 5.1 / 5.3 / 7.2 to 4.9 / 5.1 / 6.7 us.  If any
+//    range of the chunk fails the test the
 //    whole workgroup takes the exact loop instead: raw bf16 activations read
 //    per lane and widened to fp32, the fp16 levels widened likewise, and
 //    v_mfma_f32_4x4x1_16b_f32 (products exact, sums fp32).
 //  * Dequantisation.  The LDS byte -> fp16-pair table shared with the GEMV
 //    (64 bank-private copies; one ds_read_b32 per two weights).
 //  * Measured (11008 x 2048, A/B in one process against the kernels it
-//    replaces): 2 tokens 5.1 us (shared-lookup GEMV 6.3), 3 tokens 5.3
-//    (8.2), 4 tokens 5.3 (16-row matrix-core kernel 7.2), 8 tokens 7.3
-//    (7.5); the GEMV takes 4.9 us for one.  A third and fourth token group
+//    replaces): 2 tokens 4.9 us (shared-lookup GEMV 6.3), 4 tokens 5.1
+//    (16-row matrix-core kernel 7.2), 6 tokens 6.4, 8 tokens 6.7 (7.5); the
+//    GEMV takes 4.9 us for one.  A third and fourth token group
 //    (9..16 tokens) measured slower than the 16-row kernel (10.7 against
 //    7.8 us at 16): every wave reads all of the chunk's activations from
 //    LDS and runs 8 MFMAs per 32 k and group, and the conversion grows with
@@ -73,11 +78,25 @@ constexpr int kR4MaxTokens = 8;
 // 4 NTG waves (at most 12).
 constexpr int rows4_min_waves(int ntg) { return 4 * ntg < kR4MaxWaves ? 4 * ntg : kR4MaxWaves; }
 constexpr int rows4_pairs_per_wave(int ntg) {
-    return ((16 * ntg + rows4_min_waves(ntg) - 1) / rows4_min_waves(ntg) + 1) / 2 * 2;
+    return (16 * ntg + rows4_min_waves(ntg) - 1) / rows4_min_waves(ntg);
 }
 
 // A byte of the exponent table meaning "this range is not held exactly".
 constexpr int kR4Inexact = -128;
+
+// Largest of v over each row of 16 lanes (every lane gets it), as unsigned
+// integers: DPP quad and row mirrors.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+    return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+    v = dpp_max_u32<kDppQuadXor1>(v);
+    v = dpp_max_u32<kDppQuadXor2>(v);
+    v = dpp_max_u32<kDppRowHalfMirror>(v);
+    return dpp_max_u32<kDppRowMirror>(v);
+}
 
 // Lane l of the reduction receives from lane l - 2^L of its row of 16.
 template <int L>
@@ -95,13 +114,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
     constexpr int NTOK = 4 * NTG;             // tokens the kernel holds
     constexpr int kPairs = NTOK * kR4Ranges;  // (token, range) pairs at most
     constexpr int kPPW = rows4_pairs_per_wave(NTG);
-    // The activation copy has one more row and the exponent table one more
-    // dword: a wave's batch of pairs may end past the chunk's last pair, and
-    // those (zero) results go there.
     struct Smem {
         uint32_t lut[kLutDwords];
-        uint4 xh[(NTOK + 1) * kR4Pitch / 16];
-        uint32_t meta[kPairs / 4 + 1];
+        uint4 xh[NTOK * kR4Pitch / 16];
+        uint32_t meta[kPairs / 4];
     };
     __shared__ Smem sm;
     const int lane = threadIdx.x & 63;
@@ -157,64 +173,51 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
 
     fill_lut(sm.lut);
 
-    // Convert the wave's pairs, two at a time (their cross-lane steps
-    // overlap): the range's largest magnitude (over the wave) fixes its power
-    // of two 2^e; each lane checks that its nonzero values stay exact under
-    // it (biased exponent >= 110 - e, the last bit then at or above fp16's
-    // subnormal spacing), and one ballot decides.
+    // Convert the wave's pairs: the range's largest magnitude (over the
+    // wave), of biased exponent Emax, fixes its power of two 2^e with
+    // e = 141 - Emax, which puts that magnitude in [2^14, 2^15).  A bf16
+    // value of exponent E then has the fp16 exponent E - Emax + 29, so the
+    // conversion is integer arithmetic on the bits: subtract (Emax - 29) << 7
+    // from the magnitude (saturating: zero stays zero), shift left by 3 (7 to
+    // 10 mantissa bits), put the sign back -- three operations per two
+    // values.  It is exact when every nonzero value of the range gives a
+    // normal fp16 number, i.e. has E >= Emax - 28 (each lane tests its own
+    // smallest nonzero magnitude; one ballot decides), and Emax is in
+    // 29 .. 254; otherwise the range is marked inexact.
 #pragma unroll
-    for (int i0 = 0; i0 < kPPW; i0 += 2) {
-        if (wave + nw * i0 >= npairs) break;
-        float m[2];
-        uint32_t lo[2];
+    for (int i = 0; i < kPPW; ++i) {
+        const int P = wave + nw * i;
+        if (P >= npairs) break;
+        const u32x4_t v = xraw[i];
+        u16x2_t mag[4];
+        u16x2_t mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            u16x2_t mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const u16x2_t mag = __builtin_bit_cast(u16x2_t, xraw[i0 + b][c] & 0x7FFF7FFFu);
-                mx = __builtin_elementwise_max(mx, mag);
-                mn = __builtin_elementwise_min(mn, mag - u16x2_t{1, 1});
-            }
-            // Magnitude bits as fp32 values (bf16 bits shifted up) keep
-            // their order, so the float max of the DPP helpers finds the
-            // largest.
-            m[b] = __builtin_bit_cast(float, (uint32_t)(mx.x > mx.y ? mx.x : mx.y) << 16);
-            lo[b] = mn.x < mn.y ? mn.x : mn.y;
+        for (int c = 0; c < 4; ++c) {
+            mag[c] = __builtin_bit_cast(u16x2_t, v[c] & 0x7FFF7FFFu);
+            mx = __builtin_elementwise_max(mx, mag[c]);
+            mn = __builtin_elementwise_min(mn, mag[c] - u16x2_t{1, 1});
         }
+        // Rows of 16 by DPP, then the four rows' maxima in scalar registers.
+        const int mi = (int)row16_max_u32(mx.x > mx.y ? mx.x : mx.y);
+        const int r0 = __builtin_amdgcn_readlane(mi, 0), r1 = __builtin_amdgcn_readlane(mi, 16);
+        const int r2 = __builtin_amdgcn_readlane(mi, 32), r3 = __builtin_amdgcn_readlane(mi, 48);
+        const int a0 = r0 > r1 ? r0 : r1, a1 = r2 > r3 ? r2 : r3;
+        const int Emax = (a0 > a1 ? a0 : a1) >> 7;
+        const uint32_t lo = mn.x < mn.y ? mn.x : mn.y;  // smallest nonzero magnitude - 1, or 0xFFFF
+        const bool in_range = Emax >= 29 && Emax <= 254;
+        const int eb = in_range ? Emax - 29 : 0;
+        const bool ok = lo == 0xFFFFu || lo + 1u >= ((uint32_t)(eb + 1) << 7);
+        const bool exact = in_range && __builtin_amdgcn_ballot_w64(!ok) == 0;
+        const u16x2_t sub = {(unsigned short)(eb << 7), (unsigned short)(eb << 7)};
+        uint32_t h[4];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) m[b] = row16_max(m[b]);
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-            m[b] = fmaxf(m[b], __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, m[b]),
-                                                                                     0x401F)));
-#pragma unroll
-        for (int b = 0; b < 2; ++b) m[b] = fmaxf(m[b], __shfl_xor(m[b], 32));
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int P = wave + nw * (i0 + b);
-            int E = __builtin_amdgcn_readfirstlane((int)(__builtin_bit_cast(uint32_t, m[b]) >> 23));
-            if (E < 1) E = 1;
-            int e = 141 - E;
-            e = e > 126 ? 126 : (e < -126 ? -126 : e);
-            const int thr = 110 - e;
-            const bool ok = lo[b] == 0xFFFFu || thr <= 0 || lo[b] + 1u >= ((uint32_t)thr << 7);
-            const bool exact = __builtin_amdgcn_ballot_w64(!ok) == 0;
-            const float up = exp2i(e);
-            half2_t h[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t w = xraw[i0 + b][c];
-                h[c] = half2_t{(_Float16)(__builtin_bit_cast(float, w << 16) * up),
-                               (_Float16)(__builtin_bit_cast(float, w & 0xFFFF0000u) * up)};
-            }
-            const bool real = P < npairs;
-            const int t = real ? P >> 2 : NTOK, r = P & 3;
-            sm.xh[(t * kR4Pitch + (512 * r + 8 * lane) * 2) / 16] = make_uint4(
-                __builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
-                __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3]));
-            if (lane == 0) reinterpret_cast<int8_t *>(sm.meta)[real ? P : kPairs] = (int8_t)(exact ? e : kR4Inexact);
+        for (int c = 0; c < 4; ++c) {
+            const u16x2_t f = __builtin_elementwise_sub_sat(mag[c], sub) << u16x2_t{3, 3};
+            h[c] = (v[c] & 0x80008000u) | __builtin_bit_cast(uint32_t, f);
         }
+        const int t = P >> 2, r = P & 3;
+        sm.xh[(t * kR4Pitch + (512 * r + 8 * lane) * 2) / 16] = make_uint4(h[0], h[1], h[2], h[3]);
+        if (lane == 0) reinterpret_cast<int8_t *>(sm.meta)[P] = (int8_t)(exact ? 141 - Emax : kR4Inexact);
     }
     __syncthreads();
 

@@ -292,7 +292,11 @@ def test_gemv_activation_ranges(env, kind):
 # taken one binade too far.
 # ---------------------------------------------------------------------------
 
-WIDE_KINDS = ["zero_block_2^60", "code7_column_2^60", "spread_31", "spread_32", "tiny_run", "many_windows"]
+# spread_n: unit magnitudes and one value 2^n: n = 28 is the widest spread the
+# integer conversion of the 4-row-tile prefill kernel holds exactly (fp16
+# normal numbers), n = 31 the widest for the fp32-rounding conversions.
+WIDE_KINDS = ["zero_block_2^60", "code7_column_2^60", "spread_28", "spread_29", "spread_31", "spread_32", "tiny_run",
+              "many_windows"]
 K_ZERO_BLOCK, K_ZERO_COL = 64 * 3 + 5, 1000
 
 
@@ -306,7 +310,7 @@ def _wide_x(kind, K, seed):
     elif kind == "code7_column_2^60":
         v = z.copy()
         v[K_ZERO_COL] = -(2.0 ** 60)
-    elif kind in ("spread_31", "spread_32"):
+    elif kind.startswith("spread_"):
         v = sgn * (1.0 + 2.0 ** -7)
         v[K_ZERO_COL] = 2.0 ** int(kind[-2:])
     elif kind == "tiny_run":
