@@ -183,7 +183,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
     // values.  It is exact when every nonzero value of the range gives a
     // normal fp16 number, i.e. has E >= Emax - 28 (each lane tests its own
     // smallest nonzero magnitude; one ballot decides), and Emax is in
-    // 29 .. 254; otherwise the range is marked inexact.
+    // 29 .. 254 (a range of zeros counts as exact); otherwise the range is
+    // marked inexact.
 #pragma unroll
     for (int i = 0; i < kPPW; ++i) {
         const int P = wave + nw * i;
@@ -202,7 +203,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
         const int r0 = __builtin_amdgcn_readlane(mi, 0), r1 = __builtin_amdgcn_readlane(mi, 16);
         const int r2 = __builtin_amdgcn_readlane(mi, 32), r3 = __builtin_amdgcn_readlane(mi, 48);
         const int a0 = r0 > r1 ? r0 : r1, a1 = r2 > r3 ? r2 : r3;
-        const int Emax = (a0 > a1 ? a0 : a1) >> 7;
+        // (A range of zeros -- past K, or zero activations -- is held
+        // exactly by any scale: Emax 29 stands in.)
+        const int amax = a0 > a1 ? a0 : a1;
+        const int Emax = amax == 0 ? 29 : amax >> 7;
         const uint32_t lo = mn.x < mn.y ? mn.x : mn.y;  // smallest nonzero magnitude - 1, or 0xFFFF
         const bool in_range = Emax >= 29 && Emax <= 254;
         const int eb = in_range ? Emax - 29 : 0;

@@ -132,23 +132,29 @@ __device__ __forceinline__ void regroup_x(uint4 *xs, const u32x4_t (&lin)[NT * 8
 }
 
 // Prepare the slice's activations per token: lanes j, j+16, j+32, j+48 hold
-// token j's values; their largest bf16 magnitude fixes the power of two 2^e
-// that puts it in [2^14, 2^15).  A bf16 value (8 significant bits) scaled by
-// 2^e is exact in fp16 when its biased exponent is at least 110 - e (its
-// last bit then lies at or above fp16's subnormal spacing 2^-24); each lane
-// tests its nonzero values against that (the smallest nonzero magnitude is
-// found as 1 + the minimum of magnitude - 1 taken modulo 2^16, so zeros do
-// not count), and one ballot makes the decision for the wave.  Exact: xa
-// holds the scaled fp16 values and inv[t][r] the inverse power of two of the
-// token of output register r (token 4g + r of half t), times `post`.
+// token j's values; the biased exponent Emax of their largest bf16
+// magnitude fixes the power of two 2^e, e = 141 - Emax, that puts it in
+// [2^14, 2^15).  A bf16 value of exponent E then has the fp16 exponent
+// E - Emax + 29, so the conversion is integer arithmetic on the bits:
+// subtract (Emax - 29) << 7 from the magnitude (saturating: zero stays
+// zero), shift left by 3 (7 to 10 mantissa bits), restore the sign.  It is
+// exact when every nonzero value is an fp16 normal number after scaling
+// (E >= Emax - 28: each lane tests its smallest nonzero magnitude, found as
+// 1 + the minimum of magnitude - 1 taken modulo 2^16 so that zeros drop
+// out) and Emax is 29 .. 254 (a slice of zeros counts as exact); one
+// ballot makes the decision for the wave.
+// Exact: xa holds the fp16 values and inv[t][r] the inverse power of two of
+// the token of output register r (token 4g + r of half t), times `post`.
 // Otherwise xa keeps the raw bf16 bits and inv[t][r] = post.  Returns
-// whether the fp16 form is exact.
+// whether the fp16 form is exact.  (Against an fp32 multiply and round per
+// value this is ~20% fewer instructions in a set-up every wave runs before
+// the workgroup barrier.)
 template <int NT>
 __device__ __forceinline__ bool prepare_x_slice(const u32x4_t (&raw)[NT][kSliceBlocks][2],
                                                 half8_t (&xa)[NT][kSliceBlocks][2], float (&inv)[NT][4],
                                                 float post) {
     const int lane = threadIdx.x & 63;
-    int ex[NT];
+    int emax[NT];
     bool ok = true;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -167,34 +173,35 @@ __device__ __forceinline__ bool prepare_x_slice(const u32x4_t (&raw)[NT][kSliceB
         int m = (int)(mx.x > mx.y ? mx.x : mx.y);
         m = max(m, __shfl_xor(m, 16));
         m = max(m, __shfl_xor(m, 32));
-        int E = m >> 7;
-        if (E < 1) E = 1;
-        int e = 141 - E;
-        e = e > 126 ? 126 : (e < -126 ? -126 : e);
-        ex[t] = e;
+        // (A token whose slice is all zeros, such as the padding tokens
+        // past N, is held exactly by any scale: Emax 29 stands in.)
+        const int E = m == 0 ? 29 : m >> 7;
+        emax[t] = E;
         const uint32_t lo = mn.x < mn.y ? mn.x : mn.y;
-        const int thr = 110 - e;
-        ok = ok && (lo == 0xFFFFu || thr <= 0 || lo + 1u >= ((uint32_t)thr << 7));
+        ok = ok && E >= 29 && E <= 254 && (lo == 0xFFFFu || lo + 1u >= ((uint32_t)(E - 28) << 7));
     }
     const bool exact = __builtin_amdgcn_ballot_w64(!ok) == 0;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         float down = post;
         if (exact) {
-            const float up = exp2i(ex[t]);
-            down *= exp2i(-ex[t]);
+            down *= exp2i(emax[t] - 141);
+            const unsigned short sb = (unsigned short)((emax[t] - 29) << 7);
+            const u16x2_t sub = {sb, sb};
 #pragma unroll
             for (int b = 0; b < kSliceBlocks; ++b)
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    half8_t h;
+                    u32x4_t h;
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         const uint32_t w = raw[t][b][s][c];
-                        h[2 * c] = (_Float16)(__builtin_bit_cast(float, w << 16) * up);
-                        h[2 * c + 1] = (_Float16)(__builtin_bit_cast(float, w & 0xFFFF0000u) * up);
+                        const u16x2_t f =
+                            __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu), sub)
+                            << u16x2_t{3, 3};
+                        h[c] = (w & 0x80008000u) | __builtin_bit_cast(uint32_t, f);
                     }
-                    xa[t][b][s] = h;
+                    xa[t][b][s] = __builtin_bit_cast(half8_t, h);
                 }
         } else {
 #pragma unroll
