@@ -136,15 +136,17 @@ int q4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
  * Every weight is read once per call).
  *   X: bf16 bit patterns [N][K] row-major, 16-byte aligned.
  *   Y: fp32 [N][M] row-major, 4-byte aligned; must not overlap the inputs.
- * Same accuracy statement as q4_gemv, for every finite X: chunks of four or
- * more tokens take each token's activations exactly as fp16 under a power
- * of two per 256-weight slice of K, or as fp32 where the slice's nonzero
- * values span more than 2^31 (a slower path for such inputs only).  A chunk
- * of one token is computed by the q4_gemv kernels (Y[0] is then
- * bit-identical to q4_gemv of X[0]);
- * chunks of two or three tokens on rows of at most 2048 weights (and at most
- * 12 four-row tiles per compute unit) by the same kernels with each table
- * lookup serving every token.
+ * Same accuracy statement as q4_gemv, for every finite X: every activation
+ * enters its products exactly, as fp16 under a power of two per token and
+ * range of K (256 weights in the 16-row kernel, 512 in the 4-row kernel),
+ * or as fp32 where a range's nonzero values span more than 2^28 (a slower
+ * path for such inputs only).  A chunk of one token is computed by the
+ * q4_gemv kernels (Y[0] is then bit-identical to q4_gemv of X[0]); chunks of
+ * two to eight tokens on rows of at most 2048 weights (K % 128 == 0, a
+ * dword-aligned scale plane, at most 12 four-row tiles per compute unit)
+ * by one 4-row tile per wave; where those conditions fail, chunks of two
+ * or three tokens on such rows by the q4_gemv kernels with each table
+ * lookup serving every token; all others by 16-row matrix-core tiles.
  */
 int q4_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M,
                    int64_t K, const uint16_t *X, int64_t N, float *Y,
@@ -316,7 +318,7 @@ int q4_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales,
  * N == 1 runs the format's GEMV (Y[0] is bit-identical to it); N == 0 is a
  * no-op.  Accuracy as q4_gemv, for every finite X: each token's activations
  * enter exactly (fp16 under a power of two per 256-weight slice, or as fp32
- * where a slice spans more than 2^31).  Errors as q4_gemm_smalln.
+ * where a slice spans more than 2^28).  Errors as q4_gemm_smalln.
  *
  * q4_gemm_smalln_affine -- Y[n][m] = sum_k (code(m,k) - z[m][k/64])
  * * s[m][k/64] * X[n][k]; codes, scales and zeros as q4_gemv_affine.
