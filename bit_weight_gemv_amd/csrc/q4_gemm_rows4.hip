@@ -114,10 +114,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
     constexpr int NTOK = 4 * NTG;             // tokens the kernel holds
     constexpr int kPairs = NTOK * kR4Ranges;  // (token, range) pairs at most
     constexpr int kPPW = rows4_pairs_per_wave(NTG);
+    // The activation copy first: its reads' constant offsets (token group,
+    // load p, 16-byte step) then fit the DS instructions' 16-bit offset field
+    // instead of costing an address add each; the table's lookups take its
+    // base in that field instead.
     struct Smem {
-        uint32_t lut[kLutDwords];
         uint4 xh[NTOK * kR4Pitch / 16];
         uint32_t meta[kPairs / 4];
+        uint32_t lut[kLutDwords];
     };
     __shared__ Smem sm;
     const int lane = threadIdx.x & 63;
@@ -254,6 +258,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
 #pragma unroll
     for (int t = 0; t < NTOK; ++t) acc[t] = 0.0f;
     if (__builtin_expect(all_exact, 1)) {
+        // This lane's activation base (token `row` of group 0, chunk grp);
+        // groups, loads p and the 16-byte steps are constant offsets from it
+        // (the DS offset field holds them, so no address arithmetic per read).
+        const uint4 *xbase = sm.xh + (row * kR4Pitch + 64 * grp) / 16;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const u32x4_t w = q[p];
@@ -270,7 +278,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
 #pragma unroll
             for (int g = 0; g < NTG; ++g) {
                 // Token 4g + row's fp16 activations of chunk 16p + grp (64 bytes).
-                const uint4 *xp = sm.xh + ((4 * g + row) * kR4Pitch + 64 * (16 * p + grp)) / 16;
+                const uint4 *xp = xbase + (4 * g * kR4Pitch + 1024 * p) / 16;
                 float4_t D = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
