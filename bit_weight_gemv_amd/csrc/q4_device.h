@@ -166,6 +166,26 @@ __device__ __forceinline__ float wave_sum(float v) {
     return lo + hi;
 }
 
+// Largest of an unsigned value over the wave, in a scalar register: DPP
+// maxima over each row of 16 lanes (folded into v_max_u32 with a DPP
+// operand), then the four rows' maxima read into scalar registers.  No LDS
+// operation, so it does not queue behind other LDS traffic.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+    return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = dpp_max_u32<kDppQuadXor1>(v);
+    v = dpp_max_u32<kDppQuadXor2>(v);
+    v = dpp_max_u32<kDppRowHalfMirror>(v);
+    v = dpp_max_u32<kDppRowMirror>(v);
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    const uint32_t a0 = r0 > r1 ? r0 : r1, a1 = r2 > r3 ? r2 : r3;
+    return a0 > a1 ? a0 : a1;
+}
+
 // Max over the 16 lanes of a DPP row (lanes 16r .. 16r+15); all get it.
 __device__ __forceinline__ float row16_max(float v) {
     v = fmaxf(v, dpp_f<kDppQuadXor1>(v));

@@ -84,20 +84,6 @@ constexpr int rows4_pairs_per_wave(int ntg) {
 // A byte of the exponent table meaning "this range is not held exactly".
 constexpr int kR4Inexact = -128;
 
-// Largest of v over each row of 16 lanes (every lane gets it), as unsigned
-// integers: DPP quad and row mirrors.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
-    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
-    return o > v ? o : v;
-}
-__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
-    v = dpp_max_u32<kDppQuadXor1>(v);
-    v = dpp_max_u32<kDppQuadXor2>(v);
-    v = dpp_max_u32<kDppRowHalfMirror>(v);
-    return dpp_max_u32<kDppRowMirror>(v);
-}
-
 // Lane l of the reduction receives from lane l - 2^L of its row of 16.
 template <int L>
 __device__ __forceinline__ float ror_lanes(float v) {
@@ -202,14 +188,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
             mx = __builtin_elementwise_max(mx, mag[c]);
             mn = __builtin_elementwise_min(mn, mag[c] - u16x2_t{1, 1});
         }
-        // Rows of 16 by DPP, then the four rows' maxima in scalar registers.
-        const int mi = (int)row16_max_u32(mx.x > mx.y ? mx.x : mx.y);
-        const int r0 = __builtin_amdgcn_readlane(mi, 0), r1 = __builtin_amdgcn_readlane(mi, 16);
-        const int r2 = __builtin_amdgcn_readlane(mi, 32), r3 = __builtin_amdgcn_readlane(mi, 48);
-        const int a0 = r0 > r1 ? r0 : r1, a1 = r2 > r3 ? r2 : r3;
         // (A range of zeros -- past K, or zero activations -- is held
         // exactly by any scale: Emax 29 stands in.)
-        const int amax = a0 > a1 ? a0 : a1;
+        const int amax = (int)wave_max_u32(mx.x > mx.y ? mx.x : mx.y);
         const int Emax = amax == 0 ? 29 : amax >> 7;
         const uint32_t lo = mn.x < mn.y ? mn.x : mn.y;  // smallest nonzero magnitude - 1, or 0xFFFF
         const bool in_range = Emax >= 29 && Emax <= 254;

@@ -194,40 +194,41 @@ __device__ __forceinline__ void load_chunk_x_lds(const uint4 *xs, int c, bool va
     }
 }
 
-__device__ __forceinline__ void convert_chunk_x(const uint32_t (&raw)[16], float up, half2_t (&xh)[16]) {
+// One chunk's 32 bf16 activations to fp16 under the power of two that puts a
+// magnitude of biased exponent Emax in [2^14, 2^15): a bf16 value of
+// exponent E has the fp16 exponent E - Emax + 29, so the bits are rebased
+// with integer operations -- `sub` = (Emax - 29) << 7 taken from the
+// magnitude (saturating: zero stays zero), a shift left by 3 (7 to 10
+// mantissa bits), the sign put back.  Exact for values with E >= Emax - 28.
+__device__ __forceinline__ void convert_chunk_x(const uint32_t (&raw)[16], u16x2_t sub, half2_t (&xh)[16]) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-        const float lo = __builtin_bit_cast(float, raw[v] << 16);
-        const float hi = __builtin_bit_cast(float, raw[v] & 0xFFFF0000u);
-        half2_t h;
-        h.x = (_Float16)(lo * up);
-        h.y = (_Float16)(hi * up);
-        xh[v] = h;
+        const u16x2_t f = __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2_t, raw[v] & 0x7FFF7FFFu), sub)
+                          << u16x2_t{3, 3};
+        xh[v] = __builtin_bit_cast(half2_t, (raw[v] & 0x80008000u) | __builtin_bit_cast(uint32_t, f));
     }
 }
 
 // Activations: the lane's chunks are converted to fp16, scaled by a
-// wave-uniform power of two chosen from the wave's largest bf16 magnitude so
-// that no value can overflow fp16; the inverse scale (exact) is returned.
-// `load(i, raw)` fetches the raw words of the lane's chunk i.  With one chunk
-// per lane the caller passes them in `raw` (loaded early, so the conversion
-// does not wait behind the weight tiles); with several, the maximum is taken
-// in a first pass and the chunks are fetched again (from cache or LDS) for
-// the conversion, so the raw and the converted copies are never live
-// together.
+// wave-uniform power of two 2^e, e = 141 - Emax, chosen from the wave's
+// largest bf16 magnitude (biased exponent Emax) so that nothing can
+// overflow fp16; the inverse scale (exact) is returned.  `load(i, raw)`
+// fetches the raw words of the lane's chunk i.  With one chunk per lane the
+// caller passes them in `raw` (loaded early, so the conversion does not wait
+// behind the weight tiles); with several, the maximum is taken in a first
+// pass and the chunks are fetched again (from cache or LDS) for the
+// conversion, so the raw and the converted copies are never live together.
 //
 // `exact` is set (wave-uniform) when the conversion loses nothing: every
-// nonzero magnitude has a biased exponent of at least E - 31, E being the
-// largest one's.  A bf16 value of exponent e has 7 fraction bits, so its
-// scaled copy is a multiple of 2^(e - 134 + 141 - E) >= 2^-24, fp16's
-// finest step (subnormals included), and the scaled largest value is below
-// 2^15.  (A bf16 subnormal counts as exponent 0; it passes only when
-// E <= 31, where the scale is at least 2^110 and its step 2^-133 becomes at
-// least 2^-23.)
+// nonzero magnitude has a biased exponent of at least Emax - 28 (it is then
+// an fp16 normal number after scaling) and Emax is 29 .. 254; a wave of
+// zeros counts as exact.  Each lane tests its smallest nonzero magnitude
+// (1 + the minimum of magnitude - 1 taken modulo 2^16, so zeros drop out);
+// one ballot makes the answer wave-uniform.  The wave's maximum: DPP
+// maxima over rows of 16, then the four rows' read into scalar registers.
 template <int CPL, bool PRELOADED, class Load>
 __device__ __forceinline__ float convert_x(Load load, uint32_t (&raw)[16], half2_t (&xh)[CPL][16], bool &exact) {
     u16x2_t mx = {0, 0};
-    // Smallest nonzero magnitude minus one (a zero wraps to 0xFFFF).
     u16x2_t mn = {0xFFFF, 0xFFFF};
     const u16x2_t one = {1, 1};
 #pragma unroll
@@ -240,29 +241,20 @@ __device__ __forceinline__ float convert_x(Load load, uint32_t (&raw)[16], half2
             mn = __builtin_elementwise_min(mn, mag - one);
         }
     }
-    // Largest bf16 magnitude bits of the wave (integer max: bf16 magnitudes
-    // order like their bit patterns).
-    int m = (int)(mx.x > mx.y ? mx.x : mx.y);
-    m = __builtin_amdgcn_readfirstlane(__reduce_max_sync(~0ull, m));
-    // Each lane tests its own smallest nonzero magnitude against the wave's
-    // threshold; one ballot makes the answer wave-uniform.
-    const int emax = m >> 7;
+    const int m = (int)wave_max_u32(mx.x > mx.y ? mx.x : mx.y);
+    const int E = m == 0 ? 29 : m >> 7;
     const int lo = (int)(mn.x < mn.y ? mn.x : mn.y);
-    const bool lane_ok = emax <= 31 || lo == 0xFFFF || lo + 1 >= ((emax - 31) << 7);
-    exact = __builtin_amdgcn_ballot_w64(!lane_ok) == 0;
-    // Its biased exponent E; scale by 2^(141-E) so the largest value lands in
-    // [2^14, 2^15), inside fp16's range.
-    int E = m >> 7;
-    if (E < 1) E = 1;
-    int e = 141 - E;
-    e = e > 126 ? 126 : (e < -126 ? -126 : e);
-    const float up = exp2i(e);
+    const bool in_range = E >= 29 && E <= 254;
+    const bool lane_ok = lo == 0xFFFF || lo + 1 >= ((E - 28) << 7);
+    exact = in_range && __builtin_amdgcn_ballot_w64(!lane_ok) == 0;
+    const int eb = in_range ? E - 29 : 0;
+    const u16x2_t sub = {(unsigned short)(eb << 7), (unsigned short)(eb << 7)};
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         if (CPL > 1) load(i, raw);
-        convert_chunk_x(raw, up, xh[i]);
+        convert_chunk_x(raw, sub, xh[i]);
     }
-    return exp2i(-e);
+    return exp2i(eb - 112);
 }
 
 // One lane group (P lanes: a wave, or a whole workgroup for long rows) owns

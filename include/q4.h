@@ -122,7 +122,7 @@ int q4_unpack_canonical(const uint8_t *codes, const uint16_t *scales,
  * finite x and any packed matrix, while that sum stays inside fp32's range.
  * The fp16 rounding of the table costs at most 2^-11 relative per term;
  * every activation enters its product exactly (as fp16 under a power of two,
- * or widened to fp32 where the values one wave holds span more than 2^31);
+ * or widened to fp32 where the values one wave holds span more than 2^28);
  * sums are fp32.  Non-finite x propagate into y.
  */
 int q4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
