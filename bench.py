@@ -401,8 +401,8 @@ def affine_secondaries(torch, q4, wl, dev, steps, warmup):
                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": nb})
         del reps, codes, scales, zeros, x, y
         torch.cuda.empty_cache()
-    # The prefill product on the prefill shape (11008 x 2048), chunks of 32
-    # and 16 tokens.
+    # The prefill product on the prefill shape (11008 x 2048), chunks of 32,
+    # 16, 8, 4 and 2 tokens.
     c = wl.CONFIGS["smalln"]
     M, K = c["M"], c["K"]
     W = torch.from_numpy(wl.weights(M, K, c["seed"])).to(dev)
@@ -413,7 +413,7 @@ def affine_secondaries(torch, q4, wl, dev, steps, warmup):
     del W
     reps = [(codes, scales, zeros)] + [(codes.clone(), scales.clone(), zeros.clone()) for _ in range(44)]
     X = _upload_bits(torch, wl.activations(32, K, c["seed"], c["x"]), torch.bfloat16, dev)
-    for n in (32, 16):
+    for n in (32, 16, 8, 4, 2):
         Xn = X[:n].contiguous()
         Y = torch.empty((n, M), dtype=torch.float32, device=dev)
 
@@ -458,8 +458,8 @@ def nvfp4_secondaries(torch, q4, wl, dev, steps, warmup):
                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": nb})
         del reps, codes, scales, ts, x, y
         torch.cuda.empty_cache()
-    # The prefill product on the prefill shape (11008 x 2048), chunks of 32
-    # and 16 tokens.
+    # The prefill product on the prefill shape (11008 x 2048), chunks of 32,
+    # 16, 8, 4 and 2 tokens.
     c = wl.CONFIGS["smalln"]
     M, K = c["M"], c["K"]
     W = torch.from_numpy(wl.weights(M, K, c["seed"])).to(dev)
@@ -470,7 +470,7 @@ def nvfp4_secondaries(torch, q4, wl, dev, steps, warmup):
     del W
     reps = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(44)]
     X = _upload_bits(torch, wl.activations(32, K, c["seed"], c["x"]), torch.bfloat16, dev)
-    for n in (32, 16):
+    for n in (32, 16, 8, 4, 2):
         Xn = X[:n].contiguous()
         Y = torch.empty((n, M), dtype=torch.float32, device=dev)
 

@@ -1,11 +1,15 @@
 // q4_gemm_rows4.hip -- the prefill product Y[n][m] = sum_k What[m,k] * X[n][k]
-// for chunks of 2..8 tokens on rows of at most 2048 weights (NF4 codebook
-// format), one 4-row tile per wave.
+// for chunks of 2..8 tokens on rows of at most 2048 weights, one 4-row tile
+// per wave, in the three weight formats.
 //
 // What is computed: the same product as q4_gemm_smalln (the prefill form of
 // the deep-fold "Decode V2" page, section 0; accel/tensor func Int4MatMul's
 // reconstruction What = level[code] * s per 64-block), for the smallest
-// chunks.
+// chunks; likewise q4_gemm_smalln_affine ((code - z) * s per 64-block:
+// the table holds code - 8, from which z - 8 is subtracted in fp16, exact for
+// the packer's integer zero points) and q4_gemm_smalln_nvfp4 (E2M1 level
+// times an E4M3 scale per 16 weights, times the tensor scale: the two
+// 16-blocks of a 32-weight chunk accumulate apart and take their own scales).
 //
 // gfx950 design:
 //  * Tiles.  A chunk of a few tokens has as few rows per CU as the GEMV
@@ -51,7 +55,9 @@
 //  * Measured (11008 x 2048, A/B in one process against the kernels it
 //    replaces): 2 tokens 4.9 us (shared-lookup GEMV 6.3), 4 tokens 5.1
 //    (16-row matrix-core kernel 7.2), 6 tokens 6.4, 8 tokens 6.7 (7.5); the
-//    GEMV takes 4.9 us for one.  A third and fourth token group
+//    GEMV takes 4.9 us for one.  Affine format 2 / 4 / 8 tokens 5.3 / 5.5 /
+//    7.1 us (matrix-core kernel 7.7 / 7.8 / 7.9), NVFP4-style 5.1 / 5.2 /
+//    7.1 (7.5 / 7.6 / 7.8).  A third and fourth token group
 //    (9..16 tokens) measured slower than the 16-row kernel (10.7 against
 //    7.8 us at 16): every wave reads all of the chunk's activations from
 //    LDS and runs 8 MFMAs per 32 k and group, and the conversion grows with
@@ -92,11 +98,14 @@ __device__ __forceinline__ float ror_lanes(float v) {
 
 }  // namespace
 
-// NTG groups of 4 tokens (chunks of up to 4 NTG tokens), NTG = 1 or 2.
-template <int NTG>
+// NTG groups of 4 tokens (chunks of up to 4 NTG tokens), NTG = 1 or 2;
+// FMT: the NF4 codebook, the affine format (zeros: its zero points) or the
+// NVFP4-style format (scales: E4M3 bytes, tscale: the tensor scale).
+template <int NTG, int FMT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) void gemm_rows4_kernel(
-    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, int64_t M, int K,
-    const uint16_t *__restrict__ X, int N, float *__restrict__ Y) {
+    const uint8_t *__restrict__ codes, const void *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    const float *__restrict__ tscale, int64_t M, int K, const uint16_t *__restrict__ X, int N,
+    float *__restrict__ Y) {
     constexpr int NTOK = 4 * NTG;             // tokens the kernel holds
     constexpr int kPairs = NTOK * kR4Ranges;  // (token, range) pairs at most
     constexpr int kPPW = rows4_pairs_per_wave(NTG);
@@ -148,10 +157,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
     const bool live = tile < tiles;
     const int64_t row0 = uniform64(live ? tile * 4 : 0);
     const int rows = live ? (int)(M - row0 < 4 ? M - row0 : 4) : 0;
-    const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(scales + row0 * nsb, (uint32_t)(rows * nsb * 2));
+    // (NVFP4: a row's E4M3 scales are K / 16 bytes; lane L reads bytes
+    // 8 (L % 16) .. +7 of row L / 16, the scales of chunks 4 (L % 16) .. +3.
+    // Affine: the zero points like the scales.)
     const int sdw = lane & 15;
-    const uint32_t sdword = __builtin_amdgcn_raw_buffer_load_b32(
-        srs, 2 * sdw < nsb ? (lane >> 4) * nsb * 2 + 4 * sdw : 0x7FFFFFF0, 0, kLoadNonTemporal);
+    uint32_t sdword = 0, zdword = 0;
+    u32x2_t sq = {0u, 0u};
+    if constexpr (FMT == kGemmNvfp4) {
+        const int sst = K >> 4;
+        const __amdgpu_buffer_rsrc_t srs =
+            buffer_rsrc(static_cast<const uint8_t *>(scales) + row0 * sst, (uint32_t)(rows * sst));
+        sq = __builtin_amdgcn_raw_buffer_load_b64(srs, 8 * sdw < sst ? (lane >> 4) * sst + 8 * sdw : 0x7FFFFFF0, 0,
+                                                  kLoadNonTemporal);
+    } else {
+        const int soff = 2 * sdw < nsb ? (lane >> 4) * nsb * 2 + 4 * sdw : 0x7FFFFFF0;
+        sdword = __builtin_amdgcn_raw_buffer_load_b32(
+            buffer_rsrc(static_cast<const uint16_t *>(scales) + row0 * nsb, (uint32_t)(rows * nsb * 2)), soff, 0,
+            kLoadNonTemporal);
+        if constexpr (FMT == kGemmAffine)
+            zdword = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(zeros + row0 * nsb, (uint32_t)(rows * nsb * 2)),
+                                                          soff, 0, kLoadNonTemporal);
+    }
     const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(codes + row0 * row_bytes, (uint32_t)(rows * row_bytes));
     u32x4_t q[4];
 #pragma unroll
@@ -161,7 +187,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
                                                      kLoadNonTemporal);
     }
 
-    fill_lut(sm.lut);
+    if constexpr (FMT == kGemmAffine)
+        fill_lut_from(sm.lut, kAffinePairTable);
+    else if constexpr (FMT == kGemmNvfp4)
+        fill_lut_from(sm.lut, kE2m1PairTable);
+    else
+        fill_lut(sm.lut);
 
     // Convert the wave's pairs: the range's largest magnitude (over the
     // wave), of biased exponent Emax, fixes its power of two 2^e with
@@ -224,12 +255,30 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
             all_exact = all_exact && ((int)(int8_t)(eb[t] >> (8 * r)) != kR4Inexact || t >= N);
 
     // The scale of this lane's row for the block of chunk 16p + grp: dword
-    // (8p + grp / 2) / 2 of the row, held by lane 16 row + 4p + grp / 4.
-    float sc[4];
+    // (8p + grp / 2) / 2 of the row, held by lane 16 row + 4p + grp / 4
+    // (likewise the affine zero point: zz[p] = z - 8 in both halves).
+    // NVFP4: the chunk's two E4M3 bytes (its 16-blocks) are bytes
+    // 2 (grp % 4), +1 of the 8 that lane 16 row + 4p + grp / 4 holds; sc[p]
+    // and sh[p] are the first and the second 16-block's scales.
+    float sc[4], sh[4];
+    half2_t zz[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const uint32_t d = (uint32_t)__shfl((int)sdword, 16 * row + 4 * p + (grp >> 2));
-        sc[p] = f16_bits_to_f32((d >> (16 * ((grp >> 1) & 1))) & 0xFFFFu);
+        const int src = 16 * row + 4 * p + (grp >> 2);
+        if constexpr (FMT == kGemmNvfp4) {
+            const uint32_t d0 = (uint32_t)__shfl((int)sq.x, src), d1 = (uint32_t)__shfl((int)sq.y, src);
+            const uint32_t b = ((grp & 2) ? d1 : d0) >> (16 * (grp & 1));
+            sc[p] = e4m3_to_f32(b & 0xFFu);
+            sh[p] = e4m3_to_f32((b >> 8) & 0xFFu);
+        } else {
+            const uint32_t d = (uint32_t)__shfl((int)sdword, src);
+            sc[p] = f16_bits_to_f32((d >> (16 * ((grp >> 1) & 1))) & 0xFFFFu);
+            if constexpr (FMT == kGemmAffine) {
+                const uint32_t z = (uint32_t)__shfl((int)zdword, src);
+                const _Float16 z8 = (_Float16)(f16_bits_to_f32((z >> (16 * ((grp >> 1) & 1))) & 0xFFFFu) - 8.0f);
+                zz[p] = half2_t{z8, z8};
+            }
+        }
     }
 
     const uint32_t laneoff = (uint32_t)lane << 2;
@@ -249,10 +298,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
             half4_t wb[8];  // this lane's 32 weights of chunk 16p + grp, 4 a step
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const half2_t p0 = lut_pair<0>(sm.lut, w[d], laneoff);
-                const half2_t p1 = lut_pair<1>(sm.lut, w[d], laneoff);
-                const half2_t p2 = lut_pair<2>(sm.lut, w[d], laneoff);
-                const half2_t p3 = lut_pair<3>(sm.lut, w[d], laneoff);
+                half2_t p0 = lut_pair<0>(sm.lut, w[d], laneoff);
+                half2_t p1 = lut_pair<1>(sm.lut, w[d], laneoff);
+                half2_t p2 = lut_pair<2>(sm.lut, w[d], laneoff);
+                half2_t p3 = lut_pair<3>(sm.lut, w[d], laneoff);
+                if constexpr (FMT == kGemmAffine) {
+                    // code - 8 minus z - 8: exact small integers in fp16
+                    p0 -= zz[p]; p1 -= zz[p]; p2 -= zz[p]; p3 -= zz[p];
+                }
                 wb[2 * d] = half4_t{p0.x, p0.y, p1.x, p1.y};
                 wb[2 * d + 1] = half4_t{p2.x, p2.y, p3.x, p3.y};
             }
@@ -260,14 +313,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
             for (int g = 0; g < NTG; ++g) {
                 // Token 4g + row's fp16 activations of chunk 16p + grp (64 bytes).
                 const uint4 *xp = xbase + (4 * g * kR4Pitch + 1024 * p) / 16;
-                float4_t D = {0.0f, 0.0f, 0.0f, 0.0f};
+                // D: k 0..15 of the chunk, Dh: k 16..31 (one accumulator
+                // for the formats with one scale per chunk).
+                float4_t D = {0.0f, 0.0f, 0.0f, 0.0f}, Dh = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
                     const uint4 xv = xp[d];
-                    D = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, uint2{xv.x, xv.y}), wb[2 * d],
-                                                           D, 0, 0, 0);
-                    D = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, uint2{xv.z, xv.w}),
-                                                           wb[2 * d + 1], D, 0, 0, 0);
+                    float4_t &T = (FMT == kGemmNvfp4 && d >= 2) ? Dh : D;
+                    T = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, uint2{xv.x, xv.y}), wb[2 * d],
+                                                           T, 0, 0, 0);
+                    T = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, uint2{xv.z, xv.w}),
+                                                           wb[2 * d + 1], T, 0, 0, 0);
                 }
                 // (D times the block scale first: the product stays finite,
                 // and a zero sum stays zero under the largest inverse power
@@ -275,7 +331,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int e = (int)(int8_t)(eb[4 * g + t] >> (8 * p));
-                    acc[4 * g + t] = fmaf(D[t] * sc[p], exp2i(-e), acc[4 * g + t]);
+                    float v = D[t] * sc[p];
+                    if constexpr (FMT == kGemmNvfp4) v = fmaf(Dh[t], sh[p], v);
+                    acc[4 * g + t] = fmaf(v, exp2i(-e), acc[4 * g + t]);
                 }
             }
         }
@@ -293,6 +351,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
                 pr[4 * d + 1] = lut_pair<1>(sm.lut, w[d], laneoff);
                 pr[4 * d + 2] = lut_pair<2>(sm.lut, w[d], laneoff);
                 pr[4 * d + 3] = lut_pair<3>(sm.lut, w[d], laneoff);
+                if constexpr (FMT == kGemmAffine)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) pr[4 * d + b] -= zz[p];
             }
 #pragma unroll 1
             for (int g = 0; g < NTG; ++g) {
@@ -303,7 +364,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
                 for (int d = 0; d < 4; ++d)
                     xr[d] = __builtin_amdgcn_raw_buffer_load_b128(
                         xrs, ok ? (t * K + 32 * c) * 2 + 16 * d : 0x7FFFFFF0, 0, 0);
-                float4_t D = {0.0f, 0.0f, 0.0f, 0.0f};
+                float4_t D = {0.0f, 0.0f, 0.0f, 0.0f}, Dh = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -311,10 +372,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
                         // k = 8d + 2b and 8d + 2b + 1 of the chunk
                         uint32_t xw = xr[d][b];
                         __asm__ volatile("" : "+v"(xw));
-                        D = __builtin_amdgcn_mfma_f32_4x4x1f32(__builtin_bit_cast(float, xw << 16),
-                                                               (float)pr[4 * d + b].x, D, 0, 0, 0);
-                        D = __builtin_amdgcn_mfma_f32_4x4x1f32(__builtin_bit_cast(float, xw & 0xFFFF0000u),
-                                                               (float)pr[4 * d + b].y, D, 0, 0, 0);
+                        float4_t &T = (FMT == kGemmNvfp4 && d >= 2) ? Dh : D;
+                        T = __builtin_amdgcn_mfma_f32_4x4x1f32(__builtin_bit_cast(float, xw << 16),
+                                                               (float)pr[4 * d + b].x, T, 0, 0, 0);
+                        T = __builtin_amdgcn_mfma_f32_4x4x1f32(__builtin_bit_cast(float, xw & 0xFFFF0000u),
+                                                               (float)pr[4 * d + b].y, T, 0, 0, 0);
                     }
                 // (acc is indexed at run time here; the loop over groups is
                 // kept rolled to hold the exact loop's registers down.)
@@ -322,7 +384,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
                 for (int gg = 0; gg < NTG; ++gg)
                     if (gg == g)
 #pragma unroll
-                        for (int tt = 0; tt < 4; ++tt) acc[4 * gg + tt] = fmaf(D[tt], sc[p], acc[4 * gg + tt]);
+                        for (int tt = 0; tt < 4; ++tt) {
+                            float a = fmaf(D[tt], sc[p], acc[4 * gg + tt]);
+                            if constexpr (FMT == kGemmNvfp4) a = fmaf(Dh[tt], sh[p], a);
+                            acc[4 * gg + tt] = a;
+                        }
             }
         }
     }
@@ -357,6 +423,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * kR4MaxWaves))) vo
     }
     const int tok = 4 * ((lane >> 4) & (NTG - 1)) + ((lane >> 2) & 3);
     const int64_t m = row0 + row;
+    if constexpr (FMT == kGemmNvfp4) tot *= *tscale;
     if (live && lane < 16 * NTG && tok < N && m < M) Y[(int64_t)tok * M + m] = tot;
 }
 
@@ -375,19 +442,29 @@ int rows4_cus() {
     return cus[dev];
 }
 
+template <int FMT>
+const void *rows4_kernel_for(int64_t N) {
+    return N <= 4 ? reinterpret_cast<const void *>(&gemm_rows4_kernel<1, FMT>)
+                  : reinterpret_cast<const void *>(&gemm_rows4_kernel<2, FMT>);
+}
+
 }  // namespace
 
-bool gemm_rows4_fits(const uint16_t *scales, int64_t M, int64_t K, int64_t N) {
+bool gemm_rows4_fits(const void *scales, const uint16_t *zeros, int64_t M, int64_t K, int64_t N) {
     return N >= 2 && N <= kR4MaxTokens && K <= kR4MaxK && K % 128 == 0 &&
-           (reinterpret_cast<uintptr_t>(scales) & 3) == 0 && (M + 3) / 4 <= (int64_t)kR4MaxWaves * rows4_cus();
+           (reinterpret_cast<uintptr_t>(scales) & 3) == 0 && (reinterpret_cast<uintptr_t>(zeros) & 3) == 0 &&
+           (M + 3) / 4 <= (int64_t)kR4MaxWaves * rows4_cus();
 }
 
 // One tile per wave, G waves a workgroup (one workgroup per CU: the table
 // and the activation copy take 81 KB of LDS), at least 4 so that the table
 // fill is shared.
-hipError_t launch_gemm_rows4(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K, const uint16_t *X,
-                             int64_t N, float *Y, hipStream_t stream) {
-    if (!gemm_rows4_fits(scales, M, K, N)) return hipErrorInvalidValue;
+hipError_t launch_gemm_rows4(int fmt, const uint8_t *codes, const void *scales, const uint16_t *zeros,
+                             const float *tscale, int64_t M, int64_t K, const uint16_t *X, int64_t N, float *Y,
+                             hipStream_t stream) {
+    if (!gemm_rows4_fits(scales, zeros, M, K, N) || (fmt == kGemmAffine) != (zeros != nullptr) ||
+        (fmt == kGemmNvfp4) != (tscale != nullptr))
+        return hipErrorInvalidValue;
     const int64_t tiles = (M + 3) / 4;
     const int64_t cus = rows4_cus();
     int64_t G = (tiles + cus - 1) / cus;
@@ -396,9 +473,10 @@ hipError_t launch_gemm_rows4(const uint8_t *codes, const uint16_t *scales, int64
     if (G > kR4MaxWaves) G = kR4MaxWaves;
     const int64_t grid = (tiles + G - 1) / G;
     int k = (int)K, n = (int)N;
-    void *args[] = {&codes, &scales, &M, &k, &X, &n, &Y};
-    const void *fn = N <= 4 ? reinterpret_cast<const void *>(&gemm_rows4_kernel<1>)
-                            : reinterpret_cast<const void *>(&gemm_rows4_kernel<2>);
+    void *args[] = {&codes, &scales, &zeros, &tscale, &M, &k, &X, &n, &Y};
+    const void *fn = fmt == kGemmAffine ? rows4_kernel_for<kGemmAffine>(N)
+                     : fmt == kGemmNvfp4 ? rows4_kernel_for<kGemmNvfp4>(N)
+                                         : rows4_kernel_for<kGemmNf4>(N);
     return hipLaunchKernel(fn, dim3((unsigned)grid),
                            dim3((unsigned)(64 * G)), args, 0, stream);
 }

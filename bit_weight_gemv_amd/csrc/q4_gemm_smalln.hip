@@ -58,7 +58,6 @@ namespace q4 {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
-enum { kGemmNf4 = 0, kGemmAffine = 1, kGemmNvfp4 = 2 };
 
 constexpr int kGemmMaxWaves = 8;   // workgroup: up to 8 waves, one K slice each
 constexpr int kSliceBlocks = 4;    // 64-blocks per K slice (256 k)
@@ -242,13 +241,6 @@ __device__ __forceinline__ float4_t slab_mfma(const half8_t &x, const half8_t &w
         }
         return acc;
     }
-}
-
-// An E4M3 scale byte (sign clear) as fp32: its 7 magnitude bits placed at
-// fp32's exponent/mantissa boundary read as 2^(e-127) (1 + m/8), or for
-// e == 0 the denormal m 2^-129; times 2^120 that is the E4M3 value.
-__device__ __forceinline__ float e4m3_value(uint32_t b) {
-    return __builtin_bit_cast(float, (b & 0x7Fu) << 20) * 0x1p120f;
 }
 
 template <int NT, int S, bool XFIXED, int XP, int FMT>
@@ -461,7 +453,7 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
                 adj = half2_t{z, z};
             } else if constexpr (FMT == kGemmNvfp4) {
                 const uint32_t d = __shfl(sc[buf], 4 * j + b);
-                const _Float16 v = (_Float16)e4m3_value(d >> (8 * g));
+                const _Float16 v = (_Float16)e4m3_to_f32(d >> (8 * g));
                 adj = half2_t{v, v};
             }
 #pragma unroll
@@ -658,7 +650,8 @@ hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int6
     // that kernel's layout conditions fail, two or three tokens share each
     // table lookup in the GEMV kernels.
     if (N == 1) return launch_gemv(codes, scales, M, K, X, Y, stream);
-    if (gemm_rows4_fits(scales, M, K, N)) return launch_gemm_rows4(codes, scales, M, K, X, N, Y, stream);
+    if (gemm_rows4_fits(scales, nullptr, M, K, N))
+        return launch_gemm_rows4(kGemmNf4, codes, scales, nullptr, nullptr, M, K, X, N, Y, stream);
     if (gemv_tokens_fits(M, K, N)) return launch_gemv_tokens(codes, scales, M, K, X, N, Y, stream);
     return launch_matrix_core<kGemmNf4>(codes, scales, nullptr, nullptr, M, K, X, N, Y, stream);
 }
@@ -666,12 +659,16 @@ hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int6
 hipError_t launch_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
                                      int64_t K, const uint16_t *X, int64_t N, float *Y, hipStream_t stream) {
     if (N == 1) return launch_gemv_affine(codes, scales, zeros, M, K, X, Y, stream);
+    if (gemm_rows4_fits(scales, zeros, M, K, N))
+        return launch_gemm_rows4(kGemmAffine, codes, scales, zeros, nullptr, M, K, X, N, Y, stream);
     return launch_matrix_core<kGemmAffine>(codes, scales, zeros, nullptr, M, K, X, N, Y, stream);
 }
 
 hipError_t launch_gemm_smalln_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscale, int64_t M,
                                     int64_t K, const uint16_t *X, int64_t N, float *Y, hipStream_t stream) {
     if (N == 1) return launch_gemv_nvfp4(codes, scales, tscale, M, K, X, Y, stream);
+    if (gemm_rows4_fits(scales, nullptr, M, K, N))
+        return launch_gemm_rows4(kGemmNvfp4, codes, scales, nullptr, tscale, M, K, X, N, Y, stream);
     return launch_matrix_core<kGemmNvfp4>(codes, scales, nullptr, tscale, M, K, X, N, Y, stream);
 }
 

@@ -154,14 +154,6 @@ __device__ __forceinline__ float dot_word_exact(const uint32_t *lut, uint32_t w,
     return fmaf(lv(v3.y), bf16_hi(xw.w), p);
 }
 
-// An E4M3 scale byte (sign clear) as fp32: its 7 magnitude bits placed at
-// fp32's exponent/mantissa boundary give 2^(e-127) (1 + m/8) for e > 0 and
-// the denormal m 2^-129 for e == 0; times 2^120 that is exactly
-// 2^(e-7) (1 + m/8), or (m/8) 2^-6 (fp32 denormals are kept).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-    return __builtin_bit_cast(float, (b & 0x7Fu) << 20) * 0x1p120f;
-}
-
 // Raw activations of chunk c (16 dwords, two bf16 each) from global memory;
 // a lane past the row's end gets zeros.
 __device__ __forceinline__ void load_chunk_x(const uint16_t *__restrict__ x, int c, bool valid,

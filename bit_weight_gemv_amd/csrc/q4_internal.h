@@ -14,12 +14,17 @@ hipError_t launch_pack(const float *W, int64_t M, int64_t K, uint8_t *codes, uin
 bool gemv_tokens_fits(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemv_tokens(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                               const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
-// A chunk of 2..8 tokens on short rows (K <= 2048, K % 128 == 0, a
-// dword-aligned scale plane, at most 12 four-row tiles per CU): one 4-row
-// tile per wave on the 16-block 4x4x4 matrix-core instruction.
-bool gemm_rows4_fits(const uint16_t *scales, int64_t M, int64_t K, int64_t N);
-hipError_t launch_gemm_rows4(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K, const uint16_t *X,
-                             int64_t N, float *Y, hipStream_t stream);
+// Weight formats of the prefill kernels.
+enum { kGemmNf4 = 0, kGemmAffine = 1, kGemmNvfp4 = 2 };
+
+// A chunk of 2..8 tokens on short rows (K <= 2048, K % 128 == 0, dword-aligned
+// scale and zero-point planes, at most 12 four-row tiles per CU): one 4-row
+// tile per wave on the 16-block 4x4x4 matrix-core instruction.  zeros: the
+// affine format's (else null); tscale: the NVFP4-style format's (else null).
+bool gemm_rows4_fits(const void *scales, const uint16_t *zeros, int64_t M, int64_t K, int64_t N);
+hipError_t launch_gemm_rows4(int fmt, const uint8_t *codes, const void *scales, const uint16_t *zeros,
+                             const float *tscale, int64_t M, int64_t K, const uint16_t *X, int64_t N, float *Y,
+                             hipStream_t stream);
 hipError_t launch_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                        const uint16_t *x, float *y, hipStream_t stream);
 

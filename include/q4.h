@@ -322,6 +322,8 @@ int q4_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales,
  *
  * q4_gemm_smalln_affine -- Y[n][m] = sum_k (code(m,k) - z[m][k/64])
  * * s[m][k/64] * X[n][k]; codes, scales and zeros as q4_gemv_affine.
+ * Chunks of two to eight tokens take the 4-row tiles under the conditions
+ * of q4_gemm_smalln, the zero-point plane also dword-aligned.
  */
 int q4_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scales,
                           const uint16_t *zeros, int64_t M, int64_t K,
@@ -332,7 +334,8 @@ int q4_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scales,
  * q4_gemm_smalln_nvfp4 -- Y[n][m] = s * sum_k E2M1(code(m,k))
  * * E4M3(scale[m][k/16]) * X[n][k]; codes, scales and tscale as
  * q4_gemv_nvfp4, except that scales must be 4-byte aligned (the four scale
- * bytes of a 64-block are read as one dword).
+ * bytes of a 64-block are read as one dword).  Chunks of two to eight
+ * tokens take the 4-row tiles under the conditions of q4_gemm_smalln.
  */
 int q4_gemm_smalln_nvfp4(const uint8_t *codes, const uint8_t *scales,
                          const float *tscale, int64_t M, int64_t K,

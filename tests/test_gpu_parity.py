@@ -404,9 +404,14 @@ def test_fused_wide_range_activations(env, swiglu, Ms, K, kind):
 # The prefill product of the affine and NVFP4-style formats: one token (the
 # format's GEMV), two and three tokens, one and two 16-token halves,
 # activations in registers (K <= 2048, ragged last slice) and reloaded per
-# tile (longer rows), many tiles per workgroup.
+# tile (longer rows), many tiles per workgroup.  2..8 tokens on rows of at
+# most 2048 weights with K % 128 == 0 take the 4-row-tile kernel: one and
+# two token groups, ragged last tile and partial last group, rows shorter
+# than a load, one tile.
 FMT_GEMM_CASES = [(300, 2048, 1), (300, 2048, 2), (1000, 1984, 3), (77, 4160, 17), (300, 2048, 32),
-                  (20000, 192, 5), (50, 2112, 20), (70, 11008, 32), (1, 64, 2)]
+                  (20000, 192, 5), (50, 2112, 20), (70, 11008, 32), (1, 64, 2),
+                  (3001, 1920, 4), (13, 640, 7), (12288, 2048, 8), (4099, 1152, 6), (2, 256, 5),
+                  (1, 128, 3), (257, 2048, 8), (11008, 2048, 2)]
 
 
 def _nvfp4_upload(env, codes, scales, ts):
@@ -452,12 +457,35 @@ def test_gemm_smalln_formats_parity(env, M, K, N):
     _gemm_formats_case(env, M, K, N, W, X, "")
 
 
-@pytest.mark.parametrize("M,K,N", [(300, 2048, 2), (300, 2048, 17), (77, 4160, 32)])
+@pytest.mark.parametrize("M,K,N", [(300, 2048, 2), (300, 2048, 17), (77, 4160, 32), (300, 2048, 8),
+                                   (3001, 1920, 5)])
 def test_gemm_smalln_formats_wide_range_activations(env, M, K, N):
     seed = 9600 + M + K + N
     W = _wide_w(wl.weights(M, K, seed, std=0.5))
     X = np.stack([_wide_x(WIDE_KINDS[(n + seed) % len(WIDE_KINDS)], K, seed + n) for n in range(N)])
     _gemm_formats_case(env, M, K, N, W, X, "wide")
+
+
+@pytest.mark.parametrize("shift", [0, 1])
+@pytest.mark.parametrize("M,K,N", [(1001, 2048, 2), (257, 1024, 7)])
+def test_gemm_smalln_affine_zero_plane_alignment(env, M, K, N, shift):
+    """The affine prefill product with the zero-point plane dword-aligned
+    (4-row tiles) and at 2 mod 4 (the chunk then takes the matrix-core
+    kernel)."""
+    torch, q4, dev = env
+    seed = 3700 + M + K + N
+    W = wl.weights(M, K, seed, std=0.5) + np.float32(0.03)
+    X = wl.activations(N, K, seed, "unit_rms")
+    codes, scales, zeros, st = oracle.pack_affine(W)
+    assert st == 0
+    Y_ref, S = oracle.gemm_affine(codes, scales, zeros, M, K, X)
+    c, s, _ = _affine_upload(env, codes, scales, zeros)
+    z = _scales_at(env, zeros, shift)
+    assert z.data_ptr() % 4 == 2 * shift
+    Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+    Y = q4.q4_gemm_smalln_affine(c, s, z, Xd)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, S, f"affine gemm M={M} K={K} N={N} zero plane +{2 * shift} B")
 
 
 def test_gemv_bit_exact_invariants(env):
