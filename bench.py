@@ -45,11 +45,17 @@ KERNEL_SOURCES = [os.path.join(ROOT, "bit_weight_gemv_amd", "csrc", f)
 
 
 def kernel_source_hash():
+    """sha256 of the GEMV's sources with their // comments and blank lines
+    removed: an edit of a comment leaves the measured kernel as it was, so
+    it does not void the committed counter figures; any code change does."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 
@@ -826,7 +832,7 @@ def main():
         "dtype": "f16",
         "dtype_note": "fp16 table, fp32 accumulate: 4-bit codes; levels held as fp16 (rounded by at most "
                       "2^-11 relative); bf16 x converted exactly to fp16 under a power of two (or widened to "
-                      "fp32 when a wave's activations span more than 2^31); products exact in "
+                      "fp32 when a wave's activations span more than 2^28); products exact in "
                       "v_dot2_f32_f16; sums in fp32. A reading of the page's 'FP32 LUT x scale x x' that "
                       "stays inside the acceptance bound by proof",
         "data": "synthetic (seeded SplitMix64 normals; W ~ N(0, 0.02^2), x unit-RMS bf16)",

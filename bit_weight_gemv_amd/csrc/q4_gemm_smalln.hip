@@ -36,7 +36,7 @@
 //    by a power of two chosen from that token's largest magnitude in the
 //    slice, and keeps it in registers for every row tile it visits.  The
 //    inverse scale is applied to the wave's partial sums.  The conversion is
-//    exact while no nonzero value of a token's slice lies more than 2^31
+//    exact while no nonzero value of a token's slice lies more than 2^28
 //    below that token's largest (each lane tests its own values; one ballot
 //    decides for the wave).  A wave whose slice is not held exactly keeps
 //    the raw bf16 values instead and multiplies them with

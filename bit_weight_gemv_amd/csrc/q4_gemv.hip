@@ -25,7 +25,7 @@
 //    wave's largest magnitude so that no bf16 value can overflow fp16; the
 //    partial sums are scaled back by the inverse power of two (exact).  The
 //    conversion is exact while no nonzero activation of the wave lies more
-//    than 2^31 below that largest one.  A wave whose activations span more
+//    than 2^28 below that largest one.  A wave whose activations span more
 //    runs a plain loop instead (the exact loop in gemv_body) that
 //    multiplies the raw bf16 activations, widened exactly to fp32, with the
 //    table levels in fp32 FMAs: slower, same accuracy bound, for any finite

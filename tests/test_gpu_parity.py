@@ -282,19 +282,18 @@ def test_gemv_activation_ranges(env, kind):
 
 # ---------------------------------------------------------------------------
 # Activations of any range.  An fp16 copy of a wave's activations under one
-# power of two is exact only while they span at most 2^31; beyond that the
-# kernels take the raw bf16 values.  Each case puts a huge activation where
-# it meets only zero weights (a zero 64-block, or a column of code 7), so
-# the row sums come entirely from activations far below it: a conversion
-# that flushed them would give y = 0.  spread_31 / spread_32 sit on the
-# exactness threshold with activations 1 + 2^-7 (8 significant bits), which
-# the one-scale conversion would round by up to 2^-7 relative if it were
-# taken one binade too far.
+# power of two (the integer conversion on the bf16 bits) is exact only while
+# they span at most 2^28; beyond that the kernels take the raw bf16 values.
+# Each case puts a huge activation where it meets only zero weights (a zero
+# 64-block, or a column of code 7), so the row sums come entirely from
+# activations far below it: a conversion that flushed them would give y = 0.
+# spread_28 / spread_29 sit on the exactness threshold with activations
+# 1 + 2^-7 (8 significant bits), which a conversion taken one binade too far
+# would turn into wrong fp16 patterns; spread_31 / spread_32 lie past it.
 # ---------------------------------------------------------------------------
 
 # spread_n: unit magnitudes and one value 2^n: n = 28 is the widest spread the
-# integer conversion of the 4-row-tile prefill kernel holds exactly (fp16
-# normal numbers), n = 31 the widest for the fp32-rounding conversions.
+# integer conversion holds exactly (fp16 normal numbers).
 WIDE_KINDS = ["zero_block_2^60", "code7_column_2^60", "spread_28", "spread_29", "spread_31", "spread_32", "tiny_run",
               "many_windows"]
 K_ZERO_BLOCK, K_ZERO_COL = 64 * 3 + 5, 1000
