@@ -737,6 +737,34 @@ def test_gemm_smalln_full_size(env):
         _check(Y, Y_ref[:n_tok], S[:n_tok], f"smalln N={n_tok} all {M} rows")
 
 
+def test_gemm_formats_full_size(env):
+    """The prefill shape (11008 x 2048) in the affine and NVFP4-style
+    formats, packed by the oracle: chunks of 32, 17, 8, 5, 4 and 2 tokens
+    (the 16-row and the 4-row-tile kernels, in the launch configuration
+    bench.py times), every output against the oracle."""
+    torch, q4, dev = env
+    c = wl.CONFIGS["smalln"]
+    M, K, N = c["M"], c["K"], c["N"]
+    W = wl.weights(M, K, c["seed"])
+    X = wl.activations(N, K, c["seed"], c["x"])
+    Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+    threads = min(16, os.cpu_count() or 1)
+    codes, scales, zeros, st = oracle.pack_affine(W, threads=threads)
+    assert st == 0
+    Y_ref, S = oracle.gemm_affine(codes, scales, zeros, M, K, X, threads=threads)
+    cd, sd, zd = _affine_upload(env, codes, scales, zeros)
+    for n_tok in (32, 17, 8, 5, 4, 2):
+        Y = q4.q4_gemm_smalln_affine(cd, sd, zd, Xd[:n_tok].contiguous()).cpu().numpy()
+        _check(Y, Y_ref[:n_tok], S[:n_tok], f"affine smalln N={n_tok} all {M} rows")
+    ncodes, nscales, ts, st = oracle.pack_nvfp4(W, threads=threads)
+    assert st == 0
+    Y_ref, S = oracle.gemm_nvfp4(ncodes, nscales, ts, M, K, X, threads=threads)
+    cd, sd, td = _nvfp4_upload(env, ncodes, nscales, ts)
+    for n_tok in (32, 17, 8, 5, 4, 2):
+        Y = q4.q4_gemm_smalln_nvfp4(cd, sd, td, Xd[:n_tok].contiguous()).cpu().numpy()
+        _check(Y, Y_ref[:n_tok], S[:n_tok], f"nvfp4 smalln N={n_tok} all {M} rows")
+
+
 # ---------------------------------------------------------------------------
 # HIP graph capture (a decode step is captured once and replayed)
 # ---------------------------------------------------------------------------
