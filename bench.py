@@ -436,6 +436,63 @@ def affine_secondaries(torch, q4, wl, dev, steps, warmup):
     return out
 
 
+def fused_format_secondaries(torch, q4, wl, dev, steps, warmup, fmt):
+    """The fused decode projections of the affine or NVFP4-style format: the
+    gate/up pair with the SwiGLU epilogue (2 x 11008 x 2048, each matrix
+    packed on its own) and down with the residual added in place
+    (2048 x 11008), each against its unfused form (the format's GEMV per
+    matrix, then torch's epilogue)."""
+    out = []
+    pack = q4.q4_pack_affine if fmt == "affine" else q4.q4_pack_nvfp4
+    gemv = q4.q4_gemv_affine if fmt == "affine" else q4.q4_gemv_nvfp4
+    fused = q4.q4_gemv_fused_affine if fmt == "affine" else q4.q4_gemv_fused_nvfp4
+    label = "affine-format" if fmt == "affine" else "NVFP4-style"
+    for name, Ms, K, copies, seed in (("gateup_swiglu", (11008, 11008), 2048, 25, 71),
+                                      ("down_residual", (2048,), 11008, 50, 72)):
+        mats = []
+        for i, M in enumerate(Ms):
+            Wd = torch.from_numpy(wl.weights(M, K, seed + i)).to(dev)
+            *planes, status = pack(Wd)
+            torch.cuda.synchronize()
+            if int(status.item()) != 0:
+                raise RuntimeError(f"{label} pack flagged the {name} weights")
+            mats.append(tuple(planes))
+            del Wd
+        reps = [tuple(mats)] + [tuple(tuple(p.clone() for p in m) for m in mats) for _ in range(copies - 1)]
+        x = _upload_bits(torch, wl.activation(K, seed, "unit_rms"), torch.bfloat16, dev)
+        y = torch.empty(Ms[0], dtype=torch.float32, device=dev)
+        tmp = [torch.empty(M, dtype=torch.float32, device=dev) for M in Ms]
+        if name == "gateup_swiglu":
+            def f(*ms):
+                fused([m + (None,) for m in ms], x, "swiglu", [y])
+
+            def u(*ms):
+                for m, t in zip(ms, tmp):
+                    gemv(*m, x, t)
+                torch.mul(torch.nn.functional.silu(tmp[0]), tmp[1], out=y)
+        else:
+            def f(*ms):
+                fused([ms[0] + (None,)], x, "separate", [y], [y])  # residual in place
+
+            def u(*ms):
+                gemv(*ms[0], x, tmp[0])
+                y.add_(tmp[0])
+        f_ms, f_wall = time_graph(torch, f, reps, steps, warmup)
+        u_ms, _ = time_graph(torch, u, reps, steps, warmup)
+        per_row = (K // 2 + K // 16 + 0) if fmt == "nvfp4" else (K // 2 + 2 * (K // 32))
+        nb = sum(Ms) * per_row + (4 * len(Ms) if fmt == "nvfp4" else 0) + 2 * K + 4 * Ms[0] + (
+            4 * Ms[0] if name == "down_residual" else 0)
+        gbs = nb / (f_ms * 1e-3) / 1e9
+        log(f"{fmt} fused {name}: {f_ms * 1e3:.2f} us/call ({gbs:.0f} GB/s), unfused {u_ms * 1e3:.2f} us")
+        out.append({"workload": f"{label} fused {name} Ms={'+'.join(map(str, Ms))} K={K} N=1",
+                    "us_per_call": round(f_ms * 1e3, 3), "us_per_step_wall": round(f_wall * 1e3, 3),
+                    "achieved_GBs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": nb,
+                    "unfused_us_per_call": round(u_ms * 1e3, 3), "speedup_vs_unfused": round(u_ms / f_ms, 3)})
+        del reps, mats, x, y, tmp
+        torch.cuda.empty_cache()
+    return out
+
+
 def nvfp4_secondaries(torch, q4, wl, dev, steps, warmup):
     """The NVFP4-style format's GEMV (E2M1 codes, an E4M3 scale per 16
     weights, an f32 tensor scale) on the lm_head and down shapes."""
@@ -810,8 +867,10 @@ def main():
             secondary.extend(gather_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
         if "affine" in chosen:
             secondary.extend(affine_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
+            secondary.extend(fused_format_secondaries(torch, q4, wl, dev, args.steps, args.warmup, "affine"))
         if "nvfp4" in chosen:
             secondary.extend(nvfp4_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
+            secondary.extend(fused_format_secondaries(torch, q4, wl, dev, args.steps, args.warmup, "nvfp4"))
         if "x8" in chosen:
             secondary.extend(x8_secondaries(torch, q4, wl, dev, args.steps, args.warmup))
         if "pages" in chosen:

@@ -33,7 +33,8 @@ Q4_PACK_OVERFLOW = 2
 EXPORTED = ("q4_codes_bytes", "q4_scales_bytes", "q4_codebook", "q4_status_string",
             "q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused",
             "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_pack_nvfp4", "q4_gemv_nvfp4",
-            "q4_quantize_x8", "q4_gemv_affine_x8", "q4_gemm_smalln_affine", "q4_gemm_smalln_nvfp4")
+            "q4_quantize_x8", "q4_gemv_affine_x8", "q4_gemm_smalln_affine", "q4_gemm_smalln_nvfp4",
+            "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4")
 
 Q4_OUT_F32 = 0
 Q4_OUT_BF16 = 1
@@ -49,6 +50,18 @@ class Operand(ctypes.Structure):
     """q4_operand of include/q4.h."""
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("M", ctypes.c_int64),
                 ("bias", ctypes.c_void_p)]
+
+
+class OperandAffine(ctypes.Structure):
+    """q4_operand_affine of include/q4.h."""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("bias", ctypes.c_void_p)]
+
+
+class OperandNvfp4(ctypes.Structure):
+    """q4_operand_nvfp4 of include/q4.h."""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("tscale", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("bias", ctypes.c_void_p)]
 
 _lib = None
 _lock = threading.Lock()
@@ -86,8 +99,9 @@ def lib() -> ctypes.CDLL:
         L.q4_gemv.restype = I32
         L.q4_gemm_smalln.argtypes = [P, P, I64, I64, P, I64, P, P]
         L.q4_gemm_smalln.restype = I32
-        L.q4_gemv_fused.argtypes = [P, I32, I64, P, I32, P, P, P]
-        L.q4_gemv_fused.restype = I32
+        for name in ("q4_gemv_fused", "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4"):
+            getattr(L, name).argtypes = [P, I32, I64, P, I32, P, P, P]
+            getattr(L, name).restype = I32
         L.q4_gather_rows.argtypes = [P, P, I64, I64, P, I64, I32, P, P, P]
         L.q4_gather_rows.restype = I32
         L.q4_pack_affine.argtypes = [P, I64, I64, P, P, P, P, P]
@@ -248,22 +262,32 @@ def q4_gemm_smalln(codes, scales, X, Y=None, stream=None):
     return Y
 
 
-def q4_gemv_fused(ops, x, mode="separate", ys=None, residuals=None, stream=None):
-    """Several products of one bf16 x [K] in one launch.  ops: list of
-    (codes, scales, bias or None).  mode "separate": returns [y_i] with
-    y_i = W_i . x + bias_i (+ residuals[i]); mode "swiglu" (two ops, gate then
-    up): returns [y] with y = silu(W_0 . x + b_0) * (W_1 . x + b_1)
-    (+ residuals[0]).  residuals: None or a list of fp32 tensors / None; an
-    entry may be the output tensor itself (in-place add)."""
+def _fused(fmt, ops, x, mode, ys, residuals, stream):
+    """The fused launch of one weight format (see q4_gemv_fused)."""
     torch = _torch()
     if mode not in ("separate", "swiglu"):
         raise ValueError("mode must be 'separate' or 'swiglu'")
     n = len(ops)
-    arr = (Operand * max(n, 1))()
+    struct = {"nf4": Operand, "affine": OperandAffine, "nvfp4": OperandNvfp4}[fmt]
+    arr = (struct * max(n, 1))()
     K = None
-    keep = []
-    for i, (codes, scales, bias) in enumerate(ops):
-        M, Ki = _mk(codes, scales)
+    for i, op in enumerate(ops):
+        codes, scales, extra, bias = (op[0], op[1], None, op[2]) if fmt == "nf4" else op
+        if fmt == "nvfp4":
+            if codes.dim() != 2 or scales.dim() != 2:
+                raise ValueError("codes must be [M, K/2] and scales [M, K/16]")
+            M, Ki = codes.shape[0], codes.shape[1] * 2
+            if scales.shape[0] != M or scales.shape[1] * 16 != Ki:
+                raise ValueError("codes and scales disagree on M, K")
+            _check(codes, "codes", torch.uint8, codes.device)
+            _check(scales, "scales", torch.uint8, codes.device)
+            _check(extra, f"tscale[{i}]", torch.float32, codes.device)
+        else:
+            M, Ki = _mk(codes, scales)
+            if fmt == "affine":
+                _check(extra, f"zeros[{i}]", torch.float16, codes.device)
+                if tuple(extra.shape) != tuple(scales.shape):
+                    raise ValueError(f"zeros[{i}] must have the shape of scales")
         if K is not None and Ki != K:
             raise ValueError("all matrices must have the same K")
         K = Ki
@@ -271,8 +295,11 @@ def q4_gemv_fused(ops, x, mode="separate", ys=None, residuals=None, stream=None)
             _check(bias, f"bias[{i}]", torch.float32, codes.device)
             if bias.numel() != M:
                 raise ValueError(f"bias[{i}] must have M={M} entries")
-        arr[i] = Operand(codes.data_ptr(), scales.data_ptr(), M, bias.data_ptr() if bias is not None else 0)
-        keep.append((codes, scales, bias))
+        bp = bias.data_ptr() if bias is not None else 0
+        if fmt == "nf4":
+            arr[i] = Operand(codes.data_ptr(), scales.data_ptr(), M, bp)
+        else:
+            arr[i] = struct(codes.data_ptr(), scales.data_ptr(), extra.data_ptr(), M, bp)
     dev = ops[0][0].device
     _check(x, "x", torch.bfloat16, dev)
     if x.numel() != K:
@@ -295,13 +322,37 @@ def q4_gemv_fused(ops, x, mode="separate", ys=None, residuals=None, stream=None)
                 _check(r, f"residual[{i}]", torch.float32, dev)
                 if r.numel() != ys[i].numel():
                     raise ValueError(f"residual[{i}] must have as many entries as y[{i}]")
-    st = lib().q4_gemv_fused(ctypes.cast(arr, ctypes.c_void_p), n, K, _ptr(x),
-                             Q4_FUSE_SWIGLU if mode == "swiglu" else Q4_FUSE_SEPARATE,
-                             ctypes.cast(yp, ctypes.c_void_p), ctypes.cast(rp, ctypes.c_void_p) if rp is not None else None,
-                             _stream(stream))
+    name = {"nf4": "q4_gemv_fused", "affine": "q4_gemv_fused_affine", "nvfp4": "q4_gemv_fused_nvfp4"}[fmt]
+    st = getattr(lib(), name)(ctypes.cast(arr, ctypes.c_void_p), n, K, _ptr(x),
+                              Q4_FUSE_SWIGLU if mode == "swiglu" else Q4_FUSE_SEPARATE,
+                              ctypes.cast(yp, ctypes.c_void_p),
+                              ctypes.cast(rp, ctypes.c_void_p) if rp is not None else None, _stream(stream))
     if st != Q4_OK:
-        raise Q4Error(st, "q4_gemv_fused")
+        raise Q4Error(st, name)
     return ys
+
+
+def q4_gemv_fused(ops, x, mode="separate", ys=None, residuals=None, stream=None):
+    """Several products of one bf16 x [K] in one launch.  ops: list of
+    (codes, scales, bias or None).  mode "separate": returns [y_i] with
+    y_i = W_i . x + bias_i (+ residuals[i]); mode "swiglu" (two ops, gate then
+    up): returns [y] with y = silu(W_0 . x + b_0) * (W_1 . x + b_1)
+    (+ residuals[0]).  residuals: None or a list of fp32 tensors / None; an
+    entry may be the output tensor itself (in-place add)."""
+    return _fused("nf4", ops, x, mode, ys, residuals, stream)
+
+
+def q4_gemv_fused_affine(ops, x, mode="separate", ys=None, residuals=None, stream=None):
+    """q4_gemv_fused for affine-format matrices: ops is a list of (codes,
+    scales, zeros, bias or None)."""
+    return _fused("affine", ops, x, mode, ys, residuals, stream)
+
+
+def q4_gemv_fused_nvfp4(ops, x, mode="separate", ys=None, residuals=None, stream=None):
+    """q4_gemv_fused for NVFP4-style matrices: ops is a list of (codes,
+    E4M3 scales uint8 [M, K/16], tensor scale fp32 [1], bias or None); in the
+    swiglu mode each matrix keeps its own tensor scale."""
+    return _fused("nvfp4", ops, x, mode, ys, residuals, stream)
 
 
 def q4_gather_rows(codes, scales, ids, out_dtype=None, out=None, status=None, stream=None):

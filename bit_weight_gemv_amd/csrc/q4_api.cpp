@@ -248,8 +248,14 @@ int q4_gemm_smalln_nvfp4(const uint8_t *codes, const uint8_t *scales, const floa
     return launch_status(q4::launch_gemm_smalln_nvfp4(codes, scales, tscale, M, K, X, N, Y, (hipStream_t)stream));
 }
 
-int q4_gemv_fused(const q4_operand *ops, int count, int64_t K, const uint16_t *x, int mode, float *const *y,
-                  const float *const *residual, void *stream) {
+namespace {
+
+// The checks of the three fused entry points, on the operands in one form:
+// scales are fp16 per 64-block (K / 32 bytes a row) or, for the NVFP4-style
+// format, E4M3 bytes (K / 16 a row); the affine format needs zero points,
+// the NVFP4-style format a tensor scale.
+int fused_call(int fmt, const q4::FusedOperand *ops, int count, int64_t K, const uint16_t *x, int mode,
+               float *const *y, const float *const *residual, void *stream) {
     if (mode != Q4_FUSE_SEPARATE && mode != Q4_FUSE_SWIGLU) return Q4_ERR_SHAPE;
     if (count < 1 || count > Q4_MAX_FUSED) return Q4_ERR_SHAPE;
     if (mode == Q4_FUSE_SWIGLU && count != 2) return Q4_ERR_SHAPE;
@@ -264,18 +270,24 @@ int q4_gemv_fused(const q4_operand *ops, int count, int64_t K, const uint16_t *x
     if (!any) return Q4_OK;
     if (!x || !y) return Q4_ERR_NULL;
     if (!aligned(x, 16)) return Q4_ERR_ALIGN;
+    const uint64_t scale_row = fmt == q4::kGemmNvfp4 ? (uint64_t)K / 16 : (uint64_t)(K / 64) * 2;
     // Inputs (read only; they may overlap each other).
-    Range in[3 * Q4_MAX_FUSED + 1];
+    Range in[5 * Q4_MAX_FUSED + 1];
     int nin = 0;
     in[nin++] = range_of(x, (uint64_t)K * 2);
     for (int i = 0; i < count; ++i) {
         if (ops[i].M == 0) continue;
         if (!ops[i].codes || !ops[i].scales) return Q4_ERR_NULL;
-        if (!aligned(ops[i].codes, 16) || !aligned(ops[i].scales, 2) || !aligned(ops[i].bias, 4))
+        if (fmt == q4::kGemmAffine && !ops[i].zeros) return Q4_ERR_NULL;
+        if (fmt == q4::kGemmNvfp4 && !ops[i].tscale) return Q4_ERR_NULL;
+        if (!aligned(ops[i].codes, 16) || !aligned(ops[i].scales, 2) || !aligned(ops[i].bias, 4) ||
+            !aligned(ops[i].zeros, 2) || !aligned(ops[i].tscale, 4))
             return Q4_ERR_ALIGN;
         in[nin++] = range_of(ops[i].codes, (uint64_t)ops[i].M * (K / 2));
-        in[nin++] = range_of(ops[i].scales, (uint64_t)ops[i].M * (K / 64) * 2);
+        in[nin++] = range_of(ops[i].scales, (uint64_t)ops[i].M * scale_row);
         if (ops[i].bias) in[nin++] = range_of(ops[i].bias, (uint64_t)ops[i].M * 4);
+        if (ops[i].zeros) in[nin++] = range_of(ops[i].zeros, (uint64_t)ops[i].M * (K / 64) * 2);
+        if (ops[i].tscale) in[nin++] = range_of(ops[i].tscale, 4);
     }
     // Output o has ops[o].M floats (for SWIGLU, the common M).
     Range out[Q4_MAX_FUSED], res[Q4_MAX_FUSED];
@@ -300,10 +312,37 @@ int q4_gemv_fused(const q4_operand *ops, int count, int64_t K, const uint16_t *x
             if (overlap(out[o], out[p]) || overlap(out[o], res[p])) return Q4_ERR_OVERLAP;
         }
     }
-    q4::FusedOperand fo[Q4_MAX_FUSED];
-    for (int i = 0; i < count; ++i) fo[i] = {ops[i].codes, ops[i].scales, ops[i].M, ops[i].bias};
     return launch_status(
-        q4::launch_gemv_fused(fo, count, mode == Q4_FUSE_SWIGLU, K, x, y, residual, (hipStream_t)stream));
+        q4::launch_gemv_fused(fmt, ops, count, mode == Q4_FUSE_SWIGLU, K, x, y, residual, (hipStream_t)stream));
+}
+
+}  // namespace
+
+int q4_gemv_fused(const q4_operand *ops, int count, int64_t K, const uint16_t *x, int mode, float *const *y,
+                  const float *const *residual, void *stream) {
+    q4::FusedOperand fo[Q4_MAX_FUSED] = {};
+    if (ops && count >= 1 && count <= Q4_MAX_FUSED)
+        for (int i = 0; i < count; ++i) fo[i] = {ops[i].codes, ops[i].scales, ops[i].M, ops[i].bias, nullptr, nullptr};
+    return fused_call(q4::kGemmNf4, ops ? fo : nullptr, count, K, x, mode, y, residual, stream);
+}
+
+int q4_gemv_fused_affine(const q4_operand_affine *ops, int count, int64_t K, const uint16_t *x, int mode,
+                         float *const *y, const float *const *residual, void *stream) {
+    q4::FusedOperand fo[Q4_MAX_FUSED] = {};
+    if (ops && count >= 1 && count <= Q4_MAX_FUSED)
+        for (int i = 0; i < count; ++i)
+            fo[i] = {ops[i].codes, ops[i].scales, ops[i].M, ops[i].bias, ops[i].zeros, nullptr};
+    return fused_call(q4::kGemmAffine, ops ? fo : nullptr, count, K, x, mode, y, residual, stream);
+}
+
+int q4_gemv_fused_nvfp4(const q4_operand_nvfp4 *ops, int count, int64_t K, const uint16_t *x, int mode,
+                        float *const *y, const float *const *residual, void *stream) {
+    q4::FusedOperand fo[Q4_MAX_FUSED] = {};
+    if (ops && count >= 1 && count <= Q4_MAX_FUSED)
+        for (int i = 0; i < count; ++i)
+            fo[i] = {ops[i].codes, reinterpret_cast<const uint16_t *>(ops[i].scales), ops[i].M, ops[i].bias, nullptr,
+                     ops[i].tscale};
+    return fused_call(q4::kGemmNvfp4, ops ? fo : nullptr, count, K, x, mode, y, residual, stream);
 }
 
 int q4_gather_rows(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K, const int32_t *ids,

@@ -297,6 +297,8 @@ struct GemvSeg {
     const float *xd;         //   block scales [K/32]
     const uint8_t *codes1;
     const uint16_t *scales1;
+    const uint16_t *zeros1;  // affine SwiGLU form: the up matrix's zero points
+    const float *tscale1;    // NVFP4-style SwiGLU form: the up matrix's tensor scale
     const float *bias0;
     const float *bias1;
     const float *residual;
@@ -447,7 +449,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     uint32_t sc[TS ? 1 : S + 1][NR][CPL];
     uint32_t tsc[TS ? S + 1 : 1][NPART];  // TS: this lane's dword of each run
     uint32_t zc[ZEROS && !TS ? S + 1 : 1][NR][CPL];  // zero-point bits (affine codes only)
-    uint32_t tzc[ZEROS && TS ? S + 1 : 1];           // TS: this lane's dword of the zero points
+    uint32_t tzc[ZEROS && TS ? S + 1 : 1][NPART];    // TS: this lane's dword of each zero-point run
     // Tiles are loaded in order.  The next tile to load starts at output
     // r_begin + LPT * (tiles loaded so far); its pointers advance by one tile
     // per load.  Rows past r_end repeat the last valid row (their results are
@@ -460,7 +462,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     const uint16_t *next_scales0 = sg.scales0 + r_first * sst;
     const uint16_t *next_zeros0 = ZEROS ? sg.zeros0 + r_first * nsb : nullptr;
     const uint8_t *next_codes1 = MODE == kModeSwiglu ? sg.codes1 + r_first * row_bytes : nullptr;
-    const uint16_t *next_scales1 = MODE == kModeSwiglu ? sg.scales1 + r_first * nsb : nullptr;
+    const uint16_t *next_scales1 = MODE == kModeSwiglu ? sg.scales1 + r_first * sst : nullptr;
+    const uint16_t *next_zeros1 = ZEROS && MODE == kModeSwiglu ? sg.zeros1 + r_first * nsb : nullptr;
     // Outputs from the next tile's first row to the end of the group's rows
     // (to the end of the matrix when STRIDED).
     int64_t next_left = STRIDED ? sg.rows - r_first : r_end - r_begin;
@@ -476,10 +479,11 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         __amdgpu_buffer_rsrc_t zrs0 = srs0;
         if constexpr (ZEROS)
             zrs0 = buffer_rsrc(next_zeros0, real ? (uint32_t)(LPT * nsb * 2) : 0u);
-        __amdgpu_buffer_rsrc_t crs1 = crs0, srs1 = srs0;
+        __amdgpu_buffer_rsrc_t crs1 = crs0, srs1 = srs0, zrs1 = zrs0;
         if constexpr (MODE == kModeSwiglu) {
             crs1 = buffer_rsrc(next_codes1, real ? (uint32_t)(LPT * row_bytes) : 0u);
-            srs1 = buffer_rsrc(next_scales1, real ? (uint32_t)(LPT * nsb * 2) : 0u);
+            srs1 = buffer_rsrc(next_scales1, real ? (uint32_t)(LPT * sst * 2) : 0u);
+            if constexpr (ZEROS) zrs1 = buffer_rsrc(next_zeros1, real ? (uint32_t)(LPT * nsb * 2) : 0u);
         }
         if constexpr (TS) {
             // The run of the tile's valid rows (whole dwords: an even number
@@ -489,13 +493,17 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                 tsc[buf][0] = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(next_scales0, run), (int)ts_off, 0,
                                                                    kLoadNonTemporal);
                 if constexpr (ZEROS)
-                    tzc[buf] = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(next_zeros0, run), (int)ts_off, 0,
-                                                                    kLoadNonTemporal);
+                    tzc[buf][0] = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(next_zeros0, run), (int)ts_off,
+                                                                       0, kLoadNonTemporal);
             }
             if constexpr (MODE == kModeSwiglu)
-                if (r0 <= LPT && LPT < r1)
+                if (r0 <= LPT && LPT < r1) {
                     tsc[buf][NPART - 1] = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(next_scales1, run),
                                                                                (int)ts_off, 0, kLoadNonTemporal);
+                    if constexpr (ZEROS)
+                        tzc[buf][NPART - 1] = __builtin_amdgcn_raw_buffer_load_b32(
+                            buffer_rsrc(next_zeros1, run), (int)ts_off, 0, kLoadNonTemporal);
+                }
         }
 #pragma unroll
         for (int r = r0; r < r1; ++r) {
@@ -513,8 +521,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                     sc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(up ? srs1 : srs0, (int)(soff[i] * 2),
                                                                           rr * sst * 2, kLoadNonTemporal);
                 if constexpr (ZEROS && !TS)
-                    zc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(zrs0, (int)(soff[i] * 2), rr * nsb * 2,
-                                                                          kLoadNonTemporal);
+                    zc[buf][r][i] = __builtin_amdgcn_raw_buffer_load_b16(up ? zrs1 : zrs0, (int)(soff[i] * 2),
+                                                                          rr * nsb * 2, kLoadNonTemporal);
             }
         }
     };
@@ -524,7 +532,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         if constexpr (ZEROS) next_zeros0 += tile_step * nsb;
         if constexpr (MODE == kModeSwiglu) {
             next_codes1 += tile_step * row_bytes;
-            next_scales1 += tile_step * nsb;
+            next_scales1 += tile_step * sst;
+            if constexpr (ZEROS) next_zeros1 += tile_step * nsb;
         }
         next_left -= tile_step;
     };
@@ -668,8 +677,15 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
 
     const uint32_t laneoff = (uint32_t)lane << 2;
     // NVFP4-style format: the tensor scale joins the activations' inverse
-    // power of two (both multiply every finished sum).
-    if constexpr (FMT == kFmtNvfp4) down *= *sg.tscale;
+    // power of two (both multiply every finished sum).  In the SwiGLU form
+    // the gate and up matrices carry tensor scales of their own: each
+    // multiplies its finished sum in the store, before SiLU.
+    if constexpr (FMT == kFmtNvfp4 && MODE != kModeSwiglu) down *= *sg.tscale;
+    float ts_gate = 1.0f, ts_up = 1.0f;
+    if constexpr (FMT == kFmtNvfp4 && MODE == kModeSwiglu) {
+        ts_gate = *sg.tscale;
+        ts_up = *sg.tscale1;
+    }
 
     // Rows are reduced across the wave RG at a time (RG/NR tiles): the fixed
     // cost of the cross-lane reduction and of the store is paid once per RG
@@ -688,7 +704,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
 #pragma unroll
                 for (int r = 0; r < NR; ++r) {
                     tsb[r] = quad_bcast(tsc[buf][r < LPT ? 0 : NPART - 1], r % LPT);
-                    if constexpr (ZEROS) tzb[r] = quad_bcast(tzc[buf], r);
+                    if constexpr (ZEROS) tzb[r] = quad_bcast(tzc[buf][r < LPT ? 0 : NPART - 1], r % LPT);
                 }
             }
 #pragma unroll
@@ -796,8 +812,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
             // the up row LPT after.
             const int o = lane < RG / 2 ? lane : 0;
             const int gate_lane = (o / LPT) * NR + o % LPT;
-            const float g = __shfl(tot, gate_lane);
-            const float u = __shfl(tot, gate_lane + LPT);
+            const float g = __shfl(tot, gate_lane) * ts_gate;
+            const float u = __shfl(tot, gate_lane + LPT) * ts_up;
             const int64_t row = out_row(g0 * LPT + lane);
             if (lane < RG / 2 && row >= 0) {
                 const float a = sg.bias0 ? g + e.b0 : g;
@@ -846,7 +862,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                 return u32x4_t{v.x, v.y, v.z, v.w};
             };
             // The lane's part of row `row` of one matrix for token `tok`.
-            auto exact_row = [&](int tok, const uint8_t *cbase, const uint16_t *sbase, int64_t row) -> float {
+            auto exact_row = [&](int tok, const uint8_t *cbase, const uint16_t *sbase, const uint16_t *zbase,
+                                 int64_t row) -> float {
                 float a = 0.0f;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
@@ -857,7 +874,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                     const uint4 qv = *reinterpret_cast<const uint4 *>(cbase + row * row_bytes + c * 16);
                     const uint32_t sbits = sbase[row * sst + so];
                     float zoff = 0.0f;
-                    if constexpr (FMT == kFmtAffine) zoff = f16_bits_to_f32(sg.zeros0[row * nsb + so]) - 8.0f;
+                    if constexpr (FMT == kFmtAffine) zoff = f16_bits_to_f32(zbase[row * nsb + so]) - 8.0f;
                     float p0 = 0.0f, p1 = 0.0f;
 #pragma clang loop unroll(disable)
                     for (int d = 0; d < 4; ++d) {
@@ -875,7 +892,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                 }
                 return a;
             };
-            const float tsc = FMT == kFmtNvfp4 ? *sg.tscale : 1.0f;
+            const float tsc = FMT == kFmtNvfp4 && MODE != kModeSwiglu ? *sg.tscale : 1.0f;
             for (int64_t g0 = 0; g0 < nsteps; g0 += TPG) {
                 const Epi epi = fetch_epi(g0);
                 // Lane l gets the total of group row l % RG, as reduce_rows
@@ -896,7 +913,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                     for (int tk = 0; tk < NTOK; ++tk) {
                         const float v = row < 0 ? 0.0f
                                                 : exact_row(tk, up ? sg.codes1 : sg.codes0,
-                                                            up ? sg.scales1 : sg.scales0, row);
+                                                            up ? sg.scales1 : sg.scales0,
+                                                            up ? sg.zeros1 : sg.zeros0, row);
                         const float sum = wave_sum(v);
                         if ((tid & 63) % RG == gr) tot[tk] = sum;
                     }
@@ -1035,7 +1053,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
 
 // Several segments in one launch: workgroup b belongs to the last segment
 // whose first workgroup is <= b.
-template <int NR, int CPL, int S, int RG, bool MULTI, int MODE>
+template <int NR, int CPL, int S, int RG, bool MULTI, int MODE, int FMT = kFmtNf4>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
                           amdgpu_waves_per_eu(gemv_min_waves(CPL), 8))) void gemv_fused_kernel(GemvSegs segs, int K,
                                                    const uint16_t *__restrict__ x, int P) {
@@ -1045,17 +1063,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
         if (i < segs.n && (int)blockIdx.x >= segs.s[i].wg_begin) si = i;
     si = __builtin_amdgcn_readfirstlane(si);
     const GemvSeg &sg = segs.s[si];
-    gemv_body<NR, CPL, S, RG, MULTI, MODE>(sg, K, x, P, (int64_t)blockIdx.x - sg.wg_begin);
+    gemv_body<NR, CPL, S, RG, MULTI, MODE, FMT>(sg, K, x, P, (int64_t)blockIdx.x - sg.wg_begin);
 }
 
 // The one-segment form (a SwiGLU pair, or a single matrix): the segment is
 // the kernel argument itself, so its fields arrive with the first scalar
 // reads instead of after a lookup of the workgroup's segment.
-template <int NR, int CPL, int S, int RG, bool MULTI, int MODE, bool STRIDED = false, bool TS = false>
+template <int NR, int CPL, int S, int RG, bool MULTI, int MODE, bool STRIDED = false, bool TS = false,
+          int FMT = kFmtNf4>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
                           amdgpu_waves_per_eu(gemv_min_waves(CPL, TS), 8))) void gemv_fused1_kernel(GemvSeg sg, int K,
                                                    const uint16_t *__restrict__ x, int P) {
-    gemv_body<NR, CPL, S, RG, MULTI, MODE, kFmtNf4, STRIDED, TS>(sg, K, x, P, (int64_t)blockIdx.x);
+    gemv_body<NR, CPL, S, RG, MULTI, MODE, FMT, STRIDED, TS>(sg, K, x, P, (int64_t)blockIdx.x);
 }
 
 namespace {
@@ -1254,22 +1273,28 @@ int64_t plan_segments(GemvSegs &segs, int lpt, int G, int64_t *tpg, int64_t cap 
     return begin;
 }
 
-template <int NR, int CPL, int S, int RG, bool MULTI, int MODE, bool STRIDED = false>
+template <int NR, int CPL, int S, int RG, bool MULTI, int MODE, bool STRIDED = false, int FMT = kFmtNf4>
 hipError_t launch_fused_variant(GemvSegs segs, int K, const uint16_t *x, int P, int G, int64_t grid,
                                 hipStream_t stream) {
     if (!MULTI && (K / 8 > P * G || K / 8 > kSharedXUnits)) return hipErrorInvalidValue;
     if (MODE == kModeSwiglu || segs.n == 1) {
         void *args[] = {&segs.s[0], &K, &x, &P};
-        const void *fn = reinterpret_cast<const void *>(&gemv_fused1_kernel<NR, CPL, S, RG, MULTI, MODE, STRIDED>);
-        if constexpr (CPL == 1 && S == 0 && NR <= 4)
-            if (scale_runs_aligned(segs.s[0].scales0, segs.s[0].scales1, K))
-                fn = reinterpret_cast<const void *>(&gemv_fused1_kernel<NR, CPL, S, RG, MULTI, MODE, STRIDED, true>);
+        const void *fn =
+            reinterpret_cast<const void *>(&gemv_fused1_kernel<NR, CPL, S, RG, MULTI, MODE, STRIDED, false, FMT>);
+        // One run of scales (and zero points) a tile and matrix: NF4 in
+        // every order, the affine format outside the strided order (as its
+        // GEMV); the NVFP4-style scales are read per chunk.
+        if constexpr (CPL == 1 && S == 0 && NR <= 4 && FMT != kFmtNvfp4 && !(FMT == kFmtAffine && STRIDED))
+            if (scale_runs_aligned(segs.s[0].scales0, segs.s[0].scales1, K) &&
+                (FMT != kFmtAffine || scale_runs_aligned(segs.s[0].zeros0, segs.s[0].zeros1, K)))
+                fn = reinterpret_cast<const void *>(
+                    &gemv_fused1_kernel<NR, CPL, S, RG, MULTI, MODE, STRIDED, true, FMT>);
         return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
     }
     if (STRIDED) return hipErrorInvalidValue;  // the strided order serves one matrix
     if constexpr (MODE != kModeSwiglu) {
         void *args[] = {&segs, &K, &x, &P};
-        return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_fused_kernel<NR, CPL, S, RG, MULTI, MODE>),
+        return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_fused_kernel<NR, CPL, S, RG, MULTI, MODE, FMT>),
                                dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
     }
     return hipErrorInvalidValue;
@@ -1277,7 +1302,7 @@ hipError_t launch_fused_variant(GemvSegs segs, int K, const uint16_t *x, int P, 
 
 // The variant for the row length, as launch_gemv chooses it (rows of up to
 // 512 chunks, K <= 16384).
-template <int MODE>
+template <int MODE, int FMT>
 hipError_t launch_fused_mode(GemvSegs segs, int K, const uint16_t *x, hipStream_t stream) {
     const int C = K / kChunkWeights;
     constexpr int half = MODE == kModeSwiglu ? 2 : 1;  // rows per output
@@ -1290,15 +1315,15 @@ hipError_t launch_fused_mode(GemvSegs segs, int K, const uint16_t *x, hipStream_
         if (one_matrix && tiles > strided_from()) {
             const int G = strided_waves(tiles);
             const int64_t grid = plan_segments(segs, lpt, G, &tpg, 2LL * cu_count());
-            return launch_fused_variant<4, 1, 0, 4, false, MODE, true>(segs, K, x, 64, G, grid, stream);
+            return launch_fused_variant<4, 1, 0, 4, false, MODE, true, FMT>(segs, K, x, 64, G, grid, stream);
         }
         if (tiles <= one_tile_limit()) {
             const OneTileShape sh = one_tile_shape(tiles, K);
             const int64_t grid = plan_segments(segs, lpt, sh.G, &tpg, sh.cap);
-            return launch_fused_variant<4, 1, 0, 4, false, MODE>(segs, K, x, 64, sh.G, grid, stream);
+            return launch_fused_variant<4, 1, 0, 4, false, MODE, false, FMT>(segs, K, x, 64, sh.G, grid, stream);
         }
         const int64_t grid = plan_segments(segs, lpt, 8, &tpg);
-        return launch_fused_variant<4, 1, 1, 8, false, MODE>(segs, K, x, 64, 8, grid, stream);
+        return launch_fused_variant<4, 1, 1, 8, false, MODE, false, FMT>(segs, K, x, 64, 8, grid, stream);
     }
     if (C <= 64 * kMaxWavesPerGroup) {
         const int wpg = (C + 63) / 64;
@@ -1307,15 +1332,18 @@ hipError_t launch_fused_mode(GemvSegs segs, int K, const uint16_t *x, hipStream_
         for (int i = 0; i < segs.n; ++i) tiles += (segs.s[i].rows + lpt - 1) / lpt;
         const OneTileShape sh = multi_shape(tiles, wpg);
         const int64_t grid = plan_segments(segs, lpt, sh.G, &tpg, sh.cap);
-        return launch_fused_variant<4, 1, 0, 4, true, MODE>(segs, K, x, wpg * 64, sh.G, grid, stream);
+        return launch_fused_variant<4, 1, 0, 4, true, MODE, false, FMT>(segs, K, x, wpg * 64, sh.G, grid, stream);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_gemv_fused(const FusedOperand *ops, int count, bool swiglu, int64_t K, const uint16_t *x,
-                             float *const *y, const float *const *residual, hipStream_t stream) {
+namespace {
+
+template <int FMT>
+hipError_t launch_gemv_fused_fmt(const FusedOperand *ops, int count, bool swiglu, int64_t K, const uint16_t *x,
+                                 float *const *y, const float *const *residual, hipStream_t stream) {
     GemvSegs segs{};
     if (swiglu) {
         if (count != 2 || ops[0].M != ops[1].M) return hipErrorInvalidValue;
@@ -1323,15 +1351,19 @@ hipError_t launch_gemv_fused(const FusedOperand *ops, int count, bool swiglu, in
         GemvSeg &g = segs.s[0];
         g.codes0 = ops[0].codes;
         g.scales0 = ops[0].scales;
+        g.zeros0 = ops[0].zeros;
+        g.tscale = ops[0].tscale;
         g.bias0 = ops[0].bias;
         g.codes1 = ops[1].codes;
         g.scales1 = ops[1].scales;
+        g.zeros1 = ops[1].zeros;
+        g.tscale1 = ops[1].tscale;
         g.bias1 = ops[1].bias;
         g.residual = residual ? residual[0] : nullptr;
         g.y = y[0];
         g.rows = ops[0].M;
         segs.n = 1;
-        return launch_fused_mode<kModeSwiglu>(segs, (int)K, x, stream);
+        return launch_fused_mode<kModeSwiglu, FMT>(segs, (int)K, x, stream);
     }
     if (count < 1 || count > kMaxSegs) return hipErrorInvalidValue;
     for (int i = 0; i < count; ++i) {
@@ -1339,13 +1371,31 @@ hipError_t launch_gemv_fused(const FusedOperand *ops, int count, bool swiglu, in
         GemvSeg &g = segs.s[segs.n++];
         g.codes0 = ops[i].codes;
         g.scales0 = ops[i].scales;
+        g.zeros0 = ops[i].zeros;
+        g.tscale = ops[i].tscale;
         g.bias0 = ops[i].bias;
         g.residual = residual ? residual[i] : nullptr;
         g.y = y[i];
         g.rows = ops[i].M;
     }
     if (segs.n == 0) return hipSuccess;
-    return launch_fused_mode<kModeEpi>(segs, (int)K, x, stream);
+    return launch_fused_mode<kModeEpi, FMT>(segs, (int)K, x, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_fused(int fmt, const FusedOperand *ops, int count, bool swiglu, int64_t K, const uint16_t *x,
+                             float *const *y, const float *const *residual, hipStream_t stream) {
+    switch (fmt) {
+        case kGemmNf4:
+            return launch_gemv_fused_fmt<kFmtNf4>(ops, count, swiglu, K, x, y, residual, stream);
+        case kGemmAffine:
+            return launch_gemv_fused_fmt<kFmtAffine>(ops, count, swiglu, K, x, y, residual, stream);
+        case kGemmNvfp4:
+            return launch_gemv_fused_fmt<kFmtNvfp4>(ops, count, swiglu, K, x, y, residual, stream);
+        default:
+            return hipErrorInvalidValue;
+    }
 }
 
 // Variant choice (by measurement).  Rows of one wave (K <= 2048): one 4-row

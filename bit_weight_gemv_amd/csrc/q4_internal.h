@@ -48,18 +48,24 @@ hipError_t launch_pack_nvfp4(const float *W, int64_t M, int64_t K, uint8_t *code
 hipError_t launch_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscale, int64_t M,
                              int64_t K, const uint16_t *x, float *y, hipStream_t stream);
 
-// One matrix of a fused GEMV launch (sharing x with the others).
+// One matrix of a fused GEMV launch (sharing x with the others).  scales:
+// fp16 per 64-block (NF4, affine) or the E4M3 bytes (NVFP4-style, passed as
+// 16-bit units); zeros: the affine format's zero points; tscale: the
+// NVFP4-style tensor scale (device f32).
 struct FusedOperand {
     const uint8_t *codes;
     const uint16_t *scales;
     int64_t M;
     const float *bias;  // or null
+    const uint16_t *zeros;
+    const float *tscale;
 };
 
 // count matrices (at most 4) into y[i] (+ residual[i]), or, with swiglu,
 // silu(W0 . x + b0) * (W1 . x + b1) (+ residual[0]) into y[0] (count == 2,
-// equal M).  K <= 16384.  Arguments are validated by the caller.
-hipError_t launch_gemv_fused(const FusedOperand *ops, int count, bool swiglu, int64_t K, const uint16_t *x,
+// equal M), in weight format fmt (kGemmNf4, kGemmAffine, kGemmNvfp4).
+// K <= 16384.  Arguments are validated by the caller.
+hipError_t launch_gemv_fused(int fmt, const FusedOperand *ops, int count, bool swiglu, int64_t K, const uint16_t *x,
                              float *const *y, const float *const *residual, hipStream_t stream);
 
 hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,

@@ -309,6 +309,44 @@ int q4_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales,
                   const uint16_t *x, float *y, void *stream);
 
 /*
+ * The fused decode projections of q4_gemv_fused in the two formats above
+ * (the epilogues of the deep-fold "Decode V2" page, section 6 Linear
+ * primitive, and accel/tensor func Linear / func SwiGLU, on the affine
+ * format of accel/tensor type Int4 and the NVFP4-style format of gizai
+ * fp4Blocks).  One operand per matrix:
+ *   affine: codes, scales and zeros as q4_gemv_affine;
+ *   NVFP4-style: codes, E4M3 scales (2-byte aligned) and the device tensor
+ *   scale as q4_gemv_nvfp4.  In the SWIGLU mode the gate and the up matrix
+ *   keep their own tensor scales, each applied to its finished sum before
+ *   SiLU.
+ * Modes, x, y, residual, accuracy and errors as q4_gemv_fused; a missing
+ * zeros (affine) or tscale (NVFP4-style) of a non-empty matrix is
+ * Q4_ERR_NULL, and they count as inputs for Q4_ERR_OVERLAP.
+ */
+typedef struct {
+    const uint8_t *codes;    /* packed codes [M][K/2], 16-byte aligned        */
+    const uint16_t *scales;  /* fp16 bits [M][K/64], 2-byte aligned           */
+    const uint16_t *zeros;   /* fp16 zero points [M][K/64], 2-byte aligned    */
+    int64_t M;               /* rows (M >= 0)                                 */
+    const float *bias;       /* fp32 [M], 4-byte aligned, or NULL             */
+} q4_operand_affine;
+
+typedef struct {
+    const uint8_t *codes;    /* packed E2M1 codes [M][K/2], 16-byte aligned   */
+    const uint8_t *scales;   /* E4M3 bytes [M][K/16], 2-byte aligned          */
+    const float *tscale;     /* the f32 tensor scale (device), 4-byte aligned */
+    int64_t M;               /* rows (M >= 0)                                 */
+    const float *bias;       /* fp32 [M], 4-byte aligned, or NULL             */
+} q4_operand_nvfp4;
+
+int q4_gemv_fused_affine(const q4_operand_affine *ops, int count, int64_t K,
+                         const uint16_t *x, int mode, float *const *y,
+                         const float *const *residual, void *stream);
+int q4_gemv_fused_nvfp4(const q4_operand_nvfp4 *ops, int count, int64_t K,
+                        const uint16_t *x, int mode, float *const *y,
+                        const float *const *residual, void *stream);
+
+/*
  * The prefill-chunk forms of the two formats above (as q4_gemm_smalln: the
  * deep-fold "Decode V2" page, section 0 Goals, runs a prompt as chunks of up
  * to 32 tokens through one product; accel/tensor func Int4MatMul reads the

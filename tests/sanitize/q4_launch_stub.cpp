@@ -61,10 +61,18 @@ hipError_t launch_gemv_nvfp4(const uint8_t *, const uint8_t *, const float *, in
                              const uint16_t *, float *, hipStream_t) {
     return note("gemv_nvfp4 M=%lld K=%lld%.0lld", M, K, 0);
 }
-hipError_t launch_gemv_fused(const FusedOperand *ops, int count, bool swiglu, int64_t K, const uint16_t *,
+hipError_t launch_gemv_fused(int fmt, const FusedOperand *ops, int count, bool swiglu, int64_t K, const uint16_t *,
                              float *const *, const float *const *, hipStream_t) {
     long long rows = 0;
     for (int i = 0; i < count; ++i) rows += ops[i].M;
+    if (fmt == kGemmAffine)
+        return note(swiglu ? "gemv_fused_affine swiglu count=%lld K=%lld rows=%lld"
+                           : "gemv_fused_affine count=%lld K=%lld rows=%lld",
+                    count, K, rows);
+    if (fmt == kGemmNvfp4)
+        return note(swiglu ? "gemv_fused_nvfp4 swiglu count=%lld K=%lld rows=%lld"
+                           : "gemv_fused_nvfp4 count=%lld K=%lld rows=%lld",
+                    count, K, rows);
     return note(swiglu ? "gemv_fused swiglu count=%lld K=%lld rows=%lld" : "gemv_fused count=%lld K=%lld rows=%lld",
                 count, K, rows);
 }

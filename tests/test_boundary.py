@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
     for n in ("q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused",
               "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_pack_nvfp4", "q4_gemv_nvfp4",
               "q4_quantize_x8", "q4_gemv_affine_x8", "q4_gemm_smalln_affine", "q4_gemm_smalln_nvfp4",
-              "q4_codebook", "q4_codes_bytes",
+              "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4", "q4_codebook", "q4_codes_bytes",
               "q4_scales_bytes", "q4_status_string"):
         assert n in names
 
@@ -217,6 +217,45 @@ def test_fused_overlap(q4):
     assert _fused(q4, [op], 128, C, SEP, [D], [D + 4]) == q4.Q4_ERR_OVERLAP    # residual shifted onto y
     assert _fused(q4, [op, (F, G, 16, 0)], 128, C, SEP, [D, D + 4096], [0, D + 16]) == q4.Q4_ERR_OVERLAP
     assert _fused(q4, [op, (F, G, 16, 0)], 128, C, SWI, [G + 16]) == q4.Q4_ERR_OVERLAP  # y over up scales
+
+
+def _fused_fmt(q4, fmt, ops, K, x, mode, ys, res=None):
+    """fmt "affine": ops (codes, scales, zeros, M, bias); "nvfp4": (codes,
+    scales, tscale, M, bias); fake addresses."""
+    st = q4.OperandAffine if fmt == "affine" else q4.OperandNvfp4
+    fn = q4.lib().q4_gemv_fused_affine if fmt == "affine" else q4.lib().q4_gemv_fused_nvfp4
+    arr = (st * max(len(ops), 1))(*[st(*op) for op in ops])
+    yp = (ctypes.c_void_p * max(len(ys), 1))(*ys) if ys is not None else None
+    rp = (ctypes.c_void_p * max(len(res), 1))(*res) if res is not None else None
+    return fn(ctypes.cast(arr, ctypes.c_void_p) if ops else None, len(ops), K, x, mode,
+              ctypes.cast(yp, ctypes.c_void_p) if yp is not None else None,
+              ctypes.cast(rp, ctypes.c_void_p) if rp is not None else None, None)
+
+
+def test_fused_formats_host_checks(q4):
+    """The affine and NVFP4-style fused entry points: the shared checks, plus
+    their own operands (zero points, E4M3 scales, tensor scale) as inputs."""
+    SEP, SWI = q4.Q4_FUSE_SEPARATE, q4.Q4_FUSE_SWIGLU
+    aop = (A, B, E, 16, 0)   # codes 1 KB at K=128, scales 64 B, zeros 64 B at E
+    nop = (A, B, E, 16, 0)   # E4M3 scales 128 B at B, tensor scale at E
+    for fmt, op in (("affine", aop), ("nvfp4", nop)):
+        assert _fused_fmt(q4, fmt, [op], 128, C, 2, [D]) == q4.Q4_ERR_SHAPE
+        assert _fused_fmt(q4, fmt, [op] * 3, 128, C, SWI, [D]) == q4.Q4_ERR_SHAPE
+        assert _fused_fmt(q4, fmt, [op], 100, C, SEP, [D]) == q4.Q4_ERR_SHAPE
+        assert _fused_fmt(q4, fmt, [], 128, C, SEP, [D]) == q4.Q4_ERR_SHAPE
+        assert _fused_fmt(q4, fmt, [(0, 0, 0, 0, 0)], 128, 0, SEP, [0]) == q4.Q4_OK   # nothing to do
+        assert _fused_fmt(q4, fmt, [op], 128, 0, SEP, [D]) == q4.Q4_ERR_NULL
+        assert _fused_fmt(q4, fmt, [(A, B, 0, 16, 0)], 128, C, SEP, [D]) == q4.Q4_ERR_NULL  # zeros / tscale
+        assert _fused_fmt(q4, fmt, [(A, B + 1, E, 16, 0)], 128, C, SEP, [D]) == q4.Q4_ERR_ALIGN
+        assert _fused_fmt(q4, fmt, [op], 128, C, SEP, [D + 2]) == q4.Q4_ERR_ALIGN
+        assert _fused_fmt(q4, fmt, [op], 128, C, SEP, [E]) == q4.Q4_ERR_OVERLAP      # y over zeros / tscale
+        assert _fused_fmt(q4, fmt, [op], 128, C, SEP, [A + 512]) == q4.Q4_ERR_OVERLAP
+    assert _fused_fmt(q4, "affine", [(A, B, E + 1, 16, 0)], 128, C, SEP, [D]) == q4.Q4_ERR_ALIGN
+    assert _fused_fmt(q4, "nvfp4", [(A, B, E + 2, 16, 0)], 128, C, SEP, [D]) == q4.Q4_ERR_ALIGN
+    # NVFP4-style scales are K / 16 bytes a row: y 64 B after the scales' start
+    # overlaps them (it would not for fp16 scales of the same M).
+    assert _fused_fmt(q4, "nvfp4", [nop], 128, C, SEP, [B + 64]) == q4.Q4_ERR_OVERLAP
+
     # every call above fails a host check; the exact-alias residual is legal
     # and is exercised on the GPU, not here
 

@@ -898,11 +898,12 @@ def _check_bound(y_gpu, y_ref, bound, what):
 
 
 def _fused_case(env, Ms, K, seed, swiglu=False, bias=True, residual=True, alias=(), x_recipe="unit_rms",
-                bias_scale=0.5, x=None, w_hook=None):
-    """Packs len(Ms) matrices, runs q4_gemv_fused, checks every output against
-    the oracle and against the unfused q4_gemv followed by torch's epilogue.
-    `x` (bf16 bits) replaces the recipe's activations; `w_hook(W)` edits each
-    fp32 matrix before it is packed."""
+                bias_scale=0.5, x=None, w_hook=None, fmt="nf4"):
+    """Packs len(Ms) matrices in format `fmt` ("nf4", "affine", "nvfp4"),
+    runs the format's fused entry point, checks every output against the
+    oracle and against the format's unfused GEMV followed by torch's
+    epilogue.  `x` (bf16 bits) replaces the recipe's activations; `w_hook(W)`
+    edits each fp32 matrix before it is packed."""
     torch, q4, dev = env
     if x is None:
         x = wl.activation(K, seed, x_recipe)
@@ -913,17 +914,26 @@ def _fused_case(env, Ms, K, seed, swiglu=False, bias=True, residual=True, alias=
         W = wl.weights(M, K, seed + 17 * i)
         if w_hook is not None:
             W = w_hook(W)
-        codes, scales, st = oracle.pack(W)
+        if fmt == "affine":
+            codes, scales, zeros, st = oracle.pack_affine(W)
+            t, S = oracle.gemv_affine(codes, scales, zeros, M, K, x)
+            dev_ops = _affine_upload(env, codes, scales, zeros)
+        elif fmt == "nvfp4":
+            codes, scales, tsv, st = oracle.pack_nvfp4(W)
+            t, S = oracle.gemv_nvfp4(codes, scales, tsv, M, K, x)
+            dev_ops = _nvfp4_upload(env, codes, scales, tsv)
+        else:
+            codes, scales, st = oracle.pack(W)
+            t, S = oracle.gemv(codes, scales, M, K, x)
+            dev_ops = _upload_packed(env, codes, scales)
         assert st == 0
-        t, S = oracle.gemv(codes, scales, M, K, x)
-        c, s = _upload_packed(env, codes, scales)
         b = (rng.standard_normal(M) * bias_scale).astype(np.float32) if bias else None
         bd = torch.from_numpy(b).to(dev) if b is not None else None
-        ops.append((c, s, bd))
+        ops.append(tuple(dev_ops) + (bd,))
         ts.append(t)
         Ss.append(S)
         biases.append(b)
-        packed.append((c, s))
+        packed.append(tuple(dev_ops))
     nout = 1 if swiglu else len(Ms)
     res_h = [(rng.standard_normal(Ms[o]) * 2).astype(np.float32) if residual else None for o in range(nout)]
     ys = [torch.full((Ms[o],), float("nan"), device=dev) for o in range(nout)]
@@ -936,17 +946,19 @@ def _fused_case(env, Ms, K, seed, swiglu=False, bias=True, residual=True, alias=
             res_d.append(ys[o])
         else:
             res_d.append(torch.from_numpy(res_h[o]).to(dev))
-    q4.q4_gemv_fused(ops, xd, "swiglu" if swiglu else "separate", ys, res_d if residual else None)
+    fused = {"nf4": q4.q4_gemv_fused, "affine": q4.q4_gemv_fused_affine, "nvfp4": q4.q4_gemv_fused_nvfp4}[fmt]
+    gemv = {"nf4": q4.q4_gemv, "affine": q4.q4_gemv_affine, "nvfp4": q4.q4_gemv_nvfp4}[fmt]
+    fused(ops, xd, "swiglu" if swiglu else "separate", ys, res_d if residual else None)
     torch.cuda.synchronize()
     y_ref, bound = _fused_ref(ts, Ss, biases, res_h, swiglu)
-    what = f"fused {'swiglu' if swiglu else 'separate'} Ms={Ms} K={K}"
+    what = f"{fmt} fused {'swiglu' if swiglu else 'separate'} Ms={Ms} K={K}"
     for o in range(nout):
         _check_bound(ys[o].cpu().numpy(), y_ref[o], bound[o], f"{what} out {o}")
     # Unfused: one q4_gemv per matrix, then torch's epilogue in fp32.
-    tg = [q4.q4_gemv(c, s, xd) for c, s in packed]
+    tg = [gemv(*p, xd) for p in packed]
     for i in range(len(tg)):
         if biases[i] is not None:
-            tg[i] = tg[i] + ops[i][2]
+            tg[i] = tg[i] + ops[i][-1]
     if swiglu:
         un = [torch.nn.functional.silu(tg[0]) * tg[1]]
     else:
@@ -1005,6 +1017,58 @@ def test_fused_swiglu_wide_activations(env):
     # gate biases of tens drive silu into both tails (e^-z overflows to inf
     # for z < -88)
     _fused_case(env, (500, 500), 2048, seed=6200, swiglu=True, x_recipe="normal", bias_scale=60.0)
+
+
+# The fused forms of the affine and NVFP4-style formats: the launcher's
+# row-length classes (one wave a row, a workgroup a row), ragged and empty
+# segments, the strided order (11008 x 2048 SwiGLU), one-tile and ring plans,
+# an in-place residual.  Each NVFP4-style matrix has its own tensor scale.
+FUSED_FMT_SEPARATE = [((2048, 256, 256), 2048), ((1, 65, 0, 300), 512), ((2048,), 11008), ((33, 1000, 2), 4096),
+                      ((20000, 300), 1024), ((129, 5, 4100), 4160)]
+FUSED_FMT_SWIGLU = [(11008, 2048), (77, 512), (5000, 2048), (129, 11008), (300, 4096), (20000, 1024), (1, 64)]
+
+
+@pytest.mark.parametrize("fmt", ["affine", "nvfp4"])
+@pytest.mark.parametrize("Ms,K", FUSED_FMT_SEPARATE)
+def test_fused_formats_separate(env, fmt, Ms, K):
+    _fused_case(env, Ms, K, seed=5300 + K + sum(Ms), fmt=fmt, alias=(0,) if K == 11008 else ())
+
+
+@pytest.mark.parametrize("fmt", ["affine", "nvfp4"])
+@pytest.mark.parametrize("M,K", FUSED_FMT_SWIGLU)
+def test_fused_formats_swiglu(env, fmt, M, K):
+    _fused_case(env, (M, M), K, seed=6400 + M + K, swiglu=True, fmt=fmt)
+
+
+@pytest.mark.parametrize("fmt", ["affine", "nvfp4"])
+@pytest.mark.parametrize("kind", ["code7_column_2^60", "spread_32"])
+@pytest.mark.parametrize("swiglu,Ms,K", [(False, (2048, 256, 256), 2048), (True, (1000, 1000), 2048),
+                                         (True, (300, 300), 4160)])
+def test_fused_formats_wide_range_activations(env, fmt, swiglu, Ms, K, kind):
+    """Activations past the fp16 conversion's range: the exact loop, with
+    the up matrix's own zero points and tensor scale in the SwiGLU form."""
+    seed = 7700 + K + sum(Ms)
+    _fused_case(env, Ms, K, seed, swiglu=swiglu, x=_wide_x(kind, K, seed), w_hook=_wide_w, bias_scale=1e-3, fmt=fmt)
+
+
+@pytest.mark.parametrize("M,K", [(1101, 576), (1100, 1024), (9001, 192)])
+def test_fused_affine_swiglu_planes_of_one_matrix(env, M, K):
+    """Affine gate and up as the halves of one packed matrix: with an odd M
+    or an odd number of blocks a row the up half's scale and zero-point
+    planes sit at 2 mod 4, and the launch reads them per row."""
+    torch, q4, dev = env
+    W = wl.weights(2 * M, K, 6600 + M) + np.float32(0.02)
+    x = wl.activation(K, 6600 + M, "unit_rms")
+    codes, scales, zeros, st = oracle.pack_affine(W)
+    assert st == 0
+    t, S = oracle.gemv_affine(codes, scales, zeros, 2 * M, K, x)
+    c, s, z = _affine_upload(env, codes, scales, zeros)
+    _log(f"affine swiglu M={M} K={K}: up planes at {s[M:].data_ptr() % 4}, {z[M:].data_ptr() % 4} mod 4")
+    ops = [(c[:M], s[:M], z[:M], None), (c[M:], s[M:], z[M:], None)]
+    y = q4.q4_gemv_fused_affine(ops, _x_dev(env, x), "swiglu")[0]
+    torch.cuda.synchronize()
+    y_ref, bound = _fused_ref([t[:M], t[M:]], [S[:M], S[M:]], [None, None], [None], True)
+    _check_bound(y.cpu().numpy(), y_ref[0], bound[0], f"affine swiglu halves M={M} K={K}")
 
 
 def test_fused_swiglu_halves_of_one_matrix(env):

@@ -131,7 +131,13 @@ ops = (q4.Operand * 2)(q4.Operand(A, B, 64, None), q4.Operand(C, D, 64, None))
 ys = (ctypes.c_void_p * 1)(E)
 assert L.q4_gemv_fused(ops, 2, 2048, base + 6 * (1 << 19), 1, ys, None, None) == 0, last()
 assert last() == "gemv_fused swiglu count=2 K=2048 rows=128", last()
-assert L.q4stub_calls() == n0 + 8, L.q4stub_calls() - n0
+aops = (q4.OperandAffine * 1)(q4.OperandAffine(A, B, C, 64, None))
+assert L.q4_gemv_fused_affine(aops, 1, 2048, base + 6 * (1 << 19), 0, ys, None, None) == 0, last()
+assert last() == "gemv_fused_affine count=1 K=2048 rows=64", last()
+nops = (q4.OperandNvfp4 * 2)(q4.OperandNvfp4(A, B, C, 64, None), q4.OperandNvfp4(D, base + 7 * (1 << 19), C, 64, None))
+assert L.q4_gemv_fused_nvfp4(nops, 2, 2048, base + 6 * (1 << 19), 1, ys, None, None) == 0, last()
+assert last() == "gemv_fused_nvfp4 swiglu count=2 K=2048 rows=128", last()
+assert L.q4stub_calls() == n0 + 10, L.q4stub_calls() - n0
 print("launch stand-ins reached:", L.q4stub_calls() - n0)
 """
 
@@ -157,4 +163,4 @@ def test_c_abi_host_layer_under_asan_ubsan(tmp_path):
     out = r.stdout + r.stderr
     assert "Sanitizer" not in out and "runtime error" not in out, out[-4000:]
     assert r.returncode == 0, out[-4000:]
-    assert "launch stand-ins reached: 8" in out, out[-2000:]
+    assert "launch stand-ins reached: 10" in out, out[-2000:]
