@@ -1547,19 +1547,25 @@ def test_affine_x8_chain_full_size_down(env):
 
 
 def test_graph_capture_other_entry_points(env):
-    """Gather, affine, NVFP4-style, int8 quantisation and int8 GEMV captured
-    in one graph; every replay (with eager work in between) equals eager."""
+    """Gather, affine, NVFP4-style (GEMV, prefill on 4-row and 16-row
+    tiles, fused SwiGLU and bias forms), int8 quantisation and int8 GEMV
+    captured in one graph; every replay (with eager work in between) equals
+    eager."""
     torch, q4, dev = env
     M, K = 3000, 2048
     W = wl.weights(M, K, 7300)
     Wd = cases.to_dev(W, torch, dev)
     xd = _x_dev(env, wl.activation(K, 7300, "unit_rms"))
+    X4 = cases.to_dev(wl.activations(4, K, 7301, "unit_rms").view(np.int16), torch, dev).view(torch.bfloat16)
+    X17 = cases.to_dev(wl.activations(17, K, 7302, "unit_rms").view(np.int16), torch, dev).view(torch.bfloat16)
     codes, scales, _ = oracle.pack(W)
     c, s = _upload_packed(env, codes, scales)
     ac, asc, az, _ = q4.q4_pack_affine(Wd)
     nc, ns, nt, _ = q4.q4_pack_nvfp4(Wd)
     torch.cuda.synchronize()
     ids = torch.tensor([5, 0, M - 1, 17], dtype=torch.int32, device=dev)
+    h = M // 2
+    bias = torch.linspace(-1.0, 1.0, M, device=dev)
 
     def run(outs=None):
         o = outs or {}
@@ -1568,7 +1574,14 @@ def test_graph_capture_other_entry_points(env):
         yn = q4.q4_gemv_nvfp4(nc, ns, nt, xd, o.get("yn"))
         q1, q2, d = q4.q4_quantize_x8(xd, 2, o.get("q1"), o.get("q2"), o.get("d"))
         y8 = q4.q4_gemv_affine_x8(ac, asc, az, q1, q2, d, o.get("y8"))
-        return {"g": g, "gs": st, "ya": ya, "yn": yn, "q1": q1, "q2": q2, "d": d, "y8": y8}
+        Ya4 = q4.q4_gemm_smalln_affine(ac, asc, az, X4, o.get("Ya4"))
+        Yn4 = q4.q4_gemm_smalln_nvfp4(nc, ns, nt, X4, o.get("Yn4"))
+        Ya17 = q4.q4_gemm_smalln_affine(ac, asc, az, X17, o.get("Ya17"))
+        fa = q4.q4_gemv_fused_affine([(ac[:h], asc[:h], az[:h], None), (ac[h:], asc[h:], az[h:], None)], xd,
+                                     "swiglu", [o["fa"]] if "fa" in o else None)[0]
+        fn = q4.q4_gemv_fused_nvfp4([(nc, ns, nt, bias)], xd, "separate", [o["fn"]] if "fn" in o else None)[0]
+        return {"g": g, "gs": st, "ya": ya, "yn": yn, "q1": q1, "q2": q2, "d": d, "y8": y8, "Ya4": Ya4,
+                "Yn4": Yn4, "Ya17": Ya17, "fa": fa, "fn": fn}
 
     eager = {k: v.clone() for k, v in run().items()}
     torch.cuda.synchronize()
