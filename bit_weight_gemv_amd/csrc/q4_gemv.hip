@@ -691,7 +691,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     // cost of the cross-lane reduction and of the store is paid once per RG
     // rows.  Ring step: accumulate tile t from buffer `buf` into rows
     // [j*NR, j*NR+NR) of the group (if t exists), then refill the buffer
-    // with tile t + S + 1 (unconditionally; past the end it reads nothing).
+    // with tile t + S + 1 (past the end it reads nothing; see the refill).
     constexpr int TPG = RG / NR;  // tiles per reduction group
     static_assert(RG % NR == 0 && TPG % (S + 1) == 0, "group must hold whole ring turns");
     float accn[NTOK][RG];
@@ -768,7 +768,13 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
 #pragma unroll
                 for (int r = 0; r < NR; ++r) accn[t][j * NR + r] = 0.0f;
         }
-        load_tile(buf);  // tile t + S + 1
+        // Refill with tile t + S + 1.  Groups of waves (MULTI) skip refills
+        // past their last tile: those would load nothing, but each load
+        // instruction still costs the CU's address unit (down 2048 x 11008:
+        // 5.14 -> 5.05 us; 5120 x 5120: 5.75 -> 5.62).  Row-per-wave kernels
+        // keep the refill unconditional: a conditional one there changed the
+        // compiler's wait counts (lm_head 27 -> 46 us).
+        if (!MULTI || t + S + 1 < ntiles) load_tile(buf);
     };
 
     // The epilogue operands of a reduction group (first tile g0): lane l
