@@ -768,13 +768,14 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
 #pragma unroll
                 for (int r = 0; r < NR; ++r) accn[t][j * NR + r] = 0.0f;
         }
-        // Refill with tile t + S + 1.  Groups of waves (MULTI) skip refills
-        // past their last tile: those would load nothing, but each load
-        // instruction still costs the CU's address unit (down 2048 x 11008:
-        // 5.14 -> 5.05 us; 5120 x 5120: 5.75 -> 5.62).  Row-per-wave kernels
-        // keep the refill unconditional: a conditional one there changed the
-        // compiler's wait counts (lm_head 27 -> 46 us).
-        if (!MULTI || t + S + 1 < ntiles) load_tile(buf);
+        // Refill with tile t + S + 1.  The plain products of groups of waves
+        // (MULTI) skip refills past their last tile: those would load
+        // nothing, but each load instruction still costs the CU's address
+        // unit (down 2048 x 11008: 5.14 -> 5.05 us; 5120 x 5120: 5.75 ->
+        // 5.62).  Elsewhere the refill stays unconditional: a conditional one
+        // changed the compiler's wait counts (row-per-wave lm_head 27 -> 46
+        // us; the fused down + residual 5.32 -> 5.79 us).
+        if (!(MULTI && MODE == kModePlain) || t + S + 1 < ntiles) load_tile(buf);
     };
 
     // The epilogue operands of a reduction group (first tile g0): lane l
