@@ -356,8 +356,10 @@ struct X8Args {
 // NTOK > 1 (rows of one wave, one tile per wave, plain NF4): x is NTOK
 // tokens, [NTOK][K] bf16, and y is [NTOK][rows]; every table lookup serves
 // all tokens (a prefill chunk of 2 or 3 tokens).
+// ONE: every group has at most one tile (the launch guarantees it), and the
+// ring refill after it is left out.
 template <int NR, int CPL, int S, int RG, bool MULTI, int MODE, int FMT = kFmtNf4, bool STRIDED = false,
-          bool TS = false, int NTOK = 1>
+          bool TS = false, int NTOK = 1, bool ONE = false>
 __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16_t *__restrict__ x, int P,
                                           int64_t wg) {
     constexpr bool X8 = FMT == kFmtAffineX8 || FMT == kFmtAffineX8x2;
@@ -775,7 +777,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
         // 5.62).  Elsewhere the refill stays unconditional: a conditional one
         // changed the compiler's wait counts (row-per-wave lm_head 27 -> 46
         // us; the fused down + residual 5.32 -> 5.79 us).
-        if (!(MULTI && MODE == kModePlain) || t + S + 1 < ntiles) load_tile(buf);
+        if constexpr (!ONE)
+            if (!(MULTI && MODE == kModePlain) || t + S + 1 < ntiles) load_tile(buf);
     };
 
     // The epilogue operands of a reduction group (first tile g0): lane l
@@ -970,7 +973,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     }
 }
 
-template <int NR, int CPL, int S, int RG, bool MULTI, bool STRIDED = false, bool TS = false>
+template <int NR, int CPL, int S, int RG, bool MULTI, bool STRIDED = false, bool TS = false, bool ONE = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, CPL)),
                           amdgpu_waves_per_eu(gemv_min_waves(CPL, TS, true), 8))) void gemv_kernel(const uint8_t *__restrict__ codes,
                                                    const uint16_t *__restrict__ scales, int64_t M,
@@ -984,7 +987,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, gemv_max_block(MULTI, 
     sg.rows = M;
     sg.rows_q = rows_q;
     sg.rows_rem = rows_rem;
-    gemv_body<NR, CPL, S, RG, MULTI, kModePlain, kFmtNf4, STRIDED, TS>(sg, K, x, P, (int64_t)blockIdx.x);
+    gemv_body<NR, CPL, S, RG, MULTI, kModePlain, kFmtNf4, STRIDED, TS, 1, ONE>(sg, K, x, P, (int64_t)blockIdx.x);
 }
 
 // A prefill chunk of NTOK = 2 or 3 tokens on rows of one wave: Y [NTOK][M] =
@@ -1160,9 +1163,19 @@ hipError_t launch_variant(const uint8_t *codes, const uint16_t *scales, const vo
         (void)extra;
         void *args[] = {&codes, &scales, &M, &K, &x, &y, &P, &rows_q, &rows_rem};
         const void *fn = reinterpret_cast<const void *>(&gemv_kernel<NR, CPL, S, RG, MULTI, STRIDED>);
-        if constexpr (CPL == 1 && S == 0 && NR <= 4)
+        if constexpr (CPL == 1 && S == 0 && NR <= 4) {
+            // Small one-tile launches (every wave at most one tile, at most 4
+            // tiles a CU) leave out the ring refill, which would load nothing
+            // but still queue a round of loads at the wave's end: 256 x 512
+            // 3.69 -> 3.38 us, 1024 x 1024 3.71 -> 3.43, 2048 x 2048 3.80 ->
+            // 3.57.  (Larger one-tile launches measured slower that way:
+            // 11008 x 2048 4.80 -> 4.89, 16384 x 2048 5.5 -> 5.8.)
+            const int64_t tiles = (M + NR - 1) / NR;
+            const bool one = !MULTI && !STRIDED && tiles <= ngroups && tiles <= 4LL * cu_count();
             if (scale_runs_aligned(scales, nullptr, K))
-                fn = reinterpret_cast<const void *>(&gemv_kernel<NR, CPL, S, RG, MULTI, STRIDED, true>);
+                fn = one ? reinterpret_cast<const void *>(&gemv_kernel<NR, CPL, S, RG, MULTI, STRIDED, true, true>)
+                         : reinterpret_cast<const void *>(&gemv_kernel<NR, CPL, S, RG, MULTI, STRIDED, true>);
+        }
         return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)(P * G)), args, 0, stream);
     }
 }
