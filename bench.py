@@ -899,7 +899,7 @@ def main():
                    "copies_rotated": args.copies, "bytes_per_call": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "q4::gemv_kernel<4,1,0,4,false,true,true>",
+                     "kernel": "q4::gemv_kernel<4,1,0,4,false,true,true,false>",
                      "kernel_us": round(k_mean_ms * 1e3, 3),
                      "timing": "HIP graph of the timed calls, events on the replay stream"},
         "eager": eager,
