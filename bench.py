@@ -1,7 +1,7 @@
 """Benchmark of the 4-bit codebook GEMV on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--copies R] [--no-secondary]
-                    [--secondary tiny,down,smalln,gateup,fused,gather,affine,nvfp4,x8,pages]
+                    [--secondary tiny,down,smalln,gateup,prefill_down,fused,gather,affine,nvfp4,x8,pages]
 
 A step is one q4_gemv call on the lm_head workload (M x K = 151936 x 2048,
 x bf16 unit-RMS, y fp32): the projection the metric is quoted on.  Inputs are
@@ -747,9 +747,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--secondary", default="tiny,down,smalln,gateup,fused,gather,affine,nvfp4,x8,pages",
+    ap.add_argument("--secondary", default="tiny,down,smalln,gateup,prefill_down,fused,gather,affine,nvfp4,x8,pages",
                     help="comma-separated secondary workloads to time "
-                         "(tiny, down, smalln, gateup, fused, gather, affine, nvfp4, x8, pages)")
+                         "(tiny, down, smalln, gateup, prefill_down, fused, gather, affine, nvfp4, x8, pages)")
     ap.add_argument("--eager", action="store_true",
                     help="also time the calls launched one by one from Python")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -823,11 +823,15 @@ def main():
         chosen = [n.strip() for n in args.secondary.split(",") if n.strip()]
         # tiny (256 x 512, 72 KB) stays in cache and is launch-bound: one copy,
         # timed for its microseconds only.
-        for sname, ncopies, ntok in (("tiny", 1, None), ("down", 50, None), ("smalln", 45, 32), ("gateup", 25, None)):
+        # prefill_down: the prefill sweep on the down projection's shape
+        # (rows of 11008 weights, the grouped kernels' side of the dispatch).
+        for sname, cname, ncopies, ntok in (("tiny", "tiny", 1, None), ("down", "down", 50, None),
+                                            ("smalln", "smalln", 45, 32), ("gateup", "gateup", 25, None),
+                                            ("prefill_down", "down", 50, 32)):
             if sname not in chosen:
                 continue
-            sc = wl.CONFIGS[sname]
-            _, _, sreps, sx = prepare(torch, q4, wl, sname, dev, ncopies, n_tokens=ntok)
+            sc = wl.CONFIGS[cname]
+            _, _, sreps, sx = prepare(torch, q4, wl, cname, dev, ncopies, n_tokens=ntok)
             if ntok is None:
                 sy = torch.empty(sc["M"], dtype=torch.float32, device=dev)
 
@@ -850,7 +854,7 @@ def main():
             log(f"{sname}: read floor {rf_us:.2f} us ({rf_grid}x{rf_block})")
             if ntok is not None:
                 # The prefill sweep: the first n tokens of the same chunk.
-                for n in (16, 8, 4, 2, 1):
+                for n in ((16, 8, 4, 2, 1) if sname == "smalln" else (16, 8, 4, 3, 2)):
                     sxn = sx[:n].contiguous()
                     syn = torch.empty((n, sc["M"]), dtype=torch.float32, device=dev)
 

@@ -658,6 +658,7 @@ hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int6
     if (gemm_rows4_fits(scales, nullptr, M, K, N))
         return launch_gemm_rows4(kGemmNf4, codes, scales, nullptr, nullptr, M, K, X, N, Y, stream);
     if (gemv_tokens_fits(M, K, N)) return launch_gemv_tokens(codes, scales, M, K, X, N, Y, stream);
+    if (gemv_tokens_multi_fits(M, K, N)) return launch_gemv_tokens_multi(codes, scales, M, K, X, N, Y, stream);
     return launch_matrix_core<kGemmNf4>(codes, scales, nullptr, nullptr, M, K, X, N, Y, stream);
 }
 

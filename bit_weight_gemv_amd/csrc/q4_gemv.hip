@@ -353,7 +353,8 @@ struct X8Args {
 // quad broadcasts (DPP, inside each wave): one load instruction per tile and
 // plane instead of one 2-byte load per row.
 //
-// NTOK > 1 (rows of one wave, one tile per wave, plain NF4): x is NTOK
+// NTOK > 1 (plain NF4, one chunk a lane, no ring: rows of one wave, one tile
+// per wave, or rows of a group of waves): x is NTOK
 // tokens, [NTOK][K] bf16, and y is [NTOK][rows]; every table lookup serves
 // all tokens (a prefill chunk of 2 or 3 tokens).
 // ONE: every group has at most one tile (the launch guarantees it), and the
@@ -366,13 +367,13 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     constexpr bool X8TWO = FMT == kFmtAffineX8x2;
     constexpr bool ZEROS = FMT == kFmtAffine || X8;  // zero-point plane
     __shared__ uint32_t lut[X8 ? 1 : kLutDwords];
-    __shared__ float red[kMaxWavesPerBlock][RG];
+    __shared__ float red[NTOK][kMaxWavesPerBlock][RG];
     // Groups of one wave all need the whole activation vector: it is read
     // from global memory once per workgroup into LDS (raw bf16, 16 bytes per
     // lane) and every wave takes its chunks from there.
     __shared__ uint4 xs[(MULTI || X8) ? 1 : kSharedXUnits * NTOK];
-    static_assert(NTOK == 1 || (!MULTI && MODE == kModePlain && FMT == kFmtNf4 && CPL == 1 && S == 0),
-                  "several tokens: rows of one wave, plain NF4, one chunk a lane");
+    static_assert(NTOK == 1 || (MODE == kModePlain && FMT == kFmtNf4 && CPL == 1 && S == 0 && !STRIDED),
+                  "several tokens: plain NF4, one chunk a lane, no ring");
 
     static_assert(MODE != kModeSwiglu || NR % 2 == 0, "a SwiGLU tile pairs gate and up rows");
     constexpr int LPT = MODE == kModeSwiglu ? NR / 2 : NR;  // outputs per tile
@@ -554,12 +555,16 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     // The first tiles load unconditionally: an empty row range loads through
     // zero-record resources (no memory access), and no branch makes the
     // compiler's wait analysis assume the tile loads might be missing.
-    uint32_t xraw[16];
+    uint32_t xrawn[MULTI ? NTOK : 1][16];
+    auto &xraw = xrawn[0];
     u32x4_t xunit[NTOK];  // this lane's 16 bytes of the shared activation copy, per token
     const int xunits = K >> 3;
     if constexpr (!X8) {
         if (MULTI) {
-            if (CPL == 1) load_chunk_x(x, cidx[0], cvalid[0], xraw);
+            // (Token t's activations start t * K values further.)
+            if (CPL == 1)
+#pragma unroll
+                for (int t = 0; t < NTOK; ++t) load_chunk_x(x + (int64_t)t * K, cidx[0], cvalid[0], xrawn[t]);
         } else {
             // Bytes past the vector's end read as zero (buffer bounds).
 #pragma unroll
@@ -614,8 +619,14 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     if constexpr (X8) {
         // (no table and no shared activation copy to wait for)
     } else if constexpr (MULTI) {
-        down = convert_x<CPL, true>([&](int i, uint32_t(&r)[16]) { load_chunk_x(x, cidx[i], cvalid[i], r); },
-                                    xraw, xh, xexact);
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) {
+            bool ex = true;
+            downn[t] = convert_x<CPL, true>(
+                [&](int i, uint32_t(&r)[16]) { load_chunk_x(x + (int64_t)t * K, cidx[i], cvalid[i], r); }, xrawn[t],
+                xhn[t], ex);
+            xexact = xexact && ex;
+        }
         __syncthreads();
     } else {
         if ((int)threadIdx.x < xunits)
@@ -866,7 +877,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                 if (!valid) return u32x4_t{0u, 0u, 0u, 0u};
                 uint4 v;
                 if constexpr (MULTI)
-                    v = reinterpret_cast<const uint4 *>(x)[c * 4 + d];
+                    v = reinterpret_cast<const uint4 *>(x + (int64_t)tok * K)[c * 4 + d];
                 else
                     v = xs[tok * xunits + c * 4 + d];
                 return u32x4_t{v.x, v.y, v.z, v.w};
@@ -934,13 +945,20 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
 #pragma unroll
                     for (int tk = 1; tk < NTOK; ++tk) store(tot[tk], g0, epi, tk);
                 } else {
-                    if (lane < RG) red[wave][lane] = tot[0] * tsc;
+                    if (lane < RG) {
+                        red[0][wave][lane] = tot[0] * tsc;
+#pragma unroll
+                        for (int tk = 1; tk < NTOK; ++tk) red[tk][wave][lane] = tot[tk];
+                    }
                     __syncthreads();
                     if (wig == 0) {
-                        float sum = 0.0f;
-                        if (lane < RG)
-                            for (int w = 0; w < wpg; ++w) sum += red[grp * wpg + w][lane];
-                        store(sum, g0, epi);
+#pragma unroll
+                        for (int tk = 0; tk < NTOK; ++tk) {
+                            float sum = 0.0f;
+                            if (lane < RG)
+                                for (int w = 0; w < wpg; ++w) sum += red[tk][grp * wpg + w][lane];
+                            store(sum, g0, epi, tk);
+                        }
                     }
                     __syncthreads();
                 }
@@ -960,13 +978,23 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
 #pragma unroll
             for (int t = 1; t < NTOK; ++t) store(reduce_rows<RG>(accn[t]) * downn[t], g0, epi, t);
         } else {
-            if (lane < RG) red[wave][lane] = tot;
+            // (Every lane takes part in each token's cross-lane reduction.)
+            float totn[NTOK];
+            totn[0] = tot;
+#pragma unroll
+            for (int t = 1; t < NTOK; ++t) totn[t] = reduce_rows<RG>(accn[t]) * downn[t];
+            if (lane < RG)
+#pragma unroll
+                for (int t = 0; t < NTOK; ++t) red[t][wave][lane] = totn[t];
             __syncthreads();
             if (wig == 0) {
-                float sum = 0.0f;
-                if (lane < RG)
-                    for (int w = 0; w < wpg; ++w) sum += red[grp * wpg + w][lane];
-                store(sum, g0, epi);
+#pragma unroll
+                for (int t = 0; t < NTOK; ++t) {
+                    float sum = 0.0f;
+                    if (lane < RG)
+                        for (int w = 0; w < wpg; ++w) sum += red[t][grp * wpg + w][lane];
+                    store(sum, g0, epi, t);
+                }
             }
             __syncthreads();
         }
@@ -1004,6 +1032,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 768), amdgpu_waves_per
     sg.rows_q = rows_q;
     sg.rows_rem = rows_rem;
     gemv_body<4, 1, 0, 4, false, kModePlain, kFmtNf4, false, TS, NTOK>(sg, K, X, P, (int64_t)blockIdx.x);
+}
+
+// The same for rows spanning a group of waves (one chunk a lane): NTOK = 2..4
+// tokens, 16 VGPRs of activations each; up to 16 waves a CU for two tokens
+// (at most 128 VGPRs), 12 for three or four.
+constexpr int tokens_multi_waves(int ntok) { return ntok == 2 ? 16 : 12; }
+template <int NTOK, bool TS>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * tokens_multi_waves(NTOK)),
+                          amdgpu_waves_per_eu(tokens_multi_waves(NTOK) / 4, 8))) void
+gemv_tokens_multi_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, int64_t M, int K,
+                         const uint16_t *__restrict__ X, float *__restrict__ Y, int P, int64_t rows_q,
+                         int rows_rem) {
+    GemvSeg sg{};
+    sg.codes0 = codes;
+    sg.scales0 = scales;
+    sg.y = Y;
+    sg.rows = M;
+    sg.rows_q = rows_q;
+    sg.rows_rem = rows_rem;
+    gemv_body<4, 1, 0, 4, true, kModePlain, kFmtNf4, false, TS, NTOK>(sg, K, X, P, (int64_t)blockIdx.x);
 }
 
 // The affine format's GEMV (y = W . x with W = (code - z) * s).
@@ -1240,9 +1288,9 @@ OneTileShape one_tile_shape(int64_t tiles, int K) {
 // 5.75 (5 of 3), 27648 x 5120 18.9 -> 16.2 (2 of 3, two per CU), 8192 x 8192
 // 9.28 -> 8.82 (2 of 4), 4096 x 14336 8.54 -> 8.55 (1 of 7); a ring of two
 // tiles per group, or 24-32 waves per CU, was slower on every shape.
-OneTileShape multi_shape(int64_t tiles, int wpg) {
+OneTileShape multi_shape(int64_t tiles, int wpg, int max_waves = 16) {
     const int64_t cus = cu_count();
-    const int gmax = 16 / wpg > 0 ? 16 / wpg : 1;
+    const int gmax = max_waves / wpg > 0 ? max_waves / wpg : 1;
     // Groups of more than 8 waves stay one workgroup per CU (28 waves per CU
     // measured slower than 14 on 5120 x 27648: 17.1 against 15.5 us).
     const int64_t per_cu = (tiles <= cus * gmax || 2 * wpg > 16) ? 1 : 2;
@@ -1483,7 +1531,50 @@ const void *gemv_tokens_fn(bool ts) {
     return ts ? reinterpret_cast<const void *>(&gemv_tokens_kernel<NTOK, true>)
               : reinterpret_cast<const void *>(&gemv_tokens_kernel<NTOK, false>);
 }
+template <int NTOK>
+const void *gemv_tokens_multi_fn(bool ts) {
+    return ts ? reinterpret_cast<const void *>(&gemv_tokens_multi_kernel<NTOK, true>)
+              : reinterpret_cast<const void *>(&gemv_tokens_multi_kernel<NTOK, false>);
+}
 }  // namespace
+
+// Chunks of 2 or 3 tokens on rows of 65..768 chunks (groups of 2..12 waves,
+// one chunk a lane), and of 4 tokens on rows of 256..768 chunks.  Each wave
+// loads its own slice of every token's activations, so a token costs more
+// on rows of fewer chunks; measured against the 16-row matrix-core kernel
+// (A/B in one process, us): 2048 x 11008 N = 2 / 3 / 4 7.1 / 8.9 / 10.7
+// against 17.2 / 17.4 / 17.4; 27648 x 5120 N = 2 22.3 against 57.0; 5120 x
+// 5120 N = 2 / 3 8.0 / 16.3 against 17.7 / 17.8; 8192 x 8192 N = 4 17.0
+// against 23.8; 4096 x 4096 N = 2 5.4 against 7.7 -- but N = 4 on rows of
+// 4096 or 5120 weights: 4096 x 4096 8.0 against 7.8, 11008 x 4096 19.6
+// against 19.1, 5120 x 5120 19.6 against 17.8.
+bool gemv_tokens_multi_fits(int64_t M, int64_t K, int64_t N) {
+    const int64_t C = K / kChunkWeights;
+    return N >= 2 && N <= 4 && M >= 1 && C > 64 && C <= 64 * 12 && (N < 4 || C >= 256);
+}
+
+hipError_t launch_gemv_tokens_multi(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                                    const uint16_t *X, int64_t N, float *Y, hipStream_t stream) {
+    if (!gemv_tokens_multi_fits(M, K, N)) return hipErrorInvalidValue;
+    int k = (int)K;
+    const int C = k / kChunkWeights;
+    const int waves = (C + 63) / 64;
+    int P = waves * 64;
+    const int64_t tiles4 = (M + 3) / 4;
+    const int max_waves = N == 2 ? tokens_multi_waves(2) : tokens_multi_waves(3);
+    const OneTileShape sh = multi_shape(tiles4, waves, max_waves);
+    if (sh.G * waves > max_waves) return hipErrorInvalidValue;
+    int64_t grid = (tiles4 + sh.G - 1) / sh.G;
+    if (grid > sh.cap) grid = sh.cap;
+    const int64_t ngroups = grid * sh.G;
+    int64_t rows_q = M / ngroups;
+    int rows_rem = (int)(M % ngroups);
+    const bool ts = scale_runs_aligned(scales, nullptr, k);
+    const void *fn = N == 2 ? gemv_tokens_multi_fn<2>(ts) : N == 3 ? gemv_tokens_multi_fn<3>(ts)
+                                                                   : gemv_tokens_multi_fn<4>(ts);
+    void *args[] = {&codes, &scales, &M, &k, &X, &Y, &P, &rows_q, &rows_rem};
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)(P * sh.G)), args, 0, stream);
+}
 
 hipError_t launch_gemv_tokens(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                               const uint16_t *X, int64_t N, float *Y, hipStream_t stream) {

@@ -14,6 +14,12 @@ hipError_t launch_pack(const float *W, int64_t M, int64_t K, uint8_t *codes, uin
 bool gemv_tokens_fits(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemv_tokens(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                               const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
+// A chunk of 2 or 3 tokens on rows of 65..768 chunks of 32 weights (4
+// tokens: 256..768 chunks): the grouped long-row GEMV with every table
+// lookup serving all tokens.
+bool gemv_tokens_multi_fits(int64_t M, int64_t K, int64_t N);
+hipError_t launch_gemv_tokens_multi(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                                    const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
 // Weight formats of the prefill kernels.
 enum { kGemmNf4 = 0, kGemmAffine = 1, kGemmNvfp4 = 2 };
 

@@ -374,7 +374,8 @@ def test_affine_and_nvfp4_wide_range_activations(env, M, K, kind):
 
 @pytest.mark.parametrize("M,K,N", [(300, 2048, 2), (300, 2048, 3), (3001, 1984, 3), (600, 11008, 1),
                                    (300, 2048, 4), (300, 2048, 17), (3001, 1984, 32), (77, 4160, 17),
-                                   (70, 11008, 32), (300, 2048, 8), (300, 2048, 16), (3001, 1920, 11)])
+                                   (70, 11008, 32), (300, 2048, 8), (300, 2048, 16), (3001, 1920, 11),
+                                   (300, 11008, 2), (77, 4160, 3), (50, 8192, 4)])
 def test_gemm_smalln_wide_range_activations(env, M, K, N):
     """Each token of the chunk takes a different wide-range recipe."""
     torch, q4, dev = env
@@ -647,7 +648,13 @@ GEMM_SHAPES = [(1, 64, 1), (40, 128, 2), (100, 512, 3), (64, 2048, 4), (97, 1024
                # 5..8 tokens on 4-row tiles (two token groups), and 9..16
                # tokens on the same shapes (the 16-row matrix-core kernel)
                (3001, 1920, 8), (12288, 2048, 7), (13, 640, 7), (4099, 1152, 6), (2, 256, 5),
-               (3001, 1920, 16), (12288, 2048, 13), (2, 256, 16)]
+               (3001, 1920, 16), (12288, 2048, 13), (2, 256, 16),
+               # two to four tokens on rows of several waves: the grouped
+               # GEMV with shared lookups (2 and 3 tokens on rows of 65..768
+               # chunks, 4 tokens from 256 chunks), both sides of each limit,
+               # ragged row counts, scale planes without one-load scale runs
+               (64, 8128, 4), (64, 8192, 4), (40, 24576, 3), (40, 24640, 3), (3, 2112, 3),
+               (4099, 4160, 2), (2049, 11008, 3), (1, 11008, 4), (9001, 4096, 2)]
 
 
 @pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
@@ -735,6 +742,84 @@ def test_gemm_smalln_full_size(env):
     for n_tok in (32, 17, 16, 8, 4, 3, 2, 1):
         Y = q4.q4_gemm_smalln(codes, scales, Xd[:n_tok].contiguous()).cpu().numpy()
         _check(Y, Y_ref[:n_tok], S[:n_tok], f"smalln N={n_tok} all {M} rows")
+
+
+@pytest.mark.parametrize("M,K,N", [(2048, 11008, 2), (2049, 11008, 3), (1001, 4160, 3), (77, 24576, 4),
+                                   (300, 8192, 4), (20000, 4096, 2), (5, 2112, 2)])
+def test_gemm_tokens_long_rows_are_the_gemv(env, M, K, N):
+    """Two to four tokens on rows of several waves: every token's row equals
+    q4_gemv of that token bit for bit (the same conversion, products,
+    reduction and cross-wave sum per token), and the oracle within the bound."""
+    torch, q4, dev = env
+    seed = 8200 + M + K + N
+    W = wl.weights(M, K, seed)
+    X = wl.activations(N, K, seed, "swiglu")
+    codes, scales, _ = oracle.pack(W)
+    Y_ref, S = oracle.gemm(codes, scales, M, K, X)
+    c, s = _upload_packed(env, codes, scales)
+    Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+    Y = q4.q4_gemm_smalln(c, s, Xd)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, S, f"gemm tokens M={M} K={K} N={N}")
+    for n in range(N):
+        y = q4.q4_gemv(c, s, Xd[n].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(Y[n], y), f"token {n} of M={M} K={K} N={N} differs from its GEMV"
+
+
+def test_gemm_smalln_full_size_down(env):
+    """The prefill product on the down projection's shape (2048 x 11008):
+    chunks of 32, 8, 4, 3 and 2 tokens (the 16-row kernel on long rows, and
+    the grouped GEMV with shared lookups), every output against the oracle."""
+    torch, q4, dev = env
+    c = wl.CONFIGS["down"]
+    M, K, N = c["M"], c["K"], 32
+    W = wl.weights(M, K, c["seed"])
+    X = wl.activations(N, K, c["seed"], c["x"])
+    codes, scales, st = _gpu_pack(env, W)
+    assert st == 0
+    Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+    c_ref, s_ref, _ = oracle.pack(W, threads=min(16, os.cpu_count() or 1))
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    t = time.time()
+    Y_ref, S = oracle.gemm(c_ref, s_ref, M, K, X)
+    _log(f"down prefill: oracle product of {N} tokens in {time.time() - t:.1f}s")
+    for n_tok in (32, 8, 4, 3, 2):
+        Y = q4.q4_gemm_smalln(codes, scales, Xd[:n_tok].contiguous()).cpu().numpy()
+        _check(Y, Y_ref[:n_tok], S[:n_tok], f"down prefill N={n_tok} all {M} rows")
+
+
+def test_graph_capture_long_row_tokens(env):
+    """The grouped GEMV with shared lookups (2, 3 and 4 tokens on rows of
+    11008 weights) captured in a HIP graph equals eager on every replay."""
+    torch, q4, dev = env
+    M, K = 600, 11008
+    W = wl.weights(M, K, 53)
+    codes, scales, _ = oracle.pack(W)
+    c, s = _upload_packed(env, codes, scales)
+    Xs = [cases.to_dev(wl.activations(n, K, 53 + n, "swiglu").view(np.int16), torch, dev).view(torch.bfloat16)
+          for n in (2, 3, 4)]
+    eager = [q4.q4_gemm_smalln(c, s, X).clone() for X in Xs]
+    outs = [torch.full((X.shape[0], M), float("nan"), device=dev) for X in Xs]
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            for X, Y in zip(Xs, outs):
+                q4.q4_gemm_smalln(c, s, X, Y, stream=st)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for Y in outs:
+            Y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for Y, E in zip(outs, eager):
+            assert torch.equal(Y, E), f"long-row {Y.shape[0]}-token replay {rep} differs from eager"
+        q4.q4_gemm_smalln(c, s, Xs[0])
+        torch.cuda.synchronize()
 
 
 def test_gemm_formats_full_size(env):
