@@ -824,7 +824,8 @@ def main():
         # tiny (256 x 512, 72 KB) stays in cache and is launch-bound: one copy,
         # timed for its microseconds only.
         # prefill_down: the prefill sweep on the down projection's shape
-        # (rows of 11008 weights, the grouped kernels' side of the dispatch).
+        # (rows of 11008 weights), through q4_gemm_smalln_ws with scratch
+        # memory for the K split (allocated once, outside the timed region).
         for sname, cname, ncopies, ntok in (("tiny", "tiny", 1, None), ("down", "down", 50, None),
                                             ("smalln", "smalln", 45, 32), ("gateup", "gateup", 25, None),
                                             ("prefill_down", "down", 50, 32)):
@@ -840,9 +841,13 @@ def main():
                 N = 1
             else:
                 sy = torch.empty((ntok, sc["M"]), dtype=torch.float32, device=dev)
+                sws = q4.gemm_workspace(sc["M"], sc["K"], ntok, dev) if sname == "prefill_down" else None
 
-                def sstep(cd, sl, sx=sx, sy=sy):
-                    q4.q4_gemm_smalln(cd, sl, sx, sy)
+                def sstep(cd, sl, sx=sx, sy=sy, sws=sws):
+                    if sname == "prefill_down":
+                        q4.q4_gemm_smalln_ws(cd, sl, sx, sws, sy)
+                    else:
+                        q4.q4_gemm_smalln(cd, sl, sx, sy)
                 N = ntok
             sg, sw = time_graph(torch, sstep, sreps, args.steps, args.warmup)
             secondary.append(secondary_entry(sname, sc, N, sg, sw))
@@ -858,12 +863,17 @@ def main():
                     sxn = sx[:n].contiguous()
                     syn = torch.empty((n, sc["M"]), dtype=torch.float32, device=dev)
 
-                    def nstep(cd, sl, sxn=sxn, syn=syn):
-                        q4.q4_gemm_smalln(cd, sl, sxn, syn)
+                    def nstep(cd, sl, sxn=sxn, syn=syn, sws=sws):
+                        if sname == "prefill_down":
+                            q4.q4_gemm_smalln_ws(cd, sl, sxn, sws, syn)
+                        else:
+                            q4.q4_gemm_smalln(cd, sl, sxn, syn)
                     ng, nw = time_graph(torch, nstep, sreps, args.steps, args.warmup)
                     secondary.append(secondary_entry(sname, sc, n, ng, nw))
                     del sxn, syn
             del sreps, sx, sy
+            if ntok is not None:
+                del sws
             torch.cuda.empty_cache()
         if "fused" in chosen:
             secondary.extend(fused_secondaries(torch, q4, wl, dev, args.steps, args.warmup))

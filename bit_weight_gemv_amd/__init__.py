@@ -25,6 +25,7 @@ Q4_ERR_SHAPE = 2
 Q4_ERR_ALIGN = 3
 Q4_ERR_OVERLAP = 4
 Q4_ERR_DEVICE = 5
+Q4_ERR_WORKSPACE = 6
 Q4_MAX_K = 131072
 Q4_MAX_N = 32
 Q4_PACK_NONFINITE = 1
@@ -34,7 +35,7 @@ EXPORTED = ("q4_codes_bytes", "q4_scales_bytes", "q4_codebook", "q4_status_strin
             "q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused",
             "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_pack_nvfp4", "q4_gemv_nvfp4",
             "q4_quantize_x8", "q4_gemv_affine_x8", "q4_gemm_smalln_affine", "q4_gemm_smalln_nvfp4",
-            "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4")
+            "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4", "q4_gemm_smalln_ws_bytes", "q4_gemm_smalln_ws")
 
 Q4_OUT_F32 = 0
 Q4_OUT_BF16 = 1
@@ -99,6 +100,10 @@ def lib() -> ctypes.CDLL:
         L.q4_gemv.restype = I32
         L.q4_gemm_smalln.argtypes = [P, P, I64, I64, P, I64, P, P]
         L.q4_gemm_smalln.restype = I32
+        L.q4_gemm_smalln_ws_bytes.argtypes = [I64, I64, I64]
+        L.q4_gemm_smalln_ws_bytes.restype = ctypes.c_size_t
+        L.q4_gemm_smalln_ws.argtypes = [P, P, I64, I64, P, I64, P, P, ctypes.c_size_t, P]
+        L.q4_gemm_smalln_ws.restype = I32
         for name in ("q4_gemv_fused", "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4"):
             getattr(L, name).argtypes = [P, I32, I64, P, I32, P, P, P]
             getattr(L, name).restype = I32
@@ -259,6 +264,36 @@ def q4_gemm_smalln(codes, scales, X, Y=None, stream=None):
     st = lib().q4_gemm_smalln(_ptr(codes), _ptr(scales), M, K, _ptr(X), N, _ptr(Y), _stream(stream))
     if st != Q4_OK:
         raise Q4Error(st, "q4_gemm_smalln")
+    return Y
+
+
+def q4_gemm_smalln_ws_bytes(M: int, K: int, N: int) -> int:
+    """Bytes of scratch q4_gemm_smalln_ws needs for this shape (0: none)."""
+    return int(lib().q4_gemm_smalln_ws_bytes(M, K, N))
+
+
+def gemm_workspace(M: int, K: int, N: int, device):
+    """A uint8 device tensor of q4_gemm_smalln_ws_bytes(M, K, N) bytes, or None
+    where the shape needs none."""
+    n = q4_gemm_smalln_ws_bytes(M, K, N)
+    if n == 0:
+        return None
+    return _torch().empty(n, dtype=_torch().uint8, device=device)
+
+
+def q4_gemm_smalln_ws(codes, scales, X, workspace, Y=None, stream=None):
+    """q4_gemm_smalln with scratch memory (a uint8 device tensor, or None where
+    q4_gemm_smalln_ws_bytes is 0); returns fp32 Y [N, M]."""
+    torch = _torch()
+    M, K = _mk(codes, scales)
+    N, Y = _smalln_out(X, K, M, Y, codes.device)
+    ws, nb = None, 0
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8, codes.device)
+        ws, nb = _ptr(workspace), workspace.numel()
+    st = lib().q4_gemm_smalln_ws(_ptr(codes), _ptr(scales), M, K, _ptr(X), N, _ptr(Y), ws, nb, _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_gemm_smalln_ws")
     return Y
 
 

@@ -62,6 +62,7 @@ const char *q4_status_string(int status) {
         case Q4_ERR_ALIGN: return "Q4_ERR_ALIGN: a pointer is not aligned as required";
         case Q4_ERR_OVERLAP: return "Q4_ERR_OVERLAP: an output range overlaps another range";
         case Q4_ERR_DEVICE: return "Q4_ERR_DEVICE: the HIP runtime refused the launch";
+        case Q4_ERR_WORKSPACE: return "Q4_ERR_WORKSPACE: the scratch memory for partial sums is missing or too small";
         default: return "unknown q4 status";
     }
 }
@@ -217,6 +218,33 @@ int q4_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M, int6
         overlap(ry, range_of(X, (uint64_t)N * K * 2)))
         return Q4_ERR_OVERLAP;
     return launch_status(q4::launch_gemm_smalln(codes, scales, M, K, X, N, Y, (hipStream_t)stream));
+}
+
+size_t q4_gemm_smalln_ws_bytes(int64_t M, int64_t K, int64_t N) {
+    if (!shape_ok(M, K) || M == 0 || N < 1 || N > Q4_MAX_N || !q4::gemm_split_fits(M, K, N)) return 0;
+    return q4::gemm_split_bytes(M, K, N);
+}
+
+int q4_gemm_smalln_ws(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K, const uint16_t *X,
+                      int64_t N, float *Y, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!shape_ok(M, K) || N < 0 || N > Q4_MAX_N) return Q4_ERR_SHAPE;
+    if (M == 0 || N == 0) return Q4_OK;
+    if (!codes || !scales || !X || !Y) return Q4_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(X, 16) || !aligned(Y, 4))
+        return Q4_ERR_ALIGN;
+    const Range ry = range_of(Y, (uint64_t)N * M * 4);
+    const Range rc = range_of(codes, (uint64_t)M * (K / 2)), rs = range_of(scales, (uint64_t)M * (K / 64) * 2),
+                rx = range_of(X, (uint64_t)N * K * 2);
+    if (overlap(ry, rc) || overlap(ry, rs) || overlap(ry, rx)) return Q4_ERR_OVERLAP;
+    const size_t need = q4_gemm_smalln_ws_bytes(M, K, N);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return Q4_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return Q4_ERR_ALIGN;
+        const Range rw = range_of(workspace, need);
+        if (overlap(rw, ry) || overlap(rw, rc) || overlap(rw, rs) || overlap(rw, rx)) return Q4_ERR_OVERLAP;
+    }
+    return launch_status(q4::launch_gemm_smalln_ws(codes, scales, M, K, X, N, Y, static_cast<float *>(workspace),
+                                                   (hipStream_t)stream));
 }
 
 int q4_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M, int64_t K,

@@ -247,7 +247,7 @@ template <int NT, int S, bool XFIXED, int XP, int FMT>
 __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
     const uint8_t *__restrict__ codes, const void *__restrict__ scales, const uint16_t *__restrict__ zeros,
     const float *__restrict__ tscale, int64_t M, int K, const uint16_t *__restrict__ X, int N,
-    float *__restrict__ Y, int64_t tiles_q, int tiles_rem) {
+    float *__restrict__ Y, int64_t tiles_q, int tiles_rem, int kranges, float *__restrict__ part) {
     // One block of LDS with the table at address 0, so a lookup address
     // built by v_perm needs no base added (the 16-bit offset field of a DS
     // instruction cannot hold a base past 64 KB).  Activation staging is
@@ -289,11 +289,20 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
     // Slices per wave: one when the waves cover K (XFIXED: the activations
     // stay in registers), else several, reloaded per unit.
     const int spw = XFIXED ? 1 : (nslices + nw - 1) / nw;
+    // K split in `kranges` ranges of at most kGemmMaxWaves slices (rows
+    // longer than that, activations in registers): workgroup b takes range
+    // b % kranges of row range b / kranges and writes its sums into partial
+    // plane b % kranges of `part` ([kranges][N][M]); a second pass adds the
+    // planes.  With one range the sums go to Y.
+    const int krange = kranges > 1 ? (int)(blockIdx.x % (unsigned)kranges) : 0;
+    const int spr = kranges > 1 ? (nslices + kranges - 1) / kranges : nslices;  // slices per range
+    const int slice0 = krange * spr;
+    const int slice_end = min(nslices, slice0 + spr);
     const int row_bytes = K >> 1;
     // Scale plane: fp16 per 64-block (NF4, affine: also the zero points), or
     // one E4M3 byte per 16-block (NVFP4).
     const int sc_row_bytes = FMT == kGemmNvfp4 ? (K >> 4) : (nsb * 2);
-    const int64_t wg = blockIdx.x;
+    const int64_t wg = kranges > 1 ? (int64_t)(blockIdx.x / (unsigned)kranges) : (int64_t)blockIdx.x;  // row range
     const int64_t t_begin = wg * tiles_q + (wg < tiles_rem ? wg : tiles_rem);
     const int ntiles = (int)tiles_q + (wg < tiles_rem ? 1 : 0);
     const int nunits = ntiles * spw;  // (tile, slice) pairs of this wave
@@ -302,6 +311,8 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
     // NVFP4: the tensor scale multiplies every finished sum (with the
     // activations' inverse power of two).
     const float post = FMT == kGemmNvfp4 ? *tscale : 1.0f;
+    // Where the finished sums go: Y, or this range's partial plane.
+    float *const dst = kranges > 1 ? part + (int64_t)krange * N * M : Y;
 
     const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(X, (uint32_t)N * (uint32_t)K * 2u);
 
@@ -331,9 +342,9 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
     int ld_unit = 0, ld_si = 0;
     auto load_unit = [&](int buf) {
         const bool real = ld_unit < nunits;
-        const int slice = wave + nw * ld_si;
+        const int slice = slice0 + wave + nw * ld_si;
         const int rows = ld_rows < kTileRows ? (int)ld_rows : kTileRows;
-        const bool live = real && slice < nslices;
+        const bool live = real && slice < slice_end;
         const uint32_t sbytes = live ? (uint32_t)(rows * sc_row_bytes) : 0u;
         const int sblk = kSliceBlocks * slice + (lane & 3);
         const int past = (nsb - 1 - sblk) >> 31;  // all ones past the row's end
@@ -371,7 +382,9 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
     // activations, or the barrier before the conversion, is slower.)
     u32x4_t lin[NT * 8];
     u32x4_t raw[NT][kSliceBlocks][2];
-    if (XFIXED) load_x_linear<NT, XP>(xrs, K, nsb, wave, lin);
+    // (A wave past its range's last slice loads zeros: the slice index then
+    // points past the row's end.)
+    if (XFIXED) load_x_linear<NT, XP>(xrs, K, nsb, slice0 + wave < slice_end ? slice0 + wave : nslices, lin);
 #pragma unroll
     for (int s = 0; s <= S; ++s) load_unit(s);
     if constexpr (FMT == kGemmAffine)
@@ -420,7 +433,7 @@ __global__ __launch_bounds__(64 * kGemmMaxWaves) void gemm_smalln_kernel(
 #pragma unroll
                 for (int w = 0; w < nw; ++w) sum += wave_part(w)[t][out_l][out_v];
                 const int64_t m = m0 + (int64_t)t * kTileRows + out_mm;
-                if (m < M) Y[(int64_t)out_n * M + m] = sum;
+                if (m < M) dst[(int64_t)out_n * M + m] = sum;
             }
         }
     };
@@ -610,6 +623,8 @@ const void *smalln_kernel_for(int64_t N) {
     }
 }
 
+static_assert(kSliceBlocks == 4 && kGemmMaxWaves == 8, "split_kranges (q4_internal.h) assumes these");
+
 int device_cus() {
     static int cus[64] = {0};
     int dev = 0;
@@ -639,9 +654,53 @@ hipError_t launch_matrix_core(const uint8_t *codes, const void *scales, const ui
     int tiles_rem = (int)(tiles % grid);
     const int nslices = (int)((K / 64 + kSliceBlocks - 1) / kSliceBlocks);
     int k = (int)K, n = (int)N;
-    void *args[] = {&codes, &scales, &zeros, &tscale, &M, &k, &X, &n, &Y, &tiles_q, &tiles_rem};
+    int kranges = 1;
+    float *part = nullptr;
+    void *args[] = {&codes, &scales, &zeros, &tscale, &M, &k, &X, &n, &Y, &tiles_q, &tiles_rem, &kranges, &part};
     const void *fn = nslices <= kGemmMaxWaves ? smalln_kernel_for<FMT, true>(N) : smalln_kernel_for<FMT, false>(N);
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * kGemmMaxWaves), args, 0, stream);
+}
+
+// Y[i] = part[0][i] + part[1][i] + ... + part[planes - 1][i], in that order.
+__global__ __launch_bounds__(256) void sum_planes_kernel(const float *__restrict__ part, int planes, int64_t n,
+                                                         float *__restrict__ Y) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        float s = part[i];
+        for (int p = 1; p < planes; ++p) s += part[(int64_t)p * n + i];
+        Y[i] = s;
+    }
+}
+
+// Long rows with scratch memory: K in ranges of at most 8 slices (2048
+// weights), so that every workgroup keeps its range's activations in
+// registers across all its tiles instead of restaging each slice per tile;
+// workgroup b takes range b % R of row range b / R (about CUs / R row
+// ranges), writes partial plane b % R of `part`, and a second launch adds
+// the R planes into Y.
+hipError_t launch_matrix_core_split(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                                    const uint16_t *X, int64_t N, float *Y, float *part, hipStream_t stream) {
+    const int64_t tiles = (M + kTileRows - 1) / kTileRows;
+    int kranges = split_kranges(K);
+    int64_t groups = device_cus() / kranges;
+    if (groups < 1) groups = 1;
+    if (groups > tiles) groups = tiles;
+    const int64_t grid = groups * kranges;
+    int64_t tiles_q = tiles / groups;
+    int tiles_rem = (int)(tiles % groups);
+    int k = (int)K, n = (int)N;
+    const uint16_t *zeros = nullptr;
+    const float *tscale = nullptr;
+    void *args[] = {&codes, &scales, &zeros, &tscale, &M, &k, &X, &n, &Y, &tiles_q, &tiles_rem, &kranges, &part};
+    hipError_t e = hipLaunchKernel(smalln_kernel_for<kGemmNf4, true>(N), dim3((unsigned)grid),
+                                   dim3(64 * kGemmMaxWaves), args, 0, stream);
+    if (e != hipSuccess) return e;
+    const int64_t total = N * M;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    hipLaunchKernelGGL(sum_planes_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const float *)part, kranges,
+                       total, Y);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -660,6 +719,12 @@ hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int6
     if (gemv_tokens_fits(M, K, N)) return launch_gemv_tokens(codes, scales, M, K, X, N, Y, stream);
     if (gemv_tokens_multi_fits(M, K, N)) return launch_gemv_tokens_multi(codes, scales, M, K, X, N, Y, stream);
     return launch_matrix_core<kGemmNf4>(codes, scales, nullptr, nullptr, M, K, X, N, Y, stream);
+}
+
+hipError_t launch_gemm_smalln_ws(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                                 const uint16_t *X, int64_t N, float *Y, float *part, hipStream_t stream) {
+    if (!gemm_split_fits(M, K, N)) return launch_gemm_smalln(codes, scales, M, K, X, N, Y, stream);
+    return launch_matrix_core_split(codes, scales, M, K, X, N, Y, part, stream);
 }
 
 hipError_t launch_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,

@@ -1538,21 +1538,6 @@ const void *gemv_tokens_multi_fn(bool ts) {
 }
 }  // namespace
 
-// Chunks of 2 or 3 tokens on rows of 65..768 chunks (groups of 2..12 waves,
-// one chunk a lane), and of 4 tokens on rows of 256..768 chunks.  Each wave
-// loads its own slice of every token's activations, so a token costs more
-// on rows of fewer chunks; measured against the 16-row matrix-core kernel
-// (A/B in one process, us): 2048 x 11008 N = 2 / 3 / 4 7.1 / 8.9 / 10.7
-// against 17.2 / 17.4 / 17.4; 27648 x 5120 N = 2 22.3 against 57.0; 5120 x
-// 5120 N = 2 / 3 8.0 / 16.3 against 17.7 / 17.8; 8192 x 8192 N = 4 17.0
-// against 23.8; 4096 x 4096 N = 2 5.4 against 7.7 -- but N = 4 on rows of
-// 4096 or 5120 weights: 4096 x 4096 8.0 against 7.8, 11008 x 4096 19.6
-// against 19.1, 5120 x 5120 19.6 against 17.8.
-bool gemv_tokens_multi_fits(int64_t M, int64_t K, int64_t N) {
-    const int64_t C = K / kChunkWeights;
-    return N >= 2 && N <= 4 && M >= 1 && C > 64 && C <= 64 * 12 && (N < 4 || C >= 256);
-}
-
 hipError_t launch_gemv_tokens_multi(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                                     const uint16_t *X, int64_t N, float *Y, hipStream_t stream) {
     if (!gemv_tokens_multi_fits(M, K, N)) return hipErrorInvalidValue;

@@ -16,8 +16,20 @@ hipError_t launch_gemv_tokens(const uint8_t *codes, const uint16_t *scales, int6
                               const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
 // A chunk of 2 or 3 tokens on rows of 65..768 chunks of 32 weights (4
 // tokens: 256..768 chunks): the grouped long-row GEMV with every table
-// lookup serving all tokens.
-bool gemv_tokens_multi_fits(int64_t M, int64_t K, int64_t N);
+// lookup serving all tokens.  Each wave loads its own slice of every
+// token's activations, so a token costs more on rows of fewer chunks;
+// measured against the 16-row matrix-core kernel (A/B in one process, us):
+// 2048 x 11008 N = 2 / 3 / 4 7.1 / 8.9 / 10.7 against 17.2 / 17.4 / 17.4;
+// 27648 x 5120 N = 2 22.3 against 57.0; 5120 x 5120 N = 2 / 3 8.0 / 16.3
+// against 17.7 / 17.8; 8192 x 8192 N = 4 17.0 against 23.8; 4096 x 4096
+// N = 2 5.4 against 7.7 -- but N = 4 on rows of 4096 or 5120 weights:
+// 4096 x 4096 8.0 against 7.8, 11008 x 4096 19.6 against 19.1, 5120 x 5120
+// 19.6 against 17.8.  (Host arithmetic only: shared with the host-side
+// checks of the C ABI.)
+inline bool gemv_tokens_multi_fits(int64_t M, int64_t K, int64_t N) {
+    const int64_t C = K / 32;  // 32-weight chunks a row
+    return N >= 2 && N <= 4 && M >= 1 && C > 64 && C <= 64 * 12 && (N < 4 || C >= 256);
+}
 hipError_t launch_gemv_tokens_multi(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                                     const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
 // Weight formats of the prefill kernels.
@@ -76,6 +88,28 @@ hipError_t launch_gemv_fused(int fmt, const FusedOperand *ops, int count, bool s
 
 hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                               const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
+// The prefill product with scratch memory for partial sums: where
+// gemm_split_fits holds (chunks the 16-row kernel takes on rows longer than
+// 2048 weights), K is split in ranges of at most 2048 weights and the
+// partial planes (gemm_split_bytes: ranges x N x M fp32 at `part`) are added
+// by a second launch; elsewhere launch_gemm_smalln.
+// K ranges of the split: the 16-row kernel's slices of 4 64-blocks (256
+// weights), at most 8 a range (one per wave of its workgroup), dealt evenly.
+inline int split_kranges(int64_t K) {
+    const int64_t nslices = (K / 64 + 3) / 4;
+    return (int)((nslices + 7) / 8);
+}
+// The chunks the split serves: those the 16-row kernel takes on rows of more
+// than 8 slices (the 4-row kernel and the shared-lookup GEMV of one wave a
+// row take only rows of up to 2048 weights).
+inline bool gemm_split_fits(int64_t M, int64_t K, int64_t N) {
+    return N >= 2 && N <= 32 && M >= 1 && split_kranges(K) > 1 && !gemv_tokens_multi_fits(M, K, N);
+}
+inline size_t gemm_split_bytes(int64_t M, int64_t K, int64_t N) {
+    return (size_t)split_kranges(K) * (size_t)N * (size_t)M * sizeof(float);
+}
+hipError_t launch_gemm_smalln_ws(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                                 const uint16_t *X, int64_t N, float *Y, float *part, hipStream_t stream);
 // The prefill product of the affine and NVFP4-style formats (N == 1: their
 // GEMV).  Arguments are validated by the caller.
 hipError_t launch_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,

@@ -54,8 +54,10 @@ typedef enum {
     Q4_ERR_ALIGN = 3,     /* a pointer breaks the alignment stated below      */
     Q4_ERR_OVERLAP = 4,   /* an output range overlaps an input or another
                              output range                                     */
-    Q4_ERR_DEVICE = 5     /* the HIP runtime refused the launch (no gfx950
+    Q4_ERR_DEVICE = 5,    /* the HIP runtime refused the launch (no gfx950
                              device current, bad stream, ...)                  */
+    Q4_ERR_WORKSPACE = 6  /* scratch memory for partial sums is missing or
+                             smaller than the call needs                       */
 } q4_status;
 
 /* Largest K the kernels accept (a multiple of 64). */
@@ -146,11 +148,43 @@ int q4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
  * dword-aligned scale plane, at most 12 four-row tiles per compute unit)
  * by one 4-row tile per wave; where those conditions fail, chunks of two
  * or three tokens on such rows by the q4_gemv kernels with each table
- * lookup serving every token; all others by 16-row matrix-core tiles.
+ * lookup serving every token; chunks of two or three tokens on rows of
+ * 2080 .. 24576 weights (four tokens: 8192 .. 24576) likewise by the
+ * q4_gemv kernels for rows spanning several waves (each row of Y is then
+ * bit-identical to q4_gemv of that token); all others by 16-row
+ * matrix-core tiles.
  */
 int q4_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M,
                    int64_t K, const uint16_t *X, int64_t N, float *Y,
                    void *stream);
+
+/*
+ * q4_gemm_smalln_ws -- the product of q4_gemm_smalln (the same passages),
+ * given device scratch memory for partial sums.  On rows longer than 2048
+ * weights, chunks that q4_gemm_smalln runs on 16-row matrix-core tiles
+ * (2..32 tokens, except 2..4 tokens where the q4_gemv kernels take them)
+ * reload and convert every 256-weight slice of X for each tile there.  Here
+ * K is split instead into q4_gemm_smalln_ws_bytes / (4 N M) ranges of at
+ * most 2048 weights: each workgroup keeps its range's activations in
+ * registers across all of its tiles and writes its sums into that range's
+ * partial plane, and a second launch adds the planes in range order (every
+ * call gives the same bits).  Elsewhere the call is q4_gemm_smalln and the
+ * workspace is not touched (it may then be NULL).
+ *   workspace: device memory of at least q4_gemm_smalln_ws_bytes(M, K, N)
+ *     bytes, 16-byte aligned, owned by the caller; nothing in it needs to
+ *     start at any value, and it holds nothing once the call's work ends.
+ *     Calls that may run at the same time need different workspaces.
+ *   workspace_bytes: its size.
+ * Accuracy: as q4_gemm_smalln (the sums of each range are fp32, then fp32
+ * adds across ranges).
+ * Errors: as q4_gemm_smalln; Q4_ERR_WORKSPACE if scratch is needed and the
+ * workspace is NULL or smaller than asked; Q4_ERR_ALIGN for a misaligned
+ * workspace; Q4_ERR_OVERLAP if it overlaps an input or Y.
+ */
+size_t q4_gemm_smalln_ws_bytes(int64_t M, int64_t K, int64_t N);
+int q4_gemm_smalln_ws(const uint8_t *codes, const uint16_t *scales, int64_t M,
+                      int64_t K, const uint16_t *X, int64_t N, float *Y,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Fused decode projections (deep-fold "Decode V2" page, section 6 Linear primitive: one

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
               "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_pack_nvfp4", "q4_gemv_nvfp4",
               "q4_quantize_x8", "q4_gemv_affine_x8", "q4_gemm_smalln_affine", "q4_gemm_smalln_nvfp4",
               "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4", "q4_codebook", "q4_codes_bytes",
-              "q4_scales_bytes", "q4_status_string"):
+              "q4_scales_bytes", "q4_status_string", "q4_gemm_smalln_ws_bytes", "q4_gemm_smalln_ws"):
         assert n in names
 
 
@@ -62,7 +62,7 @@ def test_sizes(q4):
 
 
 def test_status_strings(q4):
-    for s in range(6):
+    for s in range(7):
         assert q4.status_string(s).startswith("Q4_")
     assert "unknown" in q4.status_string(99)
 
@@ -130,6 +130,42 @@ def test_gemm_null_alignment_overlap(q4):
     assert _gemm(q4, A, B, M, K, C + 8, N, D) == q4.Q4_ERR_ALIGN
     assert _gemm(q4, A, B, M, K, C, N, D + 1) == q4.Q4_ERR_ALIGN
     assert _gemm(q4, A, B, M, K, C, N, C + 1020) == q4.Q4_ERR_OVERLAP  # Y over X's last word (X is 1 KB)
+
+
+def _gemm_ws(q4, codes, scales, M, K, X, N, Y, ws, nb):
+    return q4.lib().q4_gemm_smalln_ws(codes, scales, M, K, X, N, Y, ws, nb, None)
+
+
+def test_gemm_ws_bytes(q4):
+    """Scratch is asked for exactly where the long-row split runs: chunks of
+    2..32 tokens on rows longer than 2048 weights, except those the grouped
+    GEMV takes (2 and 3 tokens; 4 tokens from rows of 8192 weights); its
+    size is ranges x N x M fp32 with ranges of at most 2048 weights."""
+    nb = q4.q4_gemm_smalln_ws_bytes
+    assert nb(2048, 11008, 32) == 6 * 32 * 2048 * 4  # 43 slices of 256: 6 ranges
+    assert nb(2048, 11008, 5) == 6 * 5 * 2048 * 4
+    assert nb(5120, 5120, 4) == 3 * 4 * 5120 * 4      # 4 tokens on rows of 5120: the split
+    assert nb(2048, 11008, 4) == 0                    # the grouped GEMV
+    assert nb(2048, 11008, 3) == 0 and nb(2048, 11008, 2) == 0 and nb(2048, 11008, 1) == 0
+    assert nb(11008, 2048, 32) == 0                   # rows of 2048: one range
+    assert nb(1, 2112, 5) == 2 * 5 * 4                # 9 slices: two ranges
+    assert nb(3, 131072, 32) == 64 * 32 * 3 * 4
+    assert nb(0, 11008, 8) == 0 and nb(16, 11008, 33) == 0 and nb(16, 100, 8) == 0
+
+
+def test_gemm_ws_errors(q4):
+    M, K, N = 16, 11008, 8              # codes 88064 B, scales 5504 B, X 176128 B, Y 512 B
+    need = q4.q4_gemm_smalln_ws_bytes(M, K, N)
+    assert need == 6 * N * M * 4
+    E = 0x50000000
+    assert _gemm_ws(q4, A, B, M, K, C, N, D, None, 0) == q4.Q4_ERR_WORKSPACE
+    assert _gemm_ws(q4, A, B, M, K, C, N, D, E, need - 4) == q4.Q4_ERR_WORKSPACE
+    assert _gemm_ws(q4, A, B, M, K, C, N, D, E + 4, need) == q4.Q4_ERR_ALIGN
+    assert _gemm_ws(q4, A, B, M, K, C, N, D, D + 256, need) == q4.Q4_ERR_OVERLAP   # over Y's tail
+    assert _gemm_ws(q4, A, B, M, K, C, N, D, C + 1024, need) == q4.Q4_ERR_OVERLAP  # over X
+    assert _gemm_ws(q4, A, B, M, K, C, 33, D, E, need) == q4.Q4_ERR_SHAPE
+    assert _gemm_ws(q4, A, B, M, K, None, N, D, E, need) == q4.Q4_ERR_NULL
+    assert _gemm_ws(q4, None, None, 0, K, None, N, None, None, 0) == q4.Q4_OK
 
 
 def test_pack_errors(q4):

@@ -787,11 +787,64 @@ def test_gemm_smalln_full_size_down(env):
     for n_tok in (32, 8, 4, 3, 2):
         Y = q4.q4_gemm_smalln(codes, scales, Xd[:n_tok].contiguous()).cpu().numpy()
         _check(Y, Y_ref[:n_tok], S[:n_tok], f"down prefill N={n_tok} all {M} rows")
+    # With scratch memory: K split in six ranges (chunks of 5..32 tokens).
+    for n_tok in (32, 16, 8, 5):
+        ws = q4.gemm_workspace(M, K, n_tok, dev)
+        assert ws is not None
+        Y = q4.q4_gemm_smalln_ws(codes, scales, Xd[:n_tok].contiguous(), ws).cpu().numpy()
+        _check(Y, Y_ref[:n_tok], S[:n_tok], f"down prefill with scratch N={n_tok} all {M} rows")
+
+
+WS_SHAPES = [(2048, 11008, 5), (70, 11008, 32), (4099, 4160, 9), (33, 11008, 16), (1, 2112, 5),
+             (3, 131072, 32), (77, 24576, 17), (5120, 5120, 4), (301, 8256, 12), (2, 4160, 2)]
+
+
+@pytest.mark.parametrize("M,K,N", WS_SHAPES)
+def test_gemm_ws_parity(env, M, K, N):
+    """q4_gemm_smalln_ws: K split in ranges of at most 2048 weights on long
+    rows (or q4_gemm_smalln where no scratch is needed), every output against
+    the oracle; the same bits on a second call into a workspace full of NaN."""
+    torch, q4, dev = env
+    seed = 8800 + M + K + N
+    W = wl.weights(M, K, seed)
+    X = wl.activations(N, K, seed, "unit_rms")
+    codes, scales, _ = oracle.pack(W)
+    Y_ref, S = oracle.gemm(codes, scales, M, K, X)
+    c, s = _upload_packed(env, codes, scales)
+    Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+    ws = q4.gemm_workspace(M, K, N, dev)
+    Y = q4.q4_gemm_smalln_ws(c, s, Xd, ws).clone()
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, S, f"gemm ws M={M} K={K} N={N}")
+    if ws is not None:
+        ws.view(torch.float32)[: ws.numel() // 4].fill_(float("nan"))
+    Y2 = q4.q4_gemm_smalln_ws(c, s, Xd, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2), f"M={M} K={K} N={N}: second call differs"
+    if ws is None:
+        assert torch.equal(Y, q4.q4_gemm_smalln(c, s, Xd)), "no scratch: the call is q4_gemm_smalln"
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 11008, 8), (77, 4160, 17), (20, 24576, 32)])
+def test_gemm_ws_wide_range_activations(env, M, K, N):
+    """The split's ranges each take their own exact or fp16 path per wave."""
+    torch, q4, dev = env
+    seed = 8900 + M + K + N
+    W = _wide_w(wl.weights(M, K, seed))
+    X = np.stack([_wide_x(WIDE_KINDS[(n + seed) % len(WIDE_KINDS)], K, seed + n) for n in range(N)])
+    codes, scales, _ = oracle.pack(W)
+    Y_ref, S = oracle.gemm(codes, scales, M, K, X)
+    c, s = _upload_packed(env, codes, scales)
+    Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+    Y = q4.q4_gemm_smalln_ws(c, s, Xd, q4.gemm_workspace(M, K, N, dev))
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, S, f"gemm ws wide M={M} K={K} N={N}")
 
 
 def test_graph_capture_long_row_tokens(env):
     """The grouped GEMV with shared lookups (2, 3 and 4 tokens on rows of
-    11008 weights) captured in a HIP graph equals eager on every replay."""
+    11008 weights) and the K split with scratch (9 tokens) captured in a HIP
+    graph equal eager on every replay."""
     torch, q4, dev = env
     M, K = 600, 11008
     W = wl.weights(M, K, 53)
@@ -799,8 +852,10 @@ def test_graph_capture_long_row_tokens(env):
     c, s = _upload_packed(env, codes, scales)
     Xs = [cases.to_dev(wl.activations(n, K, 53 + n, "swiglu").view(np.int16), torch, dev).view(torch.bfloat16)
           for n in (2, 3, 4)]
-    eager = [q4.q4_gemm_smalln(c, s, X).clone() for X in Xs]
-    outs = [torch.full((X.shape[0], M), float("nan"), device=dev) for X in Xs]
+    X9 = cases.to_dev(wl.activations(9, K, 59, "swiglu").view(np.int16), torch, dev).view(torch.bfloat16)
+    ws = q4.gemm_workspace(M, K, 9, dev)
+    eager = [q4.q4_gemm_smalln(c, s, X).clone() for X in Xs] + [q4.q4_gemm_smalln_ws(c, s, X9, ws).clone()]
+    outs = [torch.full((X.shape[0], M), float("nan"), device=dev) for X in Xs + [X9]]
     g = torch.cuda.CUDAGraph()
     st = torch.cuda.Stream()
     st.wait_stream(torch.cuda.current_stream())
@@ -809,6 +864,8 @@ def test_graph_capture_long_row_tokens(env):
         with torch.cuda.graph(g, stream=st):
             for X, Y in zip(Xs, outs):
                 q4.q4_gemm_smalln(c, s, X, Y, stream=st)
+            # nine tokens with scratch: the K split and the sum of its planes
+            q4.q4_gemm_smalln_ws(c, s, X9, ws, outs[-1], stream=st)
     torch.cuda.synchronize()
     for rep in range(4):
         for Y in outs:
