@@ -28,6 +28,7 @@ Q4_ERR_DEVICE = 5
 Q4_ERR_WORKSPACE = 6
 Q4_MAX_K = 131072
 Q4_MAX_N = 32
+Q4_NOALLOC_SCRATCH_BYTES = 16 << 20
 Q4_PACK_NONFINITE = 1
 Q4_PACK_OVERFLOW = 2
 
@@ -35,7 +36,8 @@ EXPORTED = ("q4_codes_bytes", "q4_scales_bytes", "q4_codebook", "q4_status_strin
             "q4_pack", "q4_unpack_canonical", "q4_gemv", "q4_gemm_smalln", "q4_gemv_fused",
             "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_pack_nvfp4", "q4_gemv_nvfp4",
             "q4_quantize_x8", "q4_gemv_affine_x8", "q4_gemm_smalln_affine", "q4_gemm_smalln_nvfp4",
-            "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4", "q4_gemm_smalln_ws_bytes", "q4_gemm_smalln_ws")
+            "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4", "q4_gemm_smalln_ws_bytes", "q4_gemm_smalln_ws",
+            "q4_gemm_smalln_noalloc")
 
 Q4_OUT_F32 = 0
 Q4_OUT_BF16 = 1
@@ -104,6 +106,8 @@ def lib() -> ctypes.CDLL:
         L.q4_gemm_smalln_ws_bytes.restype = ctypes.c_size_t
         L.q4_gemm_smalln_ws.argtypes = [P, P, I64, I64, P, I64, P, P, ctypes.c_size_t, P]
         L.q4_gemm_smalln_ws.restype = I32
+        L.q4_gemm_smalln_noalloc.argtypes = [P, P, I64, I64, P, I64, P, P]
+        L.q4_gemm_smalln_noalloc.restype = I32
         for name in ("q4_gemv_fused", "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4"):
             getattr(L, name).argtypes = [P, I32, I64, P, I32, P, P, P]
             getattr(L, name).restype = I32
@@ -294,6 +298,18 @@ def q4_gemm_smalln_ws(codes, scales, X, workspace, Y=None, stream=None):
     st = lib().q4_gemm_smalln_ws(_ptr(codes), _ptr(scales), M, K, _ptr(X), N, _ptr(Y), ws, nb, _stream(stream))
     if st != Q4_OK:
         raise Q4Error(st, "q4_gemm_smalln_ws")
+    return Y
+
+
+def q4_gemm_smalln_noalloc(codes, scales, X, Y=None, stream=None):
+    """q4_gemm_smalln_ws with the library's fixed device scratch
+    (Q4_NOALLOC_SCRATCH_BYTES per device; calls on one device must not
+    overlap in time); returns fp32 Y [N, M]."""
+    M, K = _mk(codes, scales)
+    N, Y = _smalln_out(X, K, M, Y, codes.device)
+    st = lib().q4_gemm_smalln_noalloc(_ptr(codes), _ptr(scales), M, K, _ptr(X), N, _ptr(Y), _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_gemm_smalln_noalloc")
     return Y
 
 

@@ -247,6 +247,23 @@ int q4_gemm_smalln_ws(const uint8_t *codes, const uint16_t *scales, int64_t M, i
                                                    (hipStream_t)stream));
 }
 
+int q4_gemm_smalln_noalloc(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K, const uint16_t *X,
+                           int64_t N, float *Y, void *stream) {
+    static_assert(q4::kNoallocScratchBytes == Q4_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+    if (!shape_ok(M, K) || N < 0 || N > Q4_MAX_N) return Q4_ERR_SHAPE;
+    if (M == 0 || N == 0) return Q4_OK;
+    if (!codes || !scales || !X || !Y) return Q4_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(X, 16) || !aligned(Y, 4))
+        return Q4_ERR_ALIGN;
+    const Range ry = range_of(Y, (uint64_t)N * M * 4);
+    if (overlap(ry, range_of(codes, (uint64_t)M * (K / 2))) ||
+        overlap(ry, range_of(scales, (uint64_t)M * (K / 64) * 2)) ||
+        overlap(ry, range_of(X, (uint64_t)N * K * 2)))
+        return Q4_ERR_OVERLAP;
+    if (q4_gemm_smalln_ws_bytes(M, K, N) > Q4_NOALLOC_SCRATCH_BYTES) return Q4_ERR_WORKSPACE;
+    return launch_status(q4::launch_gemm_smalln_noalloc(codes, scales, M, K, X, N, Y, (hipStream_t)stream));
+}
+
 int q4_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M, int64_t K,
                           const uint16_t *X, int64_t N, float *Y, void *stream) {
     if (!shape_ok(M, K) || N < 0 || N > Q4_MAX_N) return Q4_ERR_SHAPE;

@@ -48,6 +48,7 @@
 //    with a ring of prefetched tiles (codes and scales of tile t+1 .. t+S are
 //    in flight while tile t is multiplied).  Per tile the waves' partial
 //    tiles are summed through LDS.
+#include <mutex>
 #include <type_traits>
 
 #include "q4_device.h"
@@ -719,6 +720,48 @@ hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int6
     if (gemv_tokens_fits(M, K, N)) return launch_gemv_tokens(codes, scales, M, K, X, N, Y, stream);
     if (gemv_tokens_multi_fits(M, K, N)) return launch_gemv_tokens_multi(codes, scales, M, K, X, N, Y, stream);
     return launch_matrix_core<kGemmNf4>(codes, scales, nullptr, nullptr, M, K, X, N, Y, stream);
+}
+
+// The library's own scratch for q4_gemm_smalln_noalloc (callers that cannot
+// allocate): partial planes of the long-row split, kNoallocScratchBytes on
+// each device the library runs on, held until the process ends.  Its name
+// is a host-side stand-in: host code uses only the device address that
+// hipGetSymbolAddress returns for it (noalloc_scratch below).
+static __device__ __align__(256) float scratch[kNoallocScratchBytes / sizeof(float)];
+
+namespace {
+// Device address of `scratch` on each device, looked up on the first call
+// made with that device current.
+constexpr int kMaxDevices = 64;
+void *g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+hipError_t noalloc_scratch(float **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<float *>(g_scratch_ptr[dev]);
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_gemm_smalln_noalloc(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                                      const uint16_t *X, int64_t N, float *Y, hipStream_t stream) {
+    if (!gemm_split_fits(M, K, N)) return launch_gemm_smalln(codes, scales, M, K, X, N, Y, stream);
+    if (gemm_split_bytes(M, K, N) > kNoallocScratchBytes) return hipErrorInvalidValue;
+    float *part = nullptr;
+    const hipError_t e = noalloc_scratch(&part);
+    if (e != hipSuccess) return e;
+    return launch_matrix_core_split(codes, scales, M, K, X, N, Y, part, stream);
 }
 
 hipError_t launch_gemm_smalln_ws(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,

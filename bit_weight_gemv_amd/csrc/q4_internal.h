@@ -110,6 +110,12 @@ inline size_t gemm_split_bytes(int64_t M, int64_t K, int64_t N) {
 }
 hipError_t launch_gemm_smalln_ws(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                                  const uint16_t *X, int64_t N, float *Y, float *part, hipStream_t stream);
+// The same with the library's fixed device scratch (q4_gemm_smalln_noalloc):
+// kNoallocScratchBytes per device; the caller checks gemm_split_bytes
+// against it first.
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+hipError_t launch_gemm_smalln_noalloc(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                                      const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
 // The prefill product of the affine and NVFP4-style formats (N == 1: their
 // GEMV).  Arguments are validated by the caller.
 hipError_t launch_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,

@@ -187,6 +187,25 @@ int q4_gemm_smalln_ws(const uint8_t *codes, const uint16_t *scales, int64_t M,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * q4_gemm_smalln_noalloc -- q4_gemm_smalln_ws for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the partial planes go to a
+ * scratch array of Q4_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * device it runs on from its first use until the process ends.  The call
+ * allocates nothing.  Every call on one device shares that device's array
+ * (which keeps the last call's contents; no call depends on them), so calls
+ * that may overlap in time on one device race and must be ordered by the
+ * caller (one stream, or events).
+ * Errors: as q4_gemm_smalln; Q4_ERR_WORKSPACE (nothing launched) where
+ * q4_gemm_smalln_ws_bytes(M, K, N) exceeds Q4_NOALLOC_SCRATCH_BYTES;
+ * Q4_ERR_DEVICE if the array's device address cannot be found.
+ */
+#define Q4_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int q4_gemm_smalln_noalloc(const uint8_t *codes, const uint16_t *scales,
+                           int64_t M, int64_t K, const uint16_t *X, int64_t N,
+                           float *Y, void *stream);
+
+/*
  * Fused decode projections (deep-fold "Decode V2" page, section 6 Linear primitive: one
  * grid over the q, k and v rows sharing x with the q/k/v bias added in that
  * kernel; gate/up pairs writing silu(g) * u, SiLU only after the full

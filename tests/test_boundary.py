@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
               "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_pack_nvfp4", "q4_gemv_nvfp4",
               "q4_quantize_x8", "q4_gemv_affine_x8", "q4_gemm_smalln_affine", "q4_gemm_smalln_nvfp4",
               "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4", "q4_codebook", "q4_codes_bytes",
-              "q4_scales_bytes", "q4_status_string", "q4_gemm_smalln_ws_bytes", "q4_gemm_smalln_ws"):
+              "q4_scales_bytes", "q4_status_string", "q4_gemm_smalln_ws_bytes", "q4_gemm_smalln_ws",
+              "q4_gemm_smalln_noalloc"):
         assert n in names
 
 
@@ -166,6 +167,23 @@ def test_gemm_ws_errors(q4):
     assert _gemm_ws(q4, A, B, M, K, C, 33, D, E, need) == q4.Q4_ERR_SHAPE
     assert _gemm_ws(q4, A, B, M, K, None, N, D, E, need) == q4.Q4_ERR_NULL
     assert _gemm_ws(q4, None, None, 0, K, None, N, None, None, 0) == q4.Q4_OK
+
+
+def test_gemm_noalloc_host_checks(q4):
+    """The allocation-free entry point refuses, before any launch or device
+    lookup, chunks whose partial sums exceed its fixed scratch, and the
+    usual bad arguments."""
+    L = q4.lib()
+    M, K, N = 151936, 4096, 32       # two K ranges: 2 x 32 x 151936 x 4 bytes
+    assert q4.q4_gemm_smalln_ws_bytes(M, K, N) > q4.Q4_NOALLOC_SCRATCH_BYTES
+    big_codes, big_scales, big_x, big_y = 0x100000000, 0x200000000, 0x300000000, 0x400000000
+    assert L.q4_gemm_smalln_noalloc(big_codes, big_scales, M, K, big_x, N, big_y, None) == q4.Q4_ERR_WORKSPACE
+    assert q4.q4_gemm_smalln_ws_bytes(2048, 11008, 32) <= q4.Q4_NOALLOC_SCRATCH_BYTES
+    assert L.q4_gemm_smalln_noalloc(A, B, 16, 11008, C, 33, D, None) == q4.Q4_ERR_SHAPE
+    assert L.q4_gemm_smalln_noalloc(A, B, 16, 11008, None, 8, D, None) == q4.Q4_ERR_NULL
+    assert L.q4_gemm_smalln_noalloc(A, B, 16, 11008, C + 8, 8, D, None) == q4.Q4_ERR_ALIGN
+    assert L.q4_gemm_smalln_noalloc(A, B, 16, 11008, C, 8, C + 256, None) == q4.Q4_ERR_OVERLAP
+    assert L.q4_gemm_smalln_noalloc(None, None, 0, 11008, None, 8, None, None) == q4.Q4_OK
 
 
 def test_pack_errors(q4):

@@ -129,6 +129,9 @@ need = L.q4_gemm_smalln_ws_bytes(100, 11008, 9)
 assert need == 6 * 9 * 100 * 4, need
 assert L.q4_gemm_smalln_ws(A, B, 100, 11008, C, 9, D, E, need, None) == 0 and last() == "gemm_smalln_ws M=100 K=11008 N=9", last()
 assert L.q4_gemm_smalln_ws(A, B, 100, 11008, C, 9, D, E, need - 1, None) == 6
+L.q4_gemm_smalln_noalloc.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int64] * 2 + [ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 2
+assert L.q4_gemm_smalln_noalloc(A, B, 100, 11008, C, 9, D, None) == 0 and last() == "gemm_smalln_noalloc M=100 K=11008 N=9", last()
+assert L.q4_gemm_smalln_noalloc(1 << 32, 2 << 32, 100000, 4096, 3 << 32, 32, 4 << 32, None) == 6  # never dereferenced
 assert L.q4_pack(A, 8, 128, B, C, D, None) == 0 and last() == "pack M=8 K=128", last()
 assert L.q4_gemv_affine(A, B, C, 9, 192, D, E, None) == 0 and last() == "gemv_affine M=9 K=192", last()
 assert L.q4_gemv_nvfp4(A, B, C, 9, 192, D, E, None) == 0 and last() == "gemv_nvfp4 M=9 K=192", last()
@@ -144,7 +147,7 @@ assert last() == "gemv_fused_affine count=1 K=2048 rows=64", last()
 nops = (q4.OperandNvfp4 * 2)(q4.OperandNvfp4(A, B, C, 64, None), q4.OperandNvfp4(D, base + 7 * (1 << 19), C, 64, None))
 assert L.q4_gemv_fused_nvfp4(nops, 2, 2048, base + 6 * (1 << 19), 1, ys, None, None) == 0, last()
 assert last() == "gemv_fused_nvfp4 swiglu count=2 K=2048 rows=128", last()
-assert L.q4stub_calls() == n0 + 11, L.q4stub_calls() - n0
+assert L.q4stub_calls() == n0 + 12, L.q4stub_calls() - n0
 print("launch stand-ins reached:", L.q4stub_calls() - n0)
 """
 
@@ -170,4 +173,4 @@ def test_c_abi_host_layer_under_asan_ubsan(tmp_path):
     out = r.stdout + r.stderr
     assert "Sanitizer" not in out and "runtime error" not in out, out[-4000:]
     assert r.returncode == 0, out[-4000:]
-    assert "launch stand-ins reached: 11" in out, out[-2000:]
+    assert "launch stand-ins reached: 12" in out, out[-2000:]
