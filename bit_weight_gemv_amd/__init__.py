@@ -37,7 +37,8 @@ EXPORTED = ("q4_codes_bytes", "q4_scales_bytes", "q4_codebook", "q4_status_strin
             "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_pack_nvfp4", "q4_gemv_nvfp4",
             "q4_quantize_x8", "q4_gemv_affine_x8", "q4_gemm_smalln_affine", "q4_gemm_smalln_nvfp4",
             "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4", "q4_gemm_smalln_ws_bytes", "q4_gemm_smalln_ws",
-            "q4_gemm_smalln_noalloc")
+            "q4_gemm_smalln_noalloc", "q4_gemm_smalln_formats_ws_bytes", "q4_gemm_smalln_affine_ws",
+            "q4_gemm_smalln_nvfp4_ws")
 
 Q4_OUT_F32 = 0
 Q4_OUT_BF16 = 1
@@ -108,6 +109,11 @@ def lib() -> ctypes.CDLL:
         L.q4_gemm_smalln_ws.restype = I32
         L.q4_gemm_smalln_noalloc.argtypes = [P, P, I64, I64, P, I64, P, P]
         L.q4_gemm_smalln_noalloc.restype = I32
+        L.q4_gemm_smalln_formats_ws_bytes.argtypes = [I64, I64, I64]
+        L.q4_gemm_smalln_formats_ws_bytes.restype = ctypes.c_size_t
+        for name in ("q4_gemm_smalln_affine_ws", "q4_gemm_smalln_nvfp4_ws"):
+            getattr(L, name).argtypes = [P, P, P, I64, I64, P, I64, P, P, ctypes.c_size_t, P]
+            getattr(L, name).restype = I32
         for name in ("q4_gemv_fused", "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4"):
             getattr(L, name).argtypes = [P, I32, I64, P, I32, P, P, P]
             getattr(L, name).restype = I32
@@ -298,6 +304,42 @@ def q4_gemm_smalln_ws(codes, scales, X, workspace, Y=None, stream=None):
     st = lib().q4_gemm_smalln_ws(_ptr(codes), _ptr(scales), M, K, _ptr(X), N, _ptr(Y), ws, nb, _stream(stream))
     if st != Q4_OK:
         raise Q4Error(st, "q4_gemm_smalln_ws")
+    return Y
+
+
+def q4_gemm_smalln_formats_ws_bytes(M: int, K: int, N: int) -> int:
+    """Bytes of scratch the affine and NVFP4-style *_ws products need (0: none)."""
+    return int(lib().q4_gemm_smalln_formats_ws_bytes(M, K, N))
+
+
+def formats_workspace(M: int, K: int, N: int, device):
+    """A uint8 device tensor for q4_gemm_smalln_affine_ws / _nvfp4_ws, or None."""
+    n = q4_gemm_smalln_formats_ws_bytes(M, K, N)
+    if n == 0:
+        return None
+    return _torch().empty(n, dtype=_torch().uint8, device=device)
+
+
+def _ws_args(workspace, device):
+    if workspace is None:
+        return None, 0
+    _check(workspace, "workspace", _torch().uint8, device)
+    return _ptr(workspace), workspace.numel()
+
+
+def q4_gemm_smalln_affine_ws(codes, scales, zeros, X, workspace, Y=None, stream=None):
+    """q4_gemm_smalln_affine with scratch for the long-row K split."""
+    torch = _torch()
+    M, K = _mk(codes, scales)
+    _check(zeros, "zeros", torch.float16, codes.device)
+    if tuple(zeros.shape) != tuple(scales.shape):
+        raise ValueError("zeros must have the shape of scales")
+    N, Y = _smalln_out(X, K, M, Y, codes.device)
+    ws, nb = _ws_args(workspace, codes.device)
+    st = lib().q4_gemm_smalln_affine_ws(_ptr(codes), _ptr(scales), _ptr(zeros), M, K, _ptr(X), N, _ptr(Y), ws, nb,
+                                        _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_gemm_smalln_affine_ws")
     return Y
 
 
@@ -589,6 +631,27 @@ def q4_gemm_smalln_nvfp4(codes, scales, tscale, X, Y=None, stream=None):
                                     _stream(stream))
     if st != Q4_OK:
         raise Q4Error(st, "q4_gemm_smalln_nvfp4")
+    return Y
+
+
+def q4_gemm_smalln_nvfp4_ws(codes, scales, tscale, X, workspace, Y=None, stream=None):
+    """q4_gemm_smalln_nvfp4 with scratch for the long-row K split."""
+    torch = _torch()
+    dev = codes.device
+    if codes.dim() != 2 or scales.dim() != 2:
+        raise ValueError("codes must be [M, K/2] and scales [M, K/16]")
+    M, K = codes.shape[0], codes.shape[1] * 2
+    if scales.shape[0] != M or scales.shape[1] * 16 != K:
+        raise ValueError("codes and scales disagree on M, K")
+    _check(codes, "codes", torch.uint8, dev)
+    _check(scales, "scales", torch.uint8, dev)
+    _check(tscale, "tscale", torch.float32, dev)
+    N, Y = _smalln_out(X, K, M, Y, dev)
+    ws, nb = _ws_args(workspace, dev)
+    st = lib().q4_gemm_smalln_nvfp4_ws(_ptr(codes), _ptr(scales), _ptr(tscale), M, K, _ptr(X), N, _ptr(Y), ws, nb,
+                                       _stream(stream))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_gemm_smalln_nvfp4_ws")
     return Y
 
 

@@ -279,6 +279,67 @@ int q4_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scales, const ui
     return launch_status(q4::launch_gemm_smalln_affine(codes, scales, zeros, M, K, X, N, Y, (hipStream_t)stream));
 }
 
+size_t q4_gemm_smalln_formats_ws_bytes(int64_t M, int64_t K, int64_t N) {
+    if (!shape_ok(M, K) || M == 0 || N < 1 || N > Q4_MAX_N || !q4::gemm_split_fits_formats(M, K, N)) return 0;
+    return q4::gemm_split_bytes(M, K, N);
+}
+
+namespace {
+// The workspace checks shared by the two formats' entry points: `in` holds
+// the inputs' ranges (Y's overlap with them is checked by the caller).
+int formats_ws_check(int64_t M, int64_t K, int64_t N, Range ry, const Range *in, int nin, void *workspace,
+                     size_t workspace_bytes) {
+    const size_t need = q4_gemm_smalln_formats_ws_bytes(M, K, N);
+    if (need == 0) return Q4_OK;
+    if (!workspace || workspace_bytes < need) return Q4_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return Q4_ERR_ALIGN;
+    const Range rw = range_of(workspace, need);
+    if (overlap(rw, ry)) return Q4_ERR_OVERLAP;
+    for (int i = 0; i < nin; ++i)
+        if (overlap(rw, in[i])) return Q4_ERR_OVERLAP;
+    return Q4_OK;
+}
+}  // namespace
+
+int q4_gemm_smalln_affine_ws(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,
+                             int64_t K, const uint16_t *X, int64_t N, float *Y, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    if (!shape_ok(M, K) || N < 0 || N > Q4_MAX_N) return Q4_ERR_SHAPE;
+    if (M == 0 || N == 0) return Q4_OK;
+    if (!codes || !scales || !zeros || !X || !Y) return Q4_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2) || !aligned(X, 16) || !aligned(Y, 4))
+        return Q4_ERR_ALIGN;
+    const Range ry = range_of(Y, (uint64_t)N * M * 4);
+    const uint64_t sb = (uint64_t)M * (K / 64) * 2;
+    const Range in[4] = {range_of(codes, (uint64_t)M * (K / 2)), range_of(scales, sb), range_of(zeros, sb),
+                         range_of(X, (uint64_t)N * K * 2)};
+    for (const Range &r : in)
+        if (overlap(ry, r)) return Q4_ERR_OVERLAP;
+    const int st = formats_ws_check(M, K, N, ry, in, 4, workspace, workspace_bytes);
+    if (st != Q4_OK) return st;
+    return launch_status(q4::launch_gemm_smalln_affine_ws(codes, scales, zeros, M, K, X, N, Y,
+                                                          static_cast<float *>(workspace), (hipStream_t)stream));
+}
+
+int q4_gemm_smalln_nvfp4_ws(const uint8_t *codes, const uint8_t *scales, const float *tscale, int64_t M, int64_t K,
+                            const uint16_t *X, int64_t N, float *Y, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    if (!shape_ok(M, K) || N < 0 || N > Q4_MAX_N) return Q4_ERR_SHAPE;
+    if (M == 0 || N == 0) return Q4_OK;
+    if (!codes || !scales || !tscale || !X || !Y) return Q4_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(tscale, 4) || !aligned(X, 16) || !aligned(Y, 4))
+        return Q4_ERR_ALIGN;
+    const Range ry = range_of(Y, (uint64_t)N * M * 4);
+    const Range in[4] = {range_of(codes, (uint64_t)M * (K / 2)), range_of(scales, (uint64_t)M * (K / 16)),
+                         range_of(tscale, 4), range_of(X, (uint64_t)N * K * 2)};
+    for (const Range &r : in)
+        if (overlap(ry, r)) return Q4_ERR_OVERLAP;
+    const int st = formats_ws_check(M, K, N, ry, in, 4, workspace, workspace_bytes);
+    if (st != Q4_OK) return st;
+    return launch_status(q4::launch_gemm_smalln_nvfp4_ws(codes, scales, tscale, M, K, X, N, Y,
+                                                         static_cast<float *>(workspace), (hipStream_t)stream));
+}
+
 int q4_gemm_smalln_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscale, int64_t M, int64_t K,
                          const uint16_t *X, int64_t N, float *Y, void *stream) {
     if (!shape_ok(M, K) || N < 0 || N > Q4_MAX_N) return Q4_ERR_SHAPE;

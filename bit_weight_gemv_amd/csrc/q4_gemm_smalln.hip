@@ -679,8 +679,10 @@ __global__ __launch_bounds__(256) void sum_planes_kernel(const float *__restrict
 // workgroup b takes range b % R of row range b / R (about CUs / R row
 // ranges), writes partial plane b % R of `part`, and a second launch adds
 // the R planes into Y.
-hipError_t launch_matrix_core_split(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
-                                    const uint16_t *X, int64_t N, float *Y, float *part, hipStream_t stream) {
+template <int FMT>
+hipError_t launch_matrix_core_split(const uint8_t *codes, const void *scales, const uint16_t *zeros,
+                                    const float *tscale, int64_t M, int64_t K, const uint16_t *X, int64_t N,
+                                    float *Y, float *part, hipStream_t stream) {
     const int64_t tiles = (M + kTileRows - 1) / kTileRows;
     int kranges = split_kranges(K);
     int64_t groups = device_cus() / kranges;
@@ -690,10 +692,8 @@ hipError_t launch_matrix_core_split(const uint8_t *codes, const uint16_t *scales
     int64_t tiles_q = tiles / groups;
     int tiles_rem = (int)(tiles % groups);
     int k = (int)K, n = (int)N;
-    const uint16_t *zeros = nullptr;
-    const float *tscale = nullptr;
     void *args[] = {&codes, &scales, &zeros, &tscale, &M, &k, &X, &n, &Y, &tiles_q, &tiles_rem, &kranges, &part};
-    hipError_t e = hipLaunchKernel(smalln_kernel_for<kGemmNf4, true>(N), dim3((unsigned)grid),
+    hipError_t e = hipLaunchKernel(smalln_kernel_for<FMT, true>(N), dim3((unsigned)grid),
                                    dim3(64 * kGemmMaxWaves), args, 0, stream);
     if (e != hipSuccess) return e;
     const int64_t total = N * M;
@@ -761,13 +761,29 @@ hipError_t launch_gemm_smalln_noalloc(const uint8_t *codes, const uint16_t *scal
     float *part = nullptr;
     const hipError_t e = noalloc_scratch(&part);
     if (e != hipSuccess) return e;
-    return launch_matrix_core_split(codes, scales, M, K, X, N, Y, part, stream);
+    return launch_matrix_core_split<kGemmNf4>(codes, scales, nullptr, nullptr, M, K, X, N, Y, part, stream);
 }
 
 hipError_t launch_gemm_smalln_ws(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                                  const uint16_t *X, int64_t N, float *Y, float *part, hipStream_t stream) {
     if (!gemm_split_fits(M, K, N)) return launch_gemm_smalln(codes, scales, M, K, X, N, Y, stream);
-    return launch_matrix_core_split(codes, scales, M, K, X, N, Y, part, stream);
+    return launch_matrix_core_split<kGemmNf4>(codes, scales, nullptr, nullptr, M, K, X, N, Y, part, stream);
+}
+
+hipError_t launch_gemm_smalln_affine_ws(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros,
+                                        int64_t M, int64_t K, const uint16_t *X, int64_t N, float *Y, float *part,
+                                        hipStream_t stream) {
+    if (!gemm_split_fits_formats(M, K, N))
+        return launch_gemm_smalln_affine(codes, scales, zeros, M, K, X, N, Y, stream);
+    return launch_matrix_core_split<kGemmAffine>(codes, scales, zeros, nullptr, M, K, X, N, Y, part, stream);
+}
+
+hipError_t launch_gemm_smalln_nvfp4_ws(const uint8_t *codes, const uint8_t *scales, const float *tscale, int64_t M,
+                                       int64_t K, const uint16_t *X, int64_t N, float *Y, float *part,
+                                       hipStream_t stream) {
+    if (!gemm_split_fits_formats(M, K, N))
+        return launch_gemm_smalln_nvfp4(codes, scales, tscale, M, K, X, N, Y, stream);
+    return launch_matrix_core_split<kGemmNvfp4>(codes, scales, nullptr, tscale, M, K, X, N, Y, part, stream);
 }
 
 hipError_t launch_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t M,

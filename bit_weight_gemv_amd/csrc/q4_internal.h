@@ -105,6 +105,11 @@ inline int split_kranges(int64_t K) {
 inline bool gemm_split_fits(int64_t M, int64_t K, int64_t N) {
     return N >= 2 && N <= 32 && M >= 1 && split_kranges(K) > 1 && !gemv_tokens_multi_fits(M, K, N);
 }
+// The affine and NVFP4-style prefill products have no grouped-GEMV path for
+// a few tokens: the split serves every chunk of 2..32 tokens on long rows.
+inline bool gemm_split_fits_formats(int64_t M, int64_t K, int64_t N) {
+    return N >= 2 && N <= 32 && M >= 1 && split_kranges(K) > 1;
+}
 inline size_t gemm_split_bytes(int64_t M, int64_t K, int64_t N) {
     return (size_t)split_kranges(K) * (size_t)N * (size_t)M * sizeof(float);
 }
@@ -114,6 +119,12 @@ hipError_t launch_gemm_smalln_ws(const uint8_t *codes, const uint16_t *scales, i
 // kNoallocScratchBytes per device; the caller checks gemm_split_bytes
 // against it first.
 constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+hipError_t launch_gemm_smalln_affine_ws(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros,
+                                        int64_t M, int64_t K, const uint16_t *X, int64_t N, float *Y, float *part,
+                                        hipStream_t stream);
+hipError_t launch_gemm_smalln_nvfp4_ws(const uint8_t *codes, const uint8_t *scales, const float *tscale, int64_t M,
+                                       int64_t K, const uint16_t *X, int64_t N, float *Y, float *part,
+                                       hipStream_t stream);
 hipError_t launch_gemm_smalln_noalloc(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
                                       const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
 // The prefill product of the affine and NVFP4-style formats (N == 1: their

@@ -434,6 +434,31 @@ int q4_gemm_smalln_nvfp4(const uint8_t *codes, const uint8_t *scales,
                          void *stream);
 
 /*
+ * q4_gemm_smalln_affine_ws, q4_gemm_smalln_nvfp4_ws -- the prefill products
+ * of the two extra formats (the same passages as q4_gemm_smalln_affine and
+ * q4_gemm_smalln_nvfp4) with scratch for partial sums, as q4_gemm_smalln_ws
+ * is for the NF4 codebook format: on rows longer than 2048 weights, chunks
+ * of 2..32 tokens split K into ranges of at most 2048 weights whose partial
+ * planes a second launch adds in range order.  Elsewhere the call is the
+ * format's q4_gemm_smalln_* entry point (the workspace may then be NULL).
+ *   workspace: at least q4_gemm_smalln_formats_ws_bytes(M, K, N) bytes of
+ *     device memory, 16-byte aligned, as for q4_gemm_smalln_ws.
+ * Errors: as the format's q4_gemm_smalln_* entry point, and those of
+ * q4_gemm_smalln_ws for the workspace.
+ */
+size_t q4_gemm_smalln_formats_ws_bytes(int64_t M, int64_t K, int64_t N);
+int q4_gemm_smalln_affine_ws(const uint8_t *codes, const uint16_t *scales,
+                             const uint16_t *zeros, int64_t M, int64_t K,
+                             const uint16_t *X, int64_t N, float *Y,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
+int q4_gemm_smalln_nvfp4_ws(const uint8_t *codes, const uint8_t *scales,
+                            const float *tscale, int64_t M, int64_t K,
+                            const uint16_t *X, int64_t N, float *Y,
+                            void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/*
  * Packed row gather (deep-fold "Decode V2" page, run notes of section 6: the
  * embedding is kept as packed rows and the rows a step needs are dequantised
  * into its arena, with no dense vocabulary table; a tied embedding shares

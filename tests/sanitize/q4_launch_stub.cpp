@@ -84,6 +84,14 @@ hipError_t launch_gemm_smalln_ws(const uint8_t *, const uint16_t *, int64_t M, i
                                  int64_t N, float *, float *, hipStream_t) {
     return note("gemm_smalln_ws M=%lld K=%lld N=%lld", M, K, N);
 }
+hipError_t launch_gemm_smalln_affine_ws(const uint8_t *, const uint16_t *, const uint16_t *, int64_t M, int64_t K,
+                                        const uint16_t *, int64_t N, float *, float *, hipStream_t) {
+    return note("gemm_smalln_affine_ws M=%lld K=%lld N=%lld", M, K, N);
+}
+hipError_t launch_gemm_smalln_nvfp4_ws(const uint8_t *, const uint8_t *, const float *, int64_t M, int64_t K,
+                                       const uint16_t *, int64_t N, float *, float *, hipStream_t) {
+    return note("gemm_smalln_nvfp4_ws M=%lld K=%lld N=%lld", M, K, N);
+}
 hipError_t launch_gemm_smalln_noalloc(const uint8_t *, const uint16_t *, int64_t M, int64_t K, const uint16_t *,
                                       int64_t N, float *, hipStream_t) {
     return note("gemm_smalln_noalloc M=%lld K=%lld N=%lld", M, K, N);

@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
               "q4_quantize_x8", "q4_gemv_affine_x8", "q4_gemm_smalln_affine", "q4_gemm_smalln_nvfp4",
               "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4", "q4_codebook", "q4_codes_bytes",
               "q4_scales_bytes", "q4_status_string", "q4_gemm_smalln_ws_bytes", "q4_gemm_smalln_ws",
-              "q4_gemm_smalln_noalloc"):
+              "q4_gemm_smalln_noalloc", "q4_gemm_smalln_formats_ws_bytes", "q4_gemm_smalln_affine_ws",
+              "q4_gemm_smalln_nvfp4_ws"):
         assert n in names
 
 
@@ -167,6 +168,28 @@ def test_gemm_ws_errors(q4):
     assert _gemm_ws(q4, A, B, M, K, C, 33, D, E, need) == q4.Q4_ERR_SHAPE
     assert _gemm_ws(q4, A, B, M, K, None, N, D, E, need) == q4.Q4_ERR_NULL
     assert _gemm_ws(q4, None, None, 0, K, None, N, None, None, 0) == q4.Q4_OK
+
+
+def test_gemm_formats_ws_checks(q4):
+    """The affine and NVFP4-style products ask for scratch for every chunk of
+    2..32 tokens on rows longer than 2048 weights, and check it as
+    q4_gemm_smalln_ws does."""
+    nb = q4.q4_gemm_smalln_formats_ws_bytes
+    assert nb(2048, 11008, 2) == 6 * 2 * 2048 * 4 and nb(2048, 11008, 32) == 6 * 32 * 2048 * 4
+    assert nb(2048, 11008, 1) == 0 and nb(11008, 2048, 32) == 0 and nb(16, 11008, 33) == 0
+    L = q4.lib()
+    M, K, N = 16, 11008, 8
+    need = nb(M, K, N)
+    E = 0x50000000
+    Z = 0x60000000
+    aff = lambda ws, n_b, zeros=Z: L.q4_gemm_smalln_affine_ws(A, B, zeros, M, K, C, N, D, ws, n_b, None)
+    nv = lambda ws, n_b: L.q4_gemm_smalln_nvfp4_ws(A, B, Z, M, K, C, N, D, ws, n_b, None)
+    assert aff(None, 0) == q4.Q4_ERR_WORKSPACE and nv(None, 0) == q4.Q4_ERR_WORKSPACE
+    assert aff(E, need - 4) == q4.Q4_ERR_WORKSPACE and nv(E, need - 4) == q4.Q4_ERR_WORKSPACE
+    assert aff(E + 4, need) == q4.Q4_ERR_ALIGN and nv(E + 4, need) == q4.Q4_ERR_ALIGN
+    assert aff(Z, need) == q4.Q4_ERR_OVERLAP          # over the zero points
+    assert aff(E, need, zeros=None) == q4.Q4_ERR_NULL
+    assert nv(C + 1024, need) == q4.Q4_ERR_OVERLAP     # over X
 
 
 def test_gemm_noalloc_host_checks(q4):

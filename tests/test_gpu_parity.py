@@ -457,6 +457,53 @@ def test_gemm_smalln_formats_parity(env, M, K, N):
     _gemm_formats_case(env, M, K, N, W, X, "")
 
 
+def _gemm_formats_ws_case(env, M, K, N, W, X, what):
+    """The two formats' *_ws products against the oracle, and the same bits
+    on a second call into a workspace full of NaN."""
+    torch, q4, dev = env
+    Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+    ws = q4.formats_workspace(M, K, N, dev)
+
+    def nan_fill():
+        if ws is not None:
+            ws.view(torch.float32)[: ws.numel() // 4].fill_(float("nan"))
+    codes, scales, zeros, st = oracle.pack_affine(W)
+    assert st == 0
+    Y_ref, S = oracle.gemm_affine(codes, scales, zeros, M, K, X)
+    c, s, z = _affine_upload(env, codes, scales, zeros)
+    Y = q4.q4_gemm_smalln_affine_ws(c, s, z, Xd, ws).clone()
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, S, f"affine gemm ws {what} M={M} K={K} N={N}")
+    nan_fill()
+    assert torch.equal(Y, q4.q4_gemm_smalln_affine_ws(c, s, z, Xd, ws)), "affine: second call differs"
+    ncodes, nscales, ts, st = oracle.pack_nvfp4(W)
+    assert st == 0
+    Y_ref, S = oracle.gemm_nvfp4(ncodes, nscales, ts, M, K, X)
+    c, s, t = _nvfp4_upload(env, ncodes, nscales, ts)
+    Y = q4.q4_gemm_smalln_nvfp4_ws(c, s, t, Xd, ws).clone()
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, S, f"nvfp4 gemm ws {what} M={M} K={K} N={N}")
+    nan_fill()
+    assert torch.equal(Y, q4.q4_gemm_smalln_nvfp4_ws(c, s, t, Xd, ws)), "nvfp4: second call differs"
+
+
+@pytest.mark.parametrize("M,K,N", [(2048, 11008, 2), (70, 11008, 32), (77, 4160, 17), (301, 8256, 5),
+                                   (3, 24576, 8), (300, 2048, 8)])
+def test_gemm_formats_ws_parity(env, M, K, N):
+    seed = 9700 + M + K + N
+    W = wl.weights(M, K, seed, std=0.5) + np.float32(0.03)
+    X = wl.activations(N, K, seed, "unit_rms")
+    _gemm_formats_ws_case(env, M, K, N, W, X, "")
+
+
+@pytest.mark.parametrize("M,K,N", [(77, 11008, 9), (20, 8256, 32)])
+def test_gemm_formats_ws_wide_range_activations(env, M, K, N):
+    seed = 9800 + M + K + N
+    W = _wide_w(wl.weights(M, K, seed, std=0.5))
+    X = np.stack([_wide_x(WIDE_KINDS[(n + seed) % len(WIDE_KINDS)], K, seed + n) for n in range(N)])
+    _gemm_formats_ws_case(env, M, K, N, W, X, "wide")
+
+
 @pytest.mark.parametrize("M,K,N", [(300, 2048, 2), (300, 2048, 17), (77, 4160, 32), (300, 2048, 8),
                                    (3001, 1920, 5)])
 def test_gemm_smalln_formats_wide_range_activations(env, M, K, N):
