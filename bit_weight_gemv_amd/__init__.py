@@ -37,8 +37,7 @@ EXPORTED = ("q4_codes_bytes", "q4_scales_bytes", "q4_codebook", "q4_status_strin
             "q4_gather_rows", "q4_pack_affine", "q4_gemv_affine", "q4_pack_nvfp4", "q4_gemv_nvfp4",
             "q4_quantize_x8", "q4_gemv_affine_x8", "q4_gemm_smalln_affine", "q4_gemm_smalln_nvfp4",
             "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4", "q4_gemm_smalln_ws_bytes", "q4_gemm_smalln_ws",
-            "q4_gemm_smalln_noalloc", "q4_gemm_smalln_formats_ws_bytes", "q4_gemm_smalln_affine_ws",
-            "q4_gemm_smalln_nvfp4_ws")
+            "q4_gemm_smalln_noalloc", "q4_gemm_smalln_affine_ws", "q4_gemm_smalln_nvfp4_ws")
 
 Q4_OUT_F32 = 0
 Q4_OUT_BF16 = 1
@@ -109,8 +108,6 @@ def lib() -> ctypes.CDLL:
         L.q4_gemm_smalln_ws.restype = I32
         L.q4_gemm_smalln_noalloc.argtypes = [P, P, I64, I64, P, I64, P, P]
         L.q4_gemm_smalln_noalloc.restype = I32
-        L.q4_gemm_smalln_formats_ws_bytes.argtypes = [I64, I64, I64]
-        L.q4_gemm_smalln_formats_ws_bytes.restype = ctypes.c_size_t
         for name in ("q4_gemm_smalln_affine_ws", "q4_gemm_smalln_nvfp4_ws"):
             getattr(L, name).argtypes = [P, P, P, I64, I64, P, I64, P, P, ctypes.c_size_t, P]
             getattr(L, name).restype = I32
@@ -305,19 +302,6 @@ def q4_gemm_smalln_ws(codes, scales, X, workspace, Y=None, stream=None):
     if st != Q4_OK:
         raise Q4Error(st, "q4_gemm_smalln_ws")
     return Y
-
-
-def q4_gemm_smalln_formats_ws_bytes(M: int, K: int, N: int) -> int:
-    """Bytes of scratch the affine and NVFP4-style *_ws products need (0: none)."""
-    return int(lib().q4_gemm_smalln_formats_ws_bytes(M, K, N))
-
-
-def formats_workspace(M: int, K: int, N: int, device):
-    """A uint8 device tensor for q4_gemm_smalln_affine_ws / _nvfp4_ws, or None."""
-    n = q4_gemm_smalln_formats_ws_bytes(M, K, N)
-    if n == 0:
-        return None
-    return _torch().empty(n, dtype=_torch().uint8, device=device)
 
 
 def _ws_args(workspace, device):

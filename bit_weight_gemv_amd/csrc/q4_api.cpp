@@ -279,17 +279,12 @@ int q4_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scales, const ui
     return launch_status(q4::launch_gemm_smalln_affine(codes, scales, zeros, M, K, X, N, Y, (hipStream_t)stream));
 }
 
-size_t q4_gemm_smalln_formats_ws_bytes(int64_t M, int64_t K, int64_t N) {
-    if (!shape_ok(M, K) || M == 0 || N < 1 || N > Q4_MAX_N || !q4::gemm_split_fits_formats(M, K, N)) return 0;
-    return q4::gemm_split_bytes(M, K, N);
-}
-
 namespace {
 // The workspace checks shared by the two formats' entry points: `in` holds
 // the inputs' ranges (Y's overlap with them is checked by the caller).
 int formats_ws_check(int64_t M, int64_t K, int64_t N, Range ry, const Range *in, int nin, void *workspace,
                      size_t workspace_bytes) {
-    const size_t need = q4_gemm_smalln_formats_ws_bytes(M, K, N);
+    const size_t need = q4_gemm_smalln_ws_bytes(M, K, N);
     if (need == 0) return Q4_OK;
     if (!workspace || workspace_bytes < need) return Q4_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return Q4_ERR_ALIGN;

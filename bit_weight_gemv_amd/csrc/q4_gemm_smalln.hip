@@ -718,7 +718,8 @@ hipError_t launch_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int6
     if (gemm_rows4_fits(scales, nullptr, M, K, N))
         return launch_gemm_rows4(kGemmNf4, codes, scales, nullptr, nullptr, M, K, X, N, Y, stream);
     if (gemv_tokens_fits(M, K, N)) return launch_gemv_tokens(codes, scales, M, K, X, N, Y, stream);
-    if (gemv_tokens_multi_fits(M, K, N)) return launch_gemv_tokens_multi(codes, scales, M, K, X, N, Y, stream);
+    if (gemv_tokens_multi_fits(M, K, N))
+        return launch_gemv_tokens_multi(kGemmNf4, codes, scales, nullptr, nullptr, M, K, X, N, Y, stream);
     return launch_matrix_core<kGemmNf4>(codes, scales, nullptr, nullptr, M, K, X, N, Y, stream);
 }
 
@@ -773,16 +774,14 @@ hipError_t launch_gemm_smalln_ws(const uint8_t *codes, const uint16_t *scales, i
 hipError_t launch_gemm_smalln_affine_ws(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros,
                                         int64_t M, int64_t K, const uint16_t *X, int64_t N, float *Y, float *part,
                                         hipStream_t stream) {
-    if (!gemm_split_fits_formats(M, K, N))
-        return launch_gemm_smalln_affine(codes, scales, zeros, M, K, X, N, Y, stream);
+    if (!gemm_split_fits(M, K, N)) return launch_gemm_smalln_affine(codes, scales, zeros, M, K, X, N, Y, stream);
     return launch_matrix_core_split<kGemmAffine>(codes, scales, zeros, nullptr, M, K, X, N, Y, part, stream);
 }
 
 hipError_t launch_gemm_smalln_nvfp4_ws(const uint8_t *codes, const uint8_t *scales, const float *tscale, int64_t M,
                                        int64_t K, const uint16_t *X, int64_t N, float *Y, float *part,
                                        hipStream_t stream) {
-    if (!gemm_split_fits_formats(M, K, N))
-        return launch_gemm_smalln_nvfp4(codes, scales, tscale, M, K, X, N, Y, stream);
+    if (!gemm_split_fits(M, K, N)) return launch_gemm_smalln_nvfp4(codes, scales, tscale, M, K, X, N, Y, stream);
     return launch_matrix_core_split<kGemmNvfp4>(codes, scales, nullptr, tscale, M, K, X, N, Y, part, stream);
 }
 
@@ -791,6 +790,8 @@ hipError_t launch_gemm_smalln_affine(const uint8_t *codes, const uint16_t *scale
     if (N == 1) return launch_gemv_affine(codes, scales, zeros, M, K, X, Y, stream);
     if (gemm_rows4_fits(scales, zeros, M, K, N))
         return launch_gemm_rows4(kGemmAffine, codes, scales, zeros, nullptr, M, K, X, N, Y, stream);
+    if (gemv_tokens_multi_fits(M, K, N))
+        return launch_gemv_tokens_multi(kGemmAffine, codes, scales, zeros, nullptr, M, K, X, N, Y, stream);
     return launch_matrix_core<kGemmAffine>(codes, scales, zeros, nullptr, M, K, X, N, Y, stream);
 }
 
@@ -799,6 +800,8 @@ hipError_t launch_gemm_smalln_nvfp4(const uint8_t *codes, const uint8_t *scales,
     if (N == 1) return launch_gemv_nvfp4(codes, scales, tscale, M, K, X, Y, stream);
     if (gemm_rows4_fits(scales, nullptr, M, K, N))
         return launch_gemm_rows4(kGemmNvfp4, codes, scales, nullptr, tscale, M, K, X, N, Y, stream);
+    if (gemv_tokens_multi_fits(M, K, N))
+        return launch_gemv_tokens_multi(kGemmNvfp4, codes, scales, nullptr, tscale, M, K, X, N, Y, stream);
     return launch_matrix_core<kGemmNvfp4>(codes, scales, nullptr, tscale, M, K, X, N, Y, stream);
 }
 

@@ -104,6 +104,57 @@ __device__ __forceinline__ void chunk_dot_n(const uint32_t *lut, uint4 q, const 
     }
 }
 
+// The affine form of chunk_dot_n: z - 8 (`zz`) is taken from each looked-up
+// pair once, and the difference serves every token (the order of each
+// token's sums is chunk_dot<true>'s).
+template <int NTOK>
+__device__ __forceinline__ void chunk_dot_n_zoff(const uint32_t *lut, uint4 q, const half2_t (&xh)[NTOK][1][16],
+                                                 uint32_t laneoff, half2_t zz, float (&p)[NTOK]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) p[t] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        half2_t v[4];
+        v[0] = lut_pair<0>(lut, w[d], laneoff) - zz;
+        v[1] = lut_pair<1>(lut, w[d], laneoff) - zz;
+        v[2] = lut_pair<2>(lut, w[d], laneoff) - zz;
+        v[3] = lut_pair<3>(lut, w[d], laneoff) - zz;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int t = 0; t < NTOK; ++t) p[t] = __builtin_amdgcn_fdot2(v[b], xh[t][0][4 * d + b], p[t], false);
+    }
+}
+
+// chunk_dot_halves for NTOK tokens sharing each lookup (each token's two sums
+// in chunk_dot_halves' order).
+template <int NTOK>
+__device__ __forceinline__ void chunk_dot_halves_n(const uint32_t *lut, uint4 q, const half2_t (&xh)[NTOK][1][16],
+                                                   uint32_t laneoff, float (&p0)[NTOK], float (&p1)[NTOK]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    half2_t v[16];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        v[4 * d + 0] = lut_pair<0>(lut, w[d], laneoff);
+        v[4 * d + 1] = lut_pair<1>(lut, w[d], laneoff);
+        v[4 * d + 2] = lut_pair<2>(lut, w[d], laneoff);
+        v[4 * d + 3] = lut_pair<3>(lut, w[d], laneoff);
+    }
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) {
+        p0[t] = 0.0f;
+        p1[t] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) {
+            p0[t] = __builtin_amdgcn_fdot2(v[j], xh[t][0][j], p0[t], false);
+            p1[t] = __builtin_amdgcn_fdot2(v[j + 8], xh[t][0][j + 8], p1[t], false);
+        }
+}
+
 // The same dot split at the chunk's middle: p0 over its first 16 weights
 // (bytes 0..7), p1 over the last 16, for formats with a scale per 16 weights.
 __device__ __forceinline__ void chunk_dot_halves(const uint32_t *lut, uint4 q, const half2_t *xh,
@@ -372,8 +423,9 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     // from global memory once per workgroup into LDS (raw bf16, 16 bytes per
     // lane) and every wave takes its chunks from there.
     __shared__ uint4 xs[(MULTI || X8) ? 1 : kSharedXUnits * NTOK];
-    static_assert(NTOK == 1 || (MODE == kModePlain && FMT == kFmtNf4 && CPL == 1 && S == 0 && !STRIDED),
-                  "several tokens: plain NF4, one chunk a lane, no ring");
+    static_assert(NTOK == 1 || (MODE == kModePlain && (FMT == kFmtNf4 || FMT == kFmtAffine || FMT == kFmtNvfp4) &&
+                                CPL == 1 && S == 0 && !STRIDED),
+                  "several tokens: plain products of bf16 activations, one chunk a lane, no ring");
 
     static_assert(MODE != kModeSwiglu || NR % 2 == 0, "a SwiGLU tile pairs gate and up rows");
     constexpr int LPT = MODE == kModeSwiglu ? NR / 2 : NR;  // outputs per tile
@@ -693,7 +745,9 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
     // power of two (both multiply every finished sum).  In the SwiGLU form
     // the gate and up matrices carry tensor scales of their own: each
     // multiplies its finished sum in the store, before SiLU.
-    if constexpr (FMT == kFmtNvfp4 && MODE != kModeSwiglu) down *= *sg.tscale;
+    if constexpr (FMT == kFmtNvfp4 && MODE != kModeSwiglu)
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) downn[t] *= *sg.tscale;
     float ts_gate = 1.0f, ts_up = 1.0f;
     if constexpr (FMT == kFmtNvfp4 && MODE == kModeSwiglu) {
         ts_gate = *sg.tscale;
@@ -748,6 +802,15 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                         int tot = 128 * (t1 - 16 * zi * qs1[i]);
                         if constexpr (X8TWO) tot += t2 - 16 * zi * qs2[i];
                         a = fmaf((float)tot, f16_bits_to_f32(TS ? tsb[r] >> ts_sh : sc[buf][r][i]) * dsc[i], a);
+                    } else if constexpr (FMT == kFmtNvfp4 && NTOK > 1) {
+                        // (Each token's sums as in the one-token form below.)
+                        float p0n[NTOK], p1n[NTOK];
+                        chunk_dot_halves_n<NTOK>(lut, q[buf][r][i], xhn, laneoff, p0n, p1n);
+                        const float s0 = e4m3_to_f32(sc[buf][r][i]), s1 = e4m3_to_f32(sc[buf][r][i] >> 8);
+#pragma unroll
+                        for (int t = 1; t < NTOK; ++t) accn[t][j * NR + r] = fmaf(p1n[t], s1, p0n[t] * s0);
+                        a = fmaf(p0n[0], s0, a);
+                        a = fmaf(p1n[0], s1, a);
                     } else if constexpr (FMT == kFmtNvfp4) {
                         float p0, p1;
                         chunk_dot_halves(lut, q[buf][r][i], xh[i], laneoff, p0, p1);
@@ -755,7 +818,13 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                         a = fmaf(p1, e4m3_to_f32(sc[buf][r][i] >> 8), a);
                     } else if constexpr (NTOK > 1) {
                         float pn[NTOK];
-                        chunk_dot_n<NTOK>(lut, q[buf][r][i], xhn, laneoff, pn);
+                        if constexpr (FMT == kFmtAffine) {
+                            const _Float16 zo =
+                                (_Float16)(f16_bits_to_f32(TS ? tzb[r] >> ts_sh : zc[buf][r][i]) - 8.0f);
+                            chunk_dot_n_zoff<NTOK>(lut, q[buf][r][i], xhn, laneoff, half2_t{zo, zo}, pn);
+                        } else {
+                            chunk_dot_n<NTOK>(lut, q[buf][r][i], xhn, laneoff, pn);
+                        }
                         const float sf = f16_bits_to_f32(TS ? tsb[r] >> ts_sh : sc[buf][r][i]);
 #pragma unroll
                         for (int t = 1; t < NTOK; ++t) accn[t][j * NR + r] = pn[t] * sf;
@@ -941,15 +1010,12 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int K, const uint16
                     }
                 }
                 if (!MULTI) {
-                    store(tot[0] * tsc, g0, epi);
 #pragma unroll
-                    for (int tk = 1; tk < NTOK; ++tk) store(tot[tk], g0, epi, tk);
+                    for (int tk = 0; tk < NTOK; ++tk) store(tot[tk] * tsc, g0, epi, tk);
                 } else {
-                    if (lane < RG) {
-                        red[0][wave][lane] = tot[0] * tsc;
+                    if (lane < RG)
 #pragma unroll
-                        for (int tk = 1; tk < NTOK; ++tk) red[tk][wave][lane] = tot[tk];
-                    }
+                        for (int tk = 0; tk < NTOK; ++tk) red[tk][wave][lane] = tot[tk] * tsc;
                     __syncthreads();
                     if (wig == 0) {
 #pragma unroll
@@ -1038,20 +1104,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 768), amdgpu_waves_per
 // tokens, 16 VGPRs of activations each; up to 16 waves a CU for two tokens
 // (at most 128 VGPRs), 12 for three or four.
 constexpr int tokens_multi_waves(int ntok) { return ntok == 2 ? 16 : 12; }
-template <int NTOK, bool TS>
+// FMT: the NF4 codebook, the affine format (zeros: its zero points) or the
+// NVFP4-style format (scales: its E4M3 bytes read in pairs, tscale: the
+// tensor scale).
+template <int NTOK, int FMT, bool TS>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, 64 * tokens_multi_waves(NTOK)),
                           amdgpu_waves_per_eu(tokens_multi_waves(NTOK) / 4, 8))) void
-gemv_tokens_multi_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, int64_t M, int K,
+gemv_tokens_multi_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+                         const uint16_t *__restrict__ zeros, const float *__restrict__ tscale, int64_t M, int K,
                          const uint16_t *__restrict__ X, float *__restrict__ Y, int P, int64_t rows_q,
                          int rows_rem) {
     GemvSeg sg{};
     sg.codes0 = codes;
     sg.scales0 = scales;
+    sg.zeros0 = zeros;
+    sg.tscale = tscale;
     sg.y = Y;
     sg.rows = M;
     sg.rows_q = rows_q;
     sg.rows_rem = rows_rem;
-    gemv_body<4, 1, 0, 4, true, kModePlain, kFmtNf4, false, TS, NTOK>(sg, K, X, P, (int64_t)blockIdx.x);
+    gemv_body<4, 1, 0, 4, true, kModePlain, FMT, false, TS, NTOK>(sg, K, X, P, (int64_t)blockIdx.x);
 }
 
 // The affine format's GEMV (y = W . x with W = (code - z) * s).
@@ -1531,15 +1603,27 @@ const void *gemv_tokens_fn(bool ts) {
     return ts ? reinterpret_cast<const void *>(&gemv_tokens_kernel<NTOK, true>)
               : reinterpret_cast<const void *>(&gemv_tokens_kernel<NTOK, false>);
 }
-template <int NTOK>
+template <int NTOK, int FMT>
 const void *gemv_tokens_multi_fn(bool ts) {
-    return ts ? reinterpret_cast<const void *>(&gemv_tokens_multi_kernel<NTOK, true>)
-              : reinterpret_cast<const void *>(&gemv_tokens_multi_kernel<NTOK, false>);
+    if constexpr (FMT == kFmtNvfp4)  // (no one-load scale runs for E4M3 bytes)
+        return reinterpret_cast<const void *>(&gemv_tokens_multi_kernel<NTOK, FMT, false>);
+    else
+        return ts ? reinterpret_cast<const void *>(&gemv_tokens_multi_kernel<NTOK, FMT, true>)
+                  : reinterpret_cast<const void *>(&gemv_tokens_multi_kernel<NTOK, FMT, false>);
+}
+template <int FMT>
+const void *gemv_tokens_multi_fn(int64_t N, bool ts) {
+    return N == 2 ? gemv_tokens_multi_fn<2, FMT>(ts) : N == 3 ? gemv_tokens_multi_fn<3, FMT>(ts)
+                                                            : gemv_tokens_multi_fn<4, FMT>(ts);
 }
 }  // namespace
 
-hipError_t launch_gemv_tokens_multi(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
-                                    const uint16_t *X, int64_t N, float *Y, hipStream_t stream) {
+hipError_t launch_gemv_tokens_multi(int fmt, const uint8_t *codes, const void *scales_v, const uint16_t *zeros,
+                                    const float *tscale, int64_t M, int64_t K, const uint16_t *X, int64_t N, float *Y,
+                                    hipStream_t stream) {
+    // (The E4M3 bytes of the NVFP4-style format are read two at a time, as
+    // one 16-bit value per 32-weight chunk.)
+    const uint16_t *scales = static_cast<const uint16_t *>(scales_v);
     if (!gemv_tokens_multi_fits(M, K, N)) return hipErrorInvalidValue;
     int k = (int)K;
     const int C = k / kChunkWeights;
@@ -1554,10 +1638,11 @@ hipError_t launch_gemv_tokens_multi(const uint8_t *codes, const uint16_t *scales
     const int64_t ngroups = grid * sh.G;
     int64_t rows_q = M / ngroups;
     int rows_rem = (int)(M % ngroups);
-    const bool ts = scale_runs_aligned(scales, nullptr, k);
-    const void *fn = N == 2 ? gemv_tokens_multi_fn<2>(ts) : N == 3 ? gemv_tokens_multi_fn<3>(ts)
-                                                                   : gemv_tokens_multi_fn<4>(ts);
-    void *args[] = {&codes, &scales, &M, &k, &X, &Y, &P, &rows_q, &rows_rem};
+    const bool ts = scale_runs_aligned(scales, fmt == kGemmAffine ? zeros : nullptr, k);
+    const void *fn = fmt == kGemmAffine ? gemv_tokens_multi_fn<kFmtAffine>(N, ts)
+                     : fmt == kGemmNvfp4 ? gemv_tokens_multi_fn<kFmtNvfp4>(N, ts)
+                                         : gemv_tokens_multi_fn<kFmtNf4>(N, ts);
+    void *args[] = {&codes, &scales, &zeros, &tscale, &M, &k, &X, &Y, &P, &rows_q, &rows_rem};
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)(P * sh.G)), args, 0, stream);
 }
 

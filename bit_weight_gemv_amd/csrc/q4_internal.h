@@ -16,7 +16,7 @@ hipError_t launch_gemv_tokens(const uint8_t *codes, const uint16_t *scales, int6
                               const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
 // A chunk of 2 or 3 tokens on rows of 65..768 chunks of 32 weights (4
 // tokens: 256..768 chunks): the grouped long-row GEMV with every table
-// lookup serving all tokens.  Each wave loads its own slice of every
+// lookup serving all tokens, in the three weight formats.  Each wave loads its own slice of every
 // token's activations, so a token costs more on rows of fewer chunks;
 // measured against the 16-row matrix-core kernel (A/B in one process, us):
 // 2048 x 11008 N = 2 / 3 / 4 7.1 / 8.9 / 10.7 against 17.2 / 17.4 / 17.4;
@@ -30,8 +30,11 @@ inline bool gemv_tokens_multi_fits(int64_t M, int64_t K, int64_t N) {
     const int64_t C = K / 32;  // 32-weight chunks a row
     return N >= 2 && N <= 4 && M >= 1 && C > 64 && C <= 64 * 12 && (N < 4 || C >= 256);
 }
-hipError_t launch_gemv_tokens_multi(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
-                                    const uint16_t *X, int64_t N, float *Y, hipStream_t stream);
+// fmt: kGemmNf4, kGemmAffine (zeros) or kGemmNvfp4 (scales: the E4M3 bytes,
+// tscale); the others null.
+hipError_t launch_gemv_tokens_multi(int fmt, const uint8_t *codes, const void *scales, const uint16_t *zeros,
+                                    const float *tscale, int64_t M, int64_t K, const uint16_t *X, int64_t N, float *Y,
+                                    hipStream_t stream);
 // Weight formats of the prefill kernels.
 enum { kGemmNf4 = 0, kGemmAffine = 1, kGemmNvfp4 = 2 };
 
@@ -104,11 +107,6 @@ inline int split_kranges(int64_t K) {
 // row take only rows of up to 2048 weights).
 inline bool gemm_split_fits(int64_t M, int64_t K, int64_t N) {
     return N >= 2 && N <= 32 && M >= 1 && split_kranges(K) > 1 && !gemv_tokens_multi_fits(M, K, N);
-}
-// The affine and NVFP4-style prefill products have no grouped-GEMV path for
-// a few tokens: the split serves every chunk of 2..32 tokens on long rows.
-inline bool gemm_split_fits_formats(int64_t M, int64_t K, int64_t N) {
-    return N >= 2 && N <= 32 && M >= 1 && split_kranges(K) > 1;
 }
 inline size_t gemm_split_bytes(int64_t M, int64_t K, int64_t N) {
     return (size_t)split_kranges(K) * (size_t)N * (size_t)M * sizeof(float);

@@ -150,8 +150,10 @@ int q4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
  * or three tokens on such rows by the q4_gemv kernels with each table
  * lookup serving every token; chunks of two or three tokens on rows of
  * 2080 .. 24576 weights (four tokens: 8192 .. 24576) likewise by the
- * q4_gemv kernels for rows spanning several waves (each row of Y is then
- * bit-identical to q4_gemv of that token); all others by 16-row
+ * q4_gemv kernels for rows spanning several waves (a row of Y is then
+ * bit-identical to q4_gemv of its token while no wave holds values of
+ * another token of the chunk that span more than 2^28: such a wave takes
+ * the exact path for all the chunk's tokens); all others by 16-row
  * matrix-core tiles.
  */
 int q4_gemm_smalln(const uint8_t *codes, const uint16_t *scales, int64_t M,
@@ -437,16 +439,16 @@ int q4_gemm_smalln_nvfp4(const uint8_t *codes, const uint8_t *scales,
  * q4_gemm_smalln_affine_ws, q4_gemm_smalln_nvfp4_ws -- the prefill products
  * of the two extra formats (the same passages as q4_gemm_smalln_affine and
  * q4_gemm_smalln_nvfp4) with scratch for partial sums, as q4_gemm_smalln_ws
- * is for the NF4 codebook format: on rows longer than 2048 weights, chunks
- * of 2..32 tokens split K into ranges of at most 2048 weights whose partial
- * planes a second launch adds in range order.  Elsewhere the call is the
- * format's q4_gemm_smalln_* entry point (the workspace may then be NULL).
- *   workspace: at least q4_gemm_smalln_formats_ws_bytes(M, K, N) bytes of
- *     device memory, 16-byte aligned, as for q4_gemm_smalln_ws.
+ * is for the NF4 codebook format, and on the same chunks: on rows longer
+ * than 2048 weights, chunks that the 16-row kernel would take split K into
+ * ranges of at most 2048 weights whose partial planes a second launch adds
+ * in range order.  Elsewhere the call is the format's q4_gemm_smalln_*
+ * entry point (the workspace may then be NULL).
+ *   workspace: at least q4_gemm_smalln_ws_bytes(M, K, N) bytes of device
+ *     memory, 16-byte aligned, as for q4_gemm_smalln_ws.
  * Errors: as the format's q4_gemm_smalln_* entry point, and those of
  * q4_gemm_smalln_ws for the workspace.
  */
-size_t q4_gemm_smalln_formats_ws_bytes(int64_t M, int64_t K, int64_t N);
 int q4_gemm_smalln_affine_ws(const uint8_t *codes, const uint16_t *scales,
                              const uint16_t *zeros, int64_t M, int64_t K,
                              const uint16_t *X, int64_t N, float *Y,

@@ -37,7 +37,7 @@ def test_header_declares_the_entry_points():
               "q4_quantize_x8", "q4_gemv_affine_x8", "q4_gemm_smalln_affine", "q4_gemm_smalln_nvfp4",
               "q4_gemv_fused_affine", "q4_gemv_fused_nvfp4", "q4_codebook", "q4_codes_bytes",
               "q4_scales_bytes", "q4_status_string", "q4_gemm_smalln_ws_bytes", "q4_gemm_smalln_ws",
-              "q4_gemm_smalln_noalloc", "q4_gemm_smalln_formats_ws_bytes", "q4_gemm_smalln_affine_ws",
+              "q4_gemm_smalln_noalloc", "q4_gemm_smalln_affine_ws",
               "q4_gemm_smalln_nvfp4_ws"):
         assert n in names
 
@@ -171,12 +171,10 @@ def test_gemm_ws_errors(q4):
 
 
 def test_gemm_formats_ws_checks(q4):
-    """The affine and NVFP4-style products ask for scratch for every chunk of
-    2..32 tokens on rows longer than 2048 weights, and check it as
-    q4_gemm_smalln_ws does."""
-    nb = q4.q4_gemm_smalln_formats_ws_bytes
-    assert nb(2048, 11008, 2) == 6 * 2 * 2048 * 4 and nb(2048, 11008, 32) == 6 * 32 * 2048 * 4
-    assert nb(2048, 11008, 1) == 0 and nb(11008, 2048, 32) == 0 and nb(16, 11008, 33) == 0
+    """The affine and NVFP4-style *_ws products take scratch on the same
+    chunks as q4_gemm_smalln_ws, sized by q4_gemm_smalln_ws_bytes, and check
+    it the same way."""
+    nb = q4.q4_gemm_smalln_ws_bytes
     L = q4.lib()
     M, K, N = 16, 11008, 8
     need = nb(M, K, N)

@@ -462,7 +462,7 @@ def _gemm_formats_ws_case(env, M, K, N, W, X, what):
     on a second call into a workspace full of NaN."""
     torch, q4, dev = env
     Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
-    ws = q4.formats_workspace(M, K, N, dev)
+    ws = q4.gemm_workspace(M, K, N, dev)
 
     def nan_fill():
         if ws is not None:
@@ -496,7 +496,40 @@ def test_gemm_formats_ws_parity(env, M, K, N):
     _gemm_formats_ws_case(env, M, K, N, W, X, "")
 
 
-@pytest.mark.parametrize("M,K,N", [(77, 11008, 9), (20, 8256, 32)])
+@pytest.mark.parametrize("M,K,N", [(2048, 11008, 2), (2049, 11008, 3), (77, 24576, 4), (1001, 4160, 3),
+                                   (300, 8192, 4), (5, 2112, 2)])
+def test_gemm_formats_tokens_long_rows_are_the_gemv(env, M, K, N):
+    """Two to four tokens on rows of several waves in the affine and
+    NVFP4-style formats: every token's row equals the format's GEMV of that
+    token bit for bit, and the oracle within the bound (unit-RMS
+    activations, as in the NF4 test above)."""
+    torch, q4, dev = env
+    seed = 9900 + M + K + N
+    W = wl.weights(M, K, seed, std=0.5) + np.float32(0.03)
+    X = wl.activations(N, K, seed, "unit_rms")
+    Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+    codes, scales, zeros, st = oracle.pack_affine(W)
+    assert st == 0
+    Y_ref, S = oracle.gemm_affine(codes, scales, zeros, M, K, X)
+    c, s, z = _affine_upload(env, codes, scales, zeros)
+    Y = q4.q4_gemm_smalln_affine(c, s, z, Xd)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, S, f"affine tokens M={M} K={K} N={N}")
+    for n in range(N):
+        assert torch.equal(Y[n], q4.q4_gemv_affine(c, s, z, Xd[n].contiguous())), f"affine token {n}"
+    ncodes, nscales, ts, st = oracle.pack_nvfp4(W)
+    assert st == 0
+    Y_ref, S = oracle.gemm_nvfp4(ncodes, nscales, ts, M, K, X)
+    c, s, t = _nvfp4_upload(env, ncodes, nscales, ts)
+    Y = q4.q4_gemm_smalln_nvfp4(c, s, t, Xd)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, S, f"nvfp4 tokens M={M} K={K} N={N}")
+    for n in range(N):
+        assert torch.equal(Y[n], q4.q4_gemv_nvfp4(c, s, t, Xd[n].contiguous())), f"nvfp4 token {n}"
+
+
+@pytest.mark.parametrize("M,K,N", [(77, 11008, 9), (20, 8256, 32), (300, 11008, 3), (50, 8192, 4),
+                                   (2048, 11008, 2), (77, 24576, 4)])
 def test_gemm_formats_ws_wide_range_activations(env, M, K, N):
     seed = 9800 + M + K + N
     W = _wide_w(wl.weights(M, K, seed, std=0.5))
@@ -796,11 +829,14 @@ def test_gemm_smalln_full_size(env):
 def test_gemm_tokens_long_rows_are_the_gemv(env, M, K, N):
     """Two to four tokens on rows of several waves: every token's row equals
     q4_gemv of that token bit for bit (the same conversion, products,
-    reduction and cross-wave sum per token), and the oracle within the bound."""
+    reduction and cross-wave sum per token), and the oracle within the bound.
+    (Unit-RMS activations: no wave's values span more than 2^28, so every
+    wave takes the fp16 path for every token, as the GEMV does; a wave with
+    one token beyond that takes the exact path for all of them.)"""
     torch, q4, dev = env
     seed = 8200 + M + K + N
     W = wl.weights(M, K, seed)
-    X = wl.activations(N, K, seed, "swiglu")
+    X = wl.activations(N, K, seed, "unit_rms")
     codes, scales, _ = oracle.pack(W)
     Y_ref, S = oracle.gemm(codes, scales, M, K, X)
     c, s = _upload_packed(env, codes, scales)
