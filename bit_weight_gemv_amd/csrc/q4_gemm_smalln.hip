@@ -46,8 +46,14 @@
 //  * Schedule.  Row tiles of 16 rows are split into contiguous ranges, one
 //    per workgroup (one workgroup per CU); the waves walk the range in step
 //    with a ring of prefetched tiles (codes and scales of tile t+1 .. t+S are
-//    in flight while tile t is multiplied).  Per tile the waves' partial
-//    tiles are summed through LDS.
+//    in flight while tile t is multiplied).  The waves' partial tiles are
+//    summed through LDS, once per group of tiles.
+//  * Long rows with scratch memory (the *_ws entry points).  K is cut into
+//    ranges of at most 8 slices (2048 weights); each workgroup takes one
+//    range of one row range, keeps that range's activations in registers
+//    for all its tiles, and writes a partial plane; a second launch adds the
+//    planes in range order.  Without scratch, rows longer than 8 slices
+//    reload each slice of the activations for every tile.
 #include <mutex>
 #include <type_traits>
 

@@ -10,8 +10,9 @@
 // is laid out for gfx950:
 //
 //  * Weight stream.  A lane owns 16-byte chunks of a row (32 weights); 64
-//    lanes of a wave read 1 KB contiguous per load (global_load_dwordx4),
-//    and all chunks of a tile are in flight before any is used.
+//    lanes of a wave read 1 KB contiguous per load (non-temporal
+//    buffer_load_dwordx4), and all chunks of a tile are in flight before
+//    any is used.
 //  * Lookup table.  A byte of codes (two weights) indexes a 256-entry table
 //    whose entry is the pair (level[lo nibble], level[hi nibble]) as two fp16
 //    in one dword, so one ds_read_b32 dequantises two weights and one
@@ -32,13 +33,19 @@
 //    bf16 input.
 //  * Scale.  The dot over a 32-weight chunk is multiplied by its block
 //    scale once (fp32 FMA).
-//  * Reduction.  DPP row ops + ds_swizzle + readlane inside the wave; an LDS
-//xchange across the waves of a workgroup when one row spans several
+//  * Reduction.  DPP row ops, ds_swizzle and ds_bpermute inside the wave;
+//    an LDS exchange across the waves of a group when one row spans several
 //    waves (long K).
 //  * Schedule.  Rows are split into contiguous ranges, one per lane group
-//    (a wave, or a whole workgroup for long K); a group walks its range NR
-//    rows at a time with the next tile's loads issued before the current
-//    tile is reduced.
+//    (a wave, or a group of waves for long K), or, on large matrices of
+//    short rows, tiles are dealt to the waves in turn (the strided order);
+//    a group walks its tiles NR rows at a time with the next tile's loads
+//    issued before the current tile is reduced.
+//  * Several tokens.  A prefill chunk of 2..4 tokens (gemv_tokens_kernel,
+//    gemv_tokens_multi_kernel) runs the same body with each token's
+//    activations converted as above and every table lookup feeding each
+//    token's dot product, so each token's arithmetic is the one-token
+//    GEMV's.
 //
 // Error: the fp16 table rounds each level by at most 2^-11 relatively; every
 // other step is an fp32 add or multiply.
