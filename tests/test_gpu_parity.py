@@ -924,6 +924,34 @@ def test_gemm_ws_wide_range_activations(env, M, K, N):
     _check(Y.cpu().numpy(), Y_ref, S, f"gemm ws wide M={M} K={K} N={N}")
 
 
+def test_gemm_formats_full_size_down(env):
+    """The affine and NVFP4-style prefill products on the down projection's
+    shape (2048 x 11008): 2 and 4 tokens (the grouped GEMV with shared
+    lookups) and 8 and 32 tokens with scratch (the K split), every output
+    against the oracle."""
+    torch, q4, dev = env
+    c = wl.CONFIGS["down"]
+    M, K, N = c["M"], c["K"], 32
+    W = wl.weights(M, K, c["seed"])
+    X = wl.activations(N, K, c["seed"], c["x"])
+    Xd = cases.to_dev(X.view(np.int16), torch, dev).view(torch.bfloat16)
+    codes, scales, zeros, st = oracle.pack_affine(W)
+    assert st == 0
+    Y_ref, S = oracle.gemm_affine(codes, scales, zeros, M, K, X)
+    ca, sa, za = _affine_upload(env, codes, scales, zeros)
+    ncodes, nscales, ts, st = oracle.pack_nvfp4(W)
+    assert st == 0
+    Yn_ref, Sn = oracle.gemm_nvfp4(ncodes, nscales, ts, M, K, X)
+    cn, sn, tn = _nvfp4_upload(env, ncodes, nscales, ts)
+    ws = q4.gemm_workspace(M, K, N, dev)
+    for n_tok in (32, 8, 4, 2):
+        Xn = Xd[:n_tok].contiguous()
+        Y = q4.q4_gemm_smalln_affine_ws(ca, sa, za, Xn, ws).cpu().numpy()
+        _check(Y, Y_ref[:n_tok], S[:n_tok], f"affine down prefill N={n_tok} all {M} rows")
+        Y = q4.q4_gemm_smalln_nvfp4_ws(cn, sn, tn, Xn, ws).cpu().numpy()
+        _check(Y, Yn_ref[:n_tok], Sn[:n_tok], f"nvfp4 down prefill N={n_tok} all {M} rows")
+
+
 def test_graph_capture_long_row_tokens(env):
     """The grouped GEMV with shared lookups (2, 3 and 4 tokens on rows of
     11008 weights) and the K split with scratch (9 tokens) captured in a HIP

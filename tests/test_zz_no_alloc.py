@@ -68,6 +68,34 @@ def test_noalloc_without_split_is_the_plain_call(env):
     assert torch.equal(Y, q4.q4_gemm_smalln(c, s, Xd))
 
 
+def test_noalloc_in_a_hip_graph(env):
+    """Captured in a HIP graph (the callers it is for), the call replays to
+    the eager result every time, with eager calls of another shape (sharing
+    the same scratch) between the replays."""
+    torch, q4, dev = env
+    M, K, N = 600, 11008, 9
+    c, s, Xd, _, _ = _case(env, M, K, N, 64)
+    c2, s2, X2, _, _ = _case(env, 301, 8256, 5, 65)
+    eager = q4.q4_gemm_smalln_noalloc(c, s, Xd).clone()
+    Y = torch.full((N, M), float("nan"), device=dev)
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            q4.q4_gemm_smalln_noalloc(c, s, Xd, Y, stream=st)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        Y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, eager), f"replay {rep} differs from eager"
+        q4.q4_gemm_smalln_noalloc(c2, s2, X2)
+        torch.cuda.synchronize()
+
+
 def test_noalloc_refuses_beyond_its_scratch(env):
     torch, q4, dev = env
     M, K, N = 151936, 4096, 32
